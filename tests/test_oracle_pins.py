@@ -1,0 +1,385 @@
+"""Pins of the CPU oracle against facts other than itself: the pages' printed sizes,
+hand-built blocks with closed-form values, exact rational arithmetic, textbook special
+cases and invariants of the Llama decoder (each test names what it pins)."""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _block(size, ranges, default=0):
+    b = np.full(size, default, dtype=np.uint8)
+    for s, e, v in ranges:
+        b[s:e] = v
+    return b
+
+
+def _expected(entry, n):
+    if "runs" in entry:
+        out = []
+        for cnt, v in entry["runs"]:
+            out += [float.fromhex(v) if isinstance(v, str) else float(v)] * cnt
+        return np.array(out, dtype=np.float64)
+    sp = entry["sparse"]
+    out = np.full(n, float.fromhex(sp["default"]))
+    for i, v in sp["at"].items():
+        out[int(i)] = float.fromhex(v)
+    return out
+
+
+# ---------------------------------------------------------------- pages' numbers
+
+def test_block_sizes_match_quant_table():
+    """Show HN page quantization-format table: bits/weight and block sizes."""
+    pages = json.load(open(os.path.join(GOLDEN, "page_numbers.json")))["quant_table"]["rows"]
+    for row in pages:
+        qt = row["qtype"]
+        assert oracle.lib().orc_block_weights(qt) == row["block"]
+        bpw = oracle.lib().orc_block_bytes(qt) * 8 / row["block"]
+        step = row.get("printed_rounded_to", 0.0)
+        assert abs(bpw - row["bits_per_weight"]) <= step / 2 + 1e-12, (row, bpw)
+        assert synth.BLOCK_BYTES[qt] == oracle.lib().orc_block_bytes(qt)
+
+
+def test_70b_q6k_layer_size_matches_pages():
+    """NTransformer page: one 70B Q6_K layer is about 670 MB (NVMe direct streaming section)."""
+    g = json.load(open(os.path.join(GOLDEN, "page_numbers.json")))["layer_70b_q6_k_mb"]
+    b = synth.LLAMA70B_Q6_K_STREAM.layer_bytes()
+    assert b == 701890560
+    assert abs(b / 2**20 - g["value_mb"]) <= g["tolerance_mb"]
+
+
+def test_8b_q8_0_fits_pages_vram():
+    """Show HN page: 8B Q8_0 fully resident in about 10 GB of VRAM."""
+    g = json.load(open(os.path.join(GOLDEN, "page_numbers.json")))["vram_8b_q8_0_gb"]
+    assert synth.LLAMA8B_Q8_0.model_bytes() / 1e9 < g["upper_bound_gb"]
+
+
+# ---------------------------------------------------------------- dequant closed forms
+
+BLOCKS = json.load(open(os.path.join(GOLDEN, "blocks.json")))
+
+
+@pytest.mark.parametrize("entry", BLOCKS["blocks"], ids=[b["name"] for b in BLOCKS["blocks"]])
+def test_dequant_hand_built_block(entry):
+    qt, size = entry["qtype"], entry["size"]
+    B = oracle.lib().orc_block_weights(qt)
+    blk = _block(size, entry["set"])
+    w = oracle.dequant(qt, blk, 1, B)[0]
+    exp = _expected(entry, B)
+    assert np.array_equal(w.astype(np.float64), exp), (entry["name"], w[:40], exp[:40])
+    if entry.get("positive_zero"):
+        assert not np.any(np.signbit(w[w == 0]))
+
+
+@pytest.mark.parametrize("group", BLOCKS["onehot"], ids=lambda g: str(g["qtype"]))
+def test_dequant_onehot_positions(group):
+    qt, size = group["qtype"], group["size"]
+    B = oracle.lib().orc_block_weights(qt)
+    for ranges, idx, val in group["cases"]:
+        blk = _block(size, group["base"] + ranges)
+        w = oracle.dequant(qt, blk, 1, B)[0]
+        exp = np.full(B, float(group["default"]))
+        exp[idx] = val
+        assert np.array_equal(w.astype(np.float64), exp), (ranges, np.nonzero(w != group["default"]))
+
+
+@pytest.mark.parametrize("qt", [synth.Q8_0, synth.Q4_0, synth.Q4_K, synth.Q5_K, synth.Q6_K])
+def test_dequant_recovers_drawn_fields(qt):
+    """decode(bytes) equals the exact value of the fields the generator drew, rounded once to fp32."""
+    dist = synth.DEFAULT_DIST[qt]
+    B = synth.BLOCK_WEIGHTS[qt]
+    k, rows = 2 * B, 3
+    tk = synth.key(7, 1000 + qt)
+    W = synth.matrix(dist, k, rows, tkey=tk)
+    w = oracle.dequant(qt, W, rows, k)
+    for r in range(rows):
+        for b in range(k // B):
+            f = synth.block_fields(dist, k, r, b, tkey=tk)
+            d = Fraction(oracle.half_value(f["d"]))
+            dm = Fraction(oracle.half_value(f["dmin"]))
+            for i in range(B):
+                q = int(f["q"][i])
+                if qt == synth.Q8_0:
+                    v = d * q
+                elif qt == synth.Q4_0:
+                    v = d * (q - 8)
+                elif qt in (synth.Q4_K, synth.Q5_K):
+                    s = i // 32
+                    v = d * int(f["sc"][s]) * q - dm * int(f["m"][s])
+                else:
+                    v = d * int(f["sc"][i // 16]) * (q - 32)
+                assert float(np.float32(float(v))) == float(w[r, b * B + i]), (qt, r, b, i)
+
+
+# ---------------------------------------------------------------- GEMV
+
+def test_gemv_identity_q8_0():
+    """W = I built from Q8_0 blocks with d = 1 gives y = x exactly."""
+    n = 64
+    W = np.zeros((n, 2 * 34), dtype=np.uint8)
+    for r in range(n):
+        for b in range(2):
+            W[r, b * 34 + 1] = 0x3C  # d = 1.0
+        W[r, (r // 32) * 34 + 2 + (r % 32)] = 1
+    x = synth.normal_f32(synth.key(0, 5), n)
+    y, a = oracle.gemv(synth.Q8_0, W, n, n, x)
+    assert np.array_equal(y, x.astype(np.float64))
+    assert np.array_equal(a, np.abs(x.astype(np.float64)))
+
+
+@pytest.mark.parametrize("qt", [synth.Q8_0, synth.Q4_0, synth.Q4_K, synth.Q5_K, synth.Q6_K])
+@pytest.mark.parametrize("k", [256, 512])
+def test_gemv_exact_rational(qt, k):
+    """Brute force with exact rationals on rows <= 4: the fp64 sum is within K * 2^-53 * A."""
+    rows = 3
+    tk = synth.key(11, 2000 + qt * 10 + k)
+    W = synth.matrix(synth.DEFAULT_DIST[qt], k, rows, tkey=tk)
+    x = synth.normal_f32(synth.key(11, 3000 + k), 2 * k).reshape(2, k)
+    y, a = oracle.gemv(qt, W, rows, k, x)
+    w = oracle.dequant(qt, W, rows, k)
+    for j in range(2):
+        for r in range(rows):
+            exact = sum(Fraction(float(w[r, c])) * Fraction(float(x[j, c])) for c in range(k))
+            absum = sum(abs(Fraction(float(w[r, c])) * Fraction(float(x[j, c]))) for c in range(k))
+            assert abs(Fraction(y[j, r]) - exact) <= Fraction(k) * Fraction(2) ** -53 * absum
+            assert abs(Fraction(a[j, r]) - absum) <= Fraction(k) * Fraction(2) ** -53 * absum
+    # columns are independent: one column at a time gives the same numbers
+    y0, _ = oracle.gemv(qt, W, rows, k, x[1])
+    assert np.array_equal(y0, y[1])
+
+
+def test_gemv_rejects_bad_k():
+    with pytest.raises(ValueError):
+        oracle.gemv(synth.Q4_K, np.zeros(144, np.uint8), 1, 200, np.zeros(200))
+
+
+# ---------------------------------------------------------------- norm, rope, attention, act
+
+def test_rmsnorm_unit_rms_times_gain():
+    x = synth.normal_f32(synth.key(1, 1), 4096, 0.3, 5.0).astype(np.float64)
+    g = synth.normal_f32(synth.key(1, 2), 4096, 1.0, 0.02)
+    y = oracle.rmsnorm(x, g, 0.0)
+    assert abs(math.sqrt(np.mean((y / g) ** 2)) - 1.0) < 1e-12
+    assert np.allclose(oracle.rmsnorm(7.5 * x, g, 0.0), y, rtol=1e-13, atol=0)
+
+
+def test_rmsnorm_eps_closed_form():
+    # x = 1 everywhere, eps = 3: 1 / sqrt(1 + 3) = 1/2
+    g = np.array([1.0, 2.0, -4.0, 0.5], dtype=np.float32)
+    assert np.array_equal(oracle.rmsnorm(np.ones(4), g, 3.0), 0.5 * g.astype(np.float64))
+
+
+def test_rope_identity_at_zero_and_norms():
+    hd, nh = 128, 3
+    v = synth.normal_f32(synth.key(2, 1), nh * hd).astype(np.float64)
+    assert np.array_equal(oracle.rope(v, nh, hd, 0, 5e5), v)
+    r = oracle.rope(v, nh, hd, 1234, 5e5)
+    pn = lambda a: np.hypot(a[0::2], a[1::2])
+    assert np.allclose(pn(r), pn(v), rtol=1e-13)
+
+
+def test_rope_composition_and_relative_position():
+    hd = 128
+    v = synth.normal_f32(synth.key(2, 2), hd).astype(np.float64)
+    w = synth.normal_f32(synth.key(2, 3), hd).astype(np.float64)
+    a = oracle.rope(oracle.rope(v, 1, hd, 300, 5e5), 1, hd, 4000, 5e5)
+    assert np.allclose(a, oracle.rope(v, 1, hd, 4300, 5e5), rtol=0, atol=1e-9)
+    d1 = oracle.rope(v, 1, hd, 1000, 5e5) @ oracle.rope(w, 1, hd, 990, 5e5)
+    d2 = oracle.rope(v, 1, hd, 17, 5e5) @ oracle.rope(w, 1, hd, 7, 5e5)
+    assert abs(d1 - d2) < 1e-9 * (np.abs(v) @ np.abs(w))
+
+
+def test_rope_pairs_and_frequencies():
+    """Adjacent pairs (2i, 2i+1) rotate; pair 0 turns by pos radians; pair hd/4 has frequency
+    base^-1/2, so at pos = pi * sqrt(base) it has turned by pi."""
+    hd, base = 128, 5e5
+    e0 = np.zeros(hd)
+    e0[0] = 1.0
+    r = oracle.rope(e0, 1, hd, 3, base)
+    assert np.count_nonzero(r) == 2 and r[0] == math.cos(3.0) and r[1] == math.sin(3.0)
+    e = np.zeros(hd)
+    e[64] = 1.0  # pair 32 = hd/4
+    p = math.pi * math.sqrt(base)
+    r = oracle.rope(e, 1, hd, int(round(p)), base)
+    ang = round(p) / math.sqrt(base)
+    assert abs(r[64] - math.cos(ang)) < 1e-9 and abs(r[65] - math.sin(ang)) < 1e-9
+    assert r[64] < -0.9999
+
+
+def _f16(a):
+    return np.array([oracle.half_from_double(v) for v in np.ravel(a)], dtype=np.uint16).reshape(np.shape(a))
+
+
+def test_attention_one_position_is_v0():
+    nq, nkv, hd = 4, 2, 128
+    k = synth.normal_f16(synth.key(3, 1), nkv * hd).reshape(1, nkv, hd)
+    v = synth.normal_f16(synth.key(3, 2), nkv * hd).reshape(1, nkv, hd)
+    q = synth.normal_f32(synth.key(3, 3), nq * hd) * 10
+    o = oracle.attention(q, k, v, 1, nq, nkv, hd).reshape(nq, hd)
+    vv = np.array([oracle.half_value(b) for b in v.ravel()]).reshape(nkv, hd)
+    for h in range(nq):  # contiguous groups: heads 0,1 -> kv 0; heads 2,3 -> kv 1
+        assert np.array_equal(o[h], vv[h // 2])
+
+
+def test_attention_identical_keys_is_mean_and_weights_sum_to_one():
+    nq, nkv, hd, n = 2, 1, 128, 9
+    k1 = synth.normal_f16(synth.key(3, 4), hd)
+    kc = np.tile(k1, (n, 1)).reshape(n, 1, hd)
+    vc = synth.normal_f16(synth.key(3, 5), n * hd).reshape(n, 1, hd)
+    q = synth.normal_f32(synth.key(3, 6), nq * hd)
+    o = oracle.attention(q, kc, vc, n, nq, nkv, hd).reshape(nq, hd)
+    vv = np.array([oracle.half_value(b) for b in vc.ravel()]).reshape(n, hd)
+    assert np.allclose(o[0], vv.mean(axis=0), rtol=1e-12, atol=1e-14)
+    ones = np.full((n, 1, hd), 0x3C00, dtype=np.uint16)
+    kc2 = synth.normal_f16(synth.key(3, 7), n * hd).reshape(n, 1, hd)
+    o1 = oracle.attention(q * 3, kc2, ones, n, nq, nkv, hd)
+    assert np.allclose(o1, 1.0, rtol=1e-14)
+
+
+def test_attention_two_positions_closed_form():
+    """q = c e0, k0 = e0, k1 = 0: weight on position 0 is 1 / (1 + exp(-c / sqrt(128)))."""
+    hd, c = 128, 8.0
+    kc = np.zeros((2, 1, hd), dtype=np.uint16)
+    kc[0, 0, 0] = 0x3C00
+    vc = np.zeros((2, 1, hd), dtype=np.uint16)
+    vc[0, 0, 0] = 0x3C00  # v0 = e0, v1 = e1
+    vc[1, 0, 1] = 0x3C00
+    q = np.zeros(hd)
+    q[0] = c
+    o = oracle.attention(q, kc, vc, 2, 1, 1, hd)
+    p0 = 1.0 / (1.0 + math.exp(-c / math.sqrt(128.0)))
+    assert abs(o[0] - p0) < 1e-15 and abs(o[1] - (1 - p0)) < 1e-15
+
+
+def test_silu_special_values():
+    assert oracle.silu(0.0) == 0.0
+    assert oracle.silu(60.0) == 60.0
+    s = oracle.silu(-100.0)
+    assert s == 0.0 or abs(s) < 1e-40
+    z = oracle.silu(-1e6)
+    assert z == 0.0 and math.copysign(1.0, z) == -1.0
+    assert abs(oracle.silu(1.0) - 1.0 / (1.0 + math.exp(-1.0))) < 1e-16
+    g = np.array([0.0, 2.0, -1e6]); u = np.array([5.0, 3.0, 7.0])
+    sw = oracle.swiglu(g, u)
+    assert sw[0] == 0.0 and not np.isnan(sw).any()
+
+
+def test_cosine_special_values():
+    v = synth.normal_f32(synth.key(4, 1), 1000).astype(np.float64)
+    assert abs(oracle.cosine(v, v) - 1.0) < 1e-15
+    assert abs(oracle.cosine(v, -v) + 1.0) < 1e-15
+    assert oracle.cosine(np.array([1.0, 0.0]), np.array([0.0, 3.0])) == 0.0
+    assert oracle.cosine(np.zeros(4), np.ones(4)) == 0.0
+
+
+def test_argmax_lowest_index_on_fp32_ties():
+    assert oracle.argmax_f32(np.array([1.0, 3.0, 3.0, 2.0])) == 1
+    # 1 and 1 + 1e-12 are the same fp32 number: the decision is taken in fp32, lowest index wins
+    assert oracle.argmax_f32(np.array([0.5, 1.0, 1.0 + 1e-12])) == 1
+
+
+def test_half_rounding_through_fp32():
+    h = oracle.half_from_double
+    assert h(1.0) == 0x3C00 and h(65504.0) == 0x7BFF and h(65520.0) == 0x7C00 and h(-70000.0) == 0xFC00
+    assert h(2.0 ** -24) == 0x0001 and h(2.0 ** -25) == 0x0000 and h(3 * 2.0 ** -26) == 0x0001
+    assert h(1 + 2.0 ** -11) == 0x3C00 and h(1 + 3 * 2.0 ** -11) == 0x3C02  # ties to even
+    # 1 + 2^-11 + 2^-40 is 1 + 2^-11 in fp32 (a tie in fp16 -> even), though in fp64 it is above the tie
+    assert h(1 + 2.0 ** -11 + 2.0 ** -40) == 0x3C00
+    for b in (0x0001, 0x03FF, 0x0400, 0x3C00, 0x7BFF, 0x8001, 0xC000):
+        assert h(oracle.half_value(b)) == b
+
+
+# ---------------------------------------------------------------- model-level invariants
+
+def _zero_d(W, qt):
+    """Set every block scale of a canonical matrix to zero (the matrix becomes exactly 0)."""
+    W = W.copy()
+    bb = synth.BLOCK_BYTES[qt]
+    flat = W.reshape(-1, bb)
+    if qt == synth.Q6_K:
+        flat[:, 208:210] = 0
+    elif qt in (synth.Q4_K, synth.Q5_K):
+        flat[:, 0:4] = 0
+    else:
+        flat[:, 0:2] = 0
+    return W
+
+
+def _model_with_identity_layers(wl, layers):
+    om = oracle.OracleModel(wl)
+    for l in layers:
+        for i, t in enumerate(om.TENSORS):
+            if t in (synth.WO, synth.WDOWN):
+                z = _zero_d(wl.weight(l, t), wl.qtype_of(t))
+                om._keep.append(z)
+                om.layers[l].w[i] = z.ctypes.data
+    return om
+
+
+def test_identity_layer_skip_equals_compute():
+    wl = synth.tiny(synth.Q8_0)
+    a = _model_with_identity_layers(wl, [1, 2])
+    r = a.step(wl.first_token(), want_hidden=True)
+    assert np.array_equal(r["hidden"][2], r["hidden"][1]) and np.array_equal(r["hidden"][3], r["hidden"][2])
+    assert abs(r["cos"][1] - 1.0) < 1e-15 and abs(r["cos"][2] - 1.0) < 1e-15 and r["cos"][0] < 0.999
+    b = _model_with_identity_layers(wl, [1, 2])
+    b.skip[:] = [0, 1, 1, 0]
+    r2 = b.step(wl.first_token())
+    assert np.array_equal(r["logits"], r2["logits"])
+
+
+def test_calibration_marks_identity_layers():
+    wl = synth.tiny(synth.Q6_K)
+    m = _model_with_identity_layers(wl, [3])
+    r = m.calibrate_skip(0.98, wl.first_token())
+    assert r["mask"][3] == 1 and m.n_past == wl.n_prior + 1
+
+
+def test_step_writes_kv_only_at_position():
+    wl = synth.tiny(synth.Q4_K)
+    m = oracle.OracleModel(wl)
+    before = [k.copy() for k in m.kc]
+    m.decode(wl.first_token())
+    for l in range(wl.n_layers):
+        changed = np.nonzero(np.any(m.kc[l] != before[l], axis=(1, 2)))[0]
+        assert list(changed) == [wl.n_prior]
+
+
+def test_spec_round_is_lossless_and_accepts_all_when_tail_is_identity():
+    wl = synth.tiny(synth.Q6_K, synth.Q5_K, n_layers=4)
+    draft = 2
+    # tail layers are exact identities: the draft model equals the full model, all k accepted
+    full = _model_with_identity_layers(wl, [2, 3])
+    res = full.spec_round(wl.first_token(), draft, 3)
+    assert res["n_accepted"] == 3 and res["tokens"] == res["drafts"] + [res["verdict"][3]]
+    # greedy decode gives the same tokens (self-speculation never changes the output)
+    ref = _model_with_identity_layers(wl, [2, 3])
+    t, toks = wl.first_token(), []
+    for _ in range(4):
+        t = ref.decode(t)["next"]
+        toks.append(t)
+    assert toks == res["tokens"] and full.n_past == ref.n_past
+
+
+def test_spec_round_rejection_rolls_back():
+    wl = synth.tiny(synth.Q6_K, synth.Q5_K, n_layers=4)
+    m = oracle.OracleModel(wl)
+    ref = oracle.OracleModel(wl)
+    t0 = wl.first_token()
+    res = m.spec_round(t0, 2, 3)
+    a = res["n_accepted"]
+    assert m.n_past == wl.n_prior + a + 1 and len(res["tokens"]) == a + 1
+    t, toks = t0, []
+    for _ in range(a + 1):
+        t = ref.decode(t)["next"]
+        toks.append(t)
+    assert toks == res["tokens"]
