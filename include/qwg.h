@@ -1,0 +1,232 @@
+/*
+ * qwg.h -- C ABI of libqwg.so, the MI355X (gfx950) decode hot path of a
+ * layer-streaming Llama inference engine with block-quantized weights.
+ *
+ * Sources of the operations (the NTransformer pages):
+ *   [NT]   "NTransformer" (socker-news.uzaya.net/news/2026-02-22/article-3):
+ *          "Key results", "Key features", "Quick start", "Architecture overview".
+ *   [HN]   "Show HN: NVMe経由でCPUをバイパスして単一のRTX 3090上で動作するLlama 3.1 70B"
+ *          (hakusoku.com/story/5379): quantization-format table, speed-up techniques,
+ *          3-tier adaptive cache detail.
+ *   [UR]   "RTX 3090 1枚でLlama 70B — NVMe-to-GPU直結でCPUバイパスする革新技術"
+ *          (uravation.com): SLEP streaming pipeline, layer-skip mechanism.
+ *
+ * Conventions (every entry point):
+ *   - Returns int status: QWG_OK (0) or a negative QWG_E_* code; the message of
+ *     the last failure on the calling thread is qwg_last_error().  No C++
+ *     exception crosses this boundary.
+ *   - "d_" pointers are device (HBM) pointers owned by the caller; "h_" pointers
+ *     are host pointers owned by the caller.  Nothing is retained after return
+ *     unless stated.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the legacy default
+ *     stream).  Kernel-level calls are asynchronous on that stream; device-side
+ *     faults surface at the next call that synchronizes.
+ *   - Shapes are validated before any launch: a matrix of qtype T has k a
+ *     multiple of qwg_block_weights(T) (32 or 256), else QWG_E_SHAPE.
+ *   - The packed device layout of a weight matrix is private to the library: it
+ *     is produced by qwg_repack from canonical GGUF block bytes and has the same
+ *     payload bytes (plus < 1 KiB of alignment padding per matrix).
+ *   - A model handle is not thread-safe: one caller at a time.
+ */
+#ifndef QWG_H
+#define QWG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------------------------- */
+#define QWG_OK 0
+#define QWG_E_INVAL (-1)       /* bad pointer, enum value or argument */
+#define QWG_E_SHAPE (-2)       /* dimension not supported or not a multiple of the block */
+#define QWG_E_NOMEM (-3)       /* arena too small, or host allocation failed */
+#define QWG_E_HIP (-4)         /* a HIP runtime call failed (message carries hipGetErrorString) */
+#define QWG_E_STATE (-5)       /* call not valid in the model's current state (unbound, ctx full) */
+#define QWG_E_UNSUPPORTED (-6) /* qtype or mode not implemented */
+
+/* ---- block formats: GGUF type numbers of the formats in the quantization-format table [HN] -- */
+#define QWG_Q4_0 2  /* 32 weights, 18 B: fp16 d, 16 B nibbles; w = d (q - 8) */
+#define QWG_Q8_0 8  /* 32 weights, 34 B: fp16 d, 32 int8; w = d q */
+#define QWG_Q4_K 12 /* 256 weights, 144 B: fp16 d, dmin, 12 B 6-bit scales/mins, 128 B nibbles; w = d sc q - dmin m */
+#define QWG_Q5_K 13 /* 256 weights, 176 B: as Q4_K plus 32 B of fifth bits */
+#define QWG_Q6_K 14 /* 256 weights, 210 B: 128 B low nibbles, 64 B 2-bit highs, 16 int8 scales, fp16 d; w = d sc (q - 32) */
+
+/* ---- tensor ids of a Llama decoder ([NT] "Key features": RoPE, GQA, SwiGLU, RMSNorm, KV cache) */
+#define QWG_T_EMBED 0
+#define QWG_T_HEAD 1
+#define QWG_T_WQ 2
+#define QWG_T_WK 3
+#define QWG_T_WV 4
+#define QWG_T_WO 5
+#define QWG_T_WGATE 6
+#define QWG_T_WUP 7
+#define QWG_T_WDOWN 8
+#define QWG_NORM_ATTN 9
+#define QWG_NORM_FFN 10
+#define QWG_NORM_FINAL 11
+
+/* Message of the last failed call on this thread ("" if none). Valid until the next failing call. */
+const char* qwg_last_error(void);
+/* ABI version of this header (major * 100 + minor). */
+int qwg_version(void);
+
+/* ---- sizes of the canonical formats -------------------------------------------------------- */
+/* Bytes of one canonical block, weights per block ([HN] quantization-format table); 0 if unknown. */
+size_t qwg_block_bytes(int qtype);
+int qwg_block_weights(int qtype);
+/* Canonical bytes of one row of k weights; 0 if k is not a multiple of the block. */
+size_t qwg_row_bytes(int qtype, int64_t k);
+/* Device bytes of the packed layout of a rows x k matrix (*out); QWG_E_SHAPE on a bad shape. */
+int qwg_packed_bytes(int qtype, int64_t rows, int64_t k, size_t* out);
+
+/* ---- kernel-level entry points (caller-owned device memory, caller's stream) ------------ */
+
+/* Rearrange canonical row-major blocks (d_canon: rows x qwg_row_bytes) into the packed layout
+ * (d_packed: qwg_packed_bytes).  Pure byte movement; the buffers must not overlap. */
+int qwg_repack(int qtype, const void* d_canon, int64_t rows, int64_t k, void* d_packed, void* stream);
+
+/* Dequantize a packed matrix into fp32 d_out[rows][k].  Each weight is the fp32 nearest to its
+ * exact value (fp16 subnormal scales honoured), i.e. bit-identical to a correctly rounded decode. */
+int qwg_dequantize(int qtype, const void* d_packed, int64_t rows, int64_t k, float* d_out, void* stream);
+
+/* Fused dequantize-and-GEMV, the engine's hand-written GEMV kernels ([NT] "Architecture overview",
+ * cuda/: GEMV; [NT] "Key features": no cuBLAS): d_y[j][r] = sum_c W[r][c] d_x[j][c] for
+ * j < n_cols, with W decoded from the packed blocks in registers and never written out.
+ * d_x is fp32 [n_cols][k], d_y fp32 [n_cols][rows]; 1 <= n_cols <= 8; k <= 65536.
+ * n_cols > 1 is the multi-column form used to verify self-speculative drafts ([NT] "Key features"). */
+int qwg_gemv(int qtype, const void* d_packed, int64_t rows, int64_t k, const float* d_x, int n_cols, float* d_y,
+             void* stream);
+
+/* RMSNorm ([NT] "Key features"; cuda/ RMSNorm kernel): d_out[j][i] = g[i] x[j][i] / sqrt(mean_i x[j]^2 + eps),
+ * for j < n_cols; x, out fp32 [n_cols][n]; n <= 65536. */
+int qwg_rmsnorm(const float* d_x, const float* d_g, int64_t n, float eps, int n_cols, float* d_out, void* stream);
+
+/* Host: rotary table h_table[p][i] = (cos(p theta_i), sin(p theta_i)) as fp32 pairs, computed in fp64,
+ * theta_i = base^(-2i/head_dim), p < max_pos, i < head_dim/2.  h_table holds max_pos*head_dim floats. */
+int qwg_rope_table(int max_pos, int head_dim, double base, float* h_table);
+
+/* RoPE ([NT] "Key features"; cuda/ RoPE kernel) in place on d_v [n_heads][head_dim] at position pos:
+ * adjacent pairs (2i, 2i+1) rotate by angle pos*theta_i, read from a device copy of the table above. */
+int qwg_rope(float* d_v, int n_heads, int head_dim, const float* d_table, int pos, void* stream);
+
+/* Grouped-query decode attention over an fp16 KV cache ([NT] "Key features": GQA, KV cache; cuda/ softmax).
+ * d_q fp32 [n_cols][n_q][head_dim]; d_kc, d_vc fp16 bits [>= n_pos + n_cols - 1][n_kv][head_dim];
+ * column j attends to positions 0 .. n_pos - 1 + j (causal), query head h uses kv head h / (n_q / n_kv);
+ * scores q.k / sqrt(head_dim), softmax, weighted sum of V.  d_out fp32 [n_cols][n_q][head_dim].
+ * d_work: device scratch of qwg_attn_work_bytes(...) bytes.  head_dim must be 128; n_cols <= 8. */
+size_t qwg_attn_work_bytes(int n_pos, int n_q, int n_kv, int head_dim, int n_cols);
+int qwg_attn_decode(const float* d_q, const uint16_t* d_kc, const uint16_t* d_vc, int n_pos, int n_q, int n_kv,
+                    int head_dim, int n_cols, float* d_out, void* d_work, size_t work_bytes, void* stream);
+
+/* SwiGLU ([NT] "Key features"; cuda/ SwiGLU kernel): d_out[i] = silu(g[i]) u[i], silu(z) = z / (1 + e^-z). */
+int qwg_swiglu(const float* d_g, const float* d_u, int64_t n, float* d_out, void* stream);
+
+/* Cosine similarity of the layer-skip test ([NT] "Key results"; [UR] layer-skip mechanism):
+ * *d_out = <a,b> / (|a| |b|) in fp32 (0 if either vector is zero). */
+int qwg_cosine(const float* d_a, const float* d_b, int64_t n, float* d_out, void* stream);
+
+/* Greedy sampler ([NT] "Architecture overview", inference/ sampler): *d_out = index of the largest
+ * element of d_x[n] (fp32), lowest index on ties, NaNs ignored. */
+int qwg_argmax(const float* d_x, int64_t n, int32_t* d_out, void* stream);
+
+/* ---- model: a Llama decoder held in HBM, optionally with layers streamed from pinned RAM ---- */
+
+typedef struct qwg_model qwg_model;
+
+typedef struct {
+  int32_t n_layers, hidden, n_q, n_kv, head_dim, ffn, vocab;
+  int32_t max_ctx;    /* KV cache rows per layer (positions 0 .. max_ctx-1) */
+  float rope_theta;   /* RoPE base */
+  float rms_eps;      /* RMSNorm epsilon */
+  int32_t n_resident; /* layers [0, n_resident) live in HBM; the rest stream from pinned host RAM
+                         through two HBM slots ([HN] 3-tier cache: tier A resident, tier B pinned RAM;
+                         [UR] SLEP double buffering).  -1 = all resident. */
+  int32_t qtype_attn; /* WQ, WK, WV, WO */
+  int32_t qtype_ffn;  /* WGATE, WUP, WDOWN */
+  int32_t qtype_embed;
+  int32_t qtype_head;
+  int32_t max_cols;   /* widest multi-column pass (1 + draft k), 1..8 */
+} qwg_model_desc;
+
+/* Validate the description and create an unbound model (no device memory yet). */
+int qwg_model_create(const qwg_model_desc* desc, qwg_model** out);
+/* Device bytes the caller must provide to qwg_model_bind (weights of resident layers, two
+ * streaming slots if any layer streams, KV caches, activations and scratch). */
+size_t qwg_model_arena_bytes(const qwg_model* m);
+/* Bind caller-owned device memory (>= qwg_model_arena_bytes, 256-B aligned) and the streams:
+ * `compute` runs every kernel, `copy` carries host-to-device layer copies (may equal compute).
+ * Streamed layers get library-owned pinned host images here. */
+int qwg_model_bind(qwg_model* m, void* d_arena, size_t bytes, void* compute, void* copy);
+/* Synchronize and free everything the library owns (never the caller's arena). NULL is a no-op. */
+void qwg_model_destroy(qwg_model* m);
+
+/* Load one weight matrix from canonical host bytes (h_canon: rows x qwg_row_bytes).  layer = -1 for
+ * EMBED and HEAD.  WQ/WK/WV are stored as one fused matrix and WGATE/WUP with interleaved rows; the
+ * caller may free h_canon on return.  qtype must equal the description's type for that tensor. */
+int qwg_model_set_tensor(qwg_model* m, int layer, int tensor_id, int qtype, const void* h_canon, size_t nbytes);
+/* RMSNorm gains (fp32 [hidden]); which = QWG_NORM_ATTN / QWG_NORM_FFN (layer >= 0) or QWG_NORM_FINAL. */
+int qwg_model_set_norm(qwg_model* m, int layer, int which, const float* h_g, int n);
+/* Write KV rows 0..n_pos-1 of a layer (fp16 bits [n_pos][n_kv][head_dim], already rotated) and set
+ * the number of cached positions of the model to n_pos. */
+int qwg_model_set_kv(qwg_model* m, int layer, const uint16_t* h_k, const uint16_t* h_v, int n_pos);
+/* Read back KV rows 0..n_pos-1 of a layer (synchronizes). */
+int qwg_model_get_kv(qwg_model* m, int layer, uint16_t* h_k, uint16_t* h_v, int n_pos);
+
+/* One greedy decode step ([NT] "Quick start": resident and streaming modes): the token goes at
+ * position n_past; every non-skipped layer runs (RMSNorm, fused QKV GEMV with RoPE and KV append,
+ * attention, Wo GEMV + residual, RMSNorm, gate|up GEMV with SwiGLU, down GEMV + residual), then the
+ * final RMSNorm, head GEMV and argmax.  Streamed layers are double-buffered through two HBM slots,
+ * copying layer l+1 while layer l computes ([UR] SLEP streaming pipeline).  n_past advances by one.
+ * h_logits (optional) receives the fp32 logits [vocab]. Synchronizes. */
+int qwg_decode_step(qwg_model* m, int32_t token, int32_t* next_token, float* h_logits);
+
+/* Layer-skip calibration ([NT] "Key results"/"Key features"; [UR] layer-skip mechanism): one decode
+ * step with every layer computed that records c_l = cos(h_in, h_out) per layer (h_cos, fp32
+ * [n_layers], optional) and sets skip[l] = (c_l >= tau) (h_mask, optional).  Skipped layers then do no
+ * work and no copy in later steps and write no KV.  Returns the step's token in *next_token. */
+int qwg_calibrate_skip(qwg_model* m, float tau, int32_t token, int32_t* next_token, float* h_cos, uint8_t* h_mask);
+int qwg_set_layer_skip(qwg_model* m, int layer, int skip);
+int qwg_get_layer_skip(qwg_model* m, uint8_t* h_mask);
+
+/* Self-speculative round ([NT] "Key features"; [HN] speed-up techniques; [NT] "Quick start"
+ * --self-spec --draft-k): draft k tokens greedily with layers [0, draft_layers) + final norm + head,
+ * verify the k+1 tokens [token, d1..dk] in one k+1-column pass through all layers, accept the longest
+ * prefix of drafts that matches the verifier's argmax, emit accepted drafts plus one verifier token
+ * (out_tokens[0 .. *n_out-1], *n_out = *n_accepted + 1) and roll the KV length back to
+ * n_past + *n_out.  1 <= k, k + 1 <= max_cols. */
+int qwg_spec_step(qwg_model* m, int32_t token, int draft_layers, int k, int32_t* out_tokens, int* n_out,
+                  int* n_accepted);
+/* The verify pass alone: tokens[0..n-1] at positions n_past .. n_past+n-1 through all layers;
+ * h_logits fp32 [n][vocab] (optional), h_argmax [n] (optional).  n_past is left unchanged (the
+ * KV rows written stay beyond it). */
+int qwg_verify(qwg_model* m, const int32_t* tokens, int n, float* h_logits, int32_t* h_argmax);
+
+int qwg_model_n_past(const qwg_model* m);
+/* Set the number of cached positions (only shrink, or grow up to the rows written). */
+int qwg_model_truncate(qwg_model* m, int n_past);
+/* Keep the residual stream after every layer of the next steps (for parity checks). */
+int qwg_model_set_capture(qwg_model* m, int on);
+/* Residual stream captured in the last step: layer = -1 after the embedding, l after layer l;
+ * h_out fp32 [hidden] (column 0). Synchronizes. */
+int qwg_model_get_hidden(qwg_model* m, int layer, float* h_out);
+/* Time the kernels of one weight class over the next steps with HIP events on the compute stream
+ * (tensor_id QWG_T_WQ = fused QKV, WO, WGATE = fused gate|up, WDOWN, HEAD; -1 = off). */
+int qwg_model_set_timing(qwg_model* m, int tensor_id);
+/* Sum of the timed kernels' durations (ms), their count and algorithmic bytes per launch. */
+int qwg_model_get_timing(qwg_model* m, double* total_ms, int64_t* n_launches, int64_t* bytes_per_launch);
+/* Bytes copied host-to-device for streamed layers in the last step, and the copy-stream time (ms). */
+int qwg_model_stream_stats(qwg_model* m, int64_t* h2d_bytes, double* h2d_ms);
+int qwg_sync(qwg_model* m);
+
+/* Pinned host memory (hipHostMalloc) for callers that stage weights. */
+int qwg_host_alloc(size_t bytes, void** out);
+int qwg_host_free(void* p);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QWG_H */

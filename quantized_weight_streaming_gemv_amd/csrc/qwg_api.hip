@@ -1,0 +1,873 @@
+// qwg_api.hip -- host runtime behind the C ABI of include/qwg.h.
+//
+// Model placement follows the pages' tiers, re-sized for one MI355X: the NTransformer pages keep
+// as many layers as fit in VRAM resident (tier A) and move the rest from pinned host RAM with
+// double-buffered copies (tier B; "3-tier adaptive cache" and the SLEP streaming pipeline on the
+// Show HN page and the RTX 3090 article).  With 288 GB of HBM a 70B model at these bit widths is
+// fully resident, so residency is the primary mode; streaming is kept for layers >= n_resident.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <stdexcept>
+#include <string>
+#include <vector>
+
+#include "../../include/qwg.h"
+#include "qwg_kernels.h"
+
+using namespace qwg;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+#define QWG_HIP(expr)                                                                                \
+  do {                                                                                               \
+    hipError_t e_ = (expr);                                                                          \
+    if (e_ != hipSuccess) return fail(QWG_E_HIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+// No C++ exception crosses the ABI: every entry point that allocates runs inside guarded().
+template <class Fn>
+int guarded(Fn&& fn) {
+  try {
+    return fn();
+  } catch (const std::bad_alloc&) {
+    return fail(QWG_E_NOMEM, "host allocation failed");
+  } catch (const std::exception& ex) {
+    return fail(QWG_E_INVAL, std::string("exception: ") + ex.what());
+  } catch (...) {
+    return fail(QWG_E_INVAL, "unknown exception");
+  }
+}
+
+int64_t canon_row_bytes(int qt, int64_t k) {
+  if (!qtype_known(qt) || k <= 0 || k % block_weights(qt)) return 0;
+  return k / block_weights(qt) * block_bytes(qt);
+}
+
+size_t align_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
+
+// split workspace for the kernel-level qwg_gemv (cached per device; freed at exit)
+struct KernelWorkspace {
+  void* p[64] = {};
+  size_t n[64] = {};
+  ~KernelWorkspace() {
+    for (int i = 0; i < 64; ++i)
+      if (p[i]) (void)hipFree(p[i]);
+  }
+} g_ws;
+
+hipError_t kernel_workspace(size_t bytes, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (g_ws.n[dev] < bytes) {
+    if (g_ws.p[dev]) {
+      e = hipDeviceSynchronize();
+      if (e != hipSuccess) return e;
+      (void)hipFree(g_ws.p[dev]);
+      g_ws.p[dev] = nullptr;
+      g_ws.n[dev] = 0;
+    }
+    e = hipMalloc(&g_ws.p[dev], bytes);
+    if (e != hipSuccess) return e;
+    g_ws.n[dev] = bytes;
+  }
+  *out = g_ws.p[dev];
+  return hipSuccess;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+}  // namespace
+
+// ===================================================================================== model
+
+struct MatPlan {
+  Layout L;
+  size_t off;  // from the layer image base (layer matrices) or the arena base (embed, head)
+  int64_t canon_bytes;
+};
+
+struct LayerPlan {
+  MatPlan qkv, o, gu, down;
+  size_t image;       // bytes of the packed layer image (qkv | o | gu | down)
+  bool resident;
+  size_t arena_off;   // resident image in the arena
+  uint8_t* host;      // streamed image in pinned host memory
+  size_t g_attn, g_ffn, kc, vc;
+};
+
+struct qwg_model {
+  qwg_model_desc d{};
+  std::vector<LayerPlan> L;
+  MatPlan embed{}, head{};
+  size_t g_final = 0, rope = 0, h = 0, hin = 0, qb = 0, ob = 0, act = 0, logits = 0, amax = 0, cosv = 0;
+  size_t capture = 0, part = 0, attn = 0, slot[2] = {0, 0}, staging = 0;
+  size_t part_bytes = 0, attn_bytes = 0, staging_bytes = 0, image_max = 0, total = 0;
+  int n_streamed = 0;
+  uint8_t* arena = nullptr;
+  hipStream_t cs = nullptr, xs = nullptr;
+  hipEvent_t ev_full[2] = {}, ev_free[2] = {};
+  bool bound = false;
+  int n_past = 0;
+  std::vector<uint8_t> skip;
+  bool capture_on = false;
+  // kernel timing of one weight class
+  int timing_tensor = -1;
+  std::vector<hipEvent_t> tev;
+  int tev_used = 0;
+  double t_ms = 0.0;
+  int64_t t_n = 0, t_bytes = 0;
+  // host-to-device copy timing
+  std::vector<hipEvent_t> cev;
+  int cev_used = 0;
+  int64_t h2d_bytes = 0;
+  double h2d_ms = 0.0;
+
+  int H() const { return d.hidden; }
+  int QR() const { return d.n_q * d.head_dim; }
+  int KR() const { return d.n_kv * d.head_dim; }
+  float* f(size_t off) const { return (float*)(arena + off); }
+};
+
+static MatPlan mat_plan(int qt, int64_t rows, int64_t k, size_t& cursor) {
+  MatPlan p;
+  p.L = make_layout(qt, rows, k);
+  p.off = cursor;
+  p.canon_bytes = rows * canon_row_bytes(qt, k);
+  cursor = align_up(cursor + (size_t)p.L.total);
+  return p;
+}
+
+static int plan_model(qwg_model* m) {
+  const qwg_model_desc& d = m->d;
+  const int H = d.hidden, F = d.ffn, V = d.vocab, C = d.max_cols;
+  const int n_res = d.n_resident < 0 ? d.n_layers : d.n_resident;
+  size_t cur = 0;
+  m->L.assign(d.n_layers, LayerPlan{});
+  // image layout shared by every layer
+  size_t ic = 0;
+  LayerPlan proto{};
+  proto.qkv = mat_plan(d.qtype_attn, (int64_t)(d.n_q + 2 * d.n_kv) * d.head_dim, H, ic);
+  proto.o = mat_plan(d.qtype_attn, H, (int64_t)d.n_q * d.head_dim, ic);
+  proto.gu = mat_plan(d.qtype_ffn, 2 * (int64_t)F, H, ic);
+  proto.down = mat_plan(d.qtype_ffn, H, F, ic);
+  proto.image = ic;
+  m->image_max = ic;
+  m->n_streamed = 0;
+  for (int l = 0; l < d.n_layers; ++l) {
+    LayerPlan& P = m->L[l];
+    P = proto;
+    P.resident = l < n_res;
+    P.host = nullptr;
+    if (P.resident) {
+      P.arena_off = cur;
+      cur = align_up(cur + P.image);
+    } else {
+      ++m->n_streamed;
+    }
+  }
+  m->embed = mat_plan(d.qtype_embed, V, H, cur);
+  m->head = mat_plan(d.qtype_head, V, H, cur);
+  auto take = [&](size_t bytes) {
+    size_t o = cur;
+    cur = align_up(cur + bytes);
+    return o;
+  };
+  const size_t kv_bytes = (size_t)d.max_ctx * d.n_kv * d.head_dim * 2;
+  for (int l = 0; l < d.n_layers; ++l) {
+    m->L[l].g_attn = take((size_t)H * 4);
+    m->L[l].g_ffn = take((size_t)H * 4);
+    m->L[l].kc = take(kv_bytes);
+    m->L[l].vc = take(kv_bytes);
+  }
+  m->g_final = take((size_t)H * 4);
+  m->rope = take((size_t)d.max_ctx * d.head_dim * 4);
+  m->h = take((size_t)C * H * 4);
+  m->hin = take((size_t)H * 4);
+  m->qb = take((size_t)C * m->QR() * 4);
+  m->ob = take((size_t)C * m->QR() * 4);
+  m->act = take((size_t)C * F * 4);
+  m->logits = take((size_t)C * V * 4);
+  m->amax = take((size_t)C * 4);
+  m->cosv = take((size_t)d.n_layers * 4);
+  m->capture = take((size_t)(d.n_layers + 1) * H * 4);
+  size_t pb = 0;
+  for (int nc : {1, C}) {
+    const int64_t shapes[5][2] = {{(int64_t)(d.n_q + 2 * d.n_kv) * d.head_dim, H},
+                                  {H, (int64_t)d.n_q * d.head_dim},
+                                  {2 * (int64_t)F, H},
+                                  {H, F},
+                                  {V, H}};
+    const int qts[5] = {d.qtype_attn, d.qtype_attn, d.qtype_ffn, d.qtype_ffn, d.qtype_head};
+    for (int i = 0; i < 5; ++i) {
+      const GemvPlan gp = plan_gemv(qts[i], shapes[i][0], shapes[i][1], nc);
+      pb = std::max(pb, gp.part_bytes);
+    }
+  }
+  m->part_bytes = pb;
+  m->part = take(pb > 0 ? pb : 256);
+  m->attn_bytes = plan_attn(d.max_ctx, d.n_q, d.n_kv, C).work_bytes;
+  m->attn = take(m->attn_bytes);
+  if (m->n_streamed > 0) {
+    m->slot[0] = take(m->image_max);
+    m->slot[1] = take(m->image_max);
+  }
+  m->staging_bytes = 64u << 20;
+  m->staging = take(m->staging_bytes);
+  m->total = cur;
+  return QWG_OK;
+}
+
+static int check_desc(const qwg_model_desc* d) {
+  if (!d) return fail(QWG_E_INVAL, "desc is NULL");
+  if (d->n_layers < 1 || d->hidden < 1 || d->n_q < 1 || d->n_kv < 1 || d->ffn < 1 || d->vocab < 1 || d->max_ctx < 1)
+    return fail(QWG_E_SHAPE, "model dimensions must be positive");
+  if (d->head_dim != HEAD_DIM) return fail(QWG_E_SHAPE, "head_dim must be 128");
+  if (d->n_q % d->n_kv) return fail(QWG_E_SHAPE, "n_q must be a multiple of n_kv");
+  if (d->max_cols < 1 || d->max_cols > MAX_COLS) return fail(QWG_E_SHAPE, "max_cols must be in 1..8");
+  if (d->n_q / d->n_kv * d->max_cols > 64) return fail(QWG_E_SHAPE, "(n_q / n_kv) * max_cols must be <= 64");
+  const int qts[4] = {d->qtype_attn, d->qtype_ffn, d->qtype_embed, d->qtype_head};
+  for (int q : qts)
+    if (!qtype_known(q)) return fail(QWG_E_UNSUPPORTED, "unknown qtype " + std::to_string(q));
+  const int64_t H = d->hidden, F = d->ffn, QR = (int64_t)d->n_q * d->head_dim;
+  if (canon_row_bytes(d->qtype_attn, H) == 0 || canon_row_bytes(d->qtype_attn, QR) == 0 ||
+      canon_row_bytes(d->qtype_ffn, H) == 0 || canon_row_bytes(d->qtype_ffn, F) == 0 ||
+      canon_row_bytes(d->qtype_embed, H) == 0 || canon_row_bytes(d->qtype_head, H) == 0)
+    return fail(QWG_E_SHAPE, "hidden, ffn and n_q*head_dim must be multiples of the block size");
+  if (H > 65536 || F > 65536 || QR > 65536) return fail(QWG_E_SHAPE, "K dimensions above 65536 are not supported");
+  if (d->n_resident < -1 || d->n_resident > d->n_layers) return fail(QWG_E_SHAPE, "bad n_resident");
+  return QWG_OK;
+}
+
+static MatView view_at(const uint8_t* base, const MatPlan& p) { return make_view(base + p.off, p.L); }
+
+// ---------------------------------------------------------------------------- timing helpers
+
+static hipEvent_t pool_event(std::vector<hipEvent_t>& pool, int& used) {
+  if (used == (int)pool.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    pool.push_back(e);
+  }
+  return pool[used++];
+}
+
+static int collect_timing(qwg_model* m) {
+  for (int i = 0; i + 1 < m->tev_used; i += 2) {
+    float ms = 0.f;
+    QWG_HIP(hipEventElapsedTime(&ms, m->tev[i], m->tev[i + 1]));
+    m->t_ms += ms;
+    m->t_n += 1;
+  }
+  m->tev_used = 0;
+  for (int i = 0; i + 1 < m->cev_used; i += 2) {
+    float ms = 0.f;
+    QWG_HIP(hipEventElapsedTime(&ms, m->cev[i], m->cev[i + 1]));
+    m->h2d_ms += ms;
+  }
+  m->cev_used = 0;
+  return QWG_OK;
+}
+
+// ---------------------------------------------------------------------------- one pass
+
+static int64_t gemv_alg_bytes(const MatPlan& p, int nc, int out_rw) {
+  return p.canon_bytes + (int64_t)nc * p.L.k * 4 + (int64_t)nc * p.L.rows * 4 * out_rw;
+}
+
+static int gemv(qwg_model* m, int tensor_class, int qt, const MatView& w, const MatPlan& mp, const float* x,
+                int64_t x_stride, const float* gain, bool rms, int nc, int epi, const EpiArgs& e) {
+  const GemvPlan gp = plan_gemv(qt, w.rows, mp.L.k, nc);
+  if (gp.part_bytes > m->part_bytes) return fail(QWG_E_NOMEM, "split workspace too small");
+  const bool timed = m->timing_tensor == tensor_class;
+  if (timed) {
+    hipEvent_t e0 = pool_event(m->tev, m->tev_used);
+    if (!e0) return fail(QWG_E_HIP, "hipEventCreate failed");
+    QWG_HIP(hipEventRecord(e0, m->cs));
+  }
+  QWG_HIP(launch_gemv(qt, w, mp.L.k, x, x_stride, gain, m->d.rms_eps, rms, nc, epi, e, m->f(m->part), m->cs, gp));
+  if (timed) {
+    hipEvent_t e1 = pool_event(m->tev, m->tev_used);
+    if (!e1) return fail(QWG_E_HIP, "hipEventCreate failed");
+    QWG_HIP(hipEventRecord(e1, m->cs));
+    const int rw = epi == EPI_RESID ? 2 : 1;
+    m->t_bytes = gemv_alg_bytes(mp, nc, epi == EPI_SWIGLU ? 0 : rw) + (epi == EPI_SWIGLU ? (int64_t)nc * mp.L.rows / 2 * 4 : 0);
+  }
+  return QWG_OK;
+}
+
+static int layer_kernels(qwg_model* m, int l, const uint8_t* base, int nc, int pos) {
+  const qwg_model_desc& d = m->d;
+  const LayerPlan& P = m->L[l];
+  const int H = d.hidden, F = d.ffn, QR = m->QR(), KR = m->KR();
+  int rc;
+  EpiArgs e{};
+  e.y = m->f(m->qb);
+  e.y_stride = QR;
+  e.rope = m->f(m->rope);
+  e.pos = pos;
+  e.nq_rows = QR;
+  e.nkv_rows = KR;
+  e.kc = (uint16_t*)(m->arena + P.kc);
+  e.vc = (uint16_t*)(m->arena + P.vc);
+  e.kv_stride = KR;
+  if ((rc = gemv(m, QWG_T_WQ, d.qtype_attn, view_at(base, P.qkv), P.qkv, m->f(m->h), H, m->f(P.g_attn), true, nc,
+                 EPI_QKV, e)))
+    return rc;
+  const AttnPlan ap = plan_attn(pos + 1, d.n_q, d.n_kv, nc);
+  if (ap.work_bytes > m->attn_bytes) return fail(QWG_E_NOMEM, "attention workspace too small");
+  QWG_HIP(launch_attn(m->f(m->qb), QR, e.kc, e.vc, KR, pos + 1, d.n_q, d.n_kv, nc, m->f(m->ob), QR,
+                      m->arena + m->attn, ap, m->cs));
+  EpiArgs r{};
+  r.y = m->f(m->h);
+  r.y_stride = H;
+  if ((rc = gemv(m, QWG_T_WO, d.qtype_attn, view_at(base, P.o), P.o, m->f(m->ob), QR, nullptr, false, nc, EPI_RESID,
+                 r)))
+    return rc;
+  EpiArgs s{};
+  s.y = m->f(m->act);
+  s.y_stride = F;
+  if ((rc = gemv(m, QWG_T_WGATE, d.qtype_ffn, view_at(base, P.gu), P.gu, m->f(m->h), H, m->f(P.g_ffn), true, nc,
+                 EPI_SWIGLU, s)))
+    return rc;
+  if ((rc = gemv(m, QWG_T_WDOWN, d.qtype_ffn, view_at(base, P.down), P.down, m->f(m->act), F, nullptr, false, nc,
+                 EPI_RESID, r)))
+    return rc;
+  return QWG_OK;
+}
+
+static int issue_copy(qwg_model* m, const std::vector<int>& sl, int j) {
+  const int slot = j & 1;
+  const LayerPlan& P = m->L[sl[j]];
+  QWG_HIP(hipStreamWaitEvent(m->xs, m->ev_free[slot], 0));
+  hipEvent_t c0 = pool_event(m->cev, m->cev_used);
+  hipEvent_t c1 = pool_event(m->cev, m->cev_used);
+  if (!c0 || !c1) return fail(QWG_E_HIP, "hipEventCreate failed");
+  QWG_HIP(hipEventRecord(c0, m->xs));
+  QWG_HIP(hipMemcpyAsync(m->arena + m->slot[slot], P.host, P.image, hipMemcpyHostToDevice, m->xs));
+  QWG_HIP(hipEventRecord(c1, m->xs));
+  QWG_HIP(hipEventRecord(m->ev_full[slot], m->xs));
+  m->h2d_bytes += (int64_t)P.image;
+  return QWG_OK;
+}
+
+// Embedding, layers [0, n_run) (skipped layers bypassed unless calibrating), final norm, head, argmax.
+static int run_pass(qwg_model* m, const int32_t* toks, int nc, int pos, int n_run, bool calib) {
+  const qwg_model_desc& d = m->d;
+  const int H = d.hidden;
+  if (!m->bound) return fail(QWG_E_STATE, "model is not bound");
+  if (nc < 1 || nc > d.max_cols) return fail(QWG_E_SHAPE, "column count outside 1..max_cols");
+  if (pos < 0 || pos + nc > d.max_ctx) return fail(QWG_E_STATE, "context full (n_past + columns > max_ctx)");
+  for (int i = 0; i < nc; ++i)
+    if (toks[i] < 0 || toks[i] >= d.vocab) return fail(QWG_E_INVAL, "token id out of range");
+  QWG_HIP(launch_embed(d.qtype_embed, view_at(m->arena, m->embed), H, toks, nc, m->f(m->h), H, m->cs));
+  if (m->capture_on) QWG_HIP(hipMemcpyAsync(m->f(m->capture), m->f(m->h), (size_t)H * 4, hipMemcpyDeviceToDevice, m->cs));
+  std::vector<int> sl;
+  for (int l = 0; l < n_run; ++l)
+    if (!m->L[l].resident && (calib || !m->skip[l])) sl.push_back(l);
+  for (int j = 0; j < (int)sl.size() && j < 2; ++j)
+    if (int rc = issue_copy(m, sl, j)) return rc;
+  int sj = 0;
+  for (int l = 0; l < n_run; ++l) {
+    const bool run = calib || !m->skip[l];
+    if (run) {
+      const LayerPlan& P = m->L[l];
+      const uint8_t* base;
+      int slot = 0;
+      if (P.resident) {
+        base = m->arena + P.arena_off;
+      } else {
+        slot = sj & 1;
+        QWG_HIP(hipStreamWaitEvent(m->cs, m->ev_full[slot], 0));
+        base = m->arena + m->slot[slot];
+      }
+      if (calib) QWG_HIP(hipMemcpyAsync(m->f(m->hin), m->f(m->h), (size_t)H * 4, hipMemcpyDeviceToDevice, m->cs));
+      if (int rc = layer_kernels(m, l, base, nc, pos)) return rc;
+      if (!P.resident) {
+        QWG_HIP(hipEventRecord(m->ev_free[slot], m->cs));
+        if (sj + 2 < (int)sl.size())
+          if (int rc = issue_copy(m, sl, sj + 2)) return rc;
+        ++sj;
+      }
+      if (calib) QWG_HIP(launch_cosine(m->f(m->hin), m->f(m->h), H, m->f(m->cosv) + l, m->cs));
+    }
+    if (m->capture_on)
+      QWG_HIP(hipMemcpyAsync(m->f(m->capture) + (size_t)(l + 1) * H, m->f(m->h), (size_t)H * 4,
+                             hipMemcpyDeviceToDevice, m->cs));
+  }
+  for (int l = n_run; l < d.n_layers && m->capture_on; ++l)
+    QWG_HIP(hipMemcpyAsync(m->f(m->capture) + (size_t)(l + 1) * H, m->f(m->h), (size_t)H * 4,
+                           hipMemcpyDeviceToDevice, m->cs));
+  EpiArgs e{};
+  e.y = m->f(m->logits);
+  e.y_stride = d.vocab;
+  if (int rc = gemv(m, QWG_T_HEAD, d.qtype_head, view_at(m->arena, m->head), m->head, m->f(m->h), H, m->f(m->g_final),
+                    true, nc, EPI_STORE, e))
+    return rc;
+  QWG_HIP(launch_argmax(m->f(m->logits), d.vocab, nc, d.vocab, (int32_t*)(m->arena + m->amax), m->cs));
+  return QWG_OK;
+}
+
+static int finish_pass(qwg_model* m, int nc, int32_t* h_amax, float* h_logits) {
+  QWG_HIP(hipStreamSynchronize(m->cs));
+  QWG_HIP(hipStreamSynchronize(m->xs));
+  if (h_amax) QWG_HIP(hipMemcpy(h_amax, m->arena + m->amax, (size_t)nc * 4, hipMemcpyDeviceToHost));
+  if (h_logits)
+    QWG_HIP(hipMemcpy(h_logits, m->f(m->logits), (size_t)nc * m->d.vocab * 4, hipMemcpyDeviceToHost));
+  return collect_timing(m);
+}
+
+// ===================================================================================== C ABI
+
+extern "C" {
+
+const char* qwg_last_error(void) { return g_err.c_str(); }
+int qwg_version(void) { return 100; }
+
+size_t qwg_block_bytes(int qtype) { return qtype_known(qtype) ? (size_t)block_bytes(qtype) : 0; }
+int qwg_block_weights(int qtype) { return qtype_known(qtype) ? block_weights(qtype) : 0; }
+size_t qwg_row_bytes(int qtype, int64_t k) { return (size_t)canon_row_bytes(qtype, k); }
+
+int qwg_packed_bytes(int qtype, int64_t rows, int64_t k, size_t* out) {
+  if (!out) return fail(QWG_E_INVAL, "out is NULL");
+  if (!qtype_known(qtype)) return fail(QWG_E_UNSUPPORTED, "unknown qtype");
+  if (rows < 0 || canon_row_bytes(qtype, k) == 0) return fail(QWG_E_SHAPE, "k must be a positive multiple of the block");
+  *out = (size_t)make_layout(qtype, rows, k).total;
+  return QWG_OK;
+}
+
+static int check_matrix(int qtype, int64_t rows, int64_t k) {
+  if (!qtype_known(qtype)) return fail(QWG_E_UNSUPPORTED, "unknown qtype " + std::to_string(qtype));
+  if (rows < 0 || rows > (int64_t)1 << 30) return fail(QWG_E_SHAPE, "rows out of range");
+  if (canon_row_bytes(qtype, k) == 0) return fail(QWG_E_SHAPE, "k must be a positive multiple of the block");
+  if (k > 65536) return fail(QWG_E_SHAPE, "k above 65536");
+  return QWG_OK;
+}
+
+int qwg_repack(int qtype, const void* d_canon, int64_t rows, int64_t k, void* d_packed, void* stream) {
+  if (int rc = check_matrix(qtype, rows, k)) return rc;
+  if ((!d_canon || !d_packed) && rows > 0) return fail(QWG_E_INVAL, "NULL pointer");
+  const Layout L = make_layout(qtype, rows, k);
+  QWG_HIP(launch_repack(qtype, (const uint8_t*)d_canon, rows, k, (uint8_t*)d_packed, L, 0, 1, (hipStream_t)stream));
+  return QWG_OK;
+}
+
+int qwg_dequantize(int qtype, const void* d_packed, int64_t rows, int64_t k, float* d_out, void* stream) {
+  if (int rc = check_matrix(qtype, rows, k)) return rc;
+  if ((!d_packed || !d_out) && rows > 0) return fail(QWG_E_INVAL, "NULL pointer");
+  if (!aligned16(d_packed) || !aligned16(d_out)) return fail(QWG_E_INVAL, "pointers must be 16-byte aligned");
+  const Layout L = make_layout(qtype, rows, k);
+  QWG_HIP(launch_dequant(qtype, make_view(d_packed, L), rows, k, d_out, (hipStream_t)stream));
+  return QWG_OK;
+}
+
+int qwg_gemv(int qtype, const void* d_packed, int64_t rows, int64_t k, const float* d_x, int n_cols, float* d_y,
+             void* stream) {
+  if (int rc = check_matrix(qtype, rows, k)) return rc;
+  if (n_cols < 1 || n_cols > MAX_COLS) return fail(QWG_E_SHAPE, "n_cols must be in 1..8");
+  if (rows == 0) return QWG_OK;
+  if (!d_packed || !d_x || !d_y) return fail(QWG_E_INVAL, "NULL pointer");
+  if (!aligned16(d_packed) || !aligned16(d_x)) return fail(QWG_E_INVAL, "pointers must be 16-byte aligned");
+  const Layout L = make_layout(qtype, rows, k);
+  const GemvPlan p = plan_gemv(qtype, rows, k, n_cols);
+  void* part = nullptr;
+  if (p.part_bytes) QWG_HIP(kernel_workspace(p.part_bytes, &part));
+  EpiArgs e{};
+  e.y = d_y;
+  e.y_stride = rows;
+  QWG_HIP(launch_gemv(qtype, make_view(d_packed, L), k, d_x, k, nullptr, 0.f, false, n_cols, EPI_STORE, e,
+                      (float*)part, (hipStream_t)stream, p));
+  return QWG_OK;
+}
+
+int qwg_rmsnorm(const float* d_x, const float* d_g, int64_t n, float eps, int n_cols, float* d_out, void* stream) {
+  if (!d_x || !d_g || !d_out) return fail(QWG_E_INVAL, "NULL pointer");
+  if (n < 1 || n > 65536 || n_cols < 1 || n_cols > 65535) return fail(QWG_E_SHAPE, "bad n or n_cols");
+  QWG_HIP(launch_rmsnorm(d_x, d_g, n, eps, n_cols, d_out, (hipStream_t)stream));
+  return QWG_OK;
+}
+
+int qwg_rope_table(int max_pos, int head_dim, double base, float* h_table) {
+  if (!h_table) return fail(QWG_E_INVAL, "NULL pointer");
+  if (max_pos < 1 || head_dim < 2 || head_dim % 2) return fail(QWG_E_SHAPE, "bad max_pos or head_dim");
+  const int half = head_dim / 2;
+  for (int i = 0; i < half; ++i) {
+    const double th = std::pow(base, -2.0 * i / (double)head_dim);
+    for (int p = 0; p < max_pos; ++p) {
+      const double phi = (double)p * th;
+      h_table[((size_t)p * half + i) * 2] = (float)std::cos(phi);
+      h_table[((size_t)p * half + i) * 2 + 1] = (float)std::sin(phi);
+    }
+  }
+  return QWG_OK;
+}
+
+int qwg_rope(float* d_v, int n_heads, int head_dim, const float* d_table, int pos, void* stream) {
+  if (!d_v || !d_table) return fail(QWG_E_INVAL, "NULL pointer");
+  if (head_dim != HEAD_DIM || n_heads < 1 || pos < 0) return fail(QWG_E_SHAPE, "head_dim must be 128");
+  QWG_HIP(launch_rope(d_v, n_heads, d_table, pos, (hipStream_t)stream));
+  return QWG_OK;
+}
+
+size_t qwg_attn_work_bytes(int n_pos, int n_q, int n_kv, int head_dim, int n_cols) {
+  if (n_pos < 1 || n_q < 1 || n_kv < 1 || n_q % n_kv || head_dim != HEAD_DIM || n_cols < 1 || n_cols > MAX_COLS)
+    return 0;
+  return plan_attn(n_pos, n_q, n_kv, n_cols).work_bytes;
+}
+
+int qwg_attn_decode(const float* d_q, const uint16_t* d_kc, const uint16_t* d_vc, int n_pos, int n_q, int n_kv,
+                    int head_dim, int n_cols, float* d_out, void* d_work, size_t work_bytes, void* stream) {
+  if (!d_q || !d_kc || !d_vc || !d_out || !d_work) return fail(QWG_E_INVAL, "NULL pointer");
+  if (head_dim != HEAD_DIM) return fail(QWG_E_SHAPE, "head_dim must be 128");
+  if (n_pos < 1 || n_q < 1 || n_kv < 1 || n_q % n_kv || n_cols < 1 || n_cols > MAX_COLS)
+    return fail(QWG_E_SHAPE, "bad attention shape");
+  if (n_q / n_kv * n_cols > 64) return fail(QWG_E_SHAPE, "(n_q / n_kv) * n_cols must be <= 64");
+  const AttnPlan p = plan_attn(n_pos, n_q, n_kv, n_cols);
+  if (work_bytes < p.work_bytes) return fail(QWG_E_NOMEM, "work buffer smaller than qwg_attn_work_bytes");
+  QWG_HIP(launch_attn(d_q, (int64_t)n_q * HEAD_DIM, d_kc, d_vc, (int64_t)n_kv * HEAD_DIM, n_pos, n_q, n_kv, n_cols,
+                      d_out, (int64_t)n_q * HEAD_DIM, d_work, p, (hipStream_t)stream));
+  return QWG_OK;
+}
+
+int qwg_swiglu(const float* d_g, const float* d_u, int64_t n, float* d_out, void* stream) {
+  if (!d_g || !d_u || !d_out) return fail(QWG_E_INVAL, "NULL pointer");
+  if (n < 0) return fail(QWG_E_SHAPE, "n < 0");
+  QWG_HIP(launch_swiglu(d_g, d_u, n, d_out, (hipStream_t)stream));
+  return QWG_OK;
+}
+
+int qwg_cosine(const float* d_a, const float* d_b, int64_t n, float* d_out, void* stream) {
+  if (!d_a || !d_b || !d_out) return fail(QWG_E_INVAL, "NULL pointer");
+  if (n < 1) return fail(QWG_E_SHAPE, "n < 1");
+  QWG_HIP(launch_cosine(d_a, d_b, n, d_out, (hipStream_t)stream));
+  return QWG_OK;
+}
+
+int qwg_argmax(const float* d_x, int64_t n, int32_t* d_out, void* stream) {
+  if (!d_x || !d_out) return fail(QWG_E_INVAL, "NULL pointer");
+  if (n < 1 || n > 0x7FFFFFFE) return fail(QWG_E_SHAPE, "n out of range");
+  QWG_HIP(launch_argmax(d_x, n, 1, n, d_out, (hipStream_t)stream));
+  return QWG_OK;
+}
+
+// ------------------------------------------------------------------------------------- model ABI
+
+int qwg_model_create(const qwg_model_desc* desc, qwg_model** out) {
+  if (!out) return fail(QWG_E_INVAL, "out is NULL");
+  *out = nullptr;
+  if (int rc = check_desc(desc)) return rc;
+  return guarded([&]() -> int {
+    qwg_model* m = new qwg_model();
+    m->d = *desc;
+    m->skip.assign(desc->n_layers, 0);
+    plan_model(m);
+    *out = m;
+    return QWG_OK;
+  });
+}
+
+size_t qwg_model_arena_bytes(const qwg_model* m) { return m ? m->total : 0; }
+
+int qwg_model_bind(qwg_model* m, void* d_arena, size_t bytes, void* compute, void* copy) {
+  if (!m || !d_arena) return fail(QWG_E_INVAL, "NULL pointer");
+  if (m->bound) return fail(QWG_E_STATE, "model already bound");
+  if (bytes < m->total) return fail(QWG_E_NOMEM, "arena smaller than qwg_model_arena_bytes");
+  if ((uintptr_t)d_arena & 255) return fail(QWG_E_INVAL, "arena must be 256-byte aligned");
+  m->arena = (uint8_t*)d_arena;
+  m->cs = (hipStream_t)compute;
+  m->xs = copy ? (hipStream_t)copy : (hipStream_t)compute;
+  for (int i = 0; i < 2; ++i) {
+    QWG_HIP(hipEventCreateWithFlags(&m->ev_full[i], hipEventDisableTiming));
+    QWG_HIP(hipEventCreateWithFlags(&m->ev_free[i], hipEventDisableTiming));
+    QWG_HIP(hipEventRecord(m->ev_free[i], m->cs));
+  }
+  for (auto& P : m->L) {
+    if (P.resident) continue;
+    void* p = nullptr;
+    hipError_t e = hipHostMalloc(&p, P.image, hipHostMallocDefault);
+    if (e != hipSuccess) return fail(QWG_E_NOMEM, std::string("pinned host image: ") + hipGetErrorString(e));
+    P.host = (uint8_t*)p;
+  }
+  // rope table (fp64 -> fp32) and zeroed caches / activations
+  std::vector<float> tab((size_t)m->d.max_ctx * m->d.head_dim);
+  qwg_rope_table(m->d.max_ctx, m->d.head_dim, (double)m->d.rope_theta, tab.data());
+  QWG_HIP(hipMemcpyAsync(m->arena + m->rope, tab.data(), tab.size() * 4, hipMemcpyHostToDevice, m->cs));
+  for (auto& P : m->L) {
+    QWG_HIP(hipMemsetAsync(m->arena + P.kc, 0, (size_t)m->d.max_ctx * m->KR() * 2, m->cs));
+    QWG_HIP(hipMemsetAsync(m->arena + P.vc, 0, (size_t)m->d.max_ctx * m->KR() * 2, m->cs));
+  }
+  QWG_HIP(hipStreamSynchronize(m->cs));
+  m->bound = true;
+  return QWG_OK;
+}
+
+void qwg_model_destroy(qwg_model* m) {
+  if (!m) return;
+  if (m->bound) {
+    (void)hipStreamSynchronize(m->cs);
+    (void)hipStreamSynchronize(m->xs);
+  }
+  for (auto& P : m->L)
+    if (P.host) (void)hipHostFree(P.host);
+  for (int i = 0; i < 2; ++i) {
+    if (m->ev_full[i]) (void)hipEventDestroy(m->ev_full[i]);
+    if (m->ev_free[i]) (void)hipEventDestroy(m->ev_free[i]);
+  }
+  for (auto e : m->tev) (void)hipEventDestroy(e);
+  for (auto e : m->cev) (void)hipEventDestroy(e);
+  delete m;
+}
+
+int qwg_model_set_tensor(qwg_model* m, int layer, int tensor_id, int qtype, const void* h_canon, size_t nbytes) {
+  if (!m || !h_canon) return fail(QWG_E_INVAL, "NULL pointer");
+  if (!m->bound) return fail(QWG_E_STATE, "model is not bound");
+  const qwg_model_desc& d = m->d;
+  const MatPlan* mp = nullptr;
+  int64_t rows = 0, k = 0, row0 = 0, step = 1;
+  int want_qt;
+  bool global = tensor_id == QWG_T_EMBED || tensor_id == QWG_T_HEAD;
+  if (global ? layer != -1 : (layer < 0 || layer >= d.n_layers)) return fail(QWG_E_INVAL, "bad layer index");
+  LayerPlan* P = global ? nullptr : &m->L[layer];
+  switch (tensor_id) {
+    case QWG_T_EMBED: mp = &m->embed; rows = d.vocab; k = d.hidden; want_qt = d.qtype_embed; break;
+    case QWG_T_HEAD: mp = &m->head; rows = d.vocab; k = d.hidden; want_qt = d.qtype_head; break;
+    case QWG_T_WQ: mp = &P->qkv; rows = m->QR(); k = d.hidden; want_qt = d.qtype_attn; break;
+    case QWG_T_WK: mp = &P->qkv; rows = m->KR(); k = d.hidden; row0 = m->QR(); want_qt = d.qtype_attn; break;
+    case QWG_T_WV: mp = &P->qkv; rows = m->KR(); k = d.hidden; row0 = m->QR() + m->KR(); want_qt = d.qtype_attn; break;
+    case QWG_T_WO: mp = &P->o; rows = d.hidden; k = m->QR(); want_qt = d.qtype_attn; break;
+    case QWG_T_WGATE: mp = &P->gu; rows = d.ffn; k = d.hidden; step = 2; want_qt = d.qtype_ffn; break;
+    case QWG_T_WUP: mp = &P->gu; rows = d.ffn; k = d.hidden; row0 = 1; step = 2; want_qt = d.qtype_ffn; break;
+    case QWG_T_WDOWN: mp = &P->down; rows = d.hidden; k = d.ffn; want_qt = d.qtype_ffn; break;
+    default: return fail(QWG_E_INVAL, "unknown tensor id");
+  }
+  if (qtype != want_qt) return fail(QWG_E_UNSUPPORTED, "qtype differs from the model description");
+  const int64_t rb = canon_row_bytes(qtype, k);
+  if ((int64_t)nbytes != rows * rb) return fail(QWG_E_SHAPE, "nbytes != rows * row_bytes");
+  const bool streamed = P && !P->resident;
+  uint8_t* dst;
+  if (global) dst = m->arena + mp->off;
+  else if (!streamed) dst = m->arena + P->arena_off + mp->off;
+  else dst = m->arena + m->slot[0] + mp->off;
+  if (streamed)  // keep the rows of the fused matrix that other tensors already wrote
+    QWG_HIP(hipMemcpyAsync(dst, P->host + mp->off, (size_t)mp->L.total, hipMemcpyHostToDevice, m->cs));
+  const int64_t chunk_rows = std::max<int64_t>(1, (int64_t)m->staging_bytes / rb);
+  for (int64_t r = 0; r < rows; r += chunk_rows) {
+    const int64_t n = std::min(chunk_rows, rows - r);
+    QWG_HIP(hipMemcpyAsync(m->arena + m->staging, (const uint8_t*)h_canon + r * rb, (size_t)(n * rb),
+                           hipMemcpyHostToDevice, m->cs));
+    QWG_HIP(launch_repack(qtype, m->arena + m->staging, n, k, dst, mp->L, row0 + r * step, step, m->cs));
+  }
+  if (streamed)
+    QWG_HIP(hipMemcpyAsync(P->host + mp->off, dst, (size_t)mp->L.total, hipMemcpyDeviceToHost, m->cs));
+  QWG_HIP(hipStreamSynchronize(m->cs));
+  return QWG_OK;
+}
+
+int qwg_model_set_norm(qwg_model* m, int layer, int which, const float* h_g, int n) {
+  if (!m || !h_g) return fail(QWG_E_INVAL, "NULL pointer");
+  if (!m->bound) return fail(QWG_E_STATE, "model is not bound");
+  if (n != m->d.hidden) return fail(QWG_E_SHAPE, "gain length must equal hidden");
+  size_t off;
+  if (which == QWG_NORM_FINAL && layer == -1) off = m->g_final;
+  else if ((which == QWG_NORM_ATTN || which == QWG_NORM_FFN) && layer >= 0 && layer < m->d.n_layers)
+    off = which == QWG_NORM_ATTN ? m->L[layer].g_attn : m->L[layer].g_ffn;
+  else return fail(QWG_E_INVAL, "bad norm id / layer");
+  QWG_HIP(hipMemcpy(m->arena + off, h_g, (size_t)n * 4, hipMemcpyHostToDevice));
+  return QWG_OK;
+}
+
+int qwg_model_set_kv(qwg_model* m, int layer, const uint16_t* h_k, const uint16_t* h_v, int n_pos) {
+  if (!m || (n_pos > 0 && (!h_k || !h_v))) return fail(QWG_E_INVAL, "NULL pointer");
+  if (!m->bound) return fail(QWG_E_STATE, "model is not bound");
+  if (layer < 0 || layer >= m->d.n_layers) return fail(QWG_E_INVAL, "bad layer");
+  if (n_pos < 0 || n_pos > m->d.max_ctx) return fail(QWG_E_SHAPE, "n_pos outside 0..max_ctx");
+  const size_t bytes = (size_t)n_pos * m->KR() * 2;
+  QWG_HIP(hipStreamSynchronize(m->cs));
+  QWG_HIP(hipMemcpy(m->arena + m->L[layer].kc, h_k, bytes, hipMemcpyHostToDevice));
+  QWG_HIP(hipMemcpy(m->arena + m->L[layer].vc, h_v, bytes, hipMemcpyHostToDevice));
+  m->n_past = n_pos;
+  return QWG_OK;
+}
+
+int qwg_model_get_kv(qwg_model* m, int layer, uint16_t* h_k, uint16_t* h_v, int n_pos) {
+  if (!m || (n_pos > 0 && (!h_k || !h_v))) return fail(QWG_E_INVAL, "NULL pointer");
+  if (!m->bound) return fail(QWG_E_STATE, "model is not bound");
+  if (layer < 0 || layer >= m->d.n_layers) return fail(QWG_E_INVAL, "bad layer");
+  if (n_pos < 0 || n_pos > m->d.max_ctx) return fail(QWG_E_SHAPE, "n_pos outside 0..max_ctx");
+  const size_t bytes = (size_t)n_pos * m->KR() * 2;
+  QWG_HIP(hipStreamSynchronize(m->cs));
+  QWG_HIP(hipMemcpy(h_k, m->arena + m->L[layer].kc, bytes, hipMemcpyDeviceToHost));
+  QWG_HIP(hipMemcpy(h_v, m->arena + m->L[layer].vc, bytes, hipMemcpyDeviceToHost));
+  return QWG_OK;
+}
+
+int qwg_decode_step(qwg_model* m, int32_t token, int32_t* next_token, float* h_logits) {
+  if (!m) return fail(QWG_E_INVAL, "NULL model");
+  return guarded([&]() -> int {
+    if (int rc = run_pass(m, &token, 1, m->n_past, m->d.n_layers, false)) return rc;
+    int32_t nt = 0;
+    if (int rc = finish_pass(m, 1, &nt, h_logits)) return rc;
+    if (next_token) *next_token = nt;
+    m->n_past += 1;
+    return QWG_OK;
+  });
+}
+
+int qwg_calibrate_skip(qwg_model* m, float tau, int32_t token, int32_t* next_token, float* h_cos, uint8_t* h_mask) {
+  if (!m) return fail(QWG_E_INVAL, "NULL model");
+  return guarded([&]() -> int {
+    if (int rc = run_pass(m, &token, 1, m->n_past, m->d.n_layers, true)) return rc;
+    int32_t nt = 0;
+    if (int rc = finish_pass(m, 1, &nt, nullptr)) return rc;
+    std::vector<float> cs(m->d.n_layers);
+    QWG_HIP(hipMemcpy(cs.data(), m->f(m->cosv), cs.size() * 4, hipMemcpyDeviceToHost));
+    for (int l = 0; l < m->d.n_layers; ++l) m->skip[l] = cs[l] >= tau ? 1 : 0;
+    if (h_cos) std::memcpy(h_cos, cs.data(), cs.size() * 4);
+    if (h_mask) std::memcpy(h_mask, m->skip.data(), m->skip.size());
+    if (next_token) *next_token = nt;
+    m->n_past += 1;
+    return QWG_OK;
+  });
+}
+
+int qwg_set_layer_skip(qwg_model* m, int layer, int skip) {
+  if (!m) return fail(QWG_E_INVAL, "NULL model");
+  if (layer < 0 || layer >= m->d.n_layers) return fail(QWG_E_INVAL, "bad layer");
+  m->skip[layer] = skip ? 1 : 0;
+  return QWG_OK;
+}
+
+int qwg_get_layer_skip(qwg_model* m, uint8_t* h_mask) {
+  if (!m || !h_mask) return fail(QWG_E_INVAL, "NULL pointer");
+  std::memcpy(h_mask, m->skip.data(), m->skip.size());
+  return QWG_OK;
+}
+
+int qwg_spec_step(qwg_model* m, int32_t token, int draft_layers, int k, int32_t* out_tokens, int* n_out,
+                  int* n_accepted) {
+  if (!m || !out_tokens || !n_out || !n_accepted) return fail(QWG_E_INVAL, "NULL pointer");
+  if (k < 1 || k + 1 > m->d.max_cols) return fail(QWG_E_SHAPE, "need 1 <= k and k + 1 <= max_cols");
+  if (draft_layers < 0 || draft_layers > m->d.n_layers) return fail(QWG_E_SHAPE, "bad draft_layers");
+  return guarded([&]() -> int {
+    const int p = m->n_past;
+    if (p + k + 1 > m->d.max_ctx) return fail(QWG_E_STATE, "context full");
+    std::vector<int32_t> cols(k + 1), verdict(k + 1);
+    cols[0] = token;
+    int32_t t = token;
+    for (int j = 0; j < k; ++j) {
+      if (int rc = run_pass(m, &t, 1, p + j, draft_layers, false)) return rc;
+      if (int rc = finish_pass(m, 1, &t, nullptr)) return rc;
+      cols[j + 1] = t;
+    }
+    if (int rc = run_pass(m, cols.data(), k + 1, p, m->d.n_layers, false)) return rc;
+    if (int rc = finish_pass(m, k + 1, verdict.data(), nullptr)) return rc;
+    int a = 0;
+    while (a < k && verdict[a] == cols[a + 1]) ++a;
+    for (int j = 0; j < a; ++j) out_tokens[j] = cols[j + 1];
+    out_tokens[a] = verdict[a];
+    *n_out = a + 1;
+    *n_accepted = a;
+    m->n_past = p + a + 1;
+    return QWG_OK;
+  });
+}
+
+int qwg_verify(qwg_model* m, const int32_t* tokens, int n, float* h_logits, int32_t* h_argmax) {
+  if (!m || !tokens) return fail(QWG_E_INVAL, "NULL pointer");
+  return guarded([&]() -> int {
+    if (int rc = run_pass(m, tokens, n, m->n_past, m->d.n_layers, false)) return rc;
+    std::vector<int32_t> am(n);
+    if (int rc = finish_pass(m, n, am.data(), h_logits)) return rc;
+    if (h_argmax) std::memcpy(h_argmax, am.data(), (size_t)n * 4);
+    return QWG_OK;
+  });
+}
+
+int qwg_model_n_past(const qwg_model* m) { return m ? m->n_past : -1; }
+
+int qwg_model_truncate(qwg_model* m, int n_past) {
+  if (!m) return fail(QWG_E_INVAL, "NULL model");
+  if (n_past < 0 || n_past > m->d.max_ctx) return fail(QWG_E_STATE, "n_past outside 0..max_ctx");
+  m->n_past = n_past;
+  return QWG_OK;
+}
+
+int qwg_model_set_capture(qwg_model* m, int on) {
+  if (!m) return fail(QWG_E_INVAL, "NULL model");
+  m->capture_on = on != 0;
+  return QWG_OK;
+}
+
+int qwg_model_get_hidden(qwg_model* m, int layer, float* h_out) {
+  if (!m || !h_out) return fail(QWG_E_INVAL, "NULL pointer");
+  if (!m->bound) return fail(QWG_E_STATE, "model is not bound");
+  if (layer < -1 || layer >= m->d.n_layers) return fail(QWG_E_INVAL, "bad layer");
+  QWG_HIP(hipStreamSynchronize(m->cs));
+  QWG_HIP(hipMemcpy(h_out, m->f(m->capture) + (size_t)(layer + 1) * m->d.hidden, (size_t)m->d.hidden * 4,
+                    hipMemcpyDeviceToHost));
+  return QWG_OK;
+}
+
+int qwg_model_set_timing(qwg_model* m, int tensor_id) {
+  if (!m) return fail(QWG_E_INVAL, "NULL model");
+  if (tensor_id != -1 && tensor_id != QWG_T_WQ && tensor_id != QWG_T_WO && tensor_id != QWG_T_WGATE &&
+      tensor_id != QWG_T_WDOWN && tensor_id != QWG_T_HEAD)
+    return fail(QWG_E_INVAL, "timing class must be WQ, WO, WGATE, WDOWN, HEAD or -1");
+  m->timing_tensor = tensor_id;
+  m->t_ms = 0.0;
+  m->t_n = 0;
+  m->t_bytes = 0;
+  return QWG_OK;
+}
+
+int qwg_model_get_timing(qwg_model* m, double* total_ms, int64_t* n_launches, int64_t* bytes_per_launch) {
+  if (!m) return fail(QWG_E_INVAL, "NULL model");
+  if (total_ms) *total_ms = m->t_ms;
+  if (n_launches) *n_launches = m->t_n;
+  if (bytes_per_launch) *bytes_per_launch = m->t_bytes;
+  return QWG_OK;
+}
+
+int qwg_model_stream_stats(qwg_model* m, int64_t* h2d_bytes, double* h2d_ms) {
+  if (!m) return fail(QWG_E_INVAL, "NULL model");
+  if (h2d_bytes) *h2d_bytes = m->h2d_bytes;
+  if (h2d_ms) *h2d_ms = m->h2d_ms;
+  m->h2d_ms = 0.0;
+  m->h2d_bytes = 0;
+  return QWG_OK;
+}
+
+int qwg_sync(qwg_model* m) {
+  if (!m) return fail(QWG_E_INVAL, "NULL model");
+  if (!m->bound) return QWG_OK;
+  QWG_HIP(hipStreamSynchronize(m->cs));
+  QWG_HIP(hipStreamSynchronize(m->xs));
+  return QWG_OK;
+}
+
+int qwg_host_alloc(size_t bytes, void** out) {
+  if (!out) return fail(QWG_E_INVAL, "out is NULL");
+  hipError_t e = hipHostMalloc(out, bytes, hipHostMallocDefault);
+  if (e != hipSuccess) return fail(QWG_E_NOMEM, std::string("hipHostMalloc: ") + hipGetErrorString(e));
+  return QWG_OK;
+}
+
+int qwg_host_free(void* p) {
+  if (!p) return QWG_OK;
+  QWG_HIP(hipHostFree(p));
+  return QWG_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,650 @@
+// qwg_formats.h -- packed device layouts of the block formats and their per-chunk decoders.
+//
+// The five formats are the GGUF block formats in the quantization-format table of the
+// "Show HN ... Llama 3.1 70B" NTransformer page (Q4_0, Q8_0 with 32-weight blocks;
+// Q4_K, Q5_K, Q6_K with 256-weight superblocks).  Canonical blocks (34/18/144/176/210 B)
+// break 16-byte alignment and mix scales with quants, so at load time every matrix is
+// rearranged ("packed") into separate row-major regions with the same payload bytes:
+//
+//   region Q : the quant bytes, 16 B per "chunk" (Q8_0: 16 weights; others: 32 weights),
+//              chunk c of row r at Q + r*q_row + 16c  -> a wave reads 1 KiB contiguous
+//   region A : Q8_0 / Q4_0 fp16 d per block; Q4_K / Q5_K 16-B superblock header
+//              (d, dmin, the 12 packed 6-bit scale/min bytes); Q6_K 8 B of 2-bit highs per chunk
+//   region B : Q5_K 4 B of fifth bits per chunk; Q6_K the chunk's two int8 sub-block scales
+//   region C : Q6_K fp16 d per superblock
+//
+// Inside a 32-weight chunk (chunk-local weights e = 0..31) the 16 quant bytes hold
+// e = j in the low nibble and e = j + 16 in the high nibble of byte j, so 32-bit word m
+// carries weights 4m..4m+3 (low nibbles) and 16+4m..16+4m+3 (high nibbles) -- the
+// activation for word m is float4 m and float4 4+m of the chunk.
+//   Q5_K fifth bits (32 bits): bit 8b + 2m   = bit 4 of weight 4m+b,
+//                              bit 8b + 2m+1 = bit 4 of weight 16+4m+b.
+//   Q6_K high bits (2 words): word i, byte b, bit pair p: p=0 -> weight 4(2i)+b,
+//        p=1 -> 16+4(2i)+b, p=2 -> 4(2i+1)+b, p=3 -> 16+4(2i+1)+b.
+//   Q6_K scales: weights 0..15 of a chunk form one 16-weight sub-block, 16..31 the next.
+//
+// Everything here is __host__ __device__ so the same decoders can be exercised on the CPU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qwg {
+
+enum QType : int { Q4_0 = 2, Q8_0 = 8, Q4_K = 12, Q5_K = 13, Q6_K = 14 };
+
+__host__ __device__ inline bool qtype_known(int qt) {
+  return qt == Q4_0 || qt == Q8_0 || qt == Q4_K || qt == Q5_K || qt == Q6_K;
+}
+__host__ __device__ inline int block_weights(int qt) { return (qt == Q4_0 || qt == Q8_0) ? 32 : 256; }
+__host__ __device__ inline int block_bytes(int qt) {
+  switch (qt) {
+    case Q8_0: return 34;
+    case Q4_0: return 18;
+    case Q4_K: return 144;
+    case Q5_K: return 176;
+    case Q6_K: return 210;
+    default: return 0;
+  }
+}
+__host__ __device__ inline int chunk_weights(int qt) { return qt == Q8_0 ? 16 : 32; }
+
+// Geometry of one packed matrix (all offsets in bytes from the matrix base).
+struct Layout {
+  int32_t qtype;
+  int64_t rows, k;
+  int64_t nch;    // chunks per row
+  int64_t q_row;  // = 16 * nch
+  int64_t a_off, a_row;
+  int64_t b_off, b_row;
+  int64_t c_off, c_row;
+  int64_t total;
+};
+
+__host__ __device__ inline int64_t align256(int64_t v) { return (v + 255) & ~(int64_t)255; }
+
+__host__ __device__ inline Layout make_layout(int qt, int64_t rows, int64_t k) {
+  Layout L{};
+  L.qtype = qt;
+  L.rows = rows;
+  L.k = k;
+  L.nch = k / chunk_weights(qt);
+  L.q_row = 16 * L.nch;
+  const int64_t nb = k / block_weights(qt);
+  switch (qt) {
+    case Q8_0: L.a_row = 2 * nb; break;
+    case Q4_0: L.a_row = 2 * nb; break;
+    case Q4_K: L.a_row = 16 * nb; break;
+    case Q5_K: L.a_row = 16 * nb; L.b_row = 4 * L.nch; break;
+    case Q6_K: L.a_row = 8 * L.nch; L.b_row = 2 * L.nch; L.c_row = 2 * nb; break;
+    default: break;
+  }
+  L.a_off = align256(rows * L.q_row);
+  L.b_off = align256(L.a_off + rows * L.a_row);
+  L.c_off = align256(L.b_off + rows * L.b_row);
+  L.total = align256(L.c_off + rows * L.c_row);
+  return L;
+}
+
+// Pointers into one packed matrix, as the kernels take them.
+struct MatView {
+  const uint8_t* q;
+  const uint8_t* a;
+  const uint8_t* b;
+  const uint8_t* c;
+  int64_t q_row, a_row, b_row, c_row;
+  int32_t nch;
+  int32_t rows;
+};
+
+__host__ __device__ inline MatView make_view(const void* base, const Layout& L) {
+  const uint8_t* p = (const uint8_t*)base;
+  MatView v;
+  v.q = p;
+  v.a = p + L.a_off;
+  v.b = p + L.b_off;
+  v.c = p + L.c_off;
+  v.q_row = L.q_row;
+  v.a_row = L.a_row;
+  v.b_row = L.b_row;
+  v.c_row = L.c_row;
+  v.nch = (int32_t)L.nch;
+  v.rows = (int32_t)L.rows;
+  return v;
+}
+
+// ---------------------------------------------------------------------------- fp16
+
+// IEEE binary16 bits -> fp32, exact for every finite value including subnormals.
+__host__ __device__ inline float half_bits_to_float(uint32_t h) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+#else
+  const uint32_t sign = (h & 0x8000u) << 16, e = (h >> 10) & 31u, m = h & 1023u;
+  uint32_t bits;
+  if (e == 0) {
+    const float v = (float)m * 5.9604644775390625e-8f;  // m * 2^-24, exact
+    return (h & 0x8000u) ? -v : v;
+  } else if (e == 31) {
+    bits = sign | 0x7F800000u | (m << 13);
+  } else {
+    bits = sign | ((e + 112u) << 23) | (m << 13);
+  }
+  float f;
+  __builtin_memcpy(&f, &bits, 4);
+  return f;
+#endif
+}
+
+// fp32 -> IEEE binary16 bits, round to nearest even, overflow -> inf.
+__host__ __device__ inline uint16_t float_to_half_bits(float f) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+#else
+  uint32_t x;
+  __builtin_memcpy(&x, &f, 4);
+  const uint32_t sign = (x >> 16) & 0x8000u;
+  const uint32_t ax = x & 0x7FFFFFFFu;
+  if (ax > 0x7F800000u) return (uint16_t)(sign | 0x7E00u);
+  if (ax >= 0x477FF000u) return (uint16_t)(sign | 0x7C00u);  // >= 65520 rounds to inf
+  if (ax < 0x38800000u) {                                    // below 2^-14: subnormal half
+    float a;
+    __builtin_memcpy(&a, &ax, 4);
+    const float m = __builtin_rintf(a * 16777216.0f);
+    return (uint16_t)(sign | (uint32_t)m);
+  }
+  const uint32_t mant = ax & 0x7FFFFFu;
+  uint32_t e = (ax >> 23) - 112u;
+  uint32_t hm = mant >> 13;
+  const uint32_t rest = mant & 0x1FFFu;
+  if (rest > 0x1000u || (rest == 0x1000u && (hm & 1u))) {
+    hm += 1;
+    if (hm == 1024) { hm = 0; e += 1; }
+  }
+  return (uint16_t)(sign | (e << 10) | hm);
+#endif
+}
+
+// ---------------------------------------------------------------------------- byte helpers
+
+__host__ __device__ inline float ubyte(uint32_t v, int i) { return (float)((v >> (8 * i)) & 0xFFu); }
+__host__ __device__ inline float sbyte(uint32_t v, int i) { return (float)(int32_t)(int8_t)(uint8_t)(v >> (8 * i)); }
+
+// 6-bit scale and min of sub-block s (0..7) from the 12 packed bytes held in words S0 (bytes
+// 0..3), S1 (4..7), S2 (8..11): s < 4 -> low six bits of byte s / byte s+4; s >= 4 -> low/high
+// nibble of byte s+4 joined with the top two bits of byte s-4 (scale) / byte s (min).
+__host__ __device__ inline void kq_scale_min(uint32_t S0, uint32_t S1, uint32_t S2, int s, int& sc, int& m) {
+  const int t = s & 3;
+  const uint32_t b0 = (S0 >> (8 * t)) & 0xFFu, b1 = (S1 >> (8 * t)) & 0xFFu, b2 = (S2 >> (8 * t)) & 0xFFu;
+  const int lo_sc = (int)(b0 & 63u), lo_m = (int)(b1 & 63u);
+  const int hi_sc = (int)((b2 & 15u) | ((b0 >> 6) << 4));
+  const int hi_m = (int)((b2 >> 4) | ((b1 >> 6) << 4));
+  sc = s < 4 ? lo_sc : hi_sc;
+  m = s < 4 ? lo_m : hi_m;
+}
+
+// Weight bytes are read exactly once per pass: streaming (non-temporal) loads.
+typedef uint32_t qwg_u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t qwg_u32x2 __attribute__((ext_vector_type(2)));
+
+__host__ __device__ inline uint4 ld_stream_u4(const uint8_t* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const qwg_u32x4 v = __builtin_nontemporal_load((const qwg_u32x4*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+#else
+  return *(const uint4*)p;
+#endif
+}
+__host__ __device__ inline uint2 ld_stream_u2(const uint8_t* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const qwg_u32x2 v = __builtin_nontemporal_load((const qwg_u32x2*)p);
+  return make_uint2(v.x, v.y);
+#else
+  return *(const uint2*)p;
+#endif
+}
+__host__ __device__ inline uint32_t ld_stream_u1(const uint8_t* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_nontemporal_load((const uint32_t*)p);
+#else
+  return *(const uint32_t*)p;
+#endif
+}
+
+template <class T>
+__host__ __device__ inline T ld(const uint8_t* p) {
+  return *(const T*)p;
+}
+
+// ---------------------------------------------------------------------------- per-format chunk codecs
+//
+// Each Fmt<QT> provides
+//   CW, XQ (float4s of activation per chunk), NSUM (activation sums per chunk it needs)
+//   Raw load(view, row, chunk)          -- the chunk's quant bytes and scale data
+//   decode(raw, chunk, w[CW])           -- exact fp32 weights in chunk order (for dequantize);
+//                                          a zero weight is +0 ("+ 0.0f" turns -0 into +0)
+//   dot<NC>(raw, chunk, X, S, acc)      -- acc[n] += sum_e w_e x[n][e] without forming w_e:
+//                                          integer quants times activations, then one scale
+//                                          (and min/offset via the chunk's activation sums S).
+// X(n, q) returns float4 q of the chunk's activation for column n; S(n, j) returns the sum of
+// activation part j of the chunk (Q4_0/Q4_K/Q5_K: all 32; Q6_K: j=0 -> 0..15, j=1 -> 16..31).
+
+template <int QT>
+struct Fmt;
+
+template <>
+struct Fmt<Q8_0> {
+  static constexpr int CW = 16, XQ = 4, NSUM = 0;
+  struct Raw {
+    uint4 q;
+    uint32_t d;
+  };
+  __host__ __device__ static Raw load(const MatView& v, int64_t row, int c) {
+    Raw r;
+    r.q = ld_stream_u4(v.q + row * v.q_row + (int64_t)c * 16);
+    r.d = ld<uint16_t>(v.a + row * v.a_row + (int64_t)(c >> 1) * 2);
+    return r;
+  }
+  __host__ __device__ static void decode(const Raw& r, int, float* w) {
+    const float d = half_bits_to_float(r.d);
+    const uint32_t q[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
+    for (int m = 0; m < 4; ++m)
+      for (int b = 0; b < 4; ++b) w[4 * m + b] = d * sbyte(q[m], b) + 0.0f;
+  }
+  template <int NC, class XF, class SF>
+  __host__ __device__ static void dot(const Raw& r, int, int nc, XF X, SF, float* acc) {
+    const float d = half_bits_to_float(r.d);
+    const uint32_t q[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
+    float f[16];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) f[4 * m + b] = sbyte(q[m], b);
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+      if (n >= nc) break;
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const float4 x = X(n, m);
+        s0 += f[4 * m + 0] * x.x;
+        s1 += f[4 * m + 1] * x.y;
+        s0 += f[4 * m + 2] * x.z;
+        s1 += f[4 * m + 3] * x.w;
+      }
+      acc[n] += d * (s0 + s1);
+    }
+  }
+};
+
+// Q4_0 and Q4_K share the nibble word decode: word m -> weights 4m..4m+3 (low nibbles) and
+// 16+4m..16+4m+3 (high nibbles, kept as 16 q so only one mask is needed; scaled back by 1/16).
+template <int NC, class XF>
+__host__ __device__ inline void nibble_dots(const uint4& qv, int nc, XF X, float* lo, float* hi) {
+  const uint32_t q[4] = {qv.x, qv.y, qv.z, qv.w};
+  float fl[16], fh[16];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const uint32_t l = q[m] & 0x0F0F0F0Fu, h = q[m] & 0xF0F0F0F0u;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      fl[4 * m + b] = ubyte(l, b);
+      fh[4 * m + b] = ubyte(h, b);
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < NC; ++n) {
+    if (n >= nc) break;
+    float sl = 0.f, sh = 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const float4 xa = X(n, m), xb = X(n, 4 + m);
+      sl += fl[4 * m + 0] * xa.x;
+      sh += fh[4 * m + 0] * xb.x;
+      sl += fl[4 * m + 1] * xa.y;
+      sh += fh[4 * m + 1] * xb.y;
+      sl += fl[4 * m + 2] * xa.z;
+      sh += fh[4 * m + 2] * xb.z;
+      sl += fl[4 * m + 3] * xa.w;
+      sh += fh[4 * m + 3] * xb.w;
+    }
+    lo[n] = sl;
+    hi[n] = sh * 0.0625f;
+  }
+}
+
+template <>
+struct Fmt<Q4_0> {
+  static constexpr int CW = 32, XQ = 8, NSUM = 1;
+  struct Raw {
+    uint4 q;
+    uint32_t d;
+  };
+  __host__ __device__ static Raw load(const MatView& v, int64_t row, int c) {
+    Raw r;
+    r.q = ld_stream_u4(v.q + row * v.q_row + (int64_t)c * 16);
+    r.d = ld<uint16_t>(v.a + row * v.a_row + (int64_t)c * 2);
+    return r;
+  }
+  __host__ __device__ static void decode(const Raw& r, int, float* w) {
+    const float d = half_bits_to_float(r.d);
+    const uint32_t q[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
+    for (int m = 0; m < 4; ++m)
+      for (int b = 0; b < 4; ++b) {
+        const int byte = (int)((q[m] >> (8 * b)) & 0xFFu);
+        w[4 * m + b] = d * (float)((byte & 15) - 8) + 0.0f;
+        w[16 + 4 * m + b] = d * (float)((byte >> 4) - 8) + 0.0f;
+      }
+  }
+  template <int NC, class XF, class SF>
+  __host__ __device__ static void dot(const Raw& r, int, int nc, XF X, SF S, float* acc) {
+    const float d = half_bits_to_float(r.d);
+    float lo[NC], hi[NC];
+    nibble_dots<NC>(r.q, nc, X, lo, hi);
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+      if (n >= nc) break;
+      acc[n] += d * ((lo[n] + hi[n]) - 8.0f * S(n, 0));
+    }
+  }
+};
+
+template <>
+struct Fmt<Q4_K> {
+  static constexpr int CW = 32, XQ = 8, NSUM = 1;
+  struct Raw {
+    uint4 q;
+    uint4 h;  // d | dmin << 16, S[0..3], S[4..7], S[8..11]
+  };
+  __host__ __device__ static Raw load(const MatView& v, int64_t row, int c) {
+    Raw r;
+    r.q = ld_stream_u4(v.q + row * v.q_row + (int64_t)c * 16);
+    r.h = ld<uint4>(v.a + row * v.a_row + (int64_t)(c >> 3) * 16);
+    return r;
+  }
+  __host__ __device__ static void coef(const Raw& r, int c, float& dsc, float& dmm) {
+    int sc, m;
+    kq_scale_min(r.h.y, r.h.z, r.h.w, c & 7, sc, m);
+    dsc = half_bits_to_float(r.h.x & 0xFFFFu) * (float)sc;
+    dmm = half_bits_to_float(r.h.x >> 16) * (float)m;
+  }
+  __host__ __device__ static void decode(const Raw& r, int c, float* w) {
+    float dsc, dmm;
+    coef(r, c, dsc, dmm);
+    const uint32_t q[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
+    for (int m = 0; m < 4; ++m)
+      for (int b = 0; b < 4; ++b) {
+        const int byte = (int)((q[m] >> (8 * b)) & 0xFFu);
+        w[4 * m + b] = __builtin_fmaf(dsc, (float)(byte & 15), -dmm) + 0.0f;
+        w[16 + 4 * m + b] = __builtin_fmaf(dsc, (float)(byte >> 4), -dmm) + 0.0f;
+      }
+  }
+  template <int NC, class XF, class SF>
+  __host__ __device__ static void dot(const Raw& r, int c, int nc, XF X, SF S, float* acc) {
+    float dsc, dmm;
+    coef(r, c, dsc, dmm);
+    float lo[NC], hi[NC];
+    nibble_dots<NC>(r.q, nc, X, lo, hi);
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+      if (n >= nc) break;
+      acc[n] += dsc * (lo[n] + hi[n]) - dmm * S(n, 0);
+    }
+  }
+};
+
+template <>
+struct Fmt<Q5_K> {
+  static constexpr int CW = 32, XQ = 8, NSUM = 1;
+  struct Raw {
+    uint4 q;
+    uint4 h;
+    uint32_t qh;
+  };
+  __host__ __device__ static Raw load(const MatView& v, int64_t row, int c) {
+    Raw r;
+    r.q = ld_stream_u4(v.q + row * v.q_row + (int64_t)c * 16);
+    r.h = ld<uint4>(v.a + row * v.a_row + (int64_t)(c >> 3) * 16);
+    r.qh = ld_stream_u1(v.b + row * v.b_row + (int64_t)c * 4);
+    return r;
+  }
+  // the 5-bit quants of word m as bytes: low-nibble weights and high-nibble weights
+  __host__ __device__ static void words(const Raw& r, int m, uint32_t& lo, uint32_t& hi) {
+    const uint32_t q[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
+    const uint32_t w = q[m];
+    // bit 8b + 2m (low) / 8b + 2m + 1 (high) moved to bit 4 of byte b
+    const uint32_t l5 = (m <= 2) ? (r.qh << (4 - 2 * m)) : (r.qh >> 2);
+    const uint32_t h5 = (m <= 1) ? (r.qh << (3 - 2 * m)) : (r.qh >> (2 * m - 3));
+    lo = (w & 0x0F0F0F0Fu) | (l5 & 0x10101010u);
+    hi = ((w >> 4) & 0x0F0F0F0Fu) | (h5 & 0x10101010u);
+  }
+  __host__ __device__ static void decode(const Raw& r, int c, float* w) {
+    float dsc, dmm;
+    Fmt<Q4_K>::Raw rr{r.q, r.h};
+    Fmt<Q4_K>::coef(rr, c, dsc, dmm);
+    for (int m = 0; m < 4; ++m) {
+      uint32_t lo, hi;
+      words(r, m, lo, hi);
+      for (int b = 0; b < 4; ++b) {
+        w[4 * m + b] = __builtin_fmaf(dsc, ubyte(lo, b), -dmm) + 0.0f;
+        w[16 + 4 * m + b] = __builtin_fmaf(dsc, ubyte(hi, b), -dmm) + 0.0f;
+      }
+    }
+  }
+  template <int NC, class XF, class SF>
+  __host__ __device__ static void dot(const Raw& r, int c, int nc, XF X, SF S, float* acc) {
+    float dsc, dmm;
+    Fmt<Q4_K>::Raw rr{r.q, r.h};
+    Fmt<Q4_K>::coef(rr, c, dsc, dmm);
+    float fl[16], fh[16];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      uint32_t lo, hi;
+      words(r, m, lo, hi);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        fl[4 * m + b] = ubyte(lo, b);
+        fh[4 * m + b] = ubyte(hi, b);
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+      if (n >= nc) break;
+      float sl = 0.f, sh = 0.f;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const float4 xa = X(n, m), xb = X(n, 4 + m);
+        sl += fl[4 * m + 0] * xa.x;
+        sh += fh[4 * m + 0] * xb.x;
+        sl += fl[4 * m + 1] * xa.y;
+        sh += fh[4 * m + 1] * xb.y;
+        sl += fl[4 * m + 2] * xa.z;
+        sh += fh[4 * m + 2] * xb.z;
+        sl += fl[4 * m + 3] * xa.w;
+        sh += fh[4 * m + 3] * xb.w;
+      }
+      acc[n] += dsc * (sl + sh) - dmm * S(n, 0);
+    }
+  }
+};
+
+template <>
+struct Fmt<Q6_K> {
+  static constexpr int CW = 32, XQ = 8, NSUM = 2;
+  struct Raw {
+    uint4 q;
+    uint2 qh;
+    uint32_t sc;  // two int8 scales: byte 0 -> weights 0..15, byte 1 -> 16..31
+    uint32_t d;
+  };
+  __host__ __device__ static Raw load(const MatView& v, int64_t row, int c) {
+    Raw r;
+    r.q = ld_stream_u4(v.q + row * v.q_row + (int64_t)c * 16);
+    r.qh = ld_stream_u2(v.a + row * v.a_row + (int64_t)c * 8);
+    r.sc = ld<uint16_t>(v.b + row * v.b_row + (int64_t)c * 2);
+    r.d = ld<uint16_t>(v.c + row * v.c_row + (int64_t)(c >> 3) * 2);
+    return r;
+  }
+  // unsigned 6-bit quants of word m: low-nibble weights (4m+b) and high-nibble weights (16+4m+b)
+  __host__ __device__ static void words(const Raw& r, int m, uint32_t& lo, uint32_t& hi) {
+    const uint32_t q[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
+    const uint32_t w = q[m];
+    const uint32_t h = (m < 2) ? r.qh.x : r.qh.y;
+    const uint32_t hl = (m & 1) ? h : (h << 4);
+    const uint32_t hh = (m & 1) ? (h >> 2) : (h << 2);
+    lo = (w & 0x0F0F0F0Fu) | (hl & 0x30303030u);
+    hi = ((w >> 4) & 0x0F0F0F0Fu) | (hh & 0x30303030u);
+  }
+  __host__ __device__ static void decode(const Raw& r, int, float* w) {
+    const float d = half_bits_to_float(r.d);
+    const float dA = d * (float)(int8_t)(uint8_t)(r.sc & 0xFFu);
+    const float dB = d * (float)(int8_t)(uint8_t)((r.sc >> 8) & 0xFFu);
+    for (int m = 0; m < 4; ++m) {
+      uint32_t lo, hi;
+      words(r, m, lo, hi);
+      for (int b = 0; b < 4; ++b) {
+        w[4 * m + b] = dA * (ubyte(lo, b) - 32.0f) + 0.0f;
+        w[16 + 4 * m + b] = dB * (ubyte(hi, b) - 32.0f) + 0.0f;
+      }
+    }
+  }
+  template <int NC, class XF, class SF>
+  __host__ __device__ static void dot(const Raw& r, int, int nc, XF X, SF S, float* acc) {
+    const float d = half_bits_to_float(r.d);
+    const float dA = d * (float)(int8_t)(uint8_t)(r.sc & 0xFFu);
+    const float dB = d * (float)(int8_t)(uint8_t)((r.sc >> 8) & 0xFFu);
+    float fl[16], fh[16];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      uint32_t lo, hi;
+      words(r, m, lo, hi);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        fl[4 * m + b] = ubyte(lo, b);
+        fh[4 * m + b] = ubyte(hi, b);
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+      if (n >= nc) break;
+      float sl = 0.f, sh = 0.f;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const float4 xa = X(n, m), xb = X(n, 4 + m);
+        sl += fl[4 * m + 0] * xa.x;
+        sh += fh[4 * m + 0] * xb.x;
+        sl += fl[4 * m + 1] * xa.y;
+        sh += fh[4 * m + 1] * xb.y;
+        sl += fl[4 * m + 2] * xa.z;
+        sh += fh[4 * m + 2] * xb.z;
+        sl += fl[4 * m + 3] * xa.w;
+        sh += fh[4 * m + 3] * xb.w;
+      }
+      acc[n] += dA * (sl - 32.0f * S(n, 0)) + dB * (sh - 32.0f * S(n, 1));
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------- repack (canonical -> packed)
+//
+// One canonical block of row r, block index b, is scattered to the packed regions.  Pure byte
+// movement (nibble re-pairing and bit re-ordering); no arithmetic on values.
+
+__host__ __device__ inline void put16(uint8_t* p, const uint8_t* s) {
+  for (int i = 0; i < 16; ++i) p[i] = s[i];
+}
+
+// quant (0..63) of weight i of a canonical superblock / block
+__host__ __device__ inline int canon_q4k(const uint8_t* qs, int i) {
+  const int g = i >> 6, t = i & 63;
+  return t < 32 ? (qs[32 * g + t] & 15) : (qs[32 * g + t - 32] >> 4);
+}
+__host__ __device__ inline int canon_q5k(const uint8_t* qh, const uint8_t* qs, int i) {
+  const int g = i >> 6, t = i & 63;
+  const int nib = t < 32 ? (qs[32 * g + t] & 15) : (qs[32 * g + t - 32] >> 4);
+  const int bit = t < 32 ? ((qh[t] >> (2 * g)) & 1) : ((qh[t - 32] >> (2 * g + 1)) & 1);
+  return nib | (bit << 4);
+}
+__host__ __device__ inline int canon_q6k(const uint8_t* ql, const uint8_t* qh, int i) {
+  const int n = i >> 7, r = i & 127, u = r >> 5, l = r & 31;
+  const uint8_t byte = ql[64 * n + l + 32 * (u & 1)];
+  const int nib = u < 2 ? (byte & 15) : (byte >> 4);
+  return nib | (((qh[32 * n + l] >> (2 * u)) & 3) << 4);
+}
+
+// write packed chunk pieces for chunk-local quants q[0..31]
+__host__ __device__ inline void pack_nibbles(const int* q, uint8_t* dst) {
+  for (int j = 0; j < 16; ++j) dst[j] = (uint8_t)((q[j] & 15) | ((q[j + 16] & 15) << 4));
+}
+
+__host__ __device__ inline void repack_block(int qt, const uint8_t* blk, uint8_t* base, const Layout& L, int64_t row,
+                                             int64_t b) {
+  uint8_t* Q = base + row * L.q_row;
+  uint8_t* A = base + L.a_off + row * L.a_row;
+  uint8_t* B = base + L.b_off + row * L.b_row;
+  uint8_t* C = base + L.c_off + row * L.c_row;
+  switch (qt) {
+    case Q8_0: {
+      A[2 * b] = blk[0];
+      A[2 * b + 1] = blk[1];
+      put16(Q + (2 * b) * 16, blk + 2);
+      put16(Q + (2 * b + 1) * 16, blk + 18);
+      break;
+    }
+    case Q4_0: {
+      A[2 * b] = blk[0];
+      A[2 * b + 1] = blk[1];
+      put16(Q + b * 16, blk + 2);  // canonical Q4_0 already pairs weight j with j + 16
+      break;
+    }
+    case Q4_K:
+    case Q5_K: {
+      put16(A + b * 16, blk);  // d, dmin, S[12]
+      const uint8_t* qs = blk + (qt == Q4_K ? 16 : 48);
+      const uint8_t* qh = blk + 16;
+      for (int s = 0; s < 8; ++s) {
+        int q[32];
+        for (int e = 0; e < 32; ++e) q[e] = qt == Q4_K ? canon_q4k(qs, 32 * s + e) : canon_q5k(qh, qs, 32 * s + e);
+        const int64_t c = 8 * b + s;
+        pack_nibbles(q, Q + c * 16);
+        if (qt == Q5_K) {
+          uint32_t bits = 0;
+          for (int m = 0; m < 4; ++m)
+            for (int bb = 0; bb < 4; ++bb) {
+              bits |= (uint32_t)((q[4 * m + bb] >> 4) & 1) << (8 * bb + 2 * m);
+              bits |= (uint32_t)((q[16 + 4 * m + bb] >> 4) & 1) << (8 * bb + 2 * m + 1);
+            }
+          for (int i = 0; i < 4; ++i) B[c * 4 + i] = (uint8_t)(bits >> (8 * i));
+        }
+      }
+      break;
+    }
+    case Q6_K: {
+      const uint8_t *ql = blk, *qh = blk + 128, *sc = blk + 192;
+      C[2 * b] = blk[208];
+      C[2 * b + 1] = blk[209];
+      for (int s = 0; s < 8; ++s) {
+        int q[32];
+        for (int e = 0; e < 32; ++e) q[e] = canon_q6k(ql, qh, 32 * s + e);
+        const int64_t c = 8 * b + s;
+        pack_nibbles(q, Q + c * 16);
+        uint32_t w[2] = {0, 0};
+        for (int i = 0; i < 2; ++i)
+          for (int bb = 0; bb < 4; ++bb) {
+            const int e0 = 4 * (2 * i) + bb, e1 = 16 + 4 * (2 * i) + bb;
+            const int e2 = 4 * (2 * i + 1) + bb, e3 = 16 + 4 * (2 * i + 1) + bb;
+            const uint32_t v = (uint32_t)(((q[e0] >> 4) & 3) | (((q[e1] >> 4) & 3) << 2) | (((q[e2] >> 4) & 3) << 4) |
+                                          (((q[e3] >> 4) & 3) << 6));
+            w[i] |= v << (8 * bb);
+          }
+        for (int i = 0; i < 8; ++i) A[c * 8 + i] = (uint8_t)(w[i >> 2] >> (8 * (i & 3)));
+        B[c * 2] = sc[2 * s];
+        B[c * 2 + 1] = sc[2 * s + 1];
+      }
+      break;
+    }
+    default: break;
+  }
+}
+
+}  // namespace qwg

@@ -1,0 +1,77 @@
+// qwg_kernels.h -- host-side launchers of the gfx950 kernels (internal to libqwg.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qwg_formats.h"
+
+namespace qwg {
+
+constexpr int HEAD_DIM = 128;   // every supported model uses 128-wide heads
+constexpr int MAX_COLS = 8;     // widest multi-column pass
+constexpr size_t LDS_BUDGET = 60 * 1024;  // dynamic LDS per workgroup (static arrays take the rest of 64 KiB)
+
+// What the GEMV does with each finished output row (columns n < nc).
+enum Epi : int {
+  EPI_PART = 0,    // partial sum of one K split (written to the split workspace)
+  EPI_STORE = 1,   // y[n][r] = v
+  EPI_RESID = 2,   // y[n][r] += v                      (Wo, W_down: residual add into h)
+  EPI_SWIGLU = 3,  // rows (2i, 2i+1) = (gate_i, up_i): y[n][i] = silu(gate) * up
+  EPI_QKV = 4,     // rows = [q heads | k heads | v heads]: RoPE on q,k; k,v -> fp16 KV cache rows
+};
+
+struct EpiArgs {
+  float* y;
+  int64_t y_stride;      // floats between columns of y
+  const float* rope;     // [max_ctx][HEAD_DIM/2] (cos, sin) pairs
+  int pos;               // position of column 0
+  int nq_rows, nkv_rows; // rows of the q part and of the k part (= v part)
+  uint16_t* kc;          // K cache of the layer, [ctx][kv_stride]
+  uint16_t* vc;
+  int64_t kv_stride;     // n_kv * HEAD_DIM
+};
+
+struct GemvPlan {
+  int ncm;     // compiled column bound (1, 4 or 8)
+  int rows_per_wave;
+  int waves;   // per workgroup
+  int ks;      // K per split
+  int ksplit;
+  size_t lds;  // dynamic LDS bytes
+  size_t part_bytes;  // split workspace bytes (0 if ksplit == 1)
+};
+
+GemvPlan plan_gemv(int qt, int64_t rows, int64_t k, int nc);
+
+// y = W x with prologue (plain x or x = RMSNorm(x; gain, eps)) and epilogue; `part` must hold
+// plan.part_bytes when plan.ksplit > 1.  Returns hipSuccess or the launch error.
+hipError_t launch_gemv(int qt, const MatView& w, int64_t k, const float* x, int64_t x_stride, const float* gain,
+                       float eps, bool rms, int nc, int epi, const EpiArgs& e, float* part, hipStream_t st,
+                       const GemvPlan& plan);
+
+hipError_t launch_repack(int qt, const uint8_t* canon, int64_t rows, int64_t k, uint8_t* packed, const Layout& L,
+                         int64_t dst_row0, int64_t dst_row_step, hipStream_t st);
+hipError_t launch_dequant(int qt, const MatView& w, int64_t rows, int64_t k, float* out, hipStream_t st);
+// h[n][:] = dequantized row tokens[n] of the embedding matrix
+hipError_t launch_embed(int qt, const MatView& w, int64_t k, const int32_t* tokens, int nc, float* h, int64_t h_stride,
+                        hipStream_t st);
+
+hipError_t launch_rmsnorm(const float* x, const float* g, int64_t n, float eps, int nc, float* out, hipStream_t st);
+hipError_t launch_rope(float* v, int n_heads, const float* table, int pos, hipStream_t st);
+hipError_t launch_swiglu(const float* g, const float* u, int64_t n, float* out, hipStream_t st);
+hipError_t launch_cosine(const float* a, const float* b, int64_t n, float* out, hipStream_t st);
+hipError_t launch_argmax(const float* x, int64_t n, int nc, int64_t x_stride, int32_t* out, hipStream_t st);
+
+struct AttnPlan {
+  int T;        // positions per split
+  int nsplit;
+  size_t work_bytes;
+};
+AttnPlan plan_attn(int n_pos, int n_q, int n_kv, int nc);
+// column j attends to positions [0, n_pos + j)
+hipError_t launch_attn(const float* q, int64_t q_stride, const uint16_t* kc, const uint16_t* vc, int64_t kv_stride,
+                       int n_pos, int n_q, int n_kv, int nc, float* out, int64_t out_stride, void* work,
+                       const AttnPlan& p, hipStream_t st);
+
+}  // namespace qwg

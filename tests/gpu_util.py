@@ -1,0 +1,20 @@
+"""Helpers shared by the GPU parity tests (no arithmetic of the method here)."""
+import numpy as np
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def gemv_ok(y, y_ref, a_ref):
+    """The row bound |y - y_ref| <= 1e-4 * sum|w x| + 1e-6."""
+    y = np.asarray(y, dtype=np.float64)
+    return np.abs(y - y_ref) <= 1e-4 * a_ref + 1e-6
+
+
+def is_tie(logits_ref, i, j, rel=1e-4):
+    """Two argmax candidates count as a tie when their gap is below rel * max|logits|."""
+    L = np.asarray(logits_ref, dtype=np.float64)
+    return abs(L[i] - L[j]) <= rel * np.max(np.abs(L))

@@ -1,0 +1,68 @@
+"""The C-ABI library loads and exports every function include/qwg.h declares (no GPU calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qwg.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    names = re.findall(r"\b(qwg_[a-z0-9_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("qwg_gemv", "qwg_dequantize", "qwg_repack", "qwg_decode_step", "qwg_calibrate_skip",
+                 "qwg_spec_step", "qwg_model_set_tensor", "qwg_attn_decode"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    from quantized_weight_streaming_gemv_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libqwg.so not built")
+    L = ctypes.CDLL(_lib.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(L, n)]
+    assert not missing, missing
+    assert set(_lib.SIGNATURES) == set(declared_functions())
+
+
+def test_size_queries_without_gpu():
+    from quantized_weight_streaming_gemv_amd import _lib, ops
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libqwg.so not built")
+    assert [ops.block_bytes(q) for q in (2, 8, 12, 13, 14)] == [18, 34, 144, 176, 210]
+    assert ops.row_bytes(12, 8192) == 32 * 144 and ops.row_bytes(12, 100) == 0
+    # packed layout keeps the payload bytes (plus < 1 KiB alignment per matrix)
+    for q in (2, 8, 12, 13, 14):
+        canon = 4096 * ops.row_bytes(q, 8192)
+        pb = ops.packed_bytes(q, 4096, 8192)
+        assert canon <= pb < canon + 1024
+    with pytest.raises(_lib.QwgError):
+        ops.packed_bytes(12, 10, 100)
+    with pytest.raises(_lib.QwgError):
+        ops.packed_bytes(7, 10, 256)
+
+
+def test_model_create_validates_without_gpu():
+    from quantized_weight_streaming_gemv_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libqwg.so not built")
+    L = _lib.lib()
+    d = _lib.ModelDesc(2, 512, 4, 2, 128, 1536, 1000, 64, 5e5, 1e-5, -1, 12, 12, 12, 12, 4)
+    h = ctypes.c_void_p(None)
+    assert L.qwg_model_create(ctypes.byref(d), ctypes.byref(h)) == 0
+    assert L.qwg_model_arena_bytes(h) > 0
+    L.qwg_model_destroy(h)
+    bad = _lib.ModelDesc(2, 500, 4, 2, 128, 1536, 1000, 64, 5e5, 1e-5, -1, 12, 12, 12, 12, 4)
+    assert L.qwg_model_create(ctypes.byref(bad), ctypes.byref(h)) == -2
+    bad2 = _lib.ModelDesc(2, 512, 4, 2, 64, 1536, 1000, 64, 5e5, 1e-5, -1, 12, 12, 12, 12, 4)
+    assert L.qwg_model_create(ctypes.byref(bad2), ctypes.byref(h)) == -2
+    bad3 = _lib.ModelDesc(2, 512, 4, 2, 128, 1536, 1000, 64, 5e5, 1e-5, -1, 7, 12, 12, 12, 4)
+    assert L.qwg_model_create(ctypes.byref(bad3), ctypes.byref(h)) == -6

@@ -1,0 +1,149 @@
+"""Kernel-level parity of libqwg.so against the CPU oracle (GPU only).
+
+Dequantization must be bit-exact; GEMV rows must satisfy |y - y_ref| <= 1e-4 sum|w x| + 1e-6;
+the layer ops are compared element-wise with tolerances derived from fp32 arithmetic."""
+import dataclasses
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import gemv_ok, rel_l2
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+QTS = [synth.Q8_0, synth.Q4_0, synth.Q4_K, synth.Q5_K, synth.Q6_K]
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+@pytest.fixture(scope="module")
+def ops():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from quantized_weight_streaming_gemv_amd import ops as o
+    o.lib()  # raises if the library is missing: no fallback
+    return o
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def packed_of(ops, qt, W, rows, k):
+    return ops.repack(qt, dev(W), rows, k)
+
+
+@pytest.mark.parametrize("qt", QTS, ids=[synth.QTYPE_NAMES[q] for q in QTS])
+@pytest.mark.parametrize("shape", [(1, 256), (37, 2048), (5, 28672)])
+@pytest.mark.parametrize("mult", [1.0, 1e-3], ids=["d", "d_x1e-3_subnormal"])
+def test_dequant_bit_exact(ops, qt, shape, mult):
+    rows, k = shape
+    dist = dataclasses.replace(synth.DEFAULT_DIST[qt], d_mult=mult)
+    W = synth.matrix(dist, k, rows, tkey=synth.key(1, qt * 1000 + k))
+    out = ops.dequantize(qt, packed_of(ops, qt, W, rows, k), rows, k).cpu().numpy()
+    ref = oracle.dequant(qt, W, rows, k)
+    assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
+
+
+def test_dequant_golden_blocks(ops):
+    g = json.load(open(os.path.join(GOLDEN, "blocks.json")))
+    for e in g["blocks"]:
+        blk = np.zeros(e["size"], np.uint8)
+        for s, t, v in e["set"]:
+            blk[s:t] = v
+        B = synth.BLOCK_WEIGHTS[e["qtype"]]
+        out = ops.dequantize(e["qtype"], packed_of(ops, e["qtype"], blk.reshape(1, -1), 1, B), 1, B).cpu().numpy()
+        ref = oracle.dequant(e["qtype"], blk, 1, B)
+        assert np.array_equal(out.view(np.uint32), ref.view(np.uint32)), e["name"]
+
+
+@pytest.mark.parametrize("qt", QTS, ids=[synth.QTYPE_NAMES[q] for q in QTS])
+@pytest.mark.parametrize("shape", [(1, 256), (70, 4096), (333, 8192), (64, 28672), (130, 512)])
+@pytest.mark.parametrize("nc", [1, 3, 4, 8])
+def test_gemv_row_tolerance(ops, qt, shape, nc):
+    rows, k = shape
+    W = synth.matrix(synth.DEFAULT_DIST[qt], k, rows, tkey=synth.key(2, qt * 1000 + k))
+    x = synth.normal_f32(synth.key(2, 7 + nc), nc * k).reshape(nc, k)
+    y = ops.gemv(qt, packed_of(ops, qt, W, rows, k), rows, k, dev(x)).cpu().numpy()
+    yr, ar = oracle.gemv(qt, W, rows, k, x)
+    ok = gemv_ok(y, yr, ar)
+    assert ok.all(), (np.argwhere(~ok)[:5], y[~ok][:5], yr[~ok][:5])
+
+
+def test_gemv_q8_0_4096_full(ops):
+    """The single Q8_0 GEMV workload: W 4096 x 4096, q ~ U[-127,127], d = |N|*0.02, x ~ N(0,1)."""
+    qt, rows, k = synth.Q8_0, 4096, 4096
+    W = synth.matrix(synth.DEFAULT_DIST[qt], k, rows, tkey=synth.key(0, synth.stream_id(0, -1, synth.WQ)))
+    x = synth.normal_f32(synth.key(0, synth.stream_id(0, -1, synth.XVEC)), k)
+    y = ops.gemv(qt, packed_of(ops, qt, W, rows, k), rows, k, dev(x)).cpu().numpy()
+    yr, ar = oracle.gemv(qt, W, rows, k, x)
+    assert gemv_ok(y, yr, ar).all()
+
+
+def test_gemv_rejects_bad_shapes(ops):
+    from quantized_weight_streaming_gemv_amd import QwgError
+    W = torch.zeros(1024, dtype=torch.uint8, device=DEV)
+    x = torch.zeros(300, dtype=torch.float32, device=DEV)
+    with pytest.raises(QwgError):
+        ops.gemv(synth.Q4_K, W, 2, 300, x)
+    x9 = torch.zeros((9, 256), dtype=torch.float32, device=DEV)
+    with pytest.raises(QwgError):
+        ops.gemv(synth.Q4_K, W, 2, 256, x9)
+
+
+def test_rmsnorm(ops):
+    n = 8192
+    x = synth.normal_f32(synth.key(3, 1), 3 * n, 0.5, 40.0).reshape(3, n)
+    g = synth.normal_f32(synth.key(3, 2), n, 1.0, 0.02)
+    y = ops.rmsnorm(dev(x), dev(g), 1e-5).cpu().numpy()
+    for j in range(3):
+        ref = oracle.rmsnorm(x[j], g, 1e-5)
+        assert np.max(np.abs(y[j] - ref) / np.abs(ref).max()) < 1e-5
+
+
+def test_rope_table_and_kernel(ops):
+    hd, base, maxp = 128, 5e5, 4200
+    tab = ops.rope_table(maxp, hd, base)
+    dtab = dev(tab)
+    v = synth.normal_f32(synth.key(3, 3), 8 * hd)
+    for pos in (0, 1, 2047, 4099):
+        out = ops.rope(dev(v).clone(), 8, hd, dtab, pos).cpu().numpy()
+        ref = oracle.rope(v, 8, hd, pos, base)
+        assert np.max(np.abs(out - ref)) < 4e-6 * np.max(np.abs(v)) * 2
+
+
+@pytest.mark.parametrize("nq,nkv,npos,nc", [(4, 2, 1, 1), (8, 2, 100, 1), (8, 2, 100, 4), (64, 8, 2049, 1),
+                                            (64, 8, 4097, 4), (32, 8, 513, 1), (16, 2, 70, 8)])
+def test_attention(ops, nq, nkv, npos, nc):
+    hd = 128
+    ctx = npos + nc - 1
+    kc = synth.normal_f16(synth.key(4, 1), ctx * nkv * hd).reshape(ctx, nkv, hd)
+    vc = synth.normal_f16(synth.key(4, 2), ctx * nkv * hd).reshape(ctx, nkv, hd)
+    q = synth.normal_f32(synth.key(4, 3), nc * nq * hd, 0.0, 3.0).reshape(nc, nq * hd)
+    out = ops.attn_decode(dev(q), dev(kc.view(np.int16)), dev(vc.view(np.int16)), npos, nq, nkv, hd, nc).cpu().numpy()
+    for j in range(nc):
+        ref = oracle.attention(q[j], kc, vc, npos + j, nq, nkv, hd)
+        assert rel_l2(out[j], ref) < 1e-5, j
+
+
+def test_swiglu_cosine_argmax(ops):
+    g = synth.normal_f32(synth.key(5, 1), 5000, 0.0, 4.0)
+    g[:3] = [0.0, -1e5, 90.0]
+    u = synth.normal_f32(synth.key(5, 2), 5000)
+    s = ops.swiglu(dev(g), dev(u)).cpu().numpy()
+    ref = oracle.swiglu(g, u)
+    assert np.all(np.abs(s - ref) <= 1e-6 * np.abs(ref) + 1e-30) and not np.isnan(s).any()
+    a = synth.normal_f32(synth.key(5, 3), 8192)
+    b = synth.normal_f32(synth.key(5, 4), 8192)
+    c = ops.cosine(dev(a), dev(b)).item()
+    assert abs(c - oracle.cosine(a, b)) < 1e-6
+    assert abs(ops.cosine(dev(a), dev(a)).item() - 1.0) < 1e-6
+    assert ops.cosine(dev(np.zeros(16, np.float32)), dev(a[:16])).item() == 0.0
+    x = synth.normal_f32(synth.key(5, 5), 128256)
+    x[777] = x[90000] = 50.0
+    assert ops.argmax(dev(x)).item() == 777 == oracle.argmax_f32(x)

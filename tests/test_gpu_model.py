@@ -1,0 +1,171 @@
+"""Decode-path parity of libqwg.so's model entry points against the CPU oracle (GPU only),
+on small Llamas of the same structure (head_dim 128, GQA, SwiGLU) for every format mix.
+
+Per-layer hidden states and logits must be within relative L2 2e-3; greedy tokens must agree
+except at near-ties (gap below 1e-4 max|logits|), where the oracle's choice is forced into both."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import is_tie, rel_l2
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+MIXES = [(synth.Q8_0, synth.Q8_0), (synth.Q4_K, synth.Q4_K), (synth.Q6_K, synth.Q6_K), (synth.Q6_K, synth.Q5_K),
+         (synth.Q4_0, synth.Q4_0)]
+
+
+@pytest.fixture(scope="module")
+def qwg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from quantized_weight_streaming_gemv_amd import synthetic
+    synthetic._lib.lib()
+    return synthetic
+
+
+def run_pair(qwg, wl, n_tokens, n_resident=None, capture=True):
+    m = qwg.make_model(wl, n_resident=n_resident)
+    qwg.load(m, wl)
+    m.set_capture(capture)
+    om = oracle.OracleModel(wl)
+    t = wl.first_token()
+    records = []
+    for step in range(n_tokens):
+        g_next, g_logits = m.decode_step(t, want_logits=True)
+        r = om.decode(t, want_hidden=True)
+        hid = [m.get_hidden(l) for l in range(-1, wl.n_layers)] if capture else None
+        records.append((g_next, g_logits, hid, r))
+        if g_next != r["next"]:
+            assert is_tie(r["logits"], g_next, r["next"]), (step, g_next, r["next"])
+        t = r["next"]
+    return m, om, records
+
+
+@pytest.mark.parametrize("mix", MIXES, ids=["%s-%s" % (synth.QTYPE_NAMES[a], synth.QTYPE_NAMES[b]) for a, b in MIXES])
+def test_decode_matches_oracle(qwg, mix):
+    wl = synth.tiny(mix[0], mix[1], wid=100 + mix[0] * 20 + mix[1])
+    m, om, records = run_pair(qwg, wl, 4)
+    for g_next, g_logits, hid, r in records:
+        assert rel_l2(g_logits, r["logits"]) < 2e-3
+        for l in range(wl.n_layers + 1):
+            assert rel_l2(hid[l], r["hidden"][l]) < 2e-3, l
+    assert m.n_past == om.n_past
+    # the KV rows the step appended match the oracle's fp16 rows (up to a last-bit rounding flip)
+    k, v = m.get_kv(1, om.n_past)
+    assert np.mean(k == om.kc[1][: om.n_past]) > 0.99 and np.mean(v == om.vc[1][: om.n_past]) > 0.99
+    m.close()
+
+
+def test_streaming_equals_resident_bitwise(qwg):
+    wl = synth.tiny(synth.Q6_K, n_layers=5, wid=160)
+    outs = []
+    for res in (-1, 2, 0):
+        m = qwg.make_model(wl, n_resident=res)
+        qwg.load(m, wl)
+        t, toks, lg = wl.first_token(), [], []
+        for _ in range(3):
+            t, logits = m.decode_step(t, want_logits=True)
+            toks.append(t)
+            lg.append(logits)
+        b, ms = m.stream_stats()
+        assert (b > 0) == (res >= 0)
+        outs.append((toks, np.stack(lg)))
+        m.close()
+    for toks, lg in outs[1:]:
+        assert toks == outs[0][0] and np.array_equal(lg, outs[0][1])
+
+
+def test_calibrate_skip_matches_oracle(qwg):
+    wl = synth.tiny(synth.Q6_K, n_layers=6, near_identity_every=2, wid=170)
+    m = qwg.make_model(wl, n_resident=3)
+    qwg.load(m, wl)
+    om = oracle.OracleModel(wl)
+    t = wl.first_token()
+    g_next, g_cos, g_mask = m.calibrate_skip(0.98, t)
+    r = om.calibrate_skip(0.98, t)
+    assert np.max(np.abs(g_cos - r["cos"])) < 1e-5
+    near = np.abs(r["cos"] - 0.98) < 1e-4
+    assert np.array_equal(g_mask[~near], r["mask"][~near])
+    assert all(g_mask[l] for l in range(wl.n_layers) if l % 2 == 1)  # near-identity layers are skipped
+    # later steps bypass the masked layers (both sides), and agree
+    om.skip[:] = g_mask
+    t = r["next"]
+    for _ in range(3):
+        g_next, g_logits = m.decode_step(t, want_logits=True)
+        rr = om.decode(t)
+        assert rel_l2(g_logits, rr["logits"]) < 2e-3
+        if g_next != rr["next"]:
+            assert is_tie(rr["logits"], g_next, rr["next"])
+        t = rr["next"]
+    m.close()
+
+
+def test_verify_columns_equal_sequential_steps(qwg):
+    wl = synth.tiny(synth.Q6_K, synth.Q5_K, wid=180, draft_k=3)
+    m = qwg.make_model(wl)
+    qwg.load(m, wl)
+    om = oracle.OracleModel(wl)
+    toks = [wl.first_token(), 5, 17, 999]
+    logits, am = m.verify(toks)
+    assert m.n_past == wl.n_prior
+    for j, t in enumerate(toks):
+        r = om.decode(t)
+        assert rel_l2(logits[j], r["logits"]) < 2e-3, j
+        if am[j] != r["next"]:
+            assert is_tie(r["logits"], am[j], r["next"])
+    m.close()
+
+
+def _zero_scales(W, qt):
+    W = W.copy()
+    flat = W.reshape(-1, synth.BLOCK_BYTES[qt])
+    if qt == synth.Q6_K:
+        flat[:, 208:210] = 0
+    elif qt in (synth.Q4_K, synth.Q5_K):
+        flat[:, 0:4] = 0
+    else:
+        flat[:, 0:2] = 0
+    return W
+
+
+@pytest.mark.parametrize("identity_tail", [False, True])
+def test_spec_step_matches_oracle(qwg, identity_tail):
+    wl = synth.tiny(synth.Q6_K, synth.Q5_K, n_layers=4, wid=190, draft_k=3)
+    draft = 2
+    ov = {}
+    if identity_tail:
+        for l in (2, 3):
+            for t in (synth.WO, synth.WDOWN):
+                ov[(l, t)] = _zero_scales(wl.weight(l, t), wl.qtype_of(t))
+    m = qwg.make_model(wl)
+    qwg.load(m, wl, weights_override=ov)
+    om = oracle.OracleModel(wl)
+    for (l, t), W in ov.items():
+        om._keep.append(W)
+        om.layers[l].w[om.TENSORS.index(t)] = W.ctypes.data
+    t = wl.first_token()
+    for _ in range(3):
+        toks, acc = m.spec_step(t, draft, 3)
+        r = om.spec_round(t, draft, 3)
+        assert toks == r["tokens"] and acc == r["n_accepted"]
+        assert m.n_past == om.n_past
+        if identity_tail:
+            assert acc == 3
+        t = toks[-1]
+    m.close()
+
+
+def test_context_overflow_is_an_error(qwg):
+    from quantized_weight_streaming_gemv_amd import QwgError
+    wl = synth.tiny(synth.Q8_0, wid=200)
+    m = qwg.make_model(wl, max_ctx=wl.n_prior + 1)
+    qwg.load(m, wl)
+    m.decode_step(wl.first_token())
+    with pytest.raises(QwgError):
+        m.decode_step(1)
+    m.truncate(wl.n_prior)
+    m.decode_step(wl.first_token())
+    m.close()
