@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Decode benchmark of the MI355X block-quantized Llama hot path.
+
+Default workload: Llama-70B-shaped decode with Q4_K weights fully resident in HBM (hidden 8192,
+64/8 heads, FFN 28672, 80 layers, vocab 128256, fp16 KV cache of 2048 positions), seeded
+synthetic weights.  One step = one greedy token through every layer (embedding row, 80 x
+[RMSNorm + fused QKV GEMV + RoPE/KV append, GQA attention, Wo GEMV + residual, RMSNorm +
+gate|up GEMV + SwiGLU, down GEMV + residual], final RMSNorm, head GEMV, argmax).
+
+Prints one JSON line: decode tok/s (value), the roofline of the dominant kernel (the fused
+gate|up dequant-GEMV: HBM GB/s from HIP events on the compute stream against 8 TB/s), per-GEMV
+class GB/s, and the CPU oracle's rate on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused dequant-GEMV HBM GB/s (% of 8 TB/s); decode tok/s, 70B-shape Q4_K/Q6_K"
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(msg: str) -> None:
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def workloads():
+    import synth
+    return {
+        "llama70b-q4_k": synth.LLAMA70B_Q4_K,
+        "llama8b-q8_0": synth.LLAMA8B_Q8_0,
+        "llama70b-q6_k": synth.replace(synth.LLAMA70B_Q6_K_STREAM, n_resident=-1, skip_tau=0.0),
+        "llama70b-q6_k-slep": synth.LLAMA70B_Q6_K_STREAM,
+        "llama70b-q6_k-q5_k": synth.LLAMA70B_Q6_K_Q5_K_SPEC,
+    }
+
+
+def gemv_classes(wl):
+    """(timing class id, label, weight tensor ids) of the five GEMV launches of a step."""
+    import synth
+    from quantized_weight_streaming_gemv_amd import _lib
+    return [(_lib.T_WQ, "qkv", (synth.WQ, synth.WK, synth.WV)), (_lib.T_WO, "wo", (synth.WO,)),
+            (_lib.T_WGATE, "gate_up", (synth.WGATE, synth.WUP)), (_lib.T_WDOWN, "down", (synth.WDOWN,)),
+            (_lib.T_HEAD, "head", (synth.HEAD,))]
+
+
+def token_bytes(wl, n_pos: int) -> int:
+    """Algorithmic bytes of one decode token: canonical weight bytes of every layer, the head and one
+    embedding row, plus the K and V rows read by attention (n_pos positions)."""
+    import synth
+    layer = wl.layer_bytes()
+    head = synth.row_bytes(wl.qtype_head, wl.hidden) * wl.vocab
+    emb = synth.row_bytes(wl.qtype_embed, wl.hidden)
+    kv = 2 * n_pos * wl.n_kv * wl.head_dim * 2
+    return wl.n_layers * (layer + kv) + head + emb
+
+
+def cpu_baseline(wl, n_sample_layers: int):
+    """The CPU oracle (fp64, OpenMP over rows) on a bounded sample of the same workload: layers
+    0..n-1 and the output head for one token at the first decode position."""
+    import numpy as np
+    import oracle
+    import synth
+    pos = wl.n_prior
+    ctx = pos + 1
+    h = oracle.dequant(wl.qtype_embed, wl.weight(-1, synth.EMBED, wl.first_token(), 1), 1, wl.hidden)[0]
+    t_layers = []
+    for l in range(n_sample_layers):
+        ws = {t: wl.weight(l, t) for t in oracle.OracleModel.TENSORS}
+        kc = np.zeros((ctx, wl.n_kv, wl.head_dim), np.uint16)
+        vc = np.zeros_like(kc)
+        kc[:pos] = wl.kv_prior(l, synth.KCACHE)
+        vc[:pos] = wl.kv_prior(l, synth.VCACHE)
+        t0 = time.perf_counter()
+        h = oracle.layer_forward(wl, l, ws, h, kc, vc, pos)
+        t_layers.append(time.perf_counter() - t0)
+        del ws
+    head = wl.weight(-1, synth.HEAD)
+    t0 = time.perf_counter()
+    oracle.head_logits(wl, head, h)
+    t_head = time.perf_counter() - t0
+    per_token = wl.n_layers * (sum(t_layers) / len(t_layers)) + t_head
+    return {
+        "value": 1.0 / per_token,
+        "unit": "tok/s",
+        "cores": oracle.threads(),
+        "kind": "oracle",
+        "sample": ("layers 0..%d of %d and the output head for one token at position %d (%.1f s of CPU work); "
+                   "tok/s = 1 / (%d x mean layer time + head time)"
+                   % (n_sample_layers - 1, wl.n_layers, pos, sum(t_layers) + t_head, wl.n_layers)),
+        "layer_s": sum(t_layers) / len(t_layers),
+        "head_s": t_head,
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=32)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama70b-q4_k", choices=sorted(workloads()))
+    ap.add_argument("--class-steps", type=int, default=4, help="steps per GEMV class for the per-class table")
+    ap.add_argument("--cpu-layers", type=int, default=8, help="oracle layers in the CPU-baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+    import synth
+    from quantized_weight_streaming_gemv_amd import _lib, synthetic
+
+    if not os.path.exists(_lib.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    wl = workloads()[args.workload]
+    total_steps = args.warmup + args.steps * 2 + args.class_steps * 5 + 1
+    max_ctx = wl.n_prior + total_steps + 8
+    log("workload %s: %d layers, %.2f GB of weights, KV %d positions" %
+        (wl.name, wl.n_layers, wl.model_bytes() / 1e9, wl.n_prior))
+    m = synthetic.make_model(wl, max_ctx=max_ctx)
+    log("arena %.2f GB" % (m.arena_bytes / 1e9))
+    load_s = synthetic.load(m, wl, log=log)
+    log("loaded in %.1f s" % load_s)
+
+    tok = wl.first_token()
+    if wl.skip_tau > 0:
+        tok, cos, mask = m.calibrate_skip(wl.skip_tau, tok)
+        log("skip calibration: %d of %d layers skipped" % (int(mask.sum()), wl.n_layers))
+    for _ in range(args.warmup):
+        tok, _ = m.decode_step(tok)
+
+    # timed region: K greedy tokens
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        tok, _ = m.decode_step(tok)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_per_step = dt * 1e3 / args.steps
+    tok_s = args.steps / dt
+    n_pos_mid = wl.n_prior + args.warmup + args.steps // 2
+    log("decode: %.3f ms/token, %.1f tok/s" % (ms_per_step, tok_s))
+
+    # the same K steps again with HIP events around every gate|up GEMV on the compute stream
+    m.set_timing(_lib.T_WGATE)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        tok, _ = m.decode_step(tok)
+    torch.cuda.synchronize()
+    dt_ev = time.perf_counter() - t0
+    g_ms, g_n, g_bytes = m.get_timing()
+    g_avg = g_ms / g_n
+    achieved = g_bytes / (g_avg * 1e-3) / 1e9
+    log("gate|up GEMV: %d launches, %.2f us avg, %.1f GB/s (%.1f%% of 8 TB/s); step with events %.3f ms"
+        % (g_n, g_avg * 1e3, achieved, 100 * achieved / HBM_PEAK_GBPS, dt_ev * 1e3 / args.steps))
+
+    classes = {}
+    tot_b = tot_ms = 0.0
+    for cid, label, _ in gemv_classes(wl):
+        m.set_timing(cid)
+        for _ in range(args.class_steps):
+            tok, _ = m.decode_step(tok)
+        ms, n, b = m.get_timing()
+        per_tok_ms = ms / args.class_steps
+        per_tok_b = b * n / args.class_steps
+        classes[label] = {"us_per_launch": round(ms / n * 1e3, 3), "bytes_per_launch": b,
+                          "gbps": round(b / (ms / n * 1e-3) / 1e9, 1)}
+        tot_b += per_tok_b
+        tot_ms += per_tok_ms
+    m.set_timing(-1)
+    gemv_gbps = tot_b / (tot_ms * 1e-3) / 1e9
+    log("all GEMVs of a step: %.1f GB/s (%.1f%% of 8 TB/s), %.3f ms of %.3f ms" %
+        (gemv_gbps, 100 * gemv_gbps / HBM_PEAK_GBPS, tot_ms, ms_per_step))
+    h2d_b, h2d_ms = m.stream_stats()
+    step_bytes = token_bytes(wl, n_pos_mid)
+    m.close()
+    del m
+    torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("CPU oracle baseline (%d layers + head) ..." % args.cpu_layers)
+        cpu = cpu_baseline(wl, args.cpu_layers)
+        log("oracle: %.3g tok/s on %d threads" % (cpu["value"], cpu["cores"]))
+
+    out = {
+        "metric": METRIC,
+        "value": round(tok_s, 3),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded random weights of the stated shapes and distributions)",
+        "config": {"workload": wl.name, "layers": wl.n_layers, "hidden": wl.hidden, "n_q": wl.n_q, "n_kv": wl.n_kv,
+                   "head_dim": wl.head_dim, "ffn": wl.ffn, "vocab": wl.vocab, "kv_positions": wl.n_prior,
+                   "weights": synth.QTYPE_NAMES[wl.qtype_attn] + "/" + synth.QTYPE_NAMES[wl.qtype_ffn],
+                   "batch": 1, "greedy": True},
+        "roofline": {"bound": "hbm", "kernel": "gate_up dequant-GEMV", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "bytes_per_launch": g_bytes, "us_per_launch": round(g_avg * 1e3, 3),
+                     "launches": g_n},
+        "gemv": {"all_gbps": round(gemv_gbps, 1), "all_frac": round(gemv_gbps / HBM_PEAK_GBPS, 4),
+                 "ms_per_token": round(tot_ms, 4), "classes": classes},
+        "step_effective_gbps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "step_bytes": step_bytes,
+        "cpu_baseline": cpu,
+        "pages_context": "NTransformer pages: ~49 tok/s 8B Q8_0 resident, 0.2-0.5 tok/s 70B Q6_K/Q4_K_M streamed, "
+                         "RTX 3090 (other hardware and mode; not comparable)",
+    }
+    if h2d_b:
+        out["h2d"] = {"bytes": h2d_b, "ms": round(h2d_ms, 3), "gbps": round(h2d_b / (h2d_ms * 1e-3) / 1e9, 2)}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

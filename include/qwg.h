@@ -100,6 +100,11 @@ int qwg_dequantize(int qtype, const void* d_packed, int64_t rows, int64_t k, flo
 int qwg_gemv(int qtype, const void* d_packed, int64_t rows, int64_t k, const float* d_x, int n_cols, float* d_y,
              void* stream);
 
+/* Launch geometry of subsequent GEMV launches in this process, for tuning: waves per workgroup
+ * (2, 4 or 8) and output rows per wave for single-column GEMVs (1, 2 or 4); 0 keeps the default.
+ * Results do not depend on it beyond floating-point summation order. */
+int qwg_set_gemv_geometry(int waves_per_group, int rows_per_wave);
+
 /* RMSNorm ([NT] "Key features"; cuda/ RMSNorm kernel): d_out[j][i] = g[i] x[j][i] / sqrt(mean_i x[j]^2 + eps),
  * for j < n_cols; x, out fp32 [n_cols][n]; n <= 65536. */
 int qwg_rmsnorm(const float* d_x, const float* d_g, int64_t n, float eps, int n_cols, float* d_out, void* stream);

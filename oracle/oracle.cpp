@@ -28,6 +28,10 @@
 #include <cstring>
 #include <vector>
 
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
 namespace {
 
 enum { QT_F32 = 0, QT_F16 = 1, QT_Q4_0 = 2, QT_Q8_0 = 8, QT_Q4_K = 12, QT_Q5_K = 13, QT_Q6_K = 14 };
@@ -322,6 +326,14 @@ struct orc_model {
   int32_t qt_head;
   const float* g_final;
 };
+
+int orc_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
 
 int orc_block_weights(int qt) { return block_weights(qt); }
 int orc_block_bytes(int qt) { return block_bytes(qt); }

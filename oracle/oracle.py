@@ -91,6 +91,8 @@ def lib():
         L.orc_argmax_f32.restype = i64
         L.orc_layer_forward.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Layer), vp, i64]
         L.orc_head.argtypes = [ctypes.POINTER(Model), vp, vp]
+        L.orc_threads.argtypes = []
+        L.orc_threads.restype = ctypes.c_int
         L.orc_step.argtypes = [ctypes.POINTER(Model), i32, i64, i32, vp, vp, vp, vp, ctypes.POINTER(i32)]
         _lib = L
     return _lib
@@ -184,6 +186,45 @@ def half_from_double(v: float) -> int:
 
 
 # ------------------------------------------------------------------------------ model
+
+def threads() -> int:
+    """OpenMP threads the oracle's row loops use."""
+    return int(lib().orc_threads())
+
+
+def layer_forward(wl, layer: int, weights: dict, h: np.ndarray, kc: np.ndarray, vc: np.ndarray, pos: int,
+                  max_ctx: Optional[int] = None) -> np.ndarray:
+    """One decoder layer on explicitly given tensors: weights {tensor_id: canonical bytes}, h [hidden]
+    (any float dtype, widened exactly to fp64), KV caches [max_ctx][n_kv][hd] fp16 bits (row pos is
+    written).  Returns the layer's output h in fp64."""
+    import synth
+    ctx = max_ctx or kc.shape[0]
+    dims = Dims(wl.n_layers, wl.hidden, wl.n_q, wl.n_kv, wl.head_dim, wl.ffn, wl.vocab, ctx, wl.rope_theta,
+                wl.rms_eps)
+    lay = Layer()
+    keep = []
+    for i, t in enumerate(OracleModel.TENSORS):
+        w = _c(weights[t], np.uint8)
+        keep.append(w)
+        lay.w[i] = w.ctypes.data
+        lay.qt[i] = wl.qtype_of(t)
+    ga, gf = wl.gain(layer, synth.G_ATTN), wl.gain(layer, synth.G_FFN)
+    keep += [ga, gf]
+    lay.g_attn, lay.g_ffn = ga.ctypes.data, gf.ctypes.data
+    assert kc.dtype == np.uint16 and kc.flags["C_CONTIGUOUS"] and vc.flags["C_CONTIGUOUS"]
+    lay.kc, lay.vc = kc.ctypes.data, vc.ctypes.data
+    out = _c(h, np.float64).copy()
+    if lib().orc_layer_forward(ctypes.byref(dims), ctypes.byref(lay), _ptr(out), pos) != 0:
+        raise ValueError("orc_layer_forward failed")
+    return out
+
+
+def head_logits(wl, head: np.ndarray, h: np.ndarray) -> np.ndarray:
+    """Final RMSNorm and output head on h (fp64 logits)."""
+    import synth
+    n = rmsnorm(_c(h, np.float64), wl.gain(-1, synth.G_FINAL), wl.rms_eps)
+    y, _ = gemv(wl.qtype_head, head, wl.vocab, wl.hidden, n)
+    return y
 
 class OracleModel:
     """A Llama decoder held as canonical bytes (from `synth`), run by the CPU oracle.

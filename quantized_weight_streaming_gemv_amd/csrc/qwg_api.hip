@@ -56,34 +56,37 @@ int64_t canon_row_bytes(int qt, int64_t k) {
 
 size_t align_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
 
-// split workspace for the kernel-level qwg_gemv (cached per device; freed at exit)
+// Scratch of the kernel-level entry points that need it (GEMV K-split partials, argmax keys):
+// allocated on first use per device and purpose, grown when needed, freed at exit.
+enum { WS_GEMV = 0, WS_ARGMAX = 1, WS_KINDS = 2 };
 struct KernelWorkspace {
-  void* p[64] = {};
-  size_t n[64] = {};
+  void* p[64][WS_KINDS] = {};
+  size_t n[64][WS_KINDS] = {};
   ~KernelWorkspace() {
     for (int i = 0; i < 64; ++i)
-      if (p[i]) (void)hipFree(p[i]);
+      for (int k = 0; k < WS_KINDS; ++k)
+        if (p[i][k]) (void)hipFree(p[i][k]);
   }
 } g_ws;
 
-hipError_t kernel_workspace(size_t bytes, void** out) {
+hipError_t kernel_workspace(int kind, size_t bytes, void** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (g_ws.n[dev] < bytes) {
-    if (g_ws.p[dev]) {
+  if (g_ws.n[dev][kind] < bytes) {
+    if (g_ws.p[dev][kind]) {
       e = hipDeviceSynchronize();
       if (e != hipSuccess) return e;
-      (void)hipFree(g_ws.p[dev]);
-      g_ws.p[dev] = nullptr;
-      g_ws.n[dev] = 0;
+      (void)hipFree(g_ws.p[dev][kind]);
+      g_ws.p[dev][kind] = nullptr;
+      g_ws.n[dev][kind] = 0;
     }
-    e = hipMalloc(&g_ws.p[dev], bytes);
+    e = hipMalloc(&g_ws.p[dev][kind], bytes);
     if (e != hipSuccess) return e;
-    g_ws.n[dev] = bytes;
+    g_ws.n[dev][kind] = bytes;
   }
-  *out = g_ws.p[dev];
+  *out = g_ws.p[dev][kind];
   return hipSuccess;
 }
 
@@ -112,7 +115,7 @@ struct qwg_model {
   qwg_model_desc d{};
   std::vector<LayerPlan> L;
   MatPlan embed{}, head{};
-  size_t g_final = 0, rope = 0, h = 0, hin = 0, qb = 0, ob = 0, act = 0, logits = 0, amax = 0, cosv = 0;
+  size_t g_final = 0, rope = 0, h = 0, hin = 0, qb = 0, ob = 0, act = 0, logits = 0, amax = 0, keys = 0, cosv = 0;
   size_t capture = 0, part = 0, attn = 0, slot[2] = {0, 0}, staging = 0;
   size_t part_bytes = 0, attn_bytes = 0, staging_bytes = 0, image_max = 0, total = 0;
   int n_streamed = 0;
@@ -201,6 +204,7 @@ static int plan_model(qwg_model* m) {
   m->act = take((size_t)C * F * 4);
   m->logits = take((size_t)C * V * 4);
   m->amax = take((size_t)C * 4);
+  m->keys = take((size_t)MAX_COLS * 8);
   m->cosv = take((size_t)d.n_layers * 4);
   m->capture = take((size_t)(d.n_layers + 1) * H * 4);
   size_t pb = 0;
@@ -212,7 +216,7 @@ static int plan_model(qwg_model* m) {
                                   {V, H}};
     const int qts[5] = {d.qtype_attn, d.qtype_attn, d.qtype_ffn, d.qtype_ffn, d.qtype_head};
     for (int i = 0; i < 5; ++i) {
-      const GemvPlan gp = plan_gemv(qts[i], shapes[i][0], shapes[i][1], nc);
+      const GemvPlan gp = plan_gemv(qts[i], shapes[i][0], shapes[i][1], nc, EPI_STORE);
       pb = std::max(pb, gp.part_bytes);
     }
   }
@@ -289,7 +293,7 @@ static int64_t gemv_alg_bytes(const MatPlan& p, int nc, int out_rw) {
 
 static int gemv(qwg_model* m, int tensor_class, int qt, const MatView& w, const MatPlan& mp, const float* x,
                 int64_t x_stride, const float* gain, bool rms, int nc, int epi, const EpiArgs& e) {
-  const GemvPlan gp = plan_gemv(qt, w.rows, mp.L.k, nc);
+  const GemvPlan gp = plan_gemv(qt, w.rows, mp.L.k, nc, epi);
   if (gp.part_bytes > m->part_bytes) return fail(QWG_E_NOMEM, "split workspace too small");
   const bool timed = m->timing_tensor == tensor_class;
   if (timed) {
@@ -416,7 +420,8 @@ static int run_pass(qwg_model* m, const int32_t* toks, int nc, int pos, int n_ru
   if (int rc = gemv(m, QWG_T_HEAD, d.qtype_head, view_at(m->arena, m->head), m->head, m->f(m->h), H, m->f(m->g_final),
                     true, nc, EPI_STORE, e))
     return rc;
-  QWG_HIP(launch_argmax(m->f(m->logits), d.vocab, nc, d.vocab, (int32_t*)(m->arena + m->amax), m->cs));
+  QWG_HIP(launch_argmax(m->f(m->logits), d.vocab, nc, d.vocab, (int32_t*)(m->arena + m->amax), m->cs,
+                        (unsigned long long*)(m->arena + m->keys)));
   return QWG_OK;
 }
 
@@ -481,14 +486,23 @@ int qwg_gemv(int qtype, const void* d_packed, int64_t rows, int64_t k, const flo
   if (!d_packed || !d_x || !d_y) return fail(QWG_E_INVAL, "NULL pointer");
   if (!aligned16(d_packed) || !aligned16(d_x)) return fail(QWG_E_INVAL, "pointers must be 16-byte aligned");
   const Layout L = make_layout(qtype, rows, k);
-  const GemvPlan p = plan_gemv(qtype, rows, k, n_cols);
+  const GemvPlan p = plan_gemv(qtype, rows, k, n_cols, EPI_STORE);
   void* part = nullptr;
-  if (p.part_bytes) QWG_HIP(kernel_workspace(p.part_bytes, &part));
+  if (p.part_bytes) QWG_HIP(kernel_workspace(WS_GEMV, p.part_bytes, &part));
   EpiArgs e{};
   e.y = d_y;
   e.y_stride = rows;
   QWG_HIP(launch_gemv(qtype, make_view(d_packed, L), k, d_x, k, nullptr, 0.f, false, n_cols, EPI_STORE, e,
                       (float*)part, (hipStream_t)stream, p));
+  return QWG_OK;
+}
+
+int qwg_set_gemv_geometry(int waves_per_group, int rows_per_wave) {
+  if (!(waves_per_group == 0 || waves_per_group == 2 || waves_per_group == 4 || waves_per_group == 8))
+    return fail(QWG_E_INVAL, "waves_per_group must be 0, 2, 4 or 8");
+  if (!(rows_per_wave == 0 || rows_per_wave == 1 || rows_per_wave == 2 || rows_per_wave == 4))
+    return fail(QWG_E_INVAL, "rows_per_wave must be 0, 1, 2 or 4");
+  set_gemv_geometry(waves_per_group, rows_per_wave);
   return QWG_OK;
 }
 
@@ -558,7 +572,9 @@ int qwg_cosine(const float* d_a, const float* d_b, int64_t n, float* d_out, void
 int qwg_argmax(const float* d_x, int64_t n, int32_t* d_out, void* stream) {
   if (!d_x || !d_out) return fail(QWG_E_INVAL, "NULL pointer");
   if (n < 1 || n > 0x7FFFFFFE) return fail(QWG_E_SHAPE, "n out of range");
-  QWG_HIP(launch_argmax(d_x, n, 1, n, d_out, (hipStream_t)stream));
+  void* keys = nullptr;
+  QWG_HIP(kernel_workspace(WS_ARGMAX, 256, &keys));
+  QWG_HIP(launch_argmax(d_x, n, 1, n, d_out, (hipStream_t)stream, (unsigned long long*)keys));
   return QWG_OK;
 }
 

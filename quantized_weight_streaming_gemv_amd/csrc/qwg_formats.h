@@ -168,6 +168,15 @@ __host__ __device__ inline uint16_t float_to_half_bits(float f) {
 // ---------------------------------------------------------------------------- byte helpers
 
 __host__ __device__ inline float ubyte(uint32_t v, int i) { return (float)((v >> (8 * i)) & 0xFFu); }
+
+// Hide a masked word from the optimizer so that each byte converts with one v_cvt_f32_ubyteN
+// (otherwise the shared mask is folded into a per-byte bit-field extract plus a conversion).
+__host__ __device__ inline uint32_t opaque(uint32_t v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __asm__("" : "+v"(v));
+#endif
+  return v;
+}
 __host__ __device__ inline float sbyte(uint32_t v, int i) { return (float)(int32_t)(int8_t)(uint8_t)(v >> (8 * i)); }
 
 // 6-bit scale and min of sub-block s (0..7) from the 12 packed bytes held in words S0 (bytes
@@ -223,7 +232,9 @@ __host__ __device__ inline T ld(const uint8_t* p) {
 //   Raw load(view, row, chunk)          -- the chunk's quant bytes and scale data
 //   decode(raw, chunk, w[CW])           -- exact fp32 weights in chunk order (for dequantize);
 //                                          a zero weight is +0 ("+ 0.0f" turns -0 into +0)
-//   dot<NC>(raw, chunk, X, S, acc)      -- acc[n] += sum_e w_e x[n][e] without forming w_e:
+//   dot<NC>(raw, chunk, sub, nc, X, S, acc)
+//                                       -- acc[n] += sum_e w_e x[n][e] without forming w_e (sub =
+//                                          chunk & 7, the chunk's place in its superblock):
 //                                          integer quants times activations, then one scale
 //                                          (and min/offset via the chunk's activation sums S).
 // X(n, q) returns float4 q of the chunk's activation for column n; S(n, j) returns the sum of
@@ -252,7 +263,7 @@ struct Fmt<Q8_0> {
       for (int b = 0; b < 4; ++b) w[4 * m + b] = d * sbyte(q[m], b) + 0.0f;
   }
   template <int NC, class XF, class SF>
-  __host__ __device__ static void dot(const Raw& r, int, int nc, XF X, SF, float* acc) {
+  __host__ __device__ static void dot(const Raw& r, int, int, int nc, XF X, SF, float* acc) {
     const float d = half_bits_to_float(r.d);
     const uint32_t q[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
     float f[16];
@@ -285,7 +296,7 @@ __host__ __device__ inline void nibble_dots(const uint4& qv, int nc, XF X, float
   float fl[16], fh[16];
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    const uint32_t l = q[m] & 0x0F0F0F0Fu, h = q[m] & 0xF0F0F0F0u;
+    const uint32_t l = opaque(q[m] & 0x0F0F0F0Fu), h = opaque(q[m] & 0xF0F0F0F0u);
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       fl[4 * m + b] = ubyte(l, b);
@@ -337,7 +348,7 @@ struct Fmt<Q4_0> {
       }
   }
   template <int NC, class XF, class SF>
-  __host__ __device__ static void dot(const Raw& r, int, int nc, XF X, SF S, float* acc) {
+  __host__ __device__ static void dot(const Raw& r, int, int, int nc, XF X, SF S, float* acc) {
     const float d = half_bits_to_float(r.d);
     float lo[NC], hi[NC];
     nibble_dots<NC>(r.q, nc, X, lo, hi);
@@ -380,9 +391,9 @@ struct Fmt<Q4_K> {
       }
   }
   template <int NC, class XF, class SF>
-  __host__ __device__ static void dot(const Raw& r, int c, int nc, XF X, SF S, float* acc) {
+  __host__ __device__ static void dot(const Raw& r, int, int sub, int nc, XF X, SF S, float* acc) {
     float dsc, dmm;
-    coef(r, c, dsc, dmm);
+    coef(r, sub, dsc, dmm);
     float lo[NC], hi[NC];
     nibble_dots<NC>(r.q, nc, X, lo, hi);
 #pragma unroll
@@ -415,8 +426,8 @@ struct Fmt<Q5_K> {
     // bit 8b + 2m (low) / 8b + 2m + 1 (high) moved to bit 4 of byte b
     const uint32_t l5 = (m <= 2) ? (r.qh << (4 - 2 * m)) : (r.qh >> 2);
     const uint32_t h5 = (m <= 1) ? (r.qh << (3 - 2 * m)) : (r.qh >> (2 * m - 3));
-    lo = (w & 0x0F0F0F0Fu) | (l5 & 0x10101010u);
-    hi = ((w >> 4) & 0x0F0F0F0Fu) | (h5 & 0x10101010u);
+    lo = opaque((w & 0x0F0F0F0Fu) | (l5 & 0x10101010u));
+    hi = opaque(((w >> 4) & 0x0F0F0F0Fu) | (h5 & 0x10101010u));
   }
   __host__ __device__ static void decode(const Raw& r, int c, float* w) {
     float dsc, dmm;
@@ -432,10 +443,10 @@ struct Fmt<Q5_K> {
     }
   }
   template <int NC, class XF, class SF>
-  __host__ __device__ static void dot(const Raw& r, int c, int nc, XF X, SF S, float* acc) {
+  __host__ __device__ static void dot(const Raw& r, int, int sub, int nc, XF X, SF S, float* acc) {
     float dsc, dmm;
     Fmt<Q4_K>::Raw rr{r.q, r.h};
-    Fmt<Q4_K>::coef(rr, c, dsc, dmm);
+    Fmt<Q4_K>::coef(rr, sub, dsc, dmm);
     float fl[16], fh[16];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -492,8 +503,8 @@ struct Fmt<Q6_K> {
     const uint32_t h = (m < 2) ? r.qh.x : r.qh.y;
     const uint32_t hl = (m & 1) ? h : (h << 4);
     const uint32_t hh = (m & 1) ? (h >> 2) : (h << 2);
-    lo = (w & 0x0F0F0F0Fu) | (hl & 0x30303030u);
-    hi = ((w >> 4) & 0x0F0F0F0Fu) | (hh & 0x30303030u);
+    lo = opaque((w & 0x0F0F0F0Fu) | (hl & 0x30303030u));
+    hi = opaque(((w >> 4) & 0x0F0F0F0Fu) | (hh & 0x30303030u));
   }
   __host__ __device__ static void decode(const Raw& r, int, float* w) {
     const float d = half_bits_to_float(r.d);
@@ -509,7 +520,7 @@ struct Fmt<Q6_K> {
     }
   }
   template <int NC, class XF, class SF>
-  __host__ __device__ static void dot(const Raw& r, int, int nc, XF X, SF S, float* acc) {
+  __host__ __device__ static void dot(const Raw& r, int, int, int nc, XF X, SF S, float* acc) {
     const float d = half_bits_to_float(r.d);
     const float dA = d * (float)(int8_t)(uint8_t)(r.sc & 0xFFu);
     const float dB = d * (float)(int8_t)(uint8_t)((r.sc >> 8) & 0xFFu);

@@ -20,6 +20,8 @@
 //     sums that a second kernel adds in a fixed order, so results never depend on timing.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+
 #include "qwg_kernels.h"
 
 namespace qwg {
@@ -72,11 +74,11 @@ struct GemvArgs {
 };
 
 template <int QT, int NCM, int R, int RMS, int EPI>
-__global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
+__global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
   using F = Fmt<QT>;
   constexpr int CW = F::CW, XQ = F::XQ, NS = F::NSUM;
   extern __shared__ float4 lds4[];
-  __shared__ float red[8][8];
+  __shared__ float red[8][16];
   __shared__ float rs_sh[NCM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
@@ -92,11 +94,14 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   const bool active = row0 < rows;
 
   // 1. request the first chunk of every row of this wave before staging the activation
+  // rows past the end are clamped to the last row (loads stay in bounds, results are dropped)
+  int rr[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) rr[r] = min(row0 + r, rows - 1);
   typename F::Raw cur[R];
   if (active && lane < nchs) {
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-      if (row0 + r < rows) cur[r] = F::load(a.w, row0 + r, cbase + lane);
+    for (int r = 0; r < R; ++r) cur[r] = F::load(a.w, rr[r], cbase + lane);
   }
 
   // 2. RMSNorm scale of every column over the full K (prologue of QKV, gate|up and head GEMVs)
@@ -169,19 +174,25 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
 #pragma unroll
     for (int n = 0; n < NCM; ++n) acc[r][n] = 0.f;
 
+  const int sub = lane & 7;  // chunk index within its 256-weight superblock (splits start on superblocks)
   for (int cl = lane; cl < nchs; cl += 64) {
     typename F::Raw nxt[R];
-    const int cn = cl + 64;
-    if (cn < nchs) {
+    const int cn = min(cl + 64, nchs - 1);  // the last iteration re-requests a chunk it already has
 #pragma unroll
-      for (int r = 0; r < R; ++r)
-        if (row0 + r < rows) nxt[r] = F::load(a.w, row0 + r, cbase + cn);
+    for (int r = 0; r < R; ++r) nxt[r] = F::load(a.w, rr[r], cbase + cn);
+    // one column: the chunk's activation lives in registers and serves all R rows
+    float4 xr[NCM == 1 ? XQ : 1];
+    float sr[NCM == 1 && NS > 0 ? NS : 1];
+    if (NCM == 1) {
+#pragma unroll
+      for (int q = 0; q < XQ; ++q) xr[q] = xs[q * nchp + cl];
+#pragma unroll
+      for (int j = 0; j < NS; ++j) sr[j] = sums[cl * NS + j];
     }
-    auto X = [&](int n, int q) -> float4 { return xs[(n * XQ + q) * nchp + cl]; };
-    auto S = [&](int n, int j) -> float { return sums[(n * nchp + cl) * NS + j]; };
+    auto X = [&](int n, int q) -> float4 { return NCM == 1 ? xr[q] : xs[(n * XQ + q) * nchp + cl]; };
+    auto S = [&](int n, int j) -> float { return NCM == 1 ? sr[j] : sums[(n * nchp + cl) * NS + j]; };
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-      if (row0 + r < rows) F::template dot<NCM>(cur[r], cbase + cl, nc, X, S, acc[r]);
+    for (int r = 0; r < R; ++r) F::template dot<NCM>(cur[r], cbase + cl, sub, nc, X, S, acc[r]);
 #pragma unroll
     for (int r = 0; r < R; ++r) cur[r] = nxt[r];
   }
@@ -242,24 +253,61 @@ static void fmt_geom(int qt, int& cw, int& xq, int& ns) {
   }
 }
 
-GemvPlan plan_gemv(int qt, int64_t rows, int64_t k, int nc) {
+static int g_waves = 0, g_rows = 0;  // launch-geometry overrides (0 = default)
+
+void set_gemv_geometry(int waves, int rows_per_wave) {
+  g_waves = waves;
+  g_rows = rows_per_wave;
+}
+
+// Workgroups of 8 waves; for one column, rows per wave (4, 2 or 1) picked so that the workgroup
+// count splits evenly over the 256 CUs (one resident workgroup per CU at this register use),
+// weighted by the measured per-wave efficiency of larger row groups (activation reuse).
+static int pick_rows_per_wave(int64_t rows, int waves, int ksplit, bool pairs) {
+  const int cand[3] = {4, 2, 1};
+  const double gain[3] = {1.0, 0.97, 0.83};
+  int best = 4;
+  double best_score = -1.0;
+  for (int i = 0; i < (pairs ? 2 : 3); ++i) {
+    const double wgs = (double)((rows + (int64_t)waves * cand[i] - 1) / ((int64_t)waves * cand[i])) * ksplit;
+    const double rounds = wgs / 256.0;
+    const double balance = rounds / std::ceil(rounds);
+    const double score = balance * gain[i];
+    if (score > best_score + 1e-9) {
+      best_score = score;
+      best = cand[i];
+    }
+  }
+  return best;
+}
+
+GemvPlan plan_gemv(int qt, int64_t rows, int64_t k, int nc, int epi) {
+  // the RoPE and SwiGLU epilogues combine rows (2i, 2i+1), which must sit in one wave
+  const bool pairs = epi == EPI_QKV || epi == EPI_SWIGLU;
   GemvPlan p{};
   p.ncm = nc <= 1 ? 1 : (nc <= 4 ? 4 : 8);
-  p.rows_per_wave = p.ncm == 1 ? 4 : 2;
-  p.waves = 4;
+  p.rows_per_wave = 2;
+  p.waves = 8;
+  if (g_waves == 2 || g_waves == 4 || g_waves == 8) p.waves = g_waves;
   int cw, xq, ns;
   fmt_geom(qt, cw, xq, ns);
   const int64_t nch = k / cw;
   const size_t per_chunk = (size_t)p.ncm * (xq * 16 + ns * 4);
   int64_t max_ch = (int64_t)(LDS_BUDGET / per_chunk);
   if (max_ch < 1) max_ch = 1;
+  const int64_t sb = 256 / cw;  // chunks per 256 weights: splits start on superblock boundaries
+  max_ch = max_ch / sb * sb;
+  if (max_ch < sb) max_ch = sb;
   int ksplit = (int)((nch + max_ch - 1) / max_ch);
   if (ksplit < 1) ksplit = 1;
-  int64_t chs = (nch + ksplit - 1) / ksplit;  // chunks per split
+  int64_t chs = ((nch + ksplit - 1) / ksplit + sb - 1) / sb * sb;  // chunks per split
   p.ks = (int)(chs * cw);
   p.ksplit = (int)((k + p.ks - 1) / p.ks);
   p.lds = (size_t)chs * per_chunk;
   p.part_bytes = p.ksplit > 1 ? (size_t)p.ksplit * nc * rows * sizeof(float) : 0;
+  if (p.ncm == 1) p.rows_per_wave = pick_rows_per_wave(rows, p.waves, p.ksplit, pairs);
+  if (p.ncm == 1 && (g_rows == 1 || g_rows == 2 || g_rows == 4)) p.rows_per_wave = g_rows;
+  if (pairs && p.rows_per_wave < 2) p.rows_per_wave = 2;
   return p;
 }
 
@@ -286,6 +334,8 @@ static hipError_t launch_t(const GemvArgs& a, bool rms, int epi, int ksplit, dim
 template <int QT>
 static hipError_t launch_fmt(const GemvArgs& a, const GemvPlan& p, bool rms, int epi, dim3 grid, dim3 block,
                              hipStream_t st) {
+  if (p.ncm == 1 && p.rows_per_wave == 1) return launch_t<QT, 1, 1>(a, rms, epi, p.ksplit, grid, block, p.lds, st);
+  if (p.ncm == 1 && p.rows_per_wave == 2) return launch_t<QT, 1, 2>(a, rms, epi, p.ksplit, grid, block, p.lds, st);
   if (p.ncm == 1) return launch_t<QT, 1, 4>(a, rms, epi, p.ksplit, grid, block, p.lds, st);
   if (p.ncm == 4) return launch_t<QT, 4, 2>(a, rms, epi, p.ksplit, grid, block, p.lds, st);
   return launch_t<QT, 8, 2>(a, rms, epi, p.ksplit, grid, block, p.lds, st);

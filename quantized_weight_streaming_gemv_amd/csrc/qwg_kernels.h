@@ -42,7 +42,9 @@ struct GemvPlan {
   size_t part_bytes;  // split workspace bytes (0 if ksplit == 1)
 };
 
-GemvPlan plan_gemv(int qt, int64_t rows, int64_t k, int nc);
+// epi: the epilogue the GEMV will run (pairs of rows must share a wave for RoPE and SwiGLU)
+GemvPlan plan_gemv(int qt, int64_t rows, int64_t k, int nc, int epi);
+void set_gemv_geometry(int waves, int rows_per_wave);
 
 // y = W x with prologue (plain x or x = RMSNorm(x; gain, eps)) and epilogue; `part` must hold
 // plan.part_bytes when plan.ksplit > 1.  Returns hipSuccess or the launch error.
@@ -61,7 +63,9 @@ hipError_t launch_rmsnorm(const float* x, const float* g, int64_t n, float eps, 
 hipError_t launch_rope(float* v, int n_heads, const float* table, int pos, hipStream_t st);
 hipError_t launch_swiglu(const float* g, const float* u, int64_t n, float* out, hipStream_t st);
 hipError_t launch_cosine(const float* a, const float* b, int64_t n, float* out, hipStream_t st);
-hipError_t launch_argmax(const float* x, int64_t n, int nc, int64_t x_stride, int32_t* out, hipStream_t st);
+// keys: scratch of nc 64-bit words (cleared by the launch itself)
+hipError_t launch_argmax(const float* x, int64_t n, int nc, int64_t x_stride, int32_t* out, hipStream_t st,
+                         unsigned long long* keys);
 
 struct AttnPlan {
   int T;        // positions per split

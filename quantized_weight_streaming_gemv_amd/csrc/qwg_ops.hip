@@ -4,6 +4,8 @@
 // kernel list of its "Architecture overview": GEMV, RMSNorm, RoPE, SwiGLU, softmax).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "qwg_kernels.h"
 
 namespace qwg {
@@ -193,51 +195,60 @@ hipError_t launch_cosine(const float* a, const float* b, int64_t n, float* out, 
   return hipGetLastError();
 }
 
-// greater-than for (value, index) with NaNs ignored and ties to the lower index
-__device__ __forceinline__ bool am_better(float v, int i, float bv, int bi) {
-  if (v != v) return false;
-  if (bv != bv) return true;
-  return v > bv || (v == bv && i < bi);
+// Greedy choice over many workgroups: each reduces its slice to (value, index) and folds it into a
+// 64-bit key with one atomic max; key = (order-preserving bits of the value) << 32 | ~index, so the
+// largest value wins and, among equal values, the lowest index.  NaNs never win.
+__device__ __forceinline__ unsigned long long am_key(float v, int i) {
+  if (v != v) return 0ull;
+  uint32_t b = __float_as_uint(v);
+  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((unsigned long long)b << 32) | (uint32_t)(~(uint32_t)i);
 }
 
-__global__ void k_argmax(const float* x, int64_t n, int64_t stride, int32_t* out) {
-  __shared__ float shv[16];
-  __shared__ int shi[16];
-  const float* xr = x + (int64_t)blockIdx.x * stride;
-  float bv = __builtin_nanf("");
-  int bi = 0x7FFFFFFF;
-  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
-    const float v = xr[i];
-    if (am_better(v, (int)i, bv, bi)) { bv = v; bi = (int)i; }
+__global__ void k_argmax_clear(unsigned long long* keys, int nc) {
+  if ((int)threadIdx.x < nc) keys[threadIdx.x] = 0ull;
+}
+
+__global__ __launch_bounds__(256) void k_argmax_blocks(const float* x, int64_t n, int64_t stride,
+                                                       unsigned long long* keys) {
+  const float* xr = x + (int64_t)blockIdx.y * stride;
+  unsigned long long best = 0ull;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const unsigned long long k = am_key(xr[i], (int)i);
+    best = k > best ? k : best;
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
-    const float ov = __shfl_xor(bv, off);
-    const int oi = __shfl_xor(bi, off);
-    if (am_better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    const unsigned long long o = __shfl_xor(best, off);
+    best = o > best ? o : best;
   }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  if (lane == 0) { shv[wave] = bv; shi[wave] = bi; }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int w = 1; w < nw; ++w)
-      if (am_better(shv[w], shi[w], bv, bi)) { bv = shv[w]; bi = shi[w]; }
-    out[blockIdx.x] = bi == 0x7FFFFFFF ? 0 : bi;
-  }
+  if ((threadIdx.x & 63) == 0 && best) atomicMax(keys + blockIdx.y, best);
 }
 
-hipError_t launch_argmax(const float* x, int64_t n, int nc, int64_t x_stride, int32_t* out, hipStream_t st) {
-  hipLaunchKernelGGL(k_argmax, dim3(nc), dim3(1024), 0, st, x, n, x_stride, out);
+__global__ void k_argmax_final(const unsigned long long* keys, int nc, int32_t* out) {
+  const int j = threadIdx.x;
+  if (j < nc) out[j] = keys[j] ? (int32_t)(~(uint32_t)(keys[j] & 0xFFFFFFFFull)) : 0;
+}
+
+// keys: nc 64-bit words of scratch
+hipError_t launch_argmax(const float* x, int64_t n, int nc, int64_t x_stride, int32_t* out, hipStream_t st,
+                         unsigned long long* keys) {
+  hipLaunchKernelGGL(k_argmax_clear, dim3(1), dim3(64), 0, st, keys, nc);
+  const int blocks = (int)std::min<int64_t>(256, (n + 1023) / 1024);
+  hipLaunchKernelGGL(k_argmax_blocks, dim3(blocks, nc), dim3(256), 0, st, x, n, x_stride, keys);
+  hipLaunchKernelGGL(k_argmax_final, dim3(1), dim3(64), 0, st, keys, nc, out);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------------------------------------ attention
 //
 // Split over positions (flash-decoding style) so that 8 KV heads still fill 256 CUs: workgroup
-// (g, s) takes KV head g and positions [s*T, (s+1)*T) for all query heads of the group and all
-// columns, writes (max, sum, unnormalised output) per query, and a second kernel merges the
-// splits with the usual log-sum-exp rescaling.  K and V tiles are staged in LDS (K rows padded to
-// 65 words so that lanes reading different positions hit different banks).
+// (g, s) takes KV head g and positions [s*T, s*T + T) for every query head of the group and every
+// column, and writes (max, sum, unnormalised output) per query; a second kernel merges the splits
+// with the usual log-sum-exp rescaling.
+//   scores: lane = position (T = 64), the K row (256 B) is read straight into registers with
+//           16-B loads; queries come from LDS as broadcasts; wave w takes queries w, w+4, ...
+//   output: thread = (2 dimensions, one query slot); V rows are read as coalesced 256-B rows.
 
 struct AttnArgs {
   const float* q;
@@ -253,12 +264,12 @@ struct AttnArgs {
   int64_t out_stride;
 };
 
-constexpr int KROW = HEAD_DIM / 2 + 1;  // padded K row in 32-bit words
+constexpr int ATT_T = 64;
 
 AttnPlan plan_attn(int n_pos, int n_q, int n_kv, int nc) {
   AttnPlan p{};
   const int nqg = nc * (n_q / n_kv);
-  p.T = nqg > 32 ? 32 : 64;
+  p.T = ATT_T;
   const int span = n_pos + nc - 1;
   p.nsplit = (span + p.T - 1) / p.T;
   p.work_bytes = (size_t)n_kv * p.nsplit * nqg * (HEAD_DIM + 2) * sizeof(float);
@@ -268,55 +279,54 @@ AttnPlan plan_attn(int n_pos, int n_q, int n_kv, int nc) {
 __global__ __launch_bounds__(256) void k_attn_part(AttnArgs a) {
   extern __shared__ float sm[];
   const int g = blockIdx.x, s = blockIdx.y;
-  const int G = a.n_q / a.n_kv, NQ = a.nc * G, T = a.T;
+  const int G = a.n_q / a.n_kv, NQ = a.nc * G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float* qs = sm;                                   // [NQ][HEAD_DIM]
-  uint32_t* ks = (uint32_t*)(qs + NQ * HEAD_DIM);   // [T][KROW]
-  uint16_t* vs = (uint16_t*)(ks + T * KROW);        // [T][HEAD_DIM]
-  float* ps = (float*)(vs + T * HEAD_DIM);          // [NQ][T]
-  const int t0 = s * T;
+  float* qs = sm;                      // [NQ][HEAD_DIM]
+  float* ps = qs + NQ * HEAD_DIM;      // [NQ][ATT_T]
+  const int t0 = s * ATT_T;
   const int span = a.n_pos + a.nc - 1;
-  const int tn = min(T, span - t0);                 // positions present in this split
+  const int tn = min(ATT_T, span - t0);
 
-  for (int i = tid; i < NQ * HEAD_DIM; i += blockDim.x) {
-    const int qi = i / HEAD_DIM, d = i % HEAD_DIM;
+  for (int i = tid; i < NQ * (HEAD_DIM / 4); i += blockDim.x) {
+    const int qi = i / (HEAD_DIM / 4), d4 = i % (HEAD_DIM / 4);
     const int n = qi / G, j = qi % G;
-    qs[i] = a.q[(int64_t)n * a.q_stride + (int64_t)(g * G + j) * HEAD_DIM + d];
+    ((float4*)qs)[i] = ((const float4*)(a.q + (int64_t)n * a.q_stride + (int64_t)(g * G + j) * HEAD_DIM))[d4];
   }
-  for (int i = tid; i < T * (HEAD_DIM / 2); i += blockDim.x) {
-    const int t = i / (HEAD_DIM / 2), w = i % (HEAD_DIM / 2);
-    uint32_t kv = 0, vv = 0;
-    if (t < tn) {
-      const int64_t off = (int64_t)(t0 + t) * a.kv_stride + (int64_t)g * HEAD_DIM;
-      kv = ((const uint32_t*)(a.kc + off))[w];
-      vv = ((const uint32_t*)(a.vc + off))[w];
+  // this lane's K row (position t0 + lane) as 64 packed half pairs
+  uint32_t kr[HEAD_DIM / 2];
+  {
+    const int t = min(lane, tn - 1);
+    const uint4* src = (const uint4*)(a.kc + (int64_t)(t0 + t) * a.kv_stride + (int64_t)g * HEAD_DIM);
+#pragma unroll
+    for (int i = 0; i < HEAD_DIM / 8; ++i) {
+      const uint4 v = src[i];
+      kr[4 * i] = v.x;
+      kr[4 * i + 1] = v.y;
+      kr[4 * i + 2] = v.z;
+      kr[4 * i + 3] = v.w;
     }
-    ks[t * KROW + w] = kv;
-    ((uint32_t*)vs)[t * (HEAD_DIM / 2) + w] = vv;
   }
   __syncthreads();
 
-  // scores: wave w takes queries w, w+4, ...; lane t takes position t0 + t (two passes if T = 64 > lanes? no: T <= 64)
   const float scale = 0.08838834764831845f;  // 1/sqrt(128)
   for (int qi = wave; qi < NQ; qi += 4) {
     const int n = qi / G;
-    float sc = -INFINITY;
-    if (lane < tn) {
-      const float* qv = qs + qi * HEAD_DIM;
-      const uint32_t* kr = ks + lane * KROW;
-      float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll 8
-      for (int w = 0; w < HEAD_DIM / 2; ++w) {
-        const uint32_t kk = kr[w];
-        acc0 += qv[2 * w] * half_bits_to_float(kk & 0xFFFFu);
-        acc1 += qv[2 * w + 1] * half_bits_to_float(kk >> 16);
-      }
-      if (t0 + lane < a.n_pos + n) sc = (acc0 + acc1) * scale;
+    const float4* qv = (const float4*)(qs + qi * HEAD_DIM);
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+    for (int i = 0; i < HEAD_DIM / 4; ++i) {
+      const float4 qq = qv[i];
+      a0 += qq.x * half_bits_to_float(kr[2 * i] & 0xFFFFu);
+      a1 += qq.y * half_bits_to_float(kr[2 * i] >> 16);
+      a2 += qq.z * half_bits_to_float(kr[2 * i + 1] & 0xFFFFu);
+      a3 += qq.w * half_bits_to_float(kr[2 * i + 1] >> 16);
     }
+    const bool ok = lane < tn && t0 + lane < a.n_pos + n;
+    const float sc = ok ? ((a0 + a1) + (a2 + a3)) * scale : -INFINITY;
     const float m = wave_max(sc);
-    const float e = (sc == -INFINITY) ? 0.f : __expf(sc - m);
+    const float e = ok ? __expf(sc - m) : 0.f;
     const float l = wave_sum(e);
-    if (lane < T) ps[qi * T + lane] = e;
+    ps[qi * ATT_T + lane] = e;
     if (lane == 0) {
       float* pr = a.part + (((int64_t)g * a.nsplit + s) * NQ + qi) * (HEAD_DIM + 2);
       pr[0] = m;
@@ -325,32 +335,59 @@ __global__ __launch_bounds__(256) void k_attn_part(AttnArgs a) {
   }
   __syncthreads();
 
-  // unnormalised output: thread takes dimension d = tid % 128 for queries tid/128, +2, ...
-  const int d = tid % HEAD_DIM;
-  for (int qi = tid / HEAD_DIM; qi < NQ; qi += blockDim.x / HEAD_DIM) {
-    const float* pr = ps + qi * T;
-    float o = 0.f;
-    for (int t = 0; t < tn; ++t) o += pr[t] * half_bits_to_float(vs[t * HEAD_DIM + d]);
-    a.part[(((int64_t)g * a.nsplit + s) * NQ + qi) * (HEAD_DIM + 2) + 2 + d] = o;
+  // unnormalised output: thread = dimensions (2c, 2c+1), query slot = tid / 64 (+4, +8, ...)
+  const int c = tid & 63;
+  for (int qb = tid >> 6; qb < NQ; qb += 4) {
+    const float* pr = ps + qb * ATT_T;
+    float o0 = 0.f, o1 = 0.f;
+    const uint32_t* vrow = (const uint32_t*)(a.vc + (int64_t)t0 * a.kv_stride + (int64_t)g * HEAD_DIM) + c;
+    const int64_t vstep = a.kv_stride / 2;
+#pragma unroll 8
+    for (int t = 0; t < tn; ++t) {
+      const uint32_t vv = vrow[t * vstep];
+      const float p = pr[t];
+      o0 += p * half_bits_to_float(vv & 0xFFFFu);
+      o1 += p * half_bits_to_float(vv >> 16);
+    }
+    float* dst = a.part + (((int64_t)g * a.nsplit + s) * NQ + qb) * (HEAD_DIM + 2) + 2;
+    dst[2 * c] = o0;
+    dst[2 * c + 1] = o1;
   }
 }
 
-__global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a) {
-  const int g = blockIdx.x, qi = blockIdx.y, d = threadIdx.x;
+// one workgroup per (kv head, query): split statistics through LDS, then each thread merges two
+// output dimensions over all splits
+__global__ __launch_bounds__(64) void k_attn_combine(AttnArgs a) {
+  __shared__ float fs[1024];
+  __shared__ float Ls;
+  const int g = blockIdx.x, qi = blockIdx.y, tid = threadIdx.x;
   const int G = a.n_q / a.n_kv, NQ = a.nc * G;
   const float* base = a.part + ((int64_t)g * a.nsplit * NQ + qi) * (HEAD_DIM + 2);
   const int64_t sstride = (int64_t)NQ * (HEAD_DIM + 2);
   float M = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, base[s * sstride]);
-  float L = 0.f, O = 0.f;
-  for (int s = 0; s < a.nsplit; ++s) {
-    const float* pr = base + s * sstride;
-    const float f = pr[0] == -INFINITY ? 0.f : __expf(pr[0] - M);
-    L += f * pr[1];
-    O += f * pr[2 + d];
+  for (int s = tid; s < a.nsplit; s += 64) M = fmaxf(M, base[s * sstride]);
+  M = wave_max(M);
+  float L = 0.f;
+  for (int s = tid; s < a.nsplit; s += 64) {
+    const float m = base[s * sstride];
+    const float f = m == -INFINITY ? 0.f : __expf(m - M);
+    fs[s] = f;
+    L += f * base[s * sstride + 1];
   }
+  L = wave_sum(L);
+  if (tid == 0) Ls = L;
+  __syncthreads();
+  float o0 = 0.f, o1 = 0.f;
+#pragma unroll 4
+  for (int s = 0; s < a.nsplit; ++s) {
+    const float2 v = ((const float2*)(base + s * sstride + 2))[tid];
+    o0 += fs[s] * v.x;
+    o1 += fs[s] * v.y;
+  }
+  const float inv = 1.0f / Ls;
   const int n = qi / G, j = qi % G;
-  a.out[(int64_t)n * a.out_stride + (int64_t)(g * G + j) * HEAD_DIM + d] = O / L;
+  float2* dst = (float2*)(a.out + (int64_t)n * a.out_stride + (int64_t)(g * G + j) * HEAD_DIM);
+  dst[tid] = make_float2(o0 * inv, o1 * inv);
 }
 
 hipError_t launch_attn(const float* q, int64_t q_stride, const uint16_t* kc, const uint16_t* vc, int64_t kv_stride,
@@ -372,12 +409,12 @@ hipError_t launch_attn(const float* q, int64_t q_stride, const uint16_t* kc, con
   a.out = out;
   a.out_stride = out_stride;
   const int NQ = nc * (n_q / n_kv);
-  const size_t lds = (size_t)NQ * HEAD_DIM * 4 + (size_t)p.T * KROW * 4 + (size_t)p.T * HEAD_DIM * 2 +
-                     (size_t)NQ * p.T * 4;
+  if (p.nsplit > 1024) return hipErrorInvalidValue;
+  const size_t lds = (size_t)NQ * HEAD_DIM * 4 + (size_t)NQ * ATT_T * 4;
   hipLaunchKernelGGL(k_attn_part, dim3(n_kv, p.nsplit), dim3(256), lds, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_attn_combine, dim3(n_kv, NQ), dim3(HEAD_DIM), 0, st, a);
+  hipLaunchKernelGGL(k_attn_combine, dim3(n_kv, NQ), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 

@@ -169,3 +169,18 @@ def test_context_overflow_is_an_error(qwg):
     m.truncate(wl.n_prior)
     m.decode_step(wl.first_token())
     m.close()
+
+
+@pytest.mark.parametrize("geom", [(4, 1), (8, 1), (2, 2), (8, 4)], ids=lambda g: "w%d_r%d" % g)
+def test_decode_under_launch_geometries(qwg, geom):
+    """Every launch geometry computes the same step (the pair epilogues need two rows per wave)."""
+    from quantized_weight_streaming_gemv_amd import ops
+    wl = synth.tiny(synth.Q4_K, synth.Q6_K, wid=210)
+    ops.set_gemv_geometry(*geom)
+    try:
+        m, om, records = run_pair(qwg, wl, 2, capture=False)
+        for g_next, g_logits, _, r in records:
+            assert rel_l2(g_logits, r["logits"]) < 2e-3
+        m.close()
+    finally:
+        ops.set_gemv_geometry(0, 0)
