@@ -58,7 +58,7 @@ size_t align_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
 
 // Scratch of the kernel-level entry points that need it (GEMV K-split partials, argmax keys):
 // allocated on first use per device and purpose, grown when needed, freed at exit.
-enum { WS_GEMV = 0, WS_ARGMAX = 1, WS_KINDS = 2 };
+enum { WS_GEMV = 0, WS_ARGMAX = 1, WS_DIGITS = 2, WS_KINDS = 3 };
 struct KernelWorkspace {
   void* p[64][WS_KINDS] = {};
   size_t n[64][WS_KINDS] = {};
@@ -116,7 +116,8 @@ struct qwg_model {
   std::vector<LayerPlan> L;
   MatPlan embed{}, head{};
   size_t g_final = 0, rope = 0, h = 0, hin = 0, qb = 0, ob = 0, act = 0, logits = 0, amax = 0, keys = 0, cosv = 0;
-  size_t capture = 0, part = 0, attn = 0, slot[2] = {0, 0}, staging = 0;
+  size_t capture = 0, part = 0, attn = 0, slot[2] = {0, 0}, staging = 0, xd = 0, rsb = 0;
+  int64_t xd_col = 0;  // bytes of one column of activation digits
   size_t part_bytes = 0, attn_bytes = 0, staging_bytes = 0, image_max = 0, total = 0;
   int n_streamed = 0;
   uint8_t* arena = nullptr;
@@ -207,6 +208,10 @@ static int plan_model(qwg_model* m) {
   m->keys = take((size_t)MAX_COLS * 8);
   m->cosv = take((size_t)d.n_layers * 4);
   m->capture = take((size_t)(d.n_layers + 1) * H * 4);
+  const int64_t kmax = std::max<int64_t>(std::max<int64_t>(H, F), (int64_t)d.n_q * d.head_dim);
+  m->xd_col = digit_bytes(kmax);
+  m->xd = take((size_t)C * m->xd_col);
+  m->rsb = take((size_t)MAX_COLS * 4);
   size_t pb = 0;
   for (int nc : {1, C}) {
     const int64_t shapes[5][2] = {{(int64_t)(d.n_q + 2 * d.n_kv) * d.head_dim, H},
@@ -291,17 +296,22 @@ static int64_t gemv_alg_bytes(const MatPlan& p, int nc, int out_rw) {
   return p.canon_bytes + (int64_t)nc * p.L.k * 4 + (int64_t)nc * p.L.rows * 4 * out_rw;
 }
 
+// Digitize the GEMV input (with the RMSNorm gain when given), then run the GEMV; with timing on for
+// this weight class, HIP events on the compute stream bracket the GEMV kernel(s).
 static int gemv(qwg_model* m, int tensor_class, int qt, const MatView& w, const MatPlan& mp, const float* x,
-                int64_t x_stride, const float* gain, bool rms, int nc, int epi, const EpiArgs& e) {
+                int64_t x_stride, const float* gain, int nc, int epi, EpiArgs e) {
   const GemvPlan gp = plan_gemv(qt, w.rows, mp.L.k, nc, epi);
   if (gp.part_bytes > m->part_bytes) return fail(QWG_E_NOMEM, "split workspace too small");
+  QWG_HIP(launch_digitize(x, x_stride, gain, m->d.rms_eps, mp.L.k, nc, qt, m->arena + m->xd, m->xd_col,
+                          gain ? m->f(m->rsb) : nullptr, m->cs));
+  e.rs = gain ? m->f(m->rsb) : nullptr;
   const bool timed = m->timing_tensor == tensor_class;
   if (timed) {
     hipEvent_t e0 = pool_event(m->tev, m->tev_used);
     if (!e0) return fail(QWG_E_HIP, "hipEventCreate failed");
     QWG_HIP(hipEventRecord(e0, m->cs));
   }
-  QWG_HIP(launch_gemv(qt, w, mp.L.k, x, x_stride, gain, m->d.rms_eps, rms, nc, epi, e, m->f(m->part), m->cs, gp));
+  QWG_HIP(launch_gemv(qt, w, mp.L.k, m->arena + m->xd, m->xd_col, nc, epi, e, m->f(m->part), m->cs, gp));
   if (timed) {
     hipEvent_t e1 = pool_event(m->tev, m->tev_used);
     if (!e1) return fail(QWG_E_HIP, "hipEventCreate failed");
@@ -327,7 +337,7 @@ static int layer_kernels(qwg_model* m, int l, const uint8_t* base, int nc, int p
   e.kc = (uint16_t*)(m->arena + P.kc);
   e.vc = (uint16_t*)(m->arena + P.vc);
   e.kv_stride = KR;
-  if ((rc = gemv(m, QWG_T_WQ, d.qtype_attn, view_at(base, P.qkv), P.qkv, m->f(m->h), H, m->f(P.g_attn), true, nc,
+  if ((rc = gemv(m, QWG_T_WQ, d.qtype_attn, view_at(base, P.qkv), P.qkv, m->f(m->h), H, m->f(P.g_attn), nc,
                  EPI_QKV, e)))
     return rc;
   const AttnPlan ap = plan_attn(pos + 1, d.n_q, d.n_kv, nc);
@@ -337,17 +347,16 @@ static int layer_kernels(qwg_model* m, int l, const uint8_t* base, int nc, int p
   EpiArgs r{};
   r.y = m->f(m->h);
   r.y_stride = H;
-  if ((rc = gemv(m, QWG_T_WO, d.qtype_attn, view_at(base, P.o), P.o, m->f(m->ob), QR, nullptr, false, nc, EPI_RESID,
-                 r)))
+  if ((rc = gemv(m, QWG_T_WO, d.qtype_attn, view_at(base, P.o), P.o, m->f(m->ob), QR, nullptr, nc, EPI_RESID, r)))
     return rc;
   EpiArgs s{};
   s.y = m->f(m->act);
   s.y_stride = F;
-  if ((rc = gemv(m, QWG_T_WGATE, d.qtype_ffn, view_at(base, P.gu), P.gu, m->f(m->h), H, m->f(P.g_ffn), true, nc,
+  if ((rc = gemv(m, QWG_T_WGATE, d.qtype_ffn, view_at(base, P.gu), P.gu, m->f(m->h), H, m->f(P.g_ffn), nc,
                  EPI_SWIGLU, s)))
     return rc;
-  if ((rc = gemv(m, QWG_T_WDOWN, d.qtype_ffn, view_at(base, P.down), P.down, m->f(m->act), F, nullptr, false, nc,
-                 EPI_RESID, r)))
+  if ((rc = gemv(m, QWG_T_WDOWN, d.qtype_ffn, view_at(base, P.down), P.down, m->f(m->act), F, nullptr, nc, EPI_RESID,
+                 r)))
     return rc;
   return QWG_OK;
 }
@@ -418,7 +427,7 @@ static int run_pass(qwg_model* m, const int32_t* toks, int nc, int pos, int n_ru
   e.y = m->f(m->logits);
   e.y_stride = d.vocab;
   if (int rc = gemv(m, QWG_T_HEAD, d.qtype_head, view_at(m->arena, m->head), m->head, m->f(m->h), H, m->f(m->g_final),
-                    true, nc, EPI_STORE, e))
+                    nc, EPI_STORE, e))
     return rc;
   QWG_HIP(launch_argmax(m->f(m->logits), d.vocab, nc, d.vocab, (int32_t*)(m->arena + m->amax), m->cs,
                         (unsigned long long*)(m->arena + m->keys)));
@@ -489,11 +498,14 @@ int qwg_gemv(int qtype, const void* d_packed, int64_t rows, int64_t k, const flo
   const GemvPlan p = plan_gemv(qtype, rows, k, n_cols, EPI_STORE);
   void* part = nullptr;
   if (p.part_bytes) QWG_HIP(kernel_workspace(WS_GEMV, p.part_bytes, &part));
+  void* xd = nullptr;
+  QWG_HIP(kernel_workspace(WS_DIGITS, (size_t)n_cols * digit_bytes(k), &xd));
+  QWG_HIP(launch_digitize(d_x, k, nullptr, 0.f, k, n_cols, qtype, xd, digit_bytes(k), nullptr, (hipStream_t)stream));
   EpiArgs e{};
   e.y = d_y;
   e.y_stride = rows;
-  QWG_HIP(launch_gemv(qtype, make_view(d_packed, L), k, d_x, k, nullptr, 0.f, false, n_cols, EPI_STORE, e,
-                      (float*)part, (hipStream_t)stream, p));
+  QWG_HIP(launch_gemv(qtype, make_view(d_packed, L), k, xd, digit_bytes(k), n_cols, EPI_STORE, e, (float*)part,
+                      (hipStream_t)stream, p));
   return QWG_OK;
 }
 

@@ -27,6 +27,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 namespace qwg {
@@ -225,13 +226,116 @@ __host__ __device__ inline T ld(const uint8_t* p) {
   return *(const T*)p;
 }
 
+// ---------------------------------------------------------------------------- activation digits
+//
+// The GEMV never multiplies fp32 activations by converted weights.  Instead every 32-element chunk
+// of the activation becomes a block fixed-point integer vector: one shared power-of-two scale per
+// chunk, x_fix = rint(x * 2^s) with |x_fix| < 2^22 (24-bit two's-complement range, so the largest
+// element of the chunk keeps 22 significant bits), split into balanced digits:
+//   nibble digits (Q4_0, Q4_K): x_fix = sum_l d_l 16^l, d_l in [-8, 7], l = 0..5
+//   byte digits (Q5_K, Q6_K, Q8_0): x_fix = sum_l d_l 256^l, d_l in [-128, 127], l = 0..2
+// Adding 0x888888 (or 0x808080) maps the balanced digits to the plain base-16 (base-256) digits of
+// the sum, so each digit is a field extract followed by flipping its top bit.  The weight quants are
+// then integers too, and each dot product is a sum of exact integer products (v_dot8_i32_i4 /
+// v_dot4_i32_i8), recombined per chunk in fp32 and scaled by 2^-s.
+//
+// Digit words of a chunk (24 x 32 bits) are laid out to match the packed quant words:
+//   nibble: word m*6 + l, nibble 2b+h = digit l of element 16h + 4m + b   (h = 0 low, 1 high nibble)
+//   byte:   word (h*4 + m)*3 + l, byte b = digit l of element 16h + 4m + b
+// followed by a ChunkDesc (2^-s and the integer sums of x_fix over the chunk and its two halves).
+
+enum DigitKind : int { DIG_NIB = 0, DIG_BYTE = 1 };
+constexpr int XCHUNK = 32;         // activation elements per digit chunk
+constexpr int DIG_WORDS = 24;      // digit words per chunk
+constexpr int DIG_CHUNK_WORDS = 28;  // digit words + ChunkDesc
+
+__host__ __device__ inline int digit_kind(int qt) { return (qt == Q4_K || qt == Q4_0) ? DIG_NIB : DIG_BYTE; }
+
+struct ChunkDesc {
+  float inv_scale;  // 2^-s
+  int32_t sum;      // sum of x_fix over the chunk
+  int32_t sumA;     // over elements 0..15
+  int32_t sumB;     // over elements 16..31
+};
+
+// Digits and descriptor of one 32-element chunk (x already multiplied by its gain if any).
+__host__ __device__ inline void digitize_chunk(const float* x, int kind, uint32_t* dig, ChunkDesc* desc) {
+  float mx = 0.f;
+  for (int e = 0; e < XCHUNK; ++e) mx = fmaxf(mx, fabsf(x[e]));
+  int s = 0;
+  if (mx > 0.f && mx == mx) {
+    s = 21 - ilogbf(mx);  // mx * 2^s in [2^21, 2^22)
+    s = s > 100 ? 100 : (s < -100 ? -100 : s);
+  }
+  int32_t xf[XCHUNK];
+  int32_t sa = 0, sb = 0;
+  for (int e = 0; e < XCHUNK; ++e) {
+    const float v = ldexpf(x[e], s);
+    xf[e] = (v == v) ? (int32_t)rintf(v) : 0;
+    if (e < 16) sa += xf[e];
+    else sb += xf[e];
+  }
+  for (int i = 0; i < DIG_WORDS; ++i) dig[i] = 0;
+  for (int e = 0; e < XCHUNK; ++e) {
+    const int h = e >> 4, m = (e >> 2) & 3, b = e & 3;
+    if (kind == DIG_NIB) {
+      const uint32_t u = (uint32_t)(xf[e] + 0x888888);
+      for (int l = 0; l < 6; ++l) dig[m * 6 + l] |= (((u >> (4 * l)) & 15u) ^ 8u) << (4 * (2 * b + h));
+    } else {
+      const uint32_t u = (uint32_t)(xf[e] + 0x808080);
+      for (int l = 0; l < 3; ++l) dig[(h * 4 + m) * 3 + l] |= (((u >> (8 * l)) & 255u) ^ 128u) << (8 * b);
+    }
+  }
+  desc->inv_scale = ldexpf(1.0f, -s);
+  desc->sum = sa + sb;
+  desc->sumA = sa;
+  desc->sumB = sb;
+}
+
+// exact integer dot products (device: one v_dot8_i32_i4 / v_dot4_i32_i8 each)
+__host__ __device__ inline int32_t sdot8(uint32_t a, uint32_t b, int32_t c) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_sdot8((int)a, (int)b, c, false);
+#else
+  for (int i = 0; i < 8; ++i) {
+    int x = (int)((a >> (4 * i)) & 15u), y = (int)((b >> (4 * i)) & 15u);
+    x = x >= 8 ? x - 16 : x;
+    y = y >= 8 ? y - 16 : y;
+    c += x * y;
+  }
+  return c;
+#endif
+}
+__host__ __device__ inline int32_t sdot4(uint32_t a, uint32_t b, int32_t c) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+#else
+  for (int i = 0; i < 4; ++i) c += (int)(int8_t)(uint8_t)(a >> (8 * i)) * (int)(int8_t)(uint8_t)(b >> (8 * i));
+  return c;
+#endif
+}
+
+// sum_l 16^l D_l (six nibble levels) and sum_l 256^l D_l (three byte levels) in fp32
+__host__ __device__ inline float combine_nib(const int32_t* D) {
+  const int32_t lo = D[0] + D[1] * 16 + D[2] * 256, hi = D[3] + D[4] * 16 + D[5] * 256;
+  return __builtin_fmaf(4096.0f, (float)hi, (float)lo);
+}
+__host__ __device__ inline float combine_byte(const int32_t* D) {
+  return __builtin_fmaf(65536.0f, (float)D[2], (float)(D[0] + D[1] * 256));
+}
+
 // ---------------------------------------------------------------------------- per-format chunk codecs
 //
 // Each Fmt<QT> provides
-//   CW, XQ (float4s of activation per chunk), NSUM (activation sums per chunk it needs)
+//   CW (weights per chunk)
 //   Raw load(view, row, chunk)          -- the chunk's quant bytes and scale data
 //   decode(raw, chunk, w[CW])           -- exact fp32 weights in chunk order (for dequantize);
 //                                          a zero weight is +0 ("+ 0.0f" turns -0 into +0)
+//   U unpack(raw, chunk, sub)           -- integer quant words for the dot plus the chunk's fp32
+//                                          scale coefficients (sub = chunk & 7, its place in the
+//                                          256-weight superblock)
+//   float dotu(u, digits, desc)         -- sum_e w_e x_e of the chunk from exact integer dot
+//                                          products with the activation digits
 //   dot<NC>(raw, chunk, sub, nc, X, S, acc)
 //                                       -- acc[n] += sum_e w_e x[n][e] without forming w_e (sub =
 //                                          chunk & 7, the chunk's place in its superblock):
@@ -245,7 +349,7 @@ struct Fmt;
 
 template <>
 struct Fmt<Q8_0> {
-  static constexpr int CW = 16, XQ = 4, NSUM = 0;
+  static constexpr int CW = 16;
   struct Raw {
     uint4 q;
     uint32_t d;
@@ -262,71 +366,36 @@ struct Fmt<Q8_0> {
     for (int m = 0; m < 4; ++m)
       for (int b = 0; b < 4; ++b) w[4 * m + b] = d * sbyte(q[m], b) + 0.0f;
   }
-  template <int NC, class XF, class SF>
-  __host__ __device__ static void dot(const Raw& r, int, int, int nc, XF X, SF, float* acc) {
-    const float d = half_bits_to_float(r.d);
-    const uint32_t q[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
-    float f[16];
+  // Integer form of a chunk: quant words ready for the integer dot plus its scale coefficients.
+  struct U {
+    uint32_t w[4];
+    float d;
+    int h;  // which half of the 32-element activation chunk this 16-weight chunk covers
+  };
+  __host__ __device__ static U unpack(const Raw& r, int c, int) {
+    U u;
+    u.w[0] = r.q.x;
+    u.w[1] = r.q.y;
+    u.w[2] = r.q.z;
+    u.w[3] = r.q.w;
+    u.d = half_bits_to_float(r.d);
+    u.h = c & 1;
+    return u;
+  }
+  // dig: the 12 digit words of this half (words 12h .. 12h+11 of the activation chunk)
+  __host__ __device__ static float dotu(const U& u, const uint32_t* dig, const ChunkDesc& ds) {
+    int32_t D[3] = {0, 0, 0};
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) f[4 * m + b] = sbyte(q[m], b);
-#pragma unroll
-    for (int n = 0; n < NC; ++n) {
-      if (n >= nc) break;
-      float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const float4 x = X(n, m);
-        s0 += f[4 * m + 0] * x.x;
-        s1 += f[4 * m + 1] * x.y;
-        s0 += f[4 * m + 2] * x.z;
-        s1 += f[4 * m + 3] * x.w;
-      }
-      acc[n] += d * (s0 + s1);
-    }
+      for (int l = 0; l < 3; ++l) D[l] = sdot4(u.w[m], dig[m * 3 + l], D[l]);
+    return ds.inv_scale * (u.d * combine_byte(D));
   }
 };
 
-// Q4_0 and Q4_K share the nibble word decode: word m -> weights 4m..4m+3 (low nibbles) and
-// 16+4m..16+4m+3 (high nibbles, kept as 16 q so only one mask is needed; scaled back by 1/16).
-template <int NC, class XF>
-__host__ __device__ inline void nibble_dots(const uint4& qv, int nc, XF X, float* lo, float* hi) {
-  const uint32_t q[4] = {qv.x, qv.y, qv.z, qv.w};
-  float fl[16], fh[16];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const uint32_t l = opaque(q[m] & 0x0F0F0F0Fu), h = opaque(q[m] & 0xF0F0F0F0u);
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      fl[4 * m + b] = ubyte(l, b);
-      fh[4 * m + b] = ubyte(h, b);
-    }
-  }
-#pragma unroll
-  for (int n = 0; n < NC; ++n) {
-    if (n >= nc) break;
-    float sl = 0.f, sh = 0.f;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const float4 xa = X(n, m), xb = X(n, 4 + m);
-      sl += fl[4 * m + 0] * xa.x;
-      sh += fh[4 * m + 0] * xb.x;
-      sl += fl[4 * m + 1] * xa.y;
-      sh += fh[4 * m + 1] * xb.y;
-      sl += fl[4 * m + 2] * xa.z;
-      sh += fh[4 * m + 2] * xb.z;
-      sl += fl[4 * m + 3] * xa.w;
-      sh += fh[4 * m + 3] * xb.w;
-    }
-    lo[n] = sl;
-    hi[n] = sh * 0.0625f;
-  }
-}
-
 template <>
 struct Fmt<Q4_0> {
-  static constexpr int CW = 32, XQ = 8, NSUM = 1;
+  static constexpr int CW = 32;
   struct Raw {
     uint4 q;
     uint32_t d;
@@ -347,22 +416,32 @@ struct Fmt<Q4_0> {
         w[16 + 4 * m + b] = d * (float)((byte >> 4) - 8) + 0.0f;
       }
   }
-  template <int NC, class XF, class SF>
-  __host__ __device__ static void dot(const Raw& r, int, int, int nc, XF X, SF S, float* acc) {
-    const float d = half_bits_to_float(r.d);
-    float lo[NC], hi[NC];
-    nibble_dots<NC>(r.q, nc, X, lo, hi);
+  struct U {
+    uint32_t w[4];
+    float d;
+  };
+  __host__ __device__ static U unpack(const Raw& r, int, int) {
+    U u;
+    u.w[0] = r.q.x ^ 0x88888888u;  // q - 8 as signed nibbles
+    u.w[1] = r.q.y ^ 0x88888888u;
+    u.w[2] = r.q.z ^ 0x88888888u;
+    u.w[3] = r.q.w ^ 0x88888888u;
+    u.d = half_bits_to_float(r.d);
+    return u;
+  }
+  __host__ __device__ static float dotu(const U& u, const uint32_t* dig, const ChunkDesc& ds) {
+    int32_t D[6] = {0, 0, 0, 0, 0, 0};
 #pragma unroll
-    for (int n = 0; n < NC; ++n) {
-      if (n >= nc) break;
-      acc[n] += d * ((lo[n] + hi[n]) - 8.0f * S(n, 0));
-    }
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int l = 0; l < 6; ++l) D[l] = sdot8(u.w[m], dig[m * 6 + l], D[l]);
+    return ds.inv_scale * (u.d * combine_nib(D));
   }
 };
 
 template <>
 struct Fmt<Q4_K> {
-  static constexpr int CW = 32, XQ = 8, NSUM = 1;
+  static constexpr int CW = 32;
   struct Raw {
     uint4 q;
     uint4 h;  // d | dmin << 16, S[0..3], S[4..7], S[8..11]
@@ -390,23 +469,35 @@ struct Fmt<Q4_K> {
         w[16 + 4 * m + b] = __builtin_fmaf(dsc, (float)(byte >> 4), -dmm) + 0.0f;
       }
   }
-  template <int NC, class XF, class SF>
-  __host__ __device__ static void dot(const Raw& r, int, int sub, int nc, XF X, SF S, float* acc) {
+  struct U {
+    uint32_t w[4];
+    float c0, c1;  // sum w x = c0 * sum (q-8) x + c1 * sum x
+  };
+  __host__ __device__ static U unpack(const Raw& r, int, int sub) {
     float dsc, dmm;
     coef(r, sub, dsc, dmm);
-    float lo[NC], hi[NC];
-    nibble_dots<NC>(r.q, nc, X, lo, hi);
+    U u;
+    u.w[0] = r.q.x ^ 0x88888888u;
+    u.w[1] = r.q.y ^ 0x88888888u;
+    u.w[2] = r.q.z ^ 0x88888888u;
+    u.w[3] = r.q.w ^ 0x88888888u;
+    u.c0 = dsc;
+    u.c1 = 8.0f * dsc - dmm;
+    return u;
+  }
+  __host__ __device__ static float dotu(const U& u, const uint32_t* dig, const ChunkDesc& ds) {
+    int32_t D[6] = {0, 0, 0, 0, 0, 0};
 #pragma unroll
-    for (int n = 0; n < NC; ++n) {
-      if (n >= nc) break;
-      acc[n] += dsc * (lo[n] + hi[n]) - dmm * S(n, 0);
-    }
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int l = 0; l < 6; ++l) D[l] = sdot8(u.w[m], dig[m * 6 + l], D[l]);
+    return ds.inv_scale * __builtin_fmaf(u.c0, combine_nib(D), u.c1 * (float)ds.sum);
   }
 };
 
 template <>
 struct Fmt<Q5_K> {
-  static constexpr int CW = 32, XQ = 8, NSUM = 1;
+  static constexpr int CW = 32;
   struct Raw {
     uint4 q;
     uint4 h;
@@ -442,46 +533,37 @@ struct Fmt<Q5_K> {
       }
     }
   }
-  template <int NC, class XF, class SF>
-  __host__ __device__ static void dot(const Raw& r, int, int sub, int nc, XF X, SF S, float* acc) {
+  struct U {
+    uint32_t lo[4], hi[4];  // 5-bit quants as bytes
+    float c0, c1;           // sum w x = c0 * sum q x + c1 * sum x
+  };
+  __host__ __device__ static U unpack(const Raw& r, int, int sub) {
     float dsc, dmm;
     Fmt<Q4_K>::Raw rr{r.q, r.h};
     Fmt<Q4_K>::coef(rr, sub, dsc, dmm);
-    float fl[16], fh[16];
+    U u;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      uint32_t lo, hi;
-      words(r, m, lo, hi);
+    for (int m = 0; m < 4; ++m) words(r, m, u.lo[m], u.hi[m]);
+    u.c0 = dsc;
+    u.c1 = -dmm;
+    return u;
+  }
+  __host__ __device__ static float dotu(const U& u, const uint32_t* dig, const ChunkDesc& ds) {
+    int32_t D[3] = {0, 0, 0};
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        fl[4 * m + b] = ubyte(lo, b);
-        fh[4 * m + b] = ubyte(hi, b);
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int l = 0; l < 3; ++l) {
+        D[l] = sdot4(u.lo[m], dig[(0 * 4 + m) * 3 + l], D[l]);
+        D[l] = sdot4(u.hi[m], dig[(1 * 4 + m) * 3 + l], D[l]);
       }
-    }
-#pragma unroll
-    for (int n = 0; n < NC; ++n) {
-      if (n >= nc) break;
-      float sl = 0.f, sh = 0.f;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const float4 xa = X(n, m), xb = X(n, 4 + m);
-        sl += fl[4 * m + 0] * xa.x;
-        sh += fh[4 * m + 0] * xb.x;
-        sl += fl[4 * m + 1] * xa.y;
-        sh += fh[4 * m + 1] * xb.y;
-        sl += fl[4 * m + 2] * xa.z;
-        sh += fh[4 * m + 2] * xb.z;
-        sl += fl[4 * m + 3] * xa.w;
-        sh += fh[4 * m + 3] * xb.w;
-      }
-      acc[n] += dsc * (sl + sh) - dmm * S(n, 0);
-    }
+    return ds.inv_scale * __builtin_fmaf(u.c0, combine_byte(D), u.c1 * (float)ds.sum);
   }
 };
 
 template <>
 struct Fmt<Q6_K> {
-  static constexpr int CW = 32, XQ = 8, NSUM = 2;
+  static constexpr int CW = 32;
   struct Raw {
     uint4 q;
     uint2 qh;
@@ -519,40 +601,32 @@ struct Fmt<Q6_K> {
       }
     }
   }
-  template <int NC, class XF, class SF>
-  __host__ __device__ static void dot(const Raw& r, int, int, int nc, XF X, SF S, float* acc) {
+  struct U {
+    uint32_t lo[4], hi[4];  // unsigned 6-bit quants as bytes (weights 0..15 and 16..31)
+    float dA, dB;           // d * sc of the two 16-weight sub-blocks
+  };
+  __host__ __device__ static U unpack(const Raw& r, int, int) {
     const float d = half_bits_to_float(r.d);
-    const float dA = d * (float)(int8_t)(uint8_t)(r.sc & 0xFFu);
-    const float dB = d * (float)(int8_t)(uint8_t)((r.sc >> 8) & 0xFFu);
-    float fl[16], fh[16];
+    U u;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      uint32_t lo, hi;
-      words(r, m, lo, hi);
+    for (int m = 0; m < 4; ++m) words(r, m, u.lo[m], u.hi[m]);
+    u.dA = d * (float)(int8_t)(uint8_t)(r.sc & 0xFFu);
+    u.dB = d * (float)(int8_t)(uint8_t)((r.sc >> 8) & 0xFFu);
+    return u;
+  }
+  __host__ __device__ static float dotu(const U& u, const uint32_t* dig, const ChunkDesc& ds) {
+    int32_t A[3] = {0, 0, 0}, B[3] = {0, 0, 0};
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        fl[4 * m + b] = ubyte(lo, b);
-        fh[4 * m + b] = ubyte(hi, b);
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int l = 0; l < 3; ++l) {
+        A[l] = sdot4(u.lo[m], dig[(0 * 4 + m) * 3 + l], A[l]);
+        B[l] = sdot4(u.hi[m], dig[(1 * 4 + m) * 3 + l], B[l]);
       }
-    }
-#pragma unroll
-    for (int n = 0; n < NC; ++n) {
-      if (n >= nc) break;
-      float sl = 0.f, sh = 0.f;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const float4 xa = X(n, m), xb = X(n, 4 + m);
-        sl += fl[4 * m + 0] * xa.x;
-        sh += fh[4 * m + 0] * xb.x;
-        sl += fl[4 * m + 1] * xa.y;
-        sh += fh[4 * m + 1] * xb.y;
-        sl += fl[4 * m + 2] * xa.z;
-        sh += fh[4 * m + 2] * xb.z;
-        sl += fl[4 * m + 3] * xa.w;
-        sh += fh[4 * m + 3] * xb.w;
-      }
-      acc[n] += dA * (sl - 32.0f * S(n, 0)) + dB * (sh - 32.0f * S(n, 1));
-    }
+    // sum d sc (q - 32) x over the two 16-weight sub-blocks of the chunk
+    const float tA = combine_byte(A) - 32.0f * (float)ds.sumA;
+    const float tB = combine_byte(B) - 32.0f * (float)ds.sumB;
+    return ds.inv_scale * __builtin_fmaf(u.dA, tA, u.dB * tB);
   }
 };
 

@@ -22,6 +22,7 @@ enum Epi : int {
 };
 
 struct EpiArgs {
+  const float* rs;       // per-column factor applied before the epilogue (RMSNorm 1/rms), or null
   float* y;
   int64_t y_stride;      // floats between columns of y
   const float* rope;     // [max_ctx][HEAD_DIM/2] (cos, sin) pairs
@@ -46,11 +47,18 @@ struct GemvPlan {
 GemvPlan plan_gemv(int qt, int64_t rows, int64_t k, int nc, int epi);
 void set_gemv_geometry(int waves, int rows_per_wave);
 
-// y = W x with prologue (plain x or x = RMSNorm(x; gain, eps)) and epilogue; `part` must hold
+// Bytes of the activation digits of one column of length k (28 words per 32 elements).
+inline int64_t digit_bytes(int64_t k) { return k / XCHUNK * DIG_CHUNK_WORDS * 4; }
+
+// Digits of nc activation columns (x: [nc][x_stride] fp32) for a GEMV over weights of type qt;
+// with a gain vector, digits of gain * x and rs[n] = RMSNorm scale of column n.
+hipError_t launch_digitize(const float* x, int64_t x_stride, const float* gain, float eps, int64_t k, int nc, int qt,
+                           void* out, int64_t out_stride_bytes, float* rs, hipStream_t st);
+
+// y = W x from activation digits xd (column stride in bytes) with an epilogue; `part` must hold
 // plan.part_bytes when plan.ksplit > 1.  Returns hipSuccess or the launch error.
-hipError_t launch_gemv(int qt, const MatView& w, int64_t k, const float* x, int64_t x_stride, const float* gain,
-                       float eps, bool rms, int nc, int epi, const EpiArgs& e, float* part, hipStream_t st,
-                       const GemvPlan& plan);
+hipError_t launch_gemv(int qt, const MatView& w, int64_t k, const void* xd, int64_t xd_stride_bytes, int nc, int epi,
+                       const EpiArgs& e, float* part, hipStream_t st, const GemvPlan& plan);
 
 hipError_t launch_repack(int qt, const uint8_t* canon, int64_t rows, int64_t k, uint8_t* packed, const Layout& L,
                          int64_t dst_row0, int64_t dst_row_step, hipStream_t st);
