@@ -101,9 +101,12 @@ int qwg_gemv(int qtype, const void* d_packed, int64_t rows, int64_t k, const flo
              void* stream);
 
 /* Launch geometry of subsequent GEMV launches in this process, for tuning: waves per workgroup
- * (2, 4 or 8) and output rows per wave for single-column GEMVs (1, 2 or 4); 0 keeps the default.
- * Results do not depend on it beyond floating-point summation order. */
-int qwg_set_gemv_geometry(int waves_per_group, int rows_per_wave);
+ * (2, 4 or 8), output rows per wave for single-column GEMVs (1, 2 or 4), weight-load pipeline
+ * depth (1 or 2 iterations in flight) and row passes per wave (1 or 2; two passes apply to
+ * single-column residual and SwiGLU GEMVs with 2 or 4 rows per wave and depth 1); 0 keeps the
+ * default.  Results do not depend on it beyond floating-point summation order.  Not thread-safe:
+ * call it while no other thread launches GEMVs. */
+int qwg_set_gemv_geometry(int waves_per_group, int rows_per_wave, int pipeline_depth, int row_passes);
 
 /* RMSNorm ([NT] "Key features"; cuda/ RMSNorm kernel): d_out[j][i] = g[i] x[j][i] / sqrt(mean_i x[j]^2 + eps),
  * for j < n_cols; x, out fp32 [n_cols][n]; n <= 65536. */
@@ -121,7 +124,9 @@ int qwg_rope(float* d_v, int n_heads, int head_dim, const float* d_table, int po
  * d_q fp32 [n_cols][n_q][head_dim]; d_kc, d_vc fp16 bits [>= n_pos + n_cols - 1][n_kv][head_dim];
  * column j attends to positions 0 .. n_pos - 1 + j (causal), query head h uses kv head h / (n_q / n_kv);
  * scores q.k / sqrt(head_dim), softmax, weighted sum of V.  d_out fp32 [n_cols][n_q][head_dim].
- * d_work: device scratch of qwg_attn_work_bytes(...) bytes.  head_dim must be 128; n_cols <= 8. */
+ * d_work: device scratch of qwg_attn_work_bytes(...) bytes, which the call overwrites (calls that share
+ * it must not overlap).  head_dim must be 128; n_cols <= 8; n_kv <= 64; (n_q / n_kv) * n_cols <= 64;
+ * n_pos <= 262144.  qwg_attn_work_bytes returns 0 for shapes outside these limits. */
 size_t qwg_attn_work_bytes(int n_pos, int n_q, int n_kv, int head_dim, int n_cols);
 int qwg_attn_decode(const float* d_q, const uint16_t* d_kc, const uint16_t* d_vc, int n_pos, int n_q, int n_kv,
                     int head_dim, int n_cols, float* d_out, void* d_work, size_t work_bytes, void* stream);

@@ -116,8 +116,9 @@ struct qwg_model {
   std::vector<LayerPlan> L;
   MatPlan embed{}, head{};
   size_t g_final = 0, rope = 0, h = 0, hin = 0, qb = 0, ob = 0, act = 0, logits = 0, amax = 0, keys = 0, cosv = 0;
-  size_t capture = 0, part = 0, attn = 0, slot[2] = {0, 0}, staging = 0, xd = 0, rsb = 0;
+  size_t capture = 0, part = 0, attn = 0, slot[2] = {0, 0}, staging = 0, xd[2] = {0, 0}, sq = 0;
   int64_t xd_col = 0;  // bytes of one column of activation digits
+  int64_t sq_col = 0;  // floats of one column of per-chunk sums of squares
   size_t part_bytes = 0, attn_bytes = 0, staging_bytes = 0, image_max = 0, total = 0;
   int n_streamed = 0;
   uint8_t* arena = nullptr;
@@ -210,8 +211,10 @@ static int plan_model(qwg_model* m) {
   m->capture = take((size_t)(d.n_layers + 1) * H * 4);
   const int64_t kmax = std::max<int64_t>(std::max<int64_t>(H, F), (int64_t)d.n_q * d.head_dim);
   m->xd_col = digit_bytes(kmax);
-  m->xd = take((size_t)C * m->xd_col);
-  m->rsb = take((size_t)MAX_COLS * 4);
+  m->xd[0] = take((size_t)C * m->xd_col);
+  m->xd[1] = take((size_t)C * m->xd_col);
+  m->sq_col = kmax / XCHUNK;
+  m->sq = take((size_t)C * m->sq_col * 4);
   size_t pb = 0;
   for (int nc : {1, C}) {
     const int64_t shapes[5][2] = {{(int64_t)(d.n_q + 2 * d.n_kv) * d.head_dim, H},
@@ -257,6 +260,17 @@ static int check_desc(const qwg_model_desc* d) {
     return fail(QWG_E_SHAPE, "hidden, ffn and n_q*head_dim must be multiples of the block size");
   if (H > 65536 || F > 65536 || QR > 65536) return fail(QWG_E_SHAPE, "K dimensions above 65536 are not supported");
   if (d->n_resident < -1 || d->n_resident > d->n_layers) return fail(QWG_E_SHAPE, "bad n_resident");
+  if (d->n_kv > 64) return fail(QWG_E_SHAPE, "n_kv above 64 is not supported");
+  if (d->max_ctx > 131072) return fail(QWG_E_SHAPE, "max_ctx above 131072 is not supported");
+  const int64_t shapes[6][3] = {{d->qtype_attn, (int64_t)(d->n_q + 2 * d->n_kv) * d->head_dim, H},
+                                {d->qtype_attn, H, QR},
+                                {d->qtype_ffn, 2 * F, H},
+                                {d->qtype_ffn, H, F},
+                                {d->qtype_embed, d->vocab, H},
+                                {d->qtype_head, d->vocab, H}};
+  for (const auto& sh : shapes)
+    if (make_layout((int)sh[0], sh[1], sh[2]).total >= ((int64_t)1 << 32))
+      return fail(QWG_E_SHAPE, "a packed matrix of 4 GiB or more is not supported");
   return QWG_OK;
 }
 
@@ -296,22 +310,66 @@ static int64_t gemv_alg_bytes(const MatPlan& p, int nc, int out_rw) {
   return p.canon_bytes + (int64_t)nc * p.L.k * 4 + (int64_t)nc * p.L.rows * 4 * out_rw;
 }
 
-// Digitize the GEMV input (with the RMSNorm gain when given), then run the GEMV; with timing on for
-// this weight class, HIP events on the compute stream bracket the GEMV kernel(s).
-static int gemv(qwg_model* m, int tensor_class, int qt, const MatView& w, const MatPlan& mp, const float* x,
-                int64_t x_stride, const float* gain, int nc, int epi, EpiArgs e) {
+// Where a GEMV's output vector goes next: digits for the next GEMV (of gain * out when a gain is
+// given, with per-chunk sums of out^2 when sq is given).
+struct OutDigits {
+  int buf = -1;  // digit buffer index, or -1 (no digits)
+  const float* gain = nullptr;
+  int qt = 0;    // the consuming GEMV's qtype (picks nibble or byte digits)
+  bool sq = false;
+};
+
+// The input of a GEMV: the digits in buffer `buf` (with the RMSNorm folded in when rms is set), or
+// an fp32 vector xf that the GEMV digitizes itself (through buffer `buf` and a separate
+// digitization kernel when the launch geometry has no such variant).
+struct InDigits {
+  int buf = 0;
+  bool rms = false;
+  const float* xf = nullptr;
+  int64_t xf_stride = 0;
+};
+
+// Run one GEMV; its epilogue also digitizes the output per `od` when the launch geometry allows
+// it, else a separate digitization kernel follows.  With timing on for this weight class, HIP
+// events on the compute stream bracket the GEMV kernel(s).
+static int gemv(qwg_model* m, int tensor_class, int qt, const MatView& w, const MatPlan& mp, const InDigits& in, int nc,
+                int epi, EpiArgs e, const OutDigits& od) {
   const GemvPlan gp = plan_gemv(qt, w.rows, mp.L.k, nc, epi);
   if (gp.part_bytes > m->part_bytes) return fail(QWG_E_NOMEM, "split workspace too small");
-  QWG_HIP(launch_digitize(x, x_stride, gain, m->d.rms_eps, mp.L.k, nc, qt, m->arena + m->xd, m->xd_col,
-                          gain ? m->f(m->rsb) : nullptr, m->cs));
-  e.rs = gain ? m->f(m->rsb) : nullptr;
+  const bool rms = in.rms;
+  if (in.xf) {
+    if (gemv_can_digitize_input(gp, epi)) {
+      e.xf = in.xf;
+      e.xf_stride = in.xf_stride;
+    } else {
+      QWG_HIP(launch_digitize(in.xf, in.xf_stride, nullptr, mp.L.k, nc, qt, m->arena + m->xd[in.buf], m->xd_col,
+                              nullptr, 0, m->cs));
+    }
+  }
+  if (rms) {
+    e.sq_in = m->f(m->sq);
+    e.sq_in_n = (int)(mp.L.k / XCHUNK);
+    e.sq_in_stride = m->sq_col;
+    e.rms_k = (float)mp.L.k;
+    e.eps = m->d.rms_eps;
+  }
+  const bool want = od.buf >= 0;
+  const bool fused = want && gemv_can_digitize_output(gp, epi, w.rows);
+  if (fused) {
+    e.dig_out = (uint32_t*)(m->arena + m->xd[od.buf]);
+    e.dig_stride = m->xd_col / 4;
+    e.dig_gain = od.gain;
+    e.dig_kind = digit_kind(od.qt);
+    e.sq_out = od.sq ? m->f(m->sq) : nullptr;
+    e.sq_out_stride = m->sq_col;
+  }
   const bool timed = m->timing_tensor == tensor_class;
   if (timed) {
     hipEvent_t e0 = pool_event(m->tev, m->tev_used);
     if (!e0) return fail(QWG_E_HIP, "hipEventCreate failed");
     QWG_HIP(hipEventRecord(e0, m->cs));
   }
-  QWG_HIP(launch_gemv(qt, w, mp.L.k, m->arena + m->xd, m->xd_col, nc, epi, e, m->f(m->part), m->cs, gp));
+  QWG_HIP(launch_gemv(qt, w, mp.L.k, m->arena + m->xd[in.buf], m->xd_col, nc, epi, e, m->f(m->part), m->cs, gp));
   if (timed) {
     hipEvent_t e1 = pool_event(m->tev, m->tev_used);
     if (!e1) return fail(QWG_E_HIP, "hipEventCreate failed");
@@ -319,10 +377,17 @@ static int gemv(qwg_model* m, int tensor_class, int qt, const MatView& w, const 
     const int rw = epi == EPI_RESID ? 2 : 1;
     m->t_bytes = gemv_alg_bytes(mp, nc, epi == EPI_SWIGLU ? 0 : rw) + (epi == EPI_SWIGLU ? (int64_t)nc * mp.L.rows / 2 * 4 : 0);
   }
+  if (want && !fused) {
+    const int64_t nout = epi == EPI_SWIGLU ? w.rows / 2 : w.rows;
+    QWG_HIP(launch_digitize(e.y, e.y_stride, od.gain, nout, nc, od.qt, m->arena + m->xd[od.buf], m->xd_col,
+                            od.sq ? m->f(m->sq) : nullptr, m->sq_col, m->cs));
+  }
   return QWG_OK;
 }
 
-static int layer_kernels(qwg_model* m, int l, const uint8_t* base, int nc, int pos) {
+// One decoder layer.  Digit buffer 0 holds g_attn * h on entry (with the sums of squares of h);
+// on exit it holds the digits that `next` describes (the next layer's g_attn * h, or g_final * h).
+static int layer_kernels(qwg_model* m, int l, const uint8_t* base, int nc, int pos, const OutDigits& next) {
   const qwg_model_desc& d = m->d;
   const LayerPlan& P = m->L[l];
   const int H = d.hidden, F = d.ffn, QR = m->QR(), KR = m->KR();
@@ -337,26 +402,41 @@ static int layer_kernels(qwg_model* m, int l, const uint8_t* base, int nc, int p
   e.kc = (uint16_t*)(m->arena + P.kc);
   e.vc = (uint16_t*)(m->arena + P.vc);
   e.kv_stride = KR;
-  if ((rc = gemv(m, QWG_T_WQ, d.qtype_attn, view_at(base, P.qkv), P.qkv, m->f(m->h), H, m->f(P.g_attn), nc,
-                 EPI_QKV, e)))
+  InDigits in_qkv;
+  in_qkv.buf = 0;
+  in_qkv.rms = true;
+  if ((rc = gemv(m, QWG_T_WQ, d.qtype_attn, view_at(base, P.qkv), P.qkv, in_qkv, nc, EPI_QKV, e, OutDigits{})))
     return rc;
   const AttnPlan ap = plan_attn(pos + 1, d.n_q, d.n_kv, nc);
   if (ap.work_bytes > m->attn_bytes) return fail(QWG_E_NOMEM, "attention workspace too small");
   QWG_HIP(launch_attn(m->f(m->qb), QR, e.kc, e.vc, KR, pos + 1, d.n_q, d.n_kv, nc, m->f(m->ob), QR,
-                      m->arena + m->attn, ap, m->cs));
+                      m->arena + m->attn, ap, m->cs, (uint32_t*)(m->arena + m->xd[1]), m->xd_col / 4,
+                      digit_kind(d.qtype_attn)));
   EpiArgs r{};
   r.y = m->f(m->h);
   r.y_stride = H;
-  if ((rc = gemv(m, QWG_T_WO, d.qtype_attn, view_at(base, P.o), P.o, m->f(m->ob), QR, nullptr, nc, EPI_RESID, r)))
-    return rc;
+  OutDigits to_ffn;
+  to_ffn.buf = 0;
+  to_ffn.gain = m->f(P.g_ffn);
+  to_ffn.qt = d.qtype_ffn;
+  to_ffn.sq = true;
+  InDigits in_o;
+  in_o.buf = 1;
+  if ((rc = gemv(m, QWG_T_WO, d.qtype_attn, view_at(base, P.o), P.o, in_o, nc, EPI_RESID, r, to_ffn))) return rc;
   EpiArgs s{};
   s.y = m->f(m->act);
   s.y_stride = F;
-  if ((rc = gemv(m, QWG_T_WGATE, d.qtype_ffn, view_at(base, P.gu), P.gu, m->f(m->h), H, m->f(P.g_ffn), nc,
-                 EPI_SWIGLU, s)))
+  InDigits in_ffn;
+  in_ffn.buf = 0;
+  in_ffn.rms = true;
+  if ((rc = gemv(m, QWG_T_WGATE, d.qtype_ffn, view_at(base, P.gu), P.gu, in_ffn, nc, EPI_SWIGLU, s, OutDigits{})))
     return rc;
-  if ((rc = gemv(m, QWG_T_WDOWN, d.qtype_ffn, view_at(base, P.down), P.down, m->f(m->act), F, nullptr, nc, EPI_RESID,
-                 r)))
+  // the down GEMV digitizes silu(gate) * up itself
+  InDigits in_act;
+  in_act.buf = 1;
+  in_act.xf = m->f(m->act);
+  in_act.xf_stride = F;
+  if ((rc = gemv(m, QWG_T_WDOWN, d.qtype_ffn, view_at(base, P.down), P.down, in_act, nc, EPI_RESID, r, next)))
     return rc;
   return QWG_OK;
 }
@@ -386,6 +466,30 @@ static int run_pass(qwg_model* m, const int32_t* toks, int nc, int pos, int n_ru
   for (int i = 0; i < nc; ++i)
     if (toks[i] < 0 || toks[i] >= d.vocab) return fail(QWG_E_INVAL, "token id out of range");
   QWG_HIP(launch_embed(d.qtype_embed, view_at(m->arena, m->embed), H, toks, nc, m->f(m->h), H, m->cs));
+  // the digits every layer leaves behind are for the next layer that runs (its g_attn), or for the
+  // head (g_final) after the last one
+  std::vector<int> runs;
+  for (int l = 0; l < n_run; ++l)
+    if (calib || !m->skip[l]) runs.push_back(l);
+  auto digits_for = [&](int ri) {
+    OutDigits od;
+    od.buf = 0;
+    od.sq = true;
+    if (ri < (int)runs.size()) {
+      od.gain = m->f(m->L[runs[ri]].g_attn);
+      od.qt = d.qtype_attn;
+    } else {
+      od.gain = m->f(m->g_final);
+      od.qt = d.qtype_head;
+    }
+    return od;
+  };
+  {
+    const OutDigits od = digits_for(0);
+    QWG_HIP(launch_digitize(m->f(m->h), H, od.gain, H, nc, od.qt, m->arena + m->xd[0], m->xd_col, m->f(m->sq),
+                            m->sq_col, m->cs));
+  }
+  int ri = 0;
   if (m->capture_on) QWG_HIP(hipMemcpyAsync(m->f(m->capture), m->f(m->h), (size_t)H * 4, hipMemcpyDeviceToDevice, m->cs));
   std::vector<int> sl;
   for (int l = 0; l < n_run; ++l)
@@ -407,7 +511,7 @@ static int run_pass(qwg_model* m, const int32_t* toks, int nc, int pos, int n_ru
         base = m->arena + m->slot[slot];
       }
       if (calib) QWG_HIP(hipMemcpyAsync(m->f(m->hin), m->f(m->h), (size_t)H * 4, hipMemcpyDeviceToDevice, m->cs));
-      if (int rc = layer_kernels(m, l, base, nc, pos)) return rc;
+      if (int rc = layer_kernels(m, l, base, nc, pos, digits_for(++ri))) return rc;
       if (!P.resident) {
         QWG_HIP(hipEventRecord(m->ev_free[slot], m->cs));
         if (sj + 2 < (int)sl.size())
@@ -426,8 +530,11 @@ static int run_pass(qwg_model* m, const int32_t* toks, int nc, int pos, int n_ru
   EpiArgs e{};
   e.y = m->f(m->logits);
   e.y_stride = d.vocab;
-  if (int rc = gemv(m, QWG_T_HEAD, d.qtype_head, view_at(m->arena, m->head), m->head, m->f(m->h), H, m->f(m->g_final),
-                    nc, EPI_STORE, e))
+  InDigits in_head;
+  in_head.buf = 0;
+  in_head.rms = true;
+  if (int rc = gemv(m, QWG_T_HEAD, d.qtype_head, view_at(m->arena, m->head), m->head, in_head, nc, EPI_STORE, e,
+                    OutDigits{}))
     return rc;
   QWG_HIP(launch_argmax(m->f(m->logits), d.vocab, nc, d.vocab, (int32_t*)(m->arena + m->amax), m->cs,
                         (unsigned long long*)(m->arena + m->keys)));
@@ -467,6 +574,7 @@ static int check_matrix(int qtype, int64_t rows, int64_t k) {
   if (rows < 0 || rows > (int64_t)1 << 30) return fail(QWG_E_SHAPE, "rows out of range");
   if (canon_row_bytes(qtype, k) == 0) return fail(QWG_E_SHAPE, "k must be a positive multiple of the block");
   if (k > 65536) return fail(QWG_E_SHAPE, "k above 65536");
+  if (make_layout(qtype, rows, k).total >= ((int64_t)1 << 32)) return fail(QWG_E_SHAPE, "packed matrix of 4 GiB or more");
   return QWG_OK;
 }
 
@@ -500,7 +608,7 @@ int qwg_gemv(int qtype, const void* d_packed, int64_t rows, int64_t k, const flo
   if (p.part_bytes) QWG_HIP(kernel_workspace(WS_GEMV, p.part_bytes, &part));
   void* xd = nullptr;
   QWG_HIP(kernel_workspace(WS_DIGITS, (size_t)n_cols * digit_bytes(k), &xd));
-  QWG_HIP(launch_digitize(d_x, k, nullptr, 0.f, k, n_cols, qtype, xd, digit_bytes(k), nullptr, (hipStream_t)stream));
+  QWG_HIP(launch_digitize(d_x, k, nullptr, k, n_cols, qtype, xd, digit_bytes(k), nullptr, 0, (hipStream_t)stream));
   EpiArgs e{};
   e.y = d_y;
   e.y_stride = rows;
@@ -509,12 +617,15 @@ int qwg_gemv(int qtype, const void* d_packed, int64_t rows, int64_t k, const flo
   return QWG_OK;
 }
 
-int qwg_set_gemv_geometry(int waves_per_group, int rows_per_wave) {
+int qwg_set_gemv_geometry(int waves_per_group, int rows_per_wave, int pipeline_depth, int row_passes) {
   if (!(waves_per_group == 0 || waves_per_group == 2 || waves_per_group == 4 || waves_per_group == 8))
     return fail(QWG_E_INVAL, "waves_per_group must be 0, 2, 4 or 8");
   if (!(rows_per_wave == 0 || rows_per_wave == 1 || rows_per_wave == 2 || rows_per_wave == 4))
     return fail(QWG_E_INVAL, "rows_per_wave must be 0, 1, 2 or 4");
-  set_gemv_geometry(waves_per_group, rows_per_wave);
+  if (!(pipeline_depth == 0 || pipeline_depth == 1 || pipeline_depth == 2))
+    return fail(QWG_E_INVAL, "pipeline_depth must be 0, 1 or 2");
+  if (!(row_passes == 0 || row_passes == 1 || row_passes == 2)) return fail(QWG_E_INVAL, "row_passes must be 0, 1 or 2");
+  set_gemv_geometry(waves_per_group, rows_per_wave, pipeline_depth, row_passes);
   return QWG_OK;
 }
 
@@ -548,7 +659,8 @@ int qwg_rope(float* d_v, int n_heads, int head_dim, const float* d_table, int po
 }
 
 size_t qwg_attn_work_bytes(int n_pos, int n_q, int n_kv, int head_dim, int n_cols) {
-  if (n_pos < 1 || n_q < 1 || n_kv < 1 || n_q % n_kv || head_dim != HEAD_DIM || n_cols < 1 || n_cols > MAX_COLS)
+  if (n_pos < 1 || n_pos > 262144 || n_q < 1 || n_kv < 1 || n_kv > 64 || n_q % n_kv || head_dim != HEAD_DIM ||
+      n_cols < 1 || n_cols > MAX_COLS || n_q / n_kv * n_cols > 64)
     return 0;
   return plan_attn(n_pos, n_q, n_kv, n_cols).work_bytes;
 }
@@ -557,7 +669,7 @@ int qwg_attn_decode(const float* d_q, const uint16_t* d_kc, const uint16_t* d_vc
                     int head_dim, int n_cols, float* d_out, void* d_work, size_t work_bytes, void* stream) {
   if (!d_q || !d_kc || !d_vc || !d_out || !d_work) return fail(QWG_E_INVAL, "NULL pointer");
   if (head_dim != HEAD_DIM) return fail(QWG_E_SHAPE, "head_dim must be 128");
-  if (n_pos < 1 || n_q < 1 || n_kv < 1 || n_q % n_kv || n_cols < 1 || n_cols > MAX_COLS)
+  if (n_pos < 1 || n_pos > 262144 || n_q < 1 || n_kv < 1 || n_kv > 64 || n_q % n_kv || n_cols < 1 || n_cols > MAX_COLS)
     return fail(QWG_E_SHAPE, "bad attention shape");
   if (n_q / n_kv * n_cols > 64) return fail(QWG_E_SHAPE, "(n_q / n_kv) * n_cols must be <= 64");
   const AttnPlan p = plan_attn(n_pos, n_q, n_kv, n_cols);

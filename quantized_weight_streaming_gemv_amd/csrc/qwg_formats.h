@@ -8,8 +8,8 @@
 //
 //   region Q : the quant bytes, 16 B per "chunk" (Q8_0: 16 weights; others: 32 weights),
 //              chunk c of row r at Q + r*q_row + 16c  -> a wave reads 1 KiB contiguous
-//   region A : Q8_0 / Q4_0 fp16 d per block; Q4_K / Q5_K 16-B superblock header
-//              (d, dmin, the 12 packed 6-bit scale/min bytes); Q6_K 8 B of 2-bit highs per chunk
+//   region A : Q8_0 / Q4_0 fp16 d per block; Q4_K / Q5_K 16-B superblock header (d, dmin and the
+//              sixteen 6-bit scales/mins, re-laid out below); Q6_K 8 B of 2-bit highs per chunk
 //   region B : Q5_K 4 B of fifth bits per chunk; Q6_K the chunk's two int8 sub-block scales
 //   region C : Q6_K fp16 d per superblock
 //
@@ -17,11 +17,21 @@
 // e = j in the low nibble and e = j + 16 in the high nibble of byte j, so 32-bit word m
 // carries weights 4m..4m+3 (low nibbles) and 16+4m..16+4m+3 (high nibbles) -- the
 // activation for word m is float4 m and float4 4+m of the chunk.
+//   Q4_0, Q4_K: each nibble holds q XOR 8, i.e. q - 8 as a 4-bit two's-complement number, so the
+//        integer dot takes the quant words as they are.
+//   Q4_K / Q5_K header (4 words): word 0 = d | dmin << 16; the scale of sub-block j (6 bits) at
+//        bit 6j of the 64-bit (word 1 | word 2 << 32), its min at bit 16 + 6j of (word 2 |
+//        word 3 << 32) -- the same 16 six-bit values as the canonical 12 bytes, placed so that a
+//        lane extracts its sub-block's pair with two shifts whatever j is.
 //   Q5_K fifth bits (32 bits): bit 8b + 2m   = bit 4 of weight 4m+b,
 //                              bit 8b + 2m+1 = bit 4 of weight 16+4m+b.
 //   Q6_K high bits (2 words): word i, byte b, bit pair p: p=0 -> weight 4(2i)+b,
-//        p=1 -> 16+4(2i)+b, p=2 -> 4(2i+1)+b, p=3 -> 16+4(2i+1)+b.
+//        p=1 -> 16+4(2i)+b, p=2 -> 4(2i+1)+b, p=3 -> 16+4(2i+1)+b; each pair holds the quant's
+//        two high bits XOR 2, so that (pair << 6 | nibble << 2) read as int8 is 4 (q - 32).
 //   Q6_K scales: weights 0..15 of a chunk form one 16-weight sub-block, 16..31 the next.
+//
+// Every change from the canonical blocks is a bit permutation or a fixed bit flip: the packed
+// matrix has exactly the canonical payload bytes and decodes to the same values.
 //
 // Everything here is __host__ __device__ so the same decoders can be exercised on the CPU.
 #pragma once
@@ -170,14 +180,6 @@ __host__ __device__ inline uint16_t float_to_half_bits(float f) {
 
 __host__ __device__ inline float ubyte(uint32_t v, int i) { return (float)((v >> (8 * i)) & 0xFFu); }
 
-// Hide a masked word from the optimizer so that each byte converts with one v_cvt_f32_ubyteN
-// (otherwise the shared mask is folded into a per-byte bit-field extract plus a conversion).
-__host__ __device__ inline uint32_t opaque(uint32_t v) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __asm__("" : "+v"(v));
-#endif
-  return v;
-}
 __host__ __device__ inline float sbyte(uint32_t v, int i) { return (float)(int32_t)(int8_t)(uint8_t)(v >> (8 * i)); }
 
 // 6-bit scale and min of sub-block s (0..7) from the 12 packed bytes held in words S0 (bytes
@@ -191,6 +193,15 @@ __host__ __device__ inline void kq_scale_min(uint32_t S0, uint32_t S1, uint32_t 
   const int hi_m = (int)((b2 >> 4) | ((b1 >> 6) << 4));
   sc = s < 4 ? lo_sc : hi_sc;
   m = s < 4 ? lo_m : hi_m;
+}
+
+// 6-bit scale and min of sub-block j from a packed Q4_K / Q5_K header (words h1, h2, h3).
+__host__ __device__ inline void kq_packed_scale_min(uint32_t h1, uint32_t h2, uint32_t h3, int j, uint32_t& sc,
+                                                    uint32_t& m) {
+  const uint64_t ps = (uint64_t)h1 | ((uint64_t)h2 << 32);
+  const uint64_t pm = (uint64_t)h2 | ((uint64_t)h3 << 32);
+  sc = (uint32_t)(ps >> (6 * j)) & 63u;
+  m = (uint32_t)(pm >> (16 + 6 * j)) & 63u;
 }
 
 // Weight bytes are read exactly once per pass: streaming (non-temporal) loads.
@@ -292,6 +303,77 @@ __host__ __device__ inline void digitize_chunk(const float* x, int kind, uint32_
   desc->sumB = sb;
 }
 
+// Four consecutive lanes (lane & 3 = m) digitize one 32-element chunk together.  Lane m passes the
+// chunk elements 4m..4m+3 and 16+4m..16+4m+3 in v[0..7]; the chunk scale and integer sums travel by
+// lane shuffles; lane m writes its six digit words and lane 0 the ChunkDesc at oc (a chunk base of
+// DIG_CHUNK_WORDS words).  All four lanes must call it (write = false lets a lane take part without
+// storing).  Same digits as digitize_chunk.
+// put(i, word) stores digit word i (0..23) or descriptor word i (24..27) of the chunk.
+template <class Put>
+__device__ inline void digitize_group_to(const float* v, int m, int kind, Put&& put, bool write) {
+  float mx = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(v[i]));
+  mx = fmaxf(mx, __shfl_xor(mx, 1));
+  mx = fmaxf(mx, __shfl_xor(mx, 2));
+  int sh = 0;
+  if (mx > 0.f && mx == mx) sh = min(100, max(-100, 21 - ilogbf(mx)));  // mx * 2^sh in [2^21, 2^22)
+  int32_t xf[8];
+  int32_t sa = 0, sb = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float t = ldexpf(v[i], sh);
+    xf[i] = (t == t) ? (int32_t)rintf(t) : 0;
+    if (i < 4) sa += xf[i];
+    else sb += xf[i];
+  }
+  sa += __shfl_xor(sa, 1);
+  sa += __shfl_xor(sa, 2);
+  sb += __shfl_xor(sb, 1);
+  sb += __shfl_xor(sb, 2);
+  if (!write) return;
+  if (kind == DIG_NIB) {
+    // word m*6 + l, nibble 2b + h = digit l of element 16h + 4m + b  (v[4h + b])
+    uint32_t u[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) u[i] = (uint32_t)(xf[i] + 0x888888);
+#pragma unroll
+    for (int l = 0; l < 6; ++l) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) w |= ((u[4 * h + b] >> (4 * l)) & 15u) << (4 * (2 * b + h));
+      put(m * 6 + l, w ^ 0x88888888u);
+    }
+  } else {
+    // word (h*4 + m)*3 + l, byte b = digit l of element 16h + 4m + b
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t u[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) u[b] = (uint32_t)(xf[4 * h + b] + 0x808080);
+#pragma unroll
+      for (int l = 0; l < 3; ++l) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) w |= ((u[b] >> (8 * l)) & 255u) << (8 * b);
+        put((h * 4 + m) * 3 + l, w ^ 0x80808080u);
+      }
+    }
+  }
+  if (m == 0) {
+    put(DIG_WORDS, __float_as_uint(ldexpf(1.0f, -sh)));
+    put(DIG_WORDS + 1, (uint32_t)(sa + sb));
+    put(DIG_WORDS + 2, (uint32_t)sa);
+    put(DIG_WORDS + 3, (uint32_t)sb);
+  }
+}
+__device__ inline void digitize_group(const float* v, int m, int kind, uint32_t* oc, bool write) {
+  digitize_group_to(v, m, kind, [&](int i, uint32_t w) { oc[i] = w; }, write);
+}
+
+
 // exact integer dot products (device: one v_dot8_i32_i4 / v_dot4_i32_i8 each)
 __host__ __device__ inline int32_t sdot8(uint32_t a, uint32_t b, int32_t c) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -315,13 +397,48 @@ __host__ __device__ inline int32_t sdot4(uint32_t a, uint32_t b, int32_t c) {
 #endif
 }
 
-// sum_l 16^l D_l (six nibble levels) and sum_l 256^l D_l (three byte levels) in fp32
-__host__ __device__ inline float combine_nib(const int32_t* D) {
-  const int32_t lo = D[0] + D[1] * 16 + D[2] * 256, hi = D[3] + D[4] * 16 + D[5] * 256;
+// The value of a chunk against its digit levels, sum_l base^l D_l with D_l the integer dot of the
+// quants with digit level l, assembled in Horner form: each level's dot chain starts from base x
+// the partial of the levels above it, so no level needs its own accumulator or conversion.
+//   nibble (base 16, six levels): hi = (D5*16 + D4)*16 + D3, lo = (D2*16 + D1)*16 + D0 with
+//     |D_l| <= 32*8*8 = 2048, so |hi|, |lo| < 2^20 (exact in int32 and fp32); value = 4096 hi + lo
+//   byte (base 256, three levels): hi = D2, lo = D1*256 + D0 with |D_l| <= 32*128*128 = 2^19, so
+//     |lo| < 2^28 fits int32; value = 65536 hi + lo (lo rounds to fp32 once: relative 2^-24)
+// The quant words w[0..NW) pair with digit words dig[m*6 + l] (nibble) / dig[m*3 + l] (byte).
+template <int NW>
+__host__ __device__ inline int32_t nib_chain(const uint32_t* w, const uint32_t* dig, int l, int32_t c) {
+#pragma unroll
+  for (int m = 0; m < NW; ++m) c = sdot8(w[m], dig[m * 6 + l], c);
+  return c;
+}
+__host__ __device__ inline float nib_value(const uint32_t* w, const uint32_t* dig) {
+  int32_t hi = nib_chain<4>(w, dig, 5, 0);
+  hi = nib_chain<4>(w, dig, 4, hi * 16);
+  hi = nib_chain<4>(w, dig, 3, hi * 16);
+  int32_t lo = nib_chain<4>(w, dig, 2, 0);
+  lo = nib_chain<4>(w, dig, 1, lo * 16);
+  lo = nib_chain<4>(w, dig, 0, lo * 16);
   return __builtin_fmaf(4096.0f, (float)hi, (float)lo);
 }
-__host__ __device__ inline float combine_byte(const int32_t* D) {
-  return __builtin_fmaf(65536.0f, (float)D[2], (float)(D[0] + D[1] * 256));
+template <int NW>
+__host__ __device__ inline int32_t byte_chain(const uint32_t* w, const uint32_t* dig, int l, int32_t c) {
+#pragma unroll
+  for (int m = 0; m < NW; ++m) c = sdot4(w[m], dig[m * 3 + l], c);
+  return c;
+}
+// four quant words against the 12 digit words of one 16-element half
+__host__ __device__ inline float byte_value(const uint32_t* w, const uint32_t* dig) {
+  const int32_t hi = byte_chain<4>(w, dig, 2, 0);
+  int32_t lo = byte_chain<4>(w, dig, 1, 0);
+  lo = byte_chain<4>(w, dig, 0, lo * 256);
+  return __builtin_fmaf(65536.0f, (float)hi, (float)lo);
+}
+// both halves of a 32-element chunk (quant words wa against dig[0..12), wb against dig[12..24))
+__host__ __device__ inline float byte_value2(const uint32_t* wa, const uint32_t* wb, const uint32_t* dig) {
+  const int32_t hi = byte_chain<4>(wb, dig + 12, 2, byte_chain<4>(wa, dig, 2, 0));
+  int32_t lo = byte_chain<4>(wb, dig + 12, 1, byte_chain<4>(wa, dig, 1, 0));
+  lo = byte_chain<4>(wb, dig + 12, 0, byte_chain<4>(wa, dig, 0, lo * 256));
+  return __builtin_fmaf(65536.0f, (float)hi, (float)lo);
 }
 
 // ---------------------------------------------------------------------------- per-format chunk codecs
@@ -336,13 +453,12 @@ __host__ __device__ inline float combine_byte(const int32_t* D) {
 //                                          256-weight superblock)
 //   float dotu(u, digits, desc)         -- sum_e w_e x_e of the chunk from exact integer dot
 //                                          products with the activation digits
-//   dot<NC>(raw, chunk, sub, nc, X, S, acc)
-//                                       -- acc[n] += sum_e w_e x[n][e] without forming w_e (sub =
-//                                          chunk & 7, the chunk's place in its superblock):
-//                                          integer quants times activations, then one scale
-//                                          (and min/offset via the chunk's activation sums S).
-// X(n, q) returns float4 q of the chunk's activation for column n; S(n, j) returns the sum of
-// activation part j of the chunk (Q4_0/Q4_K/Q5_K: all 32; Q6_K: j=0 -> 0..15, j=1 -> 16..31).
+// Byte offsets inside one packed region are 32-bit (the library refuses matrices of 4 GiB or more),
+// so loads take a uniform 64-bit base plus a 32-bit lane offset.
+
+__host__ __device__ inline uint32_t roff(int64_t row, int64_t row_bytes, uint32_t within) {
+  return (uint32_t)row * (uint32_t)row_bytes + within;
+}
 
 template <int QT>
 struct Fmt;
@@ -356,8 +472,8 @@ struct Fmt<Q8_0> {
   };
   __host__ __device__ static Raw load(const MatView& v, int64_t row, int c) {
     Raw r;
-    r.q = ld_stream_u4(v.q + row * v.q_row + (int64_t)c * 16);
-    r.d = ld<uint16_t>(v.a + row * v.a_row + (int64_t)(c >> 1) * 2);
+    r.q = ld_stream_u4(v.q + roff(row, v.q_row, (uint32_t)c * 16u));
+    r.d = ld<uint16_t>(v.a + roff(row, v.a_row, (uint32_t)(c >> 1) * 2u));
     return r;
   }
   __host__ __device__ static void decode(const Raw& r, int, float* w) {
@@ -366,30 +482,22 @@ struct Fmt<Q8_0> {
     for (int m = 0; m < 4; ++m)
       for (int b = 0; b < 4; ++b) w[4 * m + b] = d * sbyte(q[m], b) + 0.0f;
   }
-  // Integer form of a chunk: quant words ready for the integer dot plus its scale coefficients.
   struct U {
     uint32_t w[4];
     float d;
-    int h;  // which half of the 32-element activation chunk this 16-weight chunk covers
   };
-  __host__ __device__ static U unpack(const Raw& r, int c, int) {
+  __host__ __device__ static U unpack(const Raw& r, int, int) {
     U u;
     u.w[0] = r.q.x;
     u.w[1] = r.q.y;
     u.w[2] = r.q.z;
     u.w[3] = r.q.w;
     u.d = half_bits_to_float(r.d);
-    u.h = c & 1;
     return u;
   }
-  // dig: the 12 digit words of this half (words 12h .. 12h+11 of the activation chunk)
+  // dig: the 12 digit words of this chunk's half of the 32-element activation chunk
   __host__ __device__ static float dotu(const U& u, const uint32_t* dig, const ChunkDesc& ds) {
-    int32_t D[3] = {0, 0, 0};
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int l = 0; l < 3; ++l) D[l] = sdot4(u.w[m], dig[m * 3 + l], D[l]);
-    return ds.inv_scale * (u.d * combine_byte(D));
+    return ds.inv_scale * (u.d * byte_value(u.w, dig));
   }
 };
 
@@ -402,8 +510,8 @@ struct Fmt<Q4_0> {
   };
   __host__ __device__ static Raw load(const MatView& v, int64_t row, int c) {
     Raw r;
-    r.q = ld_stream_u4(v.q + row * v.q_row + (int64_t)c * 16);
-    r.d = ld<uint16_t>(v.a + row * v.a_row + (int64_t)c * 2);
+    r.q = ld_stream_u4(v.q + roff(row, v.q_row, (uint32_t)c * 16u));
+    r.d = ld<uint16_t>(v.a + roff(row, v.a_row, (uint32_t)c * 2u));
     return r;
   }
   __host__ __device__ static void decode(const Raw& r, int, float* w) {
@@ -411,31 +519,26 @@ struct Fmt<Q4_0> {
     const uint32_t q[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
     for (int m = 0; m < 4; ++m)
       for (int b = 0; b < 4; ++b) {
-        const int byte = (int)((q[m] >> (8 * b)) & 0xFFu);
+        const int byte = (int)((q[m] >> (8 * b)) & 0xFFu) ^ 0x88;  // back to the canonical q
         w[4 * m + b] = d * (float)((byte & 15) - 8) + 0.0f;
         w[16 + 4 * m + b] = d * (float)((byte >> 4) - 8) + 0.0f;
       }
   }
   struct U {
-    uint32_t w[4];
+    uint32_t w[4];  // q - 8 as signed nibbles
     float d;
   };
   __host__ __device__ static U unpack(const Raw& r, int, int) {
     U u;
-    u.w[0] = r.q.x ^ 0x88888888u;  // q - 8 as signed nibbles
-    u.w[1] = r.q.y ^ 0x88888888u;
-    u.w[2] = r.q.z ^ 0x88888888u;
-    u.w[3] = r.q.w ^ 0x88888888u;
+    u.w[0] = r.q.x;
+    u.w[1] = r.q.y;
+    u.w[2] = r.q.z;
+    u.w[3] = r.q.w;
     u.d = half_bits_to_float(r.d);
     return u;
   }
   __host__ __device__ static float dotu(const U& u, const uint32_t* dig, const ChunkDesc& ds) {
-    int32_t D[6] = {0, 0, 0, 0, 0, 0};
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int l = 0; l < 6; ++l) D[l] = sdot8(u.w[m], dig[m * 6 + l], D[l]);
-    return ds.inv_scale * (u.d * combine_nib(D));
+    return ds.inv_scale * (u.d * nib_value(u.w, dig));
   }
 };
 
@@ -444,54 +547,50 @@ struct Fmt<Q4_K> {
   static constexpr int CW = 32;
   struct Raw {
     uint4 q;
-    uint4 h;  // d | dmin << 16, S[0..3], S[4..7], S[8..11]
+    uint4 h;  // d | dmin << 16, then the re-laid-out scales and mins
   };
   __host__ __device__ static Raw load(const MatView& v, int64_t row, int c) {
     Raw r;
-    r.q = ld_stream_u4(v.q + row * v.q_row + (int64_t)c * 16);
-    r.h = ld<uint4>(v.a + row * v.a_row + (int64_t)(c >> 3) * 16);
+    r.q = ld_stream_u4(v.q + roff(row, v.q_row, (uint32_t)c * 16u));
+    r.h = ld<uint4>(v.a + roff(row, v.a_row, (uint32_t)(c >> 3) * 16u));
     return r;
   }
-  __host__ __device__ static void coef(const Raw& r, int c, float& dsc, float& dmm) {
-    int sc, m;
-    kq_scale_min(r.h.y, r.h.z, r.h.w, c & 7, sc, m);
-    dsc = half_bits_to_float(r.h.x & 0xFFFFu) * (float)sc;
-    dmm = half_bits_to_float(r.h.x >> 16) * (float)m;
+  // d * scale and dmin * min of sub-block j (both exact in fp32)
+  __host__ __device__ static void coef(const uint4& h, int j, float& dsc, float& dmm) {
+    uint32_t sc, m;
+    kq_packed_scale_min(h.y, h.z, h.w, j, sc, m);
+    dsc = half_bits_to_float(h.x & 0xFFFFu) * (float)sc;
+    dmm = half_bits_to_float(h.x >> 16) * (float)m;
   }
   __host__ __device__ static void decode(const Raw& r, int c, float* w) {
     float dsc, dmm;
-    coef(r, c, dsc, dmm);
+    coef(r.h, c & 7, dsc, dmm);
     const uint32_t q[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
     for (int m = 0; m < 4; ++m)
       for (int b = 0; b < 4; ++b) {
-        const int byte = (int)((q[m] >> (8 * b)) & 0xFFu);
+        const int byte = (int)((q[m] >> (8 * b)) & 0xFFu) ^ 0x88;  // back to the canonical q
         w[4 * m + b] = __builtin_fmaf(dsc, (float)(byte & 15), -dmm) + 0.0f;
         w[16 + 4 * m + b] = __builtin_fmaf(dsc, (float)(byte >> 4), -dmm) + 0.0f;
       }
   }
   struct U {
-    uint32_t w[4];
-    float c0, c1;  // sum w x = c0 * sum (q-8) x + c1 * sum x
+    uint32_t w[4];  // q - 8 as signed nibbles
+    float c0, c1;   // sum w x = c0 * sum (q-8) x + c1 * sum x
   };
   __host__ __device__ static U unpack(const Raw& r, int, int sub) {
     float dsc, dmm;
-    coef(r, sub, dsc, dmm);
+    coef(r.h, sub, dsc, dmm);
     U u;
-    u.w[0] = r.q.x ^ 0x88888888u;
-    u.w[1] = r.q.y ^ 0x88888888u;
-    u.w[2] = r.q.z ^ 0x88888888u;
-    u.w[3] = r.q.w ^ 0x88888888u;
+    u.w[0] = r.q.x;
+    u.w[1] = r.q.y;
+    u.w[2] = r.q.z;
+    u.w[3] = r.q.w;
     u.c0 = dsc;
-    u.c1 = 8.0f * dsc - dmm;
+    u.c1 = __builtin_fmaf(8.0f, dsc, -dmm);
     return u;
   }
   __host__ __device__ static float dotu(const U& u, const uint32_t* dig, const ChunkDesc& ds) {
-    int32_t D[6] = {0, 0, 0, 0, 0, 0};
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int l = 0; l < 6; ++l) D[l] = sdot8(u.w[m], dig[m * 6 + l], D[l]);
-    return ds.inv_scale * __builtin_fmaf(u.c0, combine_nib(D), u.c1 * (float)ds.sum);
+    return ds.inv_scale * __builtin_fmaf(u.c0, nib_value(u.w, dig), u.c1 * (float)ds.sum);
   }
 };
 
@@ -505,9 +604,9 @@ struct Fmt<Q5_K> {
   };
   __host__ __device__ static Raw load(const MatView& v, int64_t row, int c) {
     Raw r;
-    r.q = ld_stream_u4(v.q + row * v.q_row + (int64_t)c * 16);
-    r.h = ld<uint4>(v.a + row * v.a_row + (int64_t)(c >> 3) * 16);
-    r.qh = ld_stream_u1(v.b + row * v.b_row + (int64_t)c * 4);
+    r.q = ld_stream_u4(v.q + roff(row, v.q_row, (uint32_t)c * 16u));
+    r.h = ld<uint4>(v.a + roff(row, v.a_row, (uint32_t)(c >> 3) * 16u));
+    r.qh = ld_stream_u1(v.b + roff(row, v.b_row, (uint32_t)c * 4u));
     return r;
   }
   // the 5-bit quants of word m as bytes: low-nibble weights and high-nibble weights
@@ -517,13 +616,12 @@ struct Fmt<Q5_K> {
     // bit 8b + 2m (low) / 8b + 2m + 1 (high) moved to bit 4 of byte b
     const uint32_t l5 = (m <= 2) ? (r.qh << (4 - 2 * m)) : (r.qh >> 2);
     const uint32_t h5 = (m <= 1) ? (r.qh << (3 - 2 * m)) : (r.qh >> (2 * m - 3));
-    lo = opaque((w & 0x0F0F0F0Fu) | (l5 & 0x10101010u));
-    hi = opaque(((w >> 4) & 0x0F0F0F0Fu) | (h5 & 0x10101010u));
+    lo = (w & 0x0F0F0F0Fu) | (l5 & 0x10101010u);
+    hi = ((w >> 4) & 0x0F0F0F0Fu) | (h5 & 0x10101010u);
   }
   __host__ __device__ static void decode(const Raw& r, int c, float* w) {
     float dsc, dmm;
-    Fmt<Q4_K>::Raw rr{r.q, r.h};
-    Fmt<Q4_K>::coef(rr, c, dsc, dmm);
+    Fmt<Q4_K>::coef(r.h, c & 7, dsc, dmm);
     for (int m = 0; m < 4; ++m) {
       uint32_t lo, hi;
       words(r, m, lo, hi);
@@ -539,8 +637,7 @@ struct Fmt<Q5_K> {
   };
   __host__ __device__ static U unpack(const Raw& r, int, int sub) {
     float dsc, dmm;
-    Fmt<Q4_K>::Raw rr{r.q, r.h};
-    Fmt<Q4_K>::coef(rr, sub, dsc, dmm);
+    Fmt<Q4_K>::coef(r.h, sub, dsc, dmm);
     U u;
 #pragma unroll
     for (int m = 0; m < 4; ++m) words(r, m, u.lo[m], u.hi[m]);
@@ -549,15 +646,7 @@ struct Fmt<Q5_K> {
     return u;
   }
   __host__ __device__ static float dotu(const U& u, const uint32_t* dig, const ChunkDesc& ds) {
-    int32_t D[3] = {0, 0, 0};
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int l = 0; l < 3; ++l) {
-        D[l] = sdot4(u.lo[m], dig[(0 * 4 + m) * 3 + l], D[l]);
-        D[l] = sdot4(u.hi[m], dig[(1 * 4 + m) * 3 + l], D[l]);
-      }
-    return ds.inv_scale * __builtin_fmaf(u.c0, combine_byte(D), u.c1 * (float)ds.sum);
+    return ds.inv_scale * __builtin_fmaf(u.c0, byte_value2(u.lo, u.hi, dig), u.c1 * (float)ds.sum);
   }
 };
 
@@ -572,21 +661,22 @@ struct Fmt<Q6_K> {
   };
   __host__ __device__ static Raw load(const MatView& v, int64_t row, int c) {
     Raw r;
-    r.q = ld_stream_u4(v.q + row * v.q_row + (int64_t)c * 16);
-    r.qh = ld_stream_u2(v.a + row * v.a_row + (int64_t)c * 8);
-    r.sc = ld<uint16_t>(v.b + row * v.b_row + (int64_t)c * 2);
-    r.d = ld<uint16_t>(v.c + row * v.c_row + (int64_t)(c >> 3) * 2);
+    r.q = ld_stream_u4(v.q + roff(row, v.q_row, (uint32_t)c * 16u));
+    r.qh = ld_stream_u2(v.a + roff(row, v.a_row, (uint32_t)c * 8u));
+    r.sc = ld<uint16_t>(v.b + roff(row, v.b_row, (uint32_t)c * 2u));
+    r.d = ld<uint16_t>(v.c + roff(row, v.c_row, (uint32_t)(c >> 3) * 2u));
     return r;
   }
-  // unsigned 6-bit quants of word m: low-nibble weights (4m+b) and high-nibble weights (16+4m+b)
+  // word m as int8 bytes 4 (q - 32): low-nibble weights (4m+b) and high-nibble weights (16+4m+b);
+  // the stored high pair (XOR 2) lands in bits 6..7, the nibble in bits 2..5
   __host__ __device__ static void words(const Raw& r, int m, uint32_t& lo, uint32_t& hi) {
     const uint32_t q[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
     const uint32_t w = q[m];
     const uint32_t h = (m < 2) ? r.qh.x : r.qh.y;
-    const uint32_t hl = (m & 1) ? h : (h << 4);
-    const uint32_t hh = (m & 1) ? (h >> 2) : (h << 2);
-    lo = opaque((w & 0x0F0F0F0Fu) | (hl & 0x30303030u));
-    hi = opaque(((w >> 4) & 0x0F0F0F0Fu) | (hh & 0x30303030u));
+    const uint32_t hl = (m & 1) ? (h << 2) : (h << 6);  // pair 2(m&1) -> bits 6..7
+    const uint32_t hh = (m & 1) ? h : (h << 4);         // pair 2(m&1)+1 -> bits 6..7
+    lo = ((w << 2) & 0x3C3C3C3Cu) | (hl & 0xC0C0C0C0u);
+    hi = ((w >> 2) & 0x3C3C3C3Cu) | (hh & 0xC0C0C0C0u);
   }
   __host__ __device__ static void decode(const Raw& r, int, float* w) {
     const float d = half_bits_to_float(r.d);
@@ -596,37 +686,26 @@ struct Fmt<Q6_K> {
       uint32_t lo, hi;
       words(r, m, lo, hi);
       for (int b = 0; b < 4; ++b) {
-        w[4 * m + b] = dA * (ubyte(lo, b) - 32.0f) + 0.0f;
-        w[16 + 4 * m + b] = dB * (ubyte(hi, b) - 32.0f) + 0.0f;
+        w[4 * m + b] = dA * (0.25f * sbyte(lo, b)) + 0.0f;
+        w[16 + 4 * m + b] = dB * (0.25f * sbyte(hi, b)) + 0.0f;
       }
     }
   }
   struct U {
-    uint32_t lo[4], hi[4];  // unsigned 6-bit quants as bytes (weights 0..15 and 16..31)
-    float dA, dB;           // d * sc of the two 16-weight sub-blocks
+    uint32_t lo[4], hi[4];  // 4 (q - 32) as int8 (weights 0..15 and 16..31)
+    float dA, dB;           // d * sc / 4 of the two 16-weight sub-blocks
   };
   __host__ __device__ static U unpack(const Raw& r, int, int) {
     const float d = half_bits_to_float(r.d);
     U u;
 #pragma unroll
     for (int m = 0; m < 4; ++m) words(r, m, u.lo[m], u.hi[m]);
-    u.dA = d * (float)(int8_t)(uint8_t)(r.sc & 0xFFu);
-    u.dB = d * (float)(int8_t)(uint8_t)((r.sc >> 8) & 0xFFu);
+    u.dA = 0.25f * (d * (float)(int8_t)(uint8_t)(r.sc & 0xFFu));
+    u.dB = 0.25f * (d * (float)(int8_t)(uint8_t)((r.sc >> 8) & 0xFFu));
     return u;
   }
   __host__ __device__ static float dotu(const U& u, const uint32_t* dig, const ChunkDesc& ds) {
-    int32_t A[3] = {0, 0, 0}, B[3] = {0, 0, 0};
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int l = 0; l < 3; ++l) {
-        A[l] = sdot4(u.lo[m], dig[(0 * 4 + m) * 3 + l], A[l]);
-        B[l] = sdot4(u.hi[m], dig[(1 * 4 + m) * 3 + l], B[l]);
-      }
-    // sum d sc (q - 32) x over the two 16-weight sub-blocks of the chunk
-    const float tA = combine_byte(A) - 32.0f * (float)ds.sumA;
-    const float tB = combine_byte(B) - 32.0f * (float)ds.sumB;
-    return ds.inv_scale * __builtin_fmaf(u.dA, tA, u.dB * tB);
+    return ds.inv_scale * __builtin_fmaf(u.dA, byte_value(u.lo, dig), u.dB * byte_value(u.hi, dig + 12));
   }
 };
 
@@ -679,17 +758,33 @@ __host__ __device__ inline void repack_block(int qt, const uint8_t* blk, uint8_t
     case Q4_0: {
       A[2 * b] = blk[0];
       A[2 * b + 1] = blk[1];
-      put16(Q + b * 16, blk + 2);  // canonical Q4_0 already pairs weight j with j + 16
+      // canonical Q4_0 already pairs weight j with j + 16; nibbles become q XOR 8
+      for (int j = 0; j < 16; ++j) Q[b * 16 + j] = (uint8_t)(blk[2 + j] ^ 0x88);
       break;
     }
     case Q4_K:
     case Q5_K: {
-      put16(A + b * 16, blk);  // d, dmin, S[12]
+      // header: d, dmin as they are; the sixteen 6-bit scales/mins re-laid out
+      for (int i = 0; i < 4; ++i) A[b * 16 + i] = blk[i];
+      uint32_t S[3];
+      for (int i = 0; i < 3; ++i)
+        S[i] = (uint32_t)blk[4 + 4 * i] | ((uint32_t)blk[5 + 4 * i] << 8) | ((uint32_t)blk[6 + 4 * i] << 16) |
+               ((uint32_t)blk[7 + 4 * i] << 24);
+      uint64_t ps = 0, pm = 0;
+      for (int j = 0; j < 8; ++j) {
+        int sc, mn;
+        kq_scale_min(S[0], S[1], S[2], j, sc, mn);
+        ps |= (uint64_t)sc << (6 * j);
+        pm |= (uint64_t)mn << (16 + 6 * j);
+      }
+      const uint32_t hw[3] = {(uint32_t)ps, (uint32_t)(ps >> 32) | (uint32_t)pm, (uint32_t)(pm >> 32)};
+      for (int i = 0; i < 12; ++i) A[b * 16 + 4 + i] = (uint8_t)(hw[i >> 2] >> (8 * (i & 3)));
       const uint8_t* qs = blk + (qt == Q4_K ? 16 : 48);
       const uint8_t* qh = blk + 16;
       for (int s = 0; s < 8; ++s) {
         int q[32];
-        for (int e = 0; e < 32; ++e) q[e] = qt == Q4_K ? canon_q4k(qs, 32 * s + e) : canon_q5k(qh, qs, 32 * s + e);
+        for (int e = 0; e < 32; ++e)
+          q[e] = qt == Q4_K ? (canon_q4k(qs, 32 * s + e) ^ 8) : canon_q5k(qh, qs, 32 * s + e);
         const int64_t c = 8 * b + s;
         pack_nibbles(q, Q + c * 16);
         if (qt == Q5_K) {
@@ -718,8 +813,9 @@ __host__ __device__ inline void repack_block(int qt, const uint8_t* blk, uint8_t
           for (int bb = 0; bb < 4; ++bb) {
             const int e0 = 4 * (2 * i) + bb, e1 = 16 + 4 * (2 * i) + bb;
             const int e2 = 4 * (2 * i + 1) + bb, e3 = 16 + 4 * (2 * i + 1) + bb;
-            const uint32_t v = (uint32_t)(((q[e0] >> 4) & 3) | (((q[e1] >> 4) & 3) << 2) | (((q[e2] >> 4) & 3) << 4) |
-                                          (((q[e3] >> 4) & 3) << 6));
+            // high pairs XOR 2 (the sign flip of q - 32 in 6-bit two's complement)
+            const uint32_t v = (uint32_t)((((q[e0] >> 4) & 3) ^ 2) | ((((q[e1] >> 4) & 3) ^ 2) << 2) |
+                                          ((((q[e2] >> 4) & 3) ^ 2) << 4) | ((((q[e3] >> 4) & 3) ^ 2) << 6));
             w[i] |= v << (8 * bb);
           }
         for (int i = 0; i < 8; ++i) A[c * 8 + i] = (uint8_t)(w[i >> 2] >> (8 * (i & 3)));

@@ -6,19 +6,21 @@
 //   * a workgroup of W wave64s owns W*R consecutive output rows and one K split;
 //   * each wave owns R rows; lane l walks chunks l, l+64, ... of those rows, so every wave-wide
 //     load instruction reads 1 KiB of contiguous quant bytes (16 B per lane);
-//   * the activation arrives as block fixed-point digits (one k_digitize launch per GEMV input,
-//     see qwg_formats.h): 28 words per 32 elements, staged once per workgroup into LDS in a
-//     chunk-transposed layout -- 16-B slot q of chunk c of column n at (n*7 + q)*nxp + c -- so
-//     the 64 lanes of a wave read 64 consecutive slots, free of bank conflicts;
+//   * the activation arrives as block fixed-point digits (see qwg_formats.h): 28 words per 32
+//     elements, staged once per workgroup into LDS in a chunk-transposed layout -- 16-B slot q of
+//     chunk c of column n at (n*7 + q)*nxp + c -- so the 64 lanes of a wave read 64 consecutive
+//     slots, free of bank conflicts;
 //   * quants stay integers: nibble formats feed v_dot8_i32_i4 directly (q - 8 by one XOR), the
 //     others feed v_dot4_i32_i8 with one byte per quant; each chunk's integer sums are recombined
 //     in fp32 and scaled once by the block scales and the activation chunk scale;
-//   * an RMSNorm in front of the GEMV is folded in: the digits are of g*h and the per-column
-//     scale 1/rms multiplies the finished row in the epilogue;
+//   * an RMSNorm in front of the GEMV is folded in: the digits are of g*h, and the finished rows are
+//     multiplied by 1/rms, reduced in a fixed order from per-chunk sums of h^2 in the prologue;
 //   * the first chunk's weights are requested before the activation is staged, and each loop
 //     iteration requests the next chunk before computing the current one;
-//   * a 64-lane butterfly (shuffles) reduces each row; lanes 0..R-1 run the epilogue
-//     (store, residual add, SwiGLU on interleaved gate|up rows, or RoPE + fp16 KV append).
+//   * a 64-lane butterfly (shuffles) reduces each row; lanes 0..R-1 run the epilogue (store,
+//     residual add, SwiGLU on interleaved gate|up rows, or RoPE + fp16 KV append), and for the
+//     residual and SwiGLU epilogues the workgroup also digitizes its slice of the output vector
+//     for the next GEMV (each workgroup writes whole 32-element chunks);
 //   * K splits (when the activation for all columns does not fit the LDS budget) write partial
 //     sums that a second kernel adds in a fixed order, so results never depend on timing.
 #include <hip/hip_runtime.h>
@@ -31,22 +33,27 @@ namespace qwg {
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
-__device__ __forceinline__ void run_epilogue(int epi, const EpiArgs& e, int n, int row, float v, float vp) {
-  if (e.rs) {
-    const float r = e.rs[n];
-    v *= r;
-    vp *= r;
-  }
+// Final value of output row `row`, column n (v: its sum; vp: the sum of its pair partner row^1),
+// stored by the epilogue; returns the value the output vector holds at that position (the new h
+// for RESID, silu(gate)*up for SWIGLU on even rows).
+__device__ __forceinline__ float run_epilogue(int epi, const EpiArgs& e, int n, int row, float v, float vp) {
   switch (epi) {
     case EPI_STORE:
       e.y[(int64_t)n * e.y_stride + row] = v;
-      break;
-    case EPI_RESID:
-      e.y[(int64_t)n * e.y_stride + row] += v;
-      break;
+      return v;
+    case EPI_RESID: {
+      float* p = e.y + (int64_t)n * e.y_stride + row;
+      const float h = *p + v;
+      *p = h;
+      return h;
+    }
     case EPI_SWIGLU:
-      if ((row & 1) == 0) e.y[(int64_t)n * e.y_stride + (row >> 1)] = silu_f(v) * vp;
-      break;
+      if ((row & 1) == 0) {
+        const float a = silu_f(v) * vp;
+        e.y[(int64_t)n * e.y_stride + (row >> 1)] = a;
+        return a;
+      }
+      return 0.f;
     case EPI_QKV: {
       const int pos = e.pos + n;
       if (row < e.nq_rows + e.nkv_rows) {
@@ -61,10 +68,60 @@ __device__ __forceinline__ void run_epilogue(int epi, const EpiArgs& e, int n, i
       } else {
         e.vc[(int64_t)pos * e.kv_stride + (row - e.nq_rows - e.nkv_rows)] = float_to_half_bits(v);
       }
-      break;
+      return 0.f;
     }
     default:
-      break;
+      return 0.f;
+  }
+}
+
+// Per-wave partial sums of the RMSNorm input's chunk sums of squares (column n) into red[n][wave].
+__device__ __forceinline__ void rms_partials(const EpiArgs& e, int nc, float (*red)[16]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int n = 0; n < nc; ++n) {
+    float s = 0.f;
+    for (int i = tid; i < e.sq_in_n; i += blockDim.x) s += e.sq_in[(int64_t)n * e.sq_in_stride + i];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    if (lane == 0) red[n][wave] = s;
+  }
+}
+
+__device__ __forceinline__ float rms_scale(const EpiArgs& e, float (*red)[16], int n) {
+  const int nw = blockDim.x >> 6;
+  float s = 0.f;
+  for (int w = 0; w < nw; ++w) s += red[n][w];
+  return 1.0f / sqrtf(s / e.rms_k + e.eps);
+}
+
+// Digitize output values held in LDS (osh[n][0 .. nout), nout a multiple of 32, output elements
+// out0 ..) for the next GEMV, with their per-chunk sums of squares.  Every group of four lanes
+// takes one (column, chunk); all threads of the block call it.
+template <int OSTRIDE>
+__device__ __forceinline__ void digitize_outputs(const EpiArgs& e, int nc, const float (*osh)[OSTRIDE], int nout,
+                                                 int out0) {
+  const int tid = threadIdx.x, m = tid & 3, g = tid >> 2;
+  const int nchunk = nout / XCHUNK;
+  for (int base = 0; base < nc * nchunk; base += blockDim.x >> 2) {
+    const int job = base + g;
+    const bool ok = job < nc * nchunk;
+    const int n = ok ? job / nchunk : 0, j = ok ? job % nchunk : 0;
+    float v[8], ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int el = j * XCHUNK + (i < 4 ? 4 * m + i : 16 + 4 * m + i - 4);
+      float x = ok ? osh[n][el] : 0.f;
+      ss += x * x;
+      if (e.dig_gain && ok) x *= e.dig_gain[out0 + el];
+      v[i] = x;
+    }
+    const int chunk = (out0 / XCHUNK) + j;
+    digitize_group(v, m, e.dig_kind, e.dig_out + (int64_t)n * e.dig_stride + (int64_t)chunk * DIG_CHUNK_WORDS, ok);
+    if (e.sq_out) {
+      ss += __shfl_xor(ss, 1);
+      ss += __shfl_xor(ss, 2);
+      if (ok && m == 0) e.sq_out[(int64_t)n * e.sq_out_stride + chunk] = ss;
+    }
   }
 }
 
@@ -81,13 +138,21 @@ struct GemvArgs {
 
 constexpr int XSLOTS = DIG_CHUNK_WORDS / 4;  // 16-B slots per activation chunk (6 digit slots + desc)
 
-template <int QT, int NCM, int R, int EPI>
-__global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
+// PD: weight loads in flight ahead of the chunk being computed (1 or 2 iterations of 64 chunks).
+// P: row passes -- a wave finishes R rows, then the next R rows nw*R further on, so a workgroup
+// covers nw*R*P rows at the registers of R (the next pass's first loads are issued before the
+// finished pass is reduced).  LB: the launch bound.  XIN: the input arrives as fp32 (EpiArgs::xf)
+// and every workgroup digitizes the part it needs straight into LDS.
+template <int QT, int NCM, int R, int EPI, int PD, int P = 1, int LB = 512, int XIN = 0>
+__global__ __launch_bounds__(LB) void k_gemv(GemvArgs a) {
+  static_assert(P == 1 || PD == 1, "row passes use the one-ahead pipeline");
   using F = Fmt<QT>;
   constexpr int CW = F::CW;
   constexpr int WPX = XCHUNK / CW;               // weight chunks per activation chunk (2 for Q8_0)
   constexpr int NDS = (CW == 16) ? 3 : 6;        // digit slots one weight chunk reads
   extern __shared__ uint4 lds[];
+  __shared__ float red[MAX_COLS][16];
+  __shared__ float osh[MAX_COLS][64];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
   const int nc = a.nc;
@@ -100,277 +165,278 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
   const int nchs = klen / CW;      // weight chunks of this split
   const int cbase = kbeg / CW;
   const int rows = a.w.rows;
-  const int row0 = (blockIdx.x * nw + wave) * R;
-  const bool active = row0 < rows;
+  const int wg_rows = nw * R * P;
+  const int wg_row0 = blockIdx.x * wg_rows;
+  const bool digitize = (EPI == EPI_RESID || EPI == EPI_SWIGLU) && a.e.dig_out != nullptr;
 
-  // 1. request the first chunk of every row of this wave before staging the activation
-  //    (rows past the end are clamped to the last row: loads stay in bounds, results are dropped)
+  // rows past the end are clamped to the last row (loads stay in bounds, results are dropped);
+  // chunk indexes past the end are clamped to the last chunk (re-read, never used)
   int rr[R];
+  typename F::Raw b0[R], b1[R], b2[R];
+  auto set_rows = [&](int r0) {
 #pragma unroll
-  for (int r = 0; r < R; ++r) rr[r] = min(row0 + r, rows - 1);
-  typename F::Raw cur[R];
-  if (active && lane < nchs) {
+    for (int r = 0; r < R; ++r) rr[r] = min(r0 + r, rows - 1);
+  };
+  auto fetch = [&](typename F::Raw* raw, int cl) {
+    const int c = min(cl, nchs - 1);
 #pragma unroll
-    for (int r = 0; r < R; ++r) cur[r] = F::load(a.w, rr[r], cbase + lane);
+    for (int r = 0; r < R; ++r) raw[r] = F::load(a.w, rr[r], cbase + c);
+  };
+
+  // 1. request the first chunks of this wave's rows before staging the activation
+  set_rows(wg_row0 + wave * R);
+  if (wg_row0 + wave * R < rows) {
+    fetch(b0, lane);
+    if (PD == 2) fetch(b1, lane + 64);
   }
 
-  // 2. stage this split's activation digits (coalesced 16-B reads, chunk-transposed LDS)
-  for (int n = 0; n < nc; ++n) {
-    const uint4* src = a.xd + (int64_t)n * a.xd_stride + (int64_t)xbase * XSLOTS;
-    for (int i = tid; i < nxs * XSLOTS; i += blockDim.x) {
-      const int c = i / XSLOTS, q = i % XSLOTS;
-      lds[(n * XSLOTS + q) * nxp + c] = src[i];
-    }
-  }
-  __syncthreads();
-  if (!active) return;
-
-  // 3. main loop over this lane's chunks
-  const int sub = lane & 7;  // chunk index within its 256-weight superblock (splits start on superblocks)
-  float acc[R][NCM];
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int n = 0; n < NCM; ++n) acc[r][n] = 0.f;
-
-  for (int cl = lane; cl < nchs; cl += 64) {
-    typename F::Raw nxt[R];
-    const int cn = min(cl + 64, nchs - 1);  // the last iteration re-requests a chunk it already has
-#pragma unroll
-    for (int r = 0; r < R; ++r) nxt[r] = F::load(a.w, rr[r], cbase + cn);
-    typename F::U u[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) u[r] = F::unpack(cur[r], cbase + cl, sub);
-    const int xc = cl / WPX;
-    const int s0 = (WPX == 2) ? (cl & 1) * 3 : 0;  // first digit slot of this half (Q8_0)
-#pragma unroll
-    for (int n = 0; n < NCM; ++n) {
-      if (n >= nc) break;
-      uint32_t dg[NDS * 4];
-#pragma unroll
-      for (int q = 0; q < NDS; ++q) {
-        const uint4 v = lds[(n * XSLOTS + s0 + q) * nxp + xc];
-        dg[4 * q] = v.x;
-        dg[4 * q + 1] = v.y;
-        dg[4 * q + 2] = v.z;
-        dg[4 * q + 3] = v.w;
+  // 2. stage this split's activation digits (coalesced 16-B reads, chunk-transposed LDS) and the
+  //    RMSNorm partial sums
+  if (XIN) {
+    // four threads per 32-element chunk digitize it into the same LDS layout
+    uint32_t* ldw = (uint32_t*)lds;
+    const int m = tid & 3;
+    for (int n = 0; n < nc; ++n) {
+      const float* xr = a.e.xf + (int64_t)n * a.e.xf_stride + (int64_t)xbase * XCHUNK;
+      for (int c = tid >> 2; c < nxs; c += blockDim.x >> 2) {
+        const float4 lo = *(const float4*)(xr + (int64_t)c * XCHUNK + 4 * m);
+        const float4 hi = *(const float4*)(xr + (int64_t)c * XCHUNK + 16 + 4 * m);
+        const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        digitize_group_to(
+            v, m, digit_kind(QT),
+            [&](int i, uint32_t w) { ldw[((n * XSLOTS + (i >> 2)) * nxp + c) * 4 + (i & 3)] = w; }, true);
       }
-      const uint4 dv = lds[(n * XSLOTS + 6) * nxp + xc];
-      ChunkDesc ds;
-      ds.inv_scale = __uint_as_float(dv.x);
-      ds.sum = (int32_t)dv.y;
-      ds.sumA = (int32_t)dv.z;
-      ds.sumB = (int32_t)dv.w;
-#pragma unroll
-      for (int r = 0; r < R; ++r) acc[r][n] += F::dotu(u[r], dg, ds);
     }
-#pragma unroll
-    for (int r = 0; r < R; ++r) cur[r] = nxt[r];
+  } else {
+    for (int n = 0; n < nc; ++n) {
+      const uint4* src = a.xd + (int64_t)n * a.xd_stride + (int64_t)xbase * XSLOTS;
+      for (int i = tid; i < nxs * XSLOTS; i += blockDim.x) {
+        const int c = i / XSLOTS, q = i % XSLOTS;
+        lds[(n * XSLOTS + q) * nxp + c] = src[i];
+      }
+    }
   }
+  if (EPI != EPI_PART && a.e.sq_in) rms_partials(a.e, nc, red);
+  __syncthreads();
 
-  // 4. reduce over the 64 lanes (every lane ends with every total)
+  const int sub = lane & 7;  // chunk index within its 256-weight superblock (splits start on superblocks)
+#pragma unroll 1
+  for (int pass = 0; pass < P; ++pass) {
+    const int row0 = wg_row0 + pass * nw * R + wave * R;
+    if (row0 >= rows) break;
+    float acc[R][NCM];
 #pragma unroll
-  for (int r = 0; r < R; ++r)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int n = 0; n < NCM; ++n) {
-      float v = acc[r][n];
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-      acc[r][n] = v;
-    }
+      for (int n = 0; n < NCM; ++n) acc[r][n] = 0.f;
 
-  // 5. epilogue: lane r finishes row row0 + r (its pair partner is row0 + (r ^ 1))
-  if (lane < R) {
-    const int row = row0 + lane;
-    if (row < rows) {
+    // 3. main loop over this lane's chunks
+    auto chunk = [&](const typename F::Raw* raw, int cl) {
+      typename F::U u[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) u[r] = F::unpack(raw[r], cbase + cl, sub);
+      const int xc = cl / WPX;
+      const int s0 = (WPX == 2) ? (cl & 1) * 3 : 0;  // first digit slot of this half (Q8_0)
 #pragma unroll
       for (int n = 0; n < NCM; ++n) {
         if (n >= nc) break;
-        float v = 0.f, vp = 0.f;
+        uint32_t dg[NDS * 4];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          if (r == lane) v = acc[r][n];
-          if (r == (lane ^ 1)) vp = acc[r][n];
+        for (int q = 0; q < NDS; ++q) {
+          const uint4 v = lds[(n * XSLOTS + s0 + q) * nxp + xc];
+          dg[4 * q] = v.x;
+          dg[4 * q + 1] = v.y;
+          dg[4 * q + 2] = v.z;
+          dg[4 * q + 3] = v.w;
         }
-        if (EPI == EPI_PART)
-          a.part[((int64_t)split * nc + n) * rows + row] = v;
-        else
-          run_epilogue(EPI, a.e, n, row, v, vp);
+        const uint4 dv = lds[(n * XSLOTS + 6) * nxp + xc];
+        ChunkDesc ds;
+        ds.inv_scale = __uint_as_float(dv.x);
+        ds.sum = (int32_t)dv.y;
+        ds.sumA = (int32_t)dv.z;
+        ds.sumB = (int32_t)dv.w;
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r][n] += F::dotu(u[r], dg, ds);
       }
-    }
-  }
-}
-
-// Activation digits of nc columns of length k.  Four threads share a 32-element chunk: thread m
-// takes elements 4m..4m+3 and 16+4m..16+4m+3 (two float4 loads), the chunk's scale and integer sums
-// come from lane shuffles, and thread m writes the six digit words of its element group.  With a
-// gain vector the digits are of g * x and rs[n] = 1 / sqrt(mean(x^2) + eps) (the RMSNorm scale the
-// GEMV epilogue applies; that needs the whole column in one workgroup: gridDim.x == 1).
-__global__ __launch_bounds__(1024) void k_digitize(const float* x, int64_t x_stride, const float* gain, float eps,
-                                                   int k, int kind, uint4* out, int64_t out_stride, float* rs) {
-  __shared__ float red[16];
-  const int n = blockIdx.y;
-  const int nx = k / XCHUNK;
-  const float* xr = x + (int64_t)n * x_stride;
-  uint32_t* o = (uint32_t*)(out + (int64_t)n * out_stride);
-  const int m = threadIdx.x & 3;
-  float ss = 0.f;
-  for (int base = blockIdx.x * (blockDim.x >> 2); base < nx; base += gridDim.x * (blockDim.x >> 2)) {
-    const int c = base + (threadIdx.x >> 2);
-    const bool ok = c < nx;
-    float v[8];
-    if (ok) {
-      const float4 lo = *(const float4*)(xr + (int64_t)c * XCHUNK + 4 * m);
-      const float4 hi = *(const float4*)(xr + (int64_t)c * XCHUNK + 16 + 4 * m);
-      v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
-      v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
-      if (gain) {
-        const float4 gl = *(const float4*)(gain + (int64_t)c * XCHUNK + 4 * m);
-        const float4 gh = *(const float4*)(gain + (int64_t)c * XCHUNK + 16 + 4 * m);
-        const float g[8] = {gl.x, gl.y, gl.z, gl.w, gh.x, gh.y, gh.z, gh.w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          ss += v[i] * v[i];
-          v[i] *= g[i];
-        }
+    };
+    if (PD == 1) {
+      for (int cl = lane; cl < nchs; cl += 128) {
+        fetch(b1, cl + 64);
+        chunk(b0, cl);
+        if (cl + 64 >= nchs) break;
+        fetch(b0, cl + 128);
+        chunk(b1, cl + 64);
       }
     } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = 0.f;
+      // three buffers in rotation: two iterations of loads stay in flight while one computes
+      for (int cl = lane; cl < nchs; cl += 192) {
+        fetch(b2, cl + 128);
+        chunk(b0, cl);
+        if (cl + 64 >= nchs) break;
+        fetch(b0, cl + 192);
+        chunk(b1, cl + 64);
+        if (cl + 128 >= nchs) break;
+        fetch(b1, cl + 256);
+        chunk(b2, cl + 128);
+      }
     }
-    float mx = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(v[i]));
-    mx = fmaxf(mx, __shfl_xor(mx, 1));
-    mx = fmaxf(mx, __shfl_xor(mx, 2));
-    int sh = 0;
-    if (mx > 0.f && mx == mx) sh = min(100, max(-100, 21 - ilogbf(mx)));  // mx * 2^sh in [2^21, 2^22)
-    int32_t xf[8];
-    int32_t sa = 0, sb = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float t = ldexpf(v[i], sh);
-      xf[i] = (t == t) ? (int32_t)rintf(t) : 0;
-      if (i < 4) sa += xf[i];
-      else sb += xf[i];
+    // the next pass's first loads go out before this pass is reduced
+    if (pass + 1 < P && row0 + nw * R < rows) {
+      set_rows(row0 + nw * R);
+      fetch(b0, lane);
     }
-    sa += __shfl_xor(sa, 1);
-    sa += __shfl_xor(sa, 2);
-    sb += __shfl_xor(sb, 1);
-    sb += __shfl_xor(sb, 2);
-    if (ok) {
-      uint32_t* oc = o + (int64_t)c * DIG_CHUNK_WORDS;
-      if (kind == DIG_NIB) {
-        // word m*6 + l, nibble 2b + h = digit l of element 16h + 4m + b  (v[4h + b])
-        uint32_t u[8];
+
+    // 4. reduce over the 64 lanes (every lane ends with every total)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) u[i] = (uint32_t)(xf[i] + 0x888888);
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int l = 0; l < 6; ++l) {
-          uint32_t w = 0;
+      for (int n = 0; n < NCM; ++n) {
+        float v = acc[r][n];
 #pragma unroll
-          for (int b = 0; b < 4; ++b)
+        for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+        acc[r][n] = v;
+      }
+
+    // 5. epilogue: lane r finishes row row0 + r (its pair partner is row0 + (r ^ 1))
+    if (lane < R) {
+      const int row = row0 + lane;
+      if (row < rows) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) w |= ((u[4 * h + b] >> (4 * l)) & 15u) << (4 * (2 * b + h));
-          oc[m * 6 + l] = w ^ 0x88888888u;
-        }
-      } else {
-        // word (h*4 + m)*3 + l, byte b = digit l of element 16h + 4m + b
+        for (int n = 0; n < NCM; ++n) {
+          if (n >= nc) break;
+          float v = 0.f, vp = 0.f;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          uint32_t u[4];
-#pragma unroll
-          for (int b = 0; b < 4; ++b) u[b] = (uint32_t)(xf[4 * h + b] + 0x808080);
-#pragma unroll
-          for (int l = 0; l < 3; ++l) {
-            uint32_t w = 0;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) w |= ((u[b] >> (8 * l)) & 255u) << (8 * b);
-            oc[(h * 4 + m) * 3 + l] = w ^ 0x80808080u;
+          for (int r = 0; r < R; ++r) {
+            if (r == lane) v = acc[r][n];
+            if (r == (lane ^ 1)) vp = acc[r][n];
+          }
+          if (EPI == EPI_PART) {
+            a.part[((int64_t)split * nc + n) * rows + row] = v;
+          } else {
+            if (a.e.sq_in) {
+              const float rs = rms_scale(a.e, red, n);
+              v *= rs;
+              vp *= rs;
+            }
+            const float out = run_epilogue(EPI, a.e, n, row, v, vp);
+            if (digitize) {
+              if (EPI == EPI_RESID) osh[n][row - wg_row0] = out;
+              else if ((row & 1) == 0) osh[n][(row - wg_row0) >> 1] = out;
+            }
           }
         }
       }
-      if (m == 0)
-        *(uint4*)(oc + DIG_WORDS) =
-            make_uint4(__float_as_uint(ldexpf(1.0f, -sh)), (uint32_t)(sa + sb), (uint32_t)sa, (uint32_t)sb);
     }
   }
-  if (gain) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+
+  // 6. digitize this workgroup's slice of the output vector for the next GEMV
+  if (digitize) {
     __syncthreads();
-    if (threadIdx.x == 0) {
-      float t = 0.f;
-      for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += red[w];
-      rs[n] = 1.0f / sqrtf(t / (float)k + eps);
-    }
+    const int nrow = min(wg_rows, rows - wg_row0);  // whole chunks: the host checks rows
+    const int nout = EPI == EPI_RESID ? nrow : nrow / 2;
+    const int out0 = EPI == EPI_RESID ? wg_row0 : wg_row0 / 2;
+    digitize_outputs<64>(a.e, nc, osh, nout, out0);
   }
 }
 
-hipError_t launch_digitize(const float* x, int64_t x_stride, const float* gain, float eps, int64_t k, int nc, int qt,
-                           void* out, int64_t out_stride_bytes, float* rs, hipStream_t st) {
-  const int64_t nx = k / XCHUNK;
-  // with an RMSNorm the whole column stays in one workgroup (its sum of squares is needed);
-  // otherwise one workgroup per 256 chunks
-  const int gx = gain ? 1 : (int)((nx + 255) / 256);
-  hipLaunchKernelGGL(k_digitize, dim3(gx, nc), dim3(1024), 0, st, x, x_stride, gain, eps, (int)k, digit_kind(qt),
-                     (uint4*)out, out_stride_bytes / 16, rs);
-  return hipGetLastError();
-}
-
-// Fixed-order sum of the K-split partials, then the epilogue.
+// Fixed-order sum of the K-split partials, then the epilogue (a block of 256 threads = 256 rows;
+// with digitization, the block's 256 rows / 128 SwiGLU outputs are whole chunks).
 template <int EPI>
 __global__ __launch_bounds__(256) void k_gemv_reduce(const float* part, int ksplit, int nc, int rows, EpiArgs e) {
+  __shared__ float red[MAX_COLS][16];
+  __shared__ float osh[MAX_COLS][256];
   const int row = blockIdx.x * blockDim.x + threadIdx.x;
+  const bool digitize = (EPI == EPI_RESID || EPI == EPI_SWIGLU) && e.dig_out != nullptr;
+  if (e.sq_in) {
+    rms_partials(e, nc, red);
+    __syncthreads();
+  }
   for (int n = 0; n < nc; ++n) {
     float v = 0.f;
     if (row < rows)
       for (int s = 0; s < ksplit; ++s) v += part[((int64_t)s * nc + n) * rows + row];
+    if (e.sq_in) v *= rms_scale(e, red, n);
     const float vp = __shfl_xor(v, 1);
-    if (row < rows) run_epilogue(EPI, e, n, row, v, vp);
+    if (row < rows) {
+      const float out = run_epilogue(EPI, e, n, row, v, vp);
+      if (digitize) {
+        if (EPI == EPI_RESID) osh[n][threadIdx.x] = out;
+        else if ((row & 1) == 0) osh[n][threadIdx.x >> 1] = out;
+      }
+    }
   }
+  if (digitize) {
+    __syncthreads();
+    const int nrow = min((int)blockDim.x, rows - (int)(blockIdx.x * blockDim.x));
+    const int nout = EPI == EPI_RESID ? nrow : nrow / 2;
+    const int out0 = EPI == EPI_RESID ? (int)(blockIdx.x * blockDim.x) : (int)(blockIdx.x * blockDim.x / 2);
+    digitize_outputs<256>(e, nc, osh, nout, out0);
+  }
+}
+
+// Activation digits of nc columns of length k, four threads per 32-element chunk (thread m takes
+// elements 4m..4m+3 and 16+4m..16+4m+3 with two float4 loads).  With a gain vector the digits are
+// of g * x and sq receives each chunk's sum of x^2 (for the consumer's RMSNorm).
+__global__ __launch_bounds__(256) void k_digitize(const float* x, int64_t x_stride, const float* gain, int k, int kind,
+                                                  uint32_t* out, int64_t out_stride, float* sq, int64_t sq_stride) {
+  const int n = blockIdx.y;
+  const int nx = k / XCHUNK;
+  const float* xr = x + (int64_t)n * x_stride;
+  const int m = threadIdx.x & 3;
+  const int c = blockIdx.x * (blockDim.x >> 2) + (threadIdx.x >> 2);
+  const bool ok = c < nx;
+  const int cc = ok ? c : 0;
+  const float4 lo = *(const float4*)(xr + (int64_t)cc * XCHUNK + 4 * m);
+  const float4 hi = *(const float4*)(xr + (int64_t)cc * XCHUNK + 16 + 4 * m);
+  float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ss += v[i] * v[i];
+  if (gain) {
+    const float4 gl = *(const float4*)(gain + (int64_t)cc * XCHUNK + 4 * m);
+    const float4 gh = *(const float4*)(gain + (int64_t)cc * XCHUNK + 16 + 4 * m);
+    const float g[8] = {gl.x, gl.y, gl.z, gl.w, gh.x, gh.y, gh.z, gh.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] *= g[i];
+  }
+  digitize_group(v, m, kind, out + (int64_t)n * out_stride + (int64_t)cc * DIG_CHUNK_WORDS, ok);
+  if (sq) {
+    ss += __shfl_xor(ss, 1);
+    ss += __shfl_xor(ss, 2);
+    if (ok && m == 0) sq[(int64_t)n * sq_stride + c] = ss;
+  }
+}
+
+hipError_t launch_digitize(const float* x, int64_t x_stride, const float* gain, int64_t k, int nc, int qt, void* out,
+                           int64_t out_stride_bytes, float* sq, int64_t sq_stride, hipStream_t st) {
+  const int64_t nx = k / XCHUNK;
+  hipLaunchKernelGGL(k_digitize, dim3((unsigned)((nx + 63) / 64), nc), dim3(256), 0, st, x, x_stride, gain, (int)k,
+                     digit_kind(qt), (uint32_t*)out, out_stride_bytes / 4, sq, sq_stride);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------------------------------ host side
 
+static int g_waves = 0, g_rows = 0, g_depth = 0, g_passes = 0;  // launch-geometry overrides (0 = default)
 
-static int g_waves = 0, g_rows = 0;  // launch-geometry overrides (0 = default)
-
-void set_gemv_geometry(int waves, int rows_per_wave) {
+void set_gemv_geometry(int waves, int rows_per_wave, int depth, int passes) {
   g_waves = waves;
   g_rows = rows_per_wave;
-}
-
-// Workgroups of 8 waves; for one column, rows per wave (4, 2 or 1) picked so that the workgroup
-// count splits evenly over the 256 CUs (one resident workgroup per CU at this register use),
-// weighted by the measured per-wave efficiency of larger row groups (activation reuse).
-static int pick_rows_per_wave(int64_t rows, int waves, int ksplit, bool pairs) {
-  const int cand[3] = {4, 2, 1};
-  const double gain[3] = {1.0, 0.97, 0.83};
-  int best = 4;
-  double best_score = -1.0;
-  for (int i = 0; i < (pairs ? 2 : 3); ++i) {
-    const double wgs = (double)((rows + (int64_t)waves * cand[i] - 1) / ((int64_t)waves * cand[i])) * ksplit;
-    const double rounds = wgs / 256.0;
-    const double balance = rounds / std::ceil(rounds);
-    const double score = balance * gain[i];
-    if (score > best_score + 1e-9) {
-      best_score = score;
-      best = cand[i];
-    }
-  }
-  return best;
+  g_depth = depth;
+  g_passes = passes;
 }
 
 GemvPlan plan_gemv(int qt, int64_t rows, int64_t k, int nc, int epi) {
+  (void)qt;
+  (void)rows;
   // the RoPE and SwiGLU epilogues combine rows (2i, 2i+1), which must sit in one wave
   const bool pairs = epi == EPI_QKV || epi == EPI_SWIGLU;
   GemvPlan p{};
   p.ncm = nc <= 1 ? 1 : (nc <= 4 ? 4 : 8);
   p.rows_per_wave = 2;
   p.waves = 8;
-  if (g_waves == 2 || g_waves == 4 || g_waves == 8) p.waves = g_waves;
+  p.passes = 1;
+  p.depth = 1;
   const int64_t nx = k / XCHUNK;                        // activation chunks
   const size_t per_chunk = (size_t)p.ncm * DIG_CHUNK_WORDS * 4;  // LDS bytes per chunk (all columns)
   int64_t max_x = (int64_t)(LDS_BUDGET / per_chunk);
@@ -383,21 +449,57 @@ GemvPlan plan_gemv(int qt, int64_t rows, int64_t k, int nc, int epi) {
   p.ksplit = (int)((k + p.ks - 1) / p.ks);
   p.lds = (size_t)xs * per_chunk;
   p.part_bytes = p.ksplit > 1 ? (size_t)p.ksplit * nc * rows * sizeof(float) : 0;
-  if (p.ncm == 1) p.rows_per_wave = pick_rows_per_wave(rows, p.waves, p.ksplit, pairs);
+  // one column, 8 waves (measured on the 70B shapes): two rows per wave for the plain and QKV
+  // epilogues; four for SwiGLU and for the residual epilogue, whose 32 rows per workgroup are a
+  // whole chunk of the next GEMV's input digits, written by this kernel.  (A SwiGLU workgroup
+  // would need 64 rows for that: as 16 waves, 8 rows per wave or two passes it ran slower than
+  // 32 rows plus a separate digitization.)
+  if (p.ncm == 1) p.rows_per_wave = (epi == EPI_RESID || epi == EPI_SWIGLU) ? 4 : 2;
+  // explicit overrides (tuning and tests)
+  if (g_waves == 2 || g_waves == 4 || g_waves == 8) p.waves = g_waves;
   if (p.ncm == 1 && (g_rows == 1 || g_rows == 2 || g_rows == 4)) p.rows_per_wave = g_rows;
+  if (g_depth == 1 || g_depth == 2) p.depth = g_depth;
+  if (g_passes == 1 || g_passes == 2) p.passes = g_passes;
   if (pairs && p.rows_per_wave < 2) p.rows_per_wave = 2;
+  // compiled row-pass variants: one column, 2 or 4 rows, one-ahead loads, digitizing epilogues
+  if (!(p.ncm == 1 && p.rows_per_wave >= 2 && p.depth == 1 && p.ksplit == 1 &&
+        (epi == EPI_RESID || epi == EPI_SWIGLU)))
+    p.passes = 1;
   return p;
 }
 
-template <int QT, int NCM, int R>
+bool gemv_can_digitize_input(const GemvPlan& p, int epi) {
+  return p.ncm == 1 && p.ksplit == 1 && epi == EPI_RESID && p.rows_per_wave == 4 && p.depth == 1 && p.passes == 1;
+}
+
+bool gemv_can_digitize_output(const GemvPlan& p, int epi, int64_t rows) {
+  if (epi != EPI_RESID && epi != EPI_SWIGLU) return false;
+  if (rows % (epi == EPI_SWIGLU ? 2 * XCHUNK : XCHUNK) != 0) return false;
+  if (p.ksplit > 1) return true;  // the reduce kernel covers 256 rows per block
+  const int outs = p.waves * p.rows_per_wave * p.passes / (epi == EPI_SWIGLU ? 2 : 1);
+  return outs % XCHUNK == 0 && outs <= 64;
+}
+
+template <int QT, int NCM, int R, int PD>
 static hipError_t launch_t(const GemvArgs& a, int epi, int ksplit, dim3 grid, dim3 block, size_t lds,
                            hipStream_t st) {
   switch (ksplit > 1 ? EPI_PART : epi) {
-    case EPI_PART: hipLaunchKernelGGL((k_gemv<QT, NCM, R, EPI_PART>), grid, block, lds, st, a); break;
-    case EPI_STORE: hipLaunchKernelGGL((k_gemv<QT, NCM, R, EPI_STORE>), grid, block, lds, st, a); break;
-    case EPI_RESID: hipLaunchKernelGGL((k_gemv<QT, NCM, R, EPI_RESID>), grid, block, lds, st, a); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((k_gemv<QT, NCM, R, EPI_SWIGLU>), grid, block, lds, st, a); break;
-    case EPI_QKV: hipLaunchKernelGGL((k_gemv<QT, NCM, R, EPI_QKV>), grid, block, lds, st, a); break;
+    case EPI_PART: hipLaunchKernelGGL((k_gemv<QT, NCM, R, EPI_PART, PD>), grid, block, lds, st, a); break;
+    case EPI_STORE: hipLaunchKernelGGL((k_gemv<QT, NCM, R, EPI_STORE, PD>), grid, block, lds, st, a); break;
+    case EPI_RESID: hipLaunchKernelGGL((k_gemv<QT, NCM, R, EPI_RESID, PD>), grid, block, lds, st, a); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((k_gemv<QT, NCM, R, EPI_SWIGLU, PD>), grid, block, lds, st, a); break;
+    case EPI_QKV: hipLaunchKernelGGL((k_gemv<QT, NCM, R, EPI_QKV, PD>), grid, block, lds, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// two row passes (one column, one-ahead loads, residual or SwiGLU epilogue)
+template <int QT, int R>
+static hipError_t launch_p2(const GemvArgs& a, int epi, dim3 grid, dim3 block, size_t lds, hipStream_t st) {
+  switch (epi) {
+    case EPI_RESID: hipLaunchKernelGGL((k_gemv<QT, 1, R, EPI_RESID, 1, 2>), grid, block, lds, st, a); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((k_gemv<QT, 1, R, EPI_SWIGLU, 1, 2>), grid, block, lds, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -405,15 +507,31 @@ static hipError_t launch_t(const GemvArgs& a, int epi, int ksplit, dim3 grid, di
 
 template <int QT>
 static hipError_t launch_fmt(const GemvArgs& a, const GemvPlan& p, int epi, dim3 grid, dim3 block, hipStream_t st) {
-  if (p.ncm == 1 && p.rows_per_wave == 1) return launch_t<QT, 1, 1>(a, epi, p.ksplit, grid, block, p.lds, st);
-  if (p.ncm == 1 && p.rows_per_wave == 2) return launch_t<QT, 1, 2>(a, epi, p.ksplit, grid, block, p.lds, st);
-  if (p.ncm == 1) return launch_t<QT, 1, 4>(a, epi, p.ksplit, grid, block, p.lds, st);
-  if (p.ncm == 4) return launch_t<QT, 4, 2>(a, epi, p.ksplit, grid, block, p.lds, st);
-  return launch_t<QT, 8, 2>(a, epi, p.ksplit, grid, block, p.lds, st);
+  const int r = p.rows_per_wave, d = p.depth;
+  if (a.e.xf) {
+    if (!gemv_can_digitize_input(p, epi)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_gemv<QT, 1, 4, EPI_RESID, 1, 1, 512, 1>), grid, block, p.lds, st, a);
+    return hipGetLastError();
+  }
+  if (p.passes == 2) {
+    if (p.ncm != 1 || d != 1 || p.ksplit > 1) return hipErrorInvalidValue;
+    if (r == 2) return launch_p2<QT, 2>(a, epi, grid, block, p.lds, st);
+    if (r == 4) return launch_p2<QT, 4>(a, epi, grid, block, p.lds, st);
+    return hipErrorInvalidValue;
+  }
+  if (p.ncm == 1 && r == 1) return d == 2 ? launch_t<QT, 1, 1, 2>(a, epi, p.ksplit, grid, block, p.lds, st)
+                                          : launch_t<QT, 1, 1, 1>(a, epi, p.ksplit, grid, block, p.lds, st);
+  if (p.ncm == 1 && r == 2) return d == 2 ? launch_t<QT, 1, 2, 2>(a, epi, p.ksplit, grid, block, p.lds, st)
+                                          : launch_t<QT, 1, 2, 1>(a, epi, p.ksplit, grid, block, p.lds, st);
+  if (p.ncm == 1) return d == 2 ? launch_t<QT, 1, 4, 2>(a, epi, p.ksplit, grid, block, p.lds, st)
+                                : launch_t<QT, 1, 4, 1>(a, epi, p.ksplit, grid, block, p.lds, st);
+  if (p.ncm == 4) return launch_t<QT, 4, 2, 1>(a, epi, p.ksplit, grid, block, p.lds, st);
+  return launch_t<QT, 8, 2, 1>(a, epi, p.ksplit, grid, block, p.lds, st);
 }
 
 hipError_t launch_gemv(int qt, const MatView& w, int64_t k, const void* xd, int64_t xd_stride_bytes, int nc, int epi,
                        const EpiArgs& e, float* part, hipStream_t st, const GemvPlan& p) {
+  if (e.dig_out && !gemv_can_digitize_output(p, epi, w.rows)) return hipErrorInvalidValue;
   GemvArgs a;
   a.w = w;
   a.xd = (const uint4*)xd;
@@ -424,7 +542,7 @@ hipError_t launch_gemv(int qt, const MatView& w, int64_t k, const void* xd, int6
   a.part = part;
   a.e = e;
   const int rows = w.rows;
-  const int rows_per_wg = p.waves * p.rows_per_wave;
+  const int rows_per_wg = p.waves * p.rows_per_wave * p.passes;
   dim3 grid((rows + rows_per_wg - 1) / rows_per_wg, p.ksplit);
   dim3 block(64 * p.waves);
   hipError_t err;

@@ -10,7 +10,7 @@ namespace qwg {
 
 constexpr int HEAD_DIM = 128;   // every supported model uses 128-wide heads
 constexpr int MAX_COLS = 8;     // widest multi-column pass
-constexpr size_t LDS_BUDGET = 60 * 1024;  // dynamic LDS per workgroup (static arrays take the rest of 64 KiB)
+constexpr size_t LDS_BUDGET = 120 * 1024;  // dynamic LDS per workgroup (gfx950: 160 KiB per CU)
 
 // What the GEMV does with each finished output row (columns n < nc).
 enum Epi : int {
@@ -22,7 +22,23 @@ enum Epi : int {
 };
 
 struct EpiArgs {
-  const float* rs;       // per-column factor applied before the epilogue (RMSNorm 1/rms), or null
+  // fp32 input that the GEMV digitizes itself in its prologue (instead of reading digits), or null
+  const float* xf;
+  int64_t xf_stride;     // floats between columns
+  // RMSNorm in front of this GEMV: its input digits are of g * x, and the row sums are multiplied by
+  // 1/sqrt(sum(x^2)/rms_k + eps), with sum(x^2) from per-chunk partials (fixed-order reduction)
+  const float* sq_in;    // [nc][sq_in_stride] per-32-element-chunk sums of x^2, or null (no RMSNorm)
+  int sq_in_n;           // chunks per column
+  int64_t sq_in_stride;
+  float rms_k;
+  float eps;
+  // digitization of this GEMV's output vector for the next GEMV (RESID: the new h; SWIGLU: silu*up)
+  uint32_t* dig_out;     // digit words, column stride dig_stride words, or null
+  int64_t dig_stride;
+  const float* dig_gain; // the next GEMV's RMSNorm gain (digits of gain * out), or null
+  int dig_kind;
+  float* sq_out;         // per-chunk sums of out^2 for the next RMSNorm, column stride sq_out_stride, or null
+  int64_t sq_out_stride;
   float* y;
   int64_t y_stride;      // floats between columns of y
   const float* rope;     // [max_ctx][HEAD_DIM/2] (cos, sin) pairs
@@ -37,6 +53,8 @@ struct GemvPlan {
   int ncm;     // compiled column bound (1, 4 or 8)
   int rows_per_wave;
   int waves;   // per workgroup
+  int depth;   // weight-load pipeline depth (iterations in flight)
+  int passes;  // row passes per wave (a workgroup covers waves * rows_per_wave * passes rows)
   int ks;      // K per split
   int ksplit;
   size_t lds;  // dynamic LDS bytes
@@ -45,15 +63,15 @@ struct GemvPlan {
 
 // epi: the epilogue the GEMV will run (pairs of rows must share a wave for RoPE and SwiGLU)
 GemvPlan plan_gemv(int qt, int64_t rows, int64_t k, int nc, int epi);
-void set_gemv_geometry(int waves, int rows_per_wave);
+void set_gemv_geometry(int waves, int rows_per_wave, int depth, int passes);
 
 // Bytes of the activation digits of one column of length k (28 words per 32 elements).
 inline int64_t digit_bytes(int64_t k) { return k / XCHUNK * DIG_CHUNK_WORDS * 4; }
 
 // Digits of nc activation columns (x: [nc][x_stride] fp32) for a GEMV over weights of type qt;
-// with a gain vector, digits of gain * x and rs[n] = RMSNorm scale of column n.
-hipError_t launch_digitize(const float* x, int64_t x_stride, const float* gain, float eps, int64_t k, int nc, int qt,
-                           void* out, int64_t out_stride_bytes, float* rs, hipStream_t st);
+// with a gain vector, digits of gain * x and per-chunk sums of x^2 into sq (column stride sq_stride).
+hipError_t launch_digitize(const float* x, int64_t x_stride, const float* gain, int64_t k, int nc, int qt, void* out,
+                           int64_t out_stride_bytes, float* sq, int64_t sq_stride, hipStream_t st);
 
 // y = W x from activation digits xd (column stride in bytes) with an epilogue; `part` must hold
 // plan.part_bytes when plan.ksplit > 1.  Returns hipSuccess or the launch error.
@@ -81,9 +99,17 @@ struct AttnPlan {
   size_t work_bytes;
 };
 AttnPlan plan_attn(int n_pos, int n_q, int n_kv, int nc);
-// column j attends to positions [0, n_pos + j)
+// column j attends to positions [0, n_pos + j); with dig_out, the output is also written as
+// activation digits (kind dig_kind, column stride dig_stride words) for the next GEMV
 hipError_t launch_attn(const float* q, int64_t q_stride, const uint16_t* kc, const uint16_t* vc, int64_t kv_stride,
                        int n_pos, int n_q, int n_kv, int nc, float* out, int64_t out_stride, void* work,
-                       const AttnPlan& p, hipStream_t st);
+                       const AttnPlan& p, hipStream_t st, uint32_t* dig_out = nullptr, int64_t dig_stride = 0,
+                       int dig_kind = 0);
+
+// Output values that the fused digitization of a GEMV covers per workgroup must be whole
+// 32-element chunks: true if every workgroup of the plan writes whole chunks of the output.
+bool gemv_can_digitize_output(const GemvPlan& p, int epi, int64_t rows);
+// true if the plan has a variant that digitizes an fp32 input itself (EpiArgs::xf)
+bool gemv_can_digitize_input(const GemvPlan& p, int epi);
 
 }  // namespace qwg

@@ -258,13 +258,17 @@ struct AttnArgs {
   int64_t kv_stride;
   int n_pos;
   int n_q, n_kv, nc;
-  int T, nsplit;
-  float* part;  // [n_kv][nsplit][NQ][HEAD_DIM + 2]
+  int nsplit;
+  float* part;    // [n_kv][nsplit][NQ][HEAD_DIM + 2]: split max, sum and unnormalised output
   float* out;
   int64_t out_stride;
+  uint32_t* dig;  // digits of the output for the next GEMV (column stride dig_stride words), or null
+  int64_t dig_stride;
+  int dig_kind;
 };
 
-constexpr int ATT_T = 64;
+constexpr int ATT_T = 64;                // positions per split (one per lane)
+constexpr int KROW = HEAD_DIM + 8;       // halves per K row in LDS: the 16-B pad keeps row reads conflict-free
 
 AttnPlan plan_attn(int n_pos, int n_q, int n_kv, int nc) {
   AttnPlan p{};
@@ -276,123 +280,171 @@ AttnPlan plan_attn(int n_pos, int n_q, int n_kv, int nc) {
   return p;
 }
 
-__global__ __launch_bounds__(256) void k_attn_part(AttnArgs a) {
+static size_t attn_lds_bytes(int NQ) {
+  return (size_t)NQ * HEAD_DIM * 4 + (size_t)NQ * ATT_T * 4 + (size_t)ATT_T * KROW * 2 + (size_t)ATT_T * HEAD_DIM * 2;
+}
+
+// One workgroup per (kv head g, split s of ATT_T positions) for all NQ = nc * n_q / n_kv query rows
+// of the group (GQA: the query heads g*G .. g*G+G-1 of every column share K/V head g):
+//   1. the K and V tiles and the queries are staged in LDS (every global load issued up front);
+//   2. wave w scores query rows w, w+4, ... against its lane's position (scale 1/sqrt(128)), with
+//      causal masking per column, and keeps the split's max m, sum l and exp(score - m);
+//   3. the unnormalised output sum_t exp(.) v_t goes to the workspace with m and l;
+// k_attn_merge then combines the splits.
+__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   extern __shared__ float sm[];
   const int g = blockIdx.x, s = blockIdx.y;
   const int G = a.n_q / a.n_kv, NQ = a.nc * G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float* qs = sm;                      // [NQ][HEAD_DIM]
-  float* ps = qs + NQ * HEAD_DIM;      // [NQ][ATT_T]
+  float* qs = sm;                                // [NQ][HEAD_DIM]
+  float* ps = qs + NQ * HEAD_DIM;                // [NQ][ATT_T]
+  uint16_t* ks = (uint16_t*)(ps + NQ * ATT_T);   // [ATT_T][KROW]
+  uint16_t* vs = ks + ATT_T * KROW;              // [ATT_T][HEAD_DIM]
   const int t0 = s * ATT_T;
   const int span = a.n_pos + a.nc - 1;
   const int tn = min(ATT_T, span - t0);
 
-  for (int i = tid; i < NQ * (HEAD_DIM / 4); i += blockDim.x) {
-    const int qi = i / (HEAD_DIM / 4), d4 = i % (HEAD_DIM / 4);
-    const int n = qi / G, j = qi % G;
-    ((float4*)qs)[i] = ((const float4*)(a.q + (int64_t)n * a.q_stride + (int64_t)(g * G + j) * HEAD_DIM))[d4];
-  }
-  // this lane's K row (position t0 + lane) as 64 packed half pairs
-  uint32_t kr[HEAD_DIM / 2];
+  // 1. tiles: thread i takes 16-B piece i & 15 of rows i >> 4, +16, +32, +48 (rows past the span
+  //    re-read the last valid one and are masked below)
   {
-    const int t = min(lane, tn - 1);
-    const uint4* src = (const uint4*)(a.kc + (int64_t)(t0 + t) * a.kv_stride + (int64_t)g * HEAD_DIM);
+    uint4 kv[4], vv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = tid + 256 * j, t = i >> 4, c = i & 15;
+      const int64_t off = (int64_t)(t0 + min(t, tn - 1)) * a.kv_stride + (int64_t)g * HEAD_DIM + c * 8;
+      kv[j] = *(const uint4*)(a.kc + off);
+      vv[j] = *(const uint4*)(a.vc + off);
+    }
+    for (int i = tid; i < NQ * (HEAD_DIM / 4); i += 256) {
+      const int qi = i / (HEAD_DIM / 4), d4 = i % (HEAD_DIM / 4);
+      const int n = qi / G, j = qi % G;
+      ((float4*)qs)[i] = ((const float4*)(a.q + (int64_t)n * a.q_stride + (int64_t)(g * G + j) * HEAD_DIM))[d4];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = tid + 256 * j, t = i >> 4, c = i & 15;
+      *(uint4*)(ks + t * KROW + c * 8) = kv[j];
+      *(uint4*)(vs + t * HEAD_DIM + c * 8) = vv[j];
+    }
+  }
+  __syncthreads();
+
+  // 2. scores and split-local softmax statistics
+  {
+    uint32_t kr[HEAD_DIM / 2];
 #pragma unroll
     for (int i = 0; i < HEAD_DIM / 8; ++i) {
-      const uint4 v = src[i];
+      const uint4 v = *(const uint4*)(ks + lane * KROW + i * 8);
       kr[4 * i] = v.x;
       kr[4 * i + 1] = v.y;
       kr[4 * i + 2] = v.z;
       kr[4 * i + 3] = v.w;
     }
-  }
-  __syncthreads();
-
-  const float scale = 0.08838834764831845f;  // 1/sqrt(128)
-  for (int qi = wave; qi < NQ; qi += 4) {
-    const int n = qi / G;
-    const float4* qv = (const float4*)(qs + qi * HEAD_DIM);
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    const float scale = 0.08838834764831845f;  // 1/sqrt(128)
+    for (int qi = wave; qi < NQ; qi += 4) {
+      const int n = qi / G;
+      const float4* qv = (const float4*)(qs + qi * HEAD_DIM);
+      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll
-    for (int i = 0; i < HEAD_DIM / 4; ++i) {
-      const float4 qq = qv[i];
-      a0 += qq.x * half_bits_to_float(kr[2 * i] & 0xFFFFu);
-      a1 += qq.y * half_bits_to_float(kr[2 * i] >> 16);
-      a2 += qq.z * half_bits_to_float(kr[2 * i + 1] & 0xFFFFu);
-      a3 += qq.w * half_bits_to_float(kr[2 * i + 1] >> 16);
-    }
-    const bool ok = lane < tn && t0 + lane < a.n_pos + n;
-    const float sc = ok ? ((a0 + a1) + (a2 + a3)) * scale : -INFINITY;
-    const float m = wave_max(sc);
-    const float e = ok ? __expf(sc - m) : 0.f;
-    const float l = wave_sum(e);
-    ps[qi * ATT_T + lane] = e;
-    if (lane == 0) {
-      float* pr = a.part + (((int64_t)g * a.nsplit + s) * NQ + qi) * (HEAD_DIM + 2);
-      pr[0] = m;
-      pr[1] = l;
+      for (int i = 0; i < HEAD_DIM / 4; ++i) {
+        const float4 qq = qv[i];
+        a0 += qq.x * half_bits_to_float(kr[2 * i] & 0xFFFFu);
+        a1 += qq.y * half_bits_to_float(kr[2 * i] >> 16);
+        a2 += qq.z * half_bits_to_float(kr[2 * i + 1] & 0xFFFFu);
+        a3 += qq.w * half_bits_to_float(kr[2 * i + 1] >> 16);
+      }
+      const bool ok = lane < tn && t0 + lane < a.n_pos + n;
+      const float sc = ok ? ((a0 + a1) + (a2 + a3)) * scale : -INFINITY;
+      const float m = wave_max(sc);
+      const float e = ok ? __expf(sc - m) : 0.f;
+      const float l = wave_sum(e);
+      ps[qi * ATT_T + lane] = e;
+      if (lane == 0) {
+        float* pr = a.part + (((int64_t)g * a.nsplit + s) * NQ + qi) * (HEAD_DIM + 2);
+        pr[0] = m;
+        pr[1] = l;
+      }
     }
   }
   __syncthreads();
 
-  // unnormalised output: thread = dimensions (2c, 2c+1), query slot = tid / 64 (+4, +8, ...)
-  const int c = tid & 63;
-  for (int qb = tid >> 6; qb < NQ; qb += 4) {
+  // 3. unnormalised output: wave w takes query rows w, w+4, ...; lane = dimensions 2c, 2c+1
+  for (int qb = wave; qb < NQ; qb += 4) {
     const float* pr = ps + qb * ATT_T;
     float o0 = 0.f, o1 = 0.f;
-    const uint32_t* vrow = (const uint32_t*)(a.vc + (int64_t)t0 * a.kv_stride + (int64_t)g * HEAD_DIM) + c;
-    const int64_t vstep = a.kv_stride / 2;
 #pragma unroll 8
     for (int t = 0; t < tn; ++t) {
-      const uint32_t vv = vrow[t * vstep];
+      const uint32_t vv = ((const uint32_t*)(vs + t * HEAD_DIM))[lane];
       const float p = pr[t];
       o0 += p * half_bits_to_float(vv & 0xFFFFu);
       o1 += p * half_bits_to_float(vv >> 16);
     }
     float* dst = a.part + (((int64_t)g * a.nsplit + s) * NQ + qb) * (HEAD_DIM + 2) + 2;
-    dst[2 * c] = o0;
-    dst[2 * c + 1] = o1;
+    *(float2*)(dst + 2 * lane) = make_float2(o0, o1);
   }
 }
 
-// one workgroup per (kv head, query): split statistics through LDS, then each thread merges two
-// output dimensions over all splits
-__global__ __launch_bounds__(64) void k_attn_combine(AttnArgs a) {
-  __shared__ float fs[1024];
-  __shared__ float Ls;
-  const int g = blockIdx.x, qi = blockIdx.y, tid = threadIdx.x;
+// One wave per (kv head g, query row qi): merges the splits in a fixed order,
+//   M = max_s m_s,  o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s,
+// in blocks of 32 splits whose loads all go out together (lane j < 32 holds split j's (m, l), every
+// lane the (2 lane, 2 lane + 1) outputs of the 32 splits), rescaling the running max, sum and
+// output from block to block; then writes the output row (and its activation digits).
+__global__ __launch_bounds__(64) void k_attn_merge(AttnArgs a) {
+  __shared__ float wsh[32];
+  __shared__ float ob[HEAD_DIM];
+  const int g = blockIdx.x, qi = blockIdx.y, lane = threadIdx.x;
   const int G = a.n_q / a.n_kv, NQ = a.nc * G;
-  const float* base = a.part + ((int64_t)g * a.nsplit * NQ + qi) * (HEAD_DIM + 2);
   const int64_t sstride = (int64_t)NQ * (HEAD_DIM + 2);
-  float M = -INFINITY;
-  for (int s = tid; s < a.nsplit; s += 64) M = fmaxf(M, base[s * sstride]);
-  M = wave_max(M);
-  float L = 0.f;
-  for (int s = tid; s < a.nsplit; s += 64) {
-    const float m = base[s * sstride];
-    const float f = m == -INFINITY ? 0.f : __expf(m - M);
-    fs[s] = f;
-    L += f * base[s * sstride + 1];
+  const float* base = a.part + ((int64_t)g * a.nsplit * NQ + qi) * (HEAD_DIM + 2);
+  float M = -INFINITY, L = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int b0 = 0; b0 < a.nsplit; b0 += 32) {
+    const int nb = min(32, a.nsplit - b0);
+    const float2 st = *(const float2*)(base + (b0 + min(lane & 31, nb - 1)) * sstride);
+    float2 ov[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) ov[j] = *(const float2*)(base + (b0 + min(j, nb - 1)) * sstride + 2 + 2 * lane);
+    const bool ok = lane < nb;
+    const float mj = ok ? st.x : -INFINITY;
+    const float Mn = fmaxf(M, wave_max(mj));
+    const float wj = (ok && mj != -INFINITY) ? __expf(mj - Mn) : 0.f;
+    const float keep = M == -INFINITY ? 0.f : __expf(M - Mn);
+    L = L * keep + wave_sum(ok ? wj * st.y : 0.f);
+    if (lane < 32) wsh[lane] = wj;
+    __syncthreads();
+    o0 *= keep;
+    o1 *= keep;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const float w = wsh[j];
+      o0 += w * ov[j].x;
+      o1 += w * ov[j].y;
+    }
+    __syncthreads();
+    M = Mn;
   }
-  L = wave_sum(L);
-  if (tid == 0) Ls = L;
-  __syncthreads();
-  float o0 = 0.f, o1 = 0.f;
-#pragma unroll 4
-  for (int s = 0; s < a.nsplit; ++s) {
-    const float2 v = ((const float2*)(base + s * sstride + 2))[tid];
-    o0 += fs[s] * v.x;
-    o1 += fs[s] * v.y;
-  }
-  const float inv = 1.0f / Ls;
+  const float inv = 1.0f / L;
   const int n = qi / G, j = qi % G;
-  float2* dst = (float2*)(a.out + (int64_t)n * a.out_stride + (int64_t)(g * G + j) * HEAD_DIM);
-  dst[tid] = make_float2(o0 * inv, o1 * inv);
+  const float2 o = make_float2(o0 * inv, o1 * inv);
+  *(float2*)(a.out + (int64_t)n * a.out_stride + (int64_t)(g * G + j) * HEAD_DIM + 2 * lane) = o;
+  if (a.dig) {
+    // the head's 128 outputs are four whole 32-element chunks: four lanes per chunk
+    ob[2 * lane] = o.x;
+    ob[2 * lane + 1] = o.y;
+    __syncthreads();
+    const int m = lane & 3, c = (lane >> 2) & 3;
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = ob[c * 32 + (i < 4 ? 4 * m + i : 16 + 4 * m + i - 4)];
+    const int64_t chunk = (int64_t)(g * G + j) * (HEAD_DIM / 32) + c;
+    digitize_group(v, m, a.dig_kind, a.dig + (int64_t)n * a.dig_stride + chunk * DIG_CHUNK_WORDS, lane < 16);
+  }
 }
 
 hipError_t launch_attn(const float* q, int64_t q_stride, const uint16_t* kc, const uint16_t* vc, int64_t kv_stride,
                        int n_pos, int n_q, int n_kv, int nc, float* out, int64_t out_stride, void* work,
-                       const AttnPlan& p, hipStream_t st) {
+                       const AttnPlan& p, hipStream_t st, uint32_t* dig_out, int64_t dig_stride, int dig_kind) {
+  const int NQ = nc * (n_q / n_kv);
+  if (NQ > 64 || p.nsplit < 1) return hipErrorInvalidValue;
   AttnArgs a;
   a.q = q;
   a.q_stride = q_stride;
@@ -403,18 +455,19 @@ hipError_t launch_attn(const float* q, int64_t q_stride, const uint16_t* kc, con
   a.n_q = n_q;
   a.n_kv = n_kv;
   a.nc = nc;
-  a.T = p.T;
   a.nsplit = p.nsplit;
   a.part = (float*)work;
   a.out = out;
   a.out_stride = out_stride;
-  const int NQ = nc * (n_q / n_kv);
-  if (p.nsplit > 1024) return hipErrorInvalidValue;
-  const size_t lds = (size_t)NQ * HEAD_DIM * 4 + (size_t)NQ * ATT_T * 4;
-  hipLaunchKernelGGL(k_attn_part, dim3(n_kv, p.nsplit), dim3(256), lds, st, a);
-  hipError_t e = hipGetLastError();
+  a.dig = dig_out;
+  a.dig_stride = dig_stride;
+  a.dig_kind = dig_kind;
+  const size_t lds = attn_lds_bytes(NQ);
+  if (lds > 150 * 1024) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_attn, dim3(n_kv, p.nsplit), dim3(256), lds, st, a);
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_attn_combine, dim3(n_kv, NQ), dim3(64), 0, st, a);
+  hipLaunchKernelGGL(k_attn_merge, dim3(n_kv, NQ), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 

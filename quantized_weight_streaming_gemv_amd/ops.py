@@ -73,8 +73,9 @@ def gemv(qtype: int, packed, rows: int, k: int, x, out=None, stream=None):
     return out.reshape(rows) if x.dim() == 1 else out
 
 
-def set_gemv_geometry(waves_per_group: int = 0, rows_per_wave: int = 0) -> None:
-    call("qwg_set_gemv_geometry", waves_per_group, rows_per_wave)
+def set_gemv_geometry(waves_per_group: int = 0, rows_per_wave: int = 0, pipeline_depth: int = 0,
+                      row_passes: int = 0) -> None:
+    call("qwg_set_gemv_geometry", waves_per_group, rows_per_wave, pipeline_depth, row_passes)
 
 
 def rmsnorm(x, g, eps: float, out=None, stream=None):

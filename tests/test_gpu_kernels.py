@@ -147,3 +147,20 @@ def test_swiglu_cosine_argmax(ops):
     x = synth.normal_f32(synth.key(5, 5), 128256)
     x[777] = x[90000] = 50.0
     assert ops.argmax(dev(x)).item() == 777 == oracle.argmax_f32(x)
+
+
+@pytest.mark.parametrize("qt", QTS, ids=[synth.QTYPE_NAMES[q] for q in QTS])
+@pytest.mark.parametrize("geom", [(8, 1, 2, 1), (8, 2, 2, 1), (8, 4, 2, 1), (4, 4, 1, 1), (2, 1, 1, 1)],
+                         ids=lambda g: "w%d_r%d_d%d_p%d" % g)
+def test_gemv_launch_geometries(ops, qt, geom):
+    """Every launch geometry and pipeline depth gives rows within the bound, incl. ragged tails."""
+    ops.set_gemv_geometry(*geom)
+    try:
+        for rows, k in ((130, 512), (77, 8192), (40, 28672)):
+            W = synth.matrix(synth.DEFAULT_DIST[qt], k, rows, tkey=synth.key(3, qt * 1000 + k))
+            x = synth.normal_f32(synth.key(3, 7), k)
+            y = ops.gemv(qt, packed_of(ops, qt, W, rows, k), rows, k, dev(x)).cpu().numpy()
+            yr, ar = oracle.gemv(qt, W, rows, k, x)
+            assert gemv_ok(y, yr, ar).all(), (rows, k)
+    finally:
+        ops.set_gemv_geometry(0, 0, 0, 0)

@@ -171,7 +171,9 @@ def test_context_overflow_is_an_error(qwg):
     m.close()
 
 
-@pytest.mark.parametrize("geom", [(4, 1), (8, 1), (2, 2), (8, 4)], ids=lambda g: "w%d_r%d" % g)
+@pytest.mark.parametrize("geom", [(4, 1, 1, 1), (8, 1, 2, 1), (2, 2, 1, 1), (8, 4, 2, 1), (8, 2, 2, 1),
+                                  (8, 2, 1, 2), (4, 4, 1, 2), (2, 4, 1, 2), (8, 4, 1, 1)],
+                         ids=lambda g: "w%d_r%d_d%d_p%d" % g)
 def test_decode_under_launch_geometries(qwg, geom):
     """Every launch geometry computes the same step (the pair epilogues need two rows per wave)."""
     from quantized_weight_streaming_gemv_amd import ops
@@ -183,4 +185,4 @@ def test_decode_under_launch_geometries(qwg, geom):
             assert rel_l2(g_logits, r["logits"]) < 2e-3
         m.close()
     finally:
-        ops.set_gemv_geometry(0, 0)
+        ops.set_gemv_geometry(0, 0, 0, 0)
