@@ -61,6 +61,66 @@ def token_bytes(wl, n_pos: int) -> int:
     return wl.n_layers * (layer + kv) + head + emb
 
 
+def round_bytes(wl, n_pos: int) -> int:
+    """Algorithmic bytes of one self-speculative round: k draft steps over the first draft_layers
+    layers (+ head, embedding row, their K/V reads) and one (k+1)-column verify over every layer
+    (weights and the K/V rows read once for all columns)."""
+    import synth
+    layer = wl.layer_bytes()
+    head = synth.row_bytes(wl.qtype_head, wl.hidden) * wl.vocab
+    emb = synth.row_bytes(wl.qtype_embed, wl.hidden)
+    kv_row = 2 * wl.n_kv * wl.head_dim * 2
+    k = wl.draft_k
+    draft = sum(wl.draft_layers * (layer + (n_pos + j) * kv_row) + head + emb for j in range(k))
+    verify = wl.n_layers * (layer + (n_pos + k) * kv_row) + head + (k + 1) * emb
+    return draft + verify
+
+
+def measure_read_ceiling(wl):
+    """A plain streaming read (the GEMV's load pattern, no arithmetic) of the gate|up matrix's bytes,
+    rotating over enough copies that each read is cold with respect to the 256 MB last-level cache."""
+    import synth
+    import torch
+    from quantized_weight_streaming_gemv_amd import ops
+    nbytes = (synth.row_bytes(wl.qtype_ffn, wl.hidden) * 2 * wl.ffn + 255) // 256 * 256
+    ncopy = max(4, -(-1200000000 // nbytes))
+    bufs = [torch.empty(nbytes // 4, dtype=torch.int32, device="cuda") for _ in range(ncopy)]
+    for b in bufs:
+        b.fill_(1)
+    sink = ops.read_bytes(bufs[0])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 8 * ncopy
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(n):
+        ops.read_bytes(bufs[i % ncopy], sink=sink)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / n
+    gbps = nbytes / (us * 1e-6) / 1e9
+    log("plain streaming read of %.1f MB: %.2f us, %.1f GB/s" % (nbytes / 1e6, us, gbps))
+    del bufs
+    torch.cuda.empty_cache()
+    return {"bytes": nbytes, "us": round(us, 3), "gbps": round(gbps, 1),
+            "note": "back-to-back launches of a plain streaming-read kernel; includes launch gaps"}
+
+
+def measure_h2d_ceiling():
+    """hipMemcpyAsync from pinned host memory into HBM: 1 GiB copies on one stream, best of 3."""
+    import torch
+    src = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    best = 0.0
+    for _ in range(3):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        dst.copy_(src, non_blocking=True)
+        torch.cuda.synchronize()
+        best = max(best, (1 << 30) / (time.perf_counter() - t0) / 1e9)
+    log("H2D ceiling (pinned, 1 GiB copies): %.1f GB/s" % best)
+    return round(best, 2)
+
+
 def cpu_baseline(wl, n_sample_layers: int):
     """The CPU oracle (fp64, OpenMP over rows) on a bounded sample of the same workload: layers
     0..n-1 and the output head for one token at the first decode position."""
@@ -108,6 +168,9 @@ def main() -> int:
     ap.add_argument("--class-steps", type=int, default=4, help="steps per GEMV class for the per-class table")
     ap.add_argument("--cpu-layers", type=int, default=8, help="oracle layers in the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-read-ceiling", action="store_true", help="skip the plain streaming-read reference")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one device-to-device copy of this many MiB first (scale for PMC byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -121,8 +184,17 @@ def main() -> int:
         import __graft_entry__
         __graft_entry__.build()
     wl = workloads()[args.workload]
+    spec = wl.draft_layers > 0
     total_steps = args.warmup + args.steps * 2 + args.class_steps * 5 + 1
-    max_ctx = wl.n_prior + total_steps + 8
+    max_ctx = wl.n_prior + total_steps * (wl.draft_k + 1 if spec else 1) + 8
+    if args.copy_probe_mib > 0:
+        src = torch.ones(args.copy_probe_mib << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy probe: %d MiB device-to-device" % args.copy_probe_mib)
+        del src, dst
+    read_ceiling = None if args.no_read_ceiling else measure_read_ceiling(wl)
     log("workload %s: %d layers, %.2f GB of weights, KV %d positions" %
         (wl.name, wl.n_layers, wl.model_bytes() / 1e9, wl.n_prior))
     m = synthetic.make_model(wl, max_ctx=max_ctx)
@@ -137,17 +209,24 @@ def main() -> int:
     for _ in range(args.warmup):
         tok, _ = m.decode_step(tok)
 
-    # timed region: K greedy tokens
+    # timed region: K greedy tokens (self-speculative workload: K rounds of k drafts + one verify)
+    n_tok = 0
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        tok, _ = m.decode_step(tok)
+        if spec:
+            out, _ = m.spec_step(tok, wl.draft_layers, wl.draft_k)
+            tok = out[-1]
+            n_tok += len(out)
+        else:
+            tok, _ = m.decode_step(tok)
+            n_tok += 1
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ms_per_step = dt * 1e3 / args.steps
-    tok_s = args.steps / dt
+    tok_s = n_tok / dt
     n_pos_mid = wl.n_prior + args.warmup + args.steps // 2
-    log("decode: %.3f ms/token, %.1f tok/s" % (ms_per_step, tok_s))
+    log("%s: %.3f ms/step, %.1f tok/s (%d tokens)" % ("spec rounds" if spec else "decode", ms_per_step, tok_s, n_tok))
 
     # the same K steps again with HIP events around every gate|up GEMV on the compute stream
     m.set_timing(_lib.T_WGATE)
@@ -181,7 +260,8 @@ def main() -> int:
     log("all GEMVs of a step: %.1f GB/s (%.1f%% of 8 TB/s), %.3f ms of %.3f ms" %
         (gemv_gbps, 100 * gemv_gbps / HBM_PEAK_GBPS, tot_ms, ms_per_step))
     h2d_b, h2d_ms = m.stream_stats()
-    step_bytes = token_bytes(wl, n_pos_mid)
+    step_bytes = round_bytes(wl, n_pos_mid) if spec else token_bytes(wl, n_pos_mid)
+    h2d_ceiling = measure_h2d_ceiling() if h2d_b else None
     m.close()
     del m
     torch.cuda.empty_cache()
@@ -222,7 +302,13 @@ def main() -> int:
                          "RTX 3090 (other hardware and mode; not comparable)",
     }
     if h2d_b:
-        out["h2d"] = {"bytes": h2d_b, "ms": round(h2d_ms, 3), "gbps": round(h2d_b / (h2d_ms * 1e-3) / 1e9, 2)}
+        out["h2d"] = {"bytes": h2d_b, "ms": round(h2d_ms, 3), "gbps": round(h2d_b / (h2d_ms * 1e-3) / 1e9, 2),
+                      "ceiling_gbps": h2d_ceiling}
+    if read_ceiling:
+        out["hbm_read_ceiling"] = read_ceiling
+    if spec:
+        out["spec"] = {"rounds": args.steps, "tokens": n_tok, "ms_per_round": round(ms_per_step, 3),
+                       "draft_layers": wl.draft_layers, "k": wl.draft_k}
     print(json.dumps(out), flush=True)
     return 0
 

@@ -222,14 +222,23 @@ int qwg_model_set_capture(qwg_model* m, int on);
 /* Residual stream captured in the last step: layer = -1 after the embedding, l after layer l;
  * h_out fp32 [hidden] (column 0). Synchronizes. */
 int qwg_model_get_hidden(qwg_model* m, int layer, float* h_out);
-/* Time the kernels of one weight class over the next steps with HIP events on the compute stream
- * (tensor_id QWG_T_WQ = fused QKV, WO, WGATE = fused gate|up, WDOWN, HEAD; -1 = off). */
+/* Time the GEMV kernels of one weight class over the next steps with HIP events on the compute
+ * stream, recorded by the kernel dispatch itself at the kernel's start and end (tensor_id
+ * QWG_T_WQ = fused QKV, WO, WGATE = fused gate|up, WDOWN, HEAD; -1 = off). */
 int qwg_model_set_timing(qwg_model* m, int tensor_id);
 /* Sum of the timed kernels' durations (ms), their count and algorithmic bytes per launch. */
 int qwg_model_get_timing(qwg_model* m, double* total_ms, int64_t* n_launches, int64_t* bytes_per_launch);
 /* Bytes copied host-to-device for streamed layers in the last step, and the copy-stream time (ms). */
 int qwg_model_stream_stats(qwg_model* m, int64_t* h2d_bytes, double* h2d_ms);
 int qwg_sync(qwg_model* m);
+
+/* Plain streaming read of `bytes` (a positive multiple of 16; d_src 16-byte aligned) with the
+ * GEMV's own 16-byte non-temporal load pattern and no arithmetic: the measured achievable HBM
+ * bandwidth, against which the pages' rule that decode speed is bounded by memory bandwidth over
+ * the bytes read per token ([UR] benchmark discussion) is checked.  Writes qwg_read_sink_words()
+ * checksum words to d_sink (device, caller-owned).  Asynchronous on `stream`. */
+size_t qwg_read_sink_words(void);
+int qwg_read_bytes(const void* d_src, size_t bytes, uint32_t* d_sink, void* stream);
 
 /* Pinned host memory (hipHostMalloc) for callers that stage weights. */
 int qwg_host_alloc(size_t bytes, void** out);

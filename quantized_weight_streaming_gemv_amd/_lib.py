@@ -80,6 +80,8 @@ SIGNATURES = {
     "qwg_model_get_timing": (ctypes.c_int, [vp, P_f64, P_i64, P_i64]),
     "qwg_model_stream_stats": (ctypes.c_int, [vp, P_i64, P_f64]),
     "qwg_sync": (ctypes.c_int, [vp]),
+    "qwg_read_sink_words": (sz, []),
+    "qwg_read_bytes": (ctypes.c_int, [vp, sz, vp, vp]),
     "qwg_host_alloc": (ctypes.c_int, [sz, ctypes.POINTER(vp)]),
     "qwg_host_free": (ctypes.c_int, [vp]),
 }

@@ -364,16 +364,15 @@ static int gemv(qwg_model* m, int tensor_class, int qt, const MatView& w, const 
     e.sq_out_stride = m->sq_col;
   }
   const bool timed = m->timing_tensor == tensor_class;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
   if (timed) {
-    hipEvent_t e0 = pool_event(m->tev, m->tev_used);
-    if (!e0) return fail(QWG_E_HIP, "hipEventCreate failed");
-    QWG_HIP(hipEventRecord(e0, m->cs));
+    e0 = pool_event(m->tev, m->tev_used);
+    e1 = pool_event(m->tev, m->tev_used);
+    if (!e0 || !e1) return fail(QWG_E_HIP, "hipEventCreate failed");
   }
-  QWG_HIP(launch_gemv(qt, w, mp.L.k, m->arena + m->xd[in.buf], m->xd_col, nc, epi, e, m->f(m->part), m->cs, gp));
+  QWG_HIP(launch_gemv(qt, w, mp.L.k, m->arena + m->xd[in.buf], m->xd_col, nc, epi, e, m->f(m->part), m->cs, gp, e0,
+                      e1));
   if (timed) {
-    hipEvent_t e1 = pool_event(m->tev, m->tev_used);
-    if (!e1) return fail(QWG_E_HIP, "hipEventCreate failed");
-    QWG_HIP(hipEventRecord(e1, m->cs));
     const int rw = epi == EPI_RESID ? 2 : 1;
     m->t_bytes = gemv_alg_bytes(mp, nc, epi == EPI_SWIGLU ? 0 : rw) + (epi == EPI_SWIGLU ? (int64_t)nc * mp.L.rows / 2 * 4 : 0);
   }
@@ -626,6 +625,16 @@ int qwg_set_gemv_geometry(int waves_per_group, int rows_per_wave, int pipeline_d
     return fail(QWG_E_INVAL, "pipeline_depth must be 0, 1 or 2");
   if (!(row_passes == 0 || row_passes == 1 || row_passes == 2)) return fail(QWG_E_INVAL, "row_passes must be 0, 1 or 2");
   set_gemv_geometry(waves_per_group, rows_per_wave, pipeline_depth, row_passes);
+  return QWG_OK;
+}
+
+size_t qwg_read_sink_words(void) { return (size_t)READ_GRID * 8; }
+
+int qwg_read_bytes(const void* d_src, size_t bytes, uint32_t* d_sink, void* stream) {
+  if (!d_src || !d_sink) return fail(QWG_E_INVAL, "NULL pointer");
+  if (bytes == 0 || bytes % 16) return fail(QWG_E_SHAPE, "bytes must be a positive multiple of 16");
+  if (!aligned16(d_src)) return fail(QWG_E_INVAL, "d_src must be 16-byte aligned");
+  QWG_HIP(launch_read(d_src, (int64_t)bytes, d_sink, (hipStream_t)stream));
   return QWG_OK;
 }
 

@@ -23,6 +23,7 @@
 //     for the next GEMV (each workgroup writes whole 32-element chunks);
 //   * K splits (when the activation for all columns does not fit the LDS budget) write partial
 //     sums that a second kernel adds in a fixed order, so results never depend on timing.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -480,15 +481,29 @@ bool gemv_can_digitize_output(const GemvPlan& p, int epi, int64_t rows) {
   return outs % XCHUNK == 0 && outs <= 64;
 }
 
+// A launch on stream st; with events, hipExtLaunchKernelGGL records them at the kernel's own start
+// and end (no dispatch latency inside the interval).
+struct Dispatch {
+  hipStream_t st;
+  hipEvent_t start, stop;
+};
+template <class Kern, class... Args>
+static void go(const Dispatch& d, Kern kern, dim3 grid, dim3 block, size_t lds, Args... args) {
+  if (d.start || d.stop)
+    hipExtLaunchKernelGGL(kern, grid, block, (uint32_t)lds, d.st, d.start, d.stop, 0u, args...);
+  else
+    hipLaunchKernelGGL(kern, grid, block, lds, d.st, args...);
+}
+
 template <int QT, int NCM, int R, int PD>
 static hipError_t launch_t(const GemvArgs& a, int epi, int ksplit, dim3 grid, dim3 block, size_t lds,
-                           hipStream_t st) {
+                           const Dispatch& d) {
   switch (ksplit > 1 ? EPI_PART : epi) {
-    case EPI_PART: hipLaunchKernelGGL((k_gemv<QT, NCM, R, EPI_PART, PD>), grid, block, lds, st, a); break;
-    case EPI_STORE: hipLaunchKernelGGL((k_gemv<QT, NCM, R, EPI_STORE, PD>), grid, block, lds, st, a); break;
-    case EPI_RESID: hipLaunchKernelGGL((k_gemv<QT, NCM, R, EPI_RESID, PD>), grid, block, lds, st, a); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((k_gemv<QT, NCM, R, EPI_SWIGLU, PD>), grid, block, lds, st, a); break;
-    case EPI_QKV: hipLaunchKernelGGL((k_gemv<QT, NCM, R, EPI_QKV, PD>), grid, block, lds, st, a); break;
+    case EPI_PART: go(d, k_gemv<QT, NCM, R, EPI_PART, PD>, grid, block, lds, a); break;
+    case EPI_STORE: go(d, k_gemv<QT, NCM, R, EPI_STORE, PD>, grid, block, lds, a); break;
+    case EPI_RESID: go(d, k_gemv<QT, NCM, R, EPI_RESID, PD>, grid, block, lds, a); break;
+    case EPI_SWIGLU: go(d, k_gemv<QT, NCM, R, EPI_SWIGLU, PD>, grid, block, lds, a); break;
+    case EPI_QKV: go(d, k_gemv<QT, NCM, R, EPI_QKV, PD>, grid, block, lds, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -496,41 +511,44 @@ static hipError_t launch_t(const GemvArgs& a, int epi, int ksplit, dim3 grid, di
 
 // two row passes (one column, one-ahead loads, residual or SwiGLU epilogue)
 template <int QT, int R>
-static hipError_t launch_p2(const GemvArgs& a, int epi, dim3 grid, dim3 block, size_t lds, hipStream_t st) {
+static hipError_t launch_p2(const GemvArgs& a, int epi, dim3 grid, dim3 block, size_t lds, const Dispatch& d) {
   switch (epi) {
-    case EPI_RESID: hipLaunchKernelGGL((k_gemv<QT, 1, R, EPI_RESID, 1, 2>), grid, block, lds, st, a); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((k_gemv<QT, 1, R, EPI_SWIGLU, 1, 2>), grid, block, lds, st, a); break;
+    case EPI_RESID: go(d, k_gemv<QT, 1, R, EPI_RESID, 1, 2>, grid, block, lds, a); break;
+    case EPI_SWIGLU: go(d, k_gemv<QT, 1, R, EPI_SWIGLU, 1, 2>, grid, block, lds, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 template <int QT>
-static hipError_t launch_fmt(const GemvArgs& a, const GemvPlan& p, int epi, dim3 grid, dim3 block, hipStream_t st) {
+static hipError_t launch_fmt(const GemvArgs& a, const GemvPlan& p, int epi, dim3 grid, dim3 block,
+                             const Dispatch& dd) {
   const int r = p.rows_per_wave, d = p.depth;
+  const size_t lds = p.lds;
   if (a.e.xf) {
     if (!gemv_can_digitize_input(p, epi)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_gemv<QT, 1, 4, EPI_RESID, 1, 1, 512, 1>), grid, block, p.lds, st, a);
+    go(dd, k_gemv<QT, 1, 4, EPI_RESID, 1, 1, 512, 1>, grid, block, lds, a);
     return hipGetLastError();
   }
   if (p.passes == 2) {
     if (p.ncm != 1 || d != 1 || p.ksplit > 1) return hipErrorInvalidValue;
-    if (r == 2) return launch_p2<QT, 2>(a, epi, grid, block, p.lds, st);
-    if (r == 4) return launch_p2<QT, 4>(a, epi, grid, block, p.lds, st);
+    if (r == 2) return launch_p2<QT, 2>(a, epi, grid, block, lds, dd);
+    if (r == 4) return launch_p2<QT, 4>(a, epi, grid, block, lds, dd);
     return hipErrorInvalidValue;
   }
-  if (p.ncm == 1 && r == 1) return d == 2 ? launch_t<QT, 1, 1, 2>(a, epi, p.ksplit, grid, block, p.lds, st)
-                                          : launch_t<QT, 1, 1, 1>(a, epi, p.ksplit, grid, block, p.lds, st);
-  if (p.ncm == 1 && r == 2) return d == 2 ? launch_t<QT, 1, 2, 2>(a, epi, p.ksplit, grid, block, p.lds, st)
-                                          : launch_t<QT, 1, 2, 1>(a, epi, p.ksplit, grid, block, p.lds, st);
-  if (p.ncm == 1) return d == 2 ? launch_t<QT, 1, 4, 2>(a, epi, p.ksplit, grid, block, p.lds, st)
-                                : launch_t<QT, 1, 4, 1>(a, epi, p.ksplit, grid, block, p.lds, st);
-  if (p.ncm == 4) return launch_t<QT, 4, 2, 1>(a, epi, p.ksplit, grid, block, p.lds, st);
-  return launch_t<QT, 8, 2, 1>(a, epi, p.ksplit, grid, block, p.lds, st);
+  if (p.ncm == 1 && r == 1) return d == 2 ? launch_t<QT, 1, 1, 2>(a, epi, p.ksplit, grid, block, lds, dd)
+                                          : launch_t<QT, 1, 1, 1>(a, epi, p.ksplit, grid, block, lds, dd);
+  if (p.ncm == 1 && r == 2) return d == 2 ? launch_t<QT, 1, 2, 2>(a, epi, p.ksplit, grid, block, lds, dd)
+                                          : launch_t<QT, 1, 2, 1>(a, epi, p.ksplit, grid, block, lds, dd);
+  if (p.ncm == 1) return d == 2 ? launch_t<QT, 1, 4, 2>(a, epi, p.ksplit, grid, block, lds, dd)
+                                : launch_t<QT, 1, 4, 1>(a, epi, p.ksplit, grid, block, lds, dd);
+  if (p.ncm == 4) return launch_t<QT, 4, 2, 1>(a, epi, p.ksplit, grid, block, lds, dd);
+  return launch_t<QT, 8, 2, 1>(a, epi, p.ksplit, grid, block, lds, dd);
 }
 
 hipError_t launch_gemv(int qt, const MatView& w, int64_t k, const void* xd, int64_t xd_stride_bytes, int nc, int epi,
-                       const EpiArgs& e, float* part, hipStream_t st, const GemvPlan& p) {
+                       const EpiArgs& e, float* part, hipStream_t st, const GemvPlan& p, hipEvent_t ev_start,
+                       hipEvent_t ev_stop) {
   if (e.dig_out && !gemv_can_digitize_output(p, epi, w.rows)) return hipErrorInvalidValue;
   GemvArgs a;
   a.w = w;
@@ -545,22 +563,25 @@ hipError_t launch_gemv(int qt, const MatView& w, int64_t k, const void* xd, int6
   const int rows_per_wg = p.waves * p.rows_per_wave * p.passes;
   dim3 grid((rows + rows_per_wg - 1) / rows_per_wg, p.ksplit);
   dim3 block(64 * p.waves);
+  // the stop event goes on the last kernel: the GEMV itself, or the split reduction after it
+  const Dispatch d1{st, ev_start, p.ksplit == 1 ? ev_stop : nullptr};
   hipError_t err;
   switch (qt) {
-    case Q8_0: err = launch_fmt<Q8_0>(a, p, epi, grid, block, st); break;
-    case Q4_0: err = launch_fmt<Q4_0>(a, p, epi, grid, block, st); break;
-    case Q4_K: err = launch_fmt<Q4_K>(a, p, epi, grid, block, st); break;
-    case Q5_K: err = launch_fmt<Q5_K>(a, p, epi, grid, block, st); break;
-    case Q6_K: err = launch_fmt<Q6_K>(a, p, epi, grid, block, st); break;
+    case Q8_0: err = launch_fmt<Q8_0>(a, p, epi, grid, block, d1); break;
+    case Q4_0: err = launch_fmt<Q4_0>(a, p, epi, grid, block, d1); break;
+    case Q4_K: err = launch_fmt<Q4_K>(a, p, epi, grid, block, d1); break;
+    case Q5_K: err = launch_fmt<Q5_K>(a, p, epi, grid, block, d1); break;
+    case Q6_K: err = launch_fmt<Q6_K>(a, p, epi, grid, block, d1); break;
     default: return hipErrorInvalidValue;
   }
   if (err != hipSuccess || p.ksplit == 1) return err;
+  const Dispatch d2{st, nullptr, ev_stop};
   dim3 rg((rows + 255) / 256);
   switch (epi) {
-    case EPI_STORE: hipLaunchKernelGGL(k_gemv_reduce<EPI_STORE>, rg, dim3(256), 0, st, part, p.ksplit, nc, rows, e); break;
-    case EPI_RESID: hipLaunchKernelGGL(k_gemv_reduce<EPI_RESID>, rg, dim3(256), 0, st, part, p.ksplit, nc, rows, e); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL(k_gemv_reduce<EPI_SWIGLU>, rg, dim3(256), 0, st, part, p.ksplit, nc, rows, e); break;
-    case EPI_QKV: hipLaunchKernelGGL(k_gemv_reduce<EPI_QKV>, rg, dim3(256), 0, st, part, p.ksplit, nc, rows, e); break;
+    case EPI_STORE: go(d2, k_gemv_reduce<EPI_STORE>, rg, dim3(256), 0, part, p.ksplit, nc, rows, e); break;
+    case EPI_RESID: go(d2, k_gemv_reduce<EPI_RESID>, rg, dim3(256), 0, part, p.ksplit, nc, rows, e); break;
+    case EPI_SWIGLU: go(d2, k_gemv_reduce<EPI_SWIGLU>, rg, dim3(256), 0, part, p.ksplit, nc, rows, e); break;
+    case EPI_QKV: go(d2, k_gemv_reduce<EPI_QKV>, rg, dim3(256), 0, part, p.ksplit, nc, rows, e); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -74,9 +74,11 @@ hipError_t launch_digitize(const float* x, int64_t x_stride, const float* gain, 
                            int64_t out_stride_bytes, float* sq, int64_t sq_stride, hipStream_t st);
 
 // y = W x from activation digits xd (column stride in bytes) with an epilogue; `part` must hold
-// plan.part_bytes when plan.ksplit > 1.  Returns hipSuccess or the launch error.
+// plan.part_bytes when plan.ksplit > 1.  With events, ev_start / ev_stop are recorded at the start of
+// the first kernel and the end of the last one.  Returns hipSuccess or the launch error.
 hipError_t launch_gemv(int qt, const MatView& w, int64_t k, const void* xd, int64_t xd_stride_bytes, int nc, int epi,
-                       const EpiArgs& e, float* part, hipStream_t st, const GemvPlan& plan);
+                       const EpiArgs& e, float* part, hipStream_t st, const GemvPlan& plan,
+                       hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 hipError_t launch_repack(int qt, const uint8_t* canon, int64_t rows, int64_t k, uint8_t* packed, const Layout& L,
                          int64_t dst_row0, int64_t dst_row_step, hipStream_t st);
@@ -105,6 +107,11 @@ hipError_t launch_attn(const float* q, int64_t q_stride, const uint16_t* kc, con
                        int n_pos, int n_q, int n_kv, int nc, float* out, int64_t out_stride, void* work,
                        const AttnPlan& p, hipStream_t st, uint32_t* dig_out = nullptr, int64_t dig_stride = 0,
                        int dig_kind = 0);
+
+// plain streaming read of `bytes` (a multiple of 16) from src; one checksum word per wave into
+// sink (READ_GRID * 8 words)
+constexpr int READ_GRID = 1024;
+hipError_t launch_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t st);
 
 // Output values that the fused digitization of a GEMV covers per workgroup must be whole
 // 32-element chunks: true if every workgroup of the plan writes whole chunks of the output.

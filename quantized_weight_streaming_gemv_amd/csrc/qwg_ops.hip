@@ -471,4 +471,39 @@ hipError_t launch_attn(const float* q, int64_t q_stride, const uint16_t* kc, con
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------------------------------ plain read
+
+// Streaming read of n16 16-byte words: wave w of the grid reads one contiguous segment, lane l the
+// words l, l+64, ... of it, four 16-B non-temporal loads in flight per lane (the GEMV's own load
+// pattern without its arithmetic).  One XOR checksum per wave keeps the loads alive.
+__global__ __launch_bounds__(512) void k_read(const uint4* __restrict__ p, int64_t n16, int64_t per_wave,
+                                              uint32_t* sink) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 6);
+  const int64_t beg = wave * per_wave, end = min(beg + per_wave, n16);
+  uint32_t acc = 0;
+  for (int64_t i = beg + lane; i < end; i += 256) {
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t j = i + 64 * u;
+      v[u] = j < end ? ld_stream_u4((const uint8_t*)(p + j)) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc ^= __shfl_xor(acc, off);
+  if (lane == 0) sink[wave] = acc;
+}
+
+hipError_t launch_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t st) {
+  const int64_t n16 = bytes / 16;
+  const int grid = READ_GRID;
+  const int64_t waves = (int64_t)grid * 8;
+  const int64_t per_wave = ((n16 + waves - 1) / waves + 63) / 64 * 64;
+  hipLaunchKernelGGL(k_read, dim3(grid), dim3(512), 0, st, (const uint4*)src, n16, per_wave, sink);
+  return hipGetLastError();
+}
+
 }  // namespace qwg

@@ -139,3 +139,13 @@ def argmax(x, out=None, stream=None):
         out = torch.empty(1, dtype=torch.int32, device=x.device)
     call("qwg_argmax", _ptr(x), x.numel(), _ptr(out), _stream(stream))
     return out
+
+
+def read_bytes(src, nbytes: Optional[int] = None, sink=None, stream=None):
+    """Plain streaming read of a device tensor's bytes (the achievable-bandwidth reference)."""
+    torch = _torch()
+    n = src.numel() * src.element_size() if nbytes is None else nbytes
+    if sink is None:
+        sink = torch.empty(int(lib().qwg_read_sink_words()), dtype=torch.int32, device=src.device)
+    call("qwg_read_bytes", _ptr(src), n, _ptr(sink), _stream(stream))
+    return sink
