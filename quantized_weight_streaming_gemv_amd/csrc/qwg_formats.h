@@ -308,6 +308,12 @@ __host__ __device__ inline void digitize_chunk(const float* x, int kind, uint32_
 // lane shuffles; lane m writes its six digit words and lane 0 the ChunkDesc at oc (a chunk base of
 // DIG_CHUNK_WORDS words).  All four lanes must call it (write = false lets a lane take part without
 // storing).  Same digits as digitize_chunk.
+// (byte j of a) << 8 | (byte j of b), j < 4: one v_perm_b32 (bytes 0..3 of the selector pick from
+// the second operand, 4..7 from the first, 12 gives zero)
+__device__ inline uint32_t byte_gather(uint32_t a, uint32_t b, uint32_t j) {
+  return __builtin_amdgcn_perm(a, b, 0x0C0C0000u | ((4u + j) << 8) | j);
+}
+
 // put(i, word) stores digit word i (0..23) or descriptor word i (24..27) of the chunk.
 template <class Put>
 __device__ inline void digitize_group_to(const float* v, int m, int kind, Put&& put, bool write) {
@@ -332,19 +338,26 @@ __device__ inline void digitize_group_to(const float* v, int m, int kind, Put&& 
   sb += __shfl_xor(sb, 1);
   sb += __shfl_xor(sb, 2);
   if (!write) return;
+  // Adding 0x888888 (0x808080) and flipping the top bit of every nibble (byte) leaves balanced digit
+  // l of x_fix, as a 4-bit (8-bit) two's-complement number, in nibble (byte) l of u.  The digit
+  // words are then byte gathers: v_perm_b32 picks byte j of two words into two byte lanes.
   if (kind == DIG_NIB) {
-    // word m*6 + l, nibble 2b + h = digit l of element 16h + 4m + b  (v[4h + b])
-    uint32_t u[8];
+    // word m*6 + l, nibble 2b + h = digit l of element 16h + 4m + b  (v[4h + b]).  Byte b of a
+    // word pairs element b (low nibble) with element 4+b (high nibble): e[b] holds those pairs for
+    // the even levels (byte j = level 2j), o[b] for the odd ones.
+    uint32_t e[4], o[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) u[i] = (uint32_t)(xf[i] + 0x888888);
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t lo = (uint32_t)(xf[b] + 0x888888) ^ 0x888888u;
+      const uint32_t hi = (uint32_t)(xf[4 + b] + 0x888888) ^ 0x888888u;
+      e[b] = (lo & 0x0F0F0Fu) | ((hi & 0x0F0F0Fu) << 4);
+      o[b] = ((lo >> 4) & 0x0F0F0Fu) | (hi & 0xF0F0F0u);
+    }
 #pragma unroll
     for (int l = 0; l < 6; ++l) {
-      uint32_t w = 0;
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) w |= ((u[4 * h + b] >> (4 * l)) & 15u) << (4 * (2 * b + h));
-      put(m * 6 + l, w ^ 0x88888888u);
+      const uint32_t* E = (l & 1) ? o : e;
+      const uint32_t j = (uint32_t)(l >> 1);
+      put(m * 6 + l, byte_gather(E[1], E[0], j) | (byte_gather(E[3], E[2], j) << 16));
     }
   } else {
     // word (h*4 + m)*3 + l, byte b = digit l of element 16h + 4m + b
@@ -352,14 +365,10 @@ __device__ inline void digitize_group_to(const float* v, int m, int kind, Put&& 
     for (int h = 0; h < 2; ++h) {
       uint32_t u[4];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) u[b] = (uint32_t)(xf[4 * h + b] + 0x808080);
+      for (int b = 0; b < 4; ++b) u[b] = (uint32_t)(xf[4 * h + b] + 0x808080) ^ 0x808080u;
 #pragma unroll
-      for (int l = 0; l < 3; ++l) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) w |= ((u[b] >> (8 * l)) & 255u) << (8 * b);
-        put((h * 4 + m) * 3 + l, w ^ 0x80808080u);
-      }
+      for (int l = 0; l < 3; ++l)
+        put((h * 4 + m) * 3 + l, byte_gather(u[1], u[0], (uint32_t)l) | (byte_gather(u[3], u[2], (uint32_t)l) << 16));
     }
   }
   if (m == 0) {

@@ -269,6 +269,8 @@ struct AttnArgs {
 
 constexpr int ATT_T = 64;                // positions per split (one per lane)
 constexpr int KROW = HEAD_DIM + 8;       // halves per K row in LDS: the 16-B pad keeps row reads conflict-free
+constexpr int ATT_WAVES = 4;             // waves per workgroup (8 read the K/V tiles twice as often and ran slower)
+constexpr int ATT_THREADS = 64 * ATT_WAVES;
 
 AttnPlan plan_attn(int n_pos, int n_q, int n_kv, int nc) {
   AttnPlan p{};
@@ -287,11 +289,11 @@ static size_t attn_lds_bytes(int NQ) {
 // One workgroup per (kv head g, split s of ATT_T positions) for all NQ = nc * n_q / n_kv query rows
 // of the group (GQA: the query heads g*G .. g*G+G-1 of every column share K/V head g):
 //   1. the K and V tiles and the queries are staged in LDS (every global load issued up front);
-//   2. wave w scores query rows w, w+4, ... against its lane's position (scale 1/sqrt(128)), with
+//   2. wave w scores query rows w, w+ATT_WAVES, ... against its lane's position (scale 1/sqrt(128)), with
 //      causal masking per column, and keeps the split's max m, sum l and exp(score - m);
 //   3. the unnormalised output sum_t exp(.) v_t goes to the workspace with m and l;
 // k_attn_merge then combines the splits.
-__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
+__global__ __launch_bounds__(ATT_THREADS) void k_attn(AttnArgs a) {
   extern __shared__ float sm[];
   const int g = blockIdx.x, s = blockIdx.y;
   const int G = a.n_q / a.n_kv, NQ = a.nc * G;
@@ -304,25 +306,26 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   const int span = a.n_pos + a.nc - 1;
   const int tn = min(ATT_T, span - t0);
 
-  // 1. tiles: thread i takes 16-B piece i & 15 of rows i >> 4, +16, +32, +48 (rows past the span
-  //    re-read the last valid one and are masked below)
+  // 1. tiles: thread i takes 16-B piece i & 15 of rows i >> 4, + ATT_THREADS / 16, ... (rows past
+  //    the span re-read the last valid one and are masked below)
+  constexpr int TP = ATT_T * 16 / ATT_THREADS;  // tile pieces per thread
   {
-    uint4 kv[4], vv[4];
+    uint4 kv[TP], vv[TP];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = tid + 256 * j, t = i >> 4, c = i & 15;
+    for (int j = 0; j < TP; ++j) {
+      const int i = tid + ATT_THREADS * j, t = i >> 4, c = i & 15;
       const int64_t off = (int64_t)(t0 + min(t, tn - 1)) * a.kv_stride + (int64_t)g * HEAD_DIM + c * 8;
       kv[j] = *(const uint4*)(a.kc + off);
       vv[j] = *(const uint4*)(a.vc + off);
     }
-    for (int i = tid; i < NQ * (HEAD_DIM / 4); i += 256) {
+    for (int i = tid; i < NQ * (HEAD_DIM / 4); i += ATT_THREADS) {
       const int qi = i / (HEAD_DIM / 4), d4 = i % (HEAD_DIM / 4);
       const int n = qi / G, j = qi % G;
       ((float4*)qs)[i] = ((const float4*)(a.q + (int64_t)n * a.q_stride + (int64_t)(g * G + j) * HEAD_DIM))[d4];
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = tid + 256 * j, t = i >> 4, c = i & 15;
+    for (int j = 0; j < TP; ++j) {
+      const int i = tid + ATT_THREADS * j, t = i >> 4, c = i & 15;
       *(uint4*)(ks + t * KROW + c * 8) = kv[j];
       *(uint4*)(vs + t * HEAD_DIM + c * 8) = vv[j];
     }
@@ -341,7 +344,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
       kr[4 * i + 3] = v.w;
     }
     const float scale = 0.08838834764831845f;  // 1/sqrt(128)
-    for (int qi = wave; qi < NQ; qi += 4) {
+    for (int qi = wave; qi < NQ; qi += ATT_WAVES) {
       const int n = qi / G;
       const float4* qv = (const float4*)(qs + qi * HEAD_DIM);
       float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
@@ -368,8 +371,8 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   }
   __syncthreads();
 
-  // 3. unnormalised output: wave w takes query rows w, w+4, ...; lane = dimensions 2c, 2c+1
-  for (int qb = wave; qb < NQ; qb += 4) {
+  // 3. unnormalised output: wave w takes query rows w, w+ATT_WAVES, ...; lane = dimensions 2c, 2c+1
+  for (int qb = wave; qb < NQ; qb += ATT_WAVES) {
     const float* pr = ps + qb * ATT_T;
     float o0 = 0.f, o1 = 0.f;
 #pragma unroll 8
@@ -386,35 +389,35 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
 
 // One wave per (kv head g, query row qi): merges the splits in a fixed order,
 //   M = max_s m_s,  o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s,
-// in blocks of 32 splits whose loads all go out together (lane j < 32 holds split j's (m, l), every
-// lane the (2 lane, 2 lane + 1) outputs of the 32 splits), rescaling the running max, sum and
+// in blocks of 64 splits whose loads all go out together (lane j holds split j's (m, l), every lane
+// the (2 lane, 2 lane + 1) outputs of the 64 splits), rescaling the running max, sum and
 // output from block to block; then writes the output row (and its activation digits).
 __global__ __launch_bounds__(64) void k_attn_merge(AttnArgs a) {
-  __shared__ float wsh[32];
+  __shared__ float wsh[64];
   __shared__ float ob[HEAD_DIM];
   const int g = blockIdx.x, qi = blockIdx.y, lane = threadIdx.x;
   const int G = a.n_q / a.n_kv, NQ = a.nc * G;
   const int64_t sstride = (int64_t)NQ * (HEAD_DIM + 2);
   const float* base = a.part + ((int64_t)g * a.nsplit * NQ + qi) * (HEAD_DIM + 2);
   float M = -INFINITY, L = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int b0 = 0; b0 < a.nsplit; b0 += 32) {
-    const int nb = min(32, a.nsplit - b0);
-    const float2 st = *(const float2*)(base + (b0 + min(lane & 31, nb - 1)) * sstride);
-    float2 ov[32];
+  for (int b0 = 0; b0 < a.nsplit; b0 += 64) {
+    const int nb = min(64, a.nsplit - b0);
+    const float2 st = *(const float2*)(base + (b0 + min(lane, nb - 1)) * sstride);
+    float2 ov[64];
 #pragma unroll
-    for (int j = 0; j < 32; ++j) ov[j] = *(const float2*)(base + (b0 + min(j, nb - 1)) * sstride + 2 + 2 * lane);
+    for (int j = 0; j < 64; ++j) ov[j] = *(const float2*)(base + (b0 + min(j, nb - 1)) * sstride + 2 + 2 * lane);
     const bool ok = lane < nb;
     const float mj = ok ? st.x : -INFINITY;
     const float Mn = fmaxf(M, wave_max(mj));
     const float wj = (ok && mj != -INFINITY) ? __expf(mj - Mn) : 0.f;
     const float keep = M == -INFINITY ? 0.f : __expf(M - Mn);
     L = L * keep + wave_sum(ok ? wj * st.y : 0.f);
-    if (lane < 32) wsh[lane] = wj;
+    wsh[lane] = wj;
     __syncthreads();
     o0 *= keep;
     o1 *= keep;
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
+    for (int j = 0; j < 64; ++j) {
       const float w = wsh[j];
       o0 += w * ov[j].x;
       o1 += w * ov[j].y;
@@ -464,7 +467,7 @@ hipError_t launch_attn(const float* q, int64_t q_stride, const uint16_t* kc, con
   a.dig_kind = dig_kind;
   const size_t lds = attn_lds_bytes(NQ);
   if (lds > 150 * 1024) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_attn, dim3(n_kv, p.nsplit), dim3(256), lds, st, a);
+  hipLaunchKernelGGL(k_attn, dim3(n_kv, p.nsplit), dim3(ATT_THREADS), lds, st, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_attn_merge, dim3(n_kv, NQ), dim3(64), 0, st, a);
