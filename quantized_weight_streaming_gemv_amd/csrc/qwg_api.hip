@@ -428,13 +428,24 @@ static int layer_kernels(qwg_model* m, int l, const uint8_t* base, int nc, int p
   InDigits in_ffn;
   in_ffn.buf = 0;
   in_ffn.rms = true;
-  if ((rc = gemv(m, QWG_T_WGATE, d.qtype_ffn, view_at(base, P.gu), P.gu, in_ffn, nc, EPI_SWIGLU, s, OutDigits{})))
+  // silu(gate) * up reaches the down GEMV as digits written by the gate|up epilogue when its launch
+  // geometry covers whole 32-output chunks, else the down GEMV digitizes the fp32 vector itself
+  const int64_t gu_rows = P.gu.L.rows;
+  const bool act_digits =
+      gemv_can_digitize_output(plan_gemv(d.qtype_ffn, gu_rows, H, nc, EPI_SWIGLU), EPI_SWIGLU, gu_rows);
+  OutDigits to_down;
+  if (act_digits) {
+    to_down.buf = 1;
+    to_down.qt = d.qtype_ffn;
+  }
+  if ((rc = gemv(m, QWG_T_WGATE, d.qtype_ffn, view_at(base, P.gu), P.gu, in_ffn, nc, EPI_SWIGLU, s, to_down)))
     return rc;
-  // the down GEMV digitizes silu(gate) * up itself
   InDigits in_act;
   in_act.buf = 1;
-  in_act.xf = m->f(m->act);
-  in_act.xf_stride = F;
+  if (!act_digits) {
+    in_act.xf = m->f(m->act);
+    in_act.xf_stride = F;
+  }
   if ((rc = gemv(m, QWG_T_WDOWN, d.qtype_ffn, view_at(base, P.down), P.down, in_act, nc, EPI_RESID, r, next)))
     return rc;
   return QWG_OK;

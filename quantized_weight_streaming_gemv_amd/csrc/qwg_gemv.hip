@@ -141,11 +141,12 @@ constexpr int XSLOTS = DIG_CHUNK_WORDS / 4;  // 16-B slots per activation chunk 
 
 // PD: weight loads in flight ahead of the chunk being computed (1 or 2 iterations of 64 chunks).
 // P: row passes -- a wave finishes R rows, then the next R rows nw*R further on, so a workgroup
-// covers nw*R*P rows at the registers of R (the next pass's first loads are issued before the
-// finished pass is reduced).  LB: the launch bound.  XIN: the input arrives as fp32 (EpiArgs::xf)
+// covers nw*R*P rows at the registers of R.  Two-pass kernels are held to 128 registers (four
+// waves per SIMD, two workgroups per CU); issuing the second pass's loads before the first is
+// reduced needed more and measured slower.  LB: the launch bound.  XIN: the input arrives as fp32 (EpiArgs::xf)
 // and every workgroup digitizes the part it needs straight into LDS.
 template <int QT, int NCM, int R, int EPI, int PD, int P = 1, int LB = 512, int XIN = 0>
-__global__ __launch_bounds__(LB) void k_gemv(GemvArgs a) {
+__global__ __launch_bounds__(LB, (P == 2 ? 4 : 1)) void k_gemv(GemvArgs a) {
   static_assert(P == 1 || PD == 1, "row passes use the one-ahead pipeline");
   using F = Fmt<QT>;
   constexpr int CW = F::CW;
@@ -225,6 +226,10 @@ __global__ __launch_bounds__(LB) void k_gemv(GemvArgs a) {
   for (int pass = 0; pass < P; ++pass) {
     const int row0 = wg_row0 + pass * nw * R + wave * R;
     if (row0 >= rows) break;
+    if (pass > 0) {
+      set_rows(row0);
+      fetch(b0, lane);
+    }
     float acc[R][NCM];
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -280,11 +285,6 @@ __global__ __launch_bounds__(LB) void k_gemv(GemvArgs a) {
         fetch(b1, cl + 256);
         chunk(b2, cl + 128);
       }
-    }
-    // the next pass's first loads go out before this pass is reduced
-    if (pass + 1 < P && row0 + nw * R < rows) {
-      set_rows(row0 + nw * R);
-      fetch(b0, lane);
     }
 
     // 4. reduce over the 64 lanes (every lane ends with every total)
@@ -427,8 +427,10 @@ void set_gemv_geometry(int waves, int rows_per_wave, int depth, int passes) {
   g_passes = passes;
 }
 
+// formats whose 4-row two-pass kernel fits 128 registers without spilling
+static bool two_pass_ok(int qt) { return qt == Q4_0 || qt == Q4_K || qt == Q8_0; }
+
 GemvPlan plan_gemv(int qt, int64_t rows, int64_t k, int nc, int epi) {
-  (void)qt;
   (void)rows;
   // the RoPE and SwiGLU epilogues combine rows (2i, 2i+1), which must sit in one wave
   const bool pairs = epi == EPI_QKV || epi == EPI_SWIGLU;
@@ -452,10 +454,11 @@ GemvPlan plan_gemv(int qt, int64_t rows, int64_t k, int nc, int epi) {
   p.part_bytes = p.ksplit > 1 ? (size_t)p.ksplit * nc * rows * sizeof(float) : 0;
   // one column, 8 waves (measured on the 70B shapes): two rows per wave for the plain and QKV
   // epilogues; four for SwiGLU and for the residual epilogue, whose 32 rows per workgroup are a
-  // whole chunk of the next GEMV's input digits, written by this kernel.  (A SwiGLU workgroup
-  // would need 64 rows for that: as 16 waves, 8 rows per wave or two passes it ran slower than
-  // 32 rows plus a separate digitization.)
+  // whole chunk of the next GEMV's input digits, written by this kernel.  SwiGLU needs 64 rows
+  // (32 outputs) for that: two passes of 32, for the formats whose 4-row kernel fits 128
+  // registers (16 waves or 8 rows per wave ran slower).
   if (p.ncm == 1) p.rows_per_wave = (epi == EPI_RESID || epi == EPI_SWIGLU) ? 4 : 2;
+  if (p.ncm == 1 && epi == EPI_SWIGLU && p.ksplit == 1 && two_pass_ok(qt)) p.passes = 2;
   // explicit overrides (tuning and tests)
   if (g_waves == 2 || g_waves == 4 || g_waves == 8) p.waves = g_waves;
   if (p.ncm == 1 && (g_rows == 1 || g_rows == 2 || g_rows == 4)) p.rows_per_wave = g_rows;
