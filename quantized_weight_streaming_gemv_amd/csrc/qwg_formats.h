@@ -6,8 +6,9 @@
 // break 16-byte alignment and mix scales with quants, so at load time every matrix is
 // rearranged ("packed") into separate row-major regions with the same payload bytes:
 //
-//   region Q : the quant bytes, 16 B per "chunk" (Q8_0: 16 weights; others: 32 weights),
-//              chunk c of row r at Q + r*q_row + 16c  -> a wave reads 1 KiB contiguous
+//   region Q : the quant bytes, 16 B per "chunk" (Q8_0: 16 weights; others: 32 weights), chunk c
+//              of row r at Q + r*q_row + 16c, or row-interleaved by groups of 4 rows when the
+//              shape allows (slot_row below) -> a wave reads 1 KiB contiguous per row and load
 //   region A : Q8_0 / Q4_0 fp16 d per block; Q4_K / Q5_K 16-B superblock header (d, dmin and the
 //              sixteen 6-bit scales/mins, re-laid out below); Q6_K 8 B of 2-bit highs per chunk
 //   region B : Q5_K 4 B of fifth bits per chunk; Q6_K the chunk's two int8 sub-block scales
@@ -70,6 +71,7 @@ struct Layout {
   int64_t b_off, b_row;
   int64_t c_off, c_row;
   int64_t total;
+  int32_t ilv;  // per-chunk regions row-interleaved in groups of 4 rows (see slot_row)
 };
 
 __host__ __device__ inline int64_t align256(int64_t v) { return (v + 255) & ~(int64_t)255; }
@@ -94,6 +96,7 @@ __host__ __device__ inline Layout make_layout(int qt, int64_t rows, int64_t k) {
   L.b_off = align256(L.a_off + rows * L.a_row);
   L.c_off = align256(L.b_off + rows * L.b_row);
   L.total = align256(L.c_off + rows * L.c_row);
+  L.ilv = (rows % 4 == 0 && L.nch % 64 == 0) ? 1 : 0;
   return L;
 }
 
@@ -106,6 +109,7 @@ struct MatView {
   int64_t q_row, a_row, b_row, c_row;
   int32_t nch;
   int32_t rows;
+  int32_t ilv;
 };
 
 __host__ __device__ inline MatView make_view(const void* base, const Layout& L) {
@@ -121,6 +125,7 @@ __host__ __device__ inline MatView make_view(const void* base, const Layout& L) 
   v.c_row = L.c_row;
   v.nch = (int32_t)L.nch;
   v.rows = (int32_t)L.rows;
+  v.ilv = L.ilv;
   return v;
 }
 
@@ -454,7 +459,8 @@ __host__ __device__ inline float byte_value2(const uint32_t* wa, const uint32_t*
 //
 // Each Fmt<QT> provides
 //   CW (weights per chunk)
-//   Raw load(view, row, chunk)          -- the chunk's quant bytes and scale data
+//   Raw load(view, row, chunk, slot)    -- the chunk's quant bytes and scale data (slot: the chunk's
+//                                          place in the per-chunk regions, slot_row + slot_chunk)
 //   decode(raw, chunk, w[CW])           -- exact fp32 weights in chunk order (for dequantize);
 //                                          a zero weight is +0 ("+ 0.0f" turns -0 into +0)
 //   U unpack(raw, chunk, sub)           -- integer quant words for the dot plus the chunk's fp32
@@ -469,6 +475,17 @@ __host__ __device__ inline uint32_t roff(int64_t row, int64_t row_bytes, uint32_
   return (uint32_t)row * (uint32_t)row_bytes + within;
 }
 
+// Per-chunk regions (one e-byte piece per chunk: quants 16 B, Q5_K fifth bits 4 B, Q6_K high bits
+// 8 B and scales 2 B) store the piece of (row, chunk c) at e * slot(row, c).  Row-major: slot =
+// row * nch + c.  Row-interleaved (ilv): rows come in groups of 4, and within a group the pieces of
+// 64 consecutive chunks of row 0, row 1, row 2, row 3 follow each other -- so the R <= 4 rows a
+// wave reads for 64 chunks are one contiguous span (fewer concurrent DRAM streams than 4 rows).
+// slot = slot_row(row) + slot_chunk(c), so a kernel adds one per-row and one per-chunk term.
+__host__ __device__ inline uint32_t slot_row(int32_t ilv, int64_t nch, int64_t row) {
+  return ilv ? ((uint32_t)row >> 2) * 4u * (uint32_t)nch + ((uint32_t)row & 3u) * 64u : (uint32_t)row * (uint32_t)nch;
+}
+__host__ __device__ inline uint32_t slot_chunk(int32_t ilv, uint32_t c) { return ilv ? (c >> 6) * 256u + (c & 63u) : c; }
+
 template <int QT>
 struct Fmt;
 
@@ -479,9 +496,9 @@ struct Fmt<Q8_0> {
     uint4 q;
     uint32_t d;
   };
-  __host__ __device__ static Raw load(const MatView& v, int64_t row, int c) {
+  __host__ __device__ static Raw load(const MatView& v, int64_t row, int c, uint32_t slot) {
     Raw r;
-    r.q = ld_stream_u4(v.q + roff(row, v.q_row, (uint32_t)c * 16u));
+    r.q = ld_stream_u4(v.q + slot * 16u);
     r.d = ld<uint16_t>(v.a + roff(row, v.a_row, (uint32_t)(c >> 1) * 2u));
     return r;
   }
@@ -517,9 +534,9 @@ struct Fmt<Q4_0> {
     uint4 q;
     uint32_t d;
   };
-  __host__ __device__ static Raw load(const MatView& v, int64_t row, int c) {
+  __host__ __device__ static Raw load(const MatView& v, int64_t row, int c, uint32_t slot) {
     Raw r;
-    r.q = ld_stream_u4(v.q + roff(row, v.q_row, (uint32_t)c * 16u));
+    r.q = ld_stream_u4(v.q + slot * 16u);
     r.d = ld<uint16_t>(v.a + roff(row, v.a_row, (uint32_t)c * 2u));
     return r;
   }
@@ -558,9 +575,9 @@ struct Fmt<Q4_K> {
     uint4 q;
     uint4 h;  // d | dmin << 16, then the re-laid-out scales and mins
   };
-  __host__ __device__ static Raw load(const MatView& v, int64_t row, int c) {
+  __host__ __device__ static Raw load(const MatView& v, int64_t row, int c, uint32_t slot) {
     Raw r;
-    r.q = ld_stream_u4(v.q + roff(row, v.q_row, (uint32_t)c * 16u));
+    r.q = ld_stream_u4(v.q + slot * 16u);
     r.h = ld<uint4>(v.a + roff(row, v.a_row, (uint32_t)(c >> 3) * 16u));
     return r;
   }
@@ -611,11 +628,11 @@ struct Fmt<Q5_K> {
     uint4 h;
     uint32_t qh;
   };
-  __host__ __device__ static Raw load(const MatView& v, int64_t row, int c) {
+  __host__ __device__ static Raw load(const MatView& v, int64_t row, int c, uint32_t slot) {
     Raw r;
-    r.q = ld_stream_u4(v.q + roff(row, v.q_row, (uint32_t)c * 16u));
+    r.q = ld_stream_u4(v.q + slot * 16u);
     r.h = ld<uint4>(v.a + roff(row, v.a_row, (uint32_t)(c >> 3) * 16u));
-    r.qh = ld_stream_u1(v.b + roff(row, v.b_row, (uint32_t)c * 4u));
+    r.qh = ld_stream_u1(v.b + slot * 4u);
     return r;
   }
   // the 5-bit quants of word m as bytes: low-nibble weights and high-nibble weights
@@ -668,11 +685,11 @@ struct Fmt<Q6_K> {
     uint32_t sc;  // two int8 scales: byte 0 -> weights 0..15, byte 1 -> 16..31
     uint32_t d;
   };
-  __host__ __device__ static Raw load(const MatView& v, int64_t row, int c) {
+  __host__ __device__ static Raw load(const MatView& v, int64_t row, int c, uint32_t slot) {
     Raw r;
-    r.q = ld_stream_u4(v.q + roff(row, v.q_row, (uint32_t)c * 16u));
-    r.qh = ld_stream_u2(v.a + roff(row, v.a_row, (uint32_t)c * 8u));
-    r.sc = ld<uint16_t>(v.b + roff(row, v.b_row, (uint32_t)c * 2u));
+    r.q = ld_stream_u4(v.q + slot * 16u);
+    r.qh = ld_stream_u2(v.a + slot * 8u);
+    r.sc = ld<uint16_t>(v.b + slot * 2u);
     r.d = ld<uint16_t>(v.c + roff(row, v.c_row, (uint32_t)(c >> 3) * 2u));
     return r;
   }
@@ -752,23 +769,28 @@ __host__ __device__ inline void pack_nibbles(const int* q, uint8_t* dst) {
 
 __host__ __device__ inline void repack_block(int qt, const uint8_t* blk, uint8_t* base, const Layout& L, int64_t row,
                                              int64_t b) {
-  uint8_t* Q = base + row * L.q_row;
+  // per-block pieces (row-major) and per-chunk pieces (coff: possibly row-interleaved)
   uint8_t* A = base + L.a_off + row * L.a_row;
-  uint8_t* B = base + L.b_off + row * L.b_row;
   uint8_t* C = base + L.c_off + row * L.c_row;
+  const uint32_t srow = slot_row(L.ilv, L.nch, row);
+  auto slot = [&](int64_t c) { return (int64_t)(srow + slot_chunk(L.ilv, (uint32_t)c)); };
+  auto Qc = [&](int64_t c) { return base + 16 * slot(c); };
+  auto Ac = [&](int64_t c, uint32_t e) { return base + L.a_off + e * slot(c); };
+  auto Bc = [&](int64_t c, uint32_t e) { return base + L.b_off + e * slot(c); };
   switch (qt) {
     case Q8_0: {
       A[2 * b] = blk[0];
       A[2 * b + 1] = blk[1];
-      put16(Q + (2 * b) * 16, blk + 2);
-      put16(Q + (2 * b + 1) * 16, blk + 18);
+      put16(Qc(2 * b), blk + 2);
+      put16(Qc(2 * b + 1), blk + 18);
       break;
     }
     case Q4_0: {
       A[2 * b] = blk[0];
       A[2 * b + 1] = blk[1];
       // canonical Q4_0 already pairs weight j with j + 16; nibbles become q XOR 8
-      for (int j = 0; j < 16; ++j) Q[b * 16 + j] = (uint8_t)(blk[2 + j] ^ 0x88);
+      uint8_t* q = Qc(b);
+      for (int j = 0; j < 16; ++j) q[j] = (uint8_t)(blk[2 + j] ^ 0x88);
       break;
     }
     case Q4_K:
@@ -795,7 +817,7 @@ __host__ __device__ inline void repack_block(int qt, const uint8_t* blk, uint8_t
         for (int e = 0; e < 32; ++e)
           q[e] = qt == Q4_K ? (canon_q4k(qs, 32 * s + e) ^ 8) : canon_q5k(qh, qs, 32 * s + e);
         const int64_t c = 8 * b + s;
-        pack_nibbles(q, Q + c * 16);
+        pack_nibbles(q, Qc(c));
         if (qt == Q5_K) {
           uint32_t bits = 0;
           for (int m = 0; m < 4; ++m)
@@ -803,7 +825,8 @@ __host__ __device__ inline void repack_block(int qt, const uint8_t* blk, uint8_t
               bits |= (uint32_t)((q[4 * m + bb] >> 4) & 1) << (8 * bb + 2 * m);
               bits |= (uint32_t)((q[16 + 4 * m + bb] >> 4) & 1) << (8 * bb + 2 * m + 1);
             }
-          for (int i = 0; i < 4; ++i) B[c * 4 + i] = (uint8_t)(bits >> (8 * i));
+          uint8_t* bp = Bc(c, 4);
+          for (int i = 0; i < 4; ++i) bp[i] = (uint8_t)(bits >> (8 * i));
         }
       }
       break;
@@ -816,7 +839,7 @@ __host__ __device__ inline void repack_block(int qt, const uint8_t* blk, uint8_t
         int q[32];
         for (int e = 0; e < 32; ++e) q[e] = canon_q6k(ql, qh, 32 * s + e);
         const int64_t c = 8 * b + s;
-        pack_nibbles(q, Q + c * 16);
+        pack_nibbles(q, Qc(c));
         uint32_t w[2] = {0, 0};
         for (int i = 0; i < 2; ++i)
           for (int bb = 0; bb < 4; ++bb) {
@@ -827,9 +850,11 @@ __host__ __device__ inline void repack_block(int qt, const uint8_t* blk, uint8_t
                                           ((((q[e2] >> 4) & 3) ^ 2) << 4) | ((((q[e3] >> 4) & 3) ^ 2) << 6));
             w[i] |= v << (8 * bb);
           }
-        for (int i = 0; i < 8; ++i) A[c * 8 + i] = (uint8_t)(w[i >> 2] >> (8 * (i & 3)));
-        B[c * 2] = sc[2 * s];
-        B[c * 2 + 1] = sc[2 * s + 1];
+        uint8_t* ap = Ac(c, 8);
+        for (int i = 0; i < 8; ++i) ap[i] = (uint8_t)(w[i >> 2] >> (8 * (i & 3)));
+        uint8_t* bp = Bc(c, 2);
+        bp[0] = sc[2 * s];
+        bp[1] = sc[2 * s + 1];
       }
       break;
     }

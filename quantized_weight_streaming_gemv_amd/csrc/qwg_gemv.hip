@@ -8,9 +8,9 @@
 //     load instruction reads 1 KiB of contiguous quant bytes (16 B per lane);
 //   * the activation arrives as block fixed-point digits (see qwg_formats.h): 28 words per 32
 //     elements, staged once per workgroup into LDS in a chunk-transposed layout -- 16-B slot q of
-//     chunk c of column n at (n*7 + q)*nxp + c -- so the 64 lanes of a wave read 64 consecutive
-//     slots, free of bank conflicts;
-//   * quants stay integers: nibble formats feed v_dot8_i32_i4 directly (q - 8 by one XOR), the
+//     chunk c of column n at (n*7 + q)*S + c, with the row stride S padded against bank conflicts
+//     of the staging writes -- so the 64 lanes of a wave read 64 consecutive slots;
+//   * quants stay integers: nibble formats feed v_dot8_i32_i4 directly (stored as q XOR 8), the
 //     others feed v_dot4_i32_i8 with one byte per quant; each chunk's integer sums are recombined
 //     in fp32 and scaled once by the block scales and the activation chunk scale;
 //   * an RMSNorm in front of the GEMV is folded in: the digits are of g*h, and the finished rows are
@@ -139,6 +139,12 @@ struct GemvArgs {
 
 constexpr int XSLOTS = DIG_CHUNK_WORDS / 4;  // 16-B slots per activation chunk (6 digit slots + desc)
 
+// LDS row stride (16-B slots) for n chunks: n rounded up to 7 mod 16.  The staging writes put the 7
+// slots of consecutive chunks into 7 rows; with this stride the 16 lanes an LDS write serves at a
+// time land on 16 distinct 16-byte bank groups (row q, chunk c -> group (7q + c) mod 16), where a
+// stride that is a multiple of 16 put all 7 rows of a chunk on the same banks.
+__host__ __device__ constexpr int lds_row_slots(int n) { return n + ((7 - n) % 16 + 16) % 16; }
+
 // PD: weight loads in flight ahead of the chunk being computed (1 or 2 iterations of 64 chunks).
 // P: row passes -- a wave finishes R rows, then the next R rows nw*R further on, so a workgroup
 // covers nw*R*P rows at the registers of R.  Two-pass kernels are held to 128 registers (four
@@ -162,7 +168,7 @@ __global__ __launch_bounds__(LB, (P == 2 ? 4 : 1)) void k_gemv(GemvArgs a) {
   const int kbeg = split * a.ks;
   const int klen = min(a.ks, a.k - kbeg);
   const int nxs = klen / XCHUNK;   // activation chunks of this split
-  const int nxp = a.ks / XCHUNK;   // LDS stride
+  const int nxp = lds_row_slots(a.ks / XCHUNK);  // LDS row stride in 16-B slots
   const int xbase = kbeg / XCHUNK;
   const int nchs = klen / CW;      // weight chunks of this split
   const int cbase = kbeg / CW;
@@ -173,16 +179,22 @@ __global__ __launch_bounds__(LB, (P == 2 ? 4 : 1)) void k_gemv(GemvArgs a) {
 
   // rows past the end are clamped to the last row (loads stay in bounds, results are dropped);
   // chunk indexes past the end are clamped to the last chunk (re-read, never used)
+  // (per-chunk regions are addressed by slot = per-row part + per-chunk part, see slot_row)
   int rr[R];
+  uint32_t srow[R];
   typename F::Raw b0[R], b1[R], b2[R];
   auto set_rows = [&](int r0) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) rr[r] = min(r0 + r, rows - 1);
+    for (int r = 0; r < R; ++r) {
+      rr[r] = min(r0 + r, rows - 1);
+      srow[r] = slot_row(a.w.ilv, a.w.nch, rr[r]);
+    }
   };
   auto fetch = [&](typename F::Raw* raw, int cl) {
-    const int c = min(cl, nchs - 1);
+    const int c = cbase + min(cl, nchs - 1);
+    const uint32_t sc = slot_chunk(a.w.ilv, (uint32_t)c);
 #pragma unroll
-    for (int r = 0; r < R; ++r) raw[r] = F::load(a.w, rr[r], cbase + c);
+    for (int r = 0; r < R; ++r) raw[r] = F::load(a.w, rr[r], c, srow[r] + sc);
   };
 
   // 1. request the first chunks of this wave's rows before staging the activation
@@ -450,7 +462,7 @@ GemvPlan plan_gemv(int qt, int64_t rows, int64_t k, int nc, int epi) {
   const int64_t xs = ((nx + ksplit - 1) / ksplit + 7) / 8 * 8;  // activation chunks per split
   p.ks = (int)(xs * XCHUNK);
   p.ksplit = (int)((k + p.ks - 1) / p.ks);
-  p.lds = (size_t)xs * per_chunk;
+  p.lds = (size_t)lds_row_slots((int)xs) * per_chunk;
   p.part_bytes = p.ksplit > 1 ? (size_t)p.ksplit * nc * rows * sizeof(float) : 0;
   // one column, 8 waves (measured on the 70B shapes): two rows per wave for the plain and QKV
   // epilogues; four for SwiGLU and for the residual epilogue, whose 32 rows per workgroup are a
