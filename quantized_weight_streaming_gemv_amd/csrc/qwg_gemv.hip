@@ -26,6 +26,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include "qwg_kernels.h"
@@ -147,13 +148,16 @@ __host__ __device__ constexpr int lds_row_slots(int n) { return n + ((7 - n) % 1
 
 // PD: weight loads in flight ahead of the chunk being computed (1 or 2 iterations of 64 chunks).
 // P: row passes -- a wave finishes R rows, then the next R rows nw*R further on, so a workgroup
-// covers nw*R*P rows at the registers of R.  Two-pass kernels are held to 128 registers (four
+// covers nw*R*P rows at the registers of R (P == 0: as many blocks as the grid stride gives it).  Two-pass kernels are held to 128 registers (four
 // waves per SIMD, two workgroups per CU); issuing the second pass's loads before the first is
 // reduced needed more and measured slower.  LB: the launch bound.  XIN: the input arrives as fp32 (EpiArgs::xf)
 // and every workgroup digitizes the part it needs straight into LDS.
 template <int QT, int NCM, int R, int EPI, int PD, int P = 1, int LB = 512, int XIN = 0>
 __global__ __launch_bounds__(LB, (P == 2 ? 4 : 1)) void k_gemv(GemvArgs a) {
   static_assert(P == 1 || PD == 1, "row passes use the one-ahead pipeline");
+  static_assert(P != 0 || EPI == EPI_PART || EPI == EPI_STORE || EPI == EPI_QKV || EPI == EPI_RESID ||
+                    EPI == EPI_SWIGLU,
+                "persistent kernels support every epilogue except the fused output digits");
   using F = Fmt<QT>;
   constexpr int CW = F::CW;
   constexpr int WPX = XCHUNK / CW;               // weight chunks per activation chunk (2 for Q8_0)
@@ -173,9 +177,15 @@ __global__ __launch_bounds__(LB, (P == 2 ? 4 : 1)) void k_gemv(GemvArgs a) {
   const int nchs = klen / CW;      // weight chunks of this split
   const int cbase = kbeg / CW;
   const int rows = a.w.rows;
-  const int wg_rows = nw * R * P;
-  const int wg_row0 = blockIdx.x * wg_rows;
-  const bool digitize = (EPI == EPI_RESID || EPI == EPI_SWIGLU) && a.e.dig_out != nullptr;
+  // P > 0: this workgroup owns P consecutive row blocks of nw*R rows.  P == 0 (persistent): the
+  // grid strides over all row blocks, so each workgroup stages the activation once for many rows.
+  const int blk_rows = nw * R;
+  const int nblk = (rows + blk_rows - 1) / blk_rows;
+  const int npass = P > 0 ? P : (nblk - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  auto block_of = [&](int pass) { return P > 0 ? (int)blockIdx.x * P + pass : (int)blockIdx.x + pass * (int)gridDim.x; };
+  const int wg_rows = blk_rows * (P > 0 ? P : 1);
+  const int wg_row0 = block_of(0) * blk_rows;
+  const bool digitize = P > 0 && (EPI == EPI_RESID || EPI == EPI_SWIGLU) && a.e.dig_out != nullptr;
 
   // rows past the end are clamped to the last row (loads stay in bounds, results are dropped);
   // chunk indexes past the end are clamped to the last chunk (re-read, never used)
@@ -235,8 +245,8 @@ __global__ __launch_bounds__(LB, (P == 2 ? 4 : 1)) void k_gemv(GemvArgs a) {
 
   const int sub = lane & 7;  // chunk index within its 256-weight superblock (splits start on superblocks)
 #pragma unroll 1
-  for (int pass = 0; pass < P; ++pass) {
-    const int row0 = wg_row0 + pass * nw * R + wave * R;
+  for (int pass = 0; pass < npass; ++pass) {
+    const int row0 = block_of(pass) * blk_rows + wave * R;
     if (row0 >= rows) break;
     if (pass > 0) {
       set_rows(row0);
@@ -431,6 +441,7 @@ hipError_t launch_digitize(const float* x, int64_t x_stride, const float* gain, 
 // ------------------------------------------------------------------------------------------ host side
 
 static int g_waves = 0, g_rows = 0, g_depth = 0, g_passes = 0;  // launch-geometry overrides (0 = default)
+constexpr int PERSISTENT_WGS = 256;  // workgroups of a persistent (several-column) GEMV: one per CU
 
 void set_gemv_geometry(int waves, int rows_per_wave, int depth, int passes) {
   g_waves = waves;
@@ -481,6 +492,14 @@ GemvPlan plan_gemv(int qt, int64_t rows, int64_t k, int nc, int epi) {
   if (!(p.ncm == 1 && p.rows_per_wave >= 2 && p.depth == 1 && p.ksplit == 1 &&
         (epi == EPI_RESID || epi == EPI_SWIGLU)))
     p.passes = 1;
+  // several columns: the staged activation (112 B per 32 elements and column) is as large as the
+  // weights a workgroup of one pass reads, so one workgroup per CU stages it once and strides over
+  // the row blocks (persistent)
+  if (p.ncm > 1) {
+    p.passes = 0;
+    p.depth = 1;
+    p.grid_x = std::max(1, PERSISTENT_WGS / p.ksplit);
+  }
   return p;
 }
 
@@ -492,6 +511,7 @@ bool gemv_can_digitize_output(const GemvPlan& p, int epi, int64_t rows) {
   if (epi != EPI_RESID && epi != EPI_SWIGLU) return false;
   if (rows % (epi == EPI_SWIGLU ? 2 * XCHUNK : XCHUNK) != 0) return false;
   if (p.ksplit > 1) return true;  // the reduce kernel covers 256 rows per block
+  if (p.passes == 0) return false;  // persistent workgroups own scattered row blocks
   const int outs = p.waves * p.rows_per_wave * p.passes / (epi == EPI_SWIGLU ? 2 : 1);
   return outs % XCHUNK == 0 && outs <= 64;
 }
@@ -510,15 +530,15 @@ static void go(const Dispatch& d, Kern kern, dim3 grid, dim3 block, size_t lds, 
     hipLaunchKernelGGL(kern, grid, block, lds, d.st, args...);
 }
 
-template <int QT, int NCM, int R, int PD>
+template <int QT, int NCM, int R, int PD, int P = 1>
 static hipError_t launch_t(const GemvArgs& a, int epi, int ksplit, dim3 grid, dim3 block, size_t lds,
                            const Dispatch& d) {
   switch (ksplit > 1 ? EPI_PART : epi) {
-    case EPI_PART: go(d, k_gemv<QT, NCM, R, EPI_PART, PD>, grid, block, lds, a); break;
-    case EPI_STORE: go(d, k_gemv<QT, NCM, R, EPI_STORE, PD>, grid, block, lds, a); break;
-    case EPI_RESID: go(d, k_gemv<QT, NCM, R, EPI_RESID, PD>, grid, block, lds, a); break;
-    case EPI_SWIGLU: go(d, k_gemv<QT, NCM, R, EPI_SWIGLU, PD>, grid, block, lds, a); break;
-    case EPI_QKV: go(d, k_gemv<QT, NCM, R, EPI_QKV, PD>, grid, block, lds, a); break;
+    case EPI_PART: go(d, k_gemv<QT, NCM, R, EPI_PART, PD, P>, grid, block, lds, a); break;
+    case EPI_STORE: go(d, k_gemv<QT, NCM, R, EPI_STORE, PD, P>, grid, block, lds, a); break;
+    case EPI_RESID: go(d, k_gemv<QT, NCM, R, EPI_RESID, PD, P>, grid, block, lds, a); break;
+    case EPI_SWIGLU: go(d, k_gemv<QT, NCM, R, EPI_SWIGLU, PD, P>, grid, block, lds, a); break;
+    case EPI_QKV: go(d, k_gemv<QT, NCM, R, EPI_QKV, PD, P>, grid, block, lds, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -557,8 +577,9 @@ static hipError_t launch_fmt(const GemvArgs& a, const GemvPlan& p, int epi, dim3
                                           : launch_t<QT, 1, 2, 1>(a, epi, p.ksplit, grid, block, lds, dd);
   if (p.ncm == 1) return d == 2 ? launch_t<QT, 1, 4, 2>(a, epi, p.ksplit, grid, block, lds, dd)
                                 : launch_t<QT, 1, 4, 1>(a, epi, p.ksplit, grid, block, lds, dd);
-  if (p.ncm == 4) return launch_t<QT, 4, 2, 1>(a, epi, p.ksplit, grid, block, lds, dd);
-  return launch_t<QT, 8, 2, 1>(a, epi, p.ksplit, grid, block, lds, dd);
+  if (p.passes != 0) return hipErrorInvalidValue;  // several columns run persistent
+  if (p.ncm == 4) return launch_t<QT, 4, 2, 1, 0>(a, epi, p.ksplit, grid, block, lds, dd);
+  return launch_t<QT, 8, 2, 1, 0>(a, epi, p.ksplit, grid, block, lds, dd);
 }
 
 hipError_t launch_gemv(int qt, const MatView& w, int64_t k, const void* xd, int64_t xd_stride_bytes, int nc, int epi,
@@ -575,8 +596,10 @@ hipError_t launch_gemv(int qt, const MatView& w, int64_t k, const void* xd, int6
   a.part = part;
   a.e = e;
   const int rows = w.rows;
-  const int rows_per_wg = p.waves * p.rows_per_wave * p.passes;
-  dim3 grid((rows + rows_per_wg - 1) / rows_per_wg, p.ksplit);
+  const int blk_rows = p.waves * p.rows_per_wave;
+  const int nblk = (rows + blk_rows - 1) / blk_rows;
+  const int gx = p.passes > 0 ? (nblk + p.passes - 1) / p.passes : std::min(nblk, std::max(1, p.grid_x));
+  dim3 grid(gx, p.ksplit);
   dim3 block(64 * p.waves);
   // the stop event goes on the last kernel: the GEMV itself, or the split reduction after it
   const Dispatch d1{st, ev_start, p.ksplit == 1 ? ev_stop : nullptr};

@@ -54,7 +54,9 @@ struct GemvPlan {
   int rows_per_wave;
   int waves;   // per workgroup
   int depth;   // weight-load pipeline depth (iterations in flight)
-  int passes;  // row passes per wave (a workgroup covers waves * rows_per_wave * passes rows)
+  int passes;  // row passes per wave (a workgroup covers waves * rows_per_wave * passes rows);
+               // 0 = persistent: grid_x workgroups stride over the row blocks
+  int grid_x;
   int ks;      // K per split
   int ksplit;
   size_t lds;  // dynamic LDS bytes
