@@ -20,10 +20,11 @@
 // activation for word m is float4 m and float4 4+m of the chunk.
 //   Q4_0, Q4_K: each nibble holds q XOR 8, i.e. q - 8 as a 4-bit two's-complement number, so the
 //        integer dot takes the quant words as they are.
-//   Q4_K / Q5_K header (4 words): word 0 = d | dmin << 16; the scale of sub-block j (6 bits) at
-//        bit 6j of the 64-bit (word 1 | word 2 << 32), its min at bit 16 + 6j of (word 2 |
-//        word 3 << 32) -- the same 16 six-bit values as the canonical 12 bytes, placed so that a
-//        lane extracts its sub-block's pair with two shifts whatever j is.
+//   Q4_K / Q5_K header (4 words): the scale of sub-block j (6 bits) at bit 6j of the 64-bit
+//        (word 0 | word 1 << 32), its min at bit 6j of (word 2 | word 3 << 32), d in the high half
+//        of word 1 and dmin in the high half of word 3 -- the same 16 six-bit values as the
+//        canonical 12 bytes, placed so that a lane extracts its sub-block's pair with two 64-bit
+//        shifts of even-aligned register pairs whatever j is.
 //   Q5_K fifth bits (32 bits): bit 8b + 2m   = bit 4 of weight 4m+b,
 //                              bit 8b + 2m+1 = bit 4 of weight 16+4m+b.
 //   Q6_K high bits (2 words): word i, byte b, bit pair p: p=0 -> weight 4(2i)+b,
@@ -200,13 +201,16 @@ __host__ __device__ inline void kq_scale_min(uint32_t S0, uint32_t S1, uint32_t 
   m = s < 4 ? lo_m : hi_m;
 }
 
-// 6-bit scale and min of sub-block j from a packed Q4_K / Q5_K header (words h1, h2, h3).
-__host__ __device__ inline void kq_packed_scale_min(uint32_t h1, uint32_t h2, uint32_t h3, int j, uint32_t& sc,
-                                                    uint32_t& m) {
-  const uint64_t ps = (uint64_t)h1 | ((uint64_t)h2 << 32);
+// Packed Q4_K / Q5_K superblock header, words h0..h3 (16 bytes, as many as the canonical d, dmin and
+// twelve scale bytes): the 6-bit scale of sub-block j at bit 6j of the 64-bit pair h0|h1, its 6-bit
+// min at bit 6j of h2|h3, d in the high half of h1 and dmin in the high half of h3.  Each pair is an
+// even-aligned register pair of the 16-byte load, so one 64-bit shift extracts a field.
+__host__ __device__ inline void kq_packed_scale_min(uint32_t h0, uint32_t h1, uint32_t h2, uint32_t h3, int j,
+                                                    uint32_t& sc, uint32_t& m) {
+  const uint64_t ps = (uint64_t)h0 | ((uint64_t)h1 << 32);
   const uint64_t pm = (uint64_t)h2 | ((uint64_t)h3 << 32);
   sc = (uint32_t)(ps >> (6 * j)) & 63u;
-  m = (uint32_t)(pm >> (16 + 6 * j)) & 63u;
+  m = (uint32_t)(pm >> (6 * j)) & 63u;
 }
 
 // Weight bytes are read exactly once per pass: streaming (non-temporal) loads.
@@ -459,8 +463,9 @@ __host__ __device__ inline float byte_value2(const uint32_t* wa, const uint32_t*
 //
 // Each Fmt<QT> provides
 //   CW (weights per chunk)
-//   Raw load(view, row, chunk, slot)    -- the chunk's quant bytes and scale data (slot: the chunk's
-//                                          place in the per-chunk regions, slot_row + slot_chunk)
+//   Raw load(view, ro, chunk, slot)     -- the chunk's quant bytes and scale data (ro: row_off of
+//                                          its row; slot: the chunk's place in the per-chunk
+//                                          regions, slot_row + slot_chunk)
 //   decode(raw, chunk, w[CW])           -- exact fp32 weights in chunk order (for dequantize);
 //                                          a zero weight is +0 ("+ 0.0f" turns -0 into +0)
 //   U unpack(raw, chunk, sub)           -- integer quant words for the dot plus the chunk's fp32
@@ -471,8 +476,10 @@ __host__ __device__ inline float byte_value2(const uint32_t* wa, const uint32_t*
 // Byte offsets inside one packed region are 32-bit (the library refuses matrices of 4 GiB or more),
 // so loads take a uniform 64-bit base plus a 32-bit lane offset.
 
-__host__ __device__ inline uint32_t roff(int64_t row, int64_t row_bytes, uint32_t within) {
-  return (uint32_t)row * (uint32_t)row_bytes + within;
+// Byte offset of a row in the per-block region a format reads per row (region A, or C for Q6_K's d),
+// computed once per row rather than once per load.
+__host__ __device__ inline uint32_t row_off(int qt, const MatView& v, int64_t row) {
+  return (uint32_t)row * (uint32_t)(qt == Q6_K ? v.c_row : v.a_row);
 }
 
 // Per-chunk regions (one e-byte piece per chunk: quants 16 B, Q5_K fifth bits 4 B, Q6_K high bits
@@ -496,10 +503,10 @@ struct Fmt<Q8_0> {
     uint4 q;
     uint32_t d;
   };
-  __host__ __device__ static Raw load(const MatView& v, int64_t row, int c, uint32_t slot) {
+  __host__ __device__ static Raw load(const MatView& v, uint32_t ro, int c, uint32_t slot) {
     Raw r;
     r.q = ld_stream_u4(v.q + slot * 16u);
-    r.d = ld<uint16_t>(v.a + roff(row, v.a_row, (uint32_t)(c >> 1) * 2u));
+    r.d = ld<uint16_t>(v.a + ro + (uint32_t)(c >> 1) * 2u);
     return r;
   }
   __host__ __device__ static void decode(const Raw& r, int, float* w) {
@@ -534,10 +541,10 @@ struct Fmt<Q4_0> {
     uint4 q;
     uint32_t d;
   };
-  __host__ __device__ static Raw load(const MatView& v, int64_t row, int c, uint32_t slot) {
+  __host__ __device__ static Raw load(const MatView& v, uint32_t ro, int c, uint32_t slot) {
     Raw r;
     r.q = ld_stream_u4(v.q + slot * 16u);
-    r.d = ld<uint16_t>(v.a + roff(row, v.a_row, (uint32_t)c * 2u));
+    r.d = ld<uint16_t>(v.a + ro + (uint32_t)c * 2u);
     return r;
   }
   __host__ __device__ static void decode(const Raw& r, int, float* w) {
@@ -573,20 +580,20 @@ struct Fmt<Q4_K> {
   static constexpr int CW = 32;
   struct Raw {
     uint4 q;
-    uint4 h;  // d | dmin << 16, then the re-laid-out scales and mins
+    uint4 h;  // the re-laid-out scales and mins, d and dmin (kq_packed_scale_min)
   };
-  __host__ __device__ static Raw load(const MatView& v, int64_t row, int c, uint32_t slot) {
+  __host__ __device__ static Raw load(const MatView& v, uint32_t ro, int c, uint32_t slot) {
     Raw r;
     r.q = ld_stream_u4(v.q + slot * 16u);
-    r.h = ld<uint4>(v.a + roff(row, v.a_row, (uint32_t)(c >> 3) * 16u));
+    r.h = ld<uint4>(v.a + ro + (uint32_t)(c >> 3) * 16u);
     return r;
   }
   // d * scale and dmin * min of sub-block j (both exact in fp32)
   __host__ __device__ static void coef(const uint4& h, int j, float& dsc, float& dmm) {
     uint32_t sc, m;
-    kq_packed_scale_min(h.y, h.z, h.w, j, sc, m);
-    dsc = half_bits_to_float(h.x & 0xFFFFu) * (float)sc;
-    dmm = half_bits_to_float(h.x >> 16) * (float)m;
+    kq_packed_scale_min(h.x, h.y, h.z, h.w, j, sc, m);
+    dsc = half_bits_to_float(h.y >> 16) * (float)sc;
+    dmm = half_bits_to_float(h.w >> 16) * (float)m;
   }
   __host__ __device__ static void decode(const Raw& r, int c, float* w) {
     float dsc, dmm;
@@ -628,10 +635,10 @@ struct Fmt<Q5_K> {
     uint4 h;
     uint32_t qh;
   };
-  __host__ __device__ static Raw load(const MatView& v, int64_t row, int c, uint32_t slot) {
+  __host__ __device__ static Raw load(const MatView& v, uint32_t ro, int c, uint32_t slot) {
     Raw r;
     r.q = ld_stream_u4(v.q + slot * 16u);
-    r.h = ld<uint4>(v.a + roff(row, v.a_row, (uint32_t)(c >> 3) * 16u));
+    r.h = ld<uint4>(v.a + ro + (uint32_t)(c >> 3) * 16u);
     r.qh = ld_stream_u1(v.b + slot * 4u);
     return r;
   }
@@ -682,17 +689,26 @@ struct Fmt<Q6_K> {
   struct Raw {
     uint4 q;
     uint2 qh;
-    uint32_t sc;  // two int8 scales: byte 0 -> weights 0..15, byte 1 -> 16..31
-    uint32_t d;
+    uint32_t scw;  // the aligned word holding the chunk's two int8 scales (byte 0 -> weights 0..15,
+                   // byte 1 -> 16..31) at bit (sh & 31)
+    uint32_t dw;   // the aligned word holding the superblock's fp16 d at bit (sh >> 8)
+    uint32_t sh;
   };
-  __host__ __device__ static Raw load(const MatView& v, int64_t row, int c, uint32_t slot) {
+  // The 2-byte fields are read as the aligned 32-bit words that hold them (every region is 256-B
+  // aligned and padded, so the word is inside the matrix): 16-bit loads made the compiler place the
+  // zero-extension of the next iteration's fields in the loop latch, where it waited for the loads.
+  __host__ __device__ static Raw load(const MatView& v, uint32_t ro, int c, uint32_t slot) {
     Raw r;
     r.q = ld_stream_u4(v.q + slot * 16u);
     r.qh = ld_stream_u2(v.a + slot * 8u);
-    r.sc = ld<uint16_t>(v.b + slot * 2u);
-    r.d = ld<uint16_t>(v.c + roff(row, v.c_row, (uint32_t)(c >> 3) * 2u));
+    const uint32_t so = slot * 2u, dof = ro + (uint32_t)(c >> 3) * 2u;
+    r.scw = ld<uint32_t>(v.b + (so & ~3u));
+    r.dw = ld<uint32_t>(v.c + (dof & ~3u));
+    r.sh = (so & 2u) * 8u | ((dof & 2u) * 8u) << 8;
     return r;
   }
+  __host__ __device__ static uint32_t sc_of(const Raw& r) { return r.scw >> (r.sh & 31u); }
+  __host__ __device__ static uint32_t d_of(const Raw& r) { return (r.dw >> (r.sh >> 8)) & 0xFFFFu; }
   // word m as int8 bytes 4 (q - 32): low-nibble weights (4m+b) and high-nibble weights (16+4m+b);
   // the stored high pair (XOR 2) lands in bits 6..7, the nibble in bits 2..5
   __host__ __device__ static void words(const Raw& r, int m, uint32_t& lo, uint32_t& hi) {
@@ -705,9 +721,10 @@ struct Fmt<Q6_K> {
     hi = ((w >> 2) & 0x3C3C3C3Cu) | (hh & 0xC0C0C0C0u);
   }
   __host__ __device__ static void decode(const Raw& r, int, float* w) {
-    const float d = half_bits_to_float(r.d);
-    const float dA = d * (float)(int8_t)(uint8_t)(r.sc & 0xFFu);
-    const float dB = d * (float)(int8_t)(uint8_t)((r.sc >> 8) & 0xFFu);
+    const float d = half_bits_to_float(d_of(r));
+    const uint32_t sc = sc_of(r);
+    const float dA = d * (float)(int8_t)(uint8_t)(sc & 0xFFu);
+    const float dB = d * (float)(int8_t)(uint8_t)((sc >> 8) & 0xFFu);
     for (int m = 0; m < 4; ++m) {
       uint32_t lo, hi;
       words(r, m, lo, hi);
@@ -722,12 +739,13 @@ struct Fmt<Q6_K> {
     float dA, dB;           // d * sc / 4 of the two 16-weight sub-blocks
   };
   __host__ __device__ static U unpack(const Raw& r, int, int) {
-    const float d = half_bits_to_float(r.d);
+    const float d = half_bits_to_float(d_of(r));
+    const uint32_t sc = sc_of(r);
     U u;
 #pragma unroll
     for (int m = 0; m < 4; ++m) words(r, m, u.lo[m], u.hi[m]);
-    u.dA = 0.25f * (d * (float)(int8_t)(uint8_t)(r.sc & 0xFFu));
-    u.dB = 0.25f * (d * (float)(int8_t)(uint8_t)((r.sc >> 8) & 0xFFu));
+    u.dA = 0.25f * (d * (float)(int8_t)(uint8_t)(sc & 0xFFu));
+    u.dB = 0.25f * (d * (float)(int8_t)(uint8_t)((sc >> 8) & 0xFFu));
     return u;
   }
   __host__ __device__ static float dotu(const U& u, const uint32_t* dig, const ChunkDesc& ds) {
@@ -795,8 +813,7 @@ __host__ __device__ inline void repack_block(int qt, const uint8_t* blk, uint8_t
     }
     case Q4_K:
     case Q5_K: {
-      // header: d, dmin as they are; the sixteen 6-bit scales/mins re-laid out
-      for (int i = 0; i < 4; ++i) A[b * 16 + i] = blk[i];
+      // header: the sixteen 6-bit scales/mins re-laid out around d and dmin (kq_packed_scale_min)
       uint32_t S[3];
       for (int i = 0; i < 3; ++i)
         S[i] = (uint32_t)blk[4 + 4 * i] | ((uint32_t)blk[5 + 4 * i] << 8) | ((uint32_t)blk[6 + 4 * i] << 16) |
@@ -806,10 +823,12 @@ __host__ __device__ inline void repack_block(int qt, const uint8_t* blk, uint8_t
         int sc, mn;
         kq_scale_min(S[0], S[1], S[2], j, sc, mn);
         ps |= (uint64_t)sc << (6 * j);
-        pm |= (uint64_t)mn << (16 + 6 * j);
+        pm |= (uint64_t)mn << (6 * j);
       }
-      const uint32_t hw[3] = {(uint32_t)ps, (uint32_t)(ps >> 32) | (uint32_t)pm, (uint32_t)(pm >> 32)};
-      for (int i = 0; i < 12; ++i) A[b * 16 + 4 + i] = (uint8_t)(hw[i >> 2] >> (8 * (i & 3)));
+      const uint32_t d = (uint32_t)blk[0] | ((uint32_t)blk[1] << 8), dmin = (uint32_t)blk[2] | ((uint32_t)blk[3] << 8);
+      const uint32_t hw[4] = {(uint32_t)ps, (uint32_t)(ps >> 32) | (d << 16), (uint32_t)pm,
+                              (uint32_t)(pm >> 32) | (dmin << 16)};
+      for (int i = 0; i < 16; ++i) A[b * 16 + i] = (uint8_t)(hw[i >> 2] >> (8 * (i & 3)));
       const uint8_t* qs = blk + (qt == Q4_K ? 16 : 48);
       const uint8_t* qh = blk + 16;
       for (int s = 0; s < 8; ++s) {

@@ -35,6 +35,25 @@ namespace qwg {
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
+// v of the lane that DPP control CTRL selects, for the rows in ROW_MASK (0 elsewhere)
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Sum over the 64 lanes, as a wave-uniform value: quad permutes (lane ^ 1, lane ^ 2) and row mirrors
+// give every lane its 16-lane row's sum, two row broadcasts carry it into lane 63, which is read as
+// a scalar.  Six DPP adds replace the LDS-routed butterfly of six shuffles; the order is fixed.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f<0x141, 0xF>(v);  // row_half_mirror: the other quad of each eight lanes
+  v += dpp_f<0x140, 0xF>(v);  // row_mirror: the other eight of each row
+  v += dpp_f<0x142, 0xA>(v);  // row_bcast15: rows 1 and 3 add lane 15 of rows 0 and 2
+  v += dpp_f<0x143, 0xC>(v);  // row_bcast31: rows 2 and 3 add lane 31
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 // Final value of output row `row`, column n (v: its sum; vp: the sum of its pair partner row^1),
 // stored by the epilogue; returns the value the output vector holds at that position (the new h
 // for RESID, silu(gate)*up for SWIGLU on even rows).
@@ -146,18 +165,21 @@ constexpr int XSLOTS = DIG_CHUNK_WORDS / 4;  // 16-B slots per activation chunk 
 // stride that is a multiple of 16 put all 7 rows of a chunk on the same banks.
 __host__ __device__ constexpr int lds_row_slots(int n) { return n + ((7 - n) % 16 + 16) % 16; }
 
-// PD: weight loads in flight ahead of the chunk being computed (1 or 2 iterations of 64 chunks).
-// P: row passes -- a wave finishes R rows, then the next R rows nw*R further on, so a workgroup
-// covers nw*R*P rows at the registers of R (P == 0: as many blocks as the grid stride gives it).  Two-pass kernels are held to 128 registers (four
-// waves per SIMD, two workgroups per CU); issuing the second pass's loads before the first is
-// reduced needed more and measured slower.  LB: the launch bound.  XIN: the input arrives as fp32 (EpiArgs::xf)
-// and every workgroup digitizes the part it needs straight into LDS.
+// Pipeline: each wave computes ng groups of R rows (group g: R rows at row0_of(g)), every group in
+// iterations of 64 chunks (lane l takes chunk l + 64 i).  The loop over all ng * nit iterations is
+// wave-uniform and runs as one software pipeline: the fetch cursor stays PD iterations ahead of the
+// compute cursor and crosses from one group into the next without draining, so the loads of the
+// next rows are in flight while a group is reduced.  Lanes past the end of a ragged row (chunk
+// index >= the split's chunks) load the clamped last chunk and add nothing.  A group's 64-lane
+// totals are parked in lane g*R + r, and the epilogue runs once after the loop (no stores in it).
+// P: groups per wave -- P row blocks of nw*R rows per workgroup (P == 0, persistent: the grid
+// strides over the row blocks, at most 64/R of them per workgroup).  Two-group kernels are held to
+// 128 registers (four waves per SIMD, two workgroups per CU).  LB: the launch bound.  XIN: the
+// input arrives as fp32 (EpiArgs::xf) and every workgroup digitizes the part it needs into LDS.
 template <int QT, int NCM, int R, int EPI, int PD, int P = 1, int LB = 512, int XIN = 0>
 __global__ __launch_bounds__(LB, (P == 2 ? 4 : 1)) void k_gemv(GemvArgs a) {
-  static_assert(P == 1 || PD == 1, "row passes use the one-ahead pipeline");
-  static_assert(P != 0 || EPI == EPI_PART || EPI == EPI_STORE || EPI == EPI_QKV || EPI == EPI_RESID ||
-                    EPI == EPI_SWIGLU,
-                "persistent kernels support every epilogue except the fused output digits");
+  static_assert(PD == 1 || PD == 2, "one or two iterations of loads in flight");
+  static_assert(R == 1 || R == 2 || R == 4, "rows per wave");
   using F = Fmt<QT>;
   constexpr int CW = F::CW;
   constexpr int WPX = XCHUNK / CW;               // weight chunks per activation chunk (2 for Q8_0)
@@ -166,7 +188,8 @@ __global__ __launch_bounds__(LB, (P == 2 ? 4 : 1)) void k_gemv(GemvArgs a) {
   __shared__ float red[MAX_COLS][16];
   __shared__ float osh[MAX_COLS][64];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, nw = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nc = a.nc;
   const int split = blockIdx.y;
   const int kbeg = split * a.ks;
@@ -176,42 +199,52 @@ __global__ __launch_bounds__(LB, (P == 2 ? 4 : 1)) void k_gemv(GemvArgs a) {
   const int xbase = kbeg / XCHUNK;
   const int nchs = klen / CW;      // weight chunks of this split
   const int cbase = kbeg / CW;
+  const int nit = (nchs + 63) >> 6;  // iterations per group
   const int rows = a.w.rows;
-  // P > 0: this workgroup owns P consecutive row blocks of nw*R rows.  P == 0 (persistent): the
-  // grid strides over all row blocks, so each workgroup stages the activation once for many rows.
   const int blk_rows = nw * R;
   const int nblk = (rows + blk_rows - 1) / blk_rows;
   const int npass = P > 0 ? P : (nblk - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
-  auto block_of = [&](int pass) { return P > 0 ? (int)blockIdx.x * P + pass : (int)blockIdx.x + pass * (int)gridDim.x; };
+  auto block_of = [&](int g) { return P > 0 ? (int)blockIdx.x * P + g : (int)blockIdx.x + g * (int)gridDim.x; };
+  auto row0_of = [&](int g) { return block_of(g) * blk_rows + wave * R; };
   const int wg_rows = blk_rows * (P > 0 ? P : 1);
   const int wg_row0 = block_of(0) * blk_rows;
   const bool digitize = P > 0 && (EPI == EPI_RESID || EPI == EPI_SWIGLU) && a.e.dig_out != nullptr;
+  int ng = 0;  // groups of this wave (its rows of the workgroup's row blocks)
+  while (ng < npass && ng < 64 / R && row0_of(ng) < rows) ++ng;
 
-  // rows past the end are clamped to the last row (loads stay in bounds, results are dropped);
-  // chunk indexes past the end are clamped to the last chunk (re-read, never used)
+  // rows past the end are clamped to the last row (loads stay in bounds, results are dropped)
   // (per-chunk regions are addressed by slot = per-row part + per-chunk part, see slot_row)
-  int rr[R];
-  uint32_t srow[R];
+  uint32_t rofs[R], srow[R];
   typename F::Raw b0[R], b1[R], b2[R];
   auto set_rows = [&](int r0) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      rr[r] = min(r0 + r, rows - 1);
-      srow[r] = slot_row(a.w.ilv, a.w.nch, rr[r]);
+      const int row = min(r0 + r, rows - 1);
+      rofs[r] = row_off(QT, a.w, row);
+      srow[r] = slot_row(a.w.ilv, a.w.nch, row);
     }
   };
-  auto fetch = [&](typename F::Raw* raw, int cl) {
-    const int c = cbase + min(cl, nchs - 1);
+  int fg = 0, fi = 0;  // fetch cursor: group, iteration
+  auto fetch_next = [&](typename F::Raw* raw) {
+    const int c = cbase + min(lane + 64 * fi, nchs - 1);
     const uint32_t sc = slot_chunk(a.w.ilv, (uint32_t)c);
 #pragma unroll
-    for (int r = 0; r < R; ++r) raw[r] = F::load(a.w, rr[r], c, srow[r] + sc);
+    for (int r = 0; r < R; ++r) raw[r] = F::load(a.w, rofs[r], c, srow[r] + sc);
+    if (++fi == nit) {
+      if (fg + 1 < ng) {
+        fi = 0;
+        set_rows(row0_of(++fg));
+      } else {
+        fi = nit - 1;  // past the last iteration: re-read the last chunks (never used)
+      }
+    }
   };
 
   // 1. request the first chunks of this wave's rows before staging the activation
-  set_rows(wg_row0 + wave * R);
-  if (wg_row0 + wave * R < rows) {
-    fetch(b0, lane);
-    if (PD == 2) fetch(b1, lane + 64);
+  if (ng > 0) {
+    set_rows(row0_of(0));
+    fetch_next(b0);
+    if (PD == 2) fetch_next(b1);
   }
 
   // 2. stage this split's activation digits (coalesced 16-B reads, chunk-transposed LDS) and the
@@ -243,116 +276,130 @@ __global__ __launch_bounds__(LB, (P == 2 ? 4 : 1)) void k_gemv(GemvArgs a) {
   if (EPI != EPI_PART && a.e.sq_in) rms_partials(a.e, nc, red);
   __syncthreads();
 
+  // 3. the pipelined loop
   const int sub = lane & 7;  // chunk index within its 256-weight superblock (splits start on superblocks)
-#pragma unroll 1
-  for (int pass = 0; pass < npass; ++pass) {
-    const int row0 = block_of(pass) * blk_rows + wave * R;
-    if (row0 >= rows) break;
-    if (pass > 0) {
-      set_rows(row0);
-      fetch(b0, lane);
-    }
-    float acc[R][NCM];
+  float acc[R][NCM], res[NCM];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+  for (int n = 0; n < NCM; ++n) {
+    res[n] = 0.f;
 #pragma unroll
-      for (int n = 0; n < NCM; ++n) acc[r][n] = 0.f;
-
-    // 3. main loop over this lane's chunks
-    auto chunk = [&](const typename F::Raw* raw, int cl) {
-      typename F::U u[R];
+    for (int r = 0; r < R; ++r) acc[r][n] = 0.f;
+  }
+  int cg = 0, ci = 0;  // compute cursor: group, iteration
+  auto compute_next = [&](const typename F::Raw* raw) {
+    const int cl = lane + 64 * ci;
+    const bool valid = cl < nchs;
+    typename F::U u[R];
 #pragma unroll
-      for (int r = 0; r < R; ++r) u[r] = F::unpack(raw[r], cbase + cl, sub);
-      const int xc = cl / WPX;
-      const int s0 = (WPX == 2) ? (cl & 1) * 3 : 0;  // first digit slot of this half (Q8_0)
+    for (int r = 0; r < R; ++r) u[r] = F::unpack(raw[r], cbase + cl, sub);
+    const int xc = min(cl, nchs - 1) / WPX;
+    const int s0 = (WPX == 2) ? (cl & 1) * 3 : 0;  // first digit slot of this half (Q8_0)
 #pragma unroll
-      for (int n = 0; n < NCM; ++n) {
-        if (n >= nc) break;
-        uint32_t dg[NDS * 4];
+    for (int n = 0; n < NCM; ++n) {
+      if (NCM > 1 && n >= nc) break;  // one-column kernels always have nc == 1
+      uint32_t dg[NDS * 4];
 #pragma unroll
-        for (int q = 0; q < NDS; ++q) {
-          const uint4 v = lds[(n * XSLOTS + s0 + q) * nxp + xc];
-          dg[4 * q] = v.x;
-          dg[4 * q + 1] = v.y;
-          dg[4 * q + 2] = v.z;
-          dg[4 * q + 3] = v.w;
-        }
-        const uint4 dv = lds[(n * XSLOTS + 6) * nxp + xc];
-        ChunkDesc ds;
-        ds.inv_scale = __uint_as_float(dv.x);
-        ds.sum = (int32_t)dv.y;
-        ds.sumA = (int32_t)dv.z;
-        ds.sumB = (int32_t)dv.w;
-#pragma unroll
-        for (int r = 0; r < R; ++r) acc[r][n] += F::dotu(u[r], dg, ds);
+      for (int q = 0; q < NDS; ++q) {
+        const uint4 v = lds[(n * XSLOTS + s0 + q) * nxp + xc];
+        dg[4 * q] = v.x;
+        dg[4 * q + 1] = v.y;
+        dg[4 * q + 2] = v.z;
+        dg[4 * q + 3] = v.w;
       }
-    };
-    if (PD == 1) {
-      for (int cl = lane; cl < nchs; cl += 128) {
-        fetch(b1, cl + 64);
-        chunk(b0, cl);
-        if (cl + 64 >= nchs) break;
-        fetch(b0, cl + 128);
-        chunk(b1, cl + 64);
-      }
-    } else {
-      // three buffers in rotation: two iterations of loads stay in flight while one computes
-      for (int cl = lane; cl < nchs; cl += 192) {
-        fetch(b2, cl + 128);
-        chunk(b0, cl);
-        if (cl + 64 >= nchs) break;
-        fetch(b0, cl + 192);
-        chunk(b1, cl + 64);
-        if (cl + 128 >= nchs) break;
-        fetch(b1, cl + 256);
-        chunk(b2, cl + 128);
+      const uint4 dv = lds[(n * XSLOTS + 6) * nxp + xc];
+      ChunkDesc ds;
+      ds.inv_scale = __uint_as_float(dv.x);
+      ds.sum = (int32_t)dv.y;
+      ds.sumA = (int32_t)dv.z;
+      ds.sumB = (int32_t)dv.w;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float d = F::dotu(u[r], dg, ds);
+        acc[r][n] += valid ? d : 0.f;
       }
     }
-
-    // 4. reduce over the 64 lanes (every lane ends with every total)
+    if (++ci == nit) {
+      // the group is done: its 64-lane sums, parked in lane cg*R + r
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int n = 0; n < NCM; ++n) {
-        float v = acc[r][n];
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-        acc[r][n] = v;
-      }
-
-    // 5. epilogue: lane r finishes row row0 + r (its pair partner is row0 + (r ^ 1))
-    if (lane < R) {
-      const int row = row0 + lane;
-      if (row < rows) {
+      for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int n = 0; n < NCM; ++n) {
-          if (n >= nc) break;
-          float v = 0.f, vp = 0.f;
+          const float v = wave_sum(acc[r][n]);
+          if (lane == cg * R + r) res[n] = v;
+          acc[r][n] = 0.f;
+        }
+      ci = 0;
+      ++cg;
+    }
+  };
+  const int total = ng * nit;
+  // Single-exit loops with scheduling barriers between the fetch and compute phases: a break in the
+  // middle of the body let the compiler build an exec-masked exit whose fall-through edge carried
+  // unconsumed loads into the loop header (which then waited for every load), and without the
+  // barriers the scheduler sank the next fetch into the current compute.
+  int t = 0;
+  if (PD == 1) {
+    for (; t + 2 <= total; t += 2) {
+      fetch_next(b1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_next(b0);
+      __builtin_amdgcn_sched_barrier(0);
+      fetch_next(b0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_next(b1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (t < total) compute_next(b0);
+  } else {
+    for (; t + 3 <= total; t += 3) {
+      fetch_next(b2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_next(b0);
+      __builtin_amdgcn_sched_barrier(0);
+      fetch_next(b0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_next(b1);
+      __builtin_amdgcn_sched_barrier(0);
+      fetch_next(b1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_next(b2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (t < total) compute_next(b0);
+    if (t + 1 < total) compute_next(b1);
+  }
+
+  // 4. epilogue: lane j < ng*R finishes row r = j % R of group g = j / R (its pair partner, row^1,
+  //    is lane j^1 of the same group)
+  float resp[NCM];
 #pragma unroll
-          for (int r = 0; r < R; ++r) {
-            if (r == lane) v = acc[r][n];
-            if (r == (lane ^ 1)) vp = acc[r][n];
+  for (int n = 0; n < NCM; ++n) resp[n] = __shfl_xor(res[n], 1);
+  if (lane < ng * R) {
+    const int row = row0_of(lane / R) + lane % R;
+    if (row < rows) {
+#pragma unroll
+      for (int n = 0; n < NCM; ++n) {
+        if (NCM > 1 && n >= nc) break;
+        float v = res[n], vp = resp[n];
+        if (EPI == EPI_PART) {
+          a.part[((int64_t)split * nc + n) * rows + row] = v;
+        } else {
+          if (a.e.sq_in) {
+            const float rs = rms_scale(a.e, red, n);
+            v *= rs;
+            vp *= rs;
           }
-          if (EPI == EPI_PART) {
-            a.part[((int64_t)split * nc + n) * rows + row] = v;
-          } else {
-            if (a.e.sq_in) {
-              const float rs = rms_scale(a.e, red, n);
-              v *= rs;
-              vp *= rs;
-            }
-            const float out = run_epilogue(EPI, a.e, n, row, v, vp);
-            if (digitize) {
-              if (EPI == EPI_RESID) osh[n][row - wg_row0] = out;
-              else if ((row & 1) == 0) osh[n][(row - wg_row0) >> 1] = out;
-            }
+          const float out = run_epilogue(EPI, a.e, n, row, v, vp);
+          if (digitize) {
+            if (EPI == EPI_RESID) osh[n][row - wg_row0] = out;
+            else if ((row & 1) == 0) osh[n][(row - wg_row0) >> 1] = out;
           }
         }
       }
     }
   }
 
-  // 6. digitize this workgroup's slice of the output vector for the next GEMV
+  // 5. digitize this workgroup's slice of the output vector for the next GEMV
   if (digitize) {
     __syncthreads();
     const int nrow = min(wg_rows, rows - wg_row0);  // whole chunks: the host checks rows
@@ -454,7 +501,6 @@ void set_gemv_geometry(int waves, int rows_per_wave, int depth, int passes) {
 static bool two_pass_ok(int qt) { return qt == Q4_0 || qt == Q4_K || qt == Q8_0; }
 
 GemvPlan plan_gemv(int qt, int64_t rows, int64_t k, int nc, int epi) {
-  (void)rows;
   // the RoPE and SwiGLU epilogues combine rows (2i, 2i+1), which must sit in one wave
   const bool pairs = epi == EPI_QKV || epi == EPI_SWIGLU;
   GemvPlan p{};
@@ -498,7 +544,11 @@ GemvPlan plan_gemv(int qt, int64_t rows, int64_t k, int nc, int epi) {
   if (p.ncm > 1) {
     p.passes = 0;
     p.depth = 1;
-    p.grid_x = std::max(1, PERSISTENT_WGS / p.ksplit);
+    // a wave parks each finished row group's totals in R lanes: at most 64 / R groups per workgroup
+    const int64_t blk = (int64_t)p.waves * p.rows_per_wave;
+    const int64_t nblk = (rows + blk - 1) / blk;
+    const int64_t min_grid = (nblk + 64 / p.rows_per_wave - 1) / (64 / p.rows_per_wave);
+    p.grid_x = (int)std::max<int64_t>(std::max(1, PERSISTENT_WGS / p.ksplit), min_grid);
   }
   return p;
 }

@@ -40,7 +40,7 @@ __global__ void k_dequant(MatView w, int64_t rows, int64_t k, float* out) {
   if (i >= rows * w.nch) return;
   const int64_t row = i / w.nch;
   const int c = (int)(i % w.nch);
-  const typename F::Raw r = F::load(w, row, c, slot_row(w.ilv, w.nch, row) + slot_chunk(w.ilv, (uint32_t)c));
+  const typename F::Raw r = F::load(w, row_off(QT, w, row), c, slot_row(w.ilv, w.nch, row) + slot_chunk(w.ilv, (uint32_t)c));
   float v[F::CW];
   F::decode(r, c, v);
   float4* o = (float4*)(out + row * k + (int64_t)c * F::CW);
@@ -76,7 +76,7 @@ __global__ void k_embed(MatView w, int64_t k, Tokens tok, int nc, float* h, int6
   const int n = blockIdx.y;
   if (c >= w.nch || n >= nc) return;
   const typename F::Raw r =
-      F::load(w, tok.t[n], c, slot_row(w.ilv, w.nch, tok.t[n]) + slot_chunk(w.ilv, (uint32_t)c));
+      F::load(w, row_off(QT, w, tok.t[n]), c, slot_row(w.ilv, w.nch, tok.t[n]) + slot_chunk(w.ilv, (uint32_t)c));
   float v[F::CW];
   F::decode(r, c, v);
   float* o = h + (int64_t)n * h_stride + (int64_t)c * F::CW;
