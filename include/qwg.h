@@ -101,10 +101,11 @@ int qwg_gemv(int qtype, const void* d_packed, int64_t rows, int64_t k, const flo
              void* stream);
 
 /* Launch geometry of subsequent GEMV launches in this process, for tuning: waves per workgroup
- * (2, 4 or 8), output rows per wave for single-column GEMVs (1, 2 or 4), weight-load pipeline
- * depth (1 or 2 iterations in flight) and row passes per wave (1 or 2; two passes apply to
- * single-column residual and SwiGLU GEMVs with 2 or 4 rows per wave and depth 1); 0 keeps the
- * default.  Results do not depend on it beyond floating-point summation order.  Not thread-safe:
+ * (2, 4 or 8; 16 for single-column GEMVs, with 2 rows per wave, depth 1 and at most 2 passes),
+ * output rows per wave for single-column GEMVs (1, 2 or 4), weight-load pipeline
+ * depth (1 or 2 iterations in flight) and row passes per wave (1, 2, 4 or 8; several passes apply
+ * to single-column residual and SwiGLU GEMVs at depth 1: 2, 4 or 8 passes with 2 rows per wave, 2
+ * passes with 4 rows for Q4_0, Q4_K and Q8_0); 0 keeps the default.  Results do not depend on it beyond floating-point summation order.  Not thread-safe:
  * call it while no other thread launches GEMVs. */
 int qwg_set_gemv_geometry(int waves_per_group, int rows_per_wave, int pipeline_depth, int row_passes);
 

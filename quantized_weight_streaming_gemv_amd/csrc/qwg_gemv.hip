@@ -173,11 +173,11 @@ __host__ __device__ constexpr int lds_row_slots(int n) { return n + ((7 - n) % 1
 // index >= the split's chunks) load the clamped last chunk and add nothing.  A group's 64-lane
 // totals are parked in lane g*R + r, and the epilogue runs once after the loop (no stores in it).
 // P: groups per wave -- P row blocks of nw*R rows per workgroup (P == 0, persistent: the grid
-// strides over the row blocks, at most 64/R of them per workgroup).  Two-group kernels are held to
-// 128 registers (four waves per SIMD, two workgroups per CU).  LB: the launch bound.  XIN: the
-// input arrives as fp32 (EpiArgs::xf) and every workgroup digitizes the part it needs into LDS.
+// strides over the row blocks, at most 64/R of them per workgroup).  Four-row two-group kernels are
+// held to 128 registers (four waves per SIMD, two workgroups per CU).  LB: the launch bound.  XIN:
+// the input arrives as fp32 (EpiArgs::xf) and every workgroup digitizes the part it needs into LDS.
 template <int QT, int NCM, int R, int EPI, int PD, int P = 1, int LB = 512, int XIN = 0>
-__global__ __launch_bounds__(LB, (P == 2 ? 4 : 1)) void k_gemv(GemvArgs a) {
+__global__ __launch_bounds__(LB, (R == 4 && P == 2 ? 4 : 1)) void k_gemv(GemvArgs a) {
   static_assert(PD == 1 || PD == 2, "one or two iterations of loads in flight");
   static_assert(R == 1 || R == 2 || R == 4, "rows per wave");
   using F = Fmt<QT>;
@@ -248,28 +248,47 @@ __global__ __launch_bounds__(LB, (P == 2 ? 4 : 1)) void k_gemv(GemvArgs a) {
   }
 
   // 2. stage this split's activation digits (coalesced 16-B reads, chunk-transposed LDS) and the
-  //    RMSNorm partial sums
+  //    RMSNorm partial sums.  Each thread issues a batch of loads before its first LDS write (a
+  //    load-then-write loop serialized one L2 round trip per 8 KiB of the workgroup's slice).
   if (XIN) {
     // four threads per 32-element chunk digitize it into the same LDS layout
+    constexpr int XU = 4;  // chunks in flight per thread
     uint32_t* ldw = (uint32_t*)lds;
-    const int m = tid & 3;
+    const int m = tid & 3, cstep = blockDim.x >> 2;
     for (int n = 0; n < nc; ++n) {
       const float* xr = a.e.xf + (int64_t)n * a.e.xf_stride + (int64_t)xbase * XCHUNK;
-      for (int c = tid >> 2; c < nxs; c += blockDim.x >> 2) {
-        const float4 lo = *(const float4*)(xr + (int64_t)c * XCHUNK + 4 * m);
-        const float4 hi = *(const float4*)(xr + (int64_t)c * XCHUNK + 16 + 4 * m);
-        const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        digitize_group_to(
-            v, m, digit_kind(QT),
-            [&](int i, uint32_t w) { ldw[((n * XSLOTS + (i >> 2)) * nxp + c) * 4 + (i & 3)] = w; }, true);
+      for (int c0 = tid >> 2; c0 < nxs; c0 += XU * cstep) {
+        float4 lo[XU], hi[XU];
+#pragma unroll
+        for (int u = 0; u < XU; ++u) {
+          const int c = min(c0 + u * cstep, nxs - 1);
+          lo[u] = *(const float4*)(xr + (int64_t)c * XCHUNK + 4 * m);
+          hi[u] = *(const float4*)(xr + (int64_t)c * XCHUNK + 16 + 4 * m);
+        }
+#pragma unroll
+        for (int u = 0; u < XU; ++u) {
+          const int c = c0 + u * cstep;  // the four threads of a chunk agree on c < nxs
+          const float v[8] = {lo[u].x, lo[u].y, lo[u].z, lo[u].w, hi[u].x, hi[u].y, hi[u].z, hi[u].w};
+          digitize_group_to(
+              v, m, digit_kind(QT),
+              [&](int i, uint32_t w) { ldw[((n * XSLOTS + (i >> 2)) * nxp + c) * 4 + (i & 3)] = w; }, c < nxs);
+        }
       }
     }
   } else {
+    constexpr int SU = 8;  // 16-B slots in flight per thread
+    const int tot = nxs * XSLOTS, step = blockDim.x;
     for (int n = 0; n < nc; ++n) {
       const uint4* src = a.xd + (int64_t)n * a.xd_stride + (int64_t)xbase * XSLOTS;
-      for (int i = tid; i < nxs * XSLOTS; i += blockDim.x) {
-        const int c = i / XSLOTS, q = i % XSLOTS;
-        lds[(n * XSLOTS + q) * nxp + c] = src[i];
+      for (int b = tid; b < tot; b += SU * step) {
+        uint4 v[SU];
+#pragma unroll
+        for (int u = 0; u < SU; ++u) v[u] = src[min(b + u * step, tot - 1)];
+#pragma unroll
+        for (int u = 0; u < SU; ++u) {
+          const int i = b + u * step;
+          if (i < tot) lds[(n * XSLOTS + i % XSLOTS) * nxp + i / XSLOTS] = v[u];
+        }
       }
     }
   }
@@ -521,23 +540,37 @@ GemvPlan plan_gemv(int qt, int64_t rows, int64_t k, int nc, int epi) {
   p.ksplit = (int)((k + p.ks - 1) / p.ks);
   p.lds = (size_t)lds_row_slots((int)xs) * per_chunk;
   p.part_bytes = p.ksplit > 1 ? (size_t)p.ksplit * nc * rows * sizeof(float) : 0;
-  // one column, 8 waves (measured on the 70B shapes): two rows per wave for the plain and QKV
-  // epilogues; four for SwiGLU and for the residual epilogue, whose 32 rows per workgroup are a
-  // whole chunk of the next GEMV's input digits, written by this kernel.  SwiGLU needs 64 rows
-  // (32 outputs) for that: two passes of 32, for the formats whose 4-row kernel fits 128
-  // registers (16 waves or 8 rows per wave ran slower).
-  if (p.ncm == 1) p.rows_per_wave = (epi == EPI_RESID || epi == EPI_SWIGLU) ? 4 : 2;
-  if (p.ncm == 1 && epi == EPI_SWIGLU && p.ksplit == 1 && two_pass_ok(qt)) p.passes = 2;
+  // one column, two rows per wave (measured on the 70B shapes: a four-row kernel needs about 110
+  // registers against about 70, and the occupancy two rows leave wins).  The residual epilogue also
+  // writes the next GEMV's input digits, which takes whole 32-element chunks of output per
+  // workgroup: 8 waves x two row passes = 32 rows.  SwiGLU runs 4 waves x four passes = 32 rows (16
+  // outputs, so the down GEMV digitizes its fp32 input itself): 64-row workgroups that could write
+  // the digits measured 4 us slower on the 28672 x 2 rows, more than the down prologue costs.
+  if (p.ncm == 1 && p.ksplit == 1) {
+    if (epi == EPI_RESID) p.passes = 2;
+    if (epi == EPI_SWIGLU) {
+      p.passes = 4;
+      p.waves = 4;
+    }
+  }
   // explicit overrides (tuning and tests)
-  if (g_waves == 2 || g_waves == 4 || g_waves == 8) p.waves = g_waves;
+  if (g_waves == 2 || g_waves == 4 || g_waves == 8 || (g_waves == 16 && p.ncm == 1)) p.waves = g_waves;
   if (p.ncm == 1 && (g_rows == 1 || g_rows == 2 || g_rows == 4)) p.rows_per_wave = g_rows;
   if (g_depth == 1 || g_depth == 2) p.depth = g_depth;
-  if (g_passes == 1 || g_passes == 2) p.passes = g_passes;
+  if (g_passes == 1 || g_passes == 2 || g_passes == 4 || g_passes == 8) p.passes = g_passes;
   if (pairs && p.rows_per_wave < 2) p.rows_per_wave = 2;
-  // compiled row-pass variants: one column, 2 or 4 rows, one-ahead loads, digitizing epilogues
-  if (!(p.ncm == 1 && p.rows_per_wave >= 2 && p.depth == 1 && p.ksplit == 1 &&
-        (epi == EPI_RESID || epi == EPI_SWIGLU)))
-    p.passes = 1;
+  if (p.waves == 16) {  // compiled for two rows and one-ahead loads only
+    p.rows_per_wave = 2;
+    p.depth = 1;
+  }
+  if ((p.rows_per_wave == 4 || p.waves == 16) && p.passes >= 4) p.passes = 2;
+  // compiled row-pass variants: one column, one-ahead loads, digitizing epilogues; two rows with two
+  // or four passes (sixteen waves: two), four rows with two passes for the formats whose four-row
+  // kernel fits 128 registers
+  const bool pass_ok = p.ncm == 1 && p.depth == 1 && p.ksplit == 1 && (epi == EPI_RESID || epi == EPI_SWIGLU) &&
+                       ((p.rows_per_wave == 2 && (p.passes == 2 || p.passes == 4 || p.passes == 8)) ||
+                        (p.rows_per_wave == 4 && p.passes == 2 && two_pass_ok(qt)));
+  if (!pass_ok) p.passes = 1;
   // several columns: the staged activation (112 B per 32 elements and column) is as large as the
   // weights a workgroup of one pass reads, so one workgroup per CU stages it once and strides over
   // the row blocks (persistent)
@@ -553,8 +586,12 @@ GemvPlan plan_gemv(int qt, int64_t rows, int64_t k, int nc, int epi) {
   return p;
 }
 
+// compiled input-digitizing kernels: 32 rows per workgroup as 8 waves x 4 rows, 8 waves x 2 rows x 2
+// passes, or 16 waves x 2 rows
 bool gemv_can_digitize_input(const GemvPlan& p, int epi) {
-  return p.ncm == 1 && p.ksplit == 1 && epi == EPI_RESID && p.rows_per_wave == 4 && p.depth == 1 && p.passes == 1;
+  if (!(p.ncm == 1 && p.ksplit == 1 && epi == EPI_RESID && p.depth == 1)) return false;
+  if (p.waves == 16) return p.rows_per_wave == 2 && p.passes == 1;
+  return p.waves == 8 && ((p.rows_per_wave == 4 && p.passes == 1) || (p.rows_per_wave == 2 && p.passes == 2));
 }
 
 bool gemv_can_digitize_output(const GemvPlan& p, int epi, int64_t rows) {
@@ -580,26 +617,26 @@ static void go(const Dispatch& d, Kern kern, dim3 grid, dim3 block, size_t lds, 
     hipLaunchKernelGGL(kern, grid, block, lds, d.st, args...);
 }
 
-template <int QT, int NCM, int R, int PD, int P = 1>
+template <int QT, int NCM, int R, int PD, int P = 1, int LB = 512>
 static hipError_t launch_t(const GemvArgs& a, int epi, int ksplit, dim3 grid, dim3 block, size_t lds,
                            const Dispatch& d) {
   switch (ksplit > 1 ? EPI_PART : epi) {
-    case EPI_PART: go(d, k_gemv<QT, NCM, R, EPI_PART, PD, P>, grid, block, lds, a); break;
-    case EPI_STORE: go(d, k_gemv<QT, NCM, R, EPI_STORE, PD, P>, grid, block, lds, a); break;
-    case EPI_RESID: go(d, k_gemv<QT, NCM, R, EPI_RESID, PD, P>, grid, block, lds, a); break;
-    case EPI_SWIGLU: go(d, k_gemv<QT, NCM, R, EPI_SWIGLU, PD, P>, grid, block, lds, a); break;
-    case EPI_QKV: go(d, k_gemv<QT, NCM, R, EPI_QKV, PD, P>, grid, block, lds, a); break;
+    case EPI_PART: go(d, k_gemv<QT, NCM, R, EPI_PART, PD, P, LB>, grid, block, lds, a); break;
+    case EPI_STORE: go(d, k_gemv<QT, NCM, R, EPI_STORE, PD, P, LB>, grid, block, lds, a); break;
+    case EPI_RESID: go(d, k_gemv<QT, NCM, R, EPI_RESID, PD, P, LB>, grid, block, lds, a); break;
+    case EPI_SWIGLU: go(d, k_gemv<QT, NCM, R, EPI_SWIGLU, PD, P, LB>, grid, block, lds, a); break;
+    case EPI_QKV: go(d, k_gemv<QT, NCM, R, EPI_QKV, PD, P, LB>, grid, block, lds, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-// two row passes (one column, one-ahead loads, residual or SwiGLU epilogue)
-template <int QT, int R>
-static hipError_t launch_p2(const GemvArgs& a, int epi, dim3 grid, dim3 block, size_t lds, const Dispatch& d) {
+// P row passes (one column, one-ahead loads, residual or SwiGLU epilogue with output digits)
+template <int QT, int R, int P, int LB = 512>
+static hipError_t launch_pn(const GemvArgs& a, int epi, dim3 grid, dim3 block, size_t lds, const Dispatch& d) {
   switch (epi) {
-    case EPI_RESID: go(d, k_gemv<QT, 1, R, EPI_RESID, 1, 2>, grid, block, lds, a); break;
-    case EPI_SWIGLU: go(d, k_gemv<QT, 1, R, EPI_SWIGLU, 1, 2>, grid, block, lds, a); break;
+    case EPI_RESID: go(d, k_gemv<QT, 1, R, EPI_RESID, 1, P, LB>, grid, block, lds, a); break;
+    case EPI_SWIGLU: go(d, k_gemv<QT, 1, R, EPI_SWIGLU, 1, P, LB>, grid, block, lds, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -612,13 +649,25 @@ static hipError_t launch_fmt(const GemvArgs& a, const GemvPlan& p, int epi, dim3
   const size_t lds = p.lds;
   if (a.e.xf) {
     if (!gemv_can_digitize_input(p, epi)) return hipErrorInvalidValue;
-    go(dd, k_gemv<QT, 1, 4, EPI_RESID, 1, 1, 512, 1>, grid, block, lds, a);
+    if (p.waves == 16)
+      go(dd, k_gemv<QT, 1, 2, EPI_RESID, 1, 1, 1024, 1>, grid, block, lds, a);
+    else if (r == 2)
+      go(dd, k_gemv<QT, 1, 2, EPI_RESID, 1, 2, 512, 1>, grid, block, lds, a);
+    else
+      go(dd, k_gemv<QT, 1, 4, EPI_RESID, 1, 1, 512, 1>, grid, block, lds, a);
     return hipGetLastError();
   }
-  if (p.passes == 2) {
+  if (p.waves == 16) {  // sixteen waves: two rows, one-ahead loads, one or two passes
+    if (p.ncm != 1 || r != 2 || d != 1) return hipErrorInvalidValue;
+    if (p.passes == 2) return launch_pn<QT, 2, 2, 1024>(a, epi, grid, block, lds, dd);
+    return launch_t<QT, 1, 2, 1, 1, 1024>(a, epi, p.ksplit, grid, block, lds, dd);
+  }
+  if (p.passes == 2 || p.passes == 4 || p.passes == 8) {
     if (p.ncm != 1 || d != 1 || p.ksplit > 1) return hipErrorInvalidValue;
-    if (r == 2) return launch_p2<QT, 2>(a, epi, grid, block, lds, dd);
-    if (r == 4) return launch_p2<QT, 4>(a, epi, grid, block, lds, dd);
+    if (r == 2 && p.passes == 8) return launch_pn<QT, 2, 8>(a, epi, grid, block, lds, dd);
+    if (r == 2) return p.passes == 2 ? launch_pn<QT, 2, 2>(a, epi, grid, block, lds, dd)
+                                     : launch_pn<QT, 2, 4>(a, epi, grid, block, lds, dd);
+    if (r == 4 && p.passes == 2) return launch_pn<QT, 4, 2>(a, epi, grid, block, lds, dd);
     return hipErrorInvalidValue;
   }
   if (p.ncm == 1 && r == 1) return d == 2 ? launch_t<QT, 1, 1, 2>(a, epi, p.ksplit, grid, block, lds, dd)

@@ -150,7 +150,7 @@ def test_swiglu_cosine_argmax(ops):
 
 
 @pytest.mark.parametrize("qt", QTS, ids=[synth.QTYPE_NAMES[q] for q in QTS])
-@pytest.mark.parametrize("geom", [(8, 1, 2, 1), (8, 2, 2, 1), (8, 4, 2, 1), (4, 4, 1, 1), (2, 1, 1, 1)],
+@pytest.mark.parametrize("geom", [(8, 1, 2, 1), (8, 2, 2, 1), (8, 4, 2, 1), (4, 4, 1, 1), (2, 1, 1, 1), (16, 2, 1, 1)],
                          ids=lambda g: "w%d_r%d_d%d_p%d" % g)
 def test_gemv_launch_geometries(ops, qt, geom):
     """Every launch geometry and pipeline depth gives rows within the bound, incl. ragged tails."""

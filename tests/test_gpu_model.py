@@ -172,7 +172,8 @@ def test_context_overflow_is_an_error(qwg):
 
 
 @pytest.mark.parametrize("geom", [(4, 1, 1, 1), (8, 1, 2, 1), (2, 2, 1, 1), (8, 4, 2, 1), (8, 2, 2, 1),
-                                  (8, 2, 1, 2), (4, 4, 1, 2), (2, 4, 1, 2), (8, 4, 1, 1)],
+                                  (8, 2, 1, 2), (4, 4, 1, 2), (2, 4, 1, 2), (8, 4, 1, 1), (8, 2, 1, 4),
+                                  (4, 2, 1, 4), (16, 2, 1, 1), (16, 2, 1, 2), (4, 2, 1, 8)],
                          ids=lambda g: "w%d_r%d_d%d_p%d" % g)
 def test_decode_under_launch_geometries(qwg, geom):
     """Every launch geometry computes the same step (the pair epilogues need two rows per wave)."""
