@@ -100,13 +100,16 @@ int qwg_dequantize(int qtype, const void* d_packed, int64_t rows, int64_t k, flo
 int qwg_gemv(int qtype, const void* d_packed, int64_t rows, int64_t k, const float* d_x, int n_cols, float* d_y,
              void* stream);
 
-/* Launch geometry of subsequent GEMV launches in this process, for tuning: waves per workgroup
- * (2, 4 or 8; 16 for single-column GEMVs, with 2 rows per wave, depth 1 and at most 2 passes),
- * output rows per wave for single-column GEMVs (1, 2 or 4), weight-load pipeline
- * depth (1 or 2 iterations in flight) and row passes per wave (1, 2, 4 or 8; several passes apply
- * to single-column residual and SwiGLU GEMVs at depth 1: 2, 4 or 8 passes with 2 rows per wave, 2
- * passes with 4 rows for Q4_0, Q4_K and Q8_0); 0 keeps the default.  Results do not depend on it beyond floating-point summation order.  Not thread-safe:
- * call it while no other thread launches GEMVs. */
+/* Launch geometry of subsequent GEMV launches in this process, for tuning; 0 keeps the default:
+ *   waves_per_group  2, 4 or 8; 16 for single-column GEMVs (2 rows per wave, depth 1, <= 2 passes)
+ *   rows_per_wave    output rows per wave of single-column GEMVs: 1, 2 or 4
+ *   pipeline_depth   iterations of weight loads in flight: 1 or 2
+ *   row_passes       row blocks per workgroup of single-column residual and SwiGLU GEMVs at depth
+ *                    1: 1, 2, 4 or 8 with 2 rows per wave; 2 with 4 rows per wave for Q4_0, Q4_K
+ *                    and Q8_0
+ * Combinations without a compiled kernel fall back to the nearest one.  Results do not depend on
+ * the geometry beyond floating-point summation order.  Not thread-safe: call it while no other
+ * thread launches GEMVs. */
 int qwg_set_gemv_geometry(int waves_per_group, int rows_per_wave, int pipeline_depth, int row_passes);
 
 /* RMSNorm ([NT] "Key features"; cuda/ RMSNorm kernel): d_out[j][i] = g[i] x[j][i] / sqrt(mean_i x[j]^2 + eps),

@@ -215,7 +215,8 @@ __global__ __launch_bounds__(LB, (R == 4 && P == 2 ? 4 : 1)) void k_gemv(GemvArg
   // rows past the end are clamped to the last row (loads stay in bounds, results are dropped)
   // (per-chunk regions are addressed by slot = per-row part + per-chunk part, see slot_row)
   uint32_t rofs[R], srow[R];
-  typename F::Raw b0[R], b1[R], b2[R];
+  constexpr int NB = PD + 1;  // buffers in rotation: PD in flight while one is computed
+  typename F::Raw buf[NB][R];
   auto set_rows = [&](int r0) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -243,8 +244,8 @@ __global__ __launch_bounds__(LB, (R == 4 && P == 2 ? 4 : 1)) void k_gemv(GemvArg
   // 1. request the first chunks of this wave's rows before staging the activation
   if (ng > 0) {
     set_rows(row0_of(0));
-    fetch_next(b0);
-    if (PD == 2) fetch_next(b1);
+#pragma unroll
+    for (int k = 0; k < PD; ++k) fetch_next(buf[k]);
   }
 
   // 2. stage this split's activation digits (coalesced 16-B reads, chunk-transposed LDS) and the
@@ -357,36 +358,19 @@ __global__ __launch_bounds__(LB, (R == 4 && P == 2 ? 4 : 1)) void k_gemv(GemvArg
   // unconsumed loads into the loop header (which then waited for every load), and without the
   // barriers the scheduler sank the next fetch into the current compute.
   int t = 0;
-  if (PD == 1) {
-    for (; t + 2 <= total; t += 2) {
-      fetch_next(b1);
+  for (; t + NB <= total; t += NB) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      fetch_next(buf[(k + PD) % NB]);
       __builtin_amdgcn_sched_barrier(0);
-      compute_next(b0);
-      __builtin_amdgcn_sched_barrier(0);
-      fetch_next(b0);
-      __builtin_amdgcn_sched_barrier(0);
-      compute_next(b1);
+      compute_next(buf[k]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (t < total) compute_next(b0);
-  } else {
-    for (; t + 3 <= total; t += 3) {
-      fetch_next(b2);
-      __builtin_amdgcn_sched_barrier(0);
-      compute_next(b0);
-      __builtin_amdgcn_sched_barrier(0);
-      fetch_next(b0);
-      __builtin_amdgcn_sched_barrier(0);
-      compute_next(b1);
-      __builtin_amdgcn_sched_barrier(0);
-      fetch_next(b1);
-      __builtin_amdgcn_sched_barrier(0);
-      compute_next(b2);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (t < total) compute_next(b0);
-    if (t + 1 < total) compute_next(b1);
   }
+  // the last total - t < NB iterations are already in flight, in buf[0 ..)
+#pragma unroll
+  for (int k = 0; k < PD; ++k)
+    if (t + k < total) compute_next(buf[k]);
 
   // 4. epilogue: lane j < ng*R finishes row r = j % R of group g = j / R (its pair partner, row^1,
   //    is lane j^1 of the same group)
