@@ -32,8 +32,8 @@ HBM_PEAK_GBPS = 8000.0
 # change to them `roofline.traffic` is reported as null until the passes are taken again.
 GEMV_TRAFFIC = {
     "workload": "llama70b-q4_k-resident",
-    "sources_sha256": "5d4fb884e99c966c74ba286c17a6f4c6159ae8e27bbeea80e88743c443740a88",
-    "fetch_kib": 130871.08, "fetch_scale": 1.99974, "write_kib": 114.25, "write_scale": 1.0,
+    "sources_sha256": "4656b7ab71a608b84cd615e6b0b282ead1421f5e0c283e401bf682f5c2a730f7",
+    "fetch_kib": 130450.79, "fetch_scale": 1.99975, "write_kib": 112.00, "write_scale": 1.00000,
 }
 GEMV_SOURCES = ("qwg_gemv.hip", "qwg_formats.h", "qwg_kernels.h")
 
