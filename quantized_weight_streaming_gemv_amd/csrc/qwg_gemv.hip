@@ -3,24 +3,26 @@
 // quantization-format table).
 //
 // Work decomposition (batch-1 decode is HBM-bound: every weight byte is read exactly once):
-//   * a workgroup of W wave64s owns W*R consecutive output rows and one K split;
-//   * each wave owns R rows; lane l walks chunks l, l+64, ... of those rows, so every wave-wide
-//     load instruction reads 1 KiB of contiguous quant bytes (16 B per lane);
+//   * a workgroup of W wave64s owns P row blocks of W*R consecutive output rows (or, persistent,
+//     every gridDim-th row block) and one K split;
+//   * each wave owns R rows of each block; lane l walks chunks l, l+64, ... of those rows, so every
+//     wave-wide load instruction reads 1 KiB of contiguous quant bytes (16 B per lane);
 //   * the activation arrives as block fixed-point digits (see qwg_formats.h): 28 words per 32
 //     elements, staged once per workgroup into LDS in a chunk-transposed layout -- 16-B slot q of
 //     chunk c of column n at (n*7 + q)*S + c, with the row stride S padded against bank conflicts
-//     of the staging writes -- so the 64 lanes of a wave read 64 consecutive slots;
+//     of the staging writes -- so the 64 lanes of a wave read 64 consecutive slots (or it arrives
+//     as fp32 and the workgroup digitizes it into the same layout);
 //   * quants stay integers: nibble formats feed v_dot8_i32_i4 directly (stored as q XOR 8), the
 //     others feed v_dot4_i32_i8 with one byte per quant; each chunk's integer sums are recombined
 //     in fp32 and scaled once by the block scales and the activation chunk scale;
 //   * an RMSNorm in front of the GEMV is folded in: the digits are of g*h, and the finished rows are
 //     multiplied by 1/rms, reduced in a fixed order from per-chunk sums of h^2 in the prologue;
-//   * the first chunk's weights are requested before the activation is staged, and each loop
-//     iteration requests the next chunk before computing the current one;
-//   * a 64-lane butterfly (shuffles) reduces each row; lanes 0..R-1 run the epilogue (store,
-//     residual add, SwiGLU on interleaved gate|up rows, or RoPE + fp16 KV append), and for the
-//     residual and SwiGLU epilogues the workgroup also digitizes its slice of the output vector
-//     for the next GEMV (each workgroup writes whole 32-element chunks);
+//   * the first chunks' weights are requested before the activation is staged; a wave's row blocks
+//     then run as one software pipeline that keeps PD iterations of loads in flight;
+//   * DPP reductions sum each finished row over the 64 lanes and park it in one lane; after the
+//     loop those lanes run the epilogue (store, residual add, SwiGLU on interleaved gate|up rows,
+//     or RoPE + fp16 KV append), and for the residual and SwiGLU epilogues the workgroup can also
+//     digitize its slice of the output vector for the next GEMV (whole 32-element chunks);
 //   * K splits (when the activation for all columns does not fit the LDS budget) write partial
 //     sums that a second kernel adds in a fixed order, so results never depend on timing.
 #include <hip/hip_ext.h>
@@ -491,7 +493,8 @@ hipError_t launch_digitize(const float* x, int64_t x_stride, const float* gain, 
 // ------------------------------------------------------------------------------------------ host side
 
 static int g_waves = 0, g_rows = 0, g_depth = 0, g_passes = 0;  // launch-geometry overrides (0 = default)
-constexpr int PERSISTENT_WGS = 256;  // workgroups of a persistent (several-column) GEMV: one per CU
+constexpr int PERSISTENT_WGS = 256;   // workgroups of a persistent several-column GEMV: one per CU
+constexpr int PERSISTENT_WGS1 = 768;  // of a persistent one-column GEMV: three per CU
 
 void set_gemv_geometry(int waves, int rows_per_wave, int depth, int passes) {
   g_waves = waves;
@@ -536,7 +539,14 @@ GemvPlan plan_gemv(int qt, int64_t rows, int64_t k, int nc, int epi) {
       p.passes = 4;
       p.waves = 4;
     }
+    if (epi == EPI_QKV) p.waves = 4;  // 8-row workgroups: 1280 of them balance 10240 rows over 256 CUs
   }
+  // Very tall one-column GEMVs (the 128256-row head: 8016 blocks of 16 rows) run persistent: a grid
+  // of PERSISTENT_WGS1 workgroups strides over the row blocks, so the activation is staged once per
+  // workgroup instead of once per 16 rows (224 MB of staging reads at 128256 x 8192).
+  const int64_t blk1 = (int64_t)p.waves * p.rows_per_wave;
+  const bool tall = p.ncm == 1 && p.ksplit == 1 && epi == EPI_STORE &&
+                    (rows + blk1 - 1) / blk1 > 4 * PERSISTENT_WGS1;
   // explicit overrides (tuning and tests)
   if (g_waves == 2 || g_waves == 4 || g_waves == 8 || (g_waves == 16 && p.ncm == 1)) p.waves = g_waves;
   if (p.ncm == 1 && (g_rows == 1 || g_rows == 2 || g_rows == 4)) p.rows_per_wave = g_rows;
@@ -558,6 +568,12 @@ GemvPlan plan_gemv(int qt, int64_t rows, int64_t k, int nc, int epi) {
   // several columns: the staged activation (112 B per 32 elements and column) is as large as the
   // weights a workgroup of one pass reads, so one workgroup per CU stages it once and strides over
   // the row blocks (persistent)
+  if (tall && p.waves == 8 && p.rows_per_wave == 2 && p.depth == 1 && g_passes == 0) {
+    const int64_t blk = (int64_t)p.waves * p.rows_per_wave;
+    const int64_t nblk = (rows + blk - 1) / blk;
+    p.passes = 0;
+    p.grid_x = (int)std::max<int64_t>(PERSISTENT_WGS1, (nblk + 64 / p.rows_per_wave - 1) / (64 / p.rows_per_wave));
+  }
   if (p.ncm > 1) {
     p.passes = 0;
     p.depth = 1;
@@ -656,6 +672,10 @@ static hipError_t launch_fmt(const GemvArgs& a, const GemvPlan& p, int epi, dim3
   }
   if (p.ncm == 1 && r == 1) return d == 2 ? launch_t<QT, 1, 1, 2>(a, epi, p.ksplit, grid, block, lds, dd)
                                           : launch_t<QT, 1, 1, 1>(a, epi, p.ksplit, grid, block, lds, dd);
+  if (p.ncm == 1 && r == 2 && p.passes == 0) {  // persistent (tall store GEMVs)
+    if (epi != EPI_STORE || d != 1 || p.waves != 8) return hipErrorInvalidValue;
+    return launch_t<QT, 1, 2, 1, 0>(a, epi, p.ksplit, grid, block, lds, dd);
+  }
   if (p.ncm == 1 && r == 2) return d == 2 ? launch_t<QT, 1, 2, 2>(a, epi, p.ksplit, grid, block, lds, dd)
                                           : launch_t<QT, 1, 2, 1>(a, epi, p.ksplit, grid, block, lds, dd);
   if (p.ncm == 1) return d == 2 ? launch_t<QT, 1, 4, 2>(a, epi, p.ksplit, grid, block, lds, dd)
