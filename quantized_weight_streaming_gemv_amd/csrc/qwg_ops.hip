@@ -388,53 +388,81 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attn(AttnArgs a) {
   }
 }
 
-// One wave per (kv head g, query row qi): merges the splits in a fixed order,
-//   M = max_s m_s,  o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s,
-// in blocks of 64 splits whose loads all go out together (lane j holds split j's (m, l), every lane
-// the (2 lane, 2 lane + 1) outputs of the 64 splits), rescaling the running max, sum and
-// output from block to block; then writes the output row (and its activation digits).
-__global__ __launch_bounds__(64) void k_attn_merge(AttnArgs a) {
-  __shared__ float wsh[64];
+// One workgroup of MW waves per (kv head g, query row qi) merges the splits in a fixed order,
+//   M = max_s m_s,  o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s.
+// Wave w takes the blocks of MB splits w, w + MW, w + 2 MW, ... (every load of a block goes out
+// together: lane j < MB holds split j's (m, l), every lane the (2 lane, 2 lane + 1) outputs of the
+// block), rescaling its running max, sum and output from block to block; the waves' partial
+// (m, l, o) are then combined in wave order through LDS.  Wave 0 writes the output row (and its
+// activation digits).  Spreading a row over four waves shortens the chain of dependent loads that
+// bounds this small kernel.
+constexpr int MW = 4;   // waves per merged row
+constexpr int MB = 16;  // splits per block
+__global__ __launch_bounds__(64 * MW) void k_attn_merge(AttnArgs a) {
+  __shared__ float wsh[MW][MB];
+  __shared__ float part_ml[MW][2];
+  __shared__ float2 part_o[MW][64];
   __shared__ float ob[HEAD_DIM];
-  const int g = blockIdx.x, qi = blockIdx.y, lane = threadIdx.x;
+  const int g = blockIdx.x, qi = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int G = a.n_q / a.n_kv, NQ = a.nc * G;
   const int64_t sstride = (int64_t)NQ * (HEAD_DIM + 2);
   const float* base = a.part + ((int64_t)g * a.nsplit * NQ + qi) * (HEAD_DIM + 2);
   float M = -INFINITY, L = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int b0 = 0; b0 < a.nsplit; b0 += 64) {
-    const int nb = min(64, a.nsplit - b0);
+  for (int b0 = wave * MB; b0 < a.nsplit; b0 += MW * MB) {
+    const int nb = min(MB, a.nsplit - b0);
     const float2 st = *(const float2*)(base + (b0 + min(lane, nb - 1)) * sstride);
-    float2 ov[64];
+    float2 ov[MB];
 #pragma unroll
-    for (int j = 0; j < 64; ++j) ov[j] = *(const float2*)(base + (b0 + min(j, nb - 1)) * sstride + 2 + 2 * lane);
+    for (int j = 0; j < MB; ++j) ov[j] = *(const float2*)(base + (b0 + min(j, nb - 1)) * sstride + 2 + 2 * lane);
     const bool ok = lane < nb;
     const float mj = ok ? st.x : -INFINITY;
     const float Mn = fmaxf(M, wave_max(mj));
     const float wj = (ok && mj != -INFINITY) ? __expf(mj - Mn) : 0.f;
     const float keep = M == -INFINITY ? 0.f : __expf(M - Mn);
     L = L * keep + wave_sum(ok ? wj * st.y : 0.f);
-    wsh[lane] = wj;
-    __syncthreads();
+    if (lane < MB) wsh[wave][lane] = wj;
+    __builtin_amdgcn_wave_barrier();  // the weights are read back by every lane of this wave
     o0 *= keep;
     o1 *= keep;
 #pragma unroll
-    for (int j = 0; j < 64; ++j) {
-      const float w = wsh[j];
+    for (int j = 0; j < MB; ++j) {
+      const float w = wsh[wave][j];  // written by lanes of this wave (wave-synchronous)
       o0 += w * ov[j].x;
       o1 += w * ov[j].y;
     }
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
     M = Mn;
   }
-  const float inv = 1.0f / L;
+  if (lane == 0) {
+    part_ml[wave][0] = M;
+    part_ml[wave][1] = L;
+  }
+  part_o[wave][lane] = make_float2(o0, o1);
+  __syncthreads();
+  if (wave != 0) return;
+  float Mt = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < MW; ++w) Mt = fmaxf(Mt, part_ml[w][0]);
+  float Lt = 0.f, t0 = 0.f, t1 = 0.f;
+#pragma unroll
+  for (int w = 0; w < MW; ++w) {
+    const float mw = part_ml[w][0];
+    const float f = mw == -INFINITY ? 0.f : __expf(mw - Mt);
+    Lt += f * part_ml[w][1];
+    t0 += f * part_o[w][lane].x;
+    t1 += f * part_o[w][lane].y;
+  }
+  const float inv = 1.0f / Lt;
   const int n = qi / G, j = qi % G;
-  const float2 o = make_float2(o0 * inv, o1 * inv);
+  const float2 o = make_float2(t0 * inv, t1 * inv);
   *(float2*)(a.out + (int64_t)n * a.out_stride + (int64_t)(g * G + j) * HEAD_DIM + 2 * lane) = o;
   if (a.dig) {
-    // the head's 128 outputs are four whole 32-element chunks: four lanes per chunk
+    // the head's 128 outputs are four whole 32-element chunks: four lanes per chunk (wave 0 only:
+    // its lanes exchange through LDS without a workgroup barrier)
     ob[2 * lane] = o.x;
     ob[2 * lane + 1] = o.y;
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     const int m = lane & 3, c = (lane >> 2) & 3;
     float v[8];
 #pragma unroll
@@ -471,7 +499,7 @@ hipError_t launch_attn(const float* q, int64_t q_stride, const uint16_t* kc, con
   hipLaunchKernelGGL(k_attn, dim3(n_kv, p.nsplit), dim3(ATT_THREADS), lds, st, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_attn_merge, dim3(n_kv, NQ), dim3(64), 0, st, a);
+  hipLaunchKernelGGL(k_attn_merge, dim3(n_kv, NQ), dim3(64 * MW), 0, st, a);
   return hipGetLastError();
 }
 

@@ -75,6 +75,21 @@ def test_gemv_row_tolerance(ops, qt, shape, nc):
     assert ok.all(), (np.argwhere(~ok)[:5], y[~ok][:5], yr[~ok][:5])
 
 
+@pytest.mark.parametrize("qt", QTS, ids=[synth.QTYPE_NAMES[q] for q in QTS])
+@pytest.mark.parametrize("nc", [1, 4])
+def test_gemv_tall_persistent(ops, qt, nc):
+    """Matrices with more than 4 x 768 blocks of 16 rows run a persistent grid that strides over
+    the row blocks (one column) or parks up to 32 finished row groups per wave (several columns);
+    a ragged row count checks the last, partial block."""
+    rows, k = 4 * 768 * 16 + 1234, 512
+    W = synth.matrix(synth.DEFAULT_DIST[qt], k, rows, tkey=synth.key(2, qt * 1000 + 77))
+    x = synth.normal_f32(synth.key(2, 90 + nc), nc * k).reshape(nc, k)
+    y = ops.gemv(qt, packed_of(ops, qt, W, rows, k), rows, k, dev(x)).cpu().numpy()
+    yr, ar = oracle.gemv(qt, W, rows, k, x)
+    ok = gemv_ok(y, yr, ar)
+    assert ok.all(), (np.argwhere(~ok)[:5], y[~ok][:5], yr[~ok][:5])
+
+
 def test_gemv_q8_0_4096_full(ops):
     """The single Q8_0 GEMV workload: W 4096 x 4096, q ~ U[-127,127], d = |N|*0.02, x ~ N(0,1)."""
     qt, rows, k = synth.Q8_0, 4096, 4096
