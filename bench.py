@@ -32,8 +32,8 @@ HBM_PEAK_GBPS = 8000.0
 # change to them `roofline.traffic` is reported as null until the passes are taken again.
 GEMV_TRAFFIC = {
     "workload": "llama70b-q4_k-resident",
-    "sources_sha256": "4656b7ab71a608b84cd615e6b0b282ead1421f5e0c283e401bf682f5c2a730f7",
-    "fetch_kib": 130450.79, "fetch_scale": 1.99975, "write_kib": 112.00, "write_scale": 1.00000,
+    "sources_sha256": "15cd7a0a64b608ca6f8fc7944afe62fcbf3feca36fee158a55ac0b235d8d6428",
+    "fetch_kib": 130426.54, "fetch_scale": 1.99974, "write_kib": 112.00, "write_scale": 1.00000,
 }
 GEMV_SOURCES = ("qwg_gemv.hip", "qwg_formats.h", "qwg_kernels.h")
 
