@@ -577,6 +577,12 @@ GemvPlan plan_gemv(int qt, int64_t rows, int64_t k, int nc, int epi) {
   if (p.ncm > 1) {
     p.passes = 0;
     p.depth = 1;
+    // four columns: the staged activation leaves one workgroup per CU whatever the registers, so
+    // waves take four rows (about 240 registers) for twice the loads in flight -- where that still
+    // leaves every workgroup two or more row blocks (gate|up, down; not QKV or Wo)
+    const int64_t nblk4 = (rows + (int64_t)p.waves * 4 - 1) / ((int64_t)p.waves * 4);
+    const int64_t grid4 = std::max<int64_t>(std::max(1, PERSISTENT_WGS / p.ksplit), (nblk4 + 15) / 16);
+    p.rows_per_wave = (p.ncm == 4 && g_rows != 2 && nblk4 >= 2 * grid4) ? 4 : 2;
     // a wave parks each finished row group's totals in R lanes: at most 64 / R groups per workgroup
     const int64_t blk = (int64_t)p.waves * p.rows_per_wave;
     const int64_t nblk = (rows + blk - 1) / blk;
@@ -681,6 +687,7 @@ static hipError_t launch_fmt(const GemvArgs& a, const GemvPlan& p, int epi, dim3
   if (p.ncm == 1) return d == 2 ? launch_t<QT, 1, 4, 2>(a, epi, p.ksplit, grid, block, lds, dd)
                                 : launch_t<QT, 1, 4, 1>(a, epi, p.ksplit, grid, block, lds, dd);
   if (p.passes != 0) return hipErrorInvalidValue;  // several columns run persistent
+  if (p.ncm == 4 && r == 4) return launch_t<QT, 4, 4, 1, 0>(a, epi, p.ksplit, grid, block, lds, dd);
   if (p.ncm == 4) return launch_t<QT, 4, 2, 1, 0>(a, epi, p.ksplit, grid, block, lds, dd);
   return launch_t<QT, 8, 2, 1, 0>(a, epi, p.ksplit, grid, block, lds, dd);
 }
