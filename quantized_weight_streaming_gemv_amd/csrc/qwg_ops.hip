@@ -287,8 +287,9 @@ static size_t attn_lds_bytes(int NQ) {
   return (size_t)NQ * HEAD_DIM * 4 + (size_t)NQ * ATT_T * 4 + (size_t)ATT_T * KROW * 2 + (size_t)ATT_T * HEAD_DIM * 2;
 }
 
-// One workgroup per (kv head g, split s of ATT_T positions) for all NQ = nc * n_q / n_kv query rows
-// of the group (GQA: the query heads g*G .. g*G+G-1 of every column share K/V head g):
+// One workgroup per (kv head g, split s of ATT_T positions, column n) for the G = n_q / n_kv query
+// rows of the group in that column (GQA: query heads g*G .. g*G+G-1 share K/V head g; a several-
+// column verify pass gets a workgroup per column, so its rows spread over more CUs):
 //   1. the K and V tiles and the queries are staged in LDS (every global load issued up front);
 //   2. wave w scores query rows w, w+ATT_WAVES, ... against its lane's position (scale 1/sqrt(128)), with
 //      causal masking per column, and keeps the split's max m, sum l and exp(score - m);
@@ -296,12 +297,12 @@ static size_t attn_lds_bytes(int NQ) {
 // k_attn_merge then combines the splits.
 __global__ __launch_bounds__(ATT_THREADS) void k_attn(AttnArgs a) {
   extern __shared__ float sm[];
-  const int g = blockIdx.x, s = blockIdx.y;
+  const int g = blockIdx.x, s = blockIdx.y, n = blockIdx.z;
   const int G = a.n_q / a.n_kv, NQ = a.nc * G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float* qs = sm;                                // [NQ][HEAD_DIM]
-  float* ps = qs + NQ * HEAD_DIM;                // [NQ][ATT_T]
-  uint16_t* ks = (uint16_t*)(ps + NQ * ATT_T);   // [ATT_T][KROW]
+  float* qs = sm;                                // [G][HEAD_DIM]
+  float* ps = qs + G * HEAD_DIM;                 // [G][ATT_T]
+  uint16_t* ks = (uint16_t*)(ps + G * ATT_T);    // [ATT_T][KROW]
   uint16_t* vs = ks + ATT_T * KROW;              // [ATT_T][HEAD_DIM]
   const int t0 = s * ATT_T;
   const int span = a.n_pos + a.nc - 1;
@@ -319,9 +320,8 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attn(AttnArgs a) {
       kv[j] = *(const uint4*)(a.kc + off);
       vv[j] = *(const uint4*)(a.vc + off);
     }
-    for (int i = tid; i < NQ * (HEAD_DIM / 4); i += ATT_THREADS) {
-      const int qi = i / (HEAD_DIM / 4), d4 = i % (HEAD_DIM / 4);
-      const int n = qi / G, j = qi % G;
+    for (int i = tid; i < G * (HEAD_DIM / 4); i += ATT_THREADS) {
+      const int j = i / (HEAD_DIM / 4), d4 = i % (HEAD_DIM / 4);
       ((float4*)qs)[i] = ((const float4*)(a.q + (int64_t)n * a.q_stride + (int64_t)(g * G + j) * HEAD_DIM))[d4];
     }
 #pragma unroll
@@ -345,9 +345,9 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attn(AttnArgs a) {
       kr[4 * i + 3] = v.w;
     }
     const float scale = 0.08838834764831845f;  // 1/sqrt(128)
-    for (int qi = wave; qi < NQ; qi += ATT_WAVES) {
-      const int n = qi / G;
-      const float4* qv = (const float4*)(qs + qi * HEAD_DIM);
+    for (int j = wave; j < G; j += ATT_WAVES) {
+      const int qi = n * G + j;
+      const float4* qv = (const float4*)(qs + j * HEAD_DIM);
       float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll
       for (int i = 0; i < HEAD_DIM / 4; ++i) {
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attn(AttnArgs a) {
       const float m = wave_max(sc);
       const float e = ok ? __expf(sc - m) : 0.f;
       const float l = wave_sum(e);
-      ps[qi * ATT_T + lane] = e;
+      ps[j * ATT_T + lane] = e;
       if (lane == 0) {
         float* pr = a.part + (((int64_t)g * a.nsplit + s) * NQ + qi) * (HEAD_DIM + 2);
         pr[0] = m;
@@ -373,8 +373,9 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attn(AttnArgs a) {
   __syncthreads();
 
   // 3. unnormalised output: wave w takes query rows w, w+ATT_WAVES, ...; lane = dimensions 2c, 2c+1
-  for (int qb = wave; qb < NQ; qb += ATT_WAVES) {
-    const float* pr = ps + qb * ATT_T;
+  for (int j = wave; j < G; j += ATT_WAVES) {
+    const int qb = n * G + j;
+    const float* pr = ps + j * ATT_T;
     float o0 = 0.f, o1 = 0.f;
 #pragma unroll 8
     for (int t = 0; t < tn; ++t) {
@@ -494,9 +495,9 @@ hipError_t launch_attn(const float* q, int64_t q_stride, const uint16_t* kc, con
   a.dig = dig_out;
   a.dig_stride = dig_stride;
   a.dig_kind = dig_kind;
-  const size_t lds = attn_lds_bytes(NQ);
+  const size_t lds = attn_lds_bytes(n_q / n_kv);
   if (lds > 150 * 1024) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_attn, dim3(n_kv, p.nsplit), dim3(ATT_THREADS), lds, st, a);
+  hipLaunchKernelGGL(k_attn, dim3(n_kv, p.nsplit, nc), dim3(ATT_THREADS), lds, st, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_attn_merge, dim3(n_kv, NQ), dim3(64 * MW), 0, st, a);
