@@ -593,8 +593,9 @@ GemvPlan plan_gemv(int qt, int64_t rows, int64_t k, int nc, int epi) {
 }
 
 // compiled input-digitizing kernels: 32 rows per workgroup as 8 waves x 4 rows, 8 waves x 2 rows x 2
-// passes, or 16 waves x 2 rows
+// passes, or 16 waves x 2 rows; four-column K-split residual GEMVs (the verify pass's down GEMV)
 bool gemv_can_digitize_input(const GemvPlan& p, int epi) {
+  if (p.ncm == 4) return epi == EPI_RESID && p.ksplit > 1 && p.passes == 0 && p.depth == 1 && p.waves == 8;
   if (!(p.ncm == 1 && p.ksplit == 1 && epi == EPI_RESID && p.depth == 1)) return false;
   if (p.waves == 16) return p.rows_per_wave == 2 && p.passes == 1;
   return p.waves == 8 && ((p.rows_per_wave == 4 && p.passes == 1) || (p.rows_per_wave == 2 && p.passes == 2));
@@ -655,7 +656,12 @@ static hipError_t launch_fmt(const GemvArgs& a, const GemvPlan& p, int epi, dim3
   const size_t lds = p.lds;
   if (a.e.xf) {
     if (!gemv_can_digitize_input(p, epi)) return hipErrorInvalidValue;
-    if (p.waves == 16)
+    if (p.ncm == 4) {  // K-split verify GEMV: partial sums out
+      if (r == 4)
+        go(dd, k_gemv<QT, 4, 4, EPI_PART, 1, 0, 512, 1>, grid, block, lds, a);
+      else
+        go(dd, k_gemv<QT, 4, 2, EPI_PART, 1, 0, 512, 1>, grid, block, lds, a);
+    } else if (p.waves == 16)
       go(dd, k_gemv<QT, 1, 2, EPI_RESID, 1, 1, 1024, 1>, grid, block, lds, a);
     else if (r == 2)
       go(dd, k_gemv<QT, 1, 2, EPI_RESID, 1, 2, 512, 1>, grid, block, lds, a);
