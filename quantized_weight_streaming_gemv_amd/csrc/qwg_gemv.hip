@@ -426,14 +426,47 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const float* part, int kspl
     rms_partials(e, nc, red);
     __syncthreads();
   }
+  // every column's partials are requested before any is added (a column-by-column loop waited for
+  // each column's loads in turn), and for the residual epilogue the residual values too
+  float vs[MAX_COLS], hs[MAX_COLS];
+#pragma unroll
+  for (int n = 0; n < MAX_COLS; ++n) {
+    vs[n] = 0.f;
+    hs[n] = 0.f;
+  }
+  if (row < rows) {
+    for (int s = 0; s < ksplit; ++s) {
+      float t[MAX_COLS];
+#pragma unroll
+      for (int n = 0; n < MAX_COLS; ++n) t[n] = n < nc ? part[((int64_t)s * nc + n) * rows + row] : 0.f;
+#pragma unroll
+      for (int n = 0; n < MAX_COLS; ++n) vs[n] += t[n];
+    }
+    if (EPI == EPI_RESID) {
+#pragma unroll
+      for (int n = 0; n < MAX_COLS; ++n)
+        if (n < nc) hs[n] = e.y[(int64_t)n * e.y_stride + row];
+    }
+  }
   for (int n = 0; n < nc; ++n) {
     float v = 0.f;
-    if (row < rows)
-      for (int s = 0; s < ksplit; ++s) v += part[((int64_t)s * nc + n) * rows + row];
+#pragma unroll
+    for (int i = 0; i < MAX_COLS; ++i)
+      if (i == n) v = vs[i];
     if (e.sq_in) v *= rms_scale(e, red, n);
     const float vp = __shfl_xor(v, 1);
     if (row < rows) {
-      const float out = run_epilogue(EPI, e, n, row, v, vp);
+      float out;
+      if (EPI == EPI_RESID) {
+        float h = 0.f;
+#pragma unroll
+        for (int i = 0; i < MAX_COLS; ++i)
+          if (i == n) h = hs[i];
+        out = h + v;
+        e.y[(int64_t)n * e.y_stride + row] = out;
+      } else {
+        out = run_epilogue(EPI, e, n, row, v, vp);
+      }
       if (digitize) {
         if (EPI == EPI_RESID) osh[n][threadIdx.x] = out;
         else if ((row & 1) == 0) osh[n][threadIdx.x >> 1] = out;
