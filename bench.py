@@ -198,6 +198,8 @@ def main() -> int:
     ap.add_argument("--cpu-layers", type=int, default=8, help="oracle layers in the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-read-ceiling", action="store_true", help="skip the plain streaming-read reference")
+    ap.add_argument("--verify-form", choices=["mfma", "dot"], default="mfma",
+                    help="2..4-column Q5_K/Q6_K GEMVs of the verify pass: matrix cores or integer dot products")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first (scale for PMC byte counters)")
     args = ap.parse_args()
@@ -207,11 +209,12 @@ def main() -> int:
 
     import torch
     import synth
-    from quantized_weight_streaming_gemv_amd import _lib, synthetic
+    from quantized_weight_streaming_gemv_amd import _lib, ops, synthetic
 
     if not os.path.exists(_lib.LIB_PATH):
         import __graft_entry__
         __graft_entry__.build()
+    ops.set_gemv_mfma(args.verify_form == "mfma")
     wl = workloads()[args.workload]
     spec = wl.draft_layers > 0
     total_steps = args.warmup + args.steps * 2 + args.class_steps * 5 + 1
@@ -284,6 +287,19 @@ def main() -> int:
                           "gbps": round(b / (ms / n * 1e-3) / 1e9, 1)}
         tot_b += per_tok_b
         tot_ms += per_tok_ms
+    verify_classes = None
+    if spec:
+        # the verify pass alone (k+1 columns through every layer; it leaves the model state as it was)
+        vtoks = [tok] * (wl.draft_k + 1)
+        verify_classes = {}
+        for cid, label, _ in gemv_classes(wl):
+            m.set_timing(cid)
+            for _ in range(args.class_steps):
+                m.verify(vtoks, want_logits=False)
+            ms, n, b = m.get_timing()
+            verify_classes[label] = {"us_per_launch": round(ms / n * 1e3, 3), "bytes_per_launch": b,
+                                     "gbps": round(b / (ms / n * 1e-3) / 1e9, 1)}
+        log("verify GEMVs (%d columns, %s): %s" % (wl.draft_k + 1, args.verify_form, json.dumps(verify_classes)))
     m.set_timing(-1)
     gemv_gbps = tot_b / (tot_ms * 1e-3) / 1e9
     log("all GEMVs of a step: %.1f GB/s (%.1f%% of 8 TB/s), %.3f ms of %.3f ms" %
@@ -337,7 +353,8 @@ def main() -> int:
         out["hbm_read_ceiling"] = read_ceiling
     if spec:
         out["spec"] = {"rounds": args.steps, "tokens": n_tok, "ms_per_round": round(ms_per_step, 3),
-                       "draft_layers": wl.draft_layers, "k": wl.draft_k}
+                       "draft_layers": wl.draft_layers, "k": wl.draft_k, "verify_form": args.verify_form,
+                       "verify_gemv": verify_classes}
     print(json.dumps(out), flush=True)
     return 0
 

@@ -112,6 +112,15 @@ int qwg_gemv(int qtype, const void* d_packed, int64_t rows, int64_t k, const flo
  * thread launches GEMVs. */
 int qwg_set_gemv_geometry(int waves_per_group, int rows_per_wave, int pipeline_depth, int row_passes);
 
+/* Form of subsequent 2..4-column GEMVs over Q5_K and Q6_K weights (the multi-column verify step of
+ * self-speculative decoding, [NT] "Key features"): on = 1 (the default) runs them on the matrix
+ * cores (v_mfma_i32_16x16x32_i8 over the activation's byte digits), on = 0 on the integer dot
+ * products of the one-column kernel.  Both are exact integer products recombined in fp32, within
+ * the same row tolerance.  Other formats and column counts always take the integer dot products.
+ * Returns QWG_E_INVAL for any other value.  Not thread-safe: call it while no other thread
+ * launches GEMVs. */
+int qwg_set_gemv_mfma(int on);
+
 /* RMSNorm ([NT] "Key features"; cuda/ RMSNorm kernel): d_out[j][i] = g[i] x[j][i] / sqrt(mean_i x[j]^2 + eps),
  * for j < n_cols; x, out fp32 [n_cols][n]; n <= 65536. */
 int qwg_rmsnorm(const float* d_x, const float* d_g, int64_t n, float eps, int n_cols, float* d_out, void* stream);

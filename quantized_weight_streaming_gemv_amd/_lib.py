@@ -50,6 +50,7 @@ SIGNATURES = {
     "qwg_dequantize": (ctypes.c_int, [ctypes.c_int, vp, i64, i64, vp, vp]),
     "qwg_gemv": (ctypes.c_int, [ctypes.c_int, vp, i64, i64, vp, ctypes.c_int, vp, vp]),
     "qwg_set_gemv_geometry": (ctypes.c_int, [ctypes.c_int] * 4),
+    "qwg_set_gemv_mfma": (ctypes.c_int, [ctypes.c_int]),
     "qwg_rmsnorm": (ctypes.c_int, [vp, vp, i64, f32, ctypes.c_int, vp, vp]),
     "qwg_rope_table": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, f64, vp]),
     "qwg_rope": (ctypes.c_int, [vp, ctypes.c_int, ctypes.c_int, vp, ctypes.c_int, vp]),

@@ -224,8 +224,10 @@ static int plan_model(qwg_model* m) {
                                   {V, H}};
     const int qts[5] = {d.qtype_attn, d.qtype_attn, d.qtype_ffn, d.qtype_ffn, d.qtype_head};
     for (int i = 0; i < 5; ++i) {
-      const GemvPlan gp = plan_gemv(qts[i], shapes[i][0], shapes[i][1], nc, EPI_STORE);
-      pb = std::max(pb, gp.part_bytes);
+      for (int mf : {0, 1}) {  // either form of a several-column GEMV may run (qwg_set_gemv_mfma)
+        const GemvPlan gp = plan_gemv(qts[i], shapes[i][0], shapes[i][1], nc, EPI_STORE, mf);
+        pb = std::max(pb, gp.part_bytes);
+      }
     }
   }
   m->part_bytes = pb;
@@ -638,6 +640,12 @@ int qwg_set_gemv_geometry(int waves_per_group, int rows_per_wave, int pipeline_d
   if (!(row_passes == 0 || row_passes == 1 || row_passes == 2 || row_passes == 4 || row_passes == 8))
     return fail(QWG_E_INVAL, "row_passes must be 0, 1, 2, 4 or 8");
   set_gemv_geometry(waves_per_group, rows_per_wave, pipeline_depth, row_passes);
+  return QWG_OK;
+}
+
+int qwg_set_gemv_mfma(int on) {
+  if (on != 0 && on != 1) return fail(QWG_E_INVAL, "on must be 0 or 1");
+  set_gemv_mfma(on);
   return QWG_OK;
 }
 

@@ -482,6 +482,321 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const float* part, int kspl
   }
 }
 
+// ------------------------------------------------------------------ several columns on the matrix cores
+//
+// The verify pass of self-speculative decoding multiplies one weight matrix by k+1 = 2..4 activation
+// columns ([NT] "Key features": self-speculative decoding).  For Q5_K and Q6_K, whose activation
+// digits are bytes, each 16-row tile and 32-weight chunk is one v_mfma_i32_16x16x32_i8 with
+//   A (16 x 32): activation digits, slot m = 4 * column + level (level 3 is zero),
+//   B (32 x 16): the chunk's quants as int8 bytes, one column per output row,
+// so the 4 x 3 digit levels of all columns meet every weight in one exact integer product.  With
+// lane l = 16 g + n:
+//   B: row n, weights 4g..4g+3 and 16+4g..16+4g+3 of the chunk (its quant word g);
+//   A: slot n (column n / 4, level n % 4), the digits of those same eight elements;
+//   D: levels 0..3 of column g, row n -- so every lane finishes one (row, column) pair per chunk:
+//      value = 65536 D2 + (256 D1 + D0), scaled by the chunk's weight scales and activation scale.
+// Each lane loads one whole 16-B chunk (chunk c0 + g of row n, 64 contiguous bytes per row and lane
+// group) and four permlane swaps turn the four chunks' words into word g of each chunk (a 4 x 4
+// transpose across the lane groups).  Q6_K's two 16-weight sub-blocks per chunk take one MFMA each
+// (B masked to the low or high four bytes).
+// A workgroup of nw waves takes blocks of T = nw / S tiles; the S waves of a tile split its chunks
+// (K parts) and add their partial sums in wave order through LDS, so the result does not depend on
+// timing.  The grid is persistent over the blocks; the activation of one K split (416 B per chunk:
+// 384 B of digits, 4 x 8 B of (2^-s, 2^-s sum x_fix)) is staged once per workgroup.
+constexpr int MF_DIG = 48;            // 8-B digit entries per chunk: [word g][column][level]
+constexpr int MF_DSTR = MF_DIG + 1;   // LDS stride of a chunk's entries: 98 words, so the staging
+                                      // writes of consecutive chunks spread over the banks
+constexpr int MF_CHUNK_LDS = MF_DSTR * 8 + 4 * 8;
+constexpr int MF_FIXED_LDS = 4 * 2 * 8;  // the descriptor rows' padding (see k_gemv_mfma)
+
+__device__ __forceinline__ void lane_swap32(uint32_t& a, uint32_t& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);  // lanes 32..63 of a <-> 0..31 of b
+  a = r[0];
+  b = r[1];
+}
+__device__ __forceinline__ void lane_swap16(uint32_t& a, uint32_t& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);  // odd 16-lane rows of a <-> even of b
+  a = r[0];
+  b = r[1];
+}
+
+typedef int qwg_i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ qwg_i32x4 mfma_i8(uint64_t a, uint64_t b) {
+  const qwg_i32x4 z = {0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_i32_16x16x32_i8((long)a, (long)b, z, 0, 0, 0);
+}
+
+// 65536 D2 + 256 D1 + D0 (|256 D1 + D0| < 2^27 is exact in int32; one fp32 rounding)
+__device__ __forceinline__ float mf_value(const qwg_i32x4& d) {
+  return __builtin_fmaf(65536.0f, (float)d[2], (float)(d[0] + d[1] * 256));
+}
+
+// Steps are two superblocks (16 chunks) of the lane's row: chunk c0 + 4 qq + g in quarter qq.
+template <int QT>
+constexpr int mf_step_chunks() { return 16; }
+
+__device__ __forceinline__ uint32_t lane_fetch(int src_lane, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane * 4, (int)v);
+}
+template <int QT>
+struct MfRaw;
+// Q5_K steps are two superblocks (16 chunks); each lane group loads a different part of the rows'
+// fifth bits and headers, and the quarter steps fetch what they need from the group that holds it
+// (ds_bpermute): one 16-B read per lane covers a row's 64 contiguous bytes of fifth bits.
+template <>
+struct MfRaw<Q5_K> {
+  uint4 q[4];  // chunks c0 + 4 qq + g, qq = 0..3
+  uint4 qh;    // fifth bits of chunks c0 + 4g .. c0 + 4g + 3
+  uint4 h;     // header of superblock (c0 / 8) + (g & 1)
+};
+// Q6_K: each lane group loads a different part of the rows' high-bit pairs and sub-block scales
+// (lane_fetch hands them to the quarter steps); the two superblocks' d share one aligned word.
+template <>
+struct MfRaw<Q6_K> {
+  uint4 q[4];
+  uint4 qhA, qhB;  // high-bit pairs of chunks c0 + 2g, c0 + 2g + 1 and c0 + 8 + 2g, c0 + 9 + 2g (8 B each)
+  uint2 sc;        // int8 sub-block scales of chunks c0 + 4g .. c0 + 4g + 3 (2 B each)
+  uint32_t dw;     // fp16 d of superblocks c0 / 8 (low half) and c0 / 8 + 1 (high half)
+};
+
+template <int QT>
+__device__ __forceinline__ MfRaw<QT> mf_load(const MatView& w, uint32_t ro, uint32_t srow, int cg, int g) {
+  MfRaw<QT> r;
+  const uint32_t s0 = srow + slot_chunk(w.ilv, (uint32_t)cg);  // the superblock's 8 chunks are consecutive slots
+  if constexpr (QT == Q5_K) {
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) r.q[qq] = ld_stream_u4(w.q + (s0 + 4u * qq + (uint32_t)g) * 16u);
+    r.qh = ld<uint4>(w.b + (s0 + 4u * g) * 4u);
+    r.h = ld<uint4>(w.a + ro + (uint32_t)((cg >> 3) + (g & 1)) * 16u);
+  } else {
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) r.q[qq] = ld_stream_u4(w.q + (s0 + 4u * qq + (uint32_t)g) * 16u);
+    r.qhA = ld<uint4>(w.a + (s0 + 2u * g) * 8u);
+    r.qhB = ld<uint4>(w.a + (s0 + 8u + 2u * g) * 8u);
+    r.sc = ld<uint2>(w.b + (s0 + 4u * g) * 2u);
+    r.dw = ld<uint32_t>(w.c + ro + (uint32_t)(cg >> 3) * 2u);  // 4-B aligned: K is a multiple of 512
+  }
+  return r;
+}
+
+template <int QT, int EPI>
+__global__ __launch_bounds__(1024) void k_gemv_mfma(GemvArgs a, int kparts) {
+  static_assert(QT == Q5_K || QT == Q6_K, "formats with byte activation digits and 32-weight chunks");
+  extern __shared__ uint4 lds[];
+  __shared__ float red[MAX_COLS][16];
+  const int tid = threadIdx.x, lane = tid & 63, nw = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int nc = a.nc;
+  const int split = blockIdx.y;
+  const int kbeg = split * a.ks;
+  const int klen = min(a.ks, a.k - kbeg);
+  const int nxs = klen / XCHUNK;  // chunks of this split (a multiple of 8)
+  const int nxp = a.ks / XCHUNK;  // LDS capacity in chunks
+  const int xbase = kbeg / XCHUNK;
+  // LDS: digit entries [nxp][MF_DSTR]; per column a row of (2^-s, 2^-s sum x_fix) per chunk, rows
+  // nxp + 2 apart (the four columns' rows then start on different banks); K-part partial sums
+  const int dstr = nxp + 2;
+  uint2* ldig = (uint2*)lds;
+  float2* ldesc = (float2*)(ldig + (size_t)nxp * MF_DSTR);
+  float* lpart = (float*)(ldesc + 4 * dstr);                // [nw][64]
+
+  // 1. stage the split's digits: one (column, chunk) per thread; columns >= nc are zeros
+  for (int job = tid; job < 4 * nxs; job += blockDim.x) {
+    const int col = job / nxs, c = job - col * nxs;
+    uint32_t wd[DIG_CHUNK_WORDS];
+    if (col < nc) {
+      const uint4* src = a.xd + (int64_t)col * a.xd_stride + (int64_t)(xbase + c) * XSLOTS;
+#pragma unroll
+      for (int q = 0; q < XSLOTS; ++q) {
+        const uint4 v = src[q];
+        wd[4 * q] = v.x;
+        wd[4 * q + 1] = v.y;
+        wd[4 * q + 2] = v.z;
+        wd[4 * q + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < DIG_CHUNK_WORDS; ++i) wd[i] = 0;
+    }
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg)
+#pragma unroll
+      for (int lv = 0; lv < 3; ++lv)
+        ldig[c * MF_DSTR + gg * 12 + col * 3 + lv] = make_uint2(wd[gg * 3 + lv], wd[12 + gg * 3 + lv]);
+    const float inv = __uint_as_float(wd[DIG_WORDS]);
+    ldesc[col * dstr + c] = make_float2(inv, inv * (float)(int32_t)wd[DIG_WORDS + 1]);
+  }
+  if (EPI != EPI_PART && a.e.sq_in) rms_partials(a.e, nc, red);
+  __syncthreads();
+
+  // 2. blocks of T tiles x S K parts
+  const int S = kparts, T = nw / kparts;
+  const int t = wave / S, s = wave - t * S;
+  const int rows = a.w.rows;
+  const int blk_rows = 16 * T;
+  const int nblk = (rows + blk_rows - 1) / blk_rows;
+  const int nst = nxs / mf_step_chunks<QT>();  // steps of 16 (Q5_K) or 8 (Q6_K) chunks
+  const int st0 = s * nst / S, st1 = (s + 1) * nst / S;
+  const int cbase = kbeg / XCHUNK;
+  const int aoff = g * 12 + (n >> 2) * 3 + min(n & 3, 2);  // this lane's A entry within a chunk
+  const uint64_t amask = (n & 3) == 3 ? 0ull : ~0ull;       // level 3 is zero
+  // per-lane bit-move amounts: Q5_K fifth bits (rotations), Q6_K high pairs (shifts)
+  const uint32_t rot_lo = (uint32_t)(28 + 2 * g) & 31u, rot_hi = (uint32_t)(29 + 2 * g) & 31u;
+  const uint32_t shl_lo = (g & 1) ? 2u : 6u, shl_hi = (g & 1) ? 0u : 4u;
+
+  // quarter qq (chunks c0 + 4 qq .. + 3) of a step: quant words transposed across the lane groups,
+  // four (Q6_K: eight) MFMAs, then the (row n, column g) updates.  hv: the Q5_K superblock header of
+  // this quarter (fetched by the caller from the lane group that loaded it).
+  auto quarter = [&](const MfRaw<QT>& r, int c0, int qq, const uint4& hv, float& acc) {
+    const uint4 qv = r.q[qq];
+    // the swaps overwrite both operands: copy the loaded words here, where they are used (left to
+    // register allocation, the copies sat right after the next step's loads and waited for them)
+    uint32_t R[4];
+    asm volatile("v_mov_b32 %0, %1" : "=v"(R[0]) : "v"(qv.x));
+    asm volatile("v_mov_b32 %0, %1" : "=v"(R[1]) : "v"(qv.y));
+    asm volatile("v_mov_b32 %0, %1" : "=v"(R[2]) : "v"(qv.z));
+    asm volatile("v_mov_b32 %0, %1" : "=v"(R[3]) : "v"(qv.w));
+    lane_swap32(R[0], R[2]);
+    lane_swap32(R[1], R[3]);
+    lane_swap16(R[0], R[1]);
+    lane_swap16(R[2], R[3]);  // R[j] = quant word g of chunk c0 + 4 qq + j
+    const int cc = c0 + 4 * qq;
+    const float4 d01 = *(const float4*)&ldesc[g * dstr + cc];
+    const float4 d23 = *(const float4*)&ldesc[g * dstr + cc + 2];
+    const float inv[4] = {d01.x, d01.z, d23.x, d23.z};
+    uint64_t A[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint2 av = ldig[(cc + j) * MF_DSTR + aoff];
+      A[j] = ((uint64_t)av.x | ((uint64_t)av.y << 32)) & amask;
+    }
+    if constexpr (QT == Q5_K) {
+      const float xs[4] = {d01.y, d01.w, d23.y, d23.w};
+      // fifth bits of this quarter's chunks, from lane group qq of the same row
+      const int src = n + 16 * qq;
+      const uint32_t qh[4] = {lane_fetch(src, r.qh.x), lane_fetch(src, r.qh.y), lane_fetch(src, r.qh.z),
+                              lane_fetch(src, r.qh.w)};
+      qwg_i32x4 D[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t l5 = __builtin_rotateright32(qh[j], rot_lo), h5 = __builtin_rotateright32(qh[j], rot_hi);
+        const uint32_t lo = (R[j] & 0x0F0F0F0Fu) | (l5 & 0x10101010u);
+        const uint32_t hi = ((R[j] >> 4) & 0x0F0F0F0Fu) | (h5 & 0x10101010u);
+        D[j] = mfma_i8(A[j], (uint64_t)lo | ((uint64_t)hi << 32));
+      }
+      const uint64_t ps = (uint64_t)hv.x | ((uint64_t)hv.y << 32);
+      const uint64_t pm = (uint64_t)hv.z | ((uint64_t)hv.w << 32);
+      const float dd = half_bits_to_float(hv.y >> 16), dm = half_bits_to_float(hv.w >> 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int sb = 4 * (qq & 1) + j;  // sub-block of the superblock
+        const float dsc = dd * (float)((uint32_t)(ps >> (6 * sb)) & 63u);
+        const float dmm = dm * (float)((uint32_t)(pm >> (6 * sb)) & 63u);
+        acc = __builtin_fmaf(inv[j] * dsc, mf_value(D[j]), acc);
+        acc = __builtin_fmaf(-dmm, xs[j], acc);
+      }
+    } else {
+      // high-bit pairs of chunk 4 qq + j: words (x, y) of qhA (qq < 2) or qhB held by lane group
+      // (2 qq + j / 2) & 3; rows take x for word groups 0, 1 and y for 2, 3
+      const int src0 = n + 16 * ((2 * qq) & 3), src1 = n + 16 * ((2 * qq + 1) & 3);
+      const uint4 qp = qq < 2 ? r.qhA : r.qhB;
+      uint32_t hq[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int src = (j >> 1) ? src1 : src0;
+        const uint32_t hx = lane_fetch(src, (j & 1) ? qp.z : qp.x), hy = lane_fetch(src, (j & 1) ? qp.w : qp.y);
+        hq[j] = g < 2 ? hx : hy;
+      }
+      qwg_i32x4 DA[4], DB[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t h = hq[j];
+        const uint32_t lo = ((R[j] << 2) & 0x3C3C3C3Cu) | ((h << shl_lo) & 0xC0C0C0C0u);
+        const uint32_t hi = ((R[j] >> 2) & 0x3C3C3C3Cu) | ((h << shl_hi) & 0xC0C0C0C0u);
+        DA[j] = mfma_i8(A[j], (uint64_t)lo);
+        DB[j] = mfma_i8(A[j], (uint64_t)hi << 32);
+      }
+      const float dq = 0.25f * half_bits_to_float((r.dw >> (16 * (qq >> 1))) & 0xFFFFu);
+      // sub-block scales of this quarter's chunks, from lane group qq
+      const uint32_t scw[2] = {lane_fetch(n + 16 * qq, r.sc.x), lane_fetch(n + 16 * qq, r.sc.y)};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = scw[j >> 1] >> (16 * (j & 1));
+        const float dA = dq * (float)(int32_t)(int8_t)(uint8_t)(w & 0xFFu);
+        const float dB = dq * (float)(int32_t)(int8_t)(uint8_t)((w >> 8) & 0xFFu);
+        acc = __builtin_fmaf(inv[j] * dA, mf_value(DA[j]), acc);
+        acc = __builtin_fmaf(inv[j] * dB, mf_value(DB[j]), acc);
+      }
+    }
+  };
+  constexpr int SC = mf_step_chunks<QT>();
+  auto step = [&](const MfRaw<QT>& r, int st, float& acc) {
+    if constexpr (QT == Q5_K) {
+#pragma unroll
+      for (int sbk = 0; sbk < 2; ++sbk) {  // the step's two superblocks: header from lane group sbk
+        const int src = n + 16 * sbk;
+        const uint4 hv = make_uint4(lane_fetch(src, r.h.x), lane_fetch(src, r.h.y), lane_fetch(src, r.h.z),
+                                    lane_fetch(src, r.h.w));
+        quarter(r, SC * st, 2 * sbk, hv, acc);
+        quarter(r, SC * st, 2 * sbk + 1, hv, acc);
+      }
+    } else {
+      const uint4 none = make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) quarter(r, SC * st, qq, none, acc);
+    }
+  };
+
+  for (int b = blockIdx.x; b < nblk; b += gridDim.x) {
+    const int r0 = b * blk_rows + t * 16;
+    const int row = min(r0 + n, rows - 1);  // rows past the end read the last row; results dropped
+    const uint32_t ro = row_off(QT, a.w, row), srow = slot_row(a.w.ilv, a.w.nch, row);
+    auto load = [&](int st) { return mf_load<QT>(a.w, ro, srow, cbase + SC * min(st, nst - 1), g); };
+    float acc = 0.f;
+    // two buffers in rotation: the next step's loads are in flight while one is computed (loads past
+    // the part's end re-read its last step, in bounds and unused)
+    MfRaw<QT> b0 = load(st0), b1;
+    int st = st0;
+    for (; st + 2 <= st1; st += 2) {
+      b1 = load(min(st + 1, st1 - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      step(b0, st, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      b0 = load(min(st + 2, st1 - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      step(b1, st + 1, acc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (st < st1) step(b0, st, acc);
+
+    // 3. the tile's K parts in wave order, then the epilogue for (row r0 + n, column g)
+    if (S > 1) {
+      lpart[wave * 64 + lane] = acc;
+      __syncthreads();
+      if (s == 0) {
+        float v = 0.f;
+        for (int i = 0; i < S; ++i) v += lpart[(wave + i) * 64 + lane];
+        acc = v;
+      }
+    }
+    if (s == 0) {
+      const int orow = r0 + n;
+      const bool ok = orow < rows && g < nc;
+      float v = acc;
+      if (EPI == EPI_PART) {
+        if (ok) a.part[((int64_t)split * nc + g) * rows + orow] = v;
+      } else {
+        if (a.e.sq_in) v *= rms_scale(a.e, red, min(g, nc - 1));
+        const float vp = __shfl_xor(v, 1);  // row n ^ 1, same column
+        if (ok) run_epilogue(EPI, a.e, g, orow, v, vp);
+      }
+    }
+    if (S > 1) __syncthreads();  // lpart is reused by the next block
+  }
+}
+
 // Activation digits of nc columns of length k, four threads per 32-element chunk (thread m takes
 // elements 4m..4m+3 and 16+4m..16+4m+3 with two float4 loads).  With a gain vector the digits are
 // of g * x and sq receives each chunk's sum of x^2 (for the consumer's RMSNorm).
@@ -536,10 +851,56 @@ void set_gemv_geometry(int waves, int rows_per_wave, int depth, int passes) {
   g_passes = passes;
 }
 
+static int g_mfma = 1;  // several-column Q5_K / Q6_K GEMVs on the matrix cores
+void set_gemv_mfma(int on) { g_mfma = on ? 1 : 0; }
+
+constexpr int MF_WAVES = 16;  // waves per workgroup of the matrix-core form (four per SIMD)
+
+// Matrix-core plan: K splits as LDS requires (a power of two, so the splits' grids tile the 256 CUs),
+// then the K parts per tile S in {1, 2, 4, 8, 16} that minimise rounds x steps per wave, where a
+// round is one block per workgroup and a workgroup runs on each CU.
+static GemvPlan plan_mfma(int64_t rows, int64_t k, int nc) {
+  const int64_t unit = 16;  // chunks per step (two superblocks): splits hold whole steps
+  GemvPlan p{};
+  p.mfma = 1;
+  p.ncm = 4;
+  p.waves = MF_WAVES;
+  p.rows_per_wave = 16;
+  p.depth = 1;
+  p.passes = 0;
+  const int64_t nx = k / XCHUNK;
+  const size_t fixed = (size_t)MF_WAVES * 64 * 4 + MF_FIXED_LDS;  // K parts' partial sums, padding
+  int64_t max_x = (int64_t)((LDS_BUDGET - fixed) / MF_CHUNK_LDS) / unit * unit;
+  int ksplit = 1;
+  while (ksplit < 64 && ((nx + ksplit - 1) / ksplit + unit - 1) / unit * unit > max_x) ksplit *= 2;
+  const int64_t xs = ((nx + ksplit - 1) / ksplit + unit - 1) / unit * unit;
+  p.ks = (int)(xs * XCHUNK);
+  p.ksplit = (int)((k + p.ks - 1) / p.ks);
+  p.lds = (size_t)xs * MF_CHUNK_LDS + fixed;
+  p.part_bytes = p.ksplit > 1 ? (size_t)p.ksplit * nc * rows * sizeof(float) : 0;
+  const int64_t tiles = (rows + 15) / 16, nst = xs / unit;
+  const int64_t G = std::max(1, PERSISTENT_WGS / p.ksplit);
+  int64_t best = -1;
+  for (int S = 1; S <= MF_WAVES; S *= 2) {
+    if (g_passes > 0 && S != g_passes) continue;  // tuning override: K parts per tile
+    const int64_t T = MF_WAVES / S, nblk = (tiles + T - 1) / T, rounds = (nblk + G - 1) / G;
+    const int64_t cost = rounds * ((nst + S - 1) / S + 3);
+    if (best < 0 || cost < best) {
+      best = cost;
+      p.kparts = S;
+      p.grid_x = (int)std::min(nblk, G);
+    }
+  }
+  return p;
+}
+
 // formats whose 4-row two-pass kernel fits 128 registers without spilling
 static bool two_pass_ok(int qt) { return qt == Q4_0 || qt == Q4_K || qt == Q8_0; }
 
-GemvPlan plan_gemv(int qt, int64_t rows, int64_t k, int nc, int epi) {
+GemvPlan plan_gemv(int qt, int64_t rows, int64_t k, int nc, int epi, int mfma) {
+  if ((mfma < 0 ? g_mfma : mfma) && nc >= 2 && nc <= 4 && (qt == Q5_K || qt == Q6_K) &&
+      k % 512 == 0)  // steps are two superblocks
+    return plan_mfma(rows, k, nc);
   // the RoPE and SwiGLU epilogues combine rows (2i, 2i+1), which must sit in one wave
   const bool pairs = epi == EPI_QKV || epi == EPI_SWIGLU;
   GemvPlan p{};
@@ -628,6 +989,7 @@ GemvPlan plan_gemv(int qt, int64_t rows, int64_t k, int nc, int epi) {
 // compiled input-digitizing kernels: 32 rows per workgroup as 8 waves x 4 rows, 8 waves x 2 rows x 2
 // passes, or 16 waves x 2 rows; four-column K-split residual GEMVs (the verify pass's down GEMV)
 bool gemv_can_digitize_input(const GemvPlan& p, int epi) {
+  if (p.mfma) return false;
   if (p.ncm == 4) return epi == EPI_RESID && p.ksplit > 1 && p.passes == 0 && p.depth == 1 && p.waves == 8;
   if (!(p.ncm == 1 && p.ksplit == 1 && epi == EPI_RESID && p.depth == 1)) return false;
   if (p.waves == 16) return p.rows_per_wave == 2 && p.passes == 1;
@@ -731,6 +1093,20 @@ static hipError_t launch_fmt(const GemvArgs& a, const GemvPlan& p, int epi, dim3
   return launch_t<QT, 8, 2, 1, 0>(a, epi, p.ksplit, grid, block, lds, dd);
 }
 
+template <int QT>
+static hipError_t launch_mfma(const GemvArgs& a, int epi, const GemvPlan& p, dim3 grid, dim3 block, const Dispatch& d) {
+  const int S = p.kparts;
+  switch (p.ksplit > 1 ? EPI_PART : epi) {
+    case EPI_PART: go(d, k_gemv_mfma<QT, EPI_PART>, grid, block, p.lds, a, S); break;
+    case EPI_STORE: go(d, k_gemv_mfma<QT, EPI_STORE>, grid, block, p.lds, a, S); break;
+    case EPI_RESID: go(d, k_gemv_mfma<QT, EPI_RESID>, grid, block, p.lds, a, S); break;
+    case EPI_SWIGLU: go(d, k_gemv_mfma<QT, EPI_SWIGLU>, grid, block, p.lds, a, S); break;
+    case EPI_QKV: go(d, k_gemv_mfma<QT, EPI_QKV>, grid, block, p.lds, a, S); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_gemv(int qt, const MatView& w, int64_t k, const void* xd, int64_t xd_stride_bytes, int nc, int epi,
                        const EpiArgs& e, float* part, hipStream_t st, const GemvPlan& p, hipEvent_t ev_start,
                        hipEvent_t ev_stop) {
@@ -753,7 +1129,12 @@ hipError_t launch_gemv(int qt, const MatView& w, int64_t k, const void* xd, int6
   // the stop event goes on the last kernel: the GEMV itself, or the split reduction after it
   const Dispatch d1{st, ev_start, p.ksplit == 1 ? ev_stop : nullptr};
   hipError_t err;
-  switch (qt) {
+  if (p.mfma) {
+    if (qt != Q5_K && qt != Q6_K) return hipErrorInvalidValue;
+    if (e.xf || nc < 1 || nc > 4) return hipErrorInvalidValue;
+    grid.x = p.grid_x;
+    err = qt == Q5_K ? launch_mfma<Q5_K>(a, epi, p, grid, block, d1) : launch_mfma<Q6_K>(a, epi, p, grid, block, d1);
+  } else switch (qt) {
     case Q8_0: err = launch_fmt<Q8_0>(a, p, epi, grid, block, d1); break;
     case Q4_0: err = launch_fmt<Q4_0>(a, p, epi, grid, block, d1); break;
     case Q4_K: err = launch_fmt<Q4_K>(a, p, epi, grid, block, d1); break;

@@ -61,11 +61,16 @@ struct GemvPlan {
   int ksplit;
   size_t lds;  // dynamic LDS bytes
   size_t part_bytes;  // split workspace bytes (0 if ksplit == 1)
+  int mfma;    // several columns on the matrix cores (k_gemv_mfma): waves = T tiles x kparts
+  int kparts;  // waves that split one 16-row tile's chunks (MFMA form)
 };
 
-// epi: the epilogue the GEMV will run (pairs of rows must share a wave for RoPE and SwiGLU)
-GemvPlan plan_gemv(int qt, int64_t rows, int64_t k, int nc, int epi);
+// epi: the epilogue the GEMV will run (pairs of rows must share a wave for RoPE and SwiGLU);
+// mfma: 1 = the matrix-core form where one exists (2..4 columns of Q5_K / Q6_K), 0 = integer dot
+// products only, -1 = the process-wide choice (set_gemv_mfma, on by default)
+GemvPlan plan_gemv(int qt, int64_t rows, int64_t k, int nc, int epi, int mfma = -1);
 void set_gemv_geometry(int waves, int rows_per_wave, int depth, int passes);
+void set_gemv_mfma(int on);
 
 // Bytes of the activation digits of one column of length k (28 words per 32 elements).
 inline int64_t digit_bytes(int64_t k) { return k / XCHUNK * DIG_CHUNK_WORDS * 4; }

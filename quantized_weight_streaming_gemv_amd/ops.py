@@ -78,6 +78,11 @@ def set_gemv_geometry(waves_per_group: int = 0, rows_per_wave: int = 0, pipeline
     call("qwg_set_gemv_geometry", waves_per_group, rows_per_wave, pipeline_depth, row_passes)
 
 
+def set_gemv_mfma(on: bool) -> None:
+    """Several-column (2..4) Q5_K / Q6_K GEMVs on the matrix cores (True, the default) or on integer dot products."""
+    call("qwg_set_gemv_mfma", 1 if on else 0)
+
+
 def rmsnorm(x, g, eps: float, out=None, stream=None):
     torch = _torch()
     n = g.numel()

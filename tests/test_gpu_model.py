@@ -103,13 +103,19 @@ def test_calibrate_skip_matches_oracle(qwg):
     m.close()
 
 
-def test_verify_columns_equal_sequential_steps(qwg):
+@pytest.mark.parametrize("mfma", [True, False], ids=["mfma", "dot"])
+def test_verify_columns_equal_sequential_steps(qwg, mfma):
+    from quantized_weight_streaming_gemv_amd import ops
     wl = synth.tiny(synth.Q6_K, synth.Q5_K, wid=180, draft_k=3)
     m = qwg.make_model(wl)
     qwg.load(m, wl)
     om = oracle.OracleModel(wl)
     toks = [wl.first_token(), 5, 17, 999]
-    logits, am = m.verify(toks)
+    ops.set_gemv_mfma(mfma)
+    try:
+        logits, am = m.verify(toks)
+    finally:
+        ops.set_gemv_mfma(True)
     assert m.n_past == wl.n_prior
     for j, t in enumerate(toks):
         r = om.decode(t)
