@@ -67,6 +67,9 @@ def workloads():
         "llama70b-q6_k": synth.replace(synth.LLAMA70B_Q6_K_STREAM, n_resident=-1, skip_tau=0.0),
         "llama70b-q6_k-slep": synth.LLAMA70B_Q6_K_STREAM,
         "llama70b-q6_k-q5_k": synth.LLAMA70B_Q6_K_Q5_K_SPEC,
+        # self-speculative decoding in streaming mode: drafts from the 20 resident layers, one
+        # 4-column verify pass streams the other (non-skipped) layers per round
+        "llama70b-q6_k-slep-selfspec": synth.replace(synth.LLAMA70B_Q6_K_STREAM, draft_layers=20, draft_k=3),
     }
 
 

@@ -164,6 +164,53 @@ def test_spec_step_matches_oracle(qwg, identity_tail):
     m.close()
 
 
+@pytest.mark.parametrize("identity_tail", [False, True])
+def test_spec_step_streamed_verify(qwg, identity_tail):
+    """Self-speculative decoding in streaming mode: the draft runs the resident layers only and the
+    verify pass streams the others from pinned host memory once per round.  Tokens and acceptance
+    match the oracle and the all-resident model bitwise; the H2D bytes of a round are those of one
+    full pass (the drafts stream nothing)."""
+    wl = synth.tiny(synth.Q6_K, synth.Q5_K, n_layers=4, wid=195, draft_k=3)
+    draft = 2
+    ov = {}
+    if identity_tail:
+        for l in (2, 3):
+            for t in (synth.WO, synth.WDOWN):
+                ov[(l, t)] = _zero_scales(wl.weight(l, t), wl.qtype_of(t))
+    om = oracle.OracleModel(wl)
+    for (l, t), W in ov.items():
+        om._keep.append(W)
+        om.layers[l].w[om.TENSORS.index(t)] = W.ctypes.data
+    # bytes one full pass streams (layers 2 and 3)
+    m = qwg.make_model(wl, n_resident=draft)
+    qwg.load(m, wl, weights_override=ov)
+    m.decode_step(wl.first_token())
+    pass_bytes, _ = m.stream_stats()
+    m.close()
+    assert pass_bytes > 0
+    runs = []
+    for res in (draft, -1):
+        m = qwg.make_model(wl, n_resident=res)
+        qwg.load(m, wl, weights_override=ov)
+        t, rounds = wl.first_token(), []
+        for _ in range(3):
+            toks, acc = m.spec_step(t, draft, 3)
+            rounds.append((toks, acc, m.n_past))
+            t = toks[-1]
+        b, _ = m.stream_stats()
+        assert b == (3 * pass_bytes if res == draft else 0)
+        runs.append(rounds)
+        m.close()
+    assert runs[0] == runs[1]
+    t = wl.first_token()
+    for toks, acc, n_past in runs[0]:
+        r = om.spec_round(t, draft, 3)
+        assert toks == r["tokens"] and acc == r["n_accepted"] and n_past == om.n_past
+        if identity_tail:
+            assert acc == 3
+        t = toks[-1]
+
+
 def test_context_overflow_is_an_error(qwg):
     from quantized_weight_streaming_gemv_amd import QwgError
     wl = synth.tiny(synth.Q8_0, wid=200)
