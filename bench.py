@@ -201,6 +201,9 @@ def main() -> int:
     ap.add_argument("--cpu-layers", type=int, default=8, help="oracle layers in the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-read-ceiling", action="store_true", help="skip the plain streaming-read reference")
+    ap.add_argument("--hbm-budget-gb", type=float, default=0.0,
+                    help="place layers automatically for this device-memory budget (GB): the resident tier "
+                         "gets what fits, the rest streams from pinned host memory (0: the workload's placement)")
     ap.add_argument("--verify-form", choices=["mfma", "dot"], default="mfma",
                     help="2..4-column Q5_K/Q6_K GEMVs of the verify pass: matrix cores or integer dot products")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -232,6 +235,13 @@ def main() -> int:
     read_ceiling = None if args.no_read_ceiling else measure_read_ceiling(wl)
     log("workload %s: %d layers, %.2f GB of weights, KV %d positions" %
         (wl.name, wl.n_layers, wl.model_bytes() / 1e9, wl.n_prior))
+    if args.hbm_budget_gb > 0:
+        cols = wl.draft_k + 1 if wl.draft_k else 1
+        n_res, a_b, p_b = synthetic.plan_residency_of(wl, max_ctx=max_ctx, max_cols=cols,
+                                                      device_budget=int(args.hbm_budget_gb * 1e9))
+        wl = synth.replace(wl, n_resident=n_res)
+        log("automatic placement for %.1f GB of HBM: %d of %d layers resident (arena %.2f GB, pinned %.2f GB)"
+            % (args.hbm_budget_gb, n_res, wl.n_layers, a_b / 1e9, p_b / 1e9))
     m = synthetic.make_model(wl, max_ctx=max_ctx)
     log("arena %.2f GB" % (m.arena_bytes / 1e9))
     load_s = synthetic.load(m, wl, log=log)
@@ -336,7 +346,9 @@ def main() -> int:
         "config": {"workload": wl.name, "layers": wl.n_layers, "hidden": wl.hidden, "n_q": wl.n_q, "n_kv": wl.n_kv,
                    "head_dim": wl.head_dim, "ffn": wl.ffn, "vocab": wl.vocab, "kv_positions": wl.n_prior,
                    "weights": synth.QTYPE_NAMES[wl.qtype_attn] + "/" + synth.QTYPE_NAMES[wl.qtype_ffn],
-                   "batch": 1, "greedy": True},
+                   "batch": 1, "greedy": True,
+                   "resident_layers": wl.n_layers if wl.n_resident < 0 else wl.n_resident,
+                   "hbm_budget_gb": args.hbm_budget_gb or None},
         "roofline": {"bound": "hbm", "kernel": "gate_up dequant-GEMV", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": gemv_traffic(wl), "bytes_per_launch": g_bytes, "us_per_launch": round(g_avg * 1e3, 3),

@@ -179,6 +179,18 @@ int qwg_model_create(const qwg_model_desc* desc, qwg_model** out);
 /* Device bytes the caller must provide to qwg_model_bind (weights of resident layers, two
  * streaming slots if any layer streams, KV caches, activations and scratch). */
 size_t qwg_model_arena_bytes(const qwg_model* m);
+/* Automatic tier placement ([NT] "3-tier adaptive cache": tier sizes computed from the device's free
+ * memory and the host's MemAvailable; [HN] 3-tier cache detail; [UR] 3-tier section): the largest
+ * n_resident for which the arena of `desc` (with that n_resident; desc->n_resident is ignored) fits
+ * device_budget bytes, with the other layers streamed from pinned host images that must fit
+ * host_budget bytes.  device_budget 0 = the current device's free memory (hipMemGetInfo) less a
+ * reserve of max(1 GiB, 2% of the device); host_budget 0 = 90% of MemAvailable (/proc/meminfo).
+ * Layers 0 .. n_resident-1 are the resident ones, so self-speculative drafts run on them.  Outputs:
+ * *n_resident; if not NULL, *arena_bytes (the arena at that placement) and *pinned_bytes (the
+ * streamed images).  QWG_E_NOMEM if no placement fits (the file-backed third tier is not built).
+ * With both budgets given it makes no GPU call. */
+int qwg_plan_residency(const qwg_model_desc* desc, size_t device_budget, size_t host_budget, int* n_resident,
+                       size_t* arena_bytes, size_t* pinned_bytes);
 /* Bind caller-owned device memory (>= qwg_model_arena_bytes, 256-B aligned) and the streams:
  * `compute` runs every kernel, `copy` carries host-to-device layer copies (may equal compute).
  * Streamed layers get library-owned pinned host images here. */

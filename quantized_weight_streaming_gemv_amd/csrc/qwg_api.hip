@@ -750,6 +750,61 @@ int qwg_model_create(const qwg_model_desc* desc, qwg_model** out) {
 
 size_t qwg_model_arena_bytes(const qwg_model* m) { return m ? m->total : 0; }
 
+// MemAvailable of /proc/meminfo in bytes, or 0 if it cannot be read
+static size_t host_mem_available() {
+  FILE* f = std::fopen("/proc/meminfo", "r");
+  if (!f) return 0;
+  char line[256];
+  size_t kib = 0;
+  while (std::fgets(line, sizeof line, f)) {
+    unsigned long long v = 0;
+    if (std::sscanf(line, "MemAvailable: %llu kB", &v) == 1) {
+      kib = (size_t)v;
+      break;
+    }
+  }
+  std::fclose(f);
+  return kib * 1024;
+}
+
+int qwg_plan_residency(const qwg_model_desc* desc, size_t device_budget, size_t host_budget, int* n_resident,
+                       size_t* arena_bytes, size_t* pinned_bytes) {
+  if (!n_resident) return fail(QWG_E_INVAL, "n_resident is NULL");
+  if (int rc = check_desc(desc)) return rc;
+  return guarded([&]() -> int {
+    size_t dev = device_budget, host = host_budget;
+    if (dev == 0) {
+      size_t fr = 0, tot = 0;
+      QWG_HIP(hipMemGetInfo(&fr, &tot));
+      const size_t reserve = std::max<size_t>((size_t)1 << 30, tot / 50);  // runtime and other allocations
+      dev = fr > reserve ? fr - reserve : 0;
+    }
+    if (host == 0) host = host_mem_available() / 10 * 9;  // leave a tenth to the rest of the system
+    // the most layers whose arena fits the device budget (the arena grows with every resident layer)
+    qwg_model m;
+    m.d = *desc;
+    int best = -1;
+    size_t best_total = 0, image = 0;
+    for (int n = desc->n_layers; n >= 0; --n) {
+      m.d.n_resident = n;
+      plan_model(&m);
+      image = m.image_max;
+      if (m.total <= dev) {
+        best = n;
+        best_total = m.total;
+        break;
+      }
+    }
+    if (best < 0) return fail(QWG_E_NOMEM, "the model's non-layer arena does not fit the device budget");
+    const size_t pinned = (size_t)(desc->n_layers - best) * image;
+    if (pinned > host) return fail(QWG_E_NOMEM, "streamed layers do not fit the pinned host budget (no file-backed tier)");
+    *n_resident = best;
+    if (arena_bytes) *arena_bytes = best_total;
+    if (pinned_bytes) *pinned_bytes = pinned;
+    return QWG_OK;
+  });
+}
+
 int qwg_model_bind(qwg_model* m, void* d_arena, size_t bytes, void* compute, void* copy) {
   if (!m || !d_arena) return fail(QWG_E_INVAL, "NULL pointer");
   if (m->bound) return fail(QWG_E_STATE, "model already bound");

@@ -13,6 +13,20 @@ import numpy as np
 from ._lib import ModelDesc, call, lib
 
 
+def plan_residency(*, n_layers, hidden, n_q, n_kv, head_dim, ffn, vocab, max_ctx, rope_theta, rms_eps, qtype_attn,
+                   qtype_ffn, qtype_embed, qtype_head, max_cols=1, device_budget: int = 0, host_budget: int = 0):
+    """Automatic tier placement (qwg_plan_residency): (n_resident, arena_bytes, pinned_bytes) for the
+    largest number of HBM-resident layers whose arena fits device_budget bytes (0 = free device
+    memory less a reserve), the rest streamed from pinned host images within host_budget bytes
+    (0 = 90% of MemAvailable).  Raises QwgError(QWG_E_NOMEM) if nothing fits."""
+    desc = ModelDesc(n_layers, hidden, n_q, n_kv, head_dim, ffn, vocab, max_ctx, rope_theta, rms_eps, -1,
+                     qtype_attn, qtype_ffn, qtype_embed, qtype_head, max_cols)
+    n, a, h = ctypes.c_int32(0), ctypes.c_size_t(0), ctypes.c_size_t(0)
+    call("qwg_plan_residency", ctypes.byref(desc), int(device_budget), int(host_budget), ctypes.byref(n),
+         ctypes.byref(a), ctypes.byref(h))
+    return int(n.value), int(a.value), int(h.value)
+
+
 class Model:
     def __init__(self, *, n_layers, hidden, n_q, n_kv, head_dim, ffn, vocab, max_ctx, rope_theta, rms_eps,
                  qtype_attn, qtype_ffn, qtype_embed, qtype_head, n_resident=-1, max_cols=1, device="cuda:0"):

@@ -16,10 +16,22 @@ def make_model(wl, *, max_ctx: Optional[int] = None, max_cols: Optional[int] = N
     cols = max_cols if max_cols is not None else (wl.draft_k + 1 if wl.draft_k else 1)
     ctx = max_ctx if max_ctx is not None else wl.n_prior + 64
     res = wl.n_resident if n_resident is None else n_resident
+    if res == "auto":  # automatic tier placement from the device's free memory and MemAvailable
+        res = plan_residency_of(wl, max_ctx=ctx, max_cols=cols)[0]
     return Model(n_layers=wl.n_layers, hidden=wl.hidden, n_q=wl.n_q, n_kv=wl.n_kv, head_dim=wl.head_dim,
                  ffn=wl.ffn, vocab=wl.vocab, max_ctx=ctx, rope_theta=wl.rope_theta, rms_eps=wl.rms_eps,
                  qtype_attn=wl.qtype_attn, qtype_ffn=wl.qtype_ffn, qtype_embed=wl.qtype_embed,
                  qtype_head=wl.qtype_head, n_resident=res, max_cols=cols, device=device)
+
+
+def plan_residency_of(wl, *, max_ctx: int, max_cols: int = 1, device_budget: int = 0, host_budget: int = 0):
+    """(n_resident, arena_bytes, pinned_bytes) of workload `wl` under the given budgets (0 = measured)."""
+    from .model import plan_residency
+    return plan_residency(n_layers=wl.n_layers, hidden=wl.hidden, n_q=wl.n_q, n_kv=wl.n_kv, head_dim=wl.head_dim,
+                          ffn=wl.ffn, vocab=wl.vocab, max_ctx=max_ctx, rope_theta=wl.rope_theta, rms_eps=wl.rms_eps,
+                          qtype_attn=wl.qtype_attn, qtype_ffn=wl.qtype_ffn, qtype_embed=wl.qtype_embed,
+                          qtype_head=wl.qtype_head, max_cols=max_cols, device_budget=device_budget,
+                          host_budget=host_budget)
 
 
 def load(model: Model, wl, *, weights_override=None, log=None) -> float:

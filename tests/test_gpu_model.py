@@ -211,6 +211,38 @@ def test_spec_step_streamed_verify(qwg, identity_tail):
         t = toks[-1]
 
 
+def test_automatic_residency(qwg):
+    """n_resident = "auto": the placement from the device's free memory keeps a small model fully
+    resident; a placement under a device budget that holds two layers streams the others and decodes
+    the same tokens and logits, bitwise, as the resident model."""
+    wl = synth.tiny(synth.Q4_K, n_layers=5, wid=165)
+    m = qwg.make_model(wl, n_resident="auto")
+    assert m.desc.n_resident == wl.n_layers
+    qwg.load(m, wl)
+    t, ref = wl.first_token(), []
+    for _ in range(2):
+        t, lg = m.decode_step(t, want_logits=True)
+        ref.append((t, lg))
+    m.close()
+    ctx = wl.n_prior + 64
+    full = qwg.plan_residency_of(wl, max_ctx=ctx, device_budget=1 << 40, host_budget=1 << 40)
+    two = qwg.make_model(wl, n_resident=0)
+    a0 = two.arena_bytes
+    two.close()
+    image = (full[1] - a0) // (wl.n_layers - 2)  # all resident = 0 resident + n_layers images - 2 slots
+    n, arena, pinned = qwg.plan_residency_of(wl, max_ctx=ctx, device_budget=a0 + 2 * image, host_budget=1 << 40)
+    assert n == 2 and pinned == (wl.n_layers - 2) * image
+    m = qwg.make_model(wl, n_resident=n)
+    assert m.arena_bytes == arena
+    qwg.load(m, wl)
+    t = wl.first_token()
+    for rt, rl in ref:
+        t, lg = m.decode_step(t, want_logits=True)
+        assert t == rt and np.array_equal(lg, rl)
+    assert m.stream_stats()[0] > 0
+    m.close()
+
+
 def test_context_overflow_is_an_error(qwg):
     from quantized_weight_streaming_gemv_amd import QwgError
     wl = synth.tiny(synth.Q8_0, wid=200)
