@@ -64,6 +64,7 @@ def workloads():
     return {
         "llama70b-q4_k": synth.LLAMA70B_Q4_K,
         "llama8b-q8_0": synth.LLAMA8B_Q8_0,
+        "llama70b-q4_k_m": synth.LLAMA70B_Q4_K_M,
         "llama70b-q6_k": synth.replace(synth.LLAMA70B_Q6_K_STREAM, n_resident=-1, skip_tau=0.0),
         "llama70b-q6_k-slep": synth.LLAMA70B_Q6_K_STREAM,
         "llama70b-q6_k-q5_k": synth.LLAMA70B_Q6_K_Q5_K_SPEC,
@@ -86,11 +87,10 @@ def token_bytes(wl, n_pos: int) -> int:
     """Algorithmic bytes of one decode token: canonical weight bytes of every layer, the head and one
     embedding row, plus the K and V rows read by attention (n_pos positions)."""
     import synth
-    layer = wl.layer_bytes()
     head = synth.row_bytes(wl.qtype_head, wl.hidden) * wl.vocab
     emb = synth.row_bytes(wl.qtype_embed, wl.hidden)
     kv = 2 * n_pos * wl.n_kv * wl.head_dim * 2
-    return wl.n_layers * (layer + kv) + head + emb
+    return wl.layers_bytes() + wl.n_layers * kv + head + emb
 
 
 def round_bytes(wl, n_pos: int) -> int:
@@ -98,13 +98,13 @@ def round_bytes(wl, n_pos: int) -> int:
     layers (+ head, embedding row, their K/V reads) and one (k+1)-column verify over every layer
     (weights and the K/V rows read once for all columns)."""
     import synth
-    layer = wl.layer_bytes()
     head = synth.row_bytes(wl.qtype_head, wl.hidden) * wl.vocab
     emb = synth.row_bytes(wl.qtype_embed, wl.hidden)
     kv_row = 2 * wl.n_kv * wl.head_dim * 2
     k = wl.draft_k
-    draft = sum(wl.draft_layers * (layer + (n_pos + j) * kv_row) + head + emb for j in range(k))
-    verify = wl.n_layers * (layer + (n_pos + k) * kv_row) + head + (k + 1) * emb
+    draft_w = sum(wl.layer_bytes(l) for l in range(wl.draft_layers))
+    draft = sum(draft_w + wl.draft_layers * (n_pos + j) * kv_row + head + emb for j in range(k))
+    verify = wl.layers_bytes() + wl.n_layers * (n_pos + k) * kv_row + head + (k + 1) * emb
     return draft + verify
 
 
@@ -345,7 +345,9 @@ def main() -> int:
         "data": "synthetic (seeded random weights of the stated shapes and distributions)",
         "config": {"workload": wl.name, "layers": wl.n_layers, "hidden": wl.hidden, "n_q": wl.n_q, "n_kv": wl.n_kv,
                    "head_dim": wl.head_dim, "ffn": wl.ffn, "vocab": wl.vocab, "kv_positions": wl.n_prior,
-                   "weights": synth.QTYPE_NAMES[wl.qtype_attn] + "/" + synth.QTYPE_NAMES[wl.qtype_ffn],
+                   "weights": synth.QTYPE_NAMES[wl.qtype_attn] + "/" + synth.QTYPE_NAMES[wl.qtype_ffn]
+                   + ("" if not wl.wide_down_every else " (W_down of every %d. layer %s, head %s)" % (
+                       wl.wide_down_every, synth.QTYPE_NAMES[wl.wide_qtype], synth.QTYPE_NAMES[wl.qtype_head])),
                    "batch": 1, "greedy": True,
                    "resident_layers": wl.n_layers if wl.n_resident < 0 else wl.n_resident,
                    "hbm_budget_gb": args.hbm_budget_gb or None},

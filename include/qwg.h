@@ -172,6 +172,11 @@ typedef struct {
   int32_t qtype_embed;
   int32_t qtype_head;
   int32_t max_cols;   /* widest multi-column pass (1 + draft k), 1..8 */
+  const int32_t* layer_qtypes; /* NULL, or a host array [n_layers][4] of per-layer types of (QKV, WO,
+                         GATE|UP, DOWN) overriding qtype_attn / qtype_ffn: mixed-type files such as
+                         Q4_K_M ([HN] quantization-format table: a mixed 256-weight type).  Read by
+                         qwg_model_create / qwg_plan_residency only (the model keeps a copy).  WQ, WK,
+                         WV of a layer share one type (one fused GEMV). */
 } qwg_model_desc;
 
 /* Validate the description and create an unbound model (no device memory yet). */

@@ -207,7 +207,7 @@ def layer_forward(wl, layer: int, weights: dict, h: np.ndarray, kc: np.ndarray, 
         w = _c(weights[t], np.uint8)
         keep.append(w)
         lay.w[i] = w.ctypes.data
-        lay.qt[i] = wl.qtype_of(t)
+        lay.qt[i] = wl.qtype_of(t, layer)
     ga, gf = wl.gain(layer, synth.G_ATTN), wl.gain(layer, synth.G_FFN)
     keep += [ga, gf]
     lay.g_attn, lay.g_ffn = ga.ctypes.data, gf.ctypes.data
@@ -260,7 +260,7 @@ class OracleModel:
                     w = wl.weight(l, t)
                     self._keep.append(w)
                     lay.w[i] = w.ctypes.data
-                    lay.qt[i] = wl.qtype_of(t)
+                    lay.qt[i] = wl.qtype_of(t, l)
             ga, gf = wl.gain(l, synth.G_ATTN), wl.gain(l, synth.G_FFN)
             self._keep += [ga, gf]
             lay.g_attn, lay.g_ffn = ga.ctypes.data, gf.ctypes.data

@@ -30,7 +30,7 @@ class ModelDesc(ctypes.Structure):
                 ("vocab", ctypes.c_int32), ("max_ctx", ctypes.c_int32), ("rope_theta", ctypes.c_float),
                 ("rms_eps", ctypes.c_float), ("n_resident", ctypes.c_int32), ("qtype_attn", ctypes.c_int32),
                 ("qtype_ffn", ctypes.c_int32), ("qtype_embed", ctypes.c_int32), ("qtype_head", ctypes.c_int32),
-                ("max_cols", ctypes.c_int32)]
+                ("max_cols", ctypes.c_int32), ("layer_qtypes", ctypes.c_void_p)]
 
 
 vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t

@@ -113,6 +113,7 @@ struct LayerPlan {
 
 struct qwg_model {
   qwg_model_desc d{};
+  std::vector<int32_t> lq;  // per-layer types [n_layers][4] of (QKV, WO, GATE|UP, DOWN); empty = class types
   std::vector<LayerPlan> L;
   MatPlan embed{}, head{};
   size_t g_final = 0, rope = 0, h = 0, hin = 0, qb = 0, ob = 0, act = 0, logits = 0, amax = 0, keys = 0, cosv = 0;
@@ -146,6 +147,22 @@ struct qwg_model {
   float* f(size_t off) const { return (float*)(arena + off); }
 };
 
+enum LayerMat : int { LM_QKV = 0, LM_O = 1, LM_GU = 2, LM_DOWN = 3 };
+
+// type of layer l's matrix group `which` (LayerMat) under description d and per-layer table lq
+static int layer_qt(const qwg_model_desc& d, const std::vector<int32_t>& lq, int l, int which) {
+  if (!lq.empty()) return lq[(size_t)l * 4 + which];
+  return which <= LM_O ? d.qtype_attn : d.qtype_ffn;
+}
+
+// copy the description (and its per-layer type table) into a model
+static void init_desc(qwg_model* m, const qwg_model_desc* desc) {
+  m->d = *desc;
+  m->d.layer_qtypes = nullptr;
+  m->lq.clear();
+  if (desc->layer_qtypes) m->lq.assign(desc->layer_qtypes, desc->layer_qtypes + (size_t)desc->n_layers * 4);
+}
+
 static MatPlan mat_plan(int qt, int64_t rows, int64_t k, size_t& cursor) {
   MatPlan p;
   p.L = make_layout(qt, rows, k);
@@ -161,19 +178,19 @@ static int plan_model(qwg_model* m) {
   const int n_res = d.n_resident < 0 ? d.n_layers : d.n_resident;
   size_t cur = 0;
   m->L.assign(d.n_layers, LayerPlan{});
-  // image layout shared by every layer
-  size_t ic = 0;
-  LayerPlan proto{};
-  proto.qkv = mat_plan(d.qtype_attn, (int64_t)(d.n_q + 2 * d.n_kv) * d.head_dim, H, ic);
-  proto.o = mat_plan(d.qtype_attn, H, (int64_t)d.n_q * d.head_dim, ic);
-  proto.gu = mat_plan(d.qtype_ffn, 2 * (int64_t)F, H, ic);
-  proto.down = mat_plan(d.qtype_ffn, H, F, ic);
-  proto.image = ic;
-  m->image_max = ic;
+  // each layer's image layout (the same for every layer unless the types mix); streaming slots hold
+  // the largest
+  m->image_max = 0;
   m->n_streamed = 0;
   for (int l = 0; l < d.n_layers; ++l) {
     LayerPlan& P = m->L[l];
-    P = proto;
+    size_t ic = 0;
+    P.qkv = mat_plan(layer_qt(d, m->lq, l, LM_QKV), (int64_t)(d.n_q + 2 * d.n_kv) * d.head_dim, H, ic);
+    P.o = mat_plan(layer_qt(d, m->lq, l, LM_O), H, (int64_t)d.n_q * d.head_dim, ic);
+    P.gu = mat_plan(layer_qt(d, m->lq, l, LM_GU), 2 * (int64_t)F, H, ic);
+    P.down = mat_plan(layer_qt(d, m->lq, l, LM_DOWN), H, F, ic);
+    P.image = ic;
+    m->image_max = std::max(m->image_max, ic);
     P.resident = l < n_res;
     P.host = nullptr;
     if (P.resident) {
@@ -222,10 +239,12 @@ static int plan_model(qwg_model* m) {
                                   {2 * (int64_t)F, H},
                                   {H, F},
                                   {V, H}};
-    const int qts[5] = {d.qtype_attn, d.qtype_attn, d.qtype_ffn, d.qtype_ffn, d.qtype_head};
-    for (int i = 0; i < 5; ++i) {
+    for (int i = 0; i < 5; ++i)
+      for (int l = 0; l < (i < 4 ? d.n_layers : 1); ++l) {
+      const int qt = i < 4 ? layer_qt(d, m->lq, l, i) : d.qtype_head;
+      if (i < 4 && l > 0 && qt == layer_qt(d, m->lq, l - 1, i)) continue;
       for (int mf : {0, 1}) {  // either form of a several-column GEMV may run (qwg_set_gemv_mfma)
-        const GemvPlan gp = plan_gemv(qts[i], shapes[i][0], shapes[i][1], nc, EPI_STORE, mf);
+        const GemvPlan gp = plan_gemv(qt, shapes[i][0], shapes[i][1], nc, EPI_STORE, mf);
         pb = std::max(pb, gp.part_bytes);
       }
     }
@@ -273,6 +292,18 @@ static int check_desc(const qwg_model_desc* d) {
   for (const auto& sh : shapes)
     if (make_layout((int)sh[0], sh[1], sh[2]).total >= ((int64_t)1 << 32))
       return fail(QWG_E_SHAPE, "a packed matrix of 4 GiB or more is not supported");
+  if (d->layer_qtypes) {
+    const int64_t ks[4] = {H, QR, H, F};
+    const int64_t rs[4] = {(int64_t)(d->n_q + 2 * d->n_kv) * d->head_dim, H, 2 * F, H};
+    for (int l = 0; l < d->n_layers; ++l)
+      for (int i = 0; i < 4; ++i) {
+        const int q = d->layer_qtypes[(size_t)l * 4 + i];
+        if (!qtype_known(q)) return fail(QWG_E_UNSUPPORTED, "unknown layer qtype " + std::to_string(q));
+        if (canon_row_bytes(q, ks[i]) == 0) return fail(QWG_E_SHAPE, "layer matrix K is not a multiple of its block");
+        if (make_layout(q, rs[i], ks[i]).total >= ((int64_t)1 << 32))
+          return fail(QWG_E_SHAPE, "a packed matrix of 4 GiB or more is not supported");
+      }
+  }
   return QWG_OK;
 }
 
@@ -406,24 +437,25 @@ static int layer_kernels(qwg_model* m, int l, const uint8_t* base, int nc, int p
   InDigits in_qkv;
   in_qkv.buf = 0;
   in_qkv.rms = true;
-  if ((rc = gemv(m, QWG_T_WQ, d.qtype_attn, view_at(base, P.qkv), P.qkv, in_qkv, nc, EPI_QKV, e, OutDigits{})))
+  const int qt_qkv = P.qkv.L.qtype, qt_o = P.o.L.qtype, qt_gu = P.gu.L.qtype, qt_down = P.down.L.qtype;
+  if ((rc = gemv(m, QWG_T_WQ, qt_qkv, view_at(base, P.qkv), P.qkv, in_qkv, nc, EPI_QKV, e, OutDigits{})))
     return rc;
   const AttnPlan ap = plan_attn(pos + 1, d.n_q, d.n_kv, nc);
   if (ap.work_bytes > m->attn_bytes) return fail(QWG_E_NOMEM, "attention workspace too small");
   QWG_HIP(launch_attn(m->f(m->qb), QR, e.kc, e.vc, KR, pos + 1, d.n_q, d.n_kv, nc, m->f(m->ob), QR,
                       m->arena + m->attn, ap, m->cs, (uint32_t*)(m->arena + m->xd[1]), m->xd_col / 4,
-                      digit_kind(d.qtype_attn)));
+                      digit_kind(qt_o)));
   EpiArgs r{};
   r.y = m->f(m->h);
   r.y_stride = H;
   OutDigits to_ffn;
   to_ffn.buf = 0;
   to_ffn.gain = m->f(P.g_ffn);
-  to_ffn.qt = d.qtype_ffn;
+  to_ffn.qt = qt_gu;
   to_ffn.sq = true;
   InDigits in_o;
   in_o.buf = 1;
-  if ((rc = gemv(m, QWG_T_WO, d.qtype_attn, view_at(base, P.o), P.o, in_o, nc, EPI_RESID, r, to_ffn))) return rc;
+  if ((rc = gemv(m, QWG_T_WO, qt_o, view_at(base, P.o), P.o, in_o, nc, EPI_RESID, r, to_ffn))) return rc;
   EpiArgs s{};
   s.y = m->f(m->act);
   s.y_stride = F;
@@ -434,13 +466,13 @@ static int layer_kernels(qwg_model* m, int l, const uint8_t* base, int nc, int p
   // geometry covers whole 32-output chunks, else the down GEMV digitizes the fp32 vector itself
   const int64_t gu_rows = P.gu.L.rows;
   const bool act_digits =
-      gemv_can_digitize_output(plan_gemv(d.qtype_ffn, gu_rows, H, nc, EPI_SWIGLU), EPI_SWIGLU, gu_rows);
+      gemv_can_digitize_output(plan_gemv(qt_gu, gu_rows, H, nc, EPI_SWIGLU), EPI_SWIGLU, gu_rows);
   OutDigits to_down;
   if (act_digits) {
     to_down.buf = 1;
-    to_down.qt = d.qtype_ffn;
+    to_down.qt = qt_down;
   }
-  if ((rc = gemv(m, QWG_T_WGATE, d.qtype_ffn, view_at(base, P.gu), P.gu, in_ffn, nc, EPI_SWIGLU, s, to_down)))
+  if ((rc = gemv(m, QWG_T_WGATE, qt_gu, view_at(base, P.gu), P.gu, in_ffn, nc, EPI_SWIGLU, s, to_down)))
     return rc;
   InDigits in_act;
   in_act.buf = 1;
@@ -448,7 +480,7 @@ static int layer_kernels(qwg_model* m, int l, const uint8_t* base, int nc, int p
     in_act.xf = m->f(m->act);
     in_act.xf_stride = F;
   }
-  if ((rc = gemv(m, QWG_T_WDOWN, d.qtype_ffn, view_at(base, P.down), P.down, in_act, nc, EPI_RESID, r, next)))
+  if ((rc = gemv(m, QWG_T_WDOWN, qt_down, view_at(base, P.down), P.down, in_act, nc, EPI_RESID, r, next)))
     return rc;
   return QWG_OK;
 }
@@ -489,7 +521,7 @@ static int run_pass(qwg_model* m, const int32_t* toks, int nc, int pos, int n_ru
     od.sq = true;
     if (ri < (int)runs.size()) {
       od.gain = m->f(m->L[runs[ri]].g_attn);
-      od.qt = d.qtype_attn;
+      od.qt = m->L[runs[ri]].qkv.L.qtype;
     } else {
       od.gain = m->f(m->g_final);
       od.qt = d.qtype_head;
@@ -740,7 +772,7 @@ int qwg_model_create(const qwg_model_desc* desc, qwg_model** out) {
   if (int rc = check_desc(desc)) return rc;
   return guarded([&]() -> int {
     qwg_model* m = new qwg_model();
-    m->d = *desc;
+    init_desc(m, desc);
     m->skip.assign(desc->n_layers, 0);
     plan_model(m);
     *out = m;
@@ -782,7 +814,7 @@ int qwg_plan_residency(const qwg_model_desc* desc, size_t device_budget, size_t 
     if (host == 0) host = host_mem_available() / 10 * 9;  // leave a tenth to the rest of the system
     // the most layers whose arena fits the device budget (the arena grows with every resident layer)
     qwg_model m;
-    m.d = *desc;
+    init_desc(&m, desc);
     int best = -1;
     size_t best_total = 0, image = 0;
     for (int n = desc->n_layers; n >= 0; --n) {
@@ -861,22 +893,23 @@ int qwg_model_set_tensor(qwg_model* m, int layer, int tensor_id, int qtype, cons
   const qwg_model_desc& d = m->d;
   const MatPlan* mp = nullptr;
   int64_t rows = 0, k = 0, row0 = 0, step = 1;
-  int want_qt;
+  int want_qt = -1;
   bool global = tensor_id == QWG_T_EMBED || tensor_id == QWG_T_HEAD;
   if (global ? layer != -1 : (layer < 0 || layer >= d.n_layers)) return fail(QWG_E_INVAL, "bad layer index");
   LayerPlan* P = global ? nullptr : &m->L[layer];
   switch (tensor_id) {
     case QWG_T_EMBED: mp = &m->embed; rows = d.vocab; k = d.hidden; want_qt = d.qtype_embed; break;
     case QWG_T_HEAD: mp = &m->head; rows = d.vocab; k = d.hidden; want_qt = d.qtype_head; break;
-    case QWG_T_WQ: mp = &P->qkv; rows = m->QR(); k = d.hidden; want_qt = d.qtype_attn; break;
-    case QWG_T_WK: mp = &P->qkv; rows = m->KR(); k = d.hidden; row0 = m->QR(); want_qt = d.qtype_attn; break;
-    case QWG_T_WV: mp = &P->qkv; rows = m->KR(); k = d.hidden; row0 = m->QR() + m->KR(); want_qt = d.qtype_attn; break;
-    case QWG_T_WO: mp = &P->o; rows = d.hidden; k = m->QR(); want_qt = d.qtype_attn; break;
-    case QWG_T_WGATE: mp = &P->gu; rows = d.ffn; k = d.hidden; step = 2; want_qt = d.qtype_ffn; break;
-    case QWG_T_WUP: mp = &P->gu; rows = d.ffn; k = d.hidden; row0 = 1; step = 2; want_qt = d.qtype_ffn; break;
-    case QWG_T_WDOWN: mp = &P->down; rows = d.hidden; k = d.ffn; want_qt = d.qtype_ffn; break;
+    case QWG_T_WQ: mp = &P->qkv; rows = m->QR(); k = d.hidden; break;
+    case QWG_T_WK: mp = &P->qkv; rows = m->KR(); k = d.hidden; row0 = m->QR(); break;
+    case QWG_T_WV: mp = &P->qkv; rows = m->KR(); k = d.hidden; row0 = m->QR() + m->KR(); break;
+    case QWG_T_WO: mp = &P->o; rows = d.hidden; k = m->QR(); break;
+    case QWG_T_WGATE: mp = &P->gu; rows = d.ffn; k = d.hidden; step = 2; break;
+    case QWG_T_WUP: mp = &P->gu; rows = d.ffn; k = d.hidden; row0 = 1; step = 2; break;
+    case QWG_T_WDOWN: mp = &P->down; rows = d.hidden; k = d.ffn; break;
     default: return fail(QWG_E_INVAL, "unknown tensor id");
   }
+  if (!global) want_qt = mp->L.qtype;  // the layer's type for this matrix
   if (qtype != want_qt) return fail(QWG_E_UNSUPPORTED, "qtype differs from the model description");
   const int64_t rb = canon_row_bytes(qtype, k);
   if ((int64_t)nbytes != rows * rb) return fail(QWG_E_SHAPE, "nbytes != rows * row_bytes");

@@ -13,14 +13,26 @@ import numpy as np
 from ._lib import ModelDesc, call, lib
 
 
+def _layer_types(layer_qtypes, n_layers):
+    """A C-contiguous int32 [n_layers][4] copy of per-layer (QKV, WO, GATE|UP, DOWN) types, or None."""
+    if layer_qtypes is None:
+        return None
+    t = np.ascontiguousarray(layer_qtypes, dtype=np.int32)
+    if t.shape != (n_layers, 4):
+        raise ValueError("layer_qtypes must be [n_layers][4]")
+    return t
+
+
 def plan_residency(*, n_layers, hidden, n_q, n_kv, head_dim, ffn, vocab, max_ctx, rope_theta, rms_eps, qtype_attn,
-                   qtype_ffn, qtype_embed, qtype_head, max_cols=1, device_budget: int = 0, host_budget: int = 0):
+                   qtype_ffn, qtype_embed, qtype_head, max_cols=1, layer_qtypes=None, device_budget: int = 0,
+                   host_budget: int = 0):
     """Automatic tier placement (qwg_plan_residency): (n_resident, arena_bytes, pinned_bytes) for the
     largest number of HBM-resident layers whose arena fits device_budget bytes (0 = free device
     memory less a reserve), the rest streamed from pinned host images within host_budget bytes
     (0 = 90% of MemAvailable).  Raises QwgError(QWG_E_NOMEM) if nothing fits."""
+    lt = _layer_types(layer_qtypes, n_layers)
     desc = ModelDesc(n_layers, hidden, n_q, n_kv, head_dim, ffn, vocab, max_ctx, rope_theta, rms_eps, -1,
-                     qtype_attn, qtype_ffn, qtype_embed, qtype_head, max_cols)
+                     qtype_attn, qtype_ffn, qtype_embed, qtype_head, max_cols, None if lt is None else lt.ctypes.data)
     n, a, h = ctypes.c_int32(0), ctypes.c_size_t(0), ctypes.c_size_t(0)
     call("qwg_plan_residency", ctypes.byref(desc), int(device_budget), int(host_budget), ctypes.byref(n),
          ctypes.byref(a), ctypes.byref(h))
@@ -29,11 +41,14 @@ def plan_residency(*, n_layers, hidden, n_q, n_kv, head_dim, ffn, vocab, max_ctx
 
 class Model:
     def __init__(self, *, n_layers, hidden, n_q, n_kv, head_dim, ffn, vocab, max_ctx, rope_theta, rms_eps,
-                 qtype_attn, qtype_ffn, qtype_embed, qtype_head, n_resident=-1, max_cols=1, device="cuda:0"):
+                 qtype_attn, qtype_ffn, qtype_embed, qtype_head, n_resident=-1, max_cols=1, layer_qtypes=None,
+                 device="cuda:0"):
         import torch
         self.torch = torch
+        lt = _layer_types(layer_qtypes, n_layers)  # read by qwg_model_create only (the model copies it)
         self.desc = ModelDesc(n_layers, hidden, n_q, n_kv, head_dim, ffn, vocab, max_ctx, rope_theta, rms_eps,
-                              n_resident, qtype_attn, qtype_ffn, qtype_embed, qtype_head, max_cols)
+                              n_resident, qtype_attn, qtype_ffn, qtype_embed, qtype_head, max_cols,
+                              None if lt is None else lt.ctypes.data)
         self.handle = ctypes.c_void_p(None)
         call("qwg_model_create", ctypes.byref(self.desc), ctypes.byref(self.handle))
         self.arena_bytes = int(lib().qwg_model_arena_bytes(self.handle))

@@ -21,7 +21,8 @@ def make_model(wl, *, max_ctx: Optional[int] = None, max_cols: Optional[int] = N
     return Model(n_layers=wl.n_layers, hidden=wl.hidden, n_q=wl.n_q, n_kv=wl.n_kv, head_dim=wl.head_dim,
                  ffn=wl.ffn, vocab=wl.vocab, max_ctx=ctx, rope_theta=wl.rope_theta, rms_eps=wl.rms_eps,
                  qtype_attn=wl.qtype_attn, qtype_ffn=wl.qtype_ffn, qtype_embed=wl.qtype_embed,
-                 qtype_head=wl.qtype_head, n_resident=res, max_cols=cols, device=device)
+                 qtype_head=wl.qtype_head, n_resident=res, max_cols=cols, layer_qtypes=wl.layer_qtypes(),
+                 device=device)
 
 
 def plan_residency_of(wl, *, max_ctx: int, max_cols: int = 1, device_budget: int = 0, host_budget: int = 0):
@@ -30,7 +31,8 @@ def plan_residency_of(wl, *, max_ctx: int, max_cols: int = 1, device_budget: int
     return plan_residency(n_layers=wl.n_layers, hidden=wl.hidden, n_q=wl.n_q, n_kv=wl.n_kv, head_dim=wl.head_dim,
                           ffn=wl.ffn, vocab=wl.vocab, max_ctx=max_ctx, rope_theta=wl.rope_theta, rms_eps=wl.rms_eps,
                           qtype_attn=wl.qtype_attn, qtype_ffn=wl.qtype_ffn, qtype_embed=wl.qtype_embed,
-                          qtype_head=wl.qtype_head, max_cols=max_cols, device_budget=device_budget,
+                          qtype_head=wl.qtype_head, max_cols=max_cols, layer_qtypes=wl.layer_qtypes(),
+                          device_budget=device_budget,
                           host_budget=host_budget)
 
 
@@ -48,7 +50,7 @@ def load(model: Model, wl, *, weights_override=None, log=None) -> float:
     model.set_norm(-1, _lib.NORM_FINAL, wl.gain(-1, synth.G_FINAL))
     for l in range(wl.n_layers):
         for t in (synth.WQ, synth.WK, synth.WV, synth.WO, synth.WGATE, synth.WUP, synth.WDOWN):
-            model.set_tensor(l, t, wl.qtype_of(t), w(l, t))
+            model.set_tensor(l, t, wl.qtype_of(t, l), w(l, t))
         model.set_norm(l, _lib.NORM_ATTN, wl.gain(l, synth.G_ATTN))
         model.set_norm(l, _lib.NORM_FFN, wl.gain(l, synth.G_FFN))
         model.set_kv(l, wl.kv_prior(l, synth.KCACHE), wl.kv_prior(l, synth.VCACHE))

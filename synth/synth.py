@@ -208,14 +208,20 @@ class Workload:
     draft_k: int = 0
     n_tokens: int = 32            # greedy tokens generated by the full run
     seed: int = 0
+    # per-layer type mix (a stand-in for Q4_K_M, a mix of K-quant types): W_down of layers
+    # l % wide_down_every == 0 in wide_qtype (0 = no mix)
+    wide_qtype: int = 0
+    wide_down_every: int = 0
 
     @property
     def resident_layers(self) -> int:
         return self.n_layers if self.n_resident < 0 else self.n_resident
 
-    def qtype_of(self, tensor: int) -> int:
+    def qtype_of(self, tensor: int, layer: int = -1) -> int:
         if tensor in (WQ, WK, WV, WO):
             return self.qtype_attn
+        if tensor == WDOWN and layer >= 0 and self.wide_down_every > 0 and layer % self.wide_down_every == 0:
+            return self.wide_qtype
         if tensor in (WGATE, WUP, WDOWN):
             return self.qtype_ffn
         if tensor == EMBED:
@@ -237,8 +243,15 @@ class Workload:
         e = self.near_identity_every
         return e > 0 and layer % e == e - 1
 
+    def layer_qtypes(self):
+        """[n_layers][4] types of (QKV, WO, GATE|UP, DOWN) if layers differ, else None."""
+        if self.wide_down_every <= 0:
+            return None
+        return np.array([[self.qtype_of(WQ, l), self.qtype_of(WO, l), self.qtype_of(WGATE, l), self.qtype_of(WDOWN, l)]
+                         for l in range(self.n_layers)], dtype=np.int32)
+
     def dist_of(self, layer: int, tensor: int) -> QDist:
-        d = DEFAULT_DIST[self.qtype_of(tensor)]
+        d = DEFAULT_DIST[self.qtype_of(tensor, layer)]
         if tensor in (WO, WDOWN) and layer >= 0 and self.is_near_identity(layer):
             d = replace(d, d_mult=self.near_identity_mult)
         return d
@@ -263,12 +276,16 @@ class Workload:
         return uniform_int(self.tkey(-1, TOKEN), 0, 0, self.vocab - 1)
 
     def layer_bytes(self, layer: int = 0) -> int:
-        return sum(row_bytes(self.qtype_of(t), self.shape_of(t)[1]) * self.shape_of(t)[0]
+        return sum(row_bytes(self.qtype_of(t, layer), self.shape_of(t)[1]) * self.shape_of(t)[0]
                    for t in (WQ, WK, WV, WO, WGATE, WUP, WDOWN))
+
+    def layers_bytes(self) -> int:
+        """Canonical bytes of every layer's weights."""
+        return sum(self.layer_bytes(l) for l in range(self.n_layers))
 
     def model_bytes(self) -> int:
         g = sum(row_bytes(self.qtype_of(t), self.shape_of(t)[1]) * self.shape_of(t)[0] for t in (EMBED, HEAD))
-        return g + self.n_layers * self.layer_bytes()
+        return g + self.layers_bytes()
 
 
 # Workloads measured by this project.  Ids are part of the random streams.
@@ -280,6 +297,11 @@ LLAMA70B_Q4_K = Workload("llama70b-q4_k-resident", 2, 80, 8192, 64, 8, 128, 2867
                          Q4_K, Q4_K, Q4_K, Q4_K)
 LLAMA70B_Q6_K_STREAM = Workload("llama70b-q6_k-slep20-skip0.98", 3, 80, 8192, 64, 8, 128, 28672, 128256, 2048,
                                 Q6_K, Q6_K, Q6_K, Q6_K, near_identity_every=4, n_resident=20, skip_tau=0.98)
+# Q4_K_M stand-in (the pages list Q4_K_M as a mixed 256-weight K-quant type at about 4.5 bits per
+# weight): Q4_K matrices with W_down of every other layer and the output head in Q6_K (4.78 bits per
+# layer weight).
+LLAMA70B_Q4_K_M = Workload("llama70b-q4_k_m-resident", 5, 80, 8192, 64, 8, 128, 28672, 128256, 2048,
+                           Q4_K, Q4_K, Q4_K, Q6_K, wide_qtype=Q6_K, wide_down_every=2)
 LLAMA70B_Q6_K_Q5_K_SPEC = Workload("llama70b-q6_k-attn-q5_k-ffn-selfspec-k3", 4, 80, 8192, 64, 8, 128, 28672,
                                    128256, 4096, Q6_K, Q5_K, Q6_K, Q6_K, draft_layers=20, draft_k=3)
 

@@ -59,6 +59,42 @@ def test_decode_matches_oracle(qwg, mix):
     m.close()
 
 
+def tiny_q4_k_m(**kw):
+    """A small model with the Q4_K_M stand-in's type mix: Q4_K, with W_down of every other layer and
+    the head in Q6_K."""
+    base = dict(wid=215, qtype_head=synth.Q6_K, wide_qtype=synth.Q6_K, wide_down_every=2)
+    base.update(kw)
+    return synth.tiny(synth.Q4_K, **base)
+
+
+@pytest.mark.parametrize("n_resident", [-1, 1], ids=["resident", "streamed"])
+def test_mixed_layer_types_match_oracle(qwg, n_resident):
+    """Per-layer types: the down GEMV's input digits take the kind of that layer's W_down, the head's
+    input the head's kind; resident and streamed (layer images of two sizes in the slots)."""
+    wl = tiny_q4_k_m()
+    assert wl.layer_bytes(0) > wl.layer_bytes(1)
+    m, om, records = run_pair(qwg, wl, 3, n_resident=n_resident)
+    for g_next, g_logits, hid, r in records:
+        assert rel_l2(g_logits, r["logits"]) < 2e-3
+        for l in range(wl.n_layers + 1):
+            assert rel_l2(hid[l], r["hidden"][l]) < 2e-3, l
+    m.close()
+
+
+def test_mixed_layer_types_spec_step(qwg):
+    wl = tiny_q4_k_m(wid=216, draft_k=3)
+    m = qwg.make_model(wl)
+    qwg.load(m, wl)
+    om = oracle.OracleModel(wl)
+    t = wl.first_token()
+    for _ in range(2):
+        toks, acc = m.spec_step(t, 2, 3)
+        r = om.spec_round(t, 2, 3)
+        assert toks == r["tokens"] and acc == r["n_accepted"]
+        t = toks[-1]
+    m.close()
+
+
 def test_streaming_equals_resident_bitwise(qwg):
     wl = synth.tiny(synth.Q6_K, n_layers=5, wid=160)
     outs = []
@@ -145,7 +181,7 @@ def test_spec_step_matches_oracle(qwg, identity_tail):
     if identity_tail:
         for l in (2, 3):
             for t in (synth.WO, synth.WDOWN):
-                ov[(l, t)] = _zero_scales(wl.weight(l, t), wl.qtype_of(t))
+                ov[(l, t)] = _zero_scales(wl.weight(l, t), wl.qtype_of(t, l))
     m = qwg.make_model(wl)
     qwg.load(m, wl, weights_override=ov)
     om = oracle.OracleModel(wl)
@@ -176,7 +212,7 @@ def test_spec_step_streamed_verify(qwg, identity_tail):
     if identity_tail:
         for l in (2, 3):
             for t in (synth.WO, synth.WDOWN):
-                ov[(l, t)] = _zero_scales(wl.weight(l, t), wl.qtype_of(t))
+                ov[(l, t)] = _zero_scales(wl.weight(l, t), wl.qtype_of(t, l))
     om = oracle.OracleModel(wl)
     for (l, t), W in ov.items():
         om._keep.append(W)

@@ -319,7 +319,7 @@ def _model_with_identity_layers(wl, layers):
     for l in layers:
         for i, t in enumerate(om.TENSORS):
             if t in (synth.WO, synth.WDOWN):
-                z = _zero_d(wl.weight(l, t), wl.qtype_of(t))
+                z = _zero_d(wl.weight(l, t), wl.qtype_of(t, l))
                 om._keep.append(z)
                 om.layers[l].w[i] = z.ctypes.data
     return om

@@ -5,6 +5,7 @@ adaptive cache"; [HN] 3-tier cache detail)."""
 import ctypes
 import os
 
+import numpy as np
 import pytest
 
 import synth
@@ -83,12 +84,53 @@ def test_nothing_fits_is_an_error(L):
     assert e.value.code == -3
 
 
+def test_mixed_layer_types(L):
+    """A per-layer type table: layers with a wider W_down have larger images; a bad type is refused."""
+    wl = synth.replace(synth.tiny(synth.Q4_K, n_layers=4), qtype_head=synth.Q6_K, wide_qtype=synth.Q6_K,
+                       wide_down_every=2)
+    lt = wl.layer_qtypes()
+    assert lt.shape == (4, 4) and list(lt[:, 3]) == [synth.Q6_K, synth.Q4_K, synth.Q6_K, synth.Q4_K]
+    assert (lt[:, :3] == synth.Q4_K).all()
+
+    def arena(table, n_res):
+        d = desc_of(wl, n_res, 64)
+        d.layer_qtypes = None if table is None else table.ctypes.data
+        h = ctypes.c_void_p()
+        _lib.call("qwg_model_create", ctypes.byref(d), ctypes.byref(h))
+        try:
+            return int(L.qwg_model_arena_bytes(h))
+        finally:
+            L.qwg_model_destroy(h)
+
+    plain = np.full((4, 4), synth.Q4_K, dtype=np.int32)
+    assert arena(lt, -1) > arena(plain, -1) == arena(None, -1)
+    # resident layer 0 (wide) costs more than resident layer 1 (narrow)
+    assert arena(lt, 1) - arena(lt, 0) > arena(lt, 2) - arena(lt, 1)
+    bad = lt.copy()
+    bad[2, 1] = 7
+    with pytest.raises(_lib.QwgError) as e:
+        arena(bad, -1)
+    assert e.value.code == -6
+
+
+def test_q4_k_m_stand_in_bits_per_weight():
+    """The Q4_K_M stand-in averages 4.78 bits per layer weight (Q4_K with half the W_down in Q6_K)."""
+    wl = synth.LLAMA70B_Q4_K_M
+    n_w = sum(wl.shape_of(t)[0] * wl.shape_of(t)[1] for t in (synth.WQ, synth.WK, synth.WV, synth.WO,
+                                                               synth.WGATE, synth.WUP, synth.WDOWN))
+    bpw = 8 * wl.layers_bytes() / (wl.n_layers * n_w)
+    assert abs(bpw - 4.78) < 0.01
+    assert wl.layer_bytes(0) - wl.layer_bytes(1) == (210 - 144) * wl.hidden * wl.ffn // 256
+
+
 def test_fewer_bits_keep_more_layers_resident(L):
     """The pages' consequence of tier sizing: at the same 24 GB device budget a 4.5-bit 70B model
     keeps about ten more layers in device memory than the 6.6-bit one (36 vs 26 there)."""
     q4 = synth.replace(synth.LLAMA70B_Q4_K, n_resident=-1)
     q6 = synth.replace(synth.LLAMA70B_Q6_K_STREAM, n_resident=-1)
+    q4m = synth.LLAMA70B_Q4_K_M
     n4 = plan(q4, 24 * 10**9, 256 * GIB, 2048 + 64)[0]
+    n4m = plan(q4m, 24 * 10**9, 256 * GIB, 2048 + 64)[0]
     n6 = plan(q6, 24 * 10**9, 256 * GIB, 2048 + 64)[0]
-    assert 0 < n6 < n4 < 80
-    assert n4 - n6 >= 10
+    assert 0 < n6 < n4m < n4 < 80
+    assert n4m - n6 >= 10
