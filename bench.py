@@ -204,6 +204,9 @@ def main() -> int:
     ap.add_argument("--hbm-budget-gb", type=float, default=0.0,
                     help="place layers automatically for this device-memory budget (GB): the resident tier "
                          "gets what fits, the rest streams from pinned host memory (0: the workload's placement)")
+    ap.add_argument("--prefill", type=int, default=0,
+                    help="after the decode measurements, time a prefill of this many prompt tokens")
+    ap.add_argument("--prefill-cols", type=int, default=8, help="columns per prefill pass (the model's max_cols)")
     ap.add_argument("--verify-form", choices=["mfma", "dot"], default="mfma",
                     help="2..4-column Q5_K/Q6_K GEMVs of the verify pass: matrix cores or integer dot products")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -224,7 +227,8 @@ def main() -> int:
     wl = workloads()[args.workload]
     spec = wl.draft_layers > 0
     total_steps = args.warmup + args.steps * 2 + args.class_steps * 5 + 1
-    max_ctx = wl.n_prior + total_steps * (wl.draft_k + 1 if spec else 1) + 8
+    max_ctx = wl.n_prior + total_steps * (wl.draft_k + 1 if spec else 1) + 8 + max(0, args.prefill)
+    max_cols = max(wl.draft_k + 1 if spec else 1, args.prefill_cols if args.prefill > 0 else 1)
     if args.copy_probe_mib > 0:
         src = torch.ones(args.copy_probe_mib << 18, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -236,13 +240,12 @@ def main() -> int:
     log("workload %s: %d layers, %.2f GB of weights, KV %d positions" %
         (wl.name, wl.n_layers, wl.model_bytes() / 1e9, wl.n_prior))
     if args.hbm_budget_gb > 0:
-        cols = wl.draft_k + 1 if wl.draft_k else 1
-        n_res, a_b, p_b = synthetic.plan_residency_of(wl, max_ctx=max_ctx, max_cols=cols,
+        n_res, a_b, p_b = synthetic.plan_residency_of(wl, max_ctx=max_ctx, max_cols=max_cols,
                                                       device_budget=int(args.hbm_budget_gb * 1e9))
         wl = synth.replace(wl, n_resident=n_res)
         log("automatic placement for %.1f GB of HBM: %d of %d layers resident (arena %.2f GB, pinned %.2f GB)"
             % (args.hbm_budget_gb, n_res, wl.n_layers, a_b / 1e9, p_b / 1e9))
-    m = synthetic.make_model(wl, max_ctx=max_ctx)
+    m = synthetic.make_model(wl, max_ctx=max_ctx, max_cols=max_cols)
     log("arena %.2f GB" % (m.arena_bytes / 1e9))
     load_s = synthetic.load(m, wl, log=log)
     log("loaded in %.1f s" % load_s)
@@ -317,6 +320,20 @@ def main() -> int:
     gemv_gbps = tot_b / (tot_ms * 1e-3) / 1e9
     log("all GEMVs of a step: %.1f GB/s (%.1f%% of 8 TB/s), %.3f ms of %.3f ms" %
         (gemv_gbps, 100 * gemv_gbps / HBM_PEAK_GBPS, tot_ms, ms_per_step))
+    prefill = None
+    if args.prefill > 0:
+        # a deterministic synthetic prompt, after everything else (it extends the context)
+        prompt = [(wl.first_token() + 7919 * i) % wl.vocab for i in range(args.prefill)]
+        m.prefill(prompt[: max_cols])  # warm-up pass
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        m.prefill(prompt)
+        torch.cuda.synchronize()
+        dt_p = time.perf_counter() - t0
+        prefill = {"tokens": args.prefill, "columns_per_pass": max_cols, "ms": round(dt_p * 1e3, 3),
+                   "tok_s": round(args.prefill / dt_p, 1)}
+        log("prefill of %d tokens in passes of %d columns: %.2f ms, %.1f tok/s"
+            % (args.prefill, max_cols, dt_p * 1e3, args.prefill / dt_p))
     h2d_b, h2d_ms = m.stream_stats()
     step_bytes = round_bytes(wl, n_pos_mid) if spec else token_bytes(wl, n_pos_mid)
     h2d_ceiling = measure_h2d_ceiling() if h2d_b else None
@@ -368,6 +385,8 @@ def main() -> int:
                       "ceiling_gbps": h2d_ceiling}
     if read_ceiling:
         out["hbm_read_ceiling"] = read_ceiling
+    if prefill:
+        out["prefill"] = prefill
     if spec:
         out["spec"] = {"rounds": args.steps, "tokens": n_tok, "ms_per_round": round(ms_per_step, 3),
                        "draft_layers": wl.draft_layers, "k": wl.draft_k, "verify_form": args.verify_form,

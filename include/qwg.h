@@ -223,6 +223,13 @@ int qwg_model_get_kv(qwg_model* m, int layer, uint16_t* h_k, uint16_t* h_v, int 
  * h_logits (optional) receives the fp32 logits [vocab]. Synchronizes. */
 int qwg_decode_step(qwg_model* m, int32_t token, int32_t* next_token, float* h_logits);
 
+/* Prompt prefill ([NT] "Quick start": the -p prompt): tokens[0..n-1] go at positions n_past ..
+ * n_past+n-1, each attending causally to the positions before it, as n decode steps would, in passes
+ * of up to max_cols columns (the multi-column GEMVs read each weight once per pass); only the last
+ * pass runs the final norm, head and argmax.  *next_token (optional) is the greedy token after the
+ * prompt, h_logits (optional) its fp32 logits [vocab].  n_past advances by n.  Synchronizes. */
+int qwg_prefill(qwg_model* m, const int32_t* tokens, int n, int32_t* next_token, float* h_logits);
+
 /* Layer-skip calibration ([NT] "Key results"/"Key features"; [UR] layer-skip mechanism): one decode
  * step with every layer computed that records c_l = cos(h_in, h_out) per layer (h_cos, fp32
  * [n_layers], optional) and sets skip[l] = (c_l >= tau) (h_mask, optional).  Skipped layers then do no

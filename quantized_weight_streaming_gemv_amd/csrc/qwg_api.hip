@@ -500,8 +500,9 @@ static int issue_copy(qwg_model* m, const std::vector<int>& sl, int j) {
   return QWG_OK;
 }
 
-// Embedding, layers [0, n_run) (skipped layers bypassed unless calibrating), final norm, head, argmax.
-static int run_pass(qwg_model* m, const int32_t* toks, int nc, int pos, int n_run, bool calib) {
+// Embedding, layers [0, n_run) (skipped layers bypassed unless calibrating), then (with head) final
+// norm, head, argmax.
+static int run_pass(qwg_model* m, const int32_t* toks, int nc, int pos, int n_run, bool calib, bool head = true) {
   const qwg_model_desc& d = m->d;
   const int H = d.hidden;
   if (!m->bound) return fail(QWG_E_STATE, "model is not bound");
@@ -571,6 +572,7 @@ static int run_pass(qwg_model* m, const int32_t* toks, int nc, int pos, int n_ru
   for (int l = n_run; l < d.n_layers && m->capture_on; ++l)
     QWG_HIP(hipMemcpyAsync(m->f(m->capture) + (size_t)(l + 1) * H, m->f(m->h), (size_t)H * 4,
                            hipMemcpyDeviceToDevice, m->cs));
+  if (!head) return QWG_OK;
   EpiArgs e{};
   e.y = m->f(m->logits);
   e.y_stride = d.vocab;
@@ -979,6 +981,30 @@ int qwg_decode_step(qwg_model* m, int32_t token, int32_t* next_token, float* h_l
     if (int rc = finish_pass(m, 1, &nt, h_logits)) return rc;
     if (next_token) *next_token = nt;
     m->n_past += 1;
+    return QWG_OK;
+  });
+}
+
+int qwg_prefill(qwg_model* m, const int32_t* tokens, int n, int32_t* next_token, float* h_logits) {
+  if (!m || !tokens) return fail(QWG_E_INVAL, "NULL pointer");
+  if (n < 1) return fail(QWG_E_SHAPE, "n must be >= 1");
+  return guarded([&]() -> int {
+    if (m->n_past + n > m->d.max_ctx) return fail(QWG_E_STATE, "context full (n_past + n > max_ctx)");
+    const int C = m->d.max_cols;
+    for (int i = 0; i < n; i += C) {
+      const int c = std::min(C, n - i);
+      const bool last = i + c == n;
+      if (int rc = run_pass(m, tokens + i, c, m->n_past, m->d.n_layers, false, last)) return rc;
+      if (last) {
+        std::vector<int32_t> am(c);
+        if (int rc = finish_pass(m, c, am.data(), nullptr)) return rc;
+        if (next_token) *next_token = am[c - 1];
+        if (h_logits)
+          QWG_HIP(hipMemcpy(h_logits, m->f(m->logits) + (size_t)(c - 1) * m->d.vocab, (size_t)m->d.vocab * 4,
+                            hipMemcpyDeviceToHost));
+      }
+      m->n_past += c;
+    }
     return QWG_OK;
   });
 }

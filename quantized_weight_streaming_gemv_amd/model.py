@@ -119,6 +119,15 @@ class Model:
         call("qwg_get_layer_skip", self.handle, m.ctypes.data)
         return m
 
+    def prefill(self, tokens: Sequence[int], want_logits: bool = False):
+        """Run a prompt (positions n_past ..); returns (next greedy token, its logits or None)."""
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        nt = ctypes.c_int32(0)
+        logits = np.empty(self.vocab, dtype=np.float32) if want_logits else None
+        call("qwg_prefill", self.handle, t.ctypes.data, t.size, ctypes.byref(nt),
+             logits.ctypes.data if want_logits else None)
+        return int(nt.value), logits
+
     def spec_step(self, token: int, draft_layers: int, k: int):
         out = np.zeros(k + 1, dtype=np.int32)
         n_out, n_acc = ctypes.c_int32(0), ctypes.c_int32(0)

@@ -95,6 +95,30 @@ def test_mixed_layer_types_spec_step(qwg):
     m.close()
 
 
+@pytest.mark.parametrize("case", [(synth.Q4_K, synth.Q4_K, 4, -1), (synth.Q6_K, synth.Q5_K, 4, -1),
+                                  (synth.Q4_K, synth.Q4_K, 8, 2)], ids=["q4k-4col", "q6k-q5k-4col-mfma", "q4k-8col-streamed"])
+def test_prefill_matches_sequential_steps(qwg, case):
+    """Prefill of an 11-token prompt in passes of max_cols columns (ragged last pass) equals 11
+    sequential decode steps of the oracle: next token, its logits, the KV rows, n_past."""
+    qa, qf, cols, res = case
+    wl = synth.tiny(qa, qf, wid=230 + cols + res)
+    prompt = [(wl.first_token() + 7919 * i) % wl.vocab for i in range(11)]
+    m = qwg.make_model(wl, max_cols=cols, n_resident=res)
+    qwg.load(m, wl)
+    nxt, logits = m.prefill(prompt, want_logits=True)
+    om = oracle.OracleModel(wl)
+    for t in prompt:
+        r = om.decode(t)
+    assert m.n_past == om.n_past == wl.n_prior + len(prompt)
+    assert rel_l2(logits, r["logits"]) < 2e-3
+    if nxt != r["next"]:
+        assert is_tie(r["logits"], nxt, r["next"])
+    for l in (0, wl.n_layers - 1):
+        k, v = m.get_kv(l, om.n_past)
+        assert np.mean(k == om.kc[l][: om.n_past]) > 0.99 and np.mean(v == om.vc[l][: om.n_past]) > 0.99
+    m.close()
+
+
 def test_streaming_equals_resident_bitwise(qwg):
     wl = synth.tiny(synth.Q6_K, n_layers=5, wid=160)
     outs = []
