@@ -204,6 +204,8 @@ def main() -> int:
     ap.add_argument("--hbm-budget-gb", type=float, default=0.0,
                     help="place layers automatically for this device-memory budget (GB): the resident tier "
                          "gets what fits, the rest streams from pinned host memory (0: the workload's placement)")
+    ap.add_argument("--file-layers", type=int, default=0,
+                    help="move the first N streamed layers to files (the file-backed tier; files in $TMPDIR)")
     ap.add_argument("--prefill", type=int, default=0,
                     help="after the decode measurements, time a prefill of this many prompt tokens")
     ap.add_argument("--prefill-cols", type=int, default=8, help="columns per prefill pass (the model's max_cols)")
@@ -249,6 +251,16 @@ def main() -> int:
     log("arena %.2f GB" % (m.arena_bytes / 1e9))
     load_s = synthetic.load(m, wl, log=log)
     log("loaded in %.1f s" % load_s)
+    spill_dir = None
+    if args.file_layers > 0:
+        import shutil
+        import tempfile
+        streamed = [l for l in range(wl.n_layers) if l >= wl.resident_layers]
+        spill = streamed[: args.file_layers]
+        spill_dir = tempfile.mkdtemp(prefix="qwg-tier-c-")
+        for l in spill:
+            m.spill_layer(l, os.path.join(spill_dir, "layer%03d.img" % l))
+        log("file-backed tier: layers %d..%d in %s" % (spill[0], spill[-1], spill_dir))
 
     tok = wl.first_token()
     if wl.skip_tau > 0:
@@ -335,11 +347,14 @@ def main() -> int:
         log("prefill of %d tokens in passes of %d columns: %.2f ms, %.1f tok/s"
             % (args.prefill, max_cols, dt_p * 1e3, args.prefill / dt_p))
     h2d_b, h2d_ms = m.stream_stats()
+    file_b, file_ms = m.file_stats()
     step_bytes = round_bytes(wl, n_pos_mid) if spec else token_bytes(wl, n_pos_mid)
     h2d_ceiling = measure_h2d_ceiling() if h2d_b else None
     m.close()
     del m
     torch.cuda.empty_cache()
+    if spill_dir:
+        shutil.rmtree(spill_dir, ignore_errors=True)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -387,6 +402,10 @@ def main() -> int:
         out["hbm_read_ceiling"] = read_ceiling
     if prefill:
         out["prefill"] = prefill
+    if spill_dir:
+        out["file_tier"] = {"layers": args.file_layers, "bytes": file_b, "host_ms": round(file_ms, 3),
+                            "gbps": round(file_b / (file_ms * 1e-3) / 1e9, 2) if file_ms > 0 else None,
+                            "note": "host reads of freshly written files (page cache) into pinned staging"}
     if spec:
         out["spec"] = {"rounds": args.steps, "tokens": n_tok, "ms_per_round": round(ms_per_step, 3),
                        "draft_layers": wl.draft_layers, "k": wl.draft_k, "verify_form": args.verify_form,

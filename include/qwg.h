@@ -267,6 +267,20 @@ int qwg_model_set_timing(qwg_model* m, int tensor_id);
 int qwg_model_get_timing(qwg_model* m, double* total_ms, int64_t* n_launches, int64_t* bytes_per_launch);
 /* Bytes copied host-to-device for streamed layers in the last step, and the copy-stream time (ms). */
 int qwg_model_stream_stats(qwg_model* m, int64_t* h2d_bytes, double* h2d_ms);
+
+/* File-backed third tier ([NT] "3-tier adaptive cache": tier C, storage / mmap, used only when the
+ * other tiers are full; [HN] 3-tier detail; data path storage -> pinned staging -> H2D -> GPU): move a
+ * streamed layer's packed image from its pinned host image to the file `path` (created or
+ * truncated, mode 0600), free the pinned image and map the file read-only.  From then on each pass
+ * that runs the layer has the host copy the mapped image (page cache or storage) into one of two
+ * library-owned pinned staging images, with several threads, before the copy stream moves it into
+ * an HBM slot; a staging image is refilled only after the copy out of it is done.  Results are
+ * identical to the pinned tier.  The layer must be streamed (not resident) and loaded; its tensors
+ * cannot be set again afterwards.  The library unmaps at qwg_model_destroy; the caller removes the
+ * file.  Synchronizes. */
+int qwg_model_spill_layer(qwg_model* m, int layer, const char* path);
+/* Bytes the host read from file-backed images and the milliseconds it spent, since the last call. */
+int qwg_model_file_stats(qwg_model* m, int64_t* bytes, double* ms);
 int qwg_sync(qwg_model* m);
 
 /* Plain streaming read of `bytes` (a positive multiple of 16; d_src 16-byte aligned) with the

@@ -51,6 +51,8 @@ SIGNATURES = {
     "qwg_gemv": (ctypes.c_int, [ctypes.c_int, vp, i64, i64, vp, ctypes.c_int, vp, vp]),
     "qwg_set_gemv_geometry": (ctypes.c_int, [ctypes.c_int] * 4),
     "qwg_set_gemv_mfma": (ctypes.c_int, [ctypes.c_int]),
+    "qwg_model_spill_layer": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_char_p]),
+    "qwg_model_file_stats": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "qwg_prefill": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]),
     "qwg_plan_residency": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_size_t, ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_void_p]),

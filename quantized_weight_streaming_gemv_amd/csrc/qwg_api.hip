@@ -7,8 +7,15 @@
 // fully resident, so residency is the primary mode; streaming is kept for layers >= n_resident.
 #include <hip/hip_runtime.h>
 
+#include <fcntl.h>
+#include <sys/mman.h>
+#include <sys/stat.h>
+#include <unistd.h>
+
+#include <chrono>
 #include <cmath>
 #include <cstdio>
+#include <thread>
 #include <cstring>
 #include <new>
 #include <stdexcept>
@@ -108,6 +115,8 @@ struct LayerPlan {
   bool resident;
   size_t arena_off;   // resident image in the arena
   uint8_t* host;      // streamed image in pinned host memory
+  const uint8_t* map; // or: file-backed image (read-only mapping of map_len bytes)
+  size_t map_len;
   size_t g_attn, g_ffn, kc, vc;
 };
 
@@ -140,6 +149,11 @@ struct qwg_model {
   int cev_used = 0;
   int64_t h2d_bytes = 0;
   double h2d_ms = 0.0;
+  // file-backed tier: two pinned staging images the host fills from the mappings
+  uint8_t* stage[2] = {nullptr, nullptr};
+  hipEvent_t ev_staged[2] = {};  // the H2D copy out of stage[i] is done
+  int64_t file_bytes = 0;
+  double file_ms = 0.0;
 
   int H() const { return d.hidden; }
   int QR() const { return d.n_q * d.head_dim; }
@@ -193,6 +207,8 @@ static int plan_model(qwg_model* m) {
     m->image_max = std::max(m->image_max, ic);
     P.resident = l < n_res;
     P.host = nullptr;
+    P.map = nullptr;
+    P.map_len = 0;
     if (P.resident) {
       P.arena_off = cur;
       cur = align_up(cur + P.image);
@@ -485,15 +501,41 @@ static int layer_kernels(qwg_model* m, int l, const uint8_t* base, int nc, int p
   return QWG_OK;
 }
 
+// Host copy of n bytes by several threads (the file-backed tier's read into pinned staging).
+static void parallel_copy(uint8_t* dst, const uint8_t* src, size_t n) {
+  const int T = (int)std::max(1u, std::min(8u, std::thread::hardware_concurrency()));
+  const size_t part = (n / T + 4095) & ~(size_t)4095;
+  std::vector<std::thread> th;
+  for (int t = 1; t < T; ++t) {
+    const size_t b = (size_t)t * part;
+    if (b >= n) break;
+    th.emplace_back([=] { std::memcpy(dst + b, src + b, std::min(part, n - b)); });
+  }
+  std::memcpy(dst, src, std::min(part, n));
+  for (auto& x : th) x.join();
+}
+
 static int issue_copy(qwg_model* m, const std::vector<int>& sl, int j) {
   const int slot = j & 1;
   const LayerPlan& P = m->L[sl[j]];
+  const uint8_t* src = P.host;
+  if (P.map) {
+    // file-backed: the host reads the image into staging image `slot` once the copy that last read
+    // it (two streamed layers ago) is done, then the copy stream moves it to the HBM slot
+    QWG_HIP(hipEventSynchronize(m->ev_staged[slot]));
+    const auto t0 = std::chrono::steady_clock::now();
+    parallel_copy(m->stage[slot], P.map, P.image);
+    m->file_ms += std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+    m->file_bytes += (int64_t)P.image;
+    src = m->stage[slot];
+  }
   QWG_HIP(hipStreamWaitEvent(m->xs, m->ev_free[slot], 0));
   hipEvent_t c0 = pool_event(m->cev, m->cev_used);
   hipEvent_t c1 = pool_event(m->cev, m->cev_used);
   if (!c0 || !c1) return fail(QWG_E_HIP, "hipEventCreate failed");
   QWG_HIP(hipEventRecord(c0, m->xs));
-  QWG_HIP(hipMemcpyAsync(m->arena + m->slot[slot], P.host, P.image, hipMemcpyHostToDevice, m->xs));
+  QWG_HIP(hipMemcpyAsync(m->arena + m->slot[slot], src, P.image, hipMemcpyHostToDevice, m->xs));
+  if (P.map) QWG_HIP(hipEventRecord(m->ev_staged[slot], m->xs));
   QWG_HIP(hipEventRecord(c1, m->xs));
   QWG_HIP(hipEventRecord(m->ev_full[slot], m->xs));
   m->h2d_bytes += (int64_t)P.image;
@@ -878,11 +920,15 @@ void qwg_model_destroy(qwg_model* m) {
     (void)hipStreamSynchronize(m->cs);
     (void)hipStreamSynchronize(m->xs);
   }
-  for (auto& P : m->L)
+  for (auto& P : m->L) {
     if (P.host) (void)hipHostFree(P.host);
+    if (P.map) munmap((void*)P.map, P.map_len);
+  }
   for (int i = 0; i < 2; ++i) {
     if (m->ev_full[i]) (void)hipEventDestroy(m->ev_full[i]);
     if (m->ev_free[i]) (void)hipEventDestroy(m->ev_free[i]);
+    if (m->ev_staged[i]) (void)hipEventDestroy(m->ev_staged[i]);
+    if (m->stage[i]) (void)hipHostFree(m->stage[i]);
   }
   for (auto e : m->tev) (void)hipEventDestroy(e);
   for (auto e : m->cev) (void)hipEventDestroy(e);
@@ -916,6 +962,7 @@ int qwg_model_set_tensor(qwg_model* m, int layer, int tensor_id, int qtype, cons
   const int64_t rb = canon_row_bytes(qtype, k);
   if ((int64_t)nbytes != rows * rb) return fail(QWG_E_SHAPE, "nbytes != rows * row_bytes");
   const bool streamed = P && !P->resident;
+  if (streamed && P->map) return fail(QWG_E_STATE, "the layer's image is file-backed (spilled)");
   uint8_t* dst;
   if (global) dst = m->arena + mp->off;
   else if (!streamed) dst = m->arena + P->arena_off + mp->off;
@@ -1121,6 +1168,57 @@ int qwg_model_get_timing(qwg_model* m, double* total_ms, int64_t* n_launches, in
   if (total_ms) *total_ms = m->t_ms;
   if (n_launches) *n_launches = m->t_n;
   if (bytes_per_launch) *bytes_per_launch = m->t_bytes;
+  return QWG_OK;
+}
+
+int qwg_model_spill_layer(qwg_model* m, int layer, const char* path) {
+  if (!m || !path) return fail(QWG_E_INVAL, "NULL pointer");
+  if (!m->bound) return fail(QWG_E_STATE, "model is not bound");
+  if (layer < 0 || layer >= m->d.n_layers) return fail(QWG_E_INVAL, "bad layer index");
+  LayerPlan& P = m->L[layer];
+  if (P.resident) return fail(QWG_E_STATE, "only streamed layers can be file-backed");
+  if (P.map) return fail(QWG_E_STATE, "layer already file-backed");
+  return guarded([&]() -> int {
+    QWG_HIP(hipStreamSynchronize(m->cs));
+    QWG_HIP(hipStreamSynchronize(m->xs));
+    if (!m->stage[0]) {
+      for (int i = 0; i < 2; ++i) {
+        void* p = nullptr;
+        hipError_t e = hipHostMalloc(&p, m->image_max, hipHostMallocDefault);
+        if (e != hipSuccess) return fail(QWG_E_NOMEM, std::string("pinned staging: ") + hipGetErrorString(e));
+        m->stage[i] = (uint8_t*)p;
+        QWG_HIP(hipEventCreateWithFlags(&m->ev_staged[i], hipEventDisableTiming));
+        QWG_HIP(hipEventRecord(m->ev_staged[i], m->xs));
+      }
+    }
+    const int fd = open(path, O_RDWR | O_CREAT | O_TRUNC, 0600);
+    if (fd < 0) return fail(QWG_E_INVAL, std::string("cannot create ") + path);
+    size_t done = 0;
+    while (done < P.image) {
+      const ssize_t w = write(fd, P.host + done, P.image - done);
+      if (w <= 0) {
+        close(fd);
+        return fail(QWG_E_NOMEM, std::string("write failed: ") + path);
+      }
+      done += (size_t)w;
+    }
+    void* map = mmap(nullptr, P.image, PROT_READ, MAP_SHARED, fd, 0);
+    close(fd);
+    if (map == MAP_FAILED) return fail(QWG_E_NOMEM, std::string("mmap failed: ") + path);
+    QWG_HIP(hipHostFree(P.host));
+    P.host = nullptr;
+    P.map = (const uint8_t*)map;
+    P.map_len = P.image;
+    return QWG_OK;
+  });
+}
+
+int qwg_model_file_stats(qwg_model* m, int64_t* bytes, double* ms) {
+  if (!m) return fail(QWG_E_INVAL, "NULL model");
+  if (bytes) *bytes = m->file_bytes;
+  if (ms) *ms = m->file_ms;
+  m->file_bytes = 0;
+  m->file_ms = 0.0;
   return QWG_OK;
 }
 

@@ -167,6 +167,15 @@ class Model:
         call("qwg_model_get_timing", self.handle, ctypes.byref(ms), ctypes.byref(n), ctypes.byref(b))
         return float(ms.value), int(n.value), int(b.value)
 
+    def spill_layer(self, layer: int, path: str) -> None:
+        """Move a streamed layer's image to a file (the file-backed tier); the caller removes the file."""
+        call("qwg_model_spill_layer", self.handle, layer, path.encode())
+
+    def file_stats(self):
+        b, ms = ctypes.c_int64(0), ctypes.c_double(0)
+        call("qwg_model_file_stats", self.handle, ctypes.byref(b), ctypes.byref(ms))
+        return int(b.value), float(ms.value)
+
     def stream_stats(self):
         b, ms = ctypes.c_int64(0), ctypes.c_double(0)
         call("qwg_model_stream_stats", self.handle, ctypes.byref(b), ctypes.byref(ms))

@@ -138,6 +138,39 @@ def test_streaming_equals_resident_bitwise(qwg):
         assert toks == outs[0][0] and np.array_equal(lg, outs[0][1])
 
 
+def test_file_backed_layers_equal_pinned_bitwise(qwg, tmp_path):
+    """The file-backed tier (streamed layers spilled to files, read by the host into pinned staging,
+    then copied to HBM) decodes bitwise like the pinned tier, also mixed with pinned layers."""
+    from quantized_weight_streaming_gemv_amd import _lib
+    wl = synth.tiny(synth.Q6_K, n_layers=5, wid=161)
+    runs = []
+    for spill in ((), (2, 4), (1, 2, 3, 4)):
+        m = qwg.make_model(wl, n_resident=1)
+        qwg.load(m, wl)
+        for l in spill:
+            m.spill_layer(l, str(tmp_path / ("layer%d-%d.img" % (l, len(spill)))))
+        t, out = wl.first_token(), []
+        for _ in range(3):
+            t, lg = m.decode_step(t, want_logits=True)
+            out.append((t, lg))
+        fb, _ = m.file_stats()
+        h2d, _ = m.stream_stats()
+        assert h2d > 0 and fb == 3 * len(spill) * (h2d // (3 * 4))
+        if spill:
+            with pytest.raises(_lib.QwgError) as e:  # a spilled layer's tensors cannot be set again
+                m.set_tensor(spill[0], synth.WO, wl.qtype_of(synth.WO, spill[0]), wl.weight(spill[0], synth.WO))
+            assert e.value.code == -5
+            with pytest.raises(_lib.QwgError):
+                m.spill_layer(spill[0], str(tmp_path / "again.img"))
+        with pytest.raises(_lib.QwgError):
+            m.spill_layer(0, str(tmp_path / "resident.img"))  # layer 0 is resident
+        runs.append(out)
+        m.close()
+    for out in runs[1:]:
+        for (t, lg), (rt, rl) in zip(out, runs[0]):
+            assert t == rt and np.array_equal(lg, rl)
+
+
 def test_calibrate_skip_matches_oracle(qwg):
     wl = synth.tiny(synth.Q6_K, n_layers=6, near_identity_every=2, wid=170)
     m = qwg.make_model(wl, n_resident=3)
