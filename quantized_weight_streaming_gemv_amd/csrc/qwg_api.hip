@@ -408,7 +408,7 @@ static int gemv(qwg_model* m, int tensor_class, int qt, const MatView& w, const 
     e.dig_out = (uint32_t*)(m->arena + m->xd[od.buf]);
     e.dig_stride = m->xd_col / 4;
     e.dig_gain = od.gain;
-    e.dig_kind = digit_kind(od.qt);
+    e.dig_kind = gemv_digit_kind(od.qt, epi == EPI_SWIGLU ? w.rows / 2 : w.rows, nc);
     e.sq_out = od.sq ? m->f(m->sq) : nullptr;
     e.sq_out_stride = m->sq_col;
   }
@@ -460,7 +460,7 @@ static int layer_kernels(qwg_model* m, int l, const uint8_t* base, int nc, int p
   if (ap.work_bytes > m->attn_bytes) return fail(QWG_E_NOMEM, "attention workspace too small");
   QWG_HIP(launch_attn(m->f(m->qb), QR, e.kc, e.vc, KR, pos + 1, d.n_q, d.n_kv, nc, m->f(m->ob), QR,
                       m->arena + m->attn, ap, m->cs, (uint32_t*)(m->arena + m->xd[1]), m->xd_col / 4,
-                      digit_kind(qt_o)));
+                      gemv_digit_kind(qt_o, QR, nc)));
   EpiArgs r{};
   r.y = m->f(m->h);
   r.y_stride = H;

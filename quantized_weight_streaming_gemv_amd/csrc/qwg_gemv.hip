@@ -485,8 +485,9 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const float* part, int kspl
 // ------------------------------------------------------------------ several columns on the matrix cores
 //
 // The verify pass of self-speculative decoding multiplies one weight matrix by k+1 = 2..4 activation
-// columns ([NT] "Key features": self-speculative decoding).  For Q5_K and Q6_K, whose activation
-// digits are bytes, each 16-row tile and 32-weight chunk is one v_mfma_i32_16x16x32_i8 with
+// columns ([NT] "Key features": self-speculative decoding), and prefill a few prompt tokens at once.
+// For Q4_K, Q5_K and Q6_K (with byte activation digits: the producers of this kernel's input pick
+// the kind with gemv_digit_kind) each 16-row tile and 32-weight chunk is one v_mfma_i32_16x16x32_i8 with
 //   A (16 x 32): activation digits, slot m = 4 * column + level (level 3 is zero),
 //   B (32 x 16): the chunk's quants as int8 bytes, one column per output row,
 // so the 4 x 3 digit levels of all columns meet every weight in one exact integer product.  With
@@ -541,6 +542,13 @@ __device__ __forceinline__ uint32_t lane_fetch(int src_lane, uint32_t v) {
 }
 template <int QT>
 struct MfRaw;
+// Q4_K: the quants (stored q XOR 8) and the header, as Q5_K without fifth bits.
+template <>
+struct MfRaw<Q4_K> {
+  uint4 q[4];
+  uint4 h;
+};
+
 // Q5_K steps are two superblocks (16 chunks); each lane group loads a different part of the rows'
 // fifth bits and headers, and the quarter steps fetch what they need from the group that holds it
 // (ds_bpermute): one 16-B read per lane covers a row's 64 contiguous bytes of fifth bits.
@@ -564,10 +572,10 @@ template <int QT>
 __device__ __forceinline__ MfRaw<QT> mf_load(const MatView& w, uint32_t ro, uint32_t srow, int cg, int g) {
   MfRaw<QT> r;
   const uint32_t s0 = srow + slot_chunk(w.ilv, (uint32_t)cg);  // the superblock's 8 chunks are consecutive slots
-  if constexpr (QT == Q5_K) {
+  if constexpr (QT == Q4_K || QT == Q5_K) {
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) r.q[qq] = ld_stream_u4(w.q + (s0 + 4u * qq + (uint32_t)g) * 16u);
-    r.qh = ld<uint4>(w.b + (s0 + 4u * g) * 4u);
+    if constexpr (QT == Q5_K) r.qh = ld<uint4>(w.b + (s0 + 4u * g) * 4u);
     r.h = ld<uint4>(w.a + ro + (uint32_t)((cg >> 3) + (g & 1)) * 16u);
   } else {
 #pragma unroll
@@ -582,7 +590,7 @@ __device__ __forceinline__ MfRaw<QT> mf_load(const MatView& w, uint32_t ro, uint
 
 template <int QT, int EPI>
 __global__ __launch_bounds__(1024) void k_gemv_mfma(GemvArgs a, int kparts) {
-  static_assert(QT == Q5_K || QT == Q6_K, "formats with byte activation digits and 32-weight chunks");
+  static_assert(QT == Q4_K || QT == Q5_K || QT == Q6_K, "K-quant formats with 32-weight chunks");
   extern __shared__ uint4 lds[];
   __shared__ float red[MAX_COLS][16];
   const int tid = threadIdx.x, lane = tid & 63, nw = blockDim.x >> 6;
@@ -637,7 +645,7 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(GemvArgs a, int kparts) {
   const int rows = a.w.rows;
   const int blk_rows = 16 * T;
   const int nblk = (rows + blk_rows - 1) / blk_rows;
-  const int nst = nxs / mf_step_chunks<QT>();  // steps of 16 (Q5_K) or 8 (Q6_K) chunks
+  const int nst = nxs / mf_step_chunks<QT>();  // steps of two superblocks
   const int st0 = s * nst / S, st1 = (s + 1) * nst / S;
   const int cbase = kbeg / XCHUNK;
   const int aoff = g * 12 + (n >> 2) * 3 + min(n & 3, 2);  // this lane's A entry within a chunk
@@ -672,19 +680,28 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(GemvArgs a, int kparts) {
       const uint2 av = ldig[(cc + j) * MF_DSTR + aoff];
       A[j] = ((uint64_t)av.x | ((uint64_t)av.y << 32)) & amask;
     }
-    if constexpr (QT == Q5_K) {
+    if constexpr (QT == Q4_K || QT == Q5_K) {
       const float xs[4] = {d01.y, d01.w, d23.y, d23.w};
-      // fifth bits of this quarter's chunks, from lane group qq of the same row
-      const int src = n + 16 * qq;
-      const uint32_t qh[4] = {lane_fetch(src, r.qh.x), lane_fetch(src, r.qh.y), lane_fetch(src, r.qh.z),
-                              lane_fetch(src, r.qh.w)};
       qwg_i32x4 D[4];
+      if constexpr (QT == Q5_K) {
+        // fifth bits of this quarter's chunks, from lane group qq of the same row
+        const int src = n + 16 * qq;
+        const uint32_t qh[4] = {lane_fetch(src, r.qh.x), lane_fetch(src, r.qh.y), lane_fetch(src, r.qh.z),
+                                lane_fetch(src, r.qh.w)};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t l5 = __builtin_rotateright32(qh[j], rot_lo), h5 = __builtin_rotateright32(qh[j], rot_hi);
-        const uint32_t lo = (R[j] & 0x0F0F0F0Fu) | (l5 & 0x10101010u);
-        const uint32_t hi = ((R[j] >> 4) & 0x0F0F0F0Fu) | (h5 & 0x10101010u);
-        D[j] = mfma_i8(A[j], (uint64_t)lo | ((uint64_t)hi << 32));
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t l5 = __builtin_rotateright32(qh[j], rot_lo), h5 = __builtin_rotateright32(qh[j], rot_hi);
+          const uint32_t lo = (R[j] & 0x0F0F0F0Fu) | (l5 & 0x10101010u);
+          const uint32_t hi = ((R[j] >> 4) & 0x0F0F0F0Fu) | (h5 & 0x10101010u);
+          D[j] = mfma_i8(A[j], (uint64_t)lo | ((uint64_t)hi << 32));
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {  // the stored nibbles are q XOR 8: flip back to q in 0..15
+          const uint32_t lo = (R[j] & 0x0F0F0F0Fu) ^ 0x08080808u;
+          const uint32_t hi = ((R[j] >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;
+          D[j] = mfma_i8(A[j], (uint64_t)lo | ((uint64_t)hi << 32));
+        }
       }
       const uint64_t ps = (uint64_t)hv.x | ((uint64_t)hv.y << 32);
       const uint64_t pm = (uint64_t)hv.z | ((uint64_t)hv.w << 32);
@@ -733,7 +750,7 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(GemvArgs a, int kparts) {
   };
   constexpr int SC = mf_step_chunks<QT>();
   auto step = [&](const MfRaw<QT>& r, int st, float& acc) {
-    if constexpr (QT == Q5_K) {
+    if constexpr (QT == Q4_K || QT == Q5_K) {
 #pragma unroll
       for (int sbk = 0; sbk < 2; ++sbk) {  // the step's two superblocks: header from lane group sbk
         const int src = n + 16 * sbk;
@@ -834,7 +851,7 @@ hipError_t launch_digitize(const float* x, int64_t x_stride, const float* gain, 
                            int64_t out_stride_bytes, float* sq, int64_t sq_stride, hipStream_t st) {
   const int64_t nx = k / XCHUNK;
   hipLaunchKernelGGL(k_digitize, dim3((unsigned)((nx + 63) / 64), nc), dim3(256), 0, st, x, x_stride, gain, (int)k,
-                     digit_kind(qt), (uint32_t*)out, out_stride_bytes / 4, sq, sq_stride);
+                     gemv_digit_kind(qt, k, nc), (uint32_t*)out, out_stride_bytes / 4, sq, sq_stride);
   return hipGetLastError();
 }
 
@@ -859,6 +876,10 @@ constexpr int MF_WAVES = 16;  // waves per workgroup of the matrix-core form (fo
 // Matrix-core plan: K splits as LDS requires (a power of two, so the splits' grids tile the 256 CUs),
 // then the K parts per tile S in {1, 2, 4, 8, 16} that minimise rounds x steps per wave, where a
 // round is one block per workgroup and a workgroup runs on each CU.
+int gemv_digit_kind(int qt, int64_t k, int nc) {
+  return plan_gemv(qt, 1, k, nc, EPI_STORE).mfma ? DIG_BYTE : digit_kind(qt);
+}
+
 static GemvPlan plan_mfma(int64_t rows, int64_t k, int nc) {
   const int64_t unit = 16;  // chunks per step (two superblocks): splits hold whole steps
   GemvPlan p{};
@@ -898,7 +919,7 @@ static GemvPlan plan_mfma(int64_t rows, int64_t k, int nc) {
 static bool two_pass_ok(int qt) { return qt == Q4_0 || qt == Q4_K || qt == Q8_0; }
 
 GemvPlan plan_gemv(int qt, int64_t rows, int64_t k, int nc, int epi, int mfma) {
-  if ((mfma < 0 ? g_mfma : mfma) && nc >= 2 && nc <= 4 && (qt == Q5_K || qt == Q6_K) &&
+  if ((mfma < 0 ? g_mfma : mfma) && nc >= 2 && nc <= 4 && (qt == Q4_K || qt == Q5_K || qt == Q6_K) &&
       k % 512 == 0)  // steps are two superblocks
     return plan_mfma(rows, k, nc);
   // the RoPE and SwiGLU epilogues combine rows (2i, 2i+1), which must sit in one wave
@@ -1130,10 +1151,14 @@ hipError_t launch_gemv(int qt, const MatView& w, int64_t k, const void* xd, int6
   const Dispatch d1{st, ev_start, p.ksplit == 1 ? ev_stop : nullptr};
   hipError_t err;
   if (p.mfma) {
-    if (qt != Q5_K && qt != Q6_K) return hipErrorInvalidValue;
     if (e.xf || nc < 1 || nc > 4) return hipErrorInvalidValue;
     grid.x = p.grid_x;
-    err = qt == Q5_K ? launch_mfma<Q5_K>(a, epi, p, grid, block, d1) : launch_mfma<Q6_K>(a, epi, p, grid, block, d1);
+    switch (qt) {
+      case Q4_K: err = launch_mfma<Q4_K>(a, epi, p, grid, block, d1); break;
+      case Q5_K: err = launch_mfma<Q5_K>(a, epi, p, grid, block, d1); break;
+      case Q6_K: err = launch_mfma<Q6_K>(a, epi, p, grid, block, d1); break;
+      default: return hipErrorInvalidValue;
+    }
   } else switch (qt) {
     case Q8_0: err = launch_fmt<Q8_0>(a, p, epi, grid, block, d1); break;
     case Q4_0: err = launch_fmt<Q4_0>(a, p, epi, grid, block, d1); break;

@@ -75,6 +75,11 @@ void set_gemv_mfma(int on);
 // Bytes of the activation digits of one column of length k (28 words per 32 elements).
 inline int64_t digit_bytes(int64_t k) { return k / XCHUNK * DIG_CHUNK_WORDS * 4; }
 
+// Digit kind (DIG_NIB / DIG_BYTE) that a GEMV over weights of type qt with K = k and nc columns
+// consumes: byte digits on the matrix cores, else the format's own kind.  Every producer of a GEMV's
+// input digits picks its kind with this.
+int gemv_digit_kind(int qt, int64_t k, int nc);
+
 // Digits of nc activation columns (x: [nc][x_stride] fp32) for a GEMV over weights of type qt;
 // with a gain vector, digits of gain * x and per-chunk sums of x^2 into sq (column stride sq_stride).
 hipError_t launch_digitize(const float* x, int64_t x_stride, const float* gain, int64_t k, int nc, int qt, void* out,

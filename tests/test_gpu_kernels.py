@@ -90,13 +90,13 @@ def test_gemv_tall_persistent(ops, qt, nc):
     assert ok.all(), (np.argwhere(~ok)[:5], y[~ok][:5], yr[~ok][:5])
 
 
-@pytest.mark.parametrize("qt", [synth.Q5_K, synth.Q6_K], ids=["Q5_K", "Q6_K"])
+@pytest.mark.parametrize("qt", [synth.Q4_K, synth.Q5_K, synth.Q6_K], ids=["Q4_K", "Q5_K", "Q6_K"])
 @pytest.mark.parametrize("shape", [(16, 256), (37, 2048), (333, 8192), (70, 28672), (2 * 4096 + 48 + 6, 512)],
                          ids=["one_tile", "ragged", "k8192", "ksplit4", "many_blocks"])
 @pytest.mark.parametrize("nc", [2, 3, 4])
 @pytest.mark.parametrize("mfma", [True, False], ids=["mfma", "dot"])
 def test_gemv_several_columns_both_forms(ops, qt, shape, nc, mfma):
-    """2..4-column Q5_K / Q6_K GEMVs on the matrix cores (tiles of 16 rows, K parts added in wave
+    """2..4-column Q4_K / Q5_K / Q6_K GEMVs on the matrix cores (tiles of 16 rows, K parts added in wave
     order, K splits through the reduction kernel) and on integer dot products: both within the row
     tolerance, for one tile, a ragged tile, 256 chunks, four K splits and more blocks than CUs."""
     rows, k = shape
