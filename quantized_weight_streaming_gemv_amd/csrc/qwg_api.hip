@@ -327,10 +327,13 @@ static MatView view_at(const uint8_t* base, const MatPlan& p) { return make_view
 
 // ---------------------------------------------------------------------------- timing helpers
 
-static hipEvent_t pool_event(std::vector<hipEvent_t>& pool, int& used) {
+// flags 0: default events; the kernel-timing events are created without the system-scope fence
+// (their times are read only after the stream has been synchronized), so recording them does not
+// write back and invalidate the caches around the kernels they time
+static hipEvent_t pool_event(std::vector<hipEvent_t>& pool, int& used, unsigned flags = 0) {
   if (used == (int)pool.size()) {
     hipEvent_t e;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&e, flags) != hipSuccess) return nullptr;
     pool.push_back(e);
   }
   return pool[used++];
@@ -415,8 +418,8 @@ static int gemv(qwg_model* m, int tensor_class, int qt, const MatView& w, const 
   const bool timed = m->timing_tensor == tensor_class;
   hipEvent_t e0 = nullptr, e1 = nullptr;
   if (timed) {
-    e0 = pool_event(m->tev, m->tev_used);
-    e1 = pool_event(m->tev, m->tev_used);
+    e0 = pool_event(m->tev, m->tev_used, hipEventDisableSystemFence);
+    e1 = pool_event(m->tev, m->tev_used, hipEventDisableSystemFence);
     if (!e0 || !e1) return fail(QWG_E_HIP, "hipEventCreate failed");
   }
   QWG_HIP(launch_gemv(qt, w, mp.L.k, m->arena + m->xd[in.buf], m->xd_col, nc, epi, e, m->f(m->part), m->cs, gp, e0,
