@@ -504,11 +504,14 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const float* part, int kspl
 // (K parts) and add their partial sums in wave order through LDS, so the result does not depend on
 // timing.  The grid is persistent over the blocks; the activation of one K split (416 B per chunk:
 // 384 B of digits, 4 x 8 B of (2^-s, 2^-s sum x_fix)) is staged once per workgroup.
-constexpr int MF_DIG = 48;            // 8-B digit entries per chunk: [word g][column][level]
-constexpr int MF_DSTR = MF_DIG + 1;   // LDS stride of a chunk's entries: 98 words, so the staging
-                                      // writes of consecutive chunks spread over the banks
-constexpr int MF_CHUNK_LDS = MF_DSTR * 8 + 4 * 8;
-constexpr int MF_FIXED_LDS = 4 * 2 * 8;  // the descriptor rows' padding (see k_gemv_mfma)
+constexpr int MF_DIG = 48;  // 8-B digit entries per chunk and group of four columns: [word g][column][level]
+// LDS stride of a chunk's entries: one entry of padding (98 or 194 words), so the staging writes of
+// consecutive chunks spread over the banks
+__host__ __device__ constexpr int mf_dig_stride(int ng) { return ng * MF_DIG + 1; }
+// LDS bytes per chunk (digit entries and one (2^-s, 2^-s sum) pair per column) and per workgroup
+// beyond the chunks (the descriptor rows' padding)
+__host__ __device__ constexpr int mf_chunk_lds(int ng) { return mf_dig_stride(ng) * 8 + 4 * ng * 8; }
+__host__ __device__ constexpr int mf_fixed_lds(int ng) { return 4 * ng * 2 * 8; }
 
 __device__ __forceinline__ void lane_swap32(uint32_t& a, uint32_t& b) {
   const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);  // lanes 32..63 of a <-> 0..31 of b
@@ -588,9 +591,13 @@ __device__ __forceinline__ MfRaw<QT> mf_load(const MatView& w, uint32_t ro, uint
   return r;
 }
 
-template <int QT, int EPI>
-__global__ __launch_bounds__(1024) void k_gemv_mfma(GemvArgs a, int kparts) {
+// NG column groups of four (NG = 2: 5..8 columns): each group is one more A operand and one more
+// MFMA per chunk (Q6_K: two) against the same B operand, processed one group after the other.
+template <int QT, int EPI, int NG>
+__global__ __launch_bounds__(NG == 1 ? 1024 : 512) void k_gemv_mfma(GemvArgs a, int kparts) {
   static_assert(QT == Q4_K || QT == Q5_K || QT == Q6_K, "K-quant formats with 32-weight chunks");
+  static_assert(NG == 1 || NG == 2, "four or eight columns");
+  constexpr int DSTR = mf_dig_stride(NG);  // 8-B digit entries per chunk in LDS: [group][word g][column][level]
   extern __shared__ uint4 lds[];
   __shared__ float red[MAX_COLS][16];
   const int tid = threadIdx.x, lane = tid & 63, nw = blockDim.x >> 6;
@@ -600,18 +607,18 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(GemvArgs a, int kparts) {
   const int split = blockIdx.y;
   const int kbeg = split * a.ks;
   const int klen = min(a.ks, a.k - kbeg);
-  const int nxs = klen / XCHUNK;  // chunks of this split (a multiple of 8)
+  const int nxs = klen / XCHUNK;  // chunks of this split (a multiple of 16)
   const int nxp = a.ks / XCHUNK;  // LDS capacity in chunks
   const int xbase = kbeg / XCHUNK;
-  // LDS: digit entries [nxp][MF_DSTR]; per column a row of (2^-s, 2^-s sum x_fix) per chunk, rows
-  // nxp + 2 apart (the four columns' rows then start on different banks); K-part partial sums
+  // LDS: digit entries [nxp][DSTR]; per column a row of (2^-s, 2^-s sum x_fix) per chunk, rows
+  // nxp + 2 apart (the columns' rows then start on different banks); K-part partial sums
   const int dstr = nxp + 2;
   uint2* ldig = (uint2*)lds;
-  float2* ldesc = (float2*)(ldig + (size_t)nxp * MF_DSTR);
-  float* lpart = (float*)(ldesc + 4 * dstr);                // [nw][64]
+  float2* ldesc = (float2*)(ldig + (size_t)nxp * DSTR);
+  float* lpart = (float*)(ldesc + 4 * NG * dstr);           // [NG][nw][64]
 
   // 1. stage the split's digits: one (column, chunk) per thread; columns >= nc are zeros
-  for (int job = tid; job < 4 * nxs; job += blockDim.x) {
+  for (int job = tid; job < 4 * NG * nxs; job += blockDim.x) {
     const int col = job / nxs, c = job - col * nxs;
     uint32_t wd[DIG_CHUNK_WORDS];
     if (col < nc) {
@@ -628,11 +635,11 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(GemvArgs a, int kparts) {
 #pragma unroll
       for (int i = 0; i < DIG_CHUNK_WORDS; ++i) wd[i] = 0;
     }
+    const int ent = c * DSTR + (col >> 2) * MF_DIG + (col & 3) * 3;
 #pragma unroll
     for (int gg = 0; gg < 4; ++gg)
 #pragma unroll
-      for (int lv = 0; lv < 3; ++lv)
-        ldig[c * MF_DSTR + gg * 12 + col * 3 + lv] = make_uint2(wd[gg * 3 + lv], wd[12 + gg * 3 + lv]);
+      for (int lv = 0; lv < 3; ++lv) ldig[ent + gg * 12 + lv] = make_uint2(wd[gg * 3 + lv], wd[12 + gg * 3 + lv]);
     const float inv = __uint_as_float(wd[DIG_WORDS]);
     ldesc[col * dstr + c] = make_float2(inv, inv * (float)(int32_t)wd[DIG_WORDS + 1]);
   }
@@ -648,16 +655,17 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(GemvArgs a, int kparts) {
   const int nst = nxs / mf_step_chunks<QT>();  // steps of two superblocks
   const int st0 = s * nst / S, st1 = (s + 1) * nst / S;
   const int cbase = kbeg / XCHUNK;
-  const int aoff = g * 12 + (n >> 2) * 3 + min(n & 3, 2);  // this lane's A entry within a chunk
+  const int aoff = g * 12 + (n >> 2) * 3 + min(n & 3, 2);  // this lane's A entry within a group
   const uint64_t amask = (n & 3) == 3 ? 0ull : ~0ull;       // level 3 is zero
   // per-lane bit-move amounts: Q5_K fifth bits (rotations), Q6_K high pairs (shifts)
   const uint32_t rot_lo = (uint32_t)(28 + 2 * g) & 31u, rot_hi = (uint32_t)(29 + 2 * g) & 31u;
   const uint32_t shl_lo = (g & 1) ? 2u : 6u, shl_hi = (g & 1) ? 0u : 4u;
 
   // quarter qq (chunks c0 + 4 qq .. + 3) of a step: quant words transposed across the lane groups,
-  // four (Q6_K: eight) MFMAs, then the (row n, column g) updates.  hv: the Q5_K superblock header of
-  // this quarter (fetched by the caller from the lane group that loaded it).
-  auto quarter = [&](const MfRaw<QT>& r, int c0, int qq, const uint4& hv, float& acc) {
+  // the B operands and weight scales of the four chunks, then per column group the A operands,
+  // four (Q6_K: eight) MFMAs and the (row n, column 4 cg + g) updates.  hv: the K-quant superblock
+  // header of this quarter (fetched by the caller from the lane group that loaded it).
+  auto quarter = [&](const MfRaw<QT>& r, int c0, int qq, const uint4& hv, float* acc) {
     const uint4 qv = r.q[qq];
     // the swaps overwrite both operands: copy the loaded words here, where they are used (left to
     // register allocation, the copies sat right after the next step's loads and waited for them)
@@ -671,18 +679,26 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(GemvArgs a, int kparts) {
     lane_swap16(R[0], R[1]);
     lane_swap16(R[2], R[3]);  // R[j] = quant word g of chunk c0 + 4 qq + j
     const int cc = c0 + 4 * qq;
-    const float4 d01 = *(const float4*)&ldesc[g * dstr + cc];
-    const float4 d23 = *(const float4*)&ldesc[g * dstr + cc + 2];
-    const float inv[4] = {d01.x, d01.z, d23.x, d23.z};
+    // A operands and activation scales of column group cg (columns 4 cg .. 4 cg + 3)
     uint64_t A[4];
+    float4 d01, d23;
+    auto load_group = [&](int cg) {
+      d01 = *(const float4*)&ldesc[(4 * cg + g) * dstr + cc];
+      d23 = *(const float4*)&ldesc[(4 * cg + g) * dstr + cc + 2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint2 av = ldig[(cc + j) * MF_DSTR + aoff];
-      A[j] = ((uint64_t)av.x | ((uint64_t)av.y << 32)) & amask;
-    }
+      for (int j = 0; j < 4; ++j) {
+        const uint2 av = ldig[(cc + j) * DSTR + cg * MF_DIG + aoff];
+        A[j] = ((uint64_t)av.x | ((uint64_t)av.y << 32)) & amask;
+      }
+    };
+    load_group(0);
+    // B operands (the quants of word g as bytes; Q6_K: the two 16-weight halves separately), each
+    // multiplied as soon as it is formed, then the chunk's weight scales (Q4_K / Q5_K: d sc and
+    // -dmin m; Q6_K: d sc / 4 of both halves)
+    uint64_t B0[4], B1[4];
+    float w0[4], w1[4];
+    qwg_i32x4 D[4], E[4];
     if constexpr (QT == Q4_K || QT == Q5_K) {
-      const float xs[4] = {d01.y, d01.w, d23.y, d23.w};
-      qwg_i32x4 D[4];
       if constexpr (QT == Q5_K) {
         // fifth bits of this quarter's chunks, from lane group qq of the same row
         const int src = n + 16 * qq;
@@ -693,14 +709,16 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(GemvArgs a, int kparts) {
           const uint32_t l5 = __builtin_rotateright32(qh[j], rot_lo), h5 = __builtin_rotateright32(qh[j], rot_hi);
           const uint32_t lo = (R[j] & 0x0F0F0F0Fu) | (l5 & 0x10101010u);
           const uint32_t hi = ((R[j] >> 4) & 0x0F0F0F0Fu) | (h5 & 0x10101010u);
-          D[j] = mfma_i8(A[j], (uint64_t)lo | ((uint64_t)hi << 32));
+          B0[j] = (uint64_t)lo | ((uint64_t)hi << 32);
+          D[j] = mfma_i8(A[j], B0[j]);
         }
       } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {  // the stored nibbles are q XOR 8: flip back to q in 0..15
           const uint32_t lo = (R[j] & 0x0F0F0F0Fu) ^ 0x08080808u;
           const uint32_t hi = ((R[j] >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;
-          D[j] = mfma_i8(A[j], (uint64_t)lo | ((uint64_t)hi << 32));
+          B0[j] = (uint64_t)lo | ((uint64_t)hi << 32);
+          D[j] = mfma_i8(A[j], B0[j]);
         }
       }
       const uint64_t ps = (uint64_t)hv.x | ((uint64_t)hv.y << 32);
@@ -709,31 +727,25 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(GemvArgs a, int kparts) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int sb = 4 * (qq & 1) + j;  // sub-block of the superblock
-        const float dsc = dd * (float)((uint32_t)(ps >> (6 * sb)) & 63u);
-        const float dmm = dm * (float)((uint32_t)(pm >> (6 * sb)) & 63u);
-        acc = __builtin_fmaf(inv[j] * dsc, mf_value(D[j]), acc);
-        acc = __builtin_fmaf(-dmm, xs[j], acc);
+        w0[j] = dd * (float)((uint32_t)(ps >> (6 * sb)) & 63u);
+        w1[j] = -(dm * (float)((uint32_t)(pm >> (6 * sb)) & 63u));
       }
     } else {
       // high-bit pairs of chunk 4 qq + j: words (x, y) of qhA (qq < 2) or qhB held by lane group
       // (2 qq + j / 2) & 3; rows take x for word groups 0, 1 and y for 2, 3
       const int src0 = n + 16 * ((2 * qq) & 3), src1 = n + 16 * ((2 * qq + 1) & 3);
       const uint4 qp = qq < 2 ? r.qhA : r.qhB;
-      uint32_t hq[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int src = (j >> 1) ? src1 : src0;
         const uint32_t hx = lane_fetch(src, (j & 1) ? qp.z : qp.x), hy = lane_fetch(src, (j & 1) ? qp.w : qp.y);
-        hq[j] = g < 2 ? hx : hy;
-      }
-      qwg_i32x4 DA[4], DB[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t h = hq[j];
+        const uint32_t h = g < 2 ? hx : hy;
         const uint32_t lo = ((R[j] << 2) & 0x3C3C3C3Cu) | ((h << shl_lo) & 0xC0C0C0C0u);
         const uint32_t hi = ((R[j] >> 2) & 0x3C3C3C3Cu) | ((h << shl_hi) & 0xC0C0C0C0u);
-        DA[j] = mfma_i8(A[j], (uint64_t)lo);
-        DB[j] = mfma_i8(A[j], (uint64_t)hi << 32);
+        B0[j] = (uint64_t)lo;
+        B1[j] = (uint64_t)hi << 32;
+        D[j] = mfma_i8(A[j], B0[j]);
+        E[j] = mfma_i8(A[j], B1[j]);
       }
       const float dq = 0.25f * half_bits_to_float((r.dw >> (16 * (qq >> 1))) & 0xFFFFu);
       // sub-block scales of this quarter's chunks, from lane group qq
@@ -741,15 +753,41 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(GemvArgs a, int kparts) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t w = scw[j >> 1] >> (16 * (j & 1));
-        const float dA = dq * (float)(int32_t)(int8_t)(uint8_t)(w & 0xFFu);
-        const float dB = dq * (float)(int32_t)(int8_t)(uint8_t)((w >> 8) & 0xFFu);
-        acc = __builtin_fmaf(inv[j] * dA, mf_value(DA[j]), acc);
-        acc = __builtin_fmaf(inv[j] * dB, mf_value(DB[j]), acc);
+        w0[j] = dq * (float)(int32_t)(int8_t)(uint8_t)(w & 0xFFu);
+        w1[j] = dq * (float)(int32_t)(int8_t)(uint8_t)((w >> 8) & 0xFFu);
       }
+    }
+    // (row n, column 4 cg + g) updates from this group's products
+    auto consume = [&](float& a_) {
+      const float inv[4] = {d01.x, d01.z, d23.x, d23.z};
+      if constexpr (QT == Q4_K || QT == Q5_K) {
+        const float xs[4] = {d01.y, d01.w, d23.y, d23.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          a_ = __builtin_fmaf(inv[j] * w0[j], mf_value(D[j]), a_);
+          a_ = __builtin_fmaf(w1[j], xs[j], a_);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          a_ = __builtin_fmaf(inv[j] * w0[j], mf_value(D[j]), a_);
+          a_ = __builtin_fmaf(inv[j] * w1[j], mf_value(E[j]), a_);
+        }
+      }
+    };
+    consume(acc[0]);
+    if constexpr (NG == 2) {
+      load_group(1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        D[j] = mfma_i8(A[j], B0[j]);
+        if constexpr (QT == Q6_K) E[j] = mfma_i8(A[j], B1[j]);
+      }
+      consume(acc[1]);
     }
   };
   constexpr int SC = mf_step_chunks<QT>();
-  auto step = [&](const MfRaw<QT>& r, int st, float& acc) {
+  auto step = [&](const MfRaw<QT>& r, int st, float* acc) {
     if constexpr (QT == Q4_K || QT == Q5_K) {
 #pragma unroll
       for (int sbk = 0; sbk < 2; ++sbk) {  // the step's two superblocks: header from lane group sbk
@@ -771,7 +809,9 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(GemvArgs a, int kparts) {
     const int row = min(r0 + n, rows - 1);  // rows past the end read the last row; results dropped
     const uint32_t ro = row_off(QT, a.w, row), srow = slot_row(a.w.ilv, a.w.nch, row);
     auto load = [&](int st) { return mf_load<QT>(a.w, ro, srow, cbase + SC * min(st, nst - 1), g); };
-    float acc = 0.f;
+    float acc[NG];
+#pragma unroll
+    for (int cg = 0; cg < NG; ++cg) acc[cg] = 0.f;
     // two buffers in rotation: the next step's loads are in flight while one is computed (loads past
     // the part's end re-read its last step, in bounds and unused)
     MfRaw<QT> b0 = load(st0), b1;
@@ -788,26 +828,34 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(GemvArgs a, int kparts) {
     }
     if (st < st1) step(b0, st, acc);
 
-    // 3. the tile's K parts in wave order, then the epilogue for (row r0 + n, column g)
+    // 3. the tile's K parts in wave order, then the epilogue for (row r0 + n, column 4 cg + g)
     if (S > 1) {
-      lpart[wave * 64 + lane] = acc;
+#pragma unroll
+      for (int cg = 0; cg < NG; ++cg) lpart[(cg * nw + wave) * 64 + lane] = acc[cg];
       __syncthreads();
       if (s == 0) {
-        float v = 0.f;
-        for (int i = 0; i < S; ++i) v += lpart[(wave + i) * 64 + lane];
-        acc = v;
+#pragma unroll
+        for (int cg = 0; cg < NG; ++cg) {
+          float v = 0.f;
+          for (int i = 0; i < S; ++i) v += lpart[(cg * nw + wave + i) * 64 + lane];
+          acc[cg] = v;
+        }
       }
     }
     if (s == 0) {
       const int orow = r0 + n;
-      const bool ok = orow < rows && g < nc;
-      float v = acc;
-      if (EPI == EPI_PART) {
-        if (ok) a.part[((int64_t)split * nc + g) * rows + orow] = v;
-      } else {
-        if (a.e.sq_in) v *= rms_scale(a.e, red, min(g, nc - 1));
-        const float vp = __shfl_xor(v, 1);  // row n ^ 1, same column
-        if (ok) run_epilogue(EPI, a.e, g, orow, v, vp);
+#pragma unroll
+      for (int cg = 0; cg < NG; ++cg) {
+        const int col = 4 * cg + g;
+        const bool ok = orow < rows && col < nc;
+        float v = acc[cg];
+        if (EPI == EPI_PART) {
+          if (ok) a.part[((int64_t)split * nc + col) * rows + orow] = v;
+        } else {
+          if (a.e.sq_in) v *= rms_scale(a.e, red, min(col, nc - 1));
+          const float vp = __shfl_xor(v, 1);  // row n ^ 1, same column
+          if (ok) run_epilogue(EPI, a.e, col, orow, v, vp);
+        }
       }
     }
     if (S > 1) __syncthreads();  // lpart is reused by the next block
@@ -871,7 +919,9 @@ void set_gemv_geometry(int waves, int rows_per_wave, int depth, int passes) {
 static int g_mfma = 1;  // several-column Q5_K / Q6_K GEMVs on the matrix cores
 void set_gemv_mfma(int on) { g_mfma = on ? 1 : 0; }
 
-constexpr int MF_WAVES = 16;  // waves per workgroup of the matrix-core form (four per SIMD)
+// waves per workgroup of the matrix-core form: four per SIMD with one column group (128 VGPRs), two
+// with two (their operands need up to 256)
+constexpr int mf_waves(int ng) { return ng == 1 ? 16 : 8; }
 
 // Matrix-core plan: K splits as LDS requires (a power of two, so the splits' grids tile the 256 CUs),
 // then the K parts per tile S in {1, 2, 4, 8, 16} that minimise rounds x steps per wave, where a
@@ -882,29 +932,30 @@ int gemv_digit_kind(int qt, int64_t k, int nc) {
 
 static GemvPlan plan_mfma(int64_t rows, int64_t k, int nc) {
   const int64_t unit = 16;  // chunks per step (two superblocks): splits hold whole steps
+  const int ng = nc > 4 ? 2 : 1;
   GemvPlan p{};
   p.mfma = 1;
-  p.ncm = 4;
-  p.waves = MF_WAVES;
+  p.ncm = 4 * ng;
+  p.waves = mf_waves(ng);
   p.rows_per_wave = 16;
   p.depth = 1;
   p.passes = 0;
   const int64_t nx = k / XCHUNK;
-  const size_t fixed = (size_t)MF_WAVES * 64 * 4 + MF_FIXED_LDS;  // K parts' partial sums, padding
-  int64_t max_x = (int64_t)((LDS_BUDGET - fixed) / MF_CHUNK_LDS) / unit * unit;
+  const size_t fixed = (size_t)ng * mf_waves(ng) * 64 * 4 + mf_fixed_lds(ng);  // K parts' partial sums, padding
+  int64_t max_x = (int64_t)((LDS_BUDGET - fixed) / mf_chunk_lds(ng)) / unit * unit;
   int ksplit = 1;
   while (ksplit < 64 && ((nx + ksplit - 1) / ksplit + unit - 1) / unit * unit > max_x) ksplit *= 2;
   const int64_t xs = ((nx + ksplit - 1) / ksplit + unit - 1) / unit * unit;
   p.ks = (int)(xs * XCHUNK);
   p.ksplit = (int)((k + p.ks - 1) / p.ks);
-  p.lds = (size_t)xs * MF_CHUNK_LDS + fixed;
+  p.lds = (size_t)xs * mf_chunk_lds(ng) + fixed;
   p.part_bytes = p.ksplit > 1 ? (size_t)p.ksplit * nc * rows * sizeof(float) : 0;
   const int64_t tiles = (rows + 15) / 16, nst = xs / unit;
   const int64_t G = std::max(1, PERSISTENT_WGS / p.ksplit);
   int64_t best = -1;
-  for (int S = 1; S <= MF_WAVES; S *= 2) {
+  for (int S = 1; S <= p.waves; S *= 2) {
     if (g_passes > 0 && S != g_passes) continue;  // tuning override: K parts per tile
-    const int64_t T = MF_WAVES / S, nblk = (tiles + T - 1) / T, rounds = (nblk + G - 1) / G;
+    const int64_t T = p.waves / S, nblk = (tiles + T - 1) / T, rounds = (nblk + G - 1) / G;
     const int64_t cost = rounds * ((nst + S - 1) / S + 3);
     if (best < 0 || cost < best) {
       best = cost;
@@ -919,7 +970,7 @@ static GemvPlan plan_mfma(int64_t rows, int64_t k, int nc) {
 static bool two_pass_ok(int qt) { return qt == Q4_0 || qt == Q4_K || qt == Q8_0; }
 
 GemvPlan plan_gemv(int qt, int64_t rows, int64_t k, int nc, int epi, int mfma) {
-  if ((mfma < 0 ? g_mfma : mfma) && nc >= 2 && nc <= 4 && (qt == Q4_K || qt == Q5_K || qt == Q6_K) &&
+  if ((mfma < 0 ? g_mfma : mfma) && nc >= 2 && nc <= 8 && (qt == Q4_K || qt == Q5_K || qt == Q6_K) &&
       k % 512 == 0)  // steps are two superblocks
     return plan_mfma(rows, k, nc);
   // the RoPE and SwiGLU epilogues combine rows (2i, 2i+1), which must sit in one wave
@@ -1114,18 +1165,23 @@ static hipError_t launch_fmt(const GemvArgs& a, const GemvPlan& p, int epi, dim3
   return launch_t<QT, 8, 2, 1, 0>(a, epi, p.ksplit, grid, block, lds, dd);
 }
 
-template <int QT>
-static hipError_t launch_mfma(const GemvArgs& a, int epi, const GemvPlan& p, dim3 grid, dim3 block, const Dispatch& d) {
+template <int QT, int NG>
+static hipError_t launch_mfma_ng(const GemvArgs& a, int epi, const GemvPlan& p, dim3 grid, dim3 block,
+                                 const Dispatch& d) {
   const int S = p.kparts;
   switch (p.ksplit > 1 ? EPI_PART : epi) {
-    case EPI_PART: go(d, k_gemv_mfma<QT, EPI_PART>, grid, block, p.lds, a, S); break;
-    case EPI_STORE: go(d, k_gemv_mfma<QT, EPI_STORE>, grid, block, p.lds, a, S); break;
-    case EPI_RESID: go(d, k_gemv_mfma<QT, EPI_RESID>, grid, block, p.lds, a, S); break;
-    case EPI_SWIGLU: go(d, k_gemv_mfma<QT, EPI_SWIGLU>, grid, block, p.lds, a, S); break;
-    case EPI_QKV: go(d, k_gemv_mfma<QT, EPI_QKV>, grid, block, p.lds, a, S); break;
+    case EPI_PART: go(d, k_gemv_mfma<QT, EPI_PART, NG>, grid, block, p.lds, a, S); break;
+    case EPI_STORE: go(d, k_gemv_mfma<QT, EPI_STORE, NG>, grid, block, p.lds, a, S); break;
+    case EPI_RESID: go(d, k_gemv_mfma<QT, EPI_RESID, NG>, grid, block, p.lds, a, S); break;
+    case EPI_SWIGLU: go(d, k_gemv_mfma<QT, EPI_SWIGLU, NG>, grid, block, p.lds, a, S); break;
+    case EPI_QKV: go(d, k_gemv_mfma<QT, EPI_QKV, NG>, grid, block, p.lds, a, S); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+template <int QT>
+static hipError_t launch_mfma(const GemvArgs& a, int epi, const GemvPlan& p, dim3 grid, dim3 block, const Dispatch& d) {
+  return p.ncm == 8 ? launch_mfma_ng<QT, 2>(a, epi, p, grid, block, d) : launch_mfma_ng<QT, 1>(a, epi, p, grid, block, d);
 }
 
 hipError_t launch_gemv(int qt, const MatView& w, int64_t k, const void* xd, int64_t xd_stride_bytes, int nc, int epi,
@@ -1151,7 +1207,7 @@ hipError_t launch_gemv(int qt, const MatView& w, int64_t k, const void* xd, int6
   const Dispatch d1{st, ev_start, p.ksplit == 1 ? ev_stop : nullptr};
   hipError_t err;
   if (p.mfma) {
-    if (e.xf || nc < 1 || nc > 4) return hipErrorInvalidValue;
+    if (e.xf || nc < 1 || nc > p.ncm) return hipErrorInvalidValue;
     grid.x = p.grid_x;
     switch (qt) {
       case Q4_K: err = launch_mfma<Q4_K>(a, epi, p, grid, block, d1); break;

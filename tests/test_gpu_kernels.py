@@ -93,12 +93,13 @@ def test_gemv_tall_persistent(ops, qt, nc):
 @pytest.mark.parametrize("qt", [synth.Q4_K, synth.Q5_K, synth.Q6_K], ids=["Q4_K", "Q5_K", "Q6_K"])
 @pytest.mark.parametrize("shape", [(16, 256), (37, 2048), (333, 8192), (70, 28672), (2 * 4096 + 48 + 6, 512)],
                          ids=["one_tile", "ragged", "k8192", "ksplit4", "many_blocks"])
-@pytest.mark.parametrize("nc", [2, 3, 4])
+@pytest.mark.parametrize("nc", [2, 3, 4, 5, 8])
 @pytest.mark.parametrize("mfma", [True, False], ids=["mfma", "dot"])
 def test_gemv_several_columns_both_forms(ops, qt, shape, nc, mfma):
-    """2..4-column Q4_K / Q5_K / Q6_K GEMVs on the matrix cores (tiles of 16 rows, K parts added in wave
-    order, K splits through the reduction kernel) and on integer dot products: both within the row
-    tolerance, for one tile, a ragged tile, 256 chunks, four K splits and more blocks than CUs."""
+    """2..8-column Q4_K / Q5_K / Q6_K GEMVs on the matrix cores (tiles of 16 rows, one or two column
+    groups, K parts added in wave order, K splits through the reduction kernel) and on integer dot
+    products: both within the row tolerance, for one tile, a ragged tile, 256 chunks, K splits and
+    more blocks than CUs."""
     rows, k = shape
     W = synth.matrix(synth.DEFAULT_DIST[qt], k, rows, tkey=synth.key(2, qt * 1000 + k + 5))
     x = synth.normal_f32(synth.key(2, 40 + nc), nc * k).reshape(nc, k)
