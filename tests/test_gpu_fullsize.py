@@ -9,6 +9,7 @@ configuration bench.py times (default geometry), on outputs the CPU oracle can c
     per-layer cosines and skip decisions on sampled layers (streamed and resident, near-identity
     and random), skipped layers passing h through unchanged in the next step, and streaming
     equal to residency bit for bit.
+  * 70B Q4_K prefill: one 8-column pass on the matrix cores equal to 8 one-column steps.
   * 70B Q6_K attention / Q5_K FFN, self-speculative k=3: one round; the (k+1)-column verify equal
     to k+1 single steps, acceptance consistent with the verify argmaxes, rollback of n_past, and
     sampled verify layers against the oracle.
@@ -132,6 +133,34 @@ def test_llama70b_q4_k_step_sampled_layers(qwg):
     r_next = oracle.argmax_f32(ref.astype(np.float32))
     if g_next != r_next:
         assert is_tie(ref, g_next, r_next)
+    free(m)
+
+
+@pytest.mark.timeout(600)
+def test_llama70b_q4_k_prefill_on_matrix_cores_equals_steps(qwg):
+    """At the 70B Q4_K shape, a prefill of 8 prompt tokens in one 8-column pass (the matrix-core
+    GEMVs; K = 8192 split in two, K = 28672 in eight) equals 8 one-column decode steps (the integer-dot
+    GEMVs, themselves checked against the oracle above): the next token's logits and the K/V rows
+    of the prompt positions on sampled layers."""
+    wl = synth.LLAMA70B_Q4_K
+    ctx = wl.n_prior + 16
+    m = qwg.make_model(wl, max_ctx=ctx, max_cols=8)
+    qwg.load(m, wl)
+    prompt = [(wl.first_token() + 7919 * i) % wl.vocab for i in range(8)]
+    p_next, p_logits = m.prefill(prompt, want_logits=True)
+    rows = slice(wl.n_prior, wl.n_prior + 8)
+    kv_p = {l: m.get_kv(l, wl.n_prior + 8) for l in (0, 40, 79)}
+    m.truncate(wl.n_prior)
+    for t in prompt:
+        s_next, s_logits = m.decode_step(t, want_logits=True)
+    assert m.n_past == wl.n_prior + 8
+    assert rel_l2(p_logits, s_logits) < 2e-3
+    if p_next != s_next:
+        assert is_tie(s_logits, p_next, s_next)
+    for l, (pk, pv) in kv_p.items():
+        sk, sv = m.get_kv(l, wl.n_prior + 8)
+        assert rel_l2(f16(pk[rows]), f16(sk[rows])) < 2e-3, l
+        assert rel_l2(f16(pv[rows]), f16(sv[rows])) < 2e-3, l
     free(m)
 
 
