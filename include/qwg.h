@@ -192,7 +192,8 @@ size_t qwg_model_arena_bytes(const qwg_model* m);
  * reserve of max(1 GiB, 2% of the device); host_budget 0 = 90% of MemAvailable (/proc/meminfo).
  * Layers 0 .. n_resident-1 are the resident ones, so self-speculative drafts run on them.  Outputs:
  * *n_resident; if not NULL, *arena_bytes (the arena at that placement) and *pinned_bytes (the
- * streamed images).  QWG_E_NOMEM if no placement fits (the file-backed third tier is not built).
+ * streamed images).  QWG_E_NOMEM if no placement fits (layers are not placed in the file-backed
+ * third tier automatically: see qwg_model_spill_layer).
  * With both budgets given it makes no GPU call. */
 int qwg_plan_residency(const qwg_model_desc* desc, size_t device_budget, size_t host_budget, int* n_resident,
                        size_t* arena_bytes, size_t* pinned_bytes);
