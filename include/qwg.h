@@ -101,10 +101,13 @@ int qwg_gemv(int qtype, const void* d_packed, int64_t rows, int64_t k, const flo
              void* stream);
 
 /* Launch geometry of subsequent GEMV launches in this process, for tuning; 0 keeps the default:
- *   waves_per_group  2, 4 or 8; 16 for single-column GEMVs (2 rows per wave, depth 1, <= 2 passes)
+ *   waves_per_group  2, 4 or 8; 16 for single-column GEMVs (2 rows per wave, depth 1, <= 2 passes);
+ *                    for the matrix-core form of 2..8 columns any even number up to 16 (2..4
+ *                    columns) or 8 (5..8 columns), the waves of one workgroup
  *   rows_per_wave    output rows per wave of single-column GEMVs: 1, 2 or 4
  *   pipeline_depth   iterations of weight loads in flight: 1 or 2
- *   row_passes       row blocks per workgroup of single-column residual and SwiGLU GEMVs at depth
+ *   row_passes       (matrix-core form: waves that split one 16-row tile's K, 1, 2, 4 or 8)
+ *                    row blocks per workgroup of single-column residual and SwiGLU GEMVs at depth
  *                    1: 1, 2, 4 or 8 with 2 rows per wave; 2 with 4 rows per wave for Q4_0, Q4_K
  *                    and Q8_0
  * Combinations without a compiled kernel fall back to the nearest one.  Results do not depend on

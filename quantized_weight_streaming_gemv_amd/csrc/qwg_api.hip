@@ -709,9 +709,8 @@ int qwg_gemv(int qtype, const void* d_packed, int64_t rows, int64_t k, const flo
 }
 
 int qwg_set_gemv_geometry(int waves_per_group, int rows_per_wave, int pipeline_depth, int row_passes) {
-  if (!(waves_per_group == 0 || waves_per_group == 2 || waves_per_group == 4 || waves_per_group == 8 ||
-        waves_per_group == 16))
-    return fail(QWG_E_INVAL, "waves_per_group must be 0, 2, 4, 8 or 16");
+  if (waves_per_group < 0 || waves_per_group > 16 || (waves_per_group & 1))
+    return fail(QWG_E_INVAL, "waves_per_group must be 0 or an even number up to 16");
   if (!(rows_per_wave == 0 || rows_per_wave == 1 || rows_per_wave == 2 || rows_per_wave == 4))
     return fail(QWG_E_INVAL, "rows_per_wave must be 0, 1, 2 or 4");
   if (!(pipeline_depth == 0 || pipeline_depth == 1 || pipeline_depth == 2))

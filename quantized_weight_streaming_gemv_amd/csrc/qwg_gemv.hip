@@ -937,6 +937,7 @@ static GemvPlan plan_mfma(int64_t rows, int64_t k, int nc) {
   p.mfma = 1;
   p.ncm = 4 * ng;
   p.waves = mf_waves(ng);
+  if (g_waves >= 2 && g_waves <= p.waves && g_waves % 2 == 0) p.waves = g_waves;  // tuning override
   p.rows_per_wave = 16;
   p.depth = 1;
   p.passes = 0;
@@ -952,17 +953,29 @@ static GemvPlan plan_mfma(int64_t rows, int64_t k, int nc) {
   p.part_bytes = p.ksplit > 1 ? (size_t)p.ksplit * nc * rows * sizeof(float) : 0;
   const int64_t tiles = (rows + 15) / 16, nst = xs / unit;
   const int64_t G = std::max(1, PERSISTENT_WGS / p.ksplit);
+  // A CU runs one workgroup per round: W waves = T tiles x S K parts.  Measured at the 70B shapes,
+  // a round costs about T x nst tile-steps of the CU (more waves per tile only hide latency) plus
+  // a fixed ~8, so the plan minimises rounds x (T x nst + 8) over W (8..16, or 4..8 with two column
+  // groups) and S, then prefers more waves and fewer K parts.
+  const int wmax = p.waves, wmin = wmax / 2;
   int64_t best = -1;
-  for (int S = 1; S <= p.waves; S *= 2) {
-    if (g_passes > 0 && S != g_passes) continue;  // tuning override: K parts per tile
-    const int64_t T = p.waves / S, nblk = (tiles + T - 1) / T, rounds = (nblk + G - 1) / G;
-    const int64_t cost = rounds * ((nst + S - 1) / S + 3);
-    if (best < 0 || cost < best) {
-      best = cost;
-      p.kparts = S;
-      p.grid_x = (int)std::min(nblk, G);
+  int best_w = wmax;
+  for (int W = wmax; W >= wmin; W -= 2) {
+    if (g_waves > 0 && W != p.waves) continue;  // tuning override: waves per workgroup
+    for (int S = 1; S <= W; S *= 2) {
+      if (W % S) continue;
+      if (g_passes > 0 && S != g_passes) continue;  // tuning override: K parts per tile
+      const int64_t T = W / S, nblk = (tiles + T - 1) / T, rounds = (nblk + G - 1) / G;
+      const int64_t cost = rounds * (T * nst + 8);
+      if (best < 0 || cost < best) {
+        best = cost;
+        best_w = W;
+        p.kparts = S;
+        p.grid_x = (int)std::min(nblk, G);
+      }
     }
   }
+  p.waves = best_w;
   return p;
 }
 
