@@ -32,8 +32,8 @@ HBM_PEAK_GBPS = 8000.0
 # change to them `roofline.traffic` is reported as null until the passes are taken again.
 GEMV_TRAFFIC = {
     "workload": "llama70b-q4_k-resident",
-    "sources_sha256": "6339b3c91b440fd225120359f8df8ce14bafd28d5c7ff5bf78ee5bec40ac0801",
-    "fetch_kib": 130431.50, "fetch_scale": 1.99974, "write_kib": 112.00, "write_scale": 1.00000,
+    "sources_sha256": "cc258d52c39ff6b8f15b133adc2777f78488cdf2d9e5e0e832b385d935eca10f",
+    "fetch_kib": 130420.74, "fetch_scale": 1.99975, "write_kib": 112.00, "write_scale": 1.00000,
 }
 GEMV_SOURCES = ("qwg_gemv.hip", "qwg_formats.h", "qwg_kernels.h")
 
