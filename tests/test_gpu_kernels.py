@@ -156,7 +156,8 @@ def test_rope_table_and_kernel(ops):
 
 
 @pytest.mark.parametrize("nq,nkv,npos,nc", [(4, 2, 1, 1), (8, 2, 100, 1), (8, 2, 100, 4), (64, 8, 2049, 1),
-                                            (64, 8, 4097, 4), (32, 8, 513, 1), (16, 2, 70, 8)])
+                                            (64, 8, 4097, 4), (32, 8, 513, 1), (16, 2, 70, 8), (8, 2, 33, 2),
+                                            (16, 2, 70, 3), (64, 8, 257, 5)])
 def test_attention(ops, nq, nkv, npos, nc):
     hd = 128
     ctx = npos + nc - 1
