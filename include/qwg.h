@@ -115,8 +115,9 @@ int qwg_gemv(int qtype, const void* d_packed, int64_t rows, int64_t k, const flo
  * thread launches GEMVs. */
 int qwg_set_gemv_geometry(int waves_per_group, int rows_per_wave, int pipeline_depth, int row_passes);
 
-/* Form of subsequent 2..4-column GEMVs over Q5_K and Q6_K weights (the multi-column verify step of
- * self-speculative decoding, [NT] "Key features"): on = 1 (the default) runs them on the matrix
+/* Form of subsequent 2..8-column GEMVs over Q4_K, Q5_K and Q6_K weights with K a multiple of 512
+ * (the multi-column verify step of self-speculative decoding, [NT] "Key features", and chunked
+ * prefill): on = 1 (the default) runs them on the matrix
  * cores (v_mfma_i32_16x16x32_i8 over the activation's byte digits), on = 0 on the integer dot
  * products of the one-column kernel.  Both are exact integer products recombined in fp32, within
  * the same row tolerance.  Other formats and column counts always take the integer dot products.

@@ -24,7 +24,10 @@
 //     or RoPE + fp16 KV append), and for the residual and SwiGLU epilogues the workgroup can also
 //     digitize its slice of the output vector for the next GEMV (whole 32-element chunks);
 //   * K splits (when the activation for all columns does not fit the LDS budget) write partial
-//     sums that a second kernel adds in a fixed order, so results never depend on timing.
+//     sums that a second kernel adds in a fixed order, so results never depend on timing;
+//   * 2..8 columns of Q4_K, Q5_K and Q6_K (self-speculative verify, chunked prefill) take the
+//     matrix-core kernel k_gemv_mfma instead: one v_mfma_i32_16x16x32_i8 per 16-row tile and
+//     chunk over byte digits of every column (its own section below).
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -484,8 +487,9 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const float* part, int kspl
 
 // ------------------------------------------------------------------ several columns on the matrix cores
 //
-// The verify pass of self-speculative decoding multiplies one weight matrix by k+1 = 2..4 activation
-// columns ([NT] "Key features": self-speculative decoding), and prefill a few prompt tokens at once.
+// The verify pass of self-speculative decoding multiplies one weight matrix by k+1 activation columns
+// ([NT] "Key features": self-speculative decoding), and chunked prefill up to 8 prompt tokens at once.
+// This form takes 2..8 columns (one or two groups of four) when K is a multiple of 512.
 // For Q4_K, Q5_K and Q6_K (with byte activation digits: the producers of this kernel's input pick
 // the kind with gemv_digit_kind) each 16-row tile and 32-weight chunk is one v_mfma_i32_16x16x32_i8 with
 //   A (16 x 32): activation digits, slot m = 4 * column + level (level 3 is zero),

@@ -66,7 +66,8 @@ struct GemvPlan {
 };
 
 // epi: the epilogue the GEMV will run (pairs of rows must share a wave for RoPE and SwiGLU);
-// mfma: 1 = the matrix-core form where one exists (2..4 columns of Q5_K / Q6_K), 0 = integer dot
+// mfma: 1 = the matrix-core form where one exists (2..8 columns of Q4_K / Q5_K / Q6_K with K a
+// multiple of 512), 0 = integer dot
 // products only, -1 = the process-wide choice (set_gemv_mfma, on by default)
 GemvPlan plan_gemv(int qt, int64_t rows, int64_t k, int nc, int epi, int mfma = -1);
 void set_gemv_geometry(int waves, int rows_per_wave, int depth, int passes);

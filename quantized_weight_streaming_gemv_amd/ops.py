@@ -79,7 +79,8 @@ def set_gemv_geometry(waves_per_group: int = 0, rows_per_wave: int = 0, pipeline
 
 
 def set_gemv_mfma(on: bool) -> None:
-    """Several-column (2..4) Q5_K / Q6_K GEMVs on the matrix cores (True, the default) or on integer dot products."""
+    """Several-column (2..8) Q4_K / Q5_K / Q6_K GEMVs on the matrix cores (True, the default) or on integer dot
+    products."""
     call("qwg_set_gemv_mfma", 1 if on else 0)
 
 
