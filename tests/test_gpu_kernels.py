@@ -123,6 +123,26 @@ def test_gemv_q8_0_4096_full(ops):
     assert gemv_ok(y, yr, ar).all()
 
 
+@pytest.mark.parametrize("qt", [synth.Q8_0, synth.Q4_0, synth.Q4_K, synth.Q6_K],
+                         ids=lambda q: synth.QTYPE_NAMES[q])
+@pytest.mark.parametrize("nc", [1, 4])
+def test_gemv_size_limits(ops, qt, nc):
+    """K = 65536 (the largest K the library takes) within the row bound, on the one-column kernel and
+    on the several-column form (matrix cores for the K-quants); 0 rows leaves the output alone."""
+    from quantized_weight_streaming_gemv_amd import QwgError
+    rows, k = 5, 65536
+    W = synth.matrix(synth.DEFAULT_DIST[qt], k, rows, tkey=synth.key(2, qt * 1000 + 3))
+    x = synth.normal_f32(synth.key(2, 40 + nc), nc * k).reshape(nc, k)
+    y = ops.gemv(qt, packed_of(ops, qt, W, rows, k), rows, k, dev(x)).cpu().numpy()
+    yr, ar = oracle.gemv(qt, W, rows, k, x)
+    assert gemv_ok(y, yr, ar).all()
+    out = torch.full((nc, 4), 7.0, dtype=torch.float32, device=DEV)
+    ops.gemv(qt, torch.zeros(256, dtype=torch.uint8, device=DEV), 0, 256, dev(x[:, :256]), out=out)
+    assert (out == 7.0).all().item()
+    with pytest.raises(QwgError):
+        ops.gemv(qt, torch.zeros(1 << 20, dtype=torch.uint8, device=DEV), 1, k + 256, torch.zeros(k + 256, device=DEV))
+
+
 def test_gemv_rejects_bad_shapes(ops):
     from quantized_weight_streaming_gemv_amd import QwgError
     W = torch.zeros(1024, dtype=torch.uint8, device=DEV)
