@@ -761,7 +761,9 @@ int qwg_rope_table(int max_pos, int head_dim, double base, float* h_table) {
 
 int qwg_rope(float* d_v, int n_heads, int head_dim, const float* d_table, int pos, void* stream) {
   if (!d_v || !d_table) return fail(QWG_E_INVAL, "NULL pointer");
-  if (head_dim != HEAD_DIM || n_heads < 1 || pos < 0) return fail(QWG_E_SHAPE, "head_dim must be 128");
+  if (head_dim != HEAD_DIM) return fail(QWG_E_SHAPE, "head_dim must be 128");
+  if (n_heads < 1 || pos < 0) return fail(QWG_E_SHAPE, "n_heads must be positive and pos non-negative");
+  if (((uintptr_t)d_v & 7) || ((uintptr_t)d_table & 7)) return fail(QWG_E_INVAL, "pointers must be 8-byte aligned");
   QWG_HIP(launch_rope(d_v, n_heads, d_table, pos, (hipStream_t)stream));
   return QWG_OK;
 }
@@ -782,6 +784,8 @@ int qwg_attn_decode(const float* d_q, const uint16_t* d_kc, const uint16_t* d_vc
   if (n_q / n_kv * n_cols > 64) return fail(QWG_E_SHAPE, "(n_q / n_kv) * n_cols must be <= 64");
   const AttnPlan p = plan_attn(n_pos, n_q, n_kv, n_cols);
   if (work_bytes < p.work_bytes) return fail(QWG_E_NOMEM, "work buffer smaller than qwg_attn_work_bytes");
+  if (!aligned16(d_q) || !aligned16(d_kc) || !aligned16(d_vc) || ((uintptr_t)d_out & 7) || ((uintptr_t)d_work & 7))
+    return fail(QWG_E_INVAL, "d_q, d_kc, d_vc must be 16-byte aligned, d_out and d_work 8-byte aligned");
   QWG_HIP(launch_attn(d_q, (int64_t)n_q * HEAD_DIM, d_kc, d_vc, (int64_t)n_kv * HEAD_DIM, n_pos, n_q, n_kv, n_cols,
                       d_out, (int64_t)n_q * HEAD_DIM, d_work, p, (hipStream_t)stream));
   return QWG_OK;

@@ -66,3 +66,27 @@ def test_model_create_validates_without_gpu():
     assert L.qwg_model_create(ctypes.byref(bad2), ctypes.byref(h)) == -2
     bad3 = _lib.ModelDesc(2, 512, 4, 2, 128, 1536, 1000, 64, 5e5, 1e-5, -1, 7, 12, 12, 12, 4)
     assert L.qwg_model_create(ctypes.byref(bad3), ctypes.byref(h)) == -6
+
+
+def test_pointer_checks_without_gpu():
+    """Misaligned or NULL device pointers are refused before anything reaches the GPU (the addresses
+    below are never dereferenced)."""
+    from quantized_weight_streaming_gemv_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libqwg.so not built")
+    L = _lib.lib()
+    A, M = 1 << 20, (1 << 20) + 4  # aligned / misaligned fake addresses
+    assert L.qwg_gemv(12, M, 16, 256, A, 1, A, None) == -1
+    assert L.qwg_gemv(12, A, 16, 256, M, 1, A, None) == -1
+    assert L.qwg_gemv(12, None, 16, 256, A, 1, A, None) == -1
+    assert L.qwg_dequantize(12, A, 16, 256, M, None) == -1
+    wb = L.qwg_attn_work_bytes(100, 8, 2, 128, 1)
+    assert wb > 0
+    for bad in range(5):
+        p = [A] * 5
+        p[bad] = M
+        assert L.qwg_attn_decode(p[0], p[1], p[2], 100, 8, 2, 128, 1, p[3], p[4], wb, None) == -1, bad
+    assert L.qwg_attn_decode(A, A, A, 100, 8, 2, 128, 1, A, A, wb - 8, None) == -3
+    assert L.qwg_rope(M, 8, 128, A, 0, None) == -1
+    assert L.qwg_rope(A, 8, 128, A, -1, None) == -2
+    assert L.qwg_rope(A, 8, 64, A, 0, None) == -2
