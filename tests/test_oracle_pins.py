@@ -260,6 +260,27 @@ def test_attention_two_positions_closed_form():
     assert abs(o[0] - p0) < 1e-15 and abs(o[1] - (1 - p0)) < 1e-15
 
 
+def test_attention_ignores_cache_rows_at_and_past_n_pos():
+    """Only positions 0 .. n_pos - 1 count: rows from n_pos on hold keys that would dominate the
+    softmax and values far from the rest, yet the output equals that of a cache cut at n_pos, and
+    admitting one more position changes it."""
+    nq, nkv, hd, n_pos, ctx = 4, 2, 128, 3, 6
+    kc = synth.normal_f16(synth.key(3, 8), ctx * nkv * hd).reshape(ctx, nkv, hd)
+    vc = synth.normal_f16(synth.key(3, 9), ctx * nkv * hd).reshape(ctx, nkv, hd)
+    q = synth.normal_f32(synth.key(3, 10), nq * hd)
+    big = oracle.half_from_double(60000.0)
+    for t in range(n_pos, ctx):  # k_t = 60000 sign(q) per head group: scores far above the others
+        for g in range(nkv):
+            qh = q[(g * (nq // nkv)) * hd:(g * (nq // nkv) + 1) * hd]
+            kc[t, g] = np.where(qh >= 0, big, big | 0x8000).astype(np.uint16)
+        vc[t] = big
+    o = oracle.attention(q, kc, vc, n_pos, nq, nkv, hd)
+    o_cut = oracle.attention(q, kc[:n_pos].copy(), vc[:n_pos].copy(), n_pos, nq, nkv, hd)
+    assert np.array_equal(o, o_cut)
+    o_more = oracle.attention(q, kc, vc, n_pos + 1, nq, nkv, hd)
+    assert np.abs(o_more - o).max() > 1000.0
+
+
 def test_silu_special_values():
     assert oracle.silu(0.0) == 0.0
     assert oracle.silu(60.0) == 60.0
