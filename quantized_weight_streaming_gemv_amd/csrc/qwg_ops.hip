@@ -70,7 +70,7 @@ struct Tokens {
 };
 
 template <int QT>
-__global__ void k_embed(MatView w, int64_t k, Tokens tok, int nc, float* h, int64_t h_stride) {
+__global__ void k_embed(MatView w, Tokens tok, int nc, float* h, int64_t h_stride) {
   using F = Fmt<QT>;
   const int c = blockIdx.x * blockDim.x + threadIdx.x;
   const int n = blockIdx.y;
@@ -86,15 +86,17 @@ __global__ void k_embed(MatView w, int64_t k, Tokens tok, int nc, float* h, int6
 
 hipError_t launch_embed(int qt, const MatView& w, int64_t k, const int32_t* tokens, int nc, float* h, int64_t h_stride,
                         hipStream_t st) {
+  (void)k;  // the row length is the matrix view's
+  if (nc < 1 || nc > MAX_COLS) return hipErrorInvalidValue;  // one token slot per column
   Tokens tk{};
-  for (int i = 0; i < nc && i < MAX_COLS; ++i) tk.t[i] = tokens[i];
+  for (int i = 0; i < nc; ++i) tk.t[i] = tokens[i];
   dim3 g((w.nch + 127) / 128, nc), b(128);
   switch (qt) {
-    case Q8_0: hipLaunchKernelGGL(k_embed<Q8_0>, g, b, 0, st, w, k, tk, nc, h, h_stride); break;
-    case Q4_0: hipLaunchKernelGGL(k_embed<Q4_0>, g, b, 0, st, w, k, tk, nc, h, h_stride); break;
-    case Q4_K: hipLaunchKernelGGL(k_embed<Q4_K>, g, b, 0, st, w, k, tk, nc, h, h_stride); break;
-    case Q5_K: hipLaunchKernelGGL(k_embed<Q5_K>, g, b, 0, st, w, k, tk, nc, h, h_stride); break;
-    case Q6_K: hipLaunchKernelGGL(k_embed<Q6_K>, g, b, 0, st, w, k, tk, nc, h, h_stride); break;
+    case Q8_0: hipLaunchKernelGGL(k_embed<Q8_0>, g, b, 0, st, w, tk, nc, h, h_stride); break;
+    case Q4_0: hipLaunchKernelGGL(k_embed<Q4_0>, g, b, 0, st, w, tk, nc, h, h_stride); break;
+    case Q4_K: hipLaunchKernelGGL(k_embed<Q4_K>, g, b, 0, st, w, tk, nc, h, h_stride); break;
+    case Q5_K: hipLaunchKernelGGL(k_embed<Q5_K>, g, b, 0, st, w, tk, nc, h, h_stride); break;
+    case Q6_K: hipLaunchKernelGGL(k_embed<Q6_K>, g, b, 0, st, w, tk, nc, h, h_stride); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
