@@ -32,8 +32,8 @@ HBM_PEAK_GBPS = 8000.0
 # change to them `roofline.traffic` is reported as null until the passes are taken again.
 GEMV_TRAFFIC = {
     "workload": "llama70b-q4_k-resident",
-    "sources_sha256": "8afe43e33b113ed5967cde0653c395adeae3a1aa22a9b7e057839d9187d6a620",
-    "fetch_kib": 130426.81, "fetch_scale": 1.99975, "write_kib": 112.00, "write_scale": 1.00000,
+    "sources_sha256": "09d3cc4941b1407203b04c69ae31868fff03b9bb77cc2b4977f3a4d49f823683",
+    "fetch_kib": 130423.29, "fetch_scale": 1.99975, "write_kib": 112.00, "write_scale": 1.00000,
 }
 GEMV_SOURCES = ("qwg_gemv.hip", "qwg_formats.h", "qwg_kernels.h")
 

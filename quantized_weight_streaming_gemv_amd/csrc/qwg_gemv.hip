@@ -1204,6 +1204,8 @@ static hipError_t launch_mfma(const GemvArgs& a, int epi, const GemvPlan& p, dim
 hipError_t launch_gemv(int qt, const MatView& w, int64_t k, const void* xd, int64_t xd_stride_bytes, int nc, int epi,
                        const EpiArgs& e, float* part, hipStream_t st, const GemvPlan& p, hipEvent_t ev_start,
                        hipEvent_t ev_stop) {
+  // the kernels keep per-column sums in arrays of MAX_COLS
+  if (nc < 1 || nc > MAX_COLS || nc > p.ncm) return hipErrorInvalidValue;
   if (e.dig_out && !gemv_can_digitize_output(p, epi, w.rows)) return hipErrorInvalidValue;
   GemvArgs a;
   a.w = w;
