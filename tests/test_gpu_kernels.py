@@ -178,10 +178,11 @@ def test_rope_table_and_kernel(ops):
 @pytest.mark.parametrize("nq,nkv,npos,nc", [(4, 2, 1, 1), (8, 2, 100, 1), (8, 2, 100, 4), (64, 8, 2049, 1),
                                             (64, 8, 4097, 4), (32, 8, 513, 1), (16, 2, 70, 8), (8, 2, 33, 2),
                                             (16, 2, 70, 3), (64, 8, 257, 5), (32, 2, 9000, 1), (24, 2, 300, 2),
-                                            (8, 8, 130, 2)])
+                                            (8, 8, 130, 2), (2, 1, 262144, 2)])
 def test_attention(ops, nq, nkv, npos, nc):
     # (32, 2, 9000): 141 splits and 16 query rows per KV head; (24, 2, 300, 2): 12 rows per head;
-    # (8, 8, 130, 2): one query head per KV head (plain multi-head attention)
+    # (8, 8, 130, 2): one query head per KV head (plain multi-head attention); (2, 1, 262144, 2): the
+    # largest n_pos the library takes, 4097 splits
     import torch
     hd = 128
     ctx = npos + nc - 1
