@@ -404,3 +404,187 @@ def test_spec_round_rejection_rolls_back():
         t = ref.decode(t)["next"]
         toks.append(t)
     assert toks == res["tokens"]
+
+
+# ---------------------------------------------------------------- layer and head composition
+#
+# Hand-built Q8_0 layers (d = 1, integer quants: the matrices are exact integers) with closed-form
+# outputs.  H = 256, two query heads sharing one KV head of 128, FFN 64, eps = 0, and a residual
+# input u of +-1 entries (mean square exactly 1), so every RMSNorm output is gain * u exactly.
+# Each case fixes one wiring choice of the pre-norm Llama layer that the Llama architecture list
+# of the NTransformer page ("Key features": RoPE, GQA, SwiGLU, RMSNorm, KV cache) implies:
+# which gain feeds which norm, gate vs up, RoPE on q and k (not v) before the cache write, the new
+# token's K/V appended before it attends, and the final norm's gain in the head.
+
+H_, NQ_, NKV_, HD_, F_ = 256, 2, 1, 128, 64
+G_ATTN_, G_FFN_, G_FINAL_ = 0.5, 2.0, 3.0
+
+
+def _q8(M):
+    """Canonical Q8_0 bytes of an integer matrix with entries in [-127, 127] (d = 1.0)."""
+    M = np.asarray(M, dtype=np.int64)
+    rows, k = M.shape
+    out = np.zeros((rows, k // 32, 34), np.uint8)
+    out[:, :, 0:2] = [0x00, 0x3C]  # fp16 1.0
+    out[:, :, 2:] = M.reshape(rows, k // 32, 32).astype(np.int8).view(np.uint8)
+    return out.reshape(rows, -1)
+
+
+def _u():
+    i = np.arange(H_)
+    return np.where((i * 7 + i // 3) % 5 < 2, -1.0, 1.0)
+
+
+class _Layer:
+    """One hand-built layer driven through orc_layer_forward, with its own fp16 caches."""
+
+    def __init__(self, mats, max_ctx=16):
+        import ctypes
+        O = oracle.oracle
+        zero = {2: (NQ_ * HD_, H_), 3: (NKV_ * HD_, H_), 4: (NKV_ * HD_, H_), 5: (H_, NQ_ * HD_),
+                6: (F_, H_), 7: (F_, H_), 8: (H_, F_)}
+        self.keep = []
+        self.dims = O.Dims(1, H_, NQ_, NKV_, HD_, F_, 1000, max_ctx, 500000.0, 0.0)
+        self.lay = O.Layer()
+        for i, t in enumerate((2, 3, 4, 5, 6, 7, 8)):
+            W = _q8(mats.get(t, np.zeros(zero[t], np.int64)))
+            self.keep.append(W)
+            self.lay.w[i] = W.ctypes.data
+            self.lay.qt[i] = synth.Q8_0
+        self.ga = np.full(H_, G_ATTN_, np.float32)
+        self.gf = np.full(H_, G_FFN_, np.float32)
+        self.lay.g_attn, self.lay.g_ffn = self.ga.ctypes.data, self.gf.ctypes.data
+        self.kc = np.zeros((max_ctx, NKV_, HD_), np.uint16)
+        self.vc = np.zeros_like(self.kc)
+        self.lay.kc, self.lay.vc = self.kc.ctypes.data, self.vc.ctypes.data
+        self.ctypes = ctypes
+
+    def run(self, h, pos):
+        out = np.ascontiguousarray(h, dtype=np.float64).copy()
+        rc = oracle.oracle.lib().orc_layer_forward(self.ctypes.byref(self.dims), self.ctypes.byref(self.lay),
+                                                   out.ctypes.data, pos)
+        assert rc == 0
+        return out
+
+
+def _eye(rows, k, col0=0):
+    M = np.zeros((rows, k), np.int64)
+    M[np.arange(rows), col0 + np.arange(rows)] = 1
+    return M
+
+
+def _f16(x):
+    return np.asarray(x, np.float64).astype(np.float16).view(np.uint16)
+
+
+def test_layer_uniform_attention_is_mean_of_v_through_wo():
+    """Wq = Wk = 0: every score is 0 and attention is the plain mean of V over positions 0..pos,
+    including the new token's V = Wv n1 = g_attn * u[128:] (appended before attending); both query
+    heads read the one KV head; Wo = I adds that mean into both halves of the residual; the zero FFN
+    adds nothing."""
+    L = _Layer({4: _eye(HD_, H_, 128), 5: _eye(H_, H_)})
+    pos = 6
+    prior = synth.normal_f16(synth.key(31, 1), pos * HD_).reshape(pos, 1, HD_)
+    L.vc[:pos] = prior
+    L.kc[:pos] = synth.normal_f16(synth.key(31, 2), pos * HD_).reshape(pos, 1, HD_)
+    u = _u()
+    out = L.run(u, pos)
+    v_new = G_ATTN_ * u[128:]
+    assert np.array_equal(L.vc[pos, 0], _f16(v_new))          # V row: no RoPE
+    assert np.all(L.kc[pos, 0].view(np.float16) == 0)              # rope(0) = +-0
+    mean = (prior.view(np.float16).astype(np.float64)[:, 0, :].sum(axis=0) + v_new) / (pos + 1)
+    assert np.max(np.abs(out - (u + np.concatenate([mean, mean])))) < 1e-12
+
+
+def test_layer_caches_rotated_k_and_unrotated_v():
+    """Wk = [I 0], Wv = [0 I]: at position 0 the cached K row is g_attn * u[:128] exactly (RoPE is
+    the identity there); at position 7 it is that row rotated (every pair keeps its norm, the row
+    differs from the unrotated one) while the cached V row stays unrotated."""
+    u = _u()
+    for pos in (0, 7):
+        L = _Layer({3: _eye(HD_, H_), 4: _eye(HD_, H_, 128)})
+        L.run(u, pos)
+        k = L.kc[pos, 0].view(np.float16).astype(np.float64)
+        a = G_ATTN_ * u[:128]
+        assert np.array_equal(L.vc[pos, 0], _f16(G_ATTN_ * u[128:]))
+        if pos == 0:
+            assert np.array_equal(L.kc[0, 0], _f16(a))
+        else:
+            pn = k[0::2] ** 2 + k[1::2] ** 2
+            assert np.all(np.abs(pn - 0.5) < 2e-3)            # (0.5^2 + 0.5^2), fp16-rounded
+            assert not np.array_equal(L.kc[pos, 0], _f16(a))
+            assert np.array_equal(L.kc[pos, 0], _f16(oracle.rope(a, 1, HD_, pos, 500000.0)))
+
+
+def test_layer_rotates_q_like_k():
+    """Position 1, Wq = Wk = [I 0]: q and the new key are the same vector a rotated by the same angle,
+    so their score is |a|^2 / sqrt(128) = 2.83 whatever the angle (up to the fp16 rounding of the
+    cached key, below 1.5e-3); the prior key is 0 (score 0).  The output is (V0 + e^s V1) / (1 + e^s),
+    in both halves of the residual through Wo = I.  A q left unrotated would score a . rope(a) =
+    2.65 instead, moving the output by about 0.04."""
+    L = _Layer({2: np.vstack([_eye(HD_, H_), _eye(HD_, H_)]), 3: _eye(HD_, H_), 4: _eye(HD_, H_, 128),
+                5: _eye(H_, H_)})
+    A = synth.normal_f16(synth.key(31, 3), HD_).reshape(1, 1, HD_)
+    L.vc[0] = A[0]
+    u = _u()
+    out = L.run(u, 1)
+    a = G_ATTN_ * u[:128]
+    s = float(a @ a) / np.sqrt(HD_)
+    v0 = A.view(np.float16).astype(np.float64)[0, 0]
+    v1 = G_ATTN_ * u[128:]
+    o = (v0 + np.exp(s) * v1) / (1.0 + np.exp(s))
+    assert np.max(np.abs(out - (u + np.concatenate([o, o])))) < 2e-3
+
+
+def test_layer_ffn_gate_up_down_and_ffn_gain():
+    """Attention adds 0 (Wo = 0).  n2 = g_ffn * u; gate row 0 picks n2[a] = +2, up row 0 picks
+    n2[b] = -2, down column 0 puts silu(gate) * up at output c:
+    h[c] += silu(2) * (-2) = -4 / (1 + e^-2).  Swapping gate and up would give silu(-2) * 2, using
+    g_attn would give silu(0.5) * (-0.5)."""
+    u = _u()
+    a = int(np.nonzero(u > 0)[0][0])
+    b = int(np.nonzero(u < 0)[0][1])
+    c = 77
+    Wg = np.zeros((F_, H_), np.int64)
+    Wu = np.zeros((F_, H_), np.int64)
+    Wd = np.zeros((H_, F_), np.int64)
+    Wg[0, a] = 1
+    Wu[0, b] = 1
+    Wd[c, 0] = 1
+    L = _Layer({6: Wg, 7: Wu, 8: Wd})
+    out = L.run(u, 3)
+    want = u.copy()
+    want[c] += -4.0 / (1.0 + np.exp(-2.0))
+    assert np.max(np.abs(out - want)) < 1e-15
+
+
+def test_head_uses_final_gain_and_step_wiring():
+    """orc_head: logits = W_head (g_final * h / rms(h)); with rms(h) = 1 and eps = 0 and a one-hot
+    head row v -> column v, logits[v] = g_final * u[v] = +-3 exactly.  orc_step on a model whose
+    embedding row is u and whose layers are exact identities (Wo = W_down = 0) returns those logits
+    and the first index of the largest (the first +1 of u)."""
+    import ctypes
+    O = oracle.oracle
+    V = H_
+    u = _u()
+    head = _q8(_eye(V, H_))
+    emb = np.zeros((V, H_), np.int64)
+    tok = 5
+    emb[tok] = u.astype(np.int64)
+    embb = _q8(emb)
+    gfin = np.full(H_, G_FINAL_, np.float32)
+    L = _Layer({})  # all-zero matrices: an exact identity layer
+    dims = O.Dims(1, H_, NQ_, NKV_, HD_, F_, V, 16, 500000.0, 0.0)
+    m = O.Model()
+    m.dims = dims
+    m.layers = ctypes.cast(ctypes.pointer(L.lay), ctypes.POINTER(O.Layer))
+    m.embed, m.qt_embed = embb.ctypes.data, synth.Q8_0
+    m.head, m.qt_head = head.ctypes.data, synth.Q8_0
+    m.g_final = gfin.ctypes.data
+    logits = np.empty(V)
+    assert O.lib().orc_head(ctypes.byref(m), u.ctypes.data, logits.ctypes.data) == 0
+    assert np.array_equal(logits, G_FINAL_ * u)
+    lg = np.empty(V)
+    nxt = ctypes.c_int32(-1)
+    assert O.lib().orc_step(ctypes.byref(m), tok, 2, 1, None, None, None, lg.ctypes.data, ctypes.byref(nxt)) == 0
+    assert np.array_equal(lg, G_FINAL_ * u) and nxt.value == int(np.argmax(u))
