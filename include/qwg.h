@@ -96,12 +96,20 @@ int qwg_dequantize(int qtype, const void* d_packed, int64_t rows, int64_t k, flo
  * cuda/: GEMV; [NT] "Key features": no cuBLAS): d_y[j][r] = sum_c W[r][c] d_x[j][c] for
  * j < n_cols, with W decoded from the packed blocks in registers and never written out.
  * d_x is fp32 [n_cols][k], d_y fp32 [n_cols][rows]; 1 <= n_cols <= 8; k <= 65536.
- * n_cols > 1 is the multi-column form used to verify self-speculative drafts ([NT] "Key features"). */
+ * n_cols > 1 is the multi-column form used to verify self-speculative drafts ([NT] "Key features").
+ * d_work: caller-owned device scratch of at least qwg_gemv_work_bytes(qtype, rows, k, n_cols) bytes
+ * (16-byte aligned), which the call overwrites with the activation's fixed-point digits and, for
+ * shapes whose activation does not fit on chip at once, the K-split partial sums.  Calls in flight
+ * at the same time (on one stream or several) need their own d_work; the library allocates nothing
+ * and never synchronizes here.  d_packed and d_x 16-byte aligned.  rows == 0 leaves d_y untouched.
+ * qwg_gemv_work_bytes returns 0 for shapes the call rejects. */
+size_t qwg_gemv_work_bytes(int qtype, int64_t rows, int64_t k, int n_cols);
 int qwg_gemv(int qtype, const void* d_packed, int64_t rows, int64_t k, const float* d_x, int n_cols, float* d_y,
-             void* stream);
+             void* d_work, size_t work_bytes, void* stream);
 
 /* Launch geometry of subsequent GEMV launches in this process, for tuning; 0 keeps the default:
- *   waves_per_group  2, 4 or 8; 16 for single-column GEMVs (2 rows per wave, depth 1, <= 2 passes);
+ *   waves_per_group  1..8; up to 16 for single-column GEMVs (above 8: 2 rows per wave, depth 1,
+ *                    <= 2 passes);
  *                    for the matrix-core form of 2..8 columns any even number up to 16 (2..4
  *                    columns) or 8 (5..8 columns), the waves of one workgroup
  *   rows_per_wave    output rows per wave of single-column GEMVs: 1, 2 or 4
@@ -159,8 +167,12 @@ int qwg_swiglu(const float* d_g, const float* d_u, int64_t n, float* d_out, void
 int qwg_cosine(const float* d_a, const float* d_b, int64_t n, float* d_out, void* stream);
 
 /* Greedy sampler ([NT] "Architecture overview", inference/ sampler): *d_out = index of the largest
- * element of d_x[n] (fp32), lowest index on ties, NaNs ignored. */
-int qwg_argmax(const float* d_x, int64_t n, int32_t* d_out, void* stream);
+ * element of d_x[n] (fp32), lowest index on ties; a NaN ranks above every number (the first NaN wins),
+ * so non-finite logits show in the chosen token.  d_work: caller-owned device scratch of
+ * qwg_argmax_work_bytes() bytes (8-byte aligned), overwritten; calls in flight at the same time need
+ * their own.  Asynchronous on `stream`. */
+size_t qwg_argmax_work_bytes(void);
+int qwg_argmax(const float* d_x, int64_t n, int32_t* d_out, void* d_work, size_t work_bytes, void* stream);
 
 /* ---- model: a Llama decoder held in HBM, optionally with layers streamed from pinned RAM ---- */
 
@@ -294,10 +306,15 @@ int qwg_sync(qwg_model* m);
 /* Plain streaming read of `bytes` (a positive multiple of 16; d_src 16-byte aligned) with the
  * GEMV's own 16-byte non-temporal load pattern and no arithmetic: the measured achievable HBM
  * bandwidth, against which the pages' rule that decode speed is bounded by memory bandwidth over
- * the bytes read per token ([UR] benchmark discussion) is checked.  Writes qwg_read_sink_words()
- * checksum words to d_sink (device, caller-owned).  Asynchronous on `stream`. */
+ * the bytes read per token ([UR] benchmark discussion) is checked.  `grid` workgroups of 8 waves
+ * (1..8192; 0 = 1024) each read a contiguous share, every lane keeping `unroll` loads in flight (4, 8
+ * or 16; 0 = 4).  Writes grid * 8 checksum words to d_sink (device, caller-owned, at least
+ * qwg_read_sink_words() words).  Asynchronous on `stream`, unless h_kernel_ms is given: then the
+ * call waits for the kernel and stores its duration (ms, from events at the kernel's own start and
+ * end) there. */
 size_t qwg_read_sink_words(void);
-int qwg_read_bytes(const void* d_src, size_t bytes, uint32_t* d_sink, void* stream);
+int qwg_read_bytes(const void* d_src, size_t bytes, uint32_t* d_sink, int grid, int unroll, float* h_kernel_ms,
+                   void* stream);
 
 /* Pinned host memory (hipHostMalloc) for callers that stage weights. */
 int qwg_host_alloc(size_t bytes, void** out);

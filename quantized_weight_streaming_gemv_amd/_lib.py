@@ -48,7 +48,8 @@ SIGNATURES = {
     "qwg_packed_bytes": (ctypes.c_int, [ctypes.c_int, i64, i64, P_sz]),
     "qwg_repack": (ctypes.c_int, [ctypes.c_int, vp, i64, i64, vp, vp]),
     "qwg_dequantize": (ctypes.c_int, [ctypes.c_int, vp, i64, i64, vp, vp]),
-    "qwg_gemv": (ctypes.c_int, [ctypes.c_int, vp, i64, i64, vp, ctypes.c_int, vp, vp]),
+    "qwg_gemv_work_bytes": (sz, [ctypes.c_int, i64, i64, ctypes.c_int]),
+    "qwg_gemv": (ctypes.c_int, [ctypes.c_int, vp, i64, i64, vp, ctypes.c_int, vp, vp, sz, vp]),
     "qwg_set_gemv_geometry": (ctypes.c_int, [ctypes.c_int] * 4),
     "qwg_set_gemv_mfma": (ctypes.c_int, [ctypes.c_int]),
     "qwg_model_spill_layer": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_char_p]),
@@ -63,7 +64,8 @@ SIGNATURES = {
     "qwg_attn_decode": (ctypes.c_int, [vp, vp, vp] + [ctypes.c_int] * 5 + [vp, vp, sz, vp]),
     "qwg_swiglu": (ctypes.c_int, [vp, vp, i64, vp, vp]),
     "qwg_cosine": (ctypes.c_int, [vp, vp, i64, vp, vp]),
-    "qwg_argmax": (ctypes.c_int, [vp, i64, vp, vp]),
+    "qwg_argmax_work_bytes": (sz, []),
+    "qwg_argmax": (ctypes.c_int, [vp, i64, vp, vp, sz, vp]),
     "qwg_model_create": (ctypes.c_int, [ctypes.POINTER(ModelDesc), ctypes.POINTER(vp)]),
     "qwg_model_arena_bytes": (sz, [vp]),
     "qwg_model_bind": (ctypes.c_int, [vp, vp, sz, vp, vp]),
@@ -87,7 +89,7 @@ SIGNATURES = {
     "qwg_model_stream_stats": (ctypes.c_int, [vp, P_i64, P_f64]),
     "qwg_sync": (ctypes.c_int, [vp]),
     "qwg_read_sink_words": (sz, []),
-    "qwg_read_bytes": (ctypes.c_int, [vp, sz, vp, vp]),
+    "qwg_read_bytes": (ctypes.c_int, [vp, sz, vp, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_float), vp]),
     "qwg_host_alloc": (ctypes.c_int, [sz, ctypes.POINTER(vp)]),
     "qwg_host_free": (ctypes.c_int, [vp]),
 }

@@ -63,40 +63,6 @@ int64_t canon_row_bytes(int qt, int64_t k) {
 
 size_t align_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
 
-// Scratch of the kernel-level entry points that need it (GEMV K-split partials, argmax keys):
-// allocated on first use per device and purpose, grown when needed, freed at exit.
-enum { WS_GEMV = 0, WS_ARGMAX = 1, WS_DIGITS = 2, WS_KINDS = 3 };
-struct KernelWorkspace {
-  void* p[64][WS_KINDS] = {};
-  size_t n[64][WS_KINDS] = {};
-  ~KernelWorkspace() {
-    for (int i = 0; i < 64; ++i)
-      for (int k = 0; k < WS_KINDS; ++k)
-        if (p[i][k]) (void)hipFree(p[i][k]);
-  }
-} g_ws;
-
-hipError_t kernel_workspace(int kind, size_t bytes, void** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (g_ws.n[dev][kind] < bytes) {
-    if (g_ws.p[dev][kind]) {
-      e = hipDeviceSynchronize();
-      if (e != hipSuccess) return e;
-      (void)hipFree(g_ws.p[dev][kind]);
-      g_ws.p[dev][kind] = nullptr;
-      g_ws.n[dev][kind] = 0;
-    }
-    e = hipMalloc(&g_ws.p[dev][kind], bytes);
-    if (e != hipSuccess) return e;
-    g_ws.n[dev][kind] = bytes;
-  }
-  *out = g_ws.p[dev][kind];
-  return hipSuccess;
-}
-
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 }  // namespace
@@ -686,31 +652,52 @@ int qwg_dequantize(int qtype, const void* d_packed, int64_t rows, int64_t k, flo
   return QWG_OK;
 }
 
+// Scratch of one qwg_gemv call: the activation digits of every column, then (256-B aligned) the
+// K-split partial sums of whichever form a several-column GEMV may take.
+static bool gemv_work_layout(int qtype, int64_t rows, int64_t k, int n_cols, size_t* dig_bytes, size_t* total) {
+  if (!qtype_known(qtype) || rows < 0 || rows > (int64_t)1 << 30 || canon_row_bytes(qtype, k) == 0 || k > 65536 ||
+      n_cols < 1 || n_cols > MAX_COLS)
+    return false;
+  const size_t dig = align_up((size_t)n_cols * (size_t)digit_bytes(k));
+  size_t part = 0;
+  for (int mf : {0, 1}) part = std::max(part, plan_gemv(qtype, rows, k, n_cols, EPI_STORE, mf).part_bytes);
+  *dig_bytes = dig;
+  *total = dig + align_up(part);
+  return true;
+}
+
+size_t qwg_gemv_work_bytes(int qtype, int64_t rows, int64_t k, int n_cols) {
+  size_t dig = 0, total = 0;
+  return gemv_work_layout(qtype, rows, k, n_cols, &dig, &total) ? total : 0;
+}
+
 int qwg_gemv(int qtype, const void* d_packed, int64_t rows, int64_t k, const float* d_x, int n_cols, float* d_y,
-             void* stream) {
+             void* d_work, size_t work_bytes, void* stream) {
   if (int rc = check_matrix(qtype, rows, k)) return rc;
   if (n_cols < 1 || n_cols > MAX_COLS) return fail(QWG_E_SHAPE, "n_cols must be in 1..8");
   if (rows == 0) return QWG_OK;
-  if (!d_packed || !d_x || !d_y) return fail(QWG_E_INVAL, "NULL pointer");
-  if (!aligned16(d_packed) || !aligned16(d_x)) return fail(QWG_E_INVAL, "pointers must be 16-byte aligned");
+  if (!d_packed || !d_x || !d_y || !d_work) return fail(QWG_E_INVAL, "NULL pointer");
+  if (!aligned16(d_packed) || !aligned16(d_x) || !aligned16(d_work))
+    return fail(QWG_E_INVAL, "d_packed, d_x and d_work must be 16-byte aligned");
+  size_t dig = 0, need = 0;
+  gemv_work_layout(qtype, rows, k, n_cols, &dig, &need);
+  if (work_bytes < need) return fail(QWG_E_NOMEM, "work buffer smaller than qwg_gemv_work_bytes");
   const Layout L = make_layout(qtype, rows, k);
   const GemvPlan p = plan_gemv(qtype, rows, k, n_cols, EPI_STORE);
-  void* part = nullptr;
-  if (p.part_bytes) QWG_HIP(kernel_workspace(WS_GEMV, p.part_bytes, &part));
-  void* xd = nullptr;
-  QWG_HIP(kernel_workspace(WS_DIGITS, (size_t)n_cols * digit_bytes(k), &xd));
+  uint8_t* xd = (uint8_t*)d_work;
+  float* part = p.part_bytes ? (float*)(xd + dig) : nullptr;
   QWG_HIP(launch_digitize(d_x, k, nullptr, k, n_cols, qtype, xd, digit_bytes(k), nullptr, 0, (hipStream_t)stream));
   EpiArgs e{};
   e.y = d_y;
   e.y_stride = rows;
-  QWG_HIP(launch_gemv(qtype, make_view(d_packed, L), k, xd, digit_bytes(k), n_cols, EPI_STORE, e, (float*)part,
+  QWG_HIP(launch_gemv(qtype, make_view(d_packed, L), k, xd, digit_bytes(k), n_cols, EPI_STORE, e, part,
                       (hipStream_t)stream, p));
   return QWG_OK;
 }
 
 int qwg_set_gemv_geometry(int waves_per_group, int rows_per_wave, int pipeline_depth, int row_passes) {
-  if (waves_per_group < 0 || waves_per_group > 16 || (waves_per_group & 1))
-    return fail(QWG_E_INVAL, "waves_per_group must be 0 or an even number up to 16");
+  if (waves_per_group < 0 || waves_per_group > 16)
+    return fail(QWG_E_INVAL, "waves_per_group must be 0..16");
   if (!(rows_per_wave == 0 || rows_per_wave == 1 || rows_per_wave == 2 || rows_per_wave == 4))
     return fail(QWG_E_INVAL, "rows_per_wave must be 0, 1, 2 or 4");
   if (!(pipeline_depth == 0 || pipeline_depth == 1 || pipeline_depth == 2))
@@ -727,13 +714,28 @@ int qwg_set_gemv_mfma(int on) {
   return QWG_OK;
 }
 
-size_t qwg_read_sink_words(void) { return (size_t)READ_GRID * 8; }
+size_t qwg_read_sink_words(void) { return (size_t)READ_GRID_MAX * 8; }
 
-int qwg_read_bytes(const void* d_src, size_t bytes, uint32_t* d_sink, void* stream) {
+int qwg_read_bytes(const void* d_src, size_t bytes, uint32_t* d_sink, int grid, int unroll, float* h_kernel_ms,
+                   void* stream) {
   if (!d_src || !d_sink) return fail(QWG_E_INVAL, "NULL pointer");
   if (bytes == 0 || bytes % 16) return fail(QWG_E_SHAPE, "bytes must be a positive multiple of 16");
   if (!aligned16(d_src)) return fail(QWG_E_INVAL, "d_src must be 16-byte aligned");
-  QWG_HIP(launch_read(d_src, (int64_t)bytes, d_sink, (hipStream_t)stream));
+  if (grid < 0 || grid > READ_GRID_MAX) return fail(QWG_E_INVAL, "grid must be 0..8192");
+  if (!(unroll == 0 || unroll == 4 || unroll == 8 || unroll == 16)) return fail(QWG_E_INVAL, "unroll must be 0, 4, 8 or 16");
+  hipStream_t st = (hipStream_t)stream;
+  if (!h_kernel_ms) {
+    QWG_HIP(launch_read(d_src, (int64_t)bytes, d_sink, st, grid, unroll));
+    return QWG_OK;
+  }
+  // timed: events recorded by the dispatch itself at the kernel's start and end, then a wait
+  hipEvent_t e[2] = {nullptr, nullptr};
+  for (auto& x : e) QWG_HIP(hipEventCreateWithFlags(&x, hipEventDisableSystemFence));
+  hipError_t err = launch_read(d_src, (int64_t)bytes, d_sink, st, grid, unroll, e[0], e[1]);
+  if (err == hipSuccess) err = hipEventSynchronize(e[1]);
+  if (err == hipSuccess) err = hipEventElapsedTime(h_kernel_ms, e[0], e[1]);
+  for (auto x : e) (void)hipEventDestroy(x);
+  if (err != hipSuccess) return fail(QWG_E_HIP, std::string("timed read: ") + hipGetErrorString(err));
   return QWG_OK;
 }
 
@@ -805,12 +807,14 @@ int qwg_cosine(const float* d_a, const float* d_b, int64_t n, float* d_out, void
   return QWG_OK;
 }
 
-int qwg_argmax(const float* d_x, int64_t n, int32_t* d_out, void* stream) {
-  if (!d_x || !d_out) return fail(QWG_E_INVAL, "NULL pointer");
+size_t qwg_argmax_work_bytes(void) { return ARGMAX_WORK_BYTES; }
+
+int qwg_argmax(const float* d_x, int64_t n, int32_t* d_out, void* d_work, size_t work_bytes, void* stream) {
+  if (!d_x || !d_out || !d_work) return fail(QWG_E_INVAL, "NULL pointer");
   if (n < 1 || n > 0x7FFFFFFE) return fail(QWG_E_SHAPE, "n out of range");
-  void* keys = nullptr;
-  QWG_HIP(kernel_workspace(WS_ARGMAX, 256, &keys));
-  QWG_HIP(launch_argmax(d_x, n, 1, n, d_out, (hipStream_t)stream, (unsigned long long*)keys));
+  if (work_bytes < ARGMAX_WORK_BYTES) return fail(QWG_E_NOMEM, "work buffer smaller than qwg_argmax_work_bytes");
+  if ((uintptr_t)d_work & 7) return fail(QWG_E_INVAL, "d_work must be 8-byte aligned");
+  QWG_HIP(launch_argmax(d_x, n, 1, n, d_out, (hipStream_t)stream, (unsigned long long*)d_work));
   return QWG_OK;
 }
 

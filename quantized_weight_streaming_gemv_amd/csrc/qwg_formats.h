@@ -250,141 +250,126 @@ __host__ __device__ inline T ld(const uint8_t* p) {
 //
 // The GEMV never multiplies fp32 activations by converted weights.  Instead every 32-element chunk
 // of the activation becomes a block fixed-point integer vector: one shared power-of-two scale per
-// chunk, x_fix = rint(x * 2^s) with |x_fix| < 2^22 (24-bit two's-complement range, so the largest
-// element of the chunk keeps 22 significant bits), split into balanced digits:
-//   nibble digits (Q4_0, Q4_K): x_fix = sum_l d_l 16^l, d_l in [-8, 7], l = 0..5
-//   byte digits (Q5_K, Q6_K, Q8_0): x_fix = sum_l d_l 256^l, d_l in [-128, 127], l = 0..2
-// Adding 0x888888 (or 0x808080) maps the balanced digits to the plain base-16 (base-256) digits of
-// the sum, so each digit is a field extract followed by flipping its top bit.  The weight quants are
-// then integers too, and each dot product is a sum of exact integer products (v_dot8_i32_i4 /
+// chunk, x_fix = rint(x * 2^s) with the chunk's largest magnitude at [2^29, 2^30) (32-bit two's-
+// complement range, so the largest element keeps 30 significant bits and every element is within
+// 2^-30 of the chunk maximum of its exact value), split into balanced digits:
+//   nibble digits (Q4_0, Q4_K): x_fix = sum_l d_l 16^l, d_l in [-8, 7], l = 0..7
+//   byte digits (Q5_K, Q6_K, Q8_0): x_fix = sum_l d_l 256^l, d_l in [-128, 127], l = 0..3
+// Adding 0x88888888 (or 0x80808080) maps the balanced digits to the plain base-16 (base-256) digits
+// of the sum, so each digit is a field extract followed by flipping its top bit.  The weight quants
+// are then integers too, and each dot product is a sum of exact integer products (v_dot8_i32_i4 /
 // v_dot4_i32_i8), recombined per chunk in fp32 and scaled by 2^-s.
 //
-// Digit words of a chunk (24 x 32 bits) are laid out to match the packed quant words:
-//   nibble: word m*6 + l, nibble 2b+h = digit l of element 16h + 4m + b   (h = 0 low, 1 high nibble)
-//   byte:   word (h*4 + m)*3 + l, byte b = digit l of element 16h + 4m + b
-// followed by a ChunkDesc (2^-s and the integer sums of x_fix over the chunk and its two halves).
+// A chunk holding a NaN or an infinity gets a NaN scale (and zero digits), so every row it touches
+// comes out NaN, as the exact sum would be non-finite; the digits never turn a non-finite input into
+// a finite output.
+//
+// Digit words of a chunk (32 x 32 bits) are laid out to match the packed quant words:
+//   nibble: word m*8 + l, nibble 2b+h = digit l of element 16h + 4m + b   (h = 0 low, 1 high nibble)
+//   byte:   word (h*4 + m)*4 + l, byte b = digit l of element 16h + 4m + b
+// followed by a ChunkDesc (2^-s and the sum of x_fix over the chunk, rounded and exact).
 
 enum DigitKind : int { DIG_NIB = 0, DIG_BYTE = 1 };
-constexpr int XCHUNK = 32;         // activation elements per digit chunk
-constexpr int DIG_WORDS = 24;      // digit words per chunk
-constexpr int DIG_CHUNK_WORDS = 28;  // digit words + ChunkDesc
+constexpr int XCHUNK = 32;           // activation elements per digit chunk
+constexpr int NIB_LEVELS = 8;        // nibble digit levels
+constexpr int BYTE_LEVELS = 4;       // byte digit levels
+constexpr int DIG_WORDS = 32;        // digit words per chunk (either kind)
+constexpr int DIG_CHUNK_WORDS = 36;  // digit words + ChunkDesc
+constexpr int FIX_TOP = 29;          // the chunk maximum times 2^s lies in [2^FIX_TOP, 2^(FIX_TOP+1))
 
 __host__ __device__ inline int digit_kind(int qt) { return (qt == Q4_K || qt == Q4_0) ? DIG_NIB : DIG_BYTE; }
 
 struct ChunkDesc {
-  float inv_scale;  // 2^-s
-  int32_t sum;      // sum of x_fix over the chunk
-  int32_t sumA;     // over elements 0..15
-  int32_t sumB;     // over elements 16..31
+  float inv_scale;  // 2^-s (NaN if the chunk holds a NaN or an infinity)
+  float sum;        // sum of x_fix over the chunk, rounded once to fp32
+  int32_t shi, slo; // the same sum exactly: 32768 shi + slo (|shi|, |slo| <= 2^20)
 };
-
-// Digits and descriptor of one 32-element chunk (x already multiplied by its gain if any).
-__host__ __device__ inline void digitize_chunk(const float* x, int kind, uint32_t* dig, ChunkDesc* desc) {
-  float mx = 0.f;
-  for (int e = 0; e < XCHUNK; ++e) mx = fmaxf(mx, fabsf(x[e]));
-  int s = 0;
-  if (mx > 0.f && mx == mx) {
-    s = 21 - ilogbf(mx);  // mx * 2^s in [2^21, 2^22)
-    s = s > 100 ? 100 : (s < -100 ? -100 : s);
-  }
-  int32_t xf[XCHUNK];
-  int32_t sa = 0, sb = 0;
-  for (int e = 0; e < XCHUNK; ++e) {
-    const float v = ldexpf(x[e], s);
-    xf[e] = (v == v) ? (int32_t)rintf(v) : 0;
-    if (e < 16) sa += xf[e];
-    else sb += xf[e];
-  }
-  for (int i = 0; i < DIG_WORDS; ++i) dig[i] = 0;
-  for (int e = 0; e < XCHUNK; ++e) {
-    const int h = e >> 4, m = (e >> 2) & 3, b = e & 3;
-    if (kind == DIG_NIB) {
-      const uint32_t u = (uint32_t)(xf[e] + 0x888888);
-      for (int l = 0; l < 6; ++l) dig[m * 6 + l] |= (((u >> (4 * l)) & 15u) ^ 8u) << (4 * (2 * b + h));
-    } else {
-      const uint32_t u = (uint32_t)(xf[e] + 0x808080);
-      for (int l = 0; l < 3; ++l) dig[(h * 4 + m) * 3 + l] |= (((u >> (8 * l)) & 255u) ^ 128u) << (8 * b);
-    }
-  }
-  desc->inv_scale = ldexpf(1.0f, -s);
-  desc->sum = sa + sb;
-  desc->sumA = sa;
-  desc->sumB = sb;
-}
 
 // Four consecutive lanes (lane & 3 = m) digitize one 32-element chunk together.  Lane m passes the
 // chunk elements 4m..4m+3 and 16+4m..16+4m+3 in v[0..7]; the chunk scale and integer sums travel by
-// lane shuffles; lane m writes its six digit words and lane 0 the ChunkDesc at oc (a chunk base of
+// lane shuffles; lane m writes its eight digit words and lane 0 the ChunkDesc at oc (a chunk base of
 // DIG_CHUNK_WORDS words).  All four lanes must call it (write = false lets a lane take part without
-// storing).  Same digits as digitize_chunk.
+// storing).
 // (byte j of a) << 8 | (byte j of b), j < 4: one v_perm_b32 (bytes 0..3 of the selector pick from
 // the second operand, 4..7 from the first, 12 gives zero)
 __device__ inline uint32_t byte_gather(uint32_t a, uint32_t b, uint32_t j) {
   return __builtin_amdgcn_perm(a, b, 0x0C0C0000u | ((4u + j) << 8) | j);
 }
 
-// put(i, word) stores digit word i (0..23) or descriptor word i (24..27) of the chunk.
+// put(i, word) stores digit word i (0..31) or descriptor word i (32..35) of the chunk.
 template <class Put>
 __device__ inline void digitize_group_to(const float* v, int m, int kind, Put&& put, bool write) {
   float mx = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(v[i]));
-  mx = fmaxf(mx, __shfl_xor(mx, 1));
-  mx = fmaxf(mx, __shfl_xor(mx, 2));
-  int sh = 0;
-  if (mx > 0.f && mx == mx) sh = min(100, max(-100, 21 - ilogbf(mx)));  // mx * 2^sh in [2^21, 2^22)
-  int32_t xf[8];
-  int32_t sa = 0, sb = 0;
+  bool bad = false;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float t = ldexpf(v[i], sh);
-    xf[i] = (t == t) ? (int32_t)rintf(t) : 0;
-    if (i < 4) sa += xf[i];
-    else sb += xf[i];
+    const float a = fabsf(v[i]);
+    bad |= !(a <= 3.402823466e38f);  // NaN or infinity (fmaxf alone would skip a NaN)
+    mx = fmaxf(mx, a);
   }
-  sa += __shfl_xor(sa, 1);
-  sa += __shfl_xor(sa, 2);
-  sb += __shfl_xor(sb, 1);
-  sb += __shfl_xor(sb, 2);
+  mx = fmaxf(mx, __shfl_xor(mx, 1));
+  mx = fmaxf(mx, __shfl_xor(mx, 2));
+  int nb = bad ? 1 : 0;
+  nb |= __shfl_xor(nb, 1);
+  nb |= __shfl_xor(nb, 2);
+  bad = nb != 0;
+  // mx * 2^sh in [2^29, 2^30); 2^-sh stays a normal number
+  int sh = 0;
+  if (mx > 0.f && !bad) sh = min(126, max(-126, FIX_TOP - ilogbf(mx)));
+  int32_t xf[8];
+  // sum of x_fix as two exact 16-bit-split integer sums (|x_fix| <= 2^30 would overflow an int32 sum
+  // of 32 elements): x_fix = hi * 2^15 + lo with 0 <= lo < 2^15
+  int32_t shi = 0, slo = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    xf[i] = bad ? 0 : (int32_t)rintf(ldexpf(v[i], sh));
+    shi += xf[i] >> 15;
+    slo += xf[i] & 0x7FFF;
+  }
+  shi += __shfl_xor(shi, 1);
+  shi += __shfl_xor(shi, 2);
+  slo += __shfl_xor(slo, 1);
+  slo += __shfl_xor(slo, 2);
   if (!write) return;
-  // Adding 0x888888 (0x808080) and flipping the top bit of every nibble (byte) leaves balanced digit
-  // l of x_fix, as a 4-bit (8-bit) two's-complement number, in nibble (byte) l of u.  The digit
+  // Adding 0x88888888 (0x80808080) and flipping the top bit of every nibble (byte) leaves balanced
+  // digit l of x_fix, as a 4-bit (8-bit) two's-complement number, in nibble (byte) l of u.  The digit
   // words are then byte gathers: v_perm_b32 picks byte j of two words into two byte lanes.
   if (kind == DIG_NIB) {
-    // word m*6 + l, nibble 2b + h = digit l of element 16h + 4m + b  (v[4h + b]).  Byte b of a
+    // word m*8 + l, nibble 2b + h = digit l of element 16h + 4m + b  (v[4h + b]).  Byte b of a
     // word pairs element b (low nibble) with element 4+b (high nibble): e[b] holds those pairs for
     // the even levels (byte j = level 2j), o[b] for the odd ones.
     uint32_t e[4], o[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const uint32_t lo = (uint32_t)(xf[b] + 0x888888) ^ 0x888888u;
-      const uint32_t hi = (uint32_t)(xf[4 + b] + 0x888888) ^ 0x888888u;
-      e[b] = (lo & 0x0F0F0Fu) | ((hi & 0x0F0F0Fu) << 4);
-      o[b] = ((lo >> 4) & 0x0F0F0Fu) | (hi & 0xF0F0F0u);
+      const uint32_t lo = (uint32_t)(xf[b] + (int32_t)0x88888888u) ^ 0x88888888u;
+      const uint32_t hi = (uint32_t)(xf[4 + b] + (int32_t)0x88888888u) ^ 0x88888888u;
+      e[b] = (lo & 0x0F0F0F0Fu) | ((hi & 0x0F0F0F0Fu) << 4);
+      o[b] = ((lo >> 4) & 0x0F0F0F0Fu) | (hi & 0xF0F0F0F0u);
     }
 #pragma unroll
-    for (int l = 0; l < 6; ++l) {
+    for (int l = 0; l < NIB_LEVELS; ++l) {
       const uint32_t* E = (l & 1) ? o : e;
       const uint32_t j = (uint32_t)(l >> 1);
-      put(m * 6 + l, byte_gather(E[1], E[0], j) | (byte_gather(E[3], E[2], j) << 16));
+      put(m * NIB_LEVELS + l, byte_gather(E[1], E[0], j) | (byte_gather(E[3], E[2], j) << 16));
     }
   } else {
-    // word (h*4 + m)*3 + l, byte b = digit l of element 16h + 4m + b
+    // word (h*4 + m)*4 + l, byte b = digit l of element 16h + 4m + b
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       uint32_t u[4];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) u[b] = (uint32_t)(xf[4 * h + b] + 0x808080) ^ 0x808080u;
+      for (int b = 0; b < 4; ++b) u[b] = (uint32_t)(xf[4 * h + b] + (int32_t)0x80808080u) ^ 0x80808080u;
 #pragma unroll
-      for (int l = 0; l < 3; ++l)
-        put((h * 4 + m) * 3 + l, byte_gather(u[1], u[0], (uint32_t)l) | (byte_gather(u[3], u[2], (uint32_t)l) << 16));
+      for (int l = 0; l < BYTE_LEVELS; ++l)
+        put((h * 4 + m) * BYTE_LEVELS + l,
+            byte_gather(u[1], u[0], (uint32_t)l) | (byte_gather(u[3], u[2], (uint32_t)l) << 16));
     }
   }
   if (m == 0) {
-    put(DIG_WORDS, __float_as_uint(ldexpf(1.0f, -sh)));
-    put(DIG_WORDS + 1, (uint32_t)(sa + sb));
-    put(DIG_WORDS + 2, (uint32_t)sa);
-    put(DIG_WORDS + 3, (uint32_t)sb);
+    put(DIG_WORDS, __float_as_uint(bad ? __builtin_nanf("") : ldexpf(1.0f, -sh)));
+    put(DIG_WORDS + 1, __float_as_uint(__builtin_fmaf(32768.0f, (float)shi, (float)slo)));
+    put(DIG_WORDS + 2, (uint32_t)shi);
+    put(DIG_WORDS + 3, (uint32_t)slo);
   }
 }
 __device__ inline void digitize_group(const float* v, int m, int kind, uint32_t* oc, bool write) {
@@ -418,44 +403,54 @@ __host__ __device__ inline int32_t sdot4(uint32_t a, uint32_t b, int32_t c) {
 // The value of a chunk against its digit levels, sum_l base^l D_l with D_l the integer dot of the
 // quants with digit level l, assembled in Horner form: each level's dot chain starts from base x
 // the partial of the levels above it, so no level needs its own accumulator or conversion.
-//   nibble (base 16, six levels): hi = (D5*16 + D4)*16 + D3, lo = (D2*16 + D1)*16 + D0 with
-//     |D_l| <= 32*8*8 = 2048, so |hi|, |lo| < 2^20 (exact in int32 and fp32); value = 4096 hi + lo
-//   byte (base 256, three levels): hi = D2, lo = D1*256 + D0 with |D_l| <= 32*128*128 = 2^19, so
-//     |lo| < 2^28 fits int32; value = 65536 hi + lo (lo rounds to fp32 once: relative 2^-24)
-// The quant words w[0..NW) pair with digit words dig[m*6 + l] (nibble) / dig[m*3 + l] (byte).
+//   nibble (base 16, eight levels): hi = ((D7*16 + D6)*16 + D5)*16 + D4, lo likewise from D3..D0,
+//     |D_l| <= 32*8*8 = 2048, so |hi|, |lo| < 2^24 (exact in int32 and fp32); value = 65536 hi + lo
+//     with one rounding
+//   byte (base 256, four levels): hi = D3*256 + D2, lo = D1*256 + D0 with |D_l| <= 32*128*128 = 2^19,
+//     so |hi|, |lo| < 2^28 fit int32; value = 65536 hi + lo (each converts to fp32 with relative
+//     error 2^-24, then one fma)
+// The quant words w[0..NW) pair with digit words dig[m*8 + l] (nibble) / dig[m*4 + l] (byte).
 template <int NW>
 __host__ __device__ inline int32_t nib_chain(const uint32_t* w, const uint32_t* dig, int l, int32_t c) {
 #pragma unroll
-  for (int m = 0; m < NW; ++m) c = sdot8(w[m], dig[m * 6 + l], c);
+  for (int m = 0; m < NW; ++m) c = sdot8(w[m], dig[m * NIB_LEVELS + l], c);
   return c;
 }
-__host__ __device__ inline float nib_value(const uint32_t* w, const uint32_t* dig) {
-  int32_t hi = nib_chain<4>(w, dig, 5, 0);
+__host__ __device__ inline void nib_levels(const uint32_t* w, const uint32_t* dig, int32_t& hi, int32_t& lo) {
+  hi = nib_chain<4>(w, dig, 7, 0);
+  hi = nib_chain<4>(w, dig, 6, hi * 16);
+  hi = nib_chain<4>(w, dig, 5, hi * 16);
   hi = nib_chain<4>(w, dig, 4, hi * 16);
-  hi = nib_chain<4>(w, dig, 3, hi * 16);
-  int32_t lo = nib_chain<4>(w, dig, 2, 0);
+  lo = nib_chain<4>(w, dig, 3, 0);
+  lo = nib_chain<4>(w, dig, 2, lo * 16);
   lo = nib_chain<4>(w, dig, 1, lo * 16);
   lo = nib_chain<4>(w, dig, 0, lo * 16);
-  return __builtin_fmaf(4096.0f, (float)hi, (float)lo);
+}
+__host__ __device__ inline float nib_value(const uint32_t* w, const uint32_t* dig) {
+  int32_t hi, lo;
+  nib_levels(w, dig, hi, lo);
+  return __builtin_fmaf(65536.0f, (float)hi, (float)lo);
 }
 template <int NW>
 __host__ __device__ inline int32_t byte_chain(const uint32_t* w, const uint32_t* dig, int l, int32_t c) {
 #pragma unroll
-  for (int m = 0; m < NW; ++m) c = sdot4(w[m], dig[m * 3 + l], c);
+  for (int m = 0; m < NW; ++m) c = sdot4(w[m], dig[m * BYTE_LEVELS + l], c);
   return c;
 }
-// four quant words against the 12 digit words of one 16-element half
+// four quant words against the 16 digit words of one 16-element half
 __host__ __device__ inline float byte_value(const uint32_t* w, const uint32_t* dig) {
-  const int32_t hi = byte_chain<4>(w, dig, 2, 0);
+  int32_t hi = byte_chain<4>(w, dig, 3, 0);
+  hi = byte_chain<4>(w, dig, 2, hi * 256);
   int32_t lo = byte_chain<4>(w, dig, 1, 0);
   lo = byte_chain<4>(w, dig, 0, lo * 256);
   return __builtin_fmaf(65536.0f, (float)hi, (float)lo);
 }
-// both halves of a 32-element chunk (quant words wa against dig[0..12), wb against dig[12..24))
+// both halves of a 32-element chunk (quant words wa against dig[0..16), wb against dig[16..32))
 __host__ __device__ inline float byte_value2(const uint32_t* wa, const uint32_t* wb, const uint32_t* dig) {
-  const int32_t hi = byte_chain<4>(wb, dig + 12, 2, byte_chain<4>(wa, dig, 2, 0));
-  int32_t lo = byte_chain<4>(wb, dig + 12, 1, byte_chain<4>(wa, dig, 1, 0));
-  lo = byte_chain<4>(wb, dig + 12, 0, byte_chain<4>(wa, dig, 0, lo * 256));
+  int32_t hi = byte_chain<4>(wb, dig + 16, 3, byte_chain<4>(wa, dig, 3, 0));
+  hi = byte_chain<4>(wb, dig + 16, 2, byte_chain<4>(wa, dig, 2, hi * 256));
+  int32_t lo = byte_chain<4>(wb, dig + 16, 1, byte_chain<4>(wa, dig, 1, 0));
+  lo = byte_chain<4>(wb, dig + 16, 0, byte_chain<4>(wa, dig, 0, lo * 256));
   return __builtin_fmaf(65536.0f, (float)hi, (float)lo);
 }
 
@@ -528,7 +523,7 @@ struct Fmt<Q8_0> {
     u.d = half_bits_to_float(r.d);
     return u;
   }
-  // dig: the 12 digit words of this chunk's half of the 32-element activation chunk
+  // dig: the 16 digit words of this chunk's half of the 32-element activation chunk
   __host__ __device__ static float dotu(const U& u, const uint32_t* dig, const ChunkDesc& ds) {
     return ds.inv_scale * (u.d * byte_value(u.w, dig));
   }
@@ -608,7 +603,7 @@ struct Fmt<Q4_K> {
   }
   struct U {
     uint32_t w[4];  // q - 8 as signed nibbles
-    float c0, c1;   // sum w x = c0 * sum (q-8) x + c1 * sum x
+    float c0, c1;   // sum w x = c0 * sum q x + c1 * sum x
   };
   __host__ __device__ static U unpack(const Raw& r, int, int sub) {
     float dsc, dmm;
@@ -619,11 +614,18 @@ struct Fmt<Q4_K> {
     u.w[2] = r.q.z;
     u.w[3] = r.q.w;
     u.c0 = dsc;
-    u.c1 = __builtin_fmaf(8.0f, dsc, -dmm);
+    u.c1 = -dmm;
     return u;
   }
+  // sum_e q_e x_fix_e stays an exact integer until one conversion: the nibble dots give
+  // sum (q - 8) x_fix = 65536 hi + lo, and adding back 8 sum x_fix = 8 (32768 shi + slo) gives
+  // 65536 (hi + 4 shi) + (lo + 8 slo).  Folding the 8 into an fp32 coefficient instead would
+  // cancel two large rounded terms whenever a chunk's largest element meets a zero quant.
   __host__ __device__ static float dotu(const U& u, const uint32_t* dig, const ChunkDesc& ds) {
-    return ds.inv_scale * __builtin_fmaf(u.c0, nib_value(u.w, dig), u.c1 * (float)ds.sum);
+    int32_t hi, lo;
+    nib_levels(u.w, dig, hi, lo);
+    const float qx = __builtin_fmaf(65536.0f, (float)(hi + 4 * ds.shi), (float)(lo + 8 * ds.slo));
+    return ds.inv_scale * __builtin_fmaf(u.c0, qx, u.c1 * ds.sum);
   }
 };
 
@@ -679,7 +681,7 @@ struct Fmt<Q5_K> {
     return u;
   }
   __host__ __device__ static float dotu(const U& u, const uint32_t* dig, const ChunkDesc& ds) {
-    return ds.inv_scale * __builtin_fmaf(u.c0, byte_value2(u.lo, u.hi, dig), u.c1 * (float)ds.sum);
+    return ds.inv_scale * __builtin_fmaf(u.c0, byte_value2(u.lo, u.hi, dig), u.c1 * ds.sum);
   }
 };
 
@@ -749,7 +751,7 @@ struct Fmt<Q6_K> {
     return u;
   }
   __host__ __device__ static float dotu(const U& u, const uint32_t* dig, const ChunkDesc& ds) {
-    return ds.inv_scale * __builtin_fmaf(u.dA, byte_value(u.lo, dig), u.dB * byte_value(u.hi, dig + 12));
+    return ds.inv_scale * __builtin_fmaf(u.dA, byte_value(u.lo, dig), u.dB * byte_value(u.hi, dig + 16));
   }
 };
 

@@ -7,9 +7,9 @@
 //     every gridDim-th row block) and one K split;
 //   * each wave owns R rows of each block; lane l walks chunks l, l+64, ... of those rows, so every
 //     wave-wide load instruction reads 1 KiB of contiguous quant bytes (16 B per lane);
-//   * the activation arrives as block fixed-point digits (see qwg_formats.h): 28 words per 32
+//   * the activation arrives as block fixed-point digits (see qwg_formats.h): 36 words per 32
 //     elements, staged once per workgroup into LDS in a chunk-transposed layout -- 16-B slot q of
-//     chunk c of column n at (n*7 + q)*S + c, with the row stride S padded against bank conflicts
+//     chunk c of column n at (n*9 + q)*S + c, with the row stride S padded against bank conflicts
 //     of the staging writes -- so the 64 lanes of a wave read 64 consecutive slots (or it arrives
 //     as fp32 and the workgroup digitizes it into the same layout);
 //   * quants stay integers: nibble formats feed v_dot8_i32_i4 directly (stored as q XOR 8), the
@@ -162,13 +162,14 @@ struct GemvArgs {
   EpiArgs e;
 };
 
-constexpr int XSLOTS = DIG_CHUNK_WORDS / 4;  // 16-B slots per activation chunk (6 digit slots + desc)
+constexpr int XSLOTS = DIG_CHUNK_WORDS / 4;  // 16-B slots per activation chunk (8 digit slots + desc)
+constexpr int DSLOT = DIG_WORDS / 4;         // the descriptor's slot
 
-// LDS row stride (16-B slots) for n chunks: n rounded up to 7 mod 16.  The staging writes put the 7
-// slots of consecutive chunks into 7 rows; with this stride the 16 lanes an LDS write serves at a
-// time land on 16 distinct 16-byte bank groups (row q, chunk c -> group (7q + c) mod 16), where a
-// stride that is a multiple of 16 put all 7 rows of a chunk on the same banks.
-__host__ __device__ constexpr int lds_row_slots(int n) { return n + ((7 - n) % 16 + 16) % 16; }
+// LDS row stride (16-B slots) for n chunks: n rounded up to 9 mod 16.  The staging writes put the 9
+// slots of consecutive chunks into 9 rows; with this stride the 16 lanes an LDS write serves at a
+// time land on 16 distinct 16-byte bank groups (row q, chunk c -> group (9q + c) mod 16), where a
+// stride that is a multiple of 16 put all 9 rows of a chunk on the same banks.
+__host__ __device__ constexpr int lds_row_slots(int n) { return n + ((XSLOTS - n) % 16 + 16) % 16; }
 
 // Pipeline: each wave computes ng groups of R rows (group g: R rows at row0_of(g)), every group in
 // iterations of 64 chunks (lane l takes chunk l + 64 i).  The loop over all ng * nit iterations is
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(LB, (R == 4 && P == 2 ? 4 : 1)) void k_gemv(GemvArg
   using F = Fmt<QT>;
   constexpr int CW = F::CW;
   constexpr int WPX = XCHUNK / CW;               // weight chunks per activation chunk (2 for Q8_0)
-  constexpr int NDS = (CW == 16) ? 3 : 6;        // digit slots one weight chunk reads
+  constexpr int NDS = DIG_WORDS / 4 / WPX;       // digit slots one weight chunk reads
   extern __shared__ uint4 lds[];
   __shared__ float red[MAX_COLS][16];
   __shared__ float osh[MAX_COLS][64];
@@ -318,7 +319,7 @@ __global__ __launch_bounds__(LB, (R == 4 && P == 2 ? 4 : 1)) void k_gemv(GemvArg
 #pragma unroll
     for (int r = 0; r < R; ++r) u[r] = F::unpack(raw[r], cbase + cl, sub);
     const int xc = min(cl, nchs - 1) / WPX;
-    const int s0 = (WPX == 2) ? (cl & 1) * 3 : 0;  // first digit slot of this half (Q8_0)
+    const int s0 = (WPX == 2) ? (cl & 1) * NDS : 0;  // first digit slot of this half (Q8_0)
 #pragma unroll
     for (int n = 0; n < NCM; ++n) {
       if (NCM > 1 && n >= nc) break;  // one-column kernels always have nc == 1
@@ -331,12 +332,12 @@ __global__ __launch_bounds__(LB, (R == 4 && P == 2 ? 4 : 1)) void k_gemv(GemvArg
         dg[4 * q + 2] = v.z;
         dg[4 * q + 3] = v.w;
       }
-      const uint4 dv = lds[(n * XSLOTS + 6) * nxp + xc];
+      const uint4 dv = lds[(n * XSLOTS + DSLOT) * nxp + xc];
       ChunkDesc ds;
       ds.inv_scale = __uint_as_float(dv.x);
-      ds.sum = (int32_t)dv.y;
-      ds.sumA = (int32_t)dv.z;
-      ds.sumB = (int32_t)dv.w;
+      ds.sum = __uint_as_float(dv.y);
+      ds.shi = (int32_t)dv.z;
+      ds.slo = (int32_t)dv.w;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const float d = F::dotu(u[r], dg, ds);
@@ -492,24 +493,25 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const float* part, int kspl
 // This form takes 2..8 columns (one or two groups of four) when K is a multiple of 512.
 // For Q4_K, Q5_K and Q6_K (with byte activation digits: the producers of this kernel's input pick
 // the kind with gemv_digit_kind) each 16-row tile and 32-weight chunk is one v_mfma_i32_16x16x32_i8 with
-//   A (16 x 32): activation digits, slot m = 4 * column + level (level 3 is zero),
+//   A (16 x 32): activation digits, slot m = 4 * column + level,
 //   B (32 x 16): the chunk's quants as int8 bytes, one column per output row,
-// so the 4 x 3 digit levels of all columns meet every weight in one exact integer product.  With
+// so the 4 x 4 digit levels of all columns meet every weight in one exact integer product.  With
 // lane l = 16 g + n:
 //   B: row n, weights 4g..4g+3 and 16+4g..16+4g+3 of the chunk (its quant word g);
 //   A: slot n (column n / 4, level n % 4), the digits of those same eight elements;
 //   D: levels 0..3 of column g, row n -- so every lane finishes one (row, column) pair per chunk:
-//      value = 65536 D2 + (256 D1 + D0), scaled by the chunk's weight scales and activation scale.
+//      value = 65536 (256 D3 + D2) + (256 D1 + D0), scaled by the chunk's weight scales and
+//      activation scale.
 // Each lane loads one whole 16-B chunk (chunk c0 + g of row n, 64 contiguous bytes per row and lane
 // group) and four permlane swaps turn the four chunks' words into word g of each chunk (a 4 x 4
 // transpose across the lane groups).  Q6_K's two 16-weight sub-blocks per chunk take one MFMA each
 // (B masked to the low or high four bytes).
 // A workgroup of nw waves takes blocks of T = nw / S tiles; the S waves of a tile split its chunks
 // (K parts) and add their partial sums in wave order through LDS, so the result does not depend on
-// timing.  The grid is persistent over the blocks; the activation of one K split (416 B per chunk:
-// 384 B of digits, 4 x 8 B of (2^-s, 2^-s sum x_fix)) is staged once per workgroup.
-constexpr int MF_DIG = 48;  // 8-B digit entries per chunk and group of four columns: [word g][column][level]
-// LDS stride of a chunk's entries: one entry of padding (98 or 194 words), so the staging writes of
+// timing.  The grid is persistent over the blocks; the activation of one K split (552 B per chunk:
+// 520 B of digits, 4 x 8 B of (2^-s, 2^-s sum x_fix)) is staged once per workgroup.
+constexpr int MF_DIG = 64;  // 8-B digit entries per chunk and group of four columns: [word g][column][level]
+// LDS stride of a chunk's entries: one entry of padding (130 or 258 words), so the staging writes of
 // consecutive chunks spread over the banks
 __host__ __device__ constexpr int mf_dig_stride(int ng) { return ng * MF_DIG + 1; }
 // LDS bytes per chunk (digit entries and one (2^-s, 2^-s sum) pair per column) and per workgroup
@@ -535,9 +537,10 @@ __device__ __forceinline__ qwg_i32x4 mfma_i8(uint64_t a, uint64_t b) {
   return __builtin_amdgcn_mfma_i32_16x16x32_i8((long)a, (long)b, z, 0, 0, 0);
 }
 
-// 65536 D2 + 256 D1 + D0 (|256 D1 + D0| < 2^27 is exact in int32; one fp32 rounding)
+// 2^24 D3 + 2^16 D2 + 256 D1 + D0 as 65536 (256 D3 + D2) + (256 D1 + D0): each bracket is below 2^28
+// in magnitude (|D_l| <= 32 * 128 * 128), exact in int32, and rounds once to fp32 before the fma
 __device__ __forceinline__ float mf_value(const qwg_i32x4& d) {
-  return __builtin_fmaf(65536.0f, (float)d[2], (float)(d[0] + d[1] * 256));
+  return __builtin_fmaf(65536.0f, (float)(d[2] + d[3] * 256), (float)(d[0] + d[1] * 256));
 }
 
 // Steps are two superblocks (16 chunks) of the lane's row: chunk c0 + 4 qq + g in quarter qq.
@@ -639,13 +642,15 @@ __global__ __launch_bounds__(NG == 1 ? 1024 : 512) void k_gemv_mfma(GemvArgs a, 
 #pragma unroll
       for (int i = 0; i < DIG_CHUNK_WORDS; ++i) wd[i] = 0;
     }
-    const int ent = c * DSTR + (col >> 2) * MF_DIG + (col & 3) * 3;
+    const int ent = c * DSTR + (col >> 2) * MF_DIG + (col & 3) * BYTE_LEVELS;
 #pragma unroll
     for (int gg = 0; gg < 4; ++gg)
 #pragma unroll
-      for (int lv = 0; lv < 3; ++lv) ldig[ent + gg * 12 + lv] = make_uint2(wd[gg * 3 + lv], wd[12 + gg * 3 + lv]);
+      for (int lv = 0; lv < BYTE_LEVELS; ++lv)
+        ldig[ent + gg * 4 * BYTE_LEVELS + lv] =
+            make_uint2(wd[gg * BYTE_LEVELS + lv], wd[16 + gg * BYTE_LEVELS + lv]);
     const float inv = __uint_as_float(wd[DIG_WORDS]);
-    ldesc[col * dstr + c] = make_float2(inv, inv * (float)(int32_t)wd[DIG_WORDS + 1]);
+    ldesc[col * dstr + c] = make_float2(inv, inv * __uint_as_float(wd[DIG_WORDS + 1]));
   }
   if (EPI != EPI_PART && a.e.sq_in) rms_partials(a.e, nc, red);
   __syncthreads();
@@ -659,8 +664,7 @@ __global__ __launch_bounds__(NG == 1 ? 1024 : 512) void k_gemv_mfma(GemvArgs a, 
   const int nst = nxs / mf_step_chunks<QT>();  // steps of two superblocks
   const int st0 = s * nst / S, st1 = (s + 1) * nst / S;
   const int cbase = kbeg / XCHUNK;
-  const int aoff = g * 12 + (n >> 2) * 3 + min(n & 3, 2);  // this lane's A entry within a group
-  const uint64_t amask = (n & 3) == 3 ? 0ull : ~0ull;       // level 3 is zero
+  const int aoff = g * 4 * BYTE_LEVELS + n;  // this lane's A entry within a group: column n / 4, level n % 4
   // per-lane bit-move amounts: Q5_K fifth bits (rotations), Q6_K high pairs (shifts)
   const uint32_t rot_lo = (uint32_t)(28 + 2 * g) & 31u, rot_hi = (uint32_t)(29 + 2 * g) & 31u;
   const uint32_t shl_lo = (g & 1) ? 2u : 6u, shl_hi = (g & 1) ? 0u : 4u;
@@ -692,7 +696,7 @@ __global__ __launch_bounds__(NG == 1 ? 1024 : 512) void k_gemv_mfma(GemvArgs a, 
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint2 av = ldig[(cc + j) * DSTR + cg * MF_DIG + aoff];
-        A[j] = ((uint64_t)av.x | ((uint64_t)av.y << 32)) & amask;
+        A[j] = (uint64_t)av.x | ((uint64_t)av.y << 32);
       }
     };
     load_group(0);
@@ -1031,16 +1035,16 @@ GemvPlan plan_gemv(int qt, int64_t rows, int64_t k, int nc, int epi, int mfma) {
   const bool tall = p.ncm == 1 && p.ksplit == 1 && epi == EPI_STORE &&
                     (rows + blk1 - 1) / blk1 > 4 * PERSISTENT_WGS1;
   // explicit overrides (tuning and tests)
-  if (g_waves == 2 || g_waves == 4 || g_waves == 8 || (g_waves == 16 && p.ncm == 1)) p.waves = g_waves;
+  if (g_waves >= 1 && (g_waves <= 8 || (g_waves <= 16 && p.ncm == 1))) p.waves = g_waves;
   if (p.ncm == 1 && (g_rows == 1 || g_rows == 2 || g_rows == 4)) p.rows_per_wave = g_rows;
   if (g_depth == 1 || g_depth == 2) p.depth = g_depth;
   if (g_passes == 1 || g_passes == 2 || g_passes == 4 || g_passes == 8) p.passes = g_passes;
   if (pairs && p.rows_per_wave < 2) p.rows_per_wave = 2;
-  if (p.waves == 16) {  // compiled for two rows and one-ahead loads only
+  if (p.waves > 8) {  // the 1024-thread kernels are compiled for two rows and one-ahead loads only
     p.rows_per_wave = 2;
     p.depth = 1;
   }
-  if ((p.rows_per_wave == 4 || p.waves == 16) && p.passes >= 4) p.passes = 2;
+  if ((p.rows_per_wave == 4 || p.waves > 8) && p.passes >= 4) p.passes = 2;
   // compiled row-pass variants: one column, one-ahead loads, digitizing epilogues; two rows with two
   // or four passes (sixteen waves: two), four rows with two passes for the formats whose four-row
   // kernel fits 128 registers
@@ -1081,8 +1085,8 @@ bool gemv_can_digitize_input(const GemvPlan& p, int epi) {
   if (p.mfma) return false;
   if (p.ncm == 4) return epi == EPI_RESID && p.ksplit > 1 && p.passes == 0 && p.depth == 1 && p.waves == 8;
   if (!(p.ncm == 1 && p.ksplit == 1 && epi == EPI_RESID && p.depth == 1)) return false;
-  if (p.waves == 16) return p.rows_per_wave == 2 && p.passes == 1;
-  return p.waves == 8 && ((p.rows_per_wave == 4 && p.passes == 1) || (p.rows_per_wave == 2 && p.passes == 2));
+  if (p.waves > 8) return p.rows_per_wave == 2 && p.passes == 1;
+  return (p.rows_per_wave == 4 && p.passes == 1) || (p.rows_per_wave == 2 && p.passes == 2);
 }
 
 bool gemv_can_digitize_output(const GemvPlan& p, int epi, int64_t rows) {
@@ -1145,7 +1149,7 @@ static hipError_t launch_fmt(const GemvArgs& a, const GemvPlan& p, int epi, dim3
         go(dd, k_gemv<QT, 4, 4, EPI_PART, 1, 0, 512, 1>, grid, block, lds, a);
       else
         go(dd, k_gemv<QT, 4, 2, EPI_PART, 1, 0, 512, 1>, grid, block, lds, a);
-    } else if (p.waves == 16)
+    } else if (p.waves > 8)
       go(dd, k_gemv<QT, 1, 2, EPI_RESID, 1, 1, 1024, 1>, grid, block, lds, a);
     else if (r == 2)
       go(dd, k_gemv<QT, 1, 2, EPI_RESID, 1, 2, 512, 1>, grid, block, lds, a);
@@ -1153,7 +1157,7 @@ static hipError_t launch_fmt(const GemvArgs& a, const GemvPlan& p, int epi, dim3
       go(dd, k_gemv<QT, 1, 4, EPI_RESID, 1, 1, 512, 1>, grid, block, lds, a);
     return hipGetLastError();
   }
-  if (p.waves == 16) {  // sixteen waves: two rows, one-ahead loads, one or two passes
+  if (p.waves > 8) {  // more than eight waves: two rows, one-ahead loads, one or two passes
     if (p.ncm != 1 || r != 2 || d != 1) return hipErrorInvalidValue;
     if (p.passes == 2) return launch_pn<QT, 2, 2, 1024>(a, epi, grid, block, lds, dd);
     return launch_t<QT, 1, 2, 1, 1, 1024>(a, epi, p.ksplit, grid, block, lds, dd);

@@ -10,7 +10,7 @@ namespace qwg {
 
 constexpr int HEAD_DIM = 128;   // every supported model uses 128-wide heads
 constexpr int MAX_COLS = 8;     // widest multi-column pass
-constexpr size_t LDS_BUDGET = 120 * 1024;  // dynamic LDS per workgroup (gfx950: 160 KiB per CU)
+constexpr size_t LDS_BUDGET = 150 * 1024;  // dynamic LDS per workgroup (gfx950: 160 KiB per CU)
 
 // What the GEMV does with each finished output row (columns n < nc).
 enum Epi : int {
@@ -73,7 +73,7 @@ GemvPlan plan_gemv(int qt, int64_t rows, int64_t k, int nc, int epi, int mfma = 
 void set_gemv_geometry(int waves, int rows_per_wave, int depth, int passes);
 void set_gemv_mfma(int on);
 
-// Bytes of the activation digits of one column of length k (28 words per 32 elements).
+// Bytes of the activation digits of one column of length k (36 words per 32 elements).
 inline int64_t digit_bytes(int64_t k) { return k / XCHUNK * DIG_CHUNK_WORDS * 4; }
 
 // Digit kind (DIG_NIB / DIG_BYTE) that a GEMV over weights of type qt with K = k and nc columns
@@ -104,7 +104,8 @@ hipError_t launch_rmsnorm(const float* x, const float* g, int64_t n, float eps, 
 hipError_t launch_rope(float* v, int n_heads, const float* table, int pos, hipStream_t st);
 hipError_t launch_swiglu(const float* g, const float* u, int64_t n, float* out, hipStream_t st);
 hipError_t launch_cosine(const float* a, const float* b, int64_t n, float* out, hipStream_t st);
-// keys: scratch of nc 64-bit words (cleared by the launch itself)
+// keys: scratch of nc 64-bit words (cleared by the launch itself, with a kernel: no memset node)
+constexpr size_t ARGMAX_WORK_BYTES = MAX_COLS * 8;
 hipError_t launch_argmax(const float* x, int64_t n, int nc, int64_t x_stride, int32_t* out, hipStream_t st,
                          unsigned long long* keys);
 
@@ -121,10 +122,13 @@ hipError_t launch_attn(const float* q, int64_t q_stride, const uint16_t* kc, con
                        const AttnPlan& p, hipStream_t st, uint32_t* dig_out = nullptr, int64_t dig_stride = 0,
                        int dig_kind = 0);
 
-// plain streaming read of `bytes` (a multiple of 16) from src; one checksum word per wave into
-// sink (READ_GRID * 8 words)
+// plain streaming read of `bytes` (a multiple of 16) from src by `grid` workgroups of 8 waves (0:
+// READ_GRID), each lane keeping `unroll` (4, 8 or 16; 0: 4) 16-byte loads in flight; one checksum
+// word per wave into sink (grid * 8 words); optional events at the kernel's own start and end
 constexpr int READ_GRID = 1024;
-hipError_t launch_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t st);
+constexpr int READ_GRID_MAX = 8192;
+hipError_t launch_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t st, int grid = 0, int unroll = 0,
+                       hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 // Output values that the fused digitization of a GEMV covers per workgroup must be whole
 // 32-element chunks: true if every workgroup of the plan writes whole chunks of the output.

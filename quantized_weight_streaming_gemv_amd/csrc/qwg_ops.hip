@@ -2,6 +2,7 @@
 // row, RMSNorm, RoPE, grouped-query decode attention over the fp16 KV cache, SwiGLU, cosine and
 // argmax (the Llama pieces listed under "Key features" on the NTransformer page, and the cuda/
 // kernel list of its "Architecture overview": GEMV, RMSNorm, RoPE, SwiGLU, softmax).
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -200,10 +201,12 @@ hipError_t launch_cosine(const float* a, const float* b, int64_t n, float* out, 
 
 // Greedy choice over many workgroups: each reduces its slice to (value, index) and folds it into a
 // 64-bit key with one atomic max; key = (order-preserving bits of the value) << 32 | ~index, so the
-// largest value wins and, among equal values, the lowest index.  NaNs never win.
+// largest value wins and, among equal values, the lowest index.  A NaN ranks above every number (its
+// value bits become all ones), so a non-finite logit vector is visible in the chosen token: the first
+// NaN wins, as numpy's argmax does.
 __device__ __forceinline__ unsigned long long am_key(float v, int i) {
-  if (v != v) return 0ull;
   uint32_t b = __float_as_uint(v);
+  if (v != v) return (0xFFFFFFFFull << 32) | (uint32_t)(~(uint32_t)i);
   b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
   return ((unsigned long long)b << 32) | (uint32_t)(~(uint32_t)i);
 }
@@ -511,33 +514,42 @@ hipError_t launch_attn(const float* q, int64_t q_stride, const uint16_t* kc, con
 // Streaming read of n16 16-byte words: wave w of the grid reads one contiguous segment, lane l the
 // words l, l+64, ... of it, four 16-B non-temporal loads in flight per lane (the GEMV's own load
 // pattern without its arithmetic).  One XOR checksum per wave keeps the loads alive.
+template <int U>
 __global__ __launch_bounds__(512) void k_read(const uint4* __restrict__ p, int64_t n16, int64_t per_wave,
                                               uint32_t* sink) {
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 6);
   const int64_t beg = wave * per_wave, end = min(beg + per_wave, n16);
   uint32_t acc = 0;
-  for (int64_t i = beg + lane; i < end; i += 256) {
-    uint4 v[4];
+  for (int64_t i = beg + lane; i < end; i += 64 * U) {
+    uint4 v[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int64_t j = i + 64 * u;
       v[u] = j < end ? ld_stream_u4((const uint8_t*)(p + j)) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) acc ^= __shfl_xor(acc, off);
   if (lane == 0) sink[wave] = acc;
 }
 
-hipError_t launch_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t st) {
+hipError_t launch_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t st, int grid, int unroll,
+                       hipEvent_t ev_start, hipEvent_t ev_stop) {
   const int64_t n16 = bytes / 16;
-  const int grid = READ_GRID;
+  if (grid <= 0) grid = READ_GRID;
+  if (unroll <= 0) unroll = 4;
   const int64_t waves = (int64_t)grid * 8;
   const int64_t per_wave = ((n16 + waves - 1) / waves + 63) / 64 * 64;
-  hipLaunchKernelGGL(k_read, dim3(grid), dim3(512), 0, st, (const uint4*)src, n16, per_wave, sink);
+  const uint4* p = (const uint4*)src;
+  switch (unroll) {
+    case 4: hipExtLaunchKernelGGL(k_read<4>, dim3(grid), dim3(512), 0, st, ev_start, ev_stop, 0u, p, n16, per_wave, sink); break;
+    case 8: hipExtLaunchKernelGGL(k_read<8>, dim3(grid), dim3(512), 0, st, ev_start, ev_stop, 0u, p, n16, per_wave, sink); break;
+    case 16: hipExtLaunchKernelGGL(k_read<16>, dim3(grid), dim3(512), 0, st, ev_start, ev_stop, 0u, p, n16, per_wave, sink); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -62,14 +62,22 @@ def dequantize(qtype: int, packed, rows: int, k: int, out=None, stream=None):
     return out
 
 
-def gemv(qtype: int, packed, rows: int, k: int, x, out=None, stream=None):
-    """x: fp32 [k] or [n][k] (n <= 8) -> y fp32 [rows] or [n][rows]."""
+def gemv_work_bytes(qtype: int, rows: int, k: int, n_cols: int) -> int:
+    return int(lib().qwg_gemv_work_bytes(qtype, rows, k, n_cols))
+
+
+def gemv(qtype: int, packed, rows: int, k: int, x, out=None, work=None, stream=None):
+    """x: fp32 [k] or [n][k] (n <= 8) -> y fp32 [rows] or [n][rows].  work: device scratch of
+    gemv_work_bytes(...) bytes (allocated here when not given)."""
     torch = _torch()
     x2 = x.reshape(-1, k)
     n = x2.shape[0]
     if out is None:
         out = torch.empty((n, rows), dtype=torch.float32, device=x.device)
-    call("qwg_gemv", qtype, _ptr(packed), rows, k, _ptr(x2), n, _ptr(out), _stream(stream))
+    if work is None:
+        work = torch.empty(max(gemv_work_bytes(qtype, rows, k, n), 16), dtype=torch.uint8, device=x.device)
+    call("qwg_gemv", qtype, _ptr(packed), rows, k, _ptr(x2), n, _ptr(out), _ptr(work),
+         work.numel() * work.element_size(), _stream(stream))
     return out.reshape(rows) if x.dim() == 1 else out
 
 
@@ -139,19 +147,26 @@ def cosine(a, b, out=None, stream=None):
     return out
 
 
-def argmax(x, out=None, stream=None):
+def argmax(x, out=None, work=None, stream=None):
     torch = _torch()
     if out is None:
         out = torch.empty(1, dtype=torch.int32, device=x.device)
-    call("qwg_argmax", _ptr(x), x.numel(), _ptr(out), _stream(stream))
+    if work is None:
+        work = torch.empty(int(lib().qwg_argmax_work_bytes()), dtype=torch.uint8, device=x.device)
+    call("qwg_argmax", _ptr(x), x.numel(), _ptr(out), _ptr(work), work.numel() * work.element_size(),
+         _stream(stream))
     return out
 
 
-def read_bytes(src, nbytes: Optional[int] = None, sink=None, stream=None):
-    """Plain streaming read of a device tensor's bytes (the achievable-bandwidth reference)."""
+def read_bytes(src, nbytes: Optional[int] = None, sink=None, grid: int = 0, unroll: int = 0, timed: bool = False,
+               stream=None):
+    """Plain streaming read of a device tensor's bytes (the achievable-bandwidth reference).  Returns the
+    sink, or with timed=True the kernel's duration in ms (the call then waits for it)."""
     torch = _torch()
     n = src.numel() * src.element_size() if nbytes is None else nbytes
     if sink is None:
         sink = torch.empty(int(lib().qwg_read_sink_words()), dtype=torch.int32, device=src.device)
-    call("qwg_read_bytes", _ptr(src), n, _ptr(sink), _stream(stream))
-    return sink
+    ms = ctypes.c_float(0.0)
+    call("qwg_read_bytes", _ptr(src), n, _ptr(sink), grid, unroll, ctypes.byref(ms) if timed else None,
+         _stream(stream))
+    return float(ms.value) if timed else sink

@@ -76,9 +76,21 @@ def test_pointer_checks_without_gpu():
         pytest.skip("libqwg.so not built")
     L = _lib.lib()
     A, M = 1 << 20, (1 << 20) + 4  # aligned / misaligned fake addresses
-    assert L.qwg_gemv(12, M, 16, 256, A, 1, A, None) == -1
-    assert L.qwg_gemv(12, A, 16, 256, M, 1, A, None) == -1
-    assert L.qwg_gemv(12, None, 16, 256, A, 1, A, None) == -1
+    gw = L.qwg_gemv_work_bytes(12, 16, 256, 1)
+    assert gw > 0 and L.qwg_gemv_work_bytes(12, 16, 300, 1) == 0 and L.qwg_gemv_work_bytes(12, 16, 256, 9) == 0
+    assert L.qwg_gemv(12, M, 16, 256, A, 1, A, A, gw, None) == -1
+    assert L.qwg_gemv(12, A, 16, 256, M, 1, A, A, gw, None) == -1
+    assert L.qwg_gemv(12, A, 16, 256, A, 1, A, M, gw, None) == -1
+    assert L.qwg_gemv(12, None, 16, 256, A, 1, A, A, gw, None) == -1
+    assert L.qwg_gemv(12, A, 16, 256, A, 1, A, None, gw, None) == -1
+    assert L.qwg_gemv(12, A, 16, 256, A, 1, A, A, gw - 16, None) == -3
+    # K-split shapes need room for the partial sums as well as the digits
+    assert L.qwg_gemv_work_bytes(12, 4096, 65536, 8) > L.qwg_gemv_work_bytes(12, 4096, 4096, 8)
+    aw = L.qwg_argmax_work_bytes()
+    assert aw >= 8
+    assert L.qwg_argmax(A, 100, A, A, aw - 1, None) == -3
+    assert L.qwg_argmax(A, 100, A, None, aw, None) == -1
+    assert L.qwg_argmax(A, 100, A, A + 4, aw, None) == -1
     assert L.qwg_dequantize(12, A, 16, 256, M, None) == -1
     wb = L.qwg_attn_work_bytes(100, 8, 2, 128, 1)
     assert wb > 0

@@ -113,6 +113,119 @@ def test_gemv_several_columns_both_forms(ops, qt, shape, nc, mfma):
     assert ok.all(), (np.argwhere(~ok)[:5], y[~ok][:5], yr[~ok][:5])
 
 
+def _outlier_x(k, nc, ratio, seed):
+    """x ~ N(0,1) with one element of magnitude `ratio` in every 32-element chunk (position 7c+3 mod
+    32, alternating sign): every chunk's fixed-point scale is set by its outlier."""
+    x = synth.normal_f32(synth.key(11, seed), nc * k).reshape(nc, k)
+    cols = np.array([32 * c + (7 * c + 3) % 32 for c in range(k // 32)])
+    x[:, cols] = ratio * np.where(np.arange(len(cols)) % 2 == 0, 1.0, -1.0)
+    return x, cols
+
+
+FORMS = [(1, True), (4, True), (4, False)]
+
+
+@pytest.mark.parametrize("qt", QTS, ids=[synth.QTYPE_NAMES[q] for q in QTS])
+@pytest.mark.parametrize("ratio", [1e2, 1e4, 1e6], ids=["1e2", "1e4", "1e6"])
+@pytest.mark.parametrize("zero_under", [False, True], ids=["w", "w0"])
+@pytest.mark.parametrize("form", FORMS, ids=["1col", "4col-mfma", "4col-dot"])
+def test_gemv_outlier_in_every_chunk(ops, qt, ratio, zero_under, form):
+    """An outlier of 1e2..1e6 x the typical magnitude in every 32-element chunk (with the weights
+    under it kept, or all zero so the outliers add nothing to sum|w x|): rows stay within
+    |y - y_ref| <= 1e-4 sum|w x| + 1e-6 on the one-column kernel and both several-column forms."""
+    import blockedit
+    nc, mfma = form
+    rows, k = 96, 2048
+    W = synth.matrix(synth.DEFAULT_DIST[qt], k, rows, tkey=synth.key(11, qt * 1000 + 1))
+    x, cols = _outlier_x(k, nc, ratio, 2 + nc)
+    if zero_under:
+        W = blockedit.zero_columns(qt, W, rows, k, cols)
+        assert np.all(oracle.dequant(qt, W, rows, k)[:, cols] == 0)
+    ops.set_gemv_mfma(mfma)
+    try:
+        y = ops.gemv(qt, packed_of(ops, qt, W, rows, k), rows, k, dev(x)).cpu().numpy()
+    finally:
+        ops.set_gemv_mfma(True)
+    yr, ar = oracle.gemv(qt, W, rows, k, x)
+    ok = gemv_ok(y, yr, ar)
+    worst = np.max(np.abs(y - yr) / (1e-4 * ar + 1e-6))
+    assert ok.all(), (worst, np.argwhere(~ok)[:5])
+
+
+@pytest.mark.parametrize("qt", QTS, ids=[synth.QTYPE_NAMES[q] for q in QTS])
+@pytest.mark.parametrize("form", FORMS, ids=["1col", "4col-mfma", "4col-dot"])
+def test_gemv_chunk_magnitudes(ops, qt, form):
+    """Chunks of very different magnitudes in one vector: all-zero chunks, chunks of fp32 subnormals,
+    chunks near 1e30 and 1e34, chunks mixing 1e-30 and 1 -- each chunk has its own power-of-two
+    scale, which stays a normal fp32 number.  (Magnitudes whose exact partial sums overflow fp32 are
+    outside what an fp32 result can hold and are not asked of it.)"""
+    nc, mfma = form
+    rows, k = 80, 2048
+    W = synth.matrix(synth.DEFAULT_DIST[qt], k, rows, tkey=synth.key(12, qt * 1000 + 1))
+    x = synth.normal_f32(synth.key(12, 5 + nc), nc * k).reshape(nc, k)
+    x[:, 0:32] = 0.0
+    x[:, 64:96] *= np.float32(1e-40)           # subnormal
+    x[:, 128:160] *= np.float32(1e30)
+    x[:, 192:208] *= np.float32(1e-30)         # half of a chunk tiny, half normal
+    x[:, 256:288] = np.float32(3.0e-45)        # the smallest subnormals
+    x[:, 320:352] *= np.float32(1e34)
+    ops.set_gemv_mfma(mfma)
+    try:
+        y = ops.gemv(qt, packed_of(ops, qt, W, rows, k), rows, k, dev(x)).cpu().numpy()
+    finally:
+        ops.set_gemv_mfma(True)
+    yr, ar = oracle.gemv(qt, W, rows, k, x)
+    assert np.isfinite(y).all()
+    ok = gemv_ok(y, yr, ar)
+    assert ok.all(), np.max(np.abs(y - yr) / (1e-4 * ar + 1e-6))
+
+
+@pytest.mark.parametrize("qt", QTS, ids=[synth.QTYPE_NAMES[q] for q in QTS])
+@pytest.mark.parametrize("form", FORMS, ids=["1col", "4col-mfma", "4col-dot"])
+@pytest.mark.parametrize("bad", ["nan", "inf", "-inf"])
+def test_gemv_non_finite_input_propagates(ops, qt, form, bad):
+    """A NaN or an infinity in the activation makes every row non-finite, as the exact sum is (the
+    oracle gives NaN, +-inf, or NaN where a zero weight meets the infinity); the other columns of a
+    several-column call stay finite and within the row bound."""
+    nc, mfma = form
+    rows, k = 64, 1024
+    W = synth.matrix(synth.DEFAULT_DIST[qt], k, rows, tkey=synth.key(13, qt * 1000 + 1))
+    x = synth.normal_f32(synth.key(13, 5 + nc), nc * k).reshape(nc, k)
+    x[0, 517] = {"nan": np.nan, "inf": np.inf, "-inf": -np.inf}[bad]
+    ops.set_gemv_mfma(mfma)
+    try:
+        y = ops.gemv(qt, packed_of(ops, qt, W, rows, k), rows, k, dev(x)).cpu().numpy()
+    finally:
+        ops.set_gemv_mfma(True)
+    with np.errstate(invalid="ignore"):
+        yr, ar = oracle.gemv(qt, W, rows, k, x)
+    assert not np.isfinite(yr[0]).any() and not np.isfinite(y[0]).any()
+    if nc > 1:
+        assert gemv_ok(y[1:], yr[1:], ar[1:]).all()
+
+
+def test_gemv_two_streams_in_flight(ops):
+    """Two GEMVs in flight at once on two streams, each with its own caller-owned work buffer: both
+    match the oracle (the library keeps no scratch of its own that they could share)."""
+    qt, rows, k = synth.Q4_K, 4096, 8192
+    W = synth.matrix(synth.DEFAULT_DIST[qt], k, rows, tkey=synth.key(14, 1))
+    P = packed_of(ops, qt, W, rows, k)
+    xs = [synth.normal_f32(synth.key(14, 2 + i), 4 * k).reshape(4, k) for i in range(2)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    dx = [dev(x) for x in xs]
+    outs = [torch.empty((4, rows), dtype=torch.float32, device=DEV) for _ in range(2)]
+    works = [torch.empty(ops.gemv_work_bytes(qt, rows, k, 4), dtype=torch.uint8, device=DEV) for _ in range(2)]
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for i in (0, 1):
+            with torch.cuda.stream(streams[i]):
+                ops.gemv(qt, P, rows, k, dx[i], out=outs[i], work=works[i], stream=streams[i])
+    torch.cuda.synchronize()
+    for i in (0, 1):
+        yr, ar = oracle.gemv(qt, W, rows, k, xs[i])
+        assert gemv_ok(outs[i].cpu().numpy(), yr, ar).all(), i
+
+
 def test_gemv_q8_0_4096_full(ops):
     """The single Q8_0 GEMV workload: W 4096 x 4096, q ~ U[-127,127], d = |N|*0.02, x ~ N(0,1)."""
     qt, rows, k = synth.Q8_0, 4096, 4096
@@ -195,8 +308,24 @@ def test_attention(ops, nq, nkv, npos, nc):
         out = ops.attn_decode(dev(q), dev(kc.view(np.int16)), dev(vc.view(np.int16)), npos, nq, nkv, hd, nc,
                               work=work).cpu().numpy()
         for j in range(nc):
-            ref = oracle.attention(q[j], kc, vc, npos + j, nq, nkv, hd)
-            assert rel_l2(out[j], ref) < 1e-5, (rep, j)
+            ref = oracle.attention(q[j], kc, vc, npos + j, nq, nkv, hd).reshape(nq, hd)
+            # element-wise, from fp32 arithmetic: each output is a convex combination of its KV
+            # head's V rows, so it is off by at most max|V| times (twice the worst score error,
+            # 128 roundings of sum_i |q_i k_i| / sqrt(128), plus one rounding per position of a
+            # split, per split merged and a few for exp and the normalisation)
+            n = npos + j
+            kf = np.abs(kc[:n].astype(np.float64))
+            vmax = np.abs(vc[:n].astype(np.float64)).max(axis=(0, 2))  # per KV head
+            qa = np.abs(q[j].astype(np.float64)).reshape(nq, hd)
+            u = 2.0 ** -24
+            bound = np.empty((nq, 1))
+            for h in range(nq):
+                g = h // (nq // nkv)
+                ds = hd * u * (kf[:, g, :] @ qa[h]).max() / np.sqrt(hd)
+                bound[h] = vmax[g] * (2 * ds + (64 + (n + 63) // 64 + 8) * u)
+            err = np.abs(out[j].reshape(nq, hd) - ref)
+            assert (err <= bound).all(), (rep, j, float((err / bound).max()))
+            assert rel_l2(out[j], ref.reshape(-1)) < 1e-5, (rep, j)
 
 
 def test_swiglu_cosine_argmax(ops):
@@ -215,6 +344,12 @@ def test_swiglu_cosine_argmax(ops):
     x = synth.normal_f32(synth.key(5, 5), 128256)
     x[777] = x[90000] = 50.0
     assert ops.argmax(dev(x)).item() == 777 == oracle.argmax_f32(x)
+    # a NaN ranks above every number (the first NaN wins), an infinity above every finite value
+    x[100000] = np.inf
+    assert ops.argmax(dev(x)).item() == 100000 == oracle.argmax_f32(x)
+    x[5000] = x[3000] = np.nan
+    assert ops.argmax(dev(x)).item() == 3000 == oracle.argmax_f32(x)
+    assert ops.argmax(dev(np.full(4000, np.nan, np.float32))).item() == 0 == oracle.argmax_f32(np.full(4000, np.nan))
 
 
 @pytest.mark.parametrize("qt", QTS, ids=[synth.QTYPE_NAMES[q] for q in QTS])
