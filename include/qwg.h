@@ -107,6 +107,12 @@ size_t qwg_gemv_work_bytes(int qtype, int64_t rows, int64_t k, int n_cols);
 int qwg_gemv(int qtype, const void* d_packed, int64_t rows, int64_t k, const float* d_x, int n_cols, float* d_y,
              void* d_work, size_t work_bytes, void* stream);
 
+/* qwg_gemv that waits for the GEMV and stores the duration (ms) of its kernel(s) in *h_kernel_ms, from
+ * events recorded by the dispatch itself at the kernel's start and end (the activation's digitization
+ * before it is not included): the measurement behind the single-GEMV bandwidth figures. */
+int qwg_gemv_timed(int qtype, const void* d_packed, int64_t rows, int64_t k, const float* d_x, int n_cols,
+                   float* d_y, void* d_work, size_t work_bytes, float* h_kernel_ms, void* stream);
+
 /* Launch geometry of subsequent GEMV launches in this process, for tuning; 0 keeps the default:
  *   waves_per_group  1..8; up to 16 for single-column GEMVs (above 8: 2 rows per wave, depth 1,
  *                    <= 2 passes);
@@ -281,9 +287,17 @@ int qwg_model_set_capture(qwg_model* m, int on);
 int qwg_model_get_hidden(qwg_model* m, int layer, float* h_out);
 /* Time the GEMV kernels of one weight class over the next steps with HIP events on the compute
  * stream, recorded by the kernel dispatch itself at the kernel's start and end (tensor_id
- * QWG_T_WQ = fused QKV, WO, WGATE = fused gate|up, WDOWN, HEAD; -1 = off). */
+ * QWG_T_WQ = fused QKV, WO, WGATE = fused gate|up, WDOWN, HEAD; QWG_TIME_ALL_GEMV = every GEMV of
+ * the step, each under its own class; -1 = off).  Clears the accumulated times. */
+#define QWG_TIME_ALL_GEMV (-2)
 int qwg_model_set_timing(qwg_model* m, int tensor_id);
-/* Sum of the timed kernels' durations (ms), their count and algorithmic bytes per launch. */
+/* Accumulated time of one class (or of all with QWG_TIME_ALL_GEMV) since qwg_model_set_timing: the
+ * sum of the timed kernels' durations (ms), their count and their summed algorithmic bytes (canonical
+ * weight bytes plus fp32 activations in and out, per launch). */
+int qwg_model_get_timing_class(qwg_model* m, int tensor_id, double* total_ms, int64_t* n_launches,
+                               int64_t* total_bytes);
+/* The same for the class being timed (all classes if timing is off or QWG_TIME_ALL_GEMV), with the
+ * mean algorithmic bytes per launch. */
 int qwg_model_get_timing(qwg_model* m, double* total_ms, int64_t* n_launches, int64_t* bytes_per_launch);
 /* Bytes copied host-to-device for streamed layers in the last step, and the copy-stream time (ms). */
 int qwg_model_stream_stats(qwg_model* m, int64_t* h2d_bytes, double* h2d_ms);

@@ -335,6 +335,19 @@ int orc_threads(void) {
 #endif
 }
 
+// Threads of the row loops from here on (for timing the oracle at 1 thread and at all threads; the
+// results do not depend on it).  Returns the previous count.
+int orc_set_threads(int n) {
+#ifdef _OPENMP
+  const int prev = omp_get_max_threads();
+  if (n > 0) omp_set_num_threads(n);
+  return prev;
+#else
+  (void)n;
+  return 1;
+#endif
+}
+
 int orc_block_weights(int qt) { return block_weights(qt); }
 int orc_block_bytes(int qt) { return block_bytes(qt); }
 double orc_half_value(uint16_t h) { return half_value(h); }

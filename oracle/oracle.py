@@ -93,6 +93,8 @@ def lib():
         L.orc_head.argtypes = [ctypes.POINTER(Model), vp, vp]
         L.orc_threads.argtypes = []
         L.orc_threads.restype = ctypes.c_int
+        L.orc_set_threads.argtypes = [ctypes.c_int]
+        L.orc_set_threads.restype = ctypes.c_int
         L.orc_step.argtypes = [ctypes.POINTER(Model), i32, i64, i32, vp, vp, vp, vp, ctypes.POINTER(i32)]
         _lib = L
     return _lib
@@ -190,6 +192,11 @@ def half_from_double(v: float) -> int:
 def threads() -> int:
     """OpenMP threads the oracle's row loops use."""
     return int(lib().orc_threads())
+
+
+def set_threads(n: int) -> int:
+    """Use n threads in the row loops from now on (results do not depend on it); returns the old count."""
+    return int(lib().orc_set_threads(n))
 
 
 def layer_forward(wl, layer: int, weights: dict, h: np.ndarray, kc: np.ndarray, vc: np.ndarray, pos: int,

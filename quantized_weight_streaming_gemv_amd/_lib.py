@@ -16,6 +16,7 @@ ERRORS = {-1: "QWG_E_INVAL", -2: "QWG_E_SHAPE", -3: "QWG_E_NOMEM", -4: "QWG_E_HI
 Q4_0, Q8_0, Q4_K, Q5_K, Q6_K = 2, 8, 12, 13, 14
 T_EMBED, T_HEAD, T_WQ, T_WK, T_WV, T_WO, T_WGATE, T_WUP, T_WDOWN = 0, 1, 2, 3, 4, 5, 6, 7, 8
 NORM_ATTN, NORM_FFN, NORM_FINAL = 9, 10, 11
+TIME_ALL_GEMV = -2
 
 
 class QwgError(RuntimeError):
@@ -50,6 +51,8 @@ SIGNATURES = {
     "qwg_dequantize": (ctypes.c_int, [ctypes.c_int, vp, i64, i64, vp, vp]),
     "qwg_gemv_work_bytes": (sz, [ctypes.c_int, i64, i64, ctypes.c_int]),
     "qwg_gemv": (ctypes.c_int, [ctypes.c_int, vp, i64, i64, vp, ctypes.c_int, vp, vp, sz, vp]),
+    "qwg_gemv_timed": (ctypes.c_int, [ctypes.c_int, vp, i64, i64, vp, ctypes.c_int, vp, vp, sz,
+                                      ctypes.POINTER(ctypes.c_float), vp]),
     "qwg_set_gemv_geometry": (ctypes.c_int, [ctypes.c_int] * 4),
     "qwg_set_gemv_mfma": (ctypes.c_int, [ctypes.c_int]),
     "qwg_model_spill_layer": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_char_p]),
@@ -86,6 +89,7 @@ SIGNATURES = {
     "qwg_model_get_hidden": (ctypes.c_int, [vp, ctypes.c_int, vp]),
     "qwg_model_set_timing": (ctypes.c_int, [vp, ctypes.c_int]),
     "qwg_model_get_timing": (ctypes.c_int, [vp, P_f64, P_i64, P_i64]),
+    "qwg_model_get_timing_class": (ctypes.c_int, [vp, ctypes.c_int, P_f64, P_i64, P_i64]),
     "qwg_model_stream_stats": (ctypes.c_int, [vp, P_i64, P_f64]),
     "qwg_sync": (ctypes.c_int, [vp]),
     "qwg_read_sink_words": (sz, []),

@@ -105,11 +105,13 @@ struct qwg_model {
   std::vector<uint8_t> skip;
   bool capture_on = false;
   // kernel timing of one weight class
-  int timing_tensor = -1;
+  int timing_tensor = -1;  // one class, QWG_TIME_ALL_GEMV, or -1 (off)
   std::vector<hipEvent_t> tev;
+  std::vector<int> tev_cls;        // class slot of each event pair
+  std::vector<int64_t> tev_bytes;  // algorithmic bytes of each event pair's launch
   int tev_used = 0;
-  double t_ms = 0.0;
-  int64_t t_n = 0, t_bytes = 0;
+  double t_ms[5] = {};             // per class slot (QKV, WO, GATE|UP, DOWN, HEAD)
+  int64_t t_n[5] = {}, t_bytes[5] = {};
   // host-to-device copy timing
   std::vector<hipEvent_t> cev;
   int cev_used = 0;
@@ -305,12 +307,26 @@ static hipEvent_t pool_event(std::vector<hipEvent_t>& pool, int& used, unsigned 
   return pool[used++];
 }
 
+// slot of a timing class (the tensor ids of the five GEMV launches of a step), or -1
+static int timing_slot(int tensor_id) {
+  switch (tensor_id) {
+    case QWG_T_WQ: return 0;
+    case QWG_T_WO: return 1;
+    case QWG_T_WGATE: return 2;
+    case QWG_T_WDOWN: return 3;
+    case QWG_T_HEAD: return 4;
+    default: return -1;
+  }
+}
+
 static int collect_timing(qwg_model* m) {
   for (int i = 0; i + 1 < m->tev_used; i += 2) {
     float ms = 0.f;
     QWG_HIP(hipEventElapsedTime(&ms, m->tev[i], m->tev[i + 1]));
-    m->t_ms += ms;
-    m->t_n += 1;
+    const int c = m->tev_cls[i / 2];
+    m->t_ms[c] += ms;
+    m->t_n[c] += 1;
+    m->t_bytes[c] += m->tev_bytes[i / 2];
   }
   m->tev_used = 0;
   for (int i = 0; i + 1 < m->cev_used; i += 2) {
@@ -381,19 +397,24 @@ static int gemv(qwg_model* m, int tensor_class, int qt, const MatView& w, const 
     e.sq_out = od.sq ? m->f(m->sq) : nullptr;
     e.sq_out_stride = m->sq_col;
   }
-  const bool timed = m->timing_tensor == tensor_class;
+  const bool timed = m->timing_tensor == tensor_class || m->timing_tensor == QWG_TIME_ALL_GEMV;
   hipEvent_t e0 = nullptr, e1 = nullptr;
   if (timed) {
     e0 = pool_event(m->tev, m->tev_used, hipEventDisableSystemFence);
     e1 = pool_event(m->tev, m->tev_used, hipEventDisableSystemFence);
     if (!e0 || !e1) return fail(QWG_E_HIP, "hipEventCreate failed");
+    const size_t pair = (size_t)(m->tev_used / 2 - 1);
+    if (m->tev_cls.size() <= pair) {
+      m->tev_cls.resize(pair + 1);
+      m->tev_bytes.resize(pair + 1);
+    }
+    const int rw = epi == EPI_RESID ? 2 : 1;
+    m->tev_cls[pair] = timing_slot(tensor_class);
+    m->tev_bytes[pair] = gemv_alg_bytes(mp, nc, epi == EPI_SWIGLU ? 0 : rw) +
+                         (epi == EPI_SWIGLU ? (int64_t)nc * mp.L.rows / 2 * 4 : 0);
   }
   QWG_HIP(launch_gemv(qt, w, mp.L.k, m->arena + m->xd[in.buf], m->xd_col, nc, epi, e, m->f(m->part), m->cs, gp, e0,
                       e1));
-  if (timed) {
-    const int rw = epi == EPI_RESID ? 2 : 1;
-    m->t_bytes = gemv_alg_bytes(mp, nc, epi == EPI_SWIGLU ? 0 : rw) + (epi == EPI_SWIGLU ? (int64_t)nc * mp.L.rows / 2 * 4 : 0);
-  }
   if (want && !fused) {
     const int64_t nout = epi == EPI_SWIGLU ? w.rows / 2 : w.rows;
     QWG_HIP(launch_digitize(e.y, e.y_stride, od.gain, nout, nc, od.qt, m->arena + m->xd[od.buf], m->xd_col,
@@ -671,6 +692,48 @@ size_t qwg_gemv_work_bytes(int qtype, int64_t rows, int64_t k, int n_cols) {
   return gemv_work_layout(qtype, rows, k, n_cols, &dig, &total) ? total : 0;
 }
 
+// One GEMV through caller-provided (or static) scratch `work` of `work_bytes`; with events, they are
+// recorded at the start and end of the GEMV kernel(s) (not the digitization before them).
+static int gemv_run(int qtype, const void* d_packed, int64_t rows, int64_t k, const float* d_x, int n_cols,
+                    float* d_y, void* work, size_t work_bytes, hipStream_t stream, hipEvent_t ev0 = nullptr,
+                    hipEvent_t ev1 = nullptr) {
+  size_t dig = 0, need = 0;
+  gemv_work_layout(qtype, rows, k, n_cols, &dig, &need);
+  if (work_bytes < need) return fail(QWG_E_NOMEM, "work buffer smaller than qwg_gemv_work_bytes");
+  const Layout L = make_layout(qtype, rows, k);
+  const GemvPlan p = plan_gemv(qtype, rows, k, n_cols, EPI_STORE);
+  uint8_t* xd = (uint8_t*)work;
+  float* part = p.part_bytes ? (float*)(xd + dig) : nullptr;
+  QWG_HIP(launch_digitize(d_x, k, nullptr, k, n_cols, qtype, xd, digit_bytes(k), nullptr, 0, stream));
+  EpiArgs e{};
+  e.y = d_y;
+  e.y_stride = rows;
+  QWG_HIP(launch_gemv(qtype, make_view(d_packed, L), k, xd, digit_bytes(k), n_cols, EPI_STORE, e, part, stream, p,
+                      ev0, ev1));
+  return QWG_OK;
+}
+
+int qwg_gemv_timed(int qtype, const void* d_packed, int64_t rows, int64_t k, const float* d_x, int n_cols,
+                   float* d_y, void* d_work, size_t work_bytes, float* h_kernel_ms, void* stream) {
+  if (!h_kernel_ms) return fail(QWG_E_INVAL, "NULL pointer");
+  if (int rc = check_matrix(qtype, rows, k)) return rc;
+  if (n_cols < 1 || n_cols > MAX_COLS) return fail(QWG_E_SHAPE, "n_cols must be in 1..8");
+  if (rows == 0) return fail(QWG_E_SHAPE, "rows must be positive to time a GEMV");
+  if (!d_packed || !d_x || !d_y || !d_work) return fail(QWG_E_INVAL, "NULL pointer");
+  if (!aligned16(d_packed) || !aligned16(d_x) || !aligned16(d_work))
+    return fail(QWG_E_INVAL, "d_packed, d_x and d_work must be 16-byte aligned");
+  hipEvent_t e[2] = {nullptr, nullptr};
+  for (auto& x : e) QWG_HIP(hipEventCreateWithFlags(&x, hipEventDisableSystemFence));
+  int rc = gemv_run(qtype, d_packed, rows, k, d_x, n_cols, d_y, d_work, work_bytes, (hipStream_t)stream, e[0], e[1]);
+  hipError_t err = hipSuccess;
+  if (rc == QWG_OK) err = hipEventSynchronize(e[1]);
+  if (rc == QWG_OK && err == hipSuccess) err = hipEventElapsedTime(h_kernel_ms, e[0], e[1]);
+  for (auto x : e) (void)hipEventDestroy(x);
+  if (rc != QWG_OK) return rc;
+  if (err != hipSuccess) return fail(QWG_E_HIP, std::string("timed GEMV: ") + hipGetErrorString(err));
+  return QWG_OK;
+}
+
 int qwg_gemv(int qtype, const void* d_packed, int64_t rows, int64_t k, const float* d_x, int n_cols, float* d_y,
              void* d_work, size_t work_bytes, void* stream) {
   if (int rc = check_matrix(qtype, rows, k)) return rc;
@@ -679,20 +742,7 @@ int qwg_gemv(int qtype, const void* d_packed, int64_t rows, int64_t k, const flo
   if (!d_packed || !d_x || !d_y || !d_work) return fail(QWG_E_INVAL, "NULL pointer");
   if (!aligned16(d_packed) || !aligned16(d_x) || !aligned16(d_work))
     return fail(QWG_E_INVAL, "d_packed, d_x and d_work must be 16-byte aligned");
-  size_t dig = 0, need = 0;
-  gemv_work_layout(qtype, rows, k, n_cols, &dig, &need);
-  if (work_bytes < need) return fail(QWG_E_NOMEM, "work buffer smaller than qwg_gemv_work_bytes");
-  const Layout L = make_layout(qtype, rows, k);
-  const GemvPlan p = plan_gemv(qtype, rows, k, n_cols, EPI_STORE);
-  uint8_t* xd = (uint8_t*)d_work;
-  float* part = p.part_bytes ? (float*)(xd + dig) : nullptr;
-  QWG_HIP(launch_digitize(d_x, k, nullptr, k, n_cols, qtype, xd, digit_bytes(k), nullptr, 0, (hipStream_t)stream));
-  EpiArgs e{};
-  e.y = d_y;
-  e.y_stride = rows;
-  QWG_HIP(launch_gemv(qtype, make_view(d_packed, L), k, xd, digit_bytes(k), n_cols, EPI_STORE, e, part,
-                      (hipStream_t)stream, p));
-  return QWG_OK;
+  return gemv_run(qtype, d_packed, rows, k, d_x, n_cols, d_y, d_work, work_bytes, (hipStream_t)stream);
 }
 
 int qwg_set_gemv_geometry(int waves_per_group, int rows_per_wave, int pipeline_depth, int row_passes) {
@@ -1163,21 +1213,45 @@ int qwg_model_get_hidden(qwg_model* m, int layer, float* h_out) {
 
 int qwg_model_set_timing(qwg_model* m, int tensor_id) {
   if (!m) return fail(QWG_E_INVAL, "NULL model");
-  if (tensor_id != -1 && tensor_id != QWG_T_WQ && tensor_id != QWG_T_WO && tensor_id != QWG_T_WGATE &&
-      tensor_id != QWG_T_WDOWN && tensor_id != QWG_T_HEAD)
-    return fail(QWG_E_INVAL, "timing class must be WQ, WO, WGATE, WDOWN, HEAD or -1");
+  if (tensor_id != -1 && tensor_id != QWG_TIME_ALL_GEMV && timing_slot(tensor_id) < 0)
+    return fail(QWG_E_INVAL, "timing class must be WQ, WO, WGATE, WDOWN, HEAD, QWG_TIME_ALL_GEMV or -1");
   m->timing_tensor = tensor_id;
-  m->t_ms = 0.0;
-  m->t_n = 0;
-  m->t_bytes = 0;
+  for (int c = 0; c < 5; ++c) {
+    m->t_ms[c] = 0.0;
+    m->t_n[c] = 0;
+    m->t_bytes[c] = 0;
+  }
+  return QWG_OK;
+}
+
+int qwg_model_get_timing_class(qwg_model* m, int tensor_id, double* total_ms, int64_t* n_launches,
+                               int64_t* total_bytes) {
+  if (!m) return fail(QWG_E_INVAL, "NULL model");
+  double ms = 0.0;
+  int64_t n = 0, b = 0;
+  for (int c = 0; c < 5; ++c) {
+    static const int ids[5] = {QWG_T_WQ, QWG_T_WO, QWG_T_WGATE, QWG_T_WDOWN, QWG_T_HEAD};
+    if (tensor_id != QWG_TIME_ALL_GEMV && ids[c] != tensor_id) continue;
+    ms += m->t_ms[c];
+    n += m->t_n[c];
+    b += m->t_bytes[c];
+  }
+  if (tensor_id != QWG_TIME_ALL_GEMV && timing_slot(tensor_id) < 0) return fail(QWG_E_INVAL, "bad timing class");
+  if (total_ms) *total_ms = ms;
+  if (n_launches) *n_launches = n;
+  if (total_bytes) *total_bytes = b;
   return QWG_OK;
 }
 
 int qwg_model_get_timing(qwg_model* m, double* total_ms, int64_t* n_launches, int64_t* bytes_per_launch) {
   if (!m) return fail(QWG_E_INVAL, "NULL model");
-  if (total_ms) *total_ms = m->t_ms;
-  if (n_launches) *n_launches = m->t_n;
-  if (bytes_per_launch) *bytes_per_launch = m->t_bytes;
+  const int cls = m->timing_tensor == -1 ? QWG_TIME_ALL_GEMV : m->timing_tensor;
+  double ms = 0.0;
+  int64_t n = 0, b = 0;
+  if (int rc = qwg_model_get_timing_class(m, cls, &ms, &n, &b)) return rc;
+  if (total_ms) *total_ms = ms;
+  if (n_launches) *n_launches = n;
+  if (bytes_per_launch) *bytes_per_launch = n > 0 ? b / n : 0;
   return QWG_OK;
 }
 

@@ -1017,16 +1017,14 @@ GemvPlan plan_gemv(int qt, int64_t rows, int64_t k, int nc, int epi, int mfma) {
   // one column, two rows per wave (measured on the 70B shapes: a four-row kernel needs about 110
   // registers against about 70, and the occupancy two rows leave wins).  The residual epilogue also
   // writes the next GEMV's input digits, which takes whole 32-element chunks of output per
-  // workgroup: 8 waves x two row passes = 32 rows.  SwiGLU runs 4 waves x four passes = 32 rows (16
-  // outputs, so the down GEMV digitizes its fp32 input itself): 64-row workgroups that could write
-  // the digits measured 4 us slower on the 28672 x 2 rows, more than the down prologue costs.
+  // workgroup: 8 waves x two row passes = 32 rows.  SwiGLU runs the same 8 waves x two passes = 32
+  // rows (16 outputs, so the down GEMV digitizes its fp32 input itself).  Every workgroup stages the
+  // whole activation (36 KB at K = 8192), so four fit a CU: measured at the 70B shapes, 8-wave
+  // workgroups beat the 4-wave ones for gate|up (46.3 against 48.8 us) and 10-wave workgroups of 20
+  // rows (two per CU, staging the activation 512 times) beat 8-row ones for QKV (14.0 against 17.7).
   if (p.ncm == 1 && p.ksplit == 1) {
-    if (epi == EPI_RESID) p.passes = 2;
-    if (epi == EPI_SWIGLU) {
-      p.passes = 4;
-      p.waves = 4;
-    }
-    if (epi == EPI_QKV) p.waves = 4;  // 8-row workgroups: 1280 of them balance 10240 rows over 256 CUs
+    if (epi == EPI_RESID || epi == EPI_SWIGLU) p.passes = 2;
+    if (epi == EPI_QKV) p.waves = 10;
   }
   // Very tall one-column GEMVs (the 128256-row head: 8016 blocks of 16 rows) run persistent: a grid
   // of PERSISTENT_WGS1 workgroups strides over the row blocks, so the activation is staged once per

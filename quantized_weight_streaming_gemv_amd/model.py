@@ -167,6 +167,13 @@ class Model:
         call("qwg_model_get_timing", self.handle, ctypes.byref(ms), ctypes.byref(n), ctypes.byref(b))
         return float(ms.value), int(n.value), int(b.value)
 
+    def get_timing_class(self, tensor_id: int):
+        """(total ms, launches, total algorithmic bytes) of one timing class since set_timing."""
+        ms, n, b = ctypes.c_double(0), ctypes.c_int64(0), ctypes.c_int64(0)
+        call("qwg_model_get_timing_class", self.handle, tensor_id, ctypes.byref(ms), ctypes.byref(n),
+             ctypes.byref(b))
+        return float(ms.value), int(n.value), int(b.value)
+
     def spill_layer(self, layer: int, path: str) -> None:
         """Move a streamed layer's image to a file (the file-backed tier); the caller removes the file."""
         call("qwg_model_spill_layer", self.handle, layer, path.encode())

@@ -81,6 +81,15 @@ def gemv(qtype: int, packed, rows: int, k: int, x, out=None, work=None, stream=N
     return out.reshape(rows) if x.dim() == 1 else out
 
 
+def gemv_timed(qtype: int, packed, rows: int, k: int, x, out, work, stream=None) -> float:
+    """qwg_gemv_timed: run the GEMV, wait, and return its kernel time in ms."""
+    x2 = x.reshape(-1, k)
+    ms = ctypes.c_float(0.0)
+    call("qwg_gemv_timed", qtype, _ptr(packed), rows, k, _ptr(x2), x2.shape[0], _ptr(out), _ptr(work),
+         work.numel() * work.element_size(), ctypes.byref(ms), _stream(stream))
+    return float(ms.value)
+
+
 def set_gemv_geometry(waves_per_group: int = 0, rows_per_wave: int = 0, pipeline_depth: int = 0,
                       row_passes: int = 0) -> None:
     call("qwg_set_gemv_geometry", waves_per_group, rows_per_wave, pipeline_depth, row_passes)
