@@ -113,6 +113,20 @@ int qwg_gemv(int qtype, const void* d_packed, int64_t rows, int64_t k, const flo
 int qwg_gemv_timed(int qtype, const void* d_packed, int64_t rows, int64_t k, const float* d_x, int n_cols,
                    float* d_y, void* d_work, size_t work_bytes, float* h_kernel_ms, void* stream);
 
+/* qwg_gemv for callers that cannot allocate device memory (code under stream capture, tight serving
+ * loops, harnesses that forbid allocation): the same kernels and results, with the scratch in a static
+ * device array of the library instead of a work buffer.  Each GPU the library runs on holds its own
+ * QWG_NOALLOC_SCRATCH_BYTES (16 MiB) copy from first use until the process ends; the call allocates
+ * and frees nothing.  A shape whose qwg_gemv_work_bytes exceeds that size is refused with QWG_E_NOMEM
+ * before anything is launched.  Every call on one GPU shares that GPU's array, which keeps the last
+ * call's contents (nothing in it needs to start at zero): calls that overlap on one GPU (several
+ * streams, or several threads) race and may return wrong results; serialize them, or use qwg_gemv
+ * with separate work buffers.  Arguments and errors otherwise as qwg_gemv; asynchronous on `stream`
+ * (the first call on a device also looks up the array's device address, a host-side call). */
+#define QWG_NOALLOC_SCRATCH_BYTES (16u << 20)
+int qwg_gemv_noalloc(int qtype, const void* d_packed, int64_t rows, int64_t k, const float* d_x, int n_cols,
+                     float* d_y, void* stream);
+
 /* Launch geometry of subsequent GEMV launches in this process, for tuning; 0 keeps the default:
  *   waves_per_group  1..8; up to 16 for single-column GEMVs (above 8: 2 rows per wave, depth 1,
  *                    <= 2 passes);

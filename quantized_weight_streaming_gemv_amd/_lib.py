@@ -51,6 +51,7 @@ SIGNATURES = {
     "qwg_dequantize": (ctypes.c_int, [ctypes.c_int, vp, i64, i64, vp, vp]),
     "qwg_gemv_work_bytes": (sz, [ctypes.c_int, i64, i64, ctypes.c_int]),
     "qwg_gemv": (ctypes.c_int, [ctypes.c_int, vp, i64, i64, vp, ctypes.c_int, vp, vp, sz, vp]),
+    "qwg_gemv_noalloc": (ctypes.c_int, [ctypes.c_int, vp, i64, i64, vp, ctypes.c_int, vp, vp]),
     "qwg_gemv_timed": (ctypes.c_int, [ctypes.c_int, vp, i64, i64, vp, ctypes.c_int, vp, vp, sz,
                                       ctypes.POINTER(ctypes.c_float), vp]),
     "qwg_set_gemv_geometry": (ctypes.c_int, [ctypes.c_int] * 4),

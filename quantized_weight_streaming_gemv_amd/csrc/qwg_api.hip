@@ -15,6 +15,7 @@
 #include <chrono>
 #include <cmath>
 #include <cstdio>
+#include <mutex>
 #include <thread>
 #include <cstring>
 #include <new>
@@ -743,6 +744,47 @@ int qwg_gemv(int qtype, const void* d_packed, int64_t rows, int64_t k, const flo
   if (!aligned16(d_packed) || !aligned16(d_x) || !aligned16(d_work))
     return fail(QWG_E_INVAL, "d_packed, d_x and d_work must be 16-byte aligned");
   return gemv_run(qtype, d_packed, rows, k, d_x, n_cols, d_y, d_work, work_bytes, (hipStream_t)stream);
+}
+
+// ---- the allocation-free GEMV: scratch in a static device array, one copy per GPU.  Host code never
+// uses the array's name as an address (on the host it is only a stand-in for the symbol): the device
+// address comes from hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) uint8_t scratch[QWG_NOALLOC_SCRATCH_BYTES];
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[64] = {};
+
+static int scratch_of_current_device(void** out) {
+  int dev = 0;
+  QWG_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64) return fail(QWG_E_HIP, "device index outside 0..63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    QWG_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return fail(QWG_E_HIP, "hipGetSymbolAddress gave a null address for the static scratch");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return QWG_OK;
+}
+
+int qwg_gemv_noalloc(int qtype, const void* d_packed, int64_t rows, int64_t k, const float* d_x, int n_cols,
+                     float* d_y, void* stream) {
+  if (int rc = check_matrix(qtype, rows, k)) return rc;
+  if (n_cols < 1 || n_cols > MAX_COLS) return fail(QWG_E_SHAPE, "n_cols must be in 1..8");
+  if (rows == 0) return QWG_OK;
+  if (!d_packed || !d_x || !d_y) return fail(QWG_E_INVAL, "NULL pointer");
+  if (!aligned16(d_packed) || !aligned16(d_x)) return fail(QWG_E_INVAL, "d_packed and d_x must be 16-byte aligned");
+  size_t dig = 0, need = 0;
+  gemv_work_layout(qtype, rows, k, n_cols, &dig, &need);
+  if (need > (size_t)QWG_NOALLOC_SCRATCH_BYTES)
+    return fail(QWG_E_NOMEM, "this GEMV needs " + std::to_string(need) + " bytes of scratch, more than the " +
+                                 std::to_string((size_t)QWG_NOALLOC_SCRATCH_BYTES) +
+                                 " of the static scratch (use qwg_gemv with a work buffer)");
+  void* work = nullptr;
+  if (int rc = scratch_of_current_device(&work)) return rc;
+  return gemv_run(qtype, d_packed, rows, k, d_x, n_cols, d_y, work, (size_t)QWG_NOALLOC_SCRATCH_BYTES,
+                  (hipStream_t)stream);
 }
 
 int qwg_set_gemv_geometry(int waves_per_group, int rows_per_wave, int pipeline_depth, int row_passes) {

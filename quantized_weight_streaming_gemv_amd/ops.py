@@ -90,6 +90,17 @@ def gemv_timed(qtype: int, packed, rows: int, k: int, x, out, work, stream=None)
     return float(ms.value)
 
 
+NOALLOC_SCRATCH_BYTES = 16 << 20  # QWG_NOALLOC_SCRATCH_BYTES
+
+
+def gemv_noalloc(qtype: int, packed, rows: int, k: int, x, out, stream=None):
+    """qwg_gemv_noalloc: the GEMV with the library's static scratch (no work buffer; `out` must be given,
+    so nothing is allocated here either)."""
+    x2 = x.reshape(-1, k)
+    call("qwg_gemv_noalloc", qtype, _ptr(packed), rows, k, _ptr(x2), x2.shape[0], _ptr(out), _stream(stream))
+    return out
+
+
 def set_gemv_geometry(waves_per_group: int = 0, rows_per_wave: int = 0, pipeline_depth: int = 0,
                       row_passes: int = 0) -> None:
     call("qwg_set_gemv_geometry", waves_per_group, rows_per_wave, pipeline_depth, row_passes)
