@@ -316,6 +316,26 @@ int qwg_model_get_timing(qwg_model* m, double* total_ms, int64_t* n_launches, in
 /* Bytes copied host-to-device for streamed layers in the last step, and the copy-stream time (ms). */
 int qwg_model_stream_stats(qwg_model* m, int64_t* h2d_bytes, double* h2d_ms);
 
+/* Test hooks for failure handling and ordering checks (all off by default):
+ *   QWG_DEBUG_SPIN_US       every streamed layer first waits `value` microseconds (0..100000) on the
+ *                           compute stream (a bounded one-wave wait kernel), so compute lags the
+ *                           copies: a copy that did not wait for "compute on this slot done" would
+ *                           overwrite weights still to be read (the double buffer's write-after-read).
+ *   QWG_DEBUG_FAIL_AT_LAYER a pass that reaches layer `value` (-1 = off) returns QWG_E_STATE there,
+ *                           after the copies of the layers before it and of the next two streamed
+ *                           layers were issued, without waiting for them: the state an error leaves.
+ *                           n_past does not advance; a later call (or qwg_model_destroy, which
+ *                           synchronizes first) is safe. */
+#define QWG_DEBUG_SPIN_US 1
+#define QWG_DEBUG_FAIL_AT_LAYER 2
+int qwg_model_set_debug(qwg_model* m, int knob, int64_t value);
+/* The failure check of the captured residual streams (qwg_model_set_capture on, after a step): *layer
+ * = the first l in -1 (after the embedding) .. n_layers-1 whose hidden state holds a NaN or an
+ * infinity, n_layers if only the logits do, -2 if everything is finite ([NT] "Key features": a
+ * non-finite fp16 scale or overflowed cache entry surfaces here with the layer that produced it).
+ * Synchronizes. */
+int qwg_model_first_nonfinite(qwg_model* m, int* layer);
+
 /* File-backed third tier ([NT] "3-tier adaptive cache": tier C, storage / mmap, used only when the
  * other tiers are full; [HN] 3-tier detail; data path storage -> pinned staging -> H2D -> GPU): move a
  * streamed layer's packed image from its pinned host image to the file `path` (created or

@@ -17,6 +17,7 @@ Q4_0, Q8_0, Q4_K, Q5_K, Q6_K = 2, 8, 12, 13, 14
 T_EMBED, T_HEAD, T_WQ, T_WK, T_WV, T_WO, T_WGATE, T_WUP, T_WDOWN = 0, 1, 2, 3, 4, 5, 6, 7, 8
 NORM_ATTN, NORM_FFN, NORM_FINAL = 9, 10, 11
 TIME_ALL_GEMV = -2
+DEBUG_SPIN_US, DEBUG_FAIL_AT_LAYER = 1, 2
 
 
 class QwgError(RuntimeError):
@@ -91,6 +92,8 @@ SIGNATURES = {
     "qwg_model_set_timing": (ctypes.c_int, [vp, ctypes.c_int]),
     "qwg_model_get_timing": (ctypes.c_int, [vp, P_f64, P_i64, P_i64]),
     "qwg_model_get_timing_class": (ctypes.c_int, [vp, ctypes.c_int, P_f64, P_i64, P_i64]),
+    "qwg_model_set_debug": (ctypes.c_int, [vp, ctypes.c_int, i64]),
+    "qwg_model_first_nonfinite": (ctypes.c_int, [vp, P_i32]),
     "qwg_model_stream_stats": (ctypes.c_int, [vp, P_i64, P_f64]),
     "qwg_sync": (ctypes.c_int, [vp]),
     "qwg_read_sink_words": (sz, []),

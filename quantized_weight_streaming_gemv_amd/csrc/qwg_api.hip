@@ -123,6 +123,9 @@ struct qwg_model {
   hipEvent_t ev_staged[2] = {};  // the H2D copy out of stage[i] is done
   int64_t file_bytes = 0;
   double file_ms = 0.0;
+  // test hooks (qwg_model_set_debug)
+  uint64_t spin_ticks = 0;  // wall-clock ticks each streamed layer waits before its kernels
+  int fail_layer = -1;      // a pass reaching this layer fails (after its copies were issued)
 
   int H() const { return d.hidden; }
   int QR() const { return d.n_q * d.head_dim; }
@@ -588,6 +591,8 @@ static int run_pass(qwg_model* m, const int32_t* toks, int nc, int pos, int n_ru
         QWG_HIP(hipStreamWaitEvent(m->cs, m->ev_full[slot], 0));
         base = m->arena + m->slot[slot];
       }
+      if (l == m->fail_layer) return fail(QWG_E_STATE, "forced failure at layer " + std::to_string(l));
+      if (!P.resident && m->spin_ticks) QWG_HIP(launch_spin(m->spin_ticks, m->cs));
       if (calib) QWG_HIP(hipMemcpyAsync(m->f(m->hin), m->f(m->h), (size_t)H * 4, hipMemcpyDeviceToDevice, m->cs));
       if (int rc = layer_kernels(m, l, base, nc, pos, digits_for(++ri))) return rc;
       if (!P.resident) {
@@ -1295,6 +1300,52 @@ int qwg_model_get_timing(qwg_model* m, double* total_ms, int64_t* n_launches, in
   if (n_launches) *n_launches = n;
   if (bytes_per_launch) *bytes_per_launch = n > 0 ? b / n : 0;
   return QWG_OK;
+}
+
+int qwg_model_set_debug(qwg_model* m, int knob, int64_t value) {
+  if (!m) return fail(QWG_E_INVAL, "NULL model");
+  switch (knob) {
+    case QWG_DEBUG_SPIN_US: {
+      if (value < 0 || value > 100000) return fail(QWG_E_INVAL, "spin must be 0..100000 us");
+      int khz = 0, dev = 0;
+      QWG_HIP(hipGetDevice(&dev));
+      QWG_HIP(hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev));
+      m->spin_ticks = (uint64_t)value * (uint64_t)khz / 1000u;
+      return QWG_OK;
+    }
+    case QWG_DEBUG_FAIL_AT_LAYER:
+      if (value < -1 || value >= m->d.n_layers) return fail(QWG_E_INVAL, "layer must be -1..n_layers-1");
+      m->fail_layer = (int)value;
+      return QWG_OK;
+    default:
+      return fail(QWG_E_INVAL, "unknown debug knob");
+  }
+}
+
+int qwg_model_first_nonfinite(qwg_model* m, int* layer) {
+  if (!m || !layer) return fail(QWG_E_INVAL, "NULL pointer");
+  if (!m->bound) return fail(QWG_E_STATE, "model is not bound");
+  return guarded([&]() -> int {
+    const int H = m->d.hidden, L = m->d.n_layers;
+    std::vector<float> cap((size_t)(L + 1) * H), lg((size_t)m->d.vocab);
+    QWG_HIP(hipStreamSynchronize(m->cs));
+    QWG_HIP(hipMemcpy(cap.data(), m->f(m->capture), cap.size() * 4, hipMemcpyDeviceToHost));
+    QWG_HIP(hipMemcpy(lg.data(), m->f(m->logits), lg.size() * 4, hipMemcpyDeviceToHost));
+    *layer = -2;
+    for (int l = -1; l < L && *layer == -2; ++l)
+      for (int i = 0; i < H; ++i)
+        if (!std::isfinite(cap[(size_t)(l + 1) * H + i])) {
+          *layer = l;
+          break;
+        }
+    if (*layer == -2)
+      for (float v : lg)
+        if (!std::isfinite(v)) {
+          *layer = L;
+          break;
+        }
+    return QWG_OK;
+  });
 }
 
 int qwg_model_spill_layer(qwg_model* m, int layer, const char* path) {

@@ -130,6 +130,9 @@ constexpr int READ_GRID_MAX = 8192;
 hipError_t launch_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t st, int grid = 0, int unroll = 0,
                        hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
+// a one-wave kernel that waits `ticks` of the wall clock (wall_clock64) and exits
+hipError_t launch_spin(uint64_t ticks, hipStream_t st);
+
 // Output values that the fused digitization of a GEMV covers per workgroup must be whole
 // 32-element chunks: true if every workgroup of the plan writes whole chunks of the output.
 bool gemv_can_digitize_output(const GemvPlan& p, int epi, int64_t rows);

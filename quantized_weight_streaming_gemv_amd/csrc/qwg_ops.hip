@@ -514,6 +514,17 @@ hipError_t launch_attn(const float* q, int64_t q_stride, const uint16_t* kc, con
 // Streaming read of n16 16-byte words: wave w of the grid reads one contiguous segment, lane l the
 // words l, l+64, ... of it, four 16-B non-temporal loads in flight per lane (the GEMV's own load
 // pattern without its arithmetic).  One XOR checksum per wave keeps the loads alive.
+// Waits `ticks` of the constant-rate wall clock, then exits (a bounded delay for ordering tests).
+__global__ void k_spin(uint64_t ticks) {
+  const uint64_t t0 = wall_clock64();
+  while (wall_clock64() - t0 < ticks) __builtin_amdgcn_s_sleep(8);
+}
+
+hipError_t launch_spin(uint64_t ticks, hipStream_t st) {
+  hipLaunchKernelGGL(k_spin, dim3(1), dim3(64), 0, st, ticks);
+  return hipGetLastError();
+}
+
 template <int U>
 __global__ __launch_bounds__(512) void k_read(const uint4* __restrict__ p, int64_t n16, int64_t per_wave,
                                               uint32_t* sink) {

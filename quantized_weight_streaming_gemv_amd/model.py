@@ -167,6 +167,17 @@ class Model:
         call("qwg_model_get_timing", self.handle, ctypes.byref(ms), ctypes.byref(n), ctypes.byref(b))
         return float(ms.value), int(n.value), int(b.value)
 
+    def set_debug(self, knob: int, value: int) -> None:
+        """Test hooks: _lib.DEBUG_SPIN_US (delay each streamed layer's compute), _lib.DEBUG_FAIL_AT_LAYER."""
+        call("qwg_model_set_debug", self.handle, knob, value)
+
+    def first_nonfinite(self) -> int:
+        """First layer (-1 = embedding) whose captured hidden state is non-finite; n_layers: only the logits;
+        -2: none."""
+        out = ctypes.c_int32(0)
+        call("qwg_model_first_nonfinite", self.handle, ctypes.byref(out))
+        return int(out.value)
+
     def get_timing_class(self, tensor_id: int):
         """(total ms, launches, total algorithmic bytes) of one timing class since set_timing."""
         ms, n, b = ctypes.c_double(0), ctypes.c_int64(0), ctypes.c_int64(0)
