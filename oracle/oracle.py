@@ -314,24 +314,32 @@ class OracleModel:
         r["mask"] = self.skip.copy()
         return r
 
-    def spec_round(self, token: int, draft_layers: int, k: int):
+    def spec_round(self, token: int, draft_layers: int, k: int, log=None):
         """Self-speculative round: draft k tokens with the first draft_layers layers, verify with k+1
-        sequential full steps, accept the longest agreeing prefix, emit accepted drafts + one more."""
+        sequential full steps, accept the longest agreeing prefix, emit accepted drafts + one more.
+        log (optional) is called with a short message after every step."""
         p = self.n_past
-        drafts = []
+        drafts, draft_logits = [], []
         t = token
         for j in range(k):
-            t = self.step(t, n_run=draft_layers, pos=p + j)["next"]
+            r = self.step(t, n_run=draft_layers, pos=p + j)
+            t = r["next"]
             drafts.append(t)
+            draft_logits.append(r["logits"])
+            if log:
+                log("oracle draft %d: %d" % (j, t))
         cols = [token] + drafts
         verdict, logits = [], []
         for j in range(k + 1):
             r = self.step(cols[j], pos=p + j)
             verdict.append(r["next"])
             logits.append(r["logits"])
+            if log:
+                log("oracle verify column %d: %d" % (j, r["next"]))
         a = 0
         while a < k and verdict[a] == drafts[a]:
             a += 1
         out = drafts[:a] + [verdict[a]]
         self.n_past = p + a + 1
-        return dict(tokens=out, n_accepted=a, drafts=drafts, verdict=verdict, logits=np.stack(logits))
+        return dict(tokens=out, n_accepted=a, drafts=drafts, verdict=verdict, logits=np.stack(logits),
+                    draft_logits=np.stack(draft_logits))

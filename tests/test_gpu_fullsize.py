@@ -3,8 +3,8 @@ configuration bench.py times (default geometry), on outputs the CPU oracle can c
 
   * 8B Q8_0: two whole decode steps against the oracle's whole steps (every layer's hidden
     state, logits, greedy token, the K/V rows written).
-  * 70B Q4_K: one decode step; sampled layers recomputed by the oracle from the GPU's own input
-    to that layer (teacher-forced), the written K/V rows, and the head on the GPU's final state.
+  * 70B Q4_K: one decode step; all 80 layers recomputed by the oracle from the GPU's own input to
+    each layer (teacher-forced), the written K/V rows, and the head on the GPU's final state.
   * 70B Q6_K, 20 layers resident + 60 streamed, cosine skip at 0.98: the calibration step's
     per-layer cosines and skip decisions on sampled layers (streamed and resident, near-identity
     and random), skipped layers passing h through unchanged in the next step, and streaming
@@ -16,8 +16,15 @@ configuration bench.py times (default geometry), on outputs the CPU oracle can c
 
 Tolerances are the ones of the model-level tests: hidden states and logits within relative L2
 2e-3; cosines within 1e-5; greedy decisions equal except at near-ties (gap below 1e-4 max|logits|
-for argmax, within 1e-4 of tau for the skip test)."""
+for argmax, within 1e-4 of tau for the skip test).
+
+  * 8B Q8_0: the workload's whole 32-token greedy decode against the oracle's, teacher-forced on
+    near-ties (about 90 s, most of it the oracle's).
+
+Opt-in with QWG_FULL_LENGTH=1, because the oracle needs about ten minutes of host time for it: two
+self-speculative rounds of the 70B Q6_K / Q5_K workload against the oracle's rounds."""
 import gc
+import os
 
 import numpy as np
 import pytest
@@ -113,8 +120,8 @@ def test_llama8b_q8_0_two_steps(qwg):
     gc.collect()
 
 
-@pytest.mark.timeout(600)
-def test_llama70b_q4_k_step_sampled_layers(qwg):
+@pytest.mark.timeout(900)
+def test_llama70b_q4_k_step_all_layers(qwg):
     wl = synth.LLAMA70B_Q4_K
     ctx = wl.n_prior + 4
     m = qwg.make_model(wl, max_ctx=ctx)
@@ -122,12 +129,14 @@ def test_llama70b_q4_k_step_sampled_layers(qwg):
     m.set_capture(True)
     t = wl.first_token()
     g_next, g_logits = m.decode_step(t, want_logits=True)
-    hid = {l: m.get_hidden(l) for l in (-1, 0, 1, 38, 39, 78, 79)}
+    hid = {l: m.get_hidden(l) for l in range(-1, wl.n_layers)}
     # the embedding row is the exact dequantized row
     emb = oracle.dequant(wl.qtype_embed, wl.weight(-1, synth.EMBED, t, 1), 1, wl.hidden)[0]
     assert np.array_equal(hid[-1], emb)
-    for l in (0, 39, 79):
+    for l in range(wl.n_layers):  # every layer, from the GPU's own input to it
         check_layer(wl, m, l, hid[l - 1], hid[l], wl.n_prior, ctx)
+        if l % 10 == 9:
+            print("70B Q4_K: layers 0..%d match the oracle" % l, flush=True)
     ref = oracle.head_logits(wl, wl.weight(-1, synth.HEAD), hid[79])
     assert rel_l2(g_logits, ref) < 2e-3
     r_next = oracle.argmax_f32(ref.astype(np.float32))
@@ -243,3 +252,82 @@ def test_llama70b_q6k_q5k_spec_round(qwg):
     ref = oracle.head_logits(wl, wl.weight(-1, synth.HEAD), hid[79])
     assert rel_l2(v_logits[0], ref) < 2e-3
     free(m)
+
+
+FULL = pytest.mark.skipif(not os.environ.get("QWG_FULL_LENGTH"),
+                          reason="needs minutes of oracle time on the host; set QWG_FULL_LENGTH=1")
+
+
+@pytest.mark.timeout(1200)
+def test_llama8b_q8_0_32_tokens_teacher_forced(qwg):
+    """The 8B Q8_0 workload's 32-token greedy decode: every step's per-layer hidden states and logits
+    against the oracle's; where the greedy tokens differ the logits must be a near-tie, and both sides
+    continue with the oracle's token."""
+    wl = synth.LLAMA8B_Q8_0
+    ctx = wl.n_prior + 40
+    m = qwg.make_model(wl, max_ctx=ctx)
+    qwg.load(m, wl)
+    m.set_capture(True)
+    om = oracle.OracleModel(wl, max_ctx=ctx)
+    t, ties, toks = wl.first_token(), 0, []
+    for step in range(32):
+        g_next, g_logits = m.decode_step(t, want_logits=True)
+        r = om.decode(t, want_hidden=True)
+        for l in range(wl.n_layers + 1):
+            assert rel_l2(m.get_hidden(l - 1), r["hidden"][l]) < 2e-3, (step, l)
+        assert rel_l2(g_logits, r["logits"]) < 2e-3, step
+        if g_next != r["next"]:
+            assert is_tie(r["logits"], g_next, r["next"]), (step, g_next, r["next"])
+            ties += 1
+        t = r["next"]
+        toks.append(t)
+        print("8B Q8_0 step %d: token %d" % (step, t), flush=True)
+    print("8B Q8_0 32 tokens: %d distinct, %d near-ties forced" % (len(set(toks)), ties), flush=True)
+    free(m)
+    del om
+    gc.collect()
+
+
+@FULL
+@pytest.mark.timeout(2400)
+def test_llama70b_q6k_q5k_two_spec_rounds_against_oracle(qwg):
+    """Two self-speculative rounds (k = 3 drafts from layers 0..19, one 4-column verify over 80 layers)
+    against the oracle's rounds (drafts from its 20-layer model, verify as four sequential full steps):
+    the same drafts, acceptance and emitted tokens (up to near-ties), and each verify column's logits
+    within relative L2 2e-3."""
+    wl = synth.LLAMA70B_Q6_K_Q5_K_SPEC
+    k = wl.draft_k
+    ctx = wl.n_prior + 4 * (k + 1)
+    m = qwg.make_model(wl, max_ctx=ctx)
+    qwg.load(m, wl)
+    om = oracle.OracleModel(wl, max_ctx=ctx)
+    t = wl.first_token()
+    for rnd in range(2):
+        p = m.n_past
+        assert p == om.n_past
+        r = om.spec_round(t, wl.draft_layers, k, log=lambda msg: print("round %d %s" % (rnd, msg), flush=True))
+        # the GPU's verify of the oracle's columns, then its own round from the same state
+        v_logits, v_am = m.verify([t] + r["drafts"])
+        for j in range(k + 1):
+            assert rel_l2(v_logits[j], r["logits"][j]) < 2e-3, (rnd, j)
+            if v_am[j] != r["verdict"][j]:
+                assert is_tie(r["logits"][j], v_am[j], r["verdict"][j]), (rnd, j)
+        out, acc = m.spec_step(t, wl.draft_layers, k)
+        if out != r["tokens"]:
+            # only a near-tie in one of the round's greedy decisions (a draft or a verify column) may
+            # change the round; then both continue from the oracle's round
+            def top2(L):
+                i = np.argsort(L)[-2:]
+                return int(i[1]), int(i[0])
+            assert any(is_tie(L, *top2(L)) for L in list(r["draft_logits"]) + list(r["logits"])), \
+                (rnd, out, r["tokens"])
+            m.truncate(p)
+            for c in [t] + r["tokens"][:-1]:  # the oracle's columns p .. p + a into the GPU's cache
+                m.decode_step(c)
+        assert m.n_past == om.n_past
+        print("round %d: drafts %s, accepted %d, emitted %s" % (rnd, r["drafts"], r["n_accepted"], r["tokens"]),
+              flush=True)
+        t = r["tokens"][-1]
+    free(m)
+    del om
+    gc.collect()
