@@ -303,7 +303,7 @@ def main() -> int:
     wl = workloads()[args.workload]
     spec = wl.draft_layers > 0
     total_steps = args.warmup + args.steps * 2 + args.class_steps * 5 + 1
-    max_ctx = wl.n_prior + total_steps * (wl.draft_k + 1 if spec else 1) + 8 + max(0, args.prefill)
+    max_ctx = wl.n_prior + total_steps * (wl.draft_k + 1 if spec else 1) + 8 + 2 * max(0, args.prefill)
     max_cols = max(wl.draft_k + 1 if spec else 1, args.prefill_cols if args.prefill > 0 else 1)
     if args.copy_probe_mib > 0:
         src = torch.ones(args.copy_probe_mib << 18, dtype=torch.float32, device="cuda")

@@ -95,8 +95,11 @@ int qwg_dequantize(int qtype, const void* d_packed, int64_t rows, int64_t k, flo
 /* Fused dequantize-and-GEMV, the engine's hand-written GEMV kernels ([NT] "Architecture overview",
  * cuda/: GEMV; [NT] "Key features": no cuBLAS): d_y[j][r] = sum_c W[r][c] d_x[j][c] for
  * j < n_cols, with W decoded from the packed blocks in registers and never written out.
- * d_x is fp32 [n_cols][k], d_y fp32 [n_cols][rows]; 1 <= n_cols <= 8; k <= 65536.
- * n_cols > 1 is the multi-column form used to verify self-speculative drafts ([NT] "Key features").
+ * d_x is fp32 [n_cols][k], d_y fp32 [n_cols][rows]; 1 <= n_cols <= 8, or up to 64 for Q4_K, Q5_K
+ * and Q6_K with k a multiple of 512; k <= 65536.
+ * n_cols > 1 is the multi-column form used to verify self-speculative drafts ([NT] "Key features");
+ * 9..64 columns run the prompt-prefill GEMM ([NT] "Quick start": -p), which reads each weight once
+ * per call on the matrix cores.
  * d_work: caller-owned device scratch of at least qwg_gemv_work_bytes(qtype, rows, k, n_cols) bytes
  * (16-byte aligned), which the call overwrites with the activation's fixed-point digits and, for
  * shapes whose activation does not fit on chip at once, the K-split partial sums.  Calls in flight
@@ -210,7 +213,9 @@ typedef struct {
   int32_t qtype_ffn;  /* WGATE, WUP, WDOWN */
   int32_t qtype_embed;
   int32_t qtype_head;
-  int32_t max_cols;   /* widest multi-column pass (1 + draft k), 1..8 */
+  int32_t max_cols;   /* widest multi-column pass, 1..64: self-speculative verify (1 + draft k) takes
+                         up to 8; qwg_prefill passes of up to 64 prompt tokens when every layer matrix
+                         is Q4_K, Q5_K or Q6_K with K a multiple of 512, else of up to 8 */
   const int32_t* layer_qtypes; /* NULL, or a host array [n_layers][4] of per-layer types of (QKV, WO,
                          GATE|UP, DOWN) overriding qtype_attn / qtype_ffn: mixed-type files such as
                          Q4_K_M ([HN] quantization-format table: a mixed 256-weight type).  Read by
@@ -265,9 +270,11 @@ int qwg_decode_step(qwg_model* m, int32_t token, int32_t* next_token, float* h_l
 
 /* Prompt prefill ([NT] "Quick start": the -p prompt): tokens[0..n-1] go at positions n_past ..
  * n_past+n-1, each attending causally to the positions before it, as n decode steps would, in passes
- * of up to max_cols columns (the multi-column GEMVs read each weight once per pass); only the last
- * pass runs the final norm, head and argmax.  *next_token (optional) is the greedy token after the
- * prompt, h_logits (optional) its fp32 logits [vocab].  n_past advances by n.  Synchronizes. */
+ * of up to max_cols columns that read each weight once per pass: passes of 9..64 columns run the
+ * prompt-prefill GEMM on the matrix cores (every layer matrix Q4_K, Q5_K or Q6_K with K a multiple of
+ * 512; otherwise passes are of at most 8 columns).  Only the last pass runs the final norm, head and
+ * argmax, for its last column.  *next_token (optional) is the greedy token after the prompt, h_logits
+ * (optional) its fp32 logits [vocab].  n_past advances by n.  Synchronizes. */
 int qwg_prefill(qwg_model* m, const int32_t* tokens, int n, int32_t* next_token, float* h_logits);
 
 /* Layer-skip calibration ([NT] "Key results"/"Key features"; [UR] layer-skip mechanism): one decode
@@ -283,10 +290,11 @@ int qwg_get_layer_skip(qwg_model* m, uint8_t* h_mask);
  * verify the k+1 tokens [token, d1..dk] in one k+1-column pass through all layers, accept the longest
  * prefix of drafts that matches the verifier's argmax, emit accepted drafts plus one verifier token
  * (out_tokens[0 .. *n_out-1], *n_out = *n_accepted + 1) and roll the KV length back to
- * n_past + *n_out.  1 <= k, k + 1 <= max_cols. */
+ * n_past + *n_out.  1 <= k, k + 1 <= min(max_cols, 8). */
 int qwg_spec_step(qwg_model* m, int32_t token, int draft_layers, int k, int32_t* out_tokens, int* n_out,
                   int* n_accepted);
-/* The verify pass alone: tokens[0..n-1] at positions n_past .. n_past+n-1 through all layers;
+/* The verify pass alone (1 <= n <= min(max_cols, 8)): tokens[0..n-1] at positions n_past ..
+ * n_past+n-1 through all layers;
  * h_logits fp32 [n][vocab] (optional), h_argmax [n] (optional).  n_past is left unchanged (the
  * KV rows written stay beyond it). */
 int qwg_verify(qwg_model* m, const int32_t* tokens, int n, float* h_logits, int32_t* h_argmax);

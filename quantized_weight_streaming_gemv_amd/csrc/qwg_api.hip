@@ -257,8 +257,9 @@ static int check_desc(const qwg_model_desc* d) {
     return fail(QWG_E_SHAPE, "model dimensions must be positive");
   if (d->head_dim != HEAD_DIM) return fail(QWG_E_SHAPE, "head_dim must be 128");
   if (d->n_q % d->n_kv) return fail(QWG_E_SHAPE, "n_q must be a multiple of n_kv");
-  if (d->max_cols < 1 || d->max_cols > MAX_COLS) return fail(QWG_E_SHAPE, "max_cols must be in 1..8");
-  if (d->n_q / d->n_kv * d->max_cols > 64) return fail(QWG_E_SHAPE, "(n_q / n_kv) * max_cols must be <= 64");
+  if (d->max_cols < 1 || d->max_cols > MAX_PREFILL_COLS) return fail(QWG_E_SHAPE, "max_cols must be in 1..64");
+  if (d->n_q / d->n_kv * std::min(d->max_cols, MAX_COLS) > 64)
+    return fail(QWG_E_SHAPE, "(n_q / n_kv) * min(max_cols, 8) must be <= 64");
   const int qts[4] = {d->qtype_attn, d->qtype_ffn, d->qtype_embed, d->qtype_head};
   for (int q : qts)
     if (!qtype_known(q)) return fail(QWG_E_UNSUPPORTED, "unknown qtype " + std::to_string(q));
@@ -611,18 +612,39 @@ static int run_pass(qwg_model* m, const int32_t* toks, int nc, int pos, int n_ru
     QWG_HIP(hipMemcpyAsync(m->f(m->capture) + (size_t)(l + 1) * H, m->f(m->h), (size_t)H * 4,
                            hipMemcpyDeviceToDevice, m->cs));
   if (!head) return QWG_OK;
+  // a wide prefill pass needs only its last column's logits: that column is digitized again for the
+  // one-column head GEMV (whose digit kind may differ from the wide GEMMs' byte digits)
+  int hc = nc;
+  if (nc > MAX_COLS) {
+    hc = 1;
+    QWG_HIP(launch_digitize(m->f(m->h) + (size_t)(nc - 1) * H, H, m->f(m->g_final), H, 1, d.qtype_head,
+                            m->arena + m->xd[0], m->xd_col, m->f(m->sq), m->sq_col, m->cs));
+  }
   EpiArgs e{};
   e.y = m->f(m->logits);
   e.y_stride = d.vocab;
   InDigits in_head;
   in_head.buf = 0;
   in_head.rms = true;
-  if (int rc = gemv(m, QWG_T_HEAD, d.qtype_head, view_at(m->arena, m->head), m->head, in_head, nc, EPI_STORE, e,
+  if (int rc = gemv(m, QWG_T_HEAD, d.qtype_head, view_at(m->arena, m->head), m->head, in_head, hc, EPI_STORE, e,
                     OutDigits{}))
     return rc;
-  QWG_HIP(launch_argmax(m->f(m->logits), d.vocab, nc, d.vocab, (int32_t*)(m->arena + m->amax), m->cs,
+  QWG_HIP(launch_argmax(m->f(m->logits), d.vocab, hc, d.vocab, (int32_t*)(m->arena + m->amax), m->cs,
                         (unsigned long long*)(m->arena + m->keys)));
   return QWG_OK;
+}
+
+// Widest pass the 64-column GEMM can take for this model: every layer matrix a K-quant with K a
+// multiple of 512 (else the multi-column kernels, up to MAX_COLS).
+static int prefill_width(const qwg_model* m) {
+  const int C = m->d.max_cols;
+  if (C <= MAX_COLS) return C;
+  for (const LayerPlan& P : m->L)
+    for (const MatPlan* mp : {&P.qkv, &P.o, &P.gu, &P.down}) {
+      const int qt = mp->L.qtype;
+      if (!(qt == Q4_K || qt == Q5_K || qt == Q6_K) || mp->L.k % 512) return MAX_COLS;
+    }
+  return C;
 }
 
 static int finish_pass(qwg_model* m, int nc, int32_t* h_amax, float* h_logits) {
@@ -681,9 +703,15 @@ int qwg_dequantize(int qtype, const void* d_packed, int64_t rows, int64_t k, flo
 
 // Scratch of one qwg_gemv call: the activation digits of every column, then (256-B aligned) the
 // K-split partial sums of whichever form a several-column GEMV may take.
+// Widest column count qwg_gemv takes: 64 for K-quants with K a multiple of 512 (the prefill GEMM),
+// else 8.
+static int gemv_max_cols(int qtype, int64_t k) {
+  return ((qtype == Q4_K || qtype == Q5_K || qtype == Q6_K) && k % 512 == 0) ? MAX_PREFILL_COLS : MAX_COLS;
+}
+
 static bool gemv_work_layout(int qtype, int64_t rows, int64_t k, int n_cols, size_t* dig_bytes, size_t* total) {
   if (!qtype_known(qtype) || rows < 0 || rows > (int64_t)1 << 30 || canon_row_bytes(qtype, k) == 0 || k > 65536 ||
-      n_cols < 1 || n_cols > MAX_COLS)
+      n_cols < 1 || n_cols > gemv_max_cols(qtype, k))
     return false;
   const size_t dig = align_up((size_t)n_cols * (size_t)digit_bytes(k));
   size_t part = 0;
@@ -723,7 +751,8 @@ int qwg_gemv_timed(int qtype, const void* d_packed, int64_t rows, int64_t k, con
                    float* d_y, void* d_work, size_t work_bytes, float* h_kernel_ms, void* stream) {
   if (!h_kernel_ms) return fail(QWG_E_INVAL, "NULL pointer");
   if (int rc = check_matrix(qtype, rows, k)) return rc;
-  if (n_cols < 1 || n_cols > MAX_COLS) return fail(QWG_E_SHAPE, "n_cols must be in 1..8");
+  if (n_cols < 1 || n_cols > gemv_max_cols(qtype, k))
+    return fail(QWG_E_SHAPE, "n_cols must be in 1..8 (1..64 for Q4_K, Q5_K, Q6_K with k a multiple of 512)");
   if (rows == 0) return fail(QWG_E_SHAPE, "rows must be positive to time a GEMV");
   if (!d_packed || !d_x || !d_y || !d_work) return fail(QWG_E_INVAL, "NULL pointer");
   if (!aligned16(d_packed) || !aligned16(d_x) || !aligned16(d_work))
@@ -743,7 +772,8 @@ int qwg_gemv_timed(int qtype, const void* d_packed, int64_t rows, int64_t k, con
 int qwg_gemv(int qtype, const void* d_packed, int64_t rows, int64_t k, const float* d_x, int n_cols, float* d_y,
              void* d_work, size_t work_bytes, void* stream) {
   if (int rc = check_matrix(qtype, rows, k)) return rc;
-  if (n_cols < 1 || n_cols > MAX_COLS) return fail(QWG_E_SHAPE, "n_cols must be in 1..8");
+  if (n_cols < 1 || n_cols > gemv_max_cols(qtype, k))
+    return fail(QWG_E_SHAPE, "n_cols must be in 1..8 (1..64 for Q4_K, Q5_K, Q6_K with k a multiple of 512)");
   if (rows == 0) return QWG_OK;
   if (!d_packed || !d_x || !d_y || !d_work) return fail(QWG_E_INVAL, "NULL pointer");
   if (!aligned16(d_packed) || !aligned16(d_x) || !aligned16(d_work))
@@ -776,7 +806,8 @@ static int scratch_of_current_device(void** out) {
 int qwg_gemv_noalloc(int qtype, const void* d_packed, int64_t rows, int64_t k, const float* d_x, int n_cols,
                      float* d_y, void* stream) {
   if (int rc = check_matrix(qtype, rows, k)) return rc;
-  if (n_cols < 1 || n_cols > MAX_COLS) return fail(QWG_E_SHAPE, "n_cols must be in 1..8");
+  if (n_cols < 1 || n_cols > gemv_max_cols(qtype, k))
+    return fail(QWG_E_SHAPE, "n_cols must be in 1..8 (1..64 for Q4_K, Q5_K, Q6_K with k a multiple of 512)");
   if (rows == 0) return QWG_OK;
   if (!d_packed || !d_x || !d_y) return fail(QWG_E_INVAL, "NULL pointer");
   if (!aligned16(d_packed) || !aligned16(d_x)) return fail(QWG_E_INVAL, "d_packed and d_x must be 16-byte aligned");
@@ -1144,17 +1175,19 @@ int qwg_prefill(qwg_model* m, const int32_t* tokens, int n, int32_t* next_token,
   if (n < 1) return fail(QWG_E_SHAPE, "n must be >= 1");
   return guarded([&]() -> int {
     if (m->n_past + n > m->d.max_ctx) return fail(QWG_E_STATE, "context full (n_past + n > max_ctx)");
-    const int C = m->d.max_cols;
+    const int C = prefill_width(m);
     for (int i = 0; i < n; i += C) {
       const int c = std::min(C, n - i);
       const bool last = i + c == n;
       if (int rc = run_pass(m, tokens + i, c, m->n_past, m->d.n_layers, false, last)) return rc;
       if (last) {
-        std::vector<int32_t> am(c);
-        if (int rc = finish_pass(m, c, am.data(), nullptr)) return rc;
-        if (next_token) *next_token = am[c - 1];
+        // a wide pass computes the head for its last column only (column 0 of the logits)
+        const int hc = c > MAX_COLS ? 1 : c;
+        std::vector<int32_t> am(hc);
+        if (int rc = finish_pass(m, hc, am.data(), nullptr)) return rc;
+        if (next_token) *next_token = am[hc - 1];
         if (h_logits)
-          QWG_HIP(hipMemcpy(h_logits, m->f(m->logits) + (size_t)(c - 1) * m->d.vocab, (size_t)m->d.vocab * 4,
+          QWG_HIP(hipMemcpy(h_logits, m->f(m->logits) + (size_t)(hc - 1) * m->d.vocab, (size_t)m->d.vocab * 4,
                             hipMemcpyDeviceToHost));
       }
       m->n_past += c;
@@ -1196,7 +1229,7 @@ int qwg_get_layer_skip(qwg_model* m, uint8_t* h_mask) {
 int qwg_spec_step(qwg_model* m, int32_t token, int draft_layers, int k, int32_t* out_tokens, int* n_out,
                   int* n_accepted) {
   if (!m || !out_tokens || !n_out || !n_accepted) return fail(QWG_E_INVAL, "NULL pointer");
-  if (k < 1 || k + 1 > m->d.max_cols) return fail(QWG_E_SHAPE, "need 1 <= k and k + 1 <= max_cols");
+  if (k < 1 || k + 1 > std::min(m->d.max_cols, MAX_COLS)) return fail(QWG_E_SHAPE, "need 1 <= k and k + 1 <= min(max_cols, 8)");
   if (draft_layers < 0 || draft_layers > m->d.n_layers) return fail(QWG_E_SHAPE, "bad draft_layers");
   return guarded([&]() -> int {
     const int p = m->n_past;
@@ -1224,6 +1257,7 @@ int qwg_spec_step(qwg_model* m, int32_t token, int draft_layers, int k, int32_t*
 
 int qwg_verify(qwg_model* m, const int32_t* tokens, int n, float* h_logits, int32_t* h_argmax) {
   if (!m || !tokens) return fail(QWG_E_INVAL, "NULL pointer");
+  if (n < 1 || n > MAX_COLS) return fail(QWG_E_SHAPE, "verify takes 1..8 columns");
   return guarded([&]() -> int {
     if (int rc = run_pass(m, tokens, n, m->n_past, m->d.n_layers, false)) return rc;
     std::vector<int32_t> am(n);

@@ -870,6 +870,228 @@ __global__ __launch_bounds__(NG == 1 ? 1024 : 512) void k_gemv_mfma(GemvArgs a, 
   }
 }
 
+// ------------------------------------------------------------------ prompt prefill: up to 64 columns
+//
+// Chunked prefill ([NT] "Quick start": the -p prompt) multiplies every weight matrix by up to 64
+// prompt-token columns, so each weight is read once per 64 tokens.  The activation of one step (16
+// chunks: two 256-weight superblocks) for all 64 columns, 128 KB of byte digits, does not leave room
+// for the whole K range on chip, so the K loop is outermost: per step the workgroup stages that step's
+// digits of every column in LDS, and each wave multiplies its 16-row tile's weights for the step by all
+// 16 column groups -- one v_mfma_i32_16x16x32_i8 per (chunk, column group) (Q6_K: two), all sharing
+// the chunk's B operand, so the weights are unpacked once per 64 columns.  Lane 16 g + n accumulates
+// (row n, column 4 cg + g) of group cg in fp32.  A workgroup takes 16 tiles (256 rows) of one K split
+// and writes partial sums; k_gemm_reduce adds the splits in a fixed order and runs the epilogue.
+constexpr int GM_NG = 16;                    // column groups of four: 64 columns
+constexpr int GM_SC = 16;                    // chunks per step
+constexpr int GM_DSTR = GM_NG * 64 + 1;      // 8-B digit entries per chunk ([group][lane]) + 1 of padding
+constexpr int GM_ESTR = GM_SC + 2;           // descriptor entries per column (+2: rows start on other banks)
+constexpr int GM_WAVES = 16;                 // waves (tiles) per workgroup
+constexpr size_t GM_LDS = (size_t)GM_SC * GM_DSTR * 8 + (size_t)GM_NG * 4 * GM_ESTR * 8;
+
+template <int QT>
+__global__ __launch_bounds__(64 * GM_WAVES) void k_gemm_mfma(GemvArgs a) {
+  static_assert(QT == Q4_K || QT == Q5_K || QT == Q6_K, "K-quant formats with 32-weight chunks");
+  extern __shared__ uint4 lds[];
+  uint2* ldig = (uint2*)lds;                            // [GM_SC][GM_DSTR]
+  float2* ldesc = (float2*)(ldig + GM_SC * GM_DSTR);   // [64 columns][GM_ESTR]: (2^-s, 2^-s sum x_fix)
+  const int tid = threadIdx.x, lane = tid & 63, nw = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int nc = a.nc, rows = a.w.rows;
+  const int split = blockIdx.y;
+  const int kbeg = split * a.ks, klen = min(a.ks, a.k - kbeg);
+  const int nst = klen / (XCHUNK * GM_SC);  // steps of this split
+  const int cbase = kbeg / XCHUNK;
+  const int r0 = (blockIdx.x * nw + wave) * 16;
+  const bool live = r0 < rows;  // waves past the last tile stage the activation and compute nothing
+  const int row = min(r0 + n, rows - 1);
+  const uint32_t ro = row_off(QT, a.w, row), srow = slot_row(a.w.ilv, a.w.nch, row);
+  // per-lane bit-move amounts: Q5_K fifth bits (rotations), Q6_K high pairs (shifts)
+  const uint32_t rot_lo = (uint32_t)(28 + 2 * g) & 31u, rot_hi = (uint32_t)(29 + 2 * g) & 31u;
+  const uint32_t shl_lo = (g & 1) ? 2u : 6u, shl_hi = (g & 1) ? 0u : 4u;
+  float acc[GM_NG];
+#pragma unroll
+  for (int cg = 0; cg < GM_NG; ++cg) acc[cg] = 0.f;
+
+  // quarter qq (chunks 4 qq .. 4 qq + 3 of the step): the quant words transposed across the lane
+  // groups, the B operands and the chunks' weight scales, then for every column group the A operands
+  // from LDS, the products and the (row n, column 4 cg + g) updates.  hv: the superblock header
+  // (Q4_K / Q5_K) from the lane group that loaded it.
+  auto quarter = [&](const MfRaw<QT>& r, int qq, const uint4& hv) {
+    const uint4 qv = r.q[qq];
+    uint32_t R[4] = {qv.x, qv.y, qv.z, qv.w};
+    lane_swap32(R[0], R[2]);
+    lane_swap32(R[1], R[3]);
+    lane_swap16(R[0], R[1]);
+    lane_swap16(R[2], R[3]);  // R[j] = quant word g of chunk 4 qq + j
+    uint64_t B0[4], B1[4];
+    float w0[4], w1[4];
+    if constexpr (QT == Q4_K || QT == Q5_K) {
+      if constexpr (QT == Q5_K) {
+        const int src = n + 16 * qq;
+        const uint32_t qh[4] = {lane_fetch(src, r.qh.x), lane_fetch(src, r.qh.y), lane_fetch(src, r.qh.z),
+                                lane_fetch(src, r.qh.w)};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t l5 = __builtin_rotateright32(qh[j], rot_lo), h5 = __builtin_rotateright32(qh[j], rot_hi);
+          const uint32_t lo = (R[j] & 0x0F0F0F0Fu) | (l5 & 0x10101010u);
+          const uint32_t hi = ((R[j] >> 4) & 0x0F0F0F0Fu) | (h5 & 0x10101010u);
+          B0[j] = (uint64_t)lo | ((uint64_t)hi << 32);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {  // the stored nibbles are q XOR 8: flip back to q in 0..15
+          const uint32_t lo = (R[j] & 0x0F0F0F0Fu) ^ 0x08080808u;
+          const uint32_t hi = ((R[j] >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;
+          B0[j] = (uint64_t)lo | ((uint64_t)hi << 32);
+        }
+      }
+      const uint64_t ps = (uint64_t)hv.x | ((uint64_t)hv.y << 32);
+      const uint64_t pm = (uint64_t)hv.z | ((uint64_t)hv.w << 32);
+      const float dd = half_bits_to_float(hv.y >> 16), dm = half_bits_to_float(hv.w >> 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int sb = 4 * (qq & 1) + j;  // sub-block of the superblock
+        w0[j] = dd * (float)((uint32_t)(ps >> (6 * sb)) & 63u);
+        w1[j] = -(dm * (float)((uint32_t)(pm >> (6 * sb)) & 63u));
+      }
+    } else {
+      const int src0 = n + 16 * ((2 * qq) & 3), src1 = n + 16 * ((2 * qq + 1) & 3);
+      const uint4 qp = qq < 2 ? r.qhA : r.qhB;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int src = (j >> 1) ? src1 : src0;
+        const uint32_t hx = lane_fetch(src, (j & 1) ? qp.z : qp.x), hy = lane_fetch(src, (j & 1) ? qp.w : qp.y);
+        const uint32_t h = g < 2 ? hx : hy;
+        const uint32_t lo = ((R[j] << 2) & 0x3C3C3C3Cu) | ((h << shl_lo) & 0xC0C0C0C0u);
+        const uint32_t hi = ((R[j] >> 2) & 0x3C3C3C3Cu) | ((h << shl_hi) & 0xC0C0C0C0u);
+        B0[j] = (uint64_t)lo;
+        B1[j] = (uint64_t)hi << 32;
+      }
+      const float dq = 0.25f * half_bits_to_float((r.dw >> (16 * (qq >> 1))) & 0xFFFFu);
+      const uint32_t scw[2] = {lane_fetch(n + 16 * qq, r.sc.x), lane_fetch(n + 16 * qq, r.sc.y)};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = scw[j >> 1] >> (16 * (j & 1));
+        w0[j] = dq * (float)(int32_t)(int8_t)(uint8_t)(w & 0xFFu);
+        w1[j] = dq * (float)(int32_t)(int8_t)(uint8_t)((w >> 8) & 0xFFu);
+      }
+    }
+#pragma unroll
+    for (int cg = 0; cg < GM_NG; ++cg) {
+      const float4 d01 = *(const float4*)&ldesc[(4 * cg + g) * GM_ESTR + 4 * qq];
+      const float4 d23 = *(const float4*)&ldesc[(4 * cg + g) * GM_ESTR + 4 * qq + 2];
+      const float inv[4] = {d01.x, d01.z, d23.x, d23.z};
+      float v = acc[cg];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint2 av = ldig[(4 * qq + j) * GM_DSTR + cg * 64 + lane];
+        const uint64_t A = (uint64_t)av.x | ((uint64_t)av.y << 32);
+        const qwg_i32x4 D = mfma_i8(A, B0[j]);
+        v = __builtin_fmaf(inv[j] * w0[j], mf_value(D), v);
+        if constexpr (QT == Q6_K) {
+          const qwg_i32x4 E = mfma_i8(A, B1[j]);
+          v = __builtin_fmaf(inv[j] * w1[j], mf_value(E), v);
+        } else {
+          const float xs[4] = {d01.y, d01.w, d23.y, d23.w};
+          v = __builtin_fmaf(w1[j], xs[j], v);
+        }
+      }
+      acc[cg] = v;
+    }
+  };
+
+  MfRaw<QT> cur;
+  auto load = [&](int st) { return mf_load<QT>(a.w, ro, srow, cbase + GM_SC * min(st, nst - 1), g); };
+  if (live && nst > 0) cur = load(0);
+  for (int st = 0; st < nst; ++st) {
+    // 1. stage this step's digits of every column (columns >= nc are zeros): one (column, chunk) per job
+    if (st > 0) __syncthreads();  // every wave is done with the previous step's digits
+    for (int job = tid; job < 4 * GM_NG * GM_SC; job += blockDim.x) {
+      const int col = job / GM_SC, c = job - col * GM_SC;
+      uint32_t wd[DIG_CHUNK_WORDS];
+      if (col < nc) {
+        const uint4* src = a.xd + (int64_t)col * a.xd_stride + (int64_t)(cbase + st * GM_SC + c) * XSLOTS;
+#pragma unroll
+        for (int q = 0; q < XSLOTS; ++q) {
+          const uint4 v = src[q];
+          wd[4 * q] = v.x;
+          wd[4 * q + 1] = v.y;
+          wd[4 * q + 2] = v.z;
+          wd[4 * q + 3] = v.w;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < DIG_CHUNK_WORDS; ++i) wd[i] = 0;
+      }
+      const int ent = c * GM_DSTR + (col >> 2) * 64 + (col & 3) * BYTE_LEVELS;
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg)
+#pragma unroll
+        for (int lv = 0; lv < BYTE_LEVELS; ++lv)
+          ldig[ent + gg * 16 + lv] = make_uint2(wd[gg * BYTE_LEVELS + lv], wd[16 + gg * BYTE_LEVELS + lv]);
+      const float inv = __uint_as_float(wd[DIG_WORDS]);
+      ldesc[col * GM_ESTR + c] = make_float2(inv, inv * __uint_as_float(wd[DIG_WORDS + 1]));
+    }
+    __syncthreads();
+    // 2. the next step's weights are requested before this step's products
+    if (live) {
+      const MfRaw<QT> r = cur;
+      if (st + 1 < nst) cur = load(st + 1);
+      if constexpr (QT == Q4_K || QT == Q5_K) {
+#pragma unroll
+        for (int sbk = 0; sbk < 2; ++sbk) {
+          const int src = n + 16 * sbk;
+          const uint4 hv = make_uint4(lane_fetch(src, r.h.x), lane_fetch(src, r.h.y), lane_fetch(src, r.h.z),
+                                      lane_fetch(src, r.h.w));
+          quarter(r, 2 * sbk, hv);
+          quarter(r, 2 * sbk + 1, hv);
+        }
+      } else {
+        const uint4 none = make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) quarter(r, qq, none);
+      }
+    }
+  }
+  // 3. partial sums of this split: (row r0 + n, column 4 cg + g)
+  if (live && r0 + n < rows) {
+#pragma unroll
+    for (int cg = 0; cg < GM_NG; ++cg) {
+      const int col = 4 * cg + g;
+      if (col < nc) a.part[((int64_t)split * nc + col) * rows + r0 + n] = acc[cg];
+    }
+  }
+}
+
+// Fixed-order sum of the K splits of k_gemm_mfma, the RMSNorm scale and the epilogue: one thread per
+// (row, column), 256 rows per workgroup (pairs of rows share a wave for RoPE and SwiGLU), column =
+// blockIdx.y.
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gemm_reduce(const float* part, int ksplit, int nc, int rows, EpiArgs e) {
+  __shared__ float red[16];
+  const int n = blockIdx.y, tid = threadIdx.x;
+  const int row = blockIdx.x * blockDim.x + tid;
+  float rs = 1.0f;
+  if (e.sq_in) {
+    float sq = 0.f;
+    for (int i = tid; i < e.sq_in_n; i += blockDim.x) sq += e.sq_in[(int64_t)n * e.sq_in_stride + i];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off);
+    if ((tid & 63) == 0) red[tid >> 6] = sq;
+    __syncthreads();
+    float t = 0.f;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += red[w];
+    rs = 1.0f / sqrtf(t / e.rms_k + e.eps);
+  }
+  float v = 0.f;
+  if (row < rows)
+    for (int s = 0; s < ksplit; ++s) v += part[((int64_t)s * nc + n) * rows + row];
+  v *= rs;
+  const float vp = __shfl_xor(v, 1);
+  if (row < rows) run_epilogue(EPI, e, n, row, v, vp);
+}
+
 // Activation digits of nc columns of length k, four threads per 32-element chunk (thread m takes
 // elements 4m..4m+3 and 16+4m..16+4m+3 with two float4 loads).  With a gain vector the digits are
 // of g * x and sq receives each chunk's sum of x^2 (for the consumer's RMSNorm).
@@ -990,7 +1212,31 @@ static GemvPlan plan_mfma(int64_t rows, int64_t k, int nc) {
 // formats whose 4-row two-pass kernel fits 128 registers without spilling
 static bool two_pass_ok(int qt) { return qt == Q4_0 || qt == Q4_K || qt == Q8_0; }
 
+// The prefill form (9..64 columns): 16 tiles of 16 rows per workgroup, and K splits (whole steps of 16
+// chunks) until the workgroups cover about one per CU; the splits always go through k_gemm_reduce.
+static GemvPlan plan_gemm64(int64_t rows, int64_t k, int nc) {
+  GemvPlan p{};
+  p.mfma = 2;
+  p.ncm = 4 * GM_NG;
+  p.waves = GM_WAVES;
+  p.rows_per_wave = 16;
+  p.depth = 1;
+  p.passes = 1;
+  const int64_t nblk = (rows + 16 * GM_WAVES - 1) / (16 * GM_WAVES);
+  const int64_t nsteps = k / (XCHUNK * GM_SC);
+  int64_t ksplit = std::max<int64_t>(1, std::min<int64_t>(nsteps, (PERSISTENT_WGS + nblk / 2) / std::max<int64_t>(1, nblk)));
+  const int64_t sps = (nsteps + ksplit - 1) / ksplit;
+  ksplit = (nsteps + sps - 1) / sps;
+  p.ks = (int)(sps * XCHUNK * GM_SC);
+  p.ksplit = (int)ksplit;
+  p.grid_x = (int)nblk;
+  p.lds = GM_LDS;
+  p.part_bytes = (size_t)ksplit * nc * rows * sizeof(float);
+  return p;
+}
+
 GemvPlan plan_gemv(int qt, int64_t rows, int64_t k, int nc, int epi, int mfma) {
+  if (nc > MAX_COLS && (qt == Q4_K || qt == Q5_K || qt == Q6_K) && k % 512 == 0) return plan_gemm64(rows, k, nc);
   if ((mfma < 0 ? g_mfma : mfma) && nc >= 2 && nc <= 8 && (qt == Q4_K || qt == Q5_K || qt == Q6_K) &&
       k % 512 == 0)  // steps are two superblocks
     return plan_mfma(rows, k, nc);
@@ -1088,6 +1334,7 @@ bool gemv_can_digitize_input(const GemvPlan& p, int epi) {
 }
 
 bool gemv_can_digitize_output(const GemvPlan& p, int epi, int64_t rows) {
+  if (p.mfma == 2) return false;  // the prefill form's reduce kernel writes fp32 only
   if (epi != EPI_RESID && epi != EPI_SWIGLU) return false;
   if (rows % (epi == EPI_SWIGLU ? 2 * XCHUNK : XCHUNK) != 0) return false;
   if (p.ksplit > 1) return true;  // the reduce kernel covers 256 rows per block
@@ -1206,8 +1453,8 @@ static hipError_t launch_mfma(const GemvArgs& a, int epi, const GemvPlan& p, dim
 hipError_t launch_gemv(int qt, const MatView& w, int64_t k, const void* xd, int64_t xd_stride_bytes, int nc, int epi,
                        const EpiArgs& e, float* part, hipStream_t st, const GemvPlan& p, hipEvent_t ev_start,
                        hipEvent_t ev_stop) {
-  // the kernels keep per-column sums in arrays of MAX_COLS
-  if (nc < 1 || nc > MAX_COLS || nc > p.ncm) return hipErrorInvalidValue;
+  // the kernels keep per-column sums in arrays of MAX_COLS (the prefill form: 64 columns)
+  if (nc < 1 || nc > p.ncm || (p.mfma != 2 && nc > MAX_COLS)) return hipErrorInvalidValue;
   if (e.dig_out && !gemv_can_digitize_output(p, epi, w.rows)) return hipErrorInvalidValue;
   GemvArgs a;
   a.w = w;
@@ -1227,6 +1474,29 @@ hipError_t launch_gemv(int qt, const MatView& w, int64_t k, const void* xd, int6
   // the stop event goes on the last kernel: the GEMV itself, or the split reduction after it
   const Dispatch d1{st, ev_start, p.ksplit == 1 ? ev_stop : nullptr};
   hipError_t err;
+  if (p.mfma == 2) {
+    if (e.xf || !part) return hipErrorInvalidValue;
+    grid.x = p.grid_x;
+    const Dispatch d0{st, ev_start, nullptr};
+    switch (qt) {
+      case Q4_K: go(d0, k_gemm_mfma<Q4_K>, grid, block, p.lds, a); break;
+      case Q5_K: go(d0, k_gemm_mfma<Q5_K>, grid, block, p.lds, a); break;
+      case Q6_K: go(d0, k_gemm_mfma<Q6_K>, grid, block, p.lds, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const Dispatch dr{st, nullptr, ev_stop};
+    dim3 rg((rows + 255) / 256, nc);
+    switch (epi) {
+      case EPI_STORE: go(dr, k_gemm_reduce<EPI_STORE>, rg, dim3(256), 0, part, p.ksplit, nc, rows, e); break;
+      case EPI_RESID: go(dr, k_gemm_reduce<EPI_RESID>, rg, dim3(256), 0, part, p.ksplit, nc, rows, e); break;
+      case EPI_SWIGLU: go(dr, k_gemm_reduce<EPI_SWIGLU>, rg, dim3(256), 0, part, p.ksplit, nc, rows, e); break;
+      case EPI_QKV: go(dr, k_gemm_reduce<EPI_QKV>, rg, dim3(256), 0, part, p.ksplit, nc, rows, e); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   if (p.mfma) {
     if (e.xf || nc < 1 || nc > p.ncm) return hipErrorInvalidValue;
     grid.x = p.grid_x;

@@ -9,7 +9,8 @@
 namespace qwg {
 
 constexpr int HEAD_DIM = 128;   // every supported model uses 128-wide heads
-constexpr int MAX_COLS = 8;     // widest multi-column pass
+constexpr int MAX_COLS = 8;     // widest multi-column pass of the decode kernels (verify, short prefill)
+constexpr int MAX_PREFILL_COLS = 64;  // widest prefill pass (K-quant layers: the 64-column GEMM)
 constexpr size_t LDS_BUDGET = 150 * 1024;  // dynamic LDS per workgroup (gfx950: 160 KiB per CU)
 
 // What the GEMV does with each finished output row (columns n < nc).

@@ -67,7 +67,7 @@ hipError_t launch_dequant(int qt, const MatView& w, int64_t rows, int64_t k, flo
 // ------------------------------------------------------------------------------------------ embedding row
 
 struct Tokens {
-  int32_t t[MAX_COLS];
+  int32_t t[MAX_PREFILL_COLS];
 };
 
 template <int QT>
@@ -88,7 +88,7 @@ __global__ void k_embed(MatView w, Tokens tok, int nc, float* h, int64_t h_strid
 hipError_t launch_embed(int qt, const MatView& w, int64_t k, const int32_t* tokens, int nc, float* h, int64_t h_stride,
                         hipStream_t st) {
   (void)k;  // the row length is the matrix view's
-  if (nc < 1 || nc > MAX_COLS) return hipErrorInvalidValue;  // one token slot per column
+  if (nc < 1 || nc > MAX_PREFILL_COLS) return hipErrorInvalidValue;  // one token slot per column
   Tokens tk{};
   for (int i = 0; i < nc; ++i) tk.t[i] = tokens[i];
   dim3 g((w.nch + 127) / 128, nc), b(128);
@@ -482,7 +482,7 @@ hipError_t launch_attn(const float* q, int64_t q_stride, const uint16_t* kc, con
                        int n_pos, int n_q, int n_kv, int nc, float* out, int64_t out_stride, void* work,
                        const AttnPlan& p, hipStream_t st, uint32_t* dig_out, int64_t dig_stride, int dig_kind) {
   const int NQ = nc * (n_q / n_kv);
-  if (NQ > 64 || p.nsplit < 1) return hipErrorInvalidValue;
+  if (n_q / n_kv > 64 || NQ > 4096 || p.nsplit < 1) return hipErrorInvalidValue;
   AttnArgs a;
   a.q = q;
   a.q_stride = q_stride;
@@ -511,9 +511,6 @@ hipError_t launch_attn(const float* q, int64_t q_stride, const uint16_t* kc, con
 
 // ------------------------------------------------------------------------------------------ plain read
 
-// Streaming read of n16 16-byte words: wave w of the grid reads one contiguous segment, lane l the
-// words l, l+64, ... of it, four 16-B non-temporal loads in flight per lane (the GEMV's own load
-// pattern without its arithmetic).  One XOR checksum per wave keeps the loads alive.
 // Waits `ticks` of the constant-rate wall clock, then exits (a bounded delay for ordering tests).
 __global__ void k_spin(uint64_t ticks) {
   const uint64_t t0 = wall_clock64();
@@ -525,6 +522,9 @@ hipError_t launch_spin(uint64_t ticks, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Streaming read of n16 16-byte words: wave w of the grid reads one contiguous segment, lane l the
+// words l, l+64, ... of it, U 16-B non-temporal loads in flight per lane (the GEMV's own load
+// pattern without its arithmetic).  One XOR checksum per wave keeps the loads alive.
 template <int U>
 __global__ __launch_bounds__(512) void k_read(const uint4* __restrict__ p, int64_t n16, int64_t per_wave,
                                               uint32_t* sink) {

@@ -173,6 +173,32 @@ def test_llama70b_q4_k_prefill_on_matrix_cores_equals_steps(qwg):
     free(m)
 
 
+@pytest.mark.timeout(600)
+def test_llama70b_q4_k_prefill_64_tokens_one_pass_equals_steps(qwg):
+    """At the 70B Q4_K shape, a 64-token prompt in one pass of the prompt-prefill GEMM (64 columns, every
+    weight read once) equals 64 one-column decode steps (themselves checked against the oracle above):
+    the next token's logits and the K/V rows of all 64 prompt positions on sampled layers."""
+    wl = synth.LLAMA70B_Q4_K
+    ctx = wl.n_prior + 72
+    m = qwg.make_model(wl, max_ctx=ctx, max_cols=64)
+    qwg.load(m, wl)
+    prompt = [(wl.first_token() + 7919 * i) % wl.vocab for i in range(64)]
+    p_next, p_logits = m.prefill(prompt, want_logits=True)
+    rows = slice(wl.n_prior, wl.n_prior + 64)
+    kv_p = {l: m.get_kv(l, wl.n_prior + 64) for l in (0, 40, 79)}
+    m.truncate(wl.n_prior)
+    for t in prompt:
+        s_next, s_logits = m.decode_step(t, want_logits=True)
+    assert rel_l2(p_logits, s_logits) < 2e-3
+    if p_next != s_next:
+        assert is_tie(s_logits, p_next, s_next)
+    for l, (pk, pv) in kv_p.items():
+        sk, sv = m.get_kv(l, wl.n_prior + 64)
+        assert rel_l2(f16(pk[rows]), f16(sk[rows])) < 2e-3, l
+        assert rel_l2(f16(pv[rows]), f16(sv[rows])) < 2e-3, l
+    free(m)
+
+
 @pytest.mark.timeout(900)
 def test_llama70b_q6_k_streamed_skip(qwg):
     wl = synth.LLAMA70B_Q6_K_STREAM

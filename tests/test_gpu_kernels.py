@@ -226,6 +226,40 @@ def test_gemv_two_streams_in_flight(ops):
         assert gemv_ok(outs[i].cpu().numpy(), yr, ar).all(), i
 
 
+@pytest.mark.parametrize("qt", [synth.Q4_K, synth.Q5_K, synth.Q6_K], ids=["Q4_K", "Q5_K", "Q6_K"])
+@pytest.mark.parametrize("shape", [(16, 512), (300, 2048), (1000, 8192), (70, 28672), (4096 + 48 + 6, 1024)],
+                         ids=["one_tile", "ragged", "k8192", "k28672_splits", "many_blocks"])
+@pytest.mark.parametrize("nc", [9, 33, 64])
+def test_gemv_prefill_columns(ops, qt, shape, nc):
+    """9..64 columns (the prompt-prefill GEMM: 64 columns per step staged in LDS, 16-row tiles, K splits
+    added by the reduction kernel): every row of every column within the row bound."""
+    rows, k = shape
+    W = synth.matrix(synth.DEFAULT_DIST[qt], k, rows, tkey=synth.key(15, qt * 1000 + k))
+    x = synth.normal_f32(synth.key(15, 70 + nc), nc * k).reshape(nc, k)
+    y = ops.gemv(qt, packed_of(ops, qt, W, rows, k), rows, k, dev(x)).cpu().numpy()
+    yr, ar = oracle.gemv(qt, W, rows, k, x)
+    ok = gemv_ok(y, yr, ar)
+    assert ok.all(), (np.argwhere(~ok)[:5], float(np.max(np.abs(y - yr) / (1e-4 * ar + 1e-6))))
+
+
+@pytest.mark.parametrize("qt", [synth.Q4_K, synth.Q6_K], ids=["Q4_K", "Q6_K"])
+def test_gemv_prefill_columns_outliers_and_nan(ops, qt):
+    """The prefill GEMM on the outlier workload (1e6 x in every chunk, zero weights under it) and with a
+    NaN in one column: that column's rows are non-finite, the other columns within the bound."""
+    import blockedit
+    rows, k, nc = 200, 2048, 40
+    W = synth.matrix(synth.DEFAULT_DIST[qt], k, rows, tkey=synth.key(16, qt))
+    x, cols = _outlier_x(k, nc, 1e6, 77)
+    W = blockedit.zero_columns(qt, W, rows, k, cols)
+    x[17, 100] = np.nan
+    y = ops.gemv(qt, packed_of(ops, qt, W, rows, k), rows, k, dev(x)).cpu().numpy()
+    with np.errstate(invalid="ignore"):
+        yr, ar = oracle.gemv(qt, W, rows, k, x)
+    assert not np.isfinite(y[17]).any()
+    keep = np.arange(nc) != 17
+    assert gemv_ok(y[keep], yr[keep], ar[keep]).all()
+
+
 def test_gemv_q8_0_4096_full(ops):
     """The single Q8_0 GEMV workload: W 4096 x 4096, q ~ U[-127,127], d = |N|*0.02, x ~ N(0,1)."""
     qt, rows, k = synth.Q8_0, 4096, 4096
@@ -263,8 +297,13 @@ def test_gemv_rejects_bad_shapes(ops):
     with pytest.raises(QwgError):
         ops.gemv(synth.Q4_K, W, 2, 300, x)
     x9 = torch.zeros((9, 256), dtype=torch.float32, device=DEV)
-    with pytest.raises(QwgError):
+    with pytest.raises(QwgError):  # 9 columns need K a multiple of 512 (and a K-quant)
         ops.gemv(synth.Q4_K, W, 2, 256, x9)
+    x65 = torch.zeros((65, 512), dtype=torch.float32, device=DEV)
+    with pytest.raises(QwgError):
+        ops.gemv(synth.Q4_K, W, 2, 512, x65)
+    with pytest.raises(QwgError):
+        ops.gemv(synth.Q8_0, W, 2, 512, x65[:9])
 
 
 def test_rmsnorm(ops):
