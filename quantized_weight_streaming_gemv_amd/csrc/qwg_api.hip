@@ -900,7 +900,7 @@ int qwg_rope(float* d_v, int n_heads, int head_dim, const float* d_table, int po
 
 size_t qwg_attn_work_bytes(int n_pos, int n_q, int n_kv, int head_dim, int n_cols) {
   if (n_pos < 1 || n_pos > 262144 || n_q < 1 || n_kv < 1 || n_kv > 64 || n_q % n_kv || head_dim != HEAD_DIM ||
-      n_cols < 1 || n_cols > MAX_COLS || n_q / n_kv * n_cols > 64)
+      n_cols < 1 || n_cols > MAX_PREFILL_COLS || n_q / n_kv > 64)
     return 0;
   return plan_attn(n_pos, n_q, n_kv, n_cols).work_bytes;
 }
@@ -909,9 +909,10 @@ int qwg_attn_decode(const float* d_q, const uint16_t* d_kc, const uint16_t* d_vc
                     int head_dim, int n_cols, float* d_out, void* d_work, size_t work_bytes, void* stream) {
   if (!d_q || !d_kc || !d_vc || !d_out || !d_work) return fail(QWG_E_INVAL, "NULL pointer");
   if (head_dim != HEAD_DIM) return fail(QWG_E_SHAPE, "head_dim must be 128");
-  if (n_pos < 1 || n_pos > 262144 || n_q < 1 || n_kv < 1 || n_kv > 64 || n_q % n_kv || n_cols < 1 || n_cols > MAX_COLS)
+  if (n_pos < 1 || n_pos > 262144 || n_q < 1 || n_kv < 1 || n_kv > 64 || n_q % n_kv || n_cols < 1 ||
+      n_cols > MAX_PREFILL_COLS)
     return fail(QWG_E_SHAPE, "bad attention shape");
-  if (n_q / n_kv * n_cols > 64) return fail(QWG_E_SHAPE, "(n_q / n_kv) * n_cols must be <= 64");
+  if (n_q / n_kv > 64) return fail(QWG_E_SHAPE, "n_q / n_kv must be <= 64");
   const AttnPlan p = plan_attn(n_pos, n_q, n_kv, n_cols);
   if (work_bytes < p.work_bytes) return fail(QWG_E_NOMEM, "work buffer smaller than qwg_attn_work_bytes");
   if (!aligned16(d_q) || !aligned16(d_kc) || !aligned16(d_vc) || ((uintptr_t)d_out & 7) || ((uintptr_t)d_work & 7))

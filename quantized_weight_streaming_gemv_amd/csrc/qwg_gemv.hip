@@ -977,27 +977,52 @@ __global__ __launch_bounds__(64 * GM_WAVES) void k_gemm_mfma(GemvArgs a) {
         w1[j] = dq * (float)(int32_t)(int8_t)(uint8_t)((w >> 8) & 0xFFu);
       }
     }
-#pragma unroll
-    for (int cg = 0; cg < GM_NG; ++cg) {
-      const float4 d01 = *(const float4*)&ldesc[(4 * cg + g) * GM_ESTR + 4 * qq];
-      const float4 d23 = *(const float4*)&ldesc[(4 * cg + g) * GM_ESTR + 4 * qq + 2];
-      const float inv[4] = {d01.x, d01.z, d23.x, d23.z};
-      float v = acc[cg];
+    // the products of column group cg + 1 are issued before group cg's are scaled, so the matrix
+    // cores work while the vector unit converts and scales (a product read right after its MFMA
+    // waits out the MFMA's latency)
+    constexpr int NP = QT == Q6_K ? 8 : 4;  // MFMAs per column group
+    auto products = [&](int cg, qwg_i32x4* P) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint2 av = ldig[(4 * qq + j) * GM_DSTR + cg * 64 + lane];
         const uint64_t A = (uint64_t)av.x | ((uint64_t)av.y << 32);
-        const qwg_i32x4 D = mfma_i8(A, B0[j]);
-        v = __builtin_fmaf(inv[j] * w0[j], mf_value(D), v);
-        if constexpr (QT == Q6_K) {
-          const qwg_i32x4 E = mfma_i8(A, B1[j]);
-          v = __builtin_fmaf(inv[j] * w1[j], mf_value(E), v);
-        } else {
-          const float xs[4] = {d01.y, d01.w, d23.y, d23.w};
+        P[j] = mfma_i8(A, B0[j]);
+        if constexpr (QT == Q6_K) P[4 + j] = mfma_i8(A, B1[j]);
+      }
+    };
+    // (Q5_K and Q6_K keep one group's products in flight only: two groups' operands overflow the 128
+    // registers a 16-wave workgroup leaves each wave)
+    constexpr bool PIPE = QT == Q4_K;
+
+    qwg_i32x4 Pc[NP], Pn[NP];
+    if (PIPE) products(0, Pc);
+#pragma unroll
+    for (int cg = 0; cg < GM_NG; ++cg) {
+      if (PIPE) {
+        if (cg + 1 < GM_NG) products(cg + 1, Pn);
+      } else {
+        products(cg, Pc);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the products ahead of this group's scaling
+      const float4 d01 = *(const float4*)&ldesc[(4 * cg + g) * GM_ESTR + 4 * qq];
+      const float4 d23 = *(const float4*)&ldesc[(4 * cg + g) * GM_ESTR + 4 * qq + 2];
+      const float inv[4] = {d01.x, d01.z, d23.x, d23.z};
+      const float xs[4] = {d01.y, d01.w, d23.y, d23.w};
+      float v = acc[cg];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v = __builtin_fmaf(inv[j] * w0[j], mf_value(Pc[j]), v);
+        if constexpr (QT == Q6_K)
+          v = __builtin_fmaf(inv[j] * w1[j], mf_value(Pc[4 + j]), v);
+        else
           v = __builtin_fmaf(w1[j], xs[j], v);
-        }
       }
       acc[cg] = v;
+      __builtin_amdgcn_sched_barrier(0);
+      if (PIPE) {
+#pragma unroll
+        for (int i = 0; i < NP; ++i) Pc[i] = Pn[i];
+      }
     }
   };
 

@@ -288,26 +288,34 @@ AttnPlan plan_attn(int n_pos, int n_q, int n_kv, int nc) {
   return p;
 }
 
-static size_t attn_lds_bytes(int NQ) {
-  return (size_t)NQ * HEAD_DIM * 4 + (size_t)NQ * ATT_T * 4 + (size_t)ATT_T * KROW * 2 + (size_t)ATT_T * HEAD_DIM * 2;
+// query rows of one attention workgroup (G per column, CPW columns): q, scores, the K and V tiles
+static size_t attn_lds_bytes(int rows) {
+  return (size_t)rows * HEAD_DIM * 4 + (size_t)rows * ATT_T * 4 + (size_t)ATT_T * KROW * 2 + (size_t)ATT_T * HEAD_DIM * 2;
 }
+// columns per workgroup of a pass wider than MAX_COLS: 2 beat 1 by ~13% on 64 columns of 2048
+// positions; 4 and 8 ran slower (their LDS leaves fewer waves per CU)
+constexpr int ATT_WIDE_CPW = 2;
 
-// One workgroup per (kv head g, split s of ATT_T positions, column n) for the G = n_q / n_kv query
-// rows of the group in that column (GQA: query heads g*G .. g*G+G-1 share K/V head g; a several-
-// column verify pass gets a workgroup per column, so its rows spread over more CUs):
+// One workgroup per (kv head g, split s of ATT_T positions, block of CPW columns) for the G = n_q / n_kv
+// query rows of the group in each of those columns (GQA: query heads g*G .. g*G+G-1 share K/V head g).
+// A decode or verify pass takes one column per workgroup (CPW = 1), so a verify's rows spread over
+// more CUs; a wide prefill pass takes two (CPW = 2), so each staged K/V tile serves 2 G rows:
 //   1. the K and V tiles and the queries are staged in LDS (every global load issued up front);
 //   2. wave w scores query rows w, w+ATT_WAVES, ... against its lane's position (scale 1/sqrt(128)), with
 //      causal masking per column, and keeps the split's max m, sum l and exp(score - m);
 //   3. the unnormalised output sum_t exp(.) v_t goes to the workspace with m and l;
 // k_attn_merge then combines the splits.
+template <int CPW>
 __global__ __launch_bounds__(ATT_THREADS) void k_attn(AttnArgs a) {
   extern __shared__ float sm[];
-  const int g = blockIdx.x, s = blockIdx.y, n = blockIdx.z;
+  const int g = blockIdx.x, s = blockIdx.y, n0 = blockIdx.z * CPW;
   const int G = a.n_q / a.n_kv, NQ = a.nc * G;
+  const int ncw = min(CPW, a.nc - n0);  // columns of this workgroup
+  const int R = ncw * G;                 // its query rows: column n0 + j / G, head g*G + j % G
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float* qs = sm;                                // [G][HEAD_DIM]
-  float* ps = qs + G * HEAD_DIM;                 // [G][ATT_T]
-  uint16_t* ks = (uint16_t*)(ps + G * ATT_T);    // [ATT_T][KROW]
+  float* qs = sm;                                // [CPW * G][HEAD_DIM]
+  float* ps = qs + CPW * G * HEAD_DIM;           // [CPW * G][ATT_T]
+  uint16_t* ks = (uint16_t*)(ps + CPW * G * ATT_T);  // [ATT_T][KROW]
   uint16_t* vs = ks + ATT_T * KROW;              // [ATT_T][HEAD_DIM]
   const int t0 = s * ATT_T;
   const int span = a.n_pos + a.nc - 1;
@@ -325,9 +333,10 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attn(AttnArgs a) {
       kv[j] = *(const uint4*)(a.kc + off);
       vv[j] = *(const uint4*)(a.vc + off);
     }
-    for (int i = tid; i < G * (HEAD_DIM / 4); i += ATT_THREADS) {
+    for (int i = tid; i < R * (HEAD_DIM / 4); i += ATT_THREADS) {
       const int j = i / (HEAD_DIM / 4), d4 = i % (HEAD_DIM / 4);
-      ((float4*)qs)[i] = ((const float4*)(a.q + (int64_t)n * a.q_stride + (int64_t)(g * G + j) * HEAD_DIM))[d4];
+      const int n = n0 + j / G, h = g * G + j % G;
+      ((float4*)qs)[i] = ((const float4*)(a.q + (int64_t)n * a.q_stride + (int64_t)h * HEAD_DIM))[d4];
     }
 #pragma unroll
     for (int j = 0; j < TP; ++j) {
@@ -350,8 +359,9 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attn(AttnArgs a) {
       kr[4 * i + 3] = v.w;
     }
     const float scale = 0.08838834764831845f;  // 1/sqrt(128)
-    for (int j = wave; j < G; j += ATT_WAVES) {
-      const int qi = n * G + j;
+    for (int j = wave; j < R; j += ATT_WAVES) {
+      const int n = n0 + j / G;
+      const int qi = n * G + j % G;
       const float4* qv = (const float4*)(qs + j * HEAD_DIM);
       float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll
@@ -378,8 +388,8 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attn(AttnArgs a) {
   __syncthreads();
 
   // 3. unnormalised output: wave w takes query rows w, w+ATT_WAVES, ...; lane = dimensions 2c, 2c+1
-  for (int j = wave; j < G; j += ATT_WAVES) {
-    const int qb = n * G + j;
+  for (int j = wave; j < R; j += ATT_WAVES) {
+    const int qb = (n0 + j / G) * G + j % G;
     const float* pr = ps + j * ATT_T;
     float o0 = 0.f, o1 = 0.f;
 #pragma unroll 8
@@ -500,9 +510,17 @@ hipError_t launch_attn(const float* q, int64_t q_stride, const uint16_t* kc, con
   a.dig = dig_out;
   a.dig_stride = dig_stride;
   a.dig_kind = dig_kind;
-  const size_t lds = attn_lds_bytes(n_q / n_kv);
-  if (lds > 150 * 1024) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_attn, dim3(n_kv, p.nsplit, nc), dim3(ATT_THREADS), lds, st, a);
+  if (nc > MAX_COLS && attn_lds_bytes(ATT_WIDE_CPW * (n_q / n_kv)) <= 150 * 1024) {
+    // wide prefill pass: ATT_WIDE_CPW columns share each staged K/V tile
+    const size_t lds = attn_lds_bytes(ATT_WIDE_CPW * (n_q / n_kv));
+    if (lds > 150 * 1024) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_attn<ATT_WIDE_CPW>, dim3(n_kv, p.nsplit, (nc + ATT_WIDE_CPW - 1) / ATT_WIDE_CPW),
+                       dim3(ATT_THREADS), lds, st, a);
+  } else {
+    const size_t lds = attn_lds_bytes(n_q / n_kv);
+    if (lds > 150 * 1024) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_attn<1>, dim3(n_kv, p.nsplit, nc), dim3(ATT_THREADS), lds, st, a);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_attn_merge, dim3(n_kv, NQ), dim3(64 * MW), 0, st, a);

@@ -99,6 +99,11 @@ def test_pointer_checks_without_gpu():
         p[bad] = M
         assert L.qwg_attn_decode(p[0], p[1], p[2], 100, 8, 2, 128, 1, p[3], p[4], wb, None) == -1, bad
     assert L.qwg_attn_decode(A, A, A, 100, 8, 2, 128, 1, A, A, wb - 8, None) == -3
+    # up to 64 columns (a prompt pass), at most 64 query heads per KV head
+    assert L.qwg_attn_work_bytes(100, 64, 8, 128, 64) > 0 and L.qwg_attn_work_bytes(100, 64, 8, 128, 65) == 0
+    assert L.qwg_attn_work_bytes(100, 65, 1, 128, 1) == 0 and L.qwg_attn_work_bytes(100, 64, 1, 128, 64) > 0
+    assert L.qwg_attn_decode(A, A, A, 100, 8, 2, 128, 65, A, A, 1 << 30, None) == -2
+    assert L.qwg_attn_decode(A, A, A, 100, 65, 1, 128, 1, A, A, 1 << 30, None) == -2
     assert L.qwg_rope(M, 8, 128, A, 0, None) == -1
     assert L.qwg_rope(A, 8, 128, A, -1, None) == -2
     assert L.qwg_rope(A, 8, 64, A, 0, None) == -2
