@@ -36,9 +36,15 @@ HBM_PEAK_GBPS = 8000.0
 # taken again.
 GEMV_TRAFFIC = {
     "workload": "llama70b-q4_k-resident",
-    "sources_sha256": None,
+    "sources_sha256": "c8a29085f592f8996f51eabe6a88a05e15cf539a462596e332d848d78d468375",
     "fetch_scale": 1.99975, "write_scale": 1.00000,
-    "classes": {},  # label -> (fetch KiB, write KiB) per launch
+    "classes": {  # label -> (fetch KiB, write KiB) per launch
+        "qkv": (23942.0, 44.8),
+        "wo": (18848.5, 80.0),
+        "gate_up": (132501.0, 112.1),
+        "down": (65320.1, 80.0),
+        "head": (290400.3, 538.2),
+    },
 }
 GEMV_SOURCES = ("qwg_gemv.hip", "qwg_formats.h", "qwg_kernels.h")
 
