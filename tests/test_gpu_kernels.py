@@ -122,19 +122,29 @@ def _outlier_x(k, nc, ratio, seed):
     return x, cols
 
 
-FORMS = [(1, True), (4, True), (4, False)]
+# (columns, matrix cores): the one-column kernel, the 4-column MFMA and dot forms, and the prompt GEMM
+# (more than 8 columns: K-quants only)
+FORMS = [(1, True), (4, True), (4, False), (40, True)]
+FORM_IDS = ["1col", "4col-mfma", "4col-dot", "40col-gemm"]
+
+
+def _skip_form(qt, nc):
+    if nc > 8 and qt not in (synth.Q4_K, synth.Q5_K, synth.Q6_K):
+        pytest.skip("the prompt GEMM takes K-quants only")
 
 
 @pytest.mark.parametrize("qt", QTS, ids=[synth.QTYPE_NAMES[q] for q in QTS])
 @pytest.mark.parametrize("ratio", [1e2, 1e4, 1e6], ids=["1e2", "1e4", "1e6"])
 @pytest.mark.parametrize("zero_under", [False, True], ids=["w", "w0"])
-@pytest.mark.parametrize("form", FORMS, ids=["1col", "4col-mfma", "4col-dot"])
+@pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
 def test_gemv_outlier_in_every_chunk(ops, qt, ratio, zero_under, form):
     """An outlier of 1e2..1e6 x the typical magnitude in every 32-element chunk (with the weights
     under it kept, or all zero so the outliers add nothing to sum|w x|): rows stay within
-    |y - y_ref| <= 1e-4 sum|w x| + 1e-6 on the one-column kernel and both several-column forms."""
+    |y - y_ref| <= 1e-4 sum|w x| + 1e-6 on the one-column kernel, both several-column forms and the
+    prompt GEMM."""
     import blockedit
     nc, mfma = form
+    _skip_form(qt, nc)
     rows, k = 96, 2048
     W = synth.matrix(synth.DEFAULT_DIST[qt], k, rows, tkey=synth.key(11, qt * 1000 + 1))
     x, cols = _outlier_x(k, nc, ratio, 2 + nc)
@@ -153,13 +163,14 @@ def test_gemv_outlier_in_every_chunk(ops, qt, ratio, zero_under, form):
 
 
 @pytest.mark.parametrize("qt", QTS, ids=[synth.QTYPE_NAMES[q] for q in QTS])
-@pytest.mark.parametrize("form", FORMS, ids=["1col", "4col-mfma", "4col-dot"])
+@pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
 def test_gemv_chunk_magnitudes(ops, qt, form):
     """Chunks of very different magnitudes in one vector: all-zero chunks, chunks of fp32 subnormals,
     chunks near 1e30 and 1e34, chunks mixing 1e-30 and 1 -- each chunk has its own power-of-two
     scale, which stays a normal fp32 number.  (Magnitudes whose exact partial sums overflow fp32 are
     outside what an fp32 result can hold and are not asked of it.)"""
     nc, mfma = form
+    _skip_form(qt, nc)
     rows, k = 80, 2048
     W = synth.matrix(synth.DEFAULT_DIST[qt], k, rows, tkey=synth.key(12, qt * 1000 + 1))
     x = synth.normal_f32(synth.key(12, 5 + nc), nc * k).reshape(nc, k)
@@ -181,13 +192,14 @@ def test_gemv_chunk_magnitudes(ops, qt, form):
 
 
 @pytest.mark.parametrize("qt", QTS, ids=[synth.QTYPE_NAMES[q] for q in QTS])
-@pytest.mark.parametrize("form", FORMS, ids=["1col", "4col-mfma", "4col-dot"])
+@pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
 @pytest.mark.parametrize("bad", ["nan", "inf", "-inf"])
 def test_gemv_non_finite_input_propagates(ops, qt, form, bad):
     """A NaN or an infinity in the activation makes every row non-finite, as the exact sum is (the
     oracle gives NaN, +-inf, or NaN where a zero weight meets the infinity); the other columns of a
     several-column call stay finite and within the row bound."""
     nc, mfma = form
+    _skip_form(qt, nc)
     rows, k = 64, 1024
     W = synth.matrix(synth.DEFAULT_DIST[qt], k, rows, tkey=synth.key(13, qt * 1000 + 1))
     x = synth.normal_f32(synth.key(13, 5 + nc), nc * k).reshape(nc, k)
