@@ -277,7 +277,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama70b-q4_k", choices=sorted(workloads()))
     ap.add_argument("--class-steps", type=int, default=4, help="steps per GEMV class for the per-class table")
-    ap.add_argument("--cpu-layers", type=int, default=8, help="oracle layers in the CPU-baseline sample")
+    ap.add_argument("--cpu-layers", type=int, default=24, help="oracle layers in the CPU-baseline sample (about 11 s of CPU work at the 70B shapes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-read-ceiling", action="store_true", help="skip the plain streaming-read reference")
     ap.add_argument("--no-q8-gemv", action="store_true", help="skip the single Q8_0 4096 x 4096 GEMV measurement")
