@@ -295,7 +295,7 @@ def main() -> int:
                     help="run one device-to-device copy of this many MiB first (scale for PMC byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         return 2
 
     import torch
