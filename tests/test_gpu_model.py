@@ -208,6 +208,45 @@ def test_calibrate_skip_matches_oracle(qwg):
     m.close()
 
 
+@pytest.mark.parametrize("cols", [8, 64], ids=["8col", "64col"])
+def test_prefill_after_calibration_skips_like_steps(qwg, cols):
+    """A prompt prefilled after skip calibration (Q6_K, near-identity odd layers, 3 of 6 resident)
+    bypasses the masked layers as decode steps do: the next token and its logits match the oracle's
+    sequential steps with the same mask, new KV rows match element by element in the computed layers,
+    and the skipped layers' caches get no new rows on either side.""" 
+    wl = synth.tiny(synth.Q6_K, n_layers=6, near_identity_every=2, wid=171)
+    max_ctx = wl.n_prior + 40
+    m = qwg.make_model(wl, n_resident=3, max_cols=cols, max_ctx=max_ctx)
+    qwg.load(m, wl)
+    om = oracle.OracleModel(wl, max_ctx=max_ctx)
+    t = wl.first_token()
+    _, _, g_mask = m.calibrate_skip(0.98, t)
+    r = om.calibrate_skip(0.98, t)
+    om.skip[:] = g_mask
+    assert g_mask.any() and not g_mask.all()
+    prompt = [(r["next"] + 7919 * i) % wl.vocab for i in range(19)]
+    n0 = m.n_past
+    assert om.n_past == n0
+    before = [m.get_kv(l, n0 + len(prompt)) for l in range(wl.n_layers)]
+    nxt, logits = m.prefill(prompt, want_logits=True)
+    for tok in prompt:
+        rr = om.decode(tok)
+    assert m.n_past == om.n_past == n0 + len(prompt)
+    assert rel_l2(logits, rr["logits"]) < 2e-3
+    if nxt != rr["next"]:
+        assert is_tie(rr["logits"], nxt, rr["next"])
+    new = slice(n0, om.n_past)
+    for l in range(wl.n_layers):
+        k, v = m.get_kv(l, om.n_past)
+        for gpu, ref, old in ((k, om.kc[l], before[l][0]), (v, om.vc[l], before[l][1])):
+            if g_mask[l]:  # no new rows: the GPU's cache is untouched, the oracle's still zero
+                assert np.array_equal(gpu[new], old[new]) and not ref[new].any(), l
+            else:
+                ok, worst = kv_rows_ok(gpu[new], ref[new])
+                assert ok.all(), (l, worst)
+    m.close()
+
+
 @pytest.mark.parametrize("mfma", [True, False], ids=["mfma", "dot"])
 def test_verify_columns_equal_sequential_steps(qwg, mfma):
     from quantized_weight_streaming_gemv_amd import ops
