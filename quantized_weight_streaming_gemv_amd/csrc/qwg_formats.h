@@ -282,7 +282,7 @@ __host__ __device__ inline int digit_kind(int qt) { return (qt == Q4_K || qt == 
 struct ChunkDesc {
   float inv_scale;  // 2^-s (NaN if the chunk holds a NaN or an infinity)
   float sum;        // sum of x_fix over the chunk, rounded once to fp32
-  int32_t shi, slo; // the same sum exactly: 32768 shi + slo (|shi|, |slo| <= 2^20)
+  int32_t shi, slo; // the same sum exactly: 32768 shi + slo (|shi| <= 2^20, 0 <= slo < 2^15)
 };
 
 // Four consecutive lanes (lane & 3 = m) digitize one 32-element chunk together.  Lane m passes the
@@ -297,39 +297,54 @@ __device__ inline uint32_t byte_gather(uint32_t a, uint32_t b, uint32_t j) {
 }
 
 // put(i, word) stores digit word i (0..31) or descriptor word i (32..35) of the chunk.
+// The value of lane (lane ^ 1) or (lane ^ 2) of the same quad: one DPP quad permute, no LDS trip.
+template <int CTRL>
+__device__ __forceinline__ uint32_t quad_swap(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, __uint_as_float(quad_swap<0xB1>(__float_as_uint(v))));  // quad_perm [1,0,3,2]
+  return fmaxf(v, __uint_as_float(quad_swap<0x4E>(__float_as_uint(v))));  // quad_perm [2,3,0,1]
+}
+__device__ __forceinline__ float quad_sum(float v) {
+  v += __uint_as_float(quad_swap<0xB1>(__float_as_uint(v)));
+  return v + __uint_as_float(quad_swap<0x4E>(__float_as_uint(v)));
+}
+template <int CTRL>
+__device__ __forceinline__ double quad_swap(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint64_t lo = quad_swap<CTRL>((uint32_t)b), hi = quad_swap<CTRL>((uint32_t)(b >> 32));
+  return __longlong_as_double((long long)((hi << 32) | lo));
+}
+__device__ __forceinline__ double quad_sum(double v) {
+  v += quad_swap<0xB1>(v);
+  return v + quad_swap<0x4E>(v);
+}
+
 template <class Put>
 __device__ inline void digitize_group_to(const float* v, int m, int kind, Put&& put, bool write) {
-  float mx = 0.f;
-  bool bad = false;
+  // the chunk maximum, and nf = NaN exactly when an element is a NaN or an infinity (0 * inf is NaN;
+  // fmaxf alone would skip a NaN)
+  float mx = 0.f, nf = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float a = fabsf(v[i]);
-    bad |= !(a <= 3.402823466e38f);  // NaN or infinity (fmaxf alone would skip a NaN)
-    mx = fmaxf(mx, a);
+    mx = fmaxf(mx, fabsf(v[i]));
+    nf = __builtin_fmaf(v[i], 0.0f, nf);
   }
-  mx = fmaxf(mx, __shfl_xor(mx, 1));
-  mx = fmaxf(mx, __shfl_xor(mx, 2));
-  int nb = bad ? 1 : 0;
-  nb |= __shfl_xor(nb, 1);
-  nb |= __shfl_xor(nb, 2);
-  bad = nb != 0;
-  // mx * 2^sh in [2^29, 2^30); 2^-sh stays a normal number
+  mx = quad_max(mx);
+  const bool bad = __builtin_isnan(quad_sum(nf));
+  // mx * 2^sh in [2^29, 2^30); 2^-sh stays a normal number (ilogb(mx) = frexp exponent - 1)
   int sh = 0;
-  if (mx > 0.f && !bad) sh = min(126, max(-126, FIX_TOP - ilogbf(mx)));
+  if (mx > 0.f && !bad) sh = min(126, max(-126, FIX_TOP + 1 - __builtin_amdgcn_frexp_expf(mx)));
   int32_t xf[8];
-  // sum of x_fix as two exact 16-bit-split integer sums (|x_fix| <= 2^30 would overflow an int32 sum
-  // of 32 elements): x_fix = hi * 2^15 + lo with 0 <= lo < 2^15
-  int32_t shi = 0, slo = 0;
+  // the sum of x_fix over the chunk, exactly (|sum| < 2^35: an fp64 sum of integers is exact)
+  double sx = 0.0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     xf[i] = bad ? 0 : (int32_t)rintf(ldexpf(v[i], sh));
-    shi += xf[i] >> 15;
-    slo += xf[i] & 0x7FFF;
+    sx += (double)xf[i];
   }
-  shi += __shfl_xor(shi, 1);
-  shi += __shfl_xor(shi, 2);
-  slo += __shfl_xor(slo, 1);
-  slo += __shfl_xor(slo, 2);
+  sx = quad_sum(sx);
   if (!write) return;
   // Adding 0x88888888 (0x80808080) and flipping the top bit of every nibble (byte) leaves balanced
   // digit l of x_fix, as a 4-bit (8-bit) two's-complement number, in nibble (byte) l of u.  The digit
@@ -366,10 +381,12 @@ __device__ inline void digitize_group_to(const float* v, int m, int kind, Put&& 
     }
   }
   if (m == 0) {
+    // sum = 32768 shi + slo with 0 <= slo < 32768
+    const double fh = floor(sx * (1.0 / 32768.0));
     put(DIG_WORDS, __float_as_uint(bad ? __builtin_nanf("") : ldexpf(1.0f, -sh)));
-    put(DIG_WORDS + 1, __float_as_uint(__builtin_fmaf(32768.0f, (float)shi, (float)slo)));
-    put(DIG_WORDS + 2, (uint32_t)shi);
-    put(DIG_WORDS + 3, (uint32_t)slo);
+    put(DIG_WORDS + 1, __float_as_uint((float)sx));
+    put(DIG_WORDS + 2, (uint32_t)(int32_t)fh);
+    put(DIG_WORDS + 3, (uint32_t)(int32_t)__builtin_fma(-32768.0, fh, sx));
   }
 }
 __device__ inline void digitize_group(const float* v, int m, int kind, uint32_t* oc, bool write) {

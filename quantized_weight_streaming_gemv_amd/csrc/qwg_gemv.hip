@@ -59,6 +59,27 @@ __device__ __forceinline__ float wave_sum(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// (cos, sin) of the RoPE pair that q/k row `row` of column n belongs to
+__device__ __forceinline__ float2 rope_pair(const EpiArgs& e, int n, int row) {
+  return ((const float2*)e.rope)[(int64_t)(e.pos + n) * (HEAD_DIM / 2) + ((row % HEAD_DIM) >> 1)];
+}
+
+// The QKV epilogue of row `row`, column n: RoPE with the pair's (cos, sin) cs on q and k, q to y,
+// k and v appended to the fp16 caches at position pos + n.
+__device__ __forceinline__ void qkv_store(const EpiArgs& e, int n, int row, float v, float vp, float2 cs) {
+  const int pos = e.pos + n;
+  if (row < e.nq_rows + e.nkv_rows) {
+    // pair (a, b) = rows (2i, 2i+1): a' = a cos - b sin, b' = a sin + b cos
+    const float out = (row & 1) == 0 ? (v * cs.x - vp * cs.y) : (vp * cs.y + v * cs.x);
+    if (row < e.nq_rows)
+      e.y[(int64_t)n * e.y_stride + row] = out;
+    else
+      e.kc[(int64_t)pos * e.kv_stride + (row - e.nq_rows)] = float_to_half_bits(out);
+  } else {
+    e.vc[(int64_t)pos * e.kv_stride + (row - e.nq_rows - e.nkv_rows)] = float_to_half_bits(v);
+  }
+}
+
 // Final value of output row `row`, column n (v: its sum; vp: the sum of its pair partner row^1),
 // stored by the epilogue; returns the value the output vector holds at that position (the new h
 // for RESID, silu(gate)*up for SWIGLU on even rows).
@@ -80,22 +101,9 @@ __device__ __forceinline__ float run_epilogue(int epi, const EpiArgs& e, int n, 
         return a;
       }
       return 0.f;
-    case EPI_QKV: {
-      const int pos = e.pos + n;
-      if (row < e.nq_rows + e.nkv_rows) {
-        const int i = (row % HEAD_DIM) >> 1;
-        const float2 cs = ((const float2*)e.rope)[(int64_t)pos * (HEAD_DIM / 2) + i];
-        // pair (a, b) = rows (2i, 2i+1): a' = a cos - b sin, b' = a sin + b cos
-        const float out = (row & 1) == 0 ? (v * cs.x - vp * cs.y) : (vp * cs.y + v * cs.x);
-        if (row < e.nq_rows)
-          e.y[(int64_t)n * e.y_stride + row] = out;
-        else
-          e.kc[(int64_t)pos * e.kv_stride + (row - e.nq_rows)] = float_to_half_bits(out);
-      } else {
-        e.vc[(int64_t)pos * e.kv_stride + (row - e.nq_rows - e.nkv_rows)] = float_to_half_bits(v);
-      }
+    case EPI_QKV:
+      qkv_store(e, n, row, v, vp, row < e.nq_rows + e.nkv_rows ? rope_pair(e, n, row) : make_float2(0.f, 0.f));
       return 0.f;
-    }
     default:
       return 0.f;
   }
@@ -123,9 +131,12 @@ __device__ __forceinline__ float rms_scale(const EpiArgs& e, float (*red)[16], i
 // Digitize output values held in LDS (osh[n][0 .. nout), nout a multiple of 32, output elements
 // out0 ..) for the next GEMV, with their per-chunk sums of squares.  Every group of four lanes
 // takes one (column, chunk); all threads of the block call it.
+// With gpre, (g0, g1) are this thread's gain values (elements 4m..4m+3 and 16+4m..16+4m+3 of chunk
+// tid / 4; one column, at most blockDim / 4 chunks), requested earlier.
 template <int OSTRIDE>
 __device__ __forceinline__ void digitize_outputs(const EpiArgs& e, int nc, const float (*osh)[OSTRIDE], int nout,
-                                                 int out0) {
+                                                 int out0, bool gpre = false, float4 g0 = {}, float4 g1 = {}) {
+  const float gp[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
   const int tid = threadIdx.x, m = tid & 3, g = tid >> 2;
   const int nchunk = nout / XCHUNK;
   for (int base = 0; base < nc * nchunk; base += blockDim.x >> 2) {
@@ -138,14 +149,13 @@ __device__ __forceinline__ void digitize_outputs(const EpiArgs& e, int nc, const
       const int el = j * XCHUNK + (i < 4 ? 4 * m + i : 16 + 4 * m + i - 4);
       float x = ok ? osh[n][el] : 0.f;
       ss += x * x;
-      if (e.dig_gain && ok) x *= e.dig_gain[out0 + el];
+      if (e.dig_gain && ok) x *= gpre ? gp[i] : e.dig_gain[out0 + el];
       v[i] = x;
     }
     const int chunk = (out0 / XCHUNK) + j;
     digitize_group(v, m, e.dig_kind, e.dig_out + (int64_t)n * e.dig_stride + (int64_t)chunk * DIG_CHUNK_WORDS, ok);
     if (e.sq_out) {
-      ss += __shfl_xor(ss, 1);
-      ss += __shfl_xor(ss, 2);
+      ss = quad_sum(ss);
       if (ok && m == 0) e.sq_out[(int64_t)n * e.sq_out_stride + chunk] = ss;
     }
   }
@@ -181,7 +191,11 @@ __host__ __device__ constexpr int lds_row_slots(int n) { return n + ((XSLOTS - n
 // P: groups per wave -- P row blocks of nw*R rows per workgroup (P == 0, persistent: the grid
 // strides over the row blocks, at most 64/R of them per workgroup).  Four-row two-group kernels are
 // held to 128 registers (four waves per SIMD, two workgroups per CU).  LB: the launch bound.  XIN:
-// the input arrives as fp32 (EpiArgs::xf) and every workgroup digitizes the part it needs into LDS.
+// the input arrives as fp32 (EpiArgs::xf) and every workgroup digitizes the part it needs into LDS:
+// XIN == 1 all of it before the loop; XIN == 2 (one column, 512 threads) in segments of 128 chunks:
+// the first before the loop, each later one right before the first iteration that reads it, from
+// fp32 values requested one segment earlier, so the digitization overlaps the weight stream
+// instead of delaying its start.
 template <int QT, int NCM, int R, int EPI, int PD, int P = 1, int LB = 512, int XIN = 0>
 __global__ __launch_bounds__(LB, (R == 4 && P == 2 ? 4 : 1)) void k_gemv(GemvArgs a) {
   static_assert(PD == 1 || PD == 2, "one or two iterations of loads in flight");
@@ -215,8 +229,13 @@ __global__ __launch_bounds__(LB, (R == 4 && P == 2 ? 4 : 1)) void k_gemv(GemvArg
   const int wg_rows = blk_rows * (P > 0 ? P : 1);
   const int wg_row0 = block_of(0) * blk_rows;
   const bool digitize = P > 0 && (EPI == EPI_RESID || EPI == EPI_SWIGLU) && a.e.dig_out != nullptr;
+  constexpr bool SEG = XIN == 2;
+  static_assert(!SEG || (NCM == 1 && PD == 1 && P > 0 && LB == 512), "segmented staging: one column, 512 threads");
   int ng = 0;  // groups of this wave (its rows of the workgroup's row blocks)
   while (ng < npass && ng < 64 / R && row0_of(ng) < rows) ++ng;
+  // segmented staging: every wave runs the same iterations (rows past the end are clamped and their
+  // results dropped), so all of them reach the same barriers
+  if (SEG) ng = P;
 
   // rows past the end are clamped to the last row (loads stay in bounds, results are dropped)
   // (per-chunk regions are addressed by slot = per-row part + per-chunk part, see slot_row)
@@ -247,6 +266,27 @@ __global__ __launch_bounds__(LB, (R == 4 && P == 2 ? 4 : 1)) void k_gemv(GemvArg
     }
   };
 
+  // segmented staging (XIN == 2): thread quad tid / 4 digitizes chunk SEGX s + tid / 4 of segment s
+  constexpr int SEGX = 128;                 // activation chunks per segment
+  constexpr int IPS = SEGX * WPX / 64;      // loop iterations per segment
+  const int nseg = (nxs + SEGX - 1) / SEGX;
+  float4 sx_lo, sx_hi;                      // the fp32 values of the next segment, in flight
+  auto seg_load = [&](int s) {
+    const int c = min(SEGX * s + (tid >> 2), nxs - 1);
+    const float* xr = a.e.xf + (int64_t)(xbase + c) * XCHUNK + 4 * (tid & 3);
+    sx_lo = *(const float4*)xr;
+    sx_hi = *(const float4*)(xr + 16);
+  };
+  auto seg_put = [&](int s) {
+    uint32_t* ldw = (uint32_t*)lds;
+    const int c = SEGX * s + (tid >> 2);
+    const float v[8] = {sx_lo.x, sx_lo.y, sx_lo.z, sx_lo.w, sx_hi.x, sx_hi.y, sx_hi.z, sx_hi.w};
+    digitize_group_to(
+        v, tid & 3, digit_kind(QT), [&](int i, uint32_t w) { ldw[(((i >> 2)) * nxp + c) * 4 + (i & 3)] = w; },
+        c < nxs);
+  };
+  if (SEG) seg_load(0);  // requested ahead of the first weights: its wait does not include them
+
   // 1. request the first chunks of this wave's rows before staging the activation
   if (ng > 0) {
     set_rows(row0_of(0));
@@ -257,7 +297,10 @@ __global__ __launch_bounds__(LB, (R == 4 && P == 2 ? 4 : 1)) void k_gemv(GemvArg
   // 2. stage this split's activation digits (coalesced 16-B reads, chunk-transposed LDS) and the
   //    RMSNorm partial sums.  Each thread issues a batch of loads before its first LDS write (a
   //    load-then-write loop serialized one L2 round trip per 8 KiB of the workgroup's slice).
-  if (XIN) {
+  if (SEG) {
+    seg_put(0);
+    if (nseg > 1) seg_load(1);
+  } else if (XIN) {
     // four threads per 32-element chunk digitize it into the same LDS layout
     constexpr int XU = 4;  // chunks in flight per thread
     uint32_t* ldw = (uint32_t*)lds;
@@ -359,12 +402,35 @@ __global__ __launch_bounds__(LB, (R == 4 && P == 2 ? 4 : 1)) void k_gemv(GemvArg
     }
   };
   const int total = ng * nit;
+  // One column: the epilogue's operands (the residual, the RoPE pair, the next RMSNorm gain of the
+  // workgroup's output chunks) are requested at the start of the last loop trip, behind the last
+  // weights in the in-order return queue, instead of after the loop.
+  constexpr bool PRE = NCM == 1 && P > 0 && (EPI == EPI_RESID || EPI == EPI_QKV);
+  const int ep_row = row0_of(lane / R) + lane % R;  // the row this lane finishes (lane < ng * R)
+  const bool ep_live = lane < ng * R && ep_row < rows;
+  const int nout_d = EPI == EPI_RESID ? min(wg_rows, rows - wg_row0) : 0;  // digitized outputs
+  float pre_h = 0.f;
+  float2 pre_cs = make_float2(0.f, 0.f);
+  float4 pre_g0 = make_float4(1.f, 1.f, 1.f, 1.f), pre_g1 = pre_g0;
+  const bool pre_gain = PRE && EPI == EPI_RESID && digitize && a.e.dig_gain != nullptr && nout_d <= 8 * (int)blockDim.x;
+  auto prefetch_epi = [&]() {
+    if (ep_live) {
+      if (EPI == EPI_RESID) pre_h = a.e.y[ep_row];
+      if (EPI == EPI_QKV && ep_row < a.e.nq_rows + a.e.nkv_rows) pre_cs = rope_pair(a.e, 0, ep_row);
+    }
+    if (pre_gain && tid < nout_d / 8) {  // thread 4 j + m: chunk j, elements 4m.. and 16 + 4m..
+      const float* gp = a.e.dig_gain + wg_row0 + (tid >> 2) * XCHUNK + 4 * (tid & 3);
+      pre_g0 = *(const float4*)gp;
+      pre_g1 = *(const float4*)(gp + 16);
+    }
+  };
   // Single-exit loops with scheduling barriers between the fetch and compute phases: a break in the
   // middle of the body let the compiler build an exec-masked exit whose fall-through edge carried
   // unconsumed loads into the loop header (which then waited for every load), and without the
   // barriers the scheduler sank the next fetch into the current compute.
   int t = 0;
   for (; t + NB <= total; t += NB) {
+    if (PRE && t + 2 * NB > total) prefetch_epi();  // the last trip (workgroup-uniform)
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
       fetch_next(buf[(k + PD) % NB]);
@@ -372,7 +438,18 @@ __global__ __launch_bounds__(LB, (R == 4 && P == 2 ? 4 : 1)) void k_gemv(GemvArg
       compute_next(buf[k]);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if (SEG) {
+      // iteration t + NB (even: IPS is 2 or 4) is the first of segment (t + NB) / IPS: digitize it
+      // from the values requested one segment ago and request the next (workgroup-uniform branch)
+      const int it = t + NB;
+      if (it % IPS == 0 && it / IPS < nseg) {
+        seg_put(it / IPS);
+        if (it / IPS + 1 < nseg) seg_load(it / IPS + 1);
+        __syncthreads();
+      }
+    }
   }
+  if (PRE && total < NB) prefetch_epi();
   // the last total - t < NB iterations are already in flight, in buf[0 ..)
 #pragma unroll
   for (int k = 0; k < PD; ++k)
@@ -382,9 +459,9 @@ __global__ __launch_bounds__(LB, (R == 4 && P == 2 ? 4 : 1)) void k_gemv(GemvArg
   //    is lane j^1 of the same group)
   float resp[NCM];
 #pragma unroll
-  for (int n = 0; n < NCM; ++n) resp[n] = __shfl_xor(res[n], 1);
+  for (int n = 0; n < NCM; ++n) resp[n] = __uint_as_float(quad_swap<0xB1>(__float_as_uint(res[n])));
   if (lane < ng * R) {
-    const int row = row0_of(lane / R) + lane % R;
+    const int row = ep_row;
     if (row < rows) {
 #pragma unroll
       for (int n = 0; n < NCM; ++n) {
@@ -398,7 +475,16 @@ __global__ __launch_bounds__(LB, (R == 4 && P == 2 ? 4 : 1)) void k_gemv(GemvArg
             v *= rs;
             vp *= rs;
           }
-          const float out = run_epilogue(EPI, a.e, n, row, v, vp);
+          float out;
+          if (PRE && EPI == EPI_RESID) {
+            out = pre_h + v;
+            a.e.y[row] = out;
+          } else if (PRE && EPI == EPI_QKV) {
+            qkv_store(a.e, 0, row, v, vp, pre_cs);
+            out = 0.f;
+          } else {
+            out = run_epilogue(EPI, a.e, n, row, v, vp);
+          }
           if (digitize) {
             if (EPI == EPI_RESID) osh[n][row - wg_row0] = out;
             else if ((row & 1) == 0) osh[n][(row - wg_row0) >> 1] = out;
@@ -414,7 +500,7 @@ __global__ __launch_bounds__(LB, (R == 4 && P == 2 ? 4 : 1)) void k_gemv(GemvArg
     const int nrow = min(wg_rows, rows - wg_row0);  // whole chunks: the host checks rows
     const int nout = EPI == EPI_RESID ? nrow : nrow / 2;
     const int out0 = EPI == EPI_RESID ? wg_row0 : wg_row0 / 2;
-    digitize_outputs<64>(a.e, nc, osh, nout, out0);
+    digitize_outputs<64>(a.e, nc, osh, nout, out0, pre_gain, pre_g0, pre_g1);
   }
 }
 
@@ -1421,6 +1507,8 @@ static hipError_t launch_fmt(const GemvArgs& a, const GemvPlan& p, int epi, dim3
         go(dd, k_gemv<QT, 4, 2, EPI_PART, 1, 0, 512, 1>, grid, block, lds, a);
     } else if (p.waves > 8)
       go(dd, k_gemv<QT, 1, 2, EPI_RESID, 1, 1, 1024, 1>, grid, block, lds, a);
+    else if (r == 2 && p.waves == 8)  // segmented staging: 512 threads digitize 128 chunks at a time
+      go(dd, k_gemv<QT, 1, 2, EPI_RESID, 1, 2, 512, 2>, grid, block, lds, a);
     else if (r == 2)
       go(dd, k_gemv<QT, 1, 2, EPI_RESID, 1, 2, 512, 1>, grid, block, lds, a);
     else

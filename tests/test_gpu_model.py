@@ -63,6 +63,23 @@ def test_decode_matches_oracle(qwg, mix):
     m.close()
 
 
+LONG_FFN = [synth.Q4_K, synth.Q6_K, synth.Q8_0]
+
+
+@pytest.mark.parametrize("qt", LONG_FFN, ids=[synth.QTYPE_NAMES[q] for q in LONG_FFN])
+def test_long_ffn_decode_matches_oracle(qwg, qt):
+    """An FFN of 4864 (152 input chunks of the down GEMV): the down GEMV digitizes its fp32 input in
+    two segments, the second ragged, while the weights stream (nibble digits for Q4_K, byte digits
+    for Q6_K and Q8_0, whose 16-weight chunks take four loop iterations per segment)."""
+    wl = synth.tiny(qt, n_layers=2, ffn=4864, wid=240 + qt)
+    m, om, records = run_pair(qwg, wl, 2)
+    for g_next, g_logits, hid, r in records:
+        assert rel_l2(g_logits, r["logits"]) < 2e-3
+        for l in range(wl.n_layers + 1):
+            assert rel_l2(hid[l], r["hidden"][l]) < 2e-3, l
+    m.close()
+
+
 def tiny_q4_k_m(**kw):
     """A small model with the Q4_K_M stand-in's type mix: Q4_K, with W_down of every other layer and
     the head in Q6_K."""
