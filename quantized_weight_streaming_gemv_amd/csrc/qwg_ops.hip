@@ -275,8 +275,10 @@ struct AttnArgs {
 
 constexpr int ATT_T = 64;                // positions per split (one per lane)
 constexpr int KROW = HEAD_DIM + 8;       // halves per K row in LDS: the 16-B pad keeps row reads conflict-free
-constexpr int ATT_WAVES = 4;             // waves per workgroup (8 read the K/V tiles twice as often and ran slower)
-constexpr int ATT_THREADS = 64 * ATT_WAVES;
+// waves per workgroup: eight for decode and verify (one query row each at G = 8: the per-wave chain of
+// LDS reads and FMAs halves), four for wide passes (measured 145 against 152 us per layer on 64
+// columns of 2048 positions)
+constexpr int ATT_WAVES = 8, ATT_WAVES_WIDE = 4;
 
 AttnPlan plan_attn(int n_pos, int n_q, int n_kv, int nc) {
   AttnPlan p{};
@@ -299,14 +301,17 @@ constexpr int ATT_WIDE_CPW = 2;
 // One workgroup per (kv head g, split s of ATT_T positions, block of CPW columns) for the G = n_q / n_kv
 // query rows of the group in each of those columns (GQA: query heads g*G .. g*G+G-1 share K/V head g).
 // A decode or verify pass takes one column per workgroup (CPW = 1), so a verify's rows spread over
-// more CUs; a wide prefill pass takes two (CPW = 2), so each staged K/V tile serves 2 G rows:
+// more CUs; a wide prefill pass takes two (CPW = 2), so each staged K/V tile serves 2 G rows.  Of the
+// AW waves, wave w owns query rows w, w + AW, ... (HOIST: the lane's K row is converted to fp32 once
+// for all of them, which takes 128 more registers):
 //   1. the K and V tiles and the queries are staged in LDS (every global load issued up front);
-//   2. wave w scores query rows w, w+ATT_WAVES, ... against its lane's position (scale 1/sqrt(128)), with
-//      causal masking per column, and keeps the split's max m, sum l and exp(score - m);
+//   2. lane t scores position t0 + t against each of the wave's rows (scale 1/sqrt(128)), with causal
+//      masking per column, and keeps the split's max m, sum l and exp(score - m);
 //   3. the unnormalised output sum_t exp(.) v_t goes to the workspace with m and l;
-// k_attn_merge then combines the splits.
-template <int CPW>
-__global__ __launch_bounds__(ATT_THREADS) void k_attn(AttnArgs a) {
+// k_attn_merge then combines the splits.  Per row, the sums run in the same order in every form.
+template <int CPW, int AW, bool HOIST>
+__global__ __launch_bounds__(64 * AW) void k_attn(AttnArgs a) {
+  constexpr int ATT_THREADS = 64 * AW;
   extern __shared__ float sm[];
   const int g = blockIdx.x, s = blockIdx.y, n0 = blockIdx.z * CPW;
   const int G = a.n_q / a.n_kv, NQ = a.nc * G;
@@ -347,48 +352,76 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attn(AttnArgs a) {
   }
   __syncthreads();
 
-  // 2. scores and split-local softmax statistics
-  {
-    uint32_t kr[HEAD_DIM / 2];
+  // 2. scores and split-local softmax statistics (four accumulators per row: dimensions 4i + c, in
+  //    the same order in both forms)
+  const float scale = 0.08838834764831845f;  // 1/sqrt(128)
+  auto finish_row = [&](int j, float a0, float a1, float a2, float a3) {
+    const int n = n0 + j / G;
+    const int qi = n * G + j % G;
+    const bool ok = lane < tn && t0 + lane < a.n_pos + n;
+    const float sc = ok ? ((a0 + a1) + (a2 + a3)) * scale : -INFINITY;
+    const float m = wave_max(sc);
+    const float e = ok ? __expf(sc - m) : 0.f;
+    const float l = wave_sum(e);
+    ps[j * ATT_T + lane] = e;
+    if (lane == 0) {
+      float* pr = a.part + (((int64_t)g * a.nsplit + s) * NQ + qi) * (HEAD_DIM + 2);
+      pr[0] = m;
+      pr[1] = l;
+    }
+  };
+  if (!HOIST) {
+    // (one row per wave at G = 8) each 8-dimension piece of the lane's K row is read from LDS per
+    // row and converted inside the FMAs
+    for (int j = wave; j < R; j += AW) {
+      const float4* qv = (const float4*)(qs + j * HEAD_DIM);
+      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+      for (int i = 0; i < HEAD_DIM / 8; ++i) {
+        const uint4 kp = *(const uint4*)(ks + lane * KROW + i * 8);
+        const uint32_t kw[4] = {kp.x, kp.y, kp.z, kp.w};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float4 qq = qv[2 * i + h];
+          a0 += qq.x * half_bits_to_float(kw[2 * h] & 0xFFFFu);
+          a1 += qq.y * half_bits_to_float(kw[2 * h] >> 16);
+          a2 += qq.z * half_bits_to_float(kw[2 * h + 1] & 0xFFFFu);
+          a3 += qq.w * half_bits_to_float(kw[2 * h + 1] >> 16);
+        }
+      }
+      finish_row(j, a0, a1, a2, a3);
+    }
+  } else {
+    // (several rows per wave) the lane's K row is converted to fp32 once, then scored against each
+    float kf[HEAD_DIM];
 #pragma unroll
     for (int i = 0; i < HEAD_DIM / 8; ++i) {
-      const uint4 v = *(const uint4*)(ks + lane * KROW + i * 8);
-      kr[4 * i] = v.x;
-      kr[4 * i + 1] = v.y;
-      kr[4 * i + 2] = v.z;
-      kr[4 * i + 3] = v.w;
+      const uint4 kp = *(const uint4*)(ks + lane * KROW + i * 8);
+      const uint32_t kw[4] = {kp.x, kp.y, kp.z, kp.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        kf[8 * i + 2 * c] = half_bits_to_float(kw[c] & 0xFFFFu);
+        kf[8 * i + 2 * c + 1] = half_bits_to_float(kw[c] >> 16);
+      }
     }
-    const float scale = 0.08838834764831845f;  // 1/sqrt(128)
-    for (int j = wave; j < R; j += ATT_WAVES) {
-      const int n = n0 + j / G;
-      const int qi = n * G + j % G;
+    for (int j = wave; j < R; j += AW) {
       const float4* qv = (const float4*)(qs + j * HEAD_DIM);
       float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll
       for (int i = 0; i < HEAD_DIM / 4; ++i) {
         const float4 qq = qv[i];
-        a0 += qq.x * half_bits_to_float(kr[2 * i] & 0xFFFFu);
-        a1 += qq.y * half_bits_to_float(kr[2 * i] >> 16);
-        a2 += qq.z * half_bits_to_float(kr[2 * i + 1] & 0xFFFFu);
-        a3 += qq.w * half_bits_to_float(kr[2 * i + 1] >> 16);
+        a0 += qq.x * kf[4 * i];
+        a1 += qq.y * kf[4 * i + 1];
+        a2 += qq.z * kf[4 * i + 2];
+        a3 += qq.w * kf[4 * i + 3];
       }
-      const bool ok = lane < tn && t0 + lane < a.n_pos + n;
-      const float sc = ok ? ((a0 + a1) + (a2 + a3)) * scale : -INFINITY;
-      const float m = wave_max(sc);
-      const float e = ok ? __expf(sc - m) : 0.f;
-      const float l = wave_sum(e);
-      ps[j * ATT_T + lane] = e;
-      if (lane == 0) {
-        float* pr = a.part + (((int64_t)g * a.nsplit + s) * NQ + qi) * (HEAD_DIM + 2);
-        pr[0] = m;
-        pr[1] = l;
-      }
+      finish_row(j, a0, a1, a2, a3);
     }
   }
   __syncthreads();
 
-  // 3. unnormalised output: wave w takes query rows w, w+ATT_WAVES, ...; lane = dimensions 2c, 2c+1
-  for (int j = wave; j < R; j += ATT_WAVES) {
+  // 3. unnormalised output: wave w takes query rows w, w + AW, ...; lane = dimensions 2 lane, 2 lane + 1
+  for (int j = wave; j < R; j += AW) {
     const int qb = (n0 + j / G) * G + j % G;
     const float* pr = ps + j * ATT_T;
     float o0 = 0.f, o1 = 0.f;
@@ -510,17 +543,17 @@ hipError_t launch_attn(const float* q, int64_t q_stride, const uint16_t* kc, con
   a.dig = dig_out;
   a.dig_stride = dig_stride;
   a.dig_kind = dig_kind;
-  if (nc > MAX_COLS && attn_lds_bytes(ATT_WIDE_CPW * (n_q / n_kv)) <= 150 * 1024) {
-    // wide prefill pass: ATT_WIDE_CPW columns share each staged K/V tile
-    const size_t lds = attn_lds_bytes(ATT_WIDE_CPW * (n_q / n_kv));
-    if (lds > 150 * 1024) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_attn<ATT_WIDE_CPW>, dim3(n_kv, p.nsplit, (nc + ATT_WIDE_CPW - 1) / ATT_WIDE_CPW),
-                       dim3(ATT_THREADS), lds, st, a);
-  } else {
-    const size_t lds = attn_lds_bytes(n_q / n_kv);
-    if (lds > 150 * 1024) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_attn<1>, dim3(n_kv, p.nsplit, nc), dim3(ATT_THREADS), lds, st, a);
-  }
+  const int G = n_q / n_kv;
+  // (wide passes: ATT_WIDE_CPW columns share each staged K/V tile)
+  const bool wide = nc > MAX_COLS && attn_lds_bytes(ATT_WIDE_CPW * G) <= 150 * 1024;
+  const int cpw = wide ? ATT_WIDE_CPW : 1, aw = wide ? ATT_WAVES_WIDE : ATT_WAVES;
+  const size_t lds = attn_lds_bytes(cpw * G);
+  if (lds > 150 * 1024) return hipErrorInvalidValue;
+  const dim3 grid(n_kv, p.nsplit, (nc + cpw - 1) / cpw), block(64 * aw);
+  if (wide)
+    hipLaunchKernelGGL((k_attn<ATT_WIDE_CPW, ATT_WAVES_WIDE, true>), grid, block, lds, st, a);
+  else
+    hipLaunchKernelGGL((k_attn<1, ATT_WAVES, false>), grid, block, lds, st, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_attn_merge, dim3(n_kv, NQ), dim3(64 * MW), 0, st, a);
