@@ -36,14 +36,14 @@ HBM_PEAK_GBPS = 8000.0
 # taken again.
 GEMV_TRAFFIC = {
     "workload": "llama70b-q4_k-resident",
-    "sources_sha256": "c8a29085f592f8996f51eabe6a88a05e15cf539a462596e332d848d78d468375",
+    "sources_sha256": "309aa6c3e1e10da03128f29930fbe3ac70a408a8690bb79c5494d6e220a7adf3",
     "fetch_scale": 1.99975, "write_scale": 1.00000,
     "classes": {  # label -> (fetch KiB, write KiB) per launch
-        "qkv": (23942.0, 44.8),
-        "wo": (18848.5, 80.0),
-        "gate_up": (132501.0, 112.1),
-        "down": (65320.1, 80.0),
-        "head": (290400.3, 538.2),
+        "qkv": (23920.2, 44.8),
+        "wo": (19194.1, 80.0),
+        "gate_up": (132515.8, 112.1),
+        "down": (65739.8, 80.0),
+        "head": (290335.6, 539.5),
     },
 }
 GEMV_SOURCES = ("qwg_gemv.hip", "qwg_formats.h", "qwg_kernels.h")

@@ -402,22 +402,19 @@ __global__ __launch_bounds__(LB, (R == 4 && P == 2 ? 4 : 1)) void k_gemv(GemvArg
     }
   };
   const int total = ng * nit;
-  // One column: the epilogue's operands (the residual, the RoPE pair, the next RMSNorm gain of the
+  // One column, residual epilogue: its operands (the residual and the next RMSNorm gain of the
   // workgroup's output chunks) are requested at the start of the last loop trip, behind the last
-  // weights in the in-order return queue, instead of after the loop.
-  constexpr bool PRE = NCM == 1 && P > 0 && (EPI == EPI_RESID || EPI == EPI_QKV);
+  // weights in the in-order return queue, instead of after the loop.  (Requesting the QKV epilogue's
+  // RoPE pairs the same way measured 0.2 us slower.)
+  constexpr bool PRE = NCM == 1 && P > 0 && EPI == EPI_RESID;
   const int ep_row = row0_of(lane / R) + lane % R;  // the row this lane finishes (lane < ng * R)
   const bool ep_live = lane < ng * R && ep_row < rows;
   const int nout_d = EPI == EPI_RESID ? min(wg_rows, rows - wg_row0) : 0;  // digitized outputs
   float pre_h = 0.f;
-  float2 pre_cs = make_float2(0.f, 0.f);
   float4 pre_g0 = make_float4(1.f, 1.f, 1.f, 1.f), pre_g1 = pre_g0;
-  const bool pre_gain = PRE && EPI == EPI_RESID && digitize && a.e.dig_gain != nullptr && nout_d <= 8 * (int)blockDim.x;
+  const bool pre_gain = PRE && digitize && a.e.dig_gain != nullptr && nout_d <= 8 * (int)blockDim.x;
   auto prefetch_epi = [&]() {
-    if (ep_live) {
-      if (EPI == EPI_RESID) pre_h = a.e.y[ep_row];
-      if (EPI == EPI_QKV && ep_row < a.e.nq_rows + a.e.nkv_rows) pre_cs = rope_pair(a.e, 0, ep_row);
-    }
+    if (ep_live) pre_h = a.e.y[ep_row];
     if (pre_gain && tid < nout_d / 8) {  // thread 4 j + m: chunk j, elements 4m.. and 16 + 4m..
       const float* gp = a.e.dig_gain + wg_row0 + (tid >> 2) * XCHUNK + 4 * (tid & 3);
       pre_g0 = *(const float4*)gp;
@@ -476,12 +473,9 @@ __global__ __launch_bounds__(LB, (R == 4 && P == 2 ? 4 : 1)) void k_gemv(GemvArg
             vp *= rs;
           }
           float out;
-          if (PRE && EPI == EPI_RESID) {
+          if (PRE) {
             out = pre_h + v;
             a.e.y[row] = out;
-          } else if (PRE && EPI == EPI_QKV) {
-            qkv_store(a.e, 0, row, v, vp, pre_cs);
-            out = 0.f;
           } else {
             out = run_epilogue(EPI, a.e, n, row, v, vp);
           }
