@@ -420,14 +420,27 @@ __global__ __launch_bounds__(64 * AW) void k_attn(AttnArgs a) {
   }
   __syncthreads();
 
-  // 3. unnormalised output: wave w takes query rows w, w + AW, ...; lane = dimensions 2 lane, 2 lane + 1
+  // 3. unnormalised output: wave w takes query rows w, w + AW, ...; lane = dimensions 2 lane, 2 lane + 1.
+  //    The weights of four positions come in one broadcast read.
   for (int j = wave; j < R; j += AW) {
     const int qb = (n0 + j / G) * G + j % G;
     const float* pr = ps + j * ATT_T;
+    const uint32_t* vw = (const uint32_t*)vs + lane;  // dimension pair of the lane, row stride HEAD_DIM / 2
     float o0 = 0.f, o1 = 0.f;
-#pragma unroll 8
-    for (int t = 0; t < tn; ++t) {
-      const uint32_t vv = ((const uint32_t*)(vs + t * HEAD_DIM))[lane];
+    int t = 0;
+#pragma unroll 2
+    for (; t + 4 <= tn; t += 4) {
+      const float4 p4 = *(const float4*)(pr + t);
+      const float pp[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t vv = vw[(t + u) * (HEAD_DIM / 2)];
+        o0 += pp[u] * half_bits_to_float(vv & 0xFFFFu);
+        o1 += pp[u] * half_bits_to_float(vv >> 16);
+      }
+    }
+    for (; t < tn; ++t) {
+      const uint32_t vv = vw[t * (HEAD_DIM / 2)];
       const float p = pr[t];
       o0 += p * half_bits_to_float(vv & 0xFFFFu);
       o1 += p * half_bits_to_float(vv >> 16);
