@@ -275,10 +275,10 @@ struct AttnArgs {
 
 constexpr int ATT_T = 64;                // positions per split (one per lane)
 constexpr int KROW = HEAD_DIM + 8;       // halves per K row in LDS: the 16-B pad keeps row reads conflict-free
-// waves per workgroup: eight for decode and verify (one query row each at G = 8: the per-wave chain of
-// LDS reads and FMAs halves), four for wide passes (measured 145 against 152 us per layer on 64
-// columns of 2048 positions)
-constexpr int ATT_WAVES = 8, ATT_WAVES_WIDE = 4;
+// waves per workgroup of k_attn: one query row each at G = 8 (four waves of two rows each kept a
+// 128-register converted K row per wave and measured 8.0 against 7.3 us per decode layer)
+constexpr int ATT_WAVES = 8;
+constexpr int ATT_THREADS = 64 * ATT_WAVES;
 
 AttnPlan plan_attn(int n_pos, int n_q, int n_kv, int nc) {
   AttnPlan p{};
@@ -290,37 +290,29 @@ AttnPlan plan_attn(int n_pos, int n_q, int n_kv, int nc) {
   return p;
 }
 
-// query rows of one attention workgroup (G per column, CPW columns): q, scores, the K and V tiles
+// LDS of a k_attn workgroup for G query rows: q, scores, the K and V tiles
 static size_t attn_lds_bytes(int rows) {
   return (size_t)rows * HEAD_DIM * 4 + (size_t)rows * ATT_T * 4 + (size_t)ATT_T * KROW * 2 + (size_t)ATT_T * HEAD_DIM * 2;
 }
-// columns per workgroup of a pass wider than MAX_COLS: 2 beat 1 by ~13% on 64 columns of 2048
-// positions; 4 and 8 ran slower (their LDS leaves fewer waves per CU)
-constexpr int ATT_WIDE_CPW = 2;
-
-// One workgroup per (kv head g, split s of ATT_T positions, block of CPW columns) for the G = n_q / n_kv
-// query rows of the group in each of those columns (GQA: query heads g*G .. g*G+G-1 share K/V head g).
-// A decode or verify pass takes one column per workgroup (CPW = 1), so a verify's rows spread over
-// more CUs; a wide prefill pass takes two (CPW = 2), so each staged K/V tile serves 2 G rows.  Of the
-// AW waves, wave w owns query rows w, w + AW, ... (HOIST: the lane's K row is converted to fp32 once
-// for all of them, which takes 128 more registers):
+// Decode and verify passes (up to MAX_COLS columns): one workgroup per (kv head g, split s of ATT_T
+// positions, column n0) for the G = n_q / n_kv query rows of the group (GQA: query heads g*G ..
+// g*G+G-1 share K/V head g), so a verify's rows spread over more CUs.  Wave w owns query rows w,
+// w + ATT_WAVES, ...:
 //   1. the K and V tiles and the queries are staged in LDS (every global load issued up front);
-//   2. lane t scores position t0 + t against each of the wave's rows (scale 1/sqrt(128)), with causal
-//      masking per column, and keeps the split's max m, sum l and exp(score - m);
+//   2. lane t scores position t0 + t against each of the wave's rows (scale 1/sqrt(128)), reading its
+//      K row from LDS in 8-dimension pieces converted inside the FMAs, with causal masking, and keeps
+//      the split's max m, sum l and exp(score - m);
 //   3. the unnormalised output sum_t exp(.) v_t goes to the workspace with m and l;
-// k_attn_merge then combines the splits.  Per row, the sums run in the same order in every form.
-template <int CPW, int AW, bool HOIST>
-__global__ __launch_bounds__(64 * AW) void k_attn(AttnArgs a) {
-  constexpr int ATT_THREADS = 64 * AW;
+// k_attn_merge then combines the splits.
+__global__ __launch_bounds__(ATT_THREADS) void k_attn(AttnArgs a) {
   extern __shared__ float sm[];
-  const int g = blockIdx.x, s = blockIdx.y, n0 = blockIdx.z * CPW;
+  const int g = blockIdx.x, s = blockIdx.y, n0 = blockIdx.z;
   const int G = a.n_q / a.n_kv, NQ = a.nc * G;
-  const int ncw = min(CPW, a.nc - n0);  // columns of this workgroup
-  const int R = ncw * G;                 // its query rows: column n0 + j / G, head g*G + j % G
+  const int R = G;  // query rows: head g*G + j of column n0
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float* qs = sm;                                // [CPW * G][HEAD_DIM]
-  float* ps = qs + CPW * G * HEAD_DIM;           // [CPW * G][ATT_T]
-  uint16_t* ks = (uint16_t*)(ps + CPW * G * ATT_T);  // [ATT_T][KROW]
+  float* qs = sm;                                // [G][HEAD_DIM]
+  float* ps = qs + G * HEAD_DIM;                 // [G][ATT_T]
+  uint16_t* ks = (uint16_t*)(ps + G * ATT_T);    // [ATT_T][KROW]
   uint16_t* vs = ks + ATT_T * KROW;              // [ATT_T][HEAD_DIM]
   const int t0 = s * ATT_T;
   const int span = a.n_pos + a.nc - 1;
@@ -340,8 +332,7 @@ __global__ __launch_bounds__(64 * AW) void k_attn(AttnArgs a) {
     }
     for (int i = tid; i < R * (HEAD_DIM / 4); i += ATT_THREADS) {
       const int j = i / (HEAD_DIM / 4), d4 = i % (HEAD_DIM / 4);
-      const int n = n0 + j / G, h = g * G + j % G;
-      ((float4*)qs)[i] = ((const float4*)(a.q + (int64_t)n * a.q_stride + (int64_t)h * HEAD_DIM))[d4];
+      ((float4*)qs)[i] = ((const float4*)(a.q + (int64_t)n0 * a.q_stride + (int64_t)(g * G + j) * HEAD_DIM))[d4];
     }
 #pragma unroll
     for (int j = 0; j < TP; ++j) {
@@ -352,13 +343,26 @@ __global__ __launch_bounds__(64 * AW) void k_attn(AttnArgs a) {
   }
   __syncthreads();
 
-  // 2. scores and split-local softmax statistics (four accumulators per row: dimensions 4i + c, in
-  //    the same order in both forms)
+  // 2. scores and split-local softmax statistics (four accumulators per row: dimensions 4i + c)
   const float scale = 0.08838834764831845f;  // 1/sqrt(128)
-  auto finish_row = [&](int j, float a0, float a1, float a2, float a3) {
-    const int n = n0 + j / G;
-    const int qi = n * G + j % G;
-    const bool ok = lane < tn && t0 + lane < a.n_pos + n;
+  for (int j = wave; j < R; j += ATT_WAVES) {
+    const float4* qv = (const float4*)(qs + j * HEAD_DIM);
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+    for (int i = 0; i < HEAD_DIM / 8; ++i) {
+      const uint4 kp = *(const uint4*)(ks + lane * KROW + i * 8);
+      const uint32_t kw[4] = {kp.x, kp.y, kp.z, kp.w};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float4 qq = qv[2 * i + h];
+        a0 += qq.x * half_bits_to_float(kw[2 * h] & 0xFFFFu);
+        a1 += qq.y * half_bits_to_float(kw[2 * h] >> 16);
+        a2 += qq.z * half_bits_to_float(kw[2 * h + 1] & 0xFFFFu);
+        a3 += qq.w * half_bits_to_float(kw[2 * h + 1] >> 16);
+      }
+    }
+    const int qi = n0 * G + j;
+    const bool ok = lane < tn && t0 + lane < a.n_pos + n0;
     const float sc = ok ? ((a0 + a1) + (a2 + a3)) * scale : -INFINITY;
     const float m = wave_max(sc);
     const float e = ok ? __expf(sc - m) : 0.f;
@@ -369,61 +373,13 @@ __global__ __launch_bounds__(64 * AW) void k_attn(AttnArgs a) {
       pr[0] = m;
       pr[1] = l;
     }
-  };
-  if (!HOIST) {
-    // (one row per wave at G = 8) each 8-dimension piece of the lane's K row is read from LDS per
-    // row and converted inside the FMAs
-    for (int j = wave; j < R; j += AW) {
-      const float4* qv = (const float4*)(qs + j * HEAD_DIM);
-      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-#pragma unroll
-      for (int i = 0; i < HEAD_DIM / 8; ++i) {
-        const uint4 kp = *(const uint4*)(ks + lane * KROW + i * 8);
-        const uint32_t kw[4] = {kp.x, kp.y, kp.z, kp.w};
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const float4 qq = qv[2 * i + h];
-          a0 += qq.x * half_bits_to_float(kw[2 * h] & 0xFFFFu);
-          a1 += qq.y * half_bits_to_float(kw[2 * h] >> 16);
-          a2 += qq.z * half_bits_to_float(kw[2 * h + 1] & 0xFFFFu);
-          a3 += qq.w * half_bits_to_float(kw[2 * h + 1] >> 16);
-        }
-      }
-      finish_row(j, a0, a1, a2, a3);
-    }
-  } else {
-    // (several rows per wave) the lane's K row is converted to fp32 once, then scored against each
-    float kf[HEAD_DIM];
-#pragma unroll
-    for (int i = 0; i < HEAD_DIM / 8; ++i) {
-      const uint4 kp = *(const uint4*)(ks + lane * KROW + i * 8);
-      const uint32_t kw[4] = {kp.x, kp.y, kp.z, kp.w};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        kf[8 * i + 2 * c] = half_bits_to_float(kw[c] & 0xFFFFu);
-        kf[8 * i + 2 * c + 1] = half_bits_to_float(kw[c] >> 16);
-      }
-    }
-    for (int j = wave; j < R; j += AW) {
-      const float4* qv = (const float4*)(qs + j * HEAD_DIM);
-      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-#pragma unroll
-      for (int i = 0; i < HEAD_DIM / 4; ++i) {
-        const float4 qq = qv[i];
-        a0 += qq.x * kf[4 * i];
-        a1 += qq.y * kf[4 * i + 1];
-        a2 += qq.z * kf[4 * i + 2];
-        a3 += qq.w * kf[4 * i + 3];
-      }
-      finish_row(j, a0, a1, a2, a3);
-    }
   }
   __syncthreads();
 
-  // 3. unnormalised output: wave w takes query rows w, w + AW, ...; lane = dimensions 2 lane, 2 lane + 1.
-  //    The weights of four positions come in one broadcast read.
-  for (int j = wave; j < R; j += AW) {
-    const int qb = (n0 + j / G) * G + j % G;
+  // 3. unnormalised output: wave w takes query rows w, w + ATT_WAVES, ...; lane = dimensions 2 lane,
+  //    2 lane + 1.  The weights of four positions come in one broadcast read.
+  for (int j = wave; j < R; j += ATT_WAVES) {
+    const int qb = n0 * G + j;
     const float* pr = ps + j * ATT_T;
     const uint32_t* vw = (const uint32_t*)vs + lane;  // dimension pair of the lane, row stride HEAD_DIM / 2
     float o0 = 0.f, o1 = 0.f;
@@ -447,6 +403,165 @@ __global__ __launch_bounds__(64 * AW) void k_attn(AttnArgs a) {
     }
     float* dst = a.part + (((int64_t)g * a.nsplit + s) * NQ + qb) * (HEAD_DIM + 2) + 2;
     *(float2*)(dst + 2 * lane) = make_float2(o0, o1);
+  }
+}
+
+// Wide passes (prompt prefill) on the matrix cores: one workgroup per (kv head g, split s of ATT_T
+// positions, block of cpw columns) holds up to 64 query rows (cpw = 64 / G columns), 16 per wave, and
+// computes them with v_mfma_f32_16x16x4_f32 (fp32 operands, fp32 accumulation; K converted exactly
+// from fp16):
+//   1. the K tile and the V tile (its dimensions regrouped so that dimensions n, n + 16, ..., n + 112
+//      are adjacent) are staged in LDS; each lane loads 32 dimensions of its query row;
+//   2. S^T = K Q^T per 16-position tile: lane 16 kk + i takes K row i and query row i, dimensions
+//      32 kk .. 32 kk + 31 (the contraction runs over the dimensions in that order), and receives
+//      S[position 4 kk + v][row i], v = 0..3, for each of the 4 tiles;
+//   3. per row: split max m, exp(s - m) and sum l (across the four lanes 16 kk + i) with causal masking;
+//   4. O = P V: the P values the lane holds are exactly the A operand of a 16x16x4 product whose
+//      4-position step is {16 pt + 4 kk + v : kk}, and the regrouped V row gives the B operand of the
+//      8 dimension tiles in one 16-byte read;
+//   5. the unnormalised output, m and l go to the workspace for k_attn_merge, as in k_attn.
+constexpr int AM_WAVES = 4;
+typedef float qwg_f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ qwg_f32x4 mfma_f32_4(float a, float b, qwg_f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+static size_t attn_mfma_lds_bytes() { return (size_t)ATT_T * KROW * 2 + (size_t)ATT_T * HEAD_DIM * 2; }
+
+__global__ __launch_bounds__(64 * AM_WAVES) void k_attn_mfma(AttnArgs a, int cpw) {
+  extern __shared__ float sm[];
+  uint16_t* ks = (uint16_t*)sm;      // [ATT_T][KROW]
+  uint16_t* vs = ks + ATT_T * KROW;  // [ATT_T][HEAD_DIM]: dimension 16 dt + n at n * 8 + dt
+  const int g = blockIdx.x, s = blockIdx.y, n0 = blockIdx.z * cpw;
+  const int G = a.n_q / a.n_kv, NQ = a.nc * G;
+  const int R = min(cpw, a.nc - n0) * G;  // rows of this workgroup: column n0 + j / G, head g*G + j % G
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i = lane & 15, kk = lane >> 4;
+  const int t0 = s * ATT_T;
+  const int tn = min(ATT_T, a.n_pos + a.nc - 1 - t0);
+
+  // 1. tiles (every global load issued before the first LDS store) and this lane's query dimensions
+  constexpr int TP = ATT_T * 16 / (64 * AM_WAVES);
+  uint4 kv[TP], vv[TP];
+#pragma unroll
+  for (int j = 0; j < TP; ++j) {
+    const int idx = tid + 64 * AM_WAVES * j, t = idx >> 4, c = idx & 15;
+    const int64_t off = (int64_t)(t0 + min(t, tn - 1)) * a.kv_stride + (int64_t)g * HEAD_DIM + c * 8;
+    kv[j] = *(const uint4*)(a.kc + off);
+    vv[j] = *(const uint4*)(a.vc + off);
+  }
+  const int jr = wave * 16 + i;  // the query row of this lane
+  const bool rvalid = jr < R;
+  const int jq = min(jr, R - 1);
+  const int ncol = n0 + jq / G;
+  float qf[32];
+  {
+    const float4* qp = (const float4*)(a.q + (int64_t)ncol * a.q_stride + (int64_t)(g * G + jq % G) * HEAD_DIM + 32 * kk);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float4 v = qp[u];
+      qf[4 * u] = v.x;
+      qf[4 * u + 1] = v.y;
+      qf[4 * u + 2] = v.z;
+      qf[4 * u + 3] = v.w;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < TP; ++j) {
+    const int idx = tid + 64 * AM_WAVES * j, t = idx >> 4, c = idx & 15;
+    *(uint4*)(ks + t * KROW + c * 8) = kv[j];
+    const uint32_t w[4] = {vv[j].x, vv[j].y, vv[j].z, vv[j].w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e)  // dimension 8 c + e = 16 (c >> 1) + 8 (c & 1) + e
+      vs[t * HEAD_DIM + (8 * (c & 1) + e) * 8 + (c >> 1)] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+  }
+  __syncthreads();
+  if (wave * 16 >= R) return;  // no rows (wave-uniform; no barrier follows)
+
+  // 2. scores, two 16-position tiles at a time (independent accumulation chains)
+  qwg_f32x4 sc[4];
+#pragma unroll
+  for (int ph = 0; ph < 2; ++ph) {
+    float kf[2][32];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint16_t* kr = ks + (16 * (2 * ph + h) + i) * KROW + 32 * kk;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 kp = *(const uint4*)(kr + 8 * q);
+        const uint32_t w[4] = {kp.x, kp.y, kp.z, kp.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kf[h][8 * q + 2 * e] = half_bits_to_float(w[e] & 0xFFFFu);
+          kf[h][8 * q + 2 * e + 1] = half_bits_to_float(w[e] >> 16);
+        }
+      }
+    }
+    qwg_f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0;
+#pragma unroll
+    for (int st = 0; st < 32; ++st) {
+      c0 = mfma_f32_4(kf[0][st], qf[st], c0);
+      c1 = mfma_f32_4(kf[1][st], qf[st], c1);
+    }
+    sc[2 * ph] = c0;
+    sc[2 * ph + 1] = c1;
+  }
+
+  // 3. split-local softmax of row i over the positions 16 pt + 4 kk + v
+  const float scale = 0.08838834764831845f;  // 1/sqrt(128)
+  const int lim = a.n_pos + ncol - t0;       // positions below lim (and tn) are visible to the row
+  float p[4][4], m = -INFINITY;
+#pragma unroll
+  for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int pos = 16 * pt + 4 * kk + v;
+      const bool ok = rvalid && pos < tn && pos < lim;
+      p[pt][v] = ok ? sc[pt][v] * scale : -INFINITY;
+      m = fmaxf(m, p[pt][v]);
+    }
+  m = fmaxf(m, __shfl_xor(m, 16));
+  m = fmaxf(m, __shfl_xor(m, 32));
+  float l = 0.f;
+#pragma unroll
+  for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      p[pt][v] = p[pt][v] == -INFINITY ? 0.f : __expf(p[pt][v] - m);
+      l += p[pt][v];
+    }
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+
+  // 4. O = P V over the 16 steps of 4 positions, 8 dimension tiles
+  qwg_f32x4 o[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) o[dt] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const uint4 vp = *(const uint4*)(vs + (16 * pt + 4 * kk + v) * HEAD_DIM + i * 8);
+      const uint32_t w[4] = {vp.x, vp.y, vp.z, vp.w};
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        o[dt] = mfma_f32_4(p[pt][v], half_bits_to_float((w[dt >> 1] >> (16 * (dt & 1))) & 0xFFFFu), o[dt]);
+    }
+
+  // 5. records: lane 16 kk + i holds O[row 4 kk + v][dimension 16 dt + i]
+  float* base = a.part + ((int64_t)g * a.nsplit + s) * NQ * (HEAD_DIM + 2);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int j = wave * 16 + 4 * kk + v;
+    if (j < R) {
+      float* dst = base + (int64_t)((n0 + j / G) * G + j % G) * (HEAD_DIM + 2) + 2;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) dst[16 * dt + i] = o[dt][v];
+    }
+  }
+  if (kk == 0 && rvalid) {
+    float* pr = base + (int64_t)((n0 + jr / G) * G + jr % G) * (HEAD_DIM + 2);
+    pr[0] = m;
+    pr[1] = l;
   }
 }
 
@@ -557,16 +672,16 @@ hipError_t launch_attn(const float* q, int64_t q_stride, const uint16_t* kc, con
   a.dig_stride = dig_stride;
   a.dig_kind = dig_kind;
   const int G = n_q / n_kv;
-  // (wide passes: ATT_WIDE_CPW columns share each staged K/V tile)
-  const bool wide = nc > MAX_COLS && attn_lds_bytes(ATT_WIDE_CPW * G) <= 150 * 1024;
-  const int cpw = wide ? ATT_WIDE_CPW : 1, aw = wide ? ATT_WAVES_WIDE : ATT_WAVES;
-  const size_t lds = attn_lds_bytes(cpw * G);
-  if (lds > 150 * 1024) return hipErrorInvalidValue;
-  const dim3 grid(n_kv, p.nsplit, (nc + cpw - 1) / cpw), block(64 * aw);
-  if (wide)
-    hipLaunchKernelGGL((k_attn<ATT_WIDE_CPW, ATT_WAVES_WIDE, true>), grid, block, lds, st, a);
-  else
-    hipLaunchKernelGGL((k_attn<1, ATT_WAVES, false>), grid, block, lds, st, a);
+  if (nc > MAX_COLS) {
+    // wide passes (prompt prefill): 64 / G columns per workgroup on the matrix cores
+    const int cpw = std::max(1, 64 / G);
+    hipLaunchKernelGGL(k_attn_mfma, dim3(n_kv, p.nsplit, (nc + cpw - 1) / cpw), dim3(64 * AM_WAVES),
+                       attn_mfma_lds_bytes(), st, a, cpw);
+  } else {
+    const size_t lds = attn_lds_bytes(G);
+    if (lds > 150 * 1024) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_attn, dim3(n_kv, p.nsplit, nc), dim3(ATT_THREADS), lds, st, a);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_attn_merge, dim3(n_kv, NQ), dim3(64 * MW), 0, st, a);
