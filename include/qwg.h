@@ -176,9 +176,11 @@ int qwg_rope(float* d_v, int n_heads, int head_dim, const float* d_table, int po
  * scores q.k / sqrt(head_dim), softmax, weighted sum of V.  d_out fp32 [n_cols][n_q][head_dim].
  * d_work: device scratch of qwg_attn_work_bytes(...) bytes, which the call overwrites (calls that share
  * it must not overlap).  d_q, d_kc and d_vc 16-byte aligned, d_out and d_work 8-byte aligned.
- * head_dim must be 128; n_cols <= 64; n_kv <= 64; n_q / n_kv <= 64; n_pos <= 262144.  Up to 8 columns
- * take one workgroup per (kv head, split, column); wider calls (a prompt pass) run on the matrix cores
- * (fp32 products and sums), 64 / (n_q / n_kv) columns (at most 64 query rows) per staged K/V tile.
+ * head_dim must be 128; n_cols <= 64; n_kv <= 64; n_q / n_kv <= 64; n_pos <= 262144.  With fewer than 32
+ * query rows per KV head (n_cols * n_q / n_kv < 32: decode steps, short verify passes) each workgroup
+ * takes one (kv head, split, column); from 32 rows (a prompt pass, a verify pass of 4+ columns at
+ * n_q / n_kv = 8) the call runs on the matrix cores (fp32 products and sums), 64 / (n_q / n_kv)
+ * columns (at most 64 query rows) per workgroup.
  * qwg_attn_work_bytes returns 0 for shapes outside these limits. */
 size_t qwg_attn_work_bytes(int n_pos, int n_q, int n_kv, int head_dim, int n_cols);
 int qwg_attn_decode(const float* d_q, const uint16_t* d_kc, const uint16_t* d_vc, int n_pos, int n_q, int n_kv,

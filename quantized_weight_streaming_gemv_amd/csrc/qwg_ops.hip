@@ -294,10 +294,10 @@ AttnPlan plan_attn(int n_pos, int n_q, int n_kv, int nc) {
 static size_t attn_lds_bytes(int rows) {
   return (size_t)rows * HEAD_DIM * 4 + (size_t)rows * ATT_T * 4 + (size_t)ATT_T * KROW * 2 + (size_t)ATT_T * HEAD_DIM * 2;
 }
-// Decode and verify passes (up to MAX_COLS columns): one workgroup per (kv head g, split s of ATT_T
-// positions, column n0) for the G = n_q / n_kv query rows of the group (GQA: query heads g*G ..
-// g*G+G-1 share K/V head g), so a verify's rows spread over more CUs.  Wave w owns query rows w,
-// w + ATT_WAVES, ...:
+// Decode steps and narrow verify passes (fewer than 32 query rows per KV head): one workgroup per
+// (kv head g, split s of ATT_T positions, column n0) for the G = n_q / n_kv query rows of the group
+// (GQA: query heads g*G .. g*G+G-1 share K/V head g), so a verify's rows spread over more CUs.  Wave
+// w owns query rows w, w + ATT_WAVES, ...:
 //   1. the K and V tiles and the queries are staged in LDS (every global load issued up front);
 //   2. lane t scores position t0 + t against each of the wave's rows (scale 1/sqrt(128)), reading its
 //      K row from LDS in 8-dimension pieces converted inside the FMAs, with causal masking, and keeps
@@ -406,10 +406,10 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attn(AttnArgs a) {
   }
 }
 
-// Wide passes (prompt prefill) on the matrix cores: one workgroup per (kv head g, split s of ATT_T
-// positions, block of cpw columns) holds up to 64 query rows (cpw = 64 / G columns), 16 per wave, and
-// computes them with v_mfma_f32_16x16x4_f32 (fp32 operands, fp32 accumulation; K converted exactly
-// from fp16):
+// Passes of 32 or more query rows per KV head (prompt prefill, verify) on the matrix cores: one
+// workgroup per (kv head g, split s of ATT_T positions, block of cpw columns) holds up to 64 query
+// rows (cpw = 64 / G columns), 16 per wave, and computes them with v_mfma_f32_16x16x4_f32 (fp32
+// operands, fp32 accumulation; K converted exactly from fp16):
 //   1. the K tile and the V tile (its dimensions regrouped so that dimensions n, n + 16, ..., n + 112
 //      are adjacent) are staged in LDS; each lane loads 32 dimensions of its query row;
 //   2. S^T = K Q^T per 16-position tile: lane 16 kk + i takes K row i and query row i, dimensions
@@ -672,8 +672,10 @@ hipError_t launch_attn(const float* q, int64_t q_stride, const uint16_t* kc, con
   a.dig_stride = dig_stride;
   a.dig_kind = dig_kind;
   const int G = n_q / n_kv;
-  if (nc > MAX_COLS) {
-    // wide passes (prompt prefill): 64 / G columns per workgroup on the matrix cores
+  if (nc * G >= 32) {
+    // passes with at least two 16-row blocks of query rows (prompt prefill; a verify pass of 4 or
+    // more columns at G = 8): 64 / G columns per workgroup on the matrix cores.  (A decode step's 8
+    // rows fill half of one block, and one wave's 256 products measured 4% slower per decode step.)
     const int cpw = std::max(1, 64 / G);
     hipLaunchKernelGGL(k_attn_mfma, dim3(n_kv, p.nsplit, (nc + cpw - 1) / cpw), dim3(64 * AM_WAVES),
                        attn_mfma_lds_bytes(), st, a, cpw);

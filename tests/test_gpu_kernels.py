@@ -348,10 +348,11 @@ def test_rope_table_and_kernel(ops):
 def test_attention(ops, nq, nkv, npos, nc):
     # (32, 2, 9000): 141 splits and 16 query rows per KV head; (24, 2, 300, 2): 12 rows per head;
     # (8, 8, 130, 2): one query head per KV head (plain multi-head attention); (2, 1, 262144, 2): the
-    # largest n_pos the library takes, 4097 splits.  Wider than 8 columns (prompt passes), on the
-    # matrix cores: 64 / G columns per workgroup (64 query rows, 16 per wave), with a last block of
-    # 5 columns in (64, 8, 300, 13), one column of 64 rows per workgroup in (64, 1, 90, 64), and G = 12
-    # in (24, 2, 300, 20): 5 columns, 60 rows, the last wave's block partly empty
+    # largest n_pos the library takes, 4097 splits.  From 32 query rows per KV head (n_cols * G >= 32:
+    # (64, 8, 4097, 4), (64, 8, 257, 5) and the prompt-width cases) on the matrix cores: 64 / G columns
+    # per workgroup (64 query rows, 16 per wave), with a last block of 5 columns in (64, 8, 300, 13),
+    # one column of 64 rows per workgroup in (64, 1, 90, 64), and G = 12 in (24, 2, 300, 20): 5
+    # columns, 60 rows, the last wave's block partly empty
     import torch
     hd = 128
     ctx = npos + nc - 1
