@@ -1,7 +1,7 @@
 // qwg_ops.hip -- the other kernels of the decode step for gfx950: repack, dequantize, embedding
 // row, RMSNorm, RoPE, grouped-query decode attention over the fp16 KV cache, SwiGLU, cosine and
-// argmax (the Llama pieces listed under "Key features" on the NTransformer page, and the cuda/
-// kernel list of its "Architecture overview": GEMV, RMSNorm, RoPE, SwiGLU, softmax).
+// argmax (the Llama pieces listed under "Key features" on the NTransformer page, [NT] below, and
+// the cuda/ kernel list of its "Architecture overview": GEMV, RMSNorm, RoPE, SwiGLU, softmax).
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -294,6 +294,7 @@ AttnPlan plan_attn(int n_pos, int n_q, int n_kv, int nc) {
 static size_t attn_lds_bytes(int rows) {
   return (size_t)rows * HEAD_DIM * 4 + (size_t)rows * ATT_T * 4 + (size_t)ATT_T * KROW * 2 + (size_t)ATT_T * HEAD_DIM * 2;
 }
+// Grouped-query attention over the fp16 KV cache ([NT] "Key features": GQA, KV cache).
 // Decode steps and narrow verify passes (fewer than 32 query rows per KV head): one workgroup per
 // (kv head g, split s of ATT_T positions, column n0) for the G = n_q / n_kv query rows of the group
 // (GQA: query heads g*G .. g*G+G-1 share K/V head g), so a verify's rows spread over more CUs.  Wave
@@ -406,10 +407,11 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attn(AttnArgs a) {
   }
 }
 
-// Passes of 32 or more query rows per KV head (prompt prefill, verify) on the matrix cores: one
-// workgroup per (kv head g, split s of ATT_T positions, block of cpw columns) holds up to 64 query
-// rows (cpw = 64 / G columns), 16 per wave, and computes them with v_mfma_f32_16x16x4_f32 (fp32
-// operands, fp32 accumulation; K converted exactly from fp16):
+// Passes of 32 or more query rows per KV head (the prompt pass, [NT] "Quick start": -p; the
+// self-speculative verify pass, [NT] "Key features") on the matrix cores: one workgroup per (kv
+// head g, split s of ATT_T positions, block of cpw columns) holds up to 64 query rows (cpw = 64 / G
+// columns), 16 per wave, and computes them with v_mfma_f32_16x16x4_f32 (fp32 operands, fp32
+// accumulation; K converted exactly from fp16):
 //   1. the K tile and the V tile (its dimensions regrouped so that dimensions n, n + 16, ..., n + 112
 //      are adjacent) are staged in LDS; each lane loads 32 dimensions of its query row;
 //   2. S^T = K Q^T per 16-position tile: lane 16 kk + i takes K row i and query row i, dimensions
