@@ -36,7 +36,7 @@ HBM_PEAK_GBPS = 8000.0
 # taken again.
 GEMV_TRAFFIC = {
     "workload": "llama70b-q4_k-resident",
-    "sources_sha256": "309aa6c3e1e10da03128f29930fbe3ac70a408a8690bb79c5494d6e220a7adf3",
+    "sources_sha256": "a805c914e336b6e431f0e284bf85eb41d9f51b83cd6e41f9684f7148e546cca5",
     "fetch_scale": 1.99975, "write_scale": 1.00000,
     "classes": {  # label -> (fetch KiB, write KiB) per launch
         "qkv": (23920.2, 44.8),

@@ -1,5 +1,5 @@
 // qwg_gemv.hip -- fused dequantize-and-GEMV for gfx950 (the engine's hand-written GEMV kernels,
-// NTransformer page "Architecture overview", cuda/; formats from the Show HN page's
+// NTransformer page, [NT] below, "Architecture overview", cuda/; formats from the Show HN page's
 // quantization-format table).
 //
 // Work decomposition (batch-1 decode is HBM-bound: every weight byte is read exactly once):
