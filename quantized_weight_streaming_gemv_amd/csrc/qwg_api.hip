@@ -393,7 +393,8 @@ static int gemv(qwg_model* m, int tensor_class, int qt, const MatView& w, const 
     e.eps = m->d.rms_eps;
   }
   const bool want = od.buf >= 0;
-  const bool fused = want && gemv_can_digitize_output(gp, epi, w.rows);
+  const bool fused = want && gemv_can_digitize_output(gp, epi, w.rows) &&
+                     gemv_digit_kind(od.qt, epi == EPI_SWIGLU ? w.rows / 2 : w.rows, nc) != DIG_F16;
   if (fused) {
     e.dig_out = (uint32_t*)(m->arena + m->xd[od.buf]);
     e.dig_stride = m->xd_col / 4;
@@ -453,9 +454,15 @@ static int layer_kernels(qwg_model* m, int l, const uint8_t* base, int nc, int p
     return rc;
   const AttnPlan ap = plan_attn(pos + 1, d.n_q, d.n_kv, nc);
   if (ap.work_bytes > m->attn_bytes) return fail(QWG_E_NOMEM, "attention workspace too small");
+  // the merge writes Wo's input digits itself, except fp16 pieces (their scale spans a superblock,
+  // two heads), which are digitized from its fp32 output
+  const int dk_o = gemv_digit_kind(qt_o, QR, nc);
   QWG_HIP(launch_attn(m->f(m->qb), QR, e.kc, e.vc, KR, pos + 1, d.n_q, d.n_kv, nc, m->f(m->ob), QR,
-                      m->arena + m->attn, ap, m->cs, (uint32_t*)(m->arena + m->xd[1]), m->xd_col / 4,
-                      gemv_digit_kind(qt_o, QR, nc)));
+                      m->arena + m->attn, ap, m->cs,
+                      dk_o == DIG_F16 ? nullptr : (uint32_t*)(m->arena + m->xd[1]), m->xd_col / 4, dk_o));
+  if (dk_o == DIG_F16)
+    QWG_HIP(launch_digitize(m->f(m->ob), QR, nullptr, QR, nc, qt_o, m->arena + m->xd[1], m->xd_col, nullptr, 0,
+                            m->cs));
   EpiArgs r{};
   r.y = m->f(m->h);
   r.y_stride = H;

@@ -269,13 +269,26 @@ __host__ __device__ inline T ld(const uint8_t* p) {
 //   byte:   word (h*4 + m)*4 + l, byte b = digit l of element 16h + 4m + b
 // followed by a ChunkDesc (2^-s and the sum of x_fix over the chunk, rounded and exact).
 
-enum DigitKind : int { DIG_NIB = 0, DIG_BYTE = 1 };
+enum DigitKind : int { DIG_NIB = 0, DIG_BYTE = 1, DIG_F16 = 2 };
+// DIG_F16 (the operands of the fp16 prompt GEMM, Q4_K / Q5_K with 9..64 columns) is not a fixed-point
+// form: per column and 256-element superblock, x' = x 2^sh with the superblock maximum in [2^14, 2^15)
+// (2^-sh kept a normal or subnormal fp32 power of two), each element as two fp16 pieces
+// hi = fp16(x') and lo = fp16((x' - hi) 2^11), and each chunk's sum of x' (times 2^-6) as the same
+// two pieces.  In the superblock's 8 x 36 words:
+//   words 0..255: [chunk c][piece p][group m] 4 words = eight fp16 of elements 4m, 4m+2, 4m+1, 4m+3,
+//                 16+4m, 16+4m+2, 16+4m+1, 16+4m+3 (the order in which one packed quant word's
+//                 nibbles unpack into half pairs)
+//   words 256..259 / 260..263: hi / lo pieces of the 8 chunk sums (fp16, chunk c in half c)
+//   word 264: 2^-sh as fp32 (NaN if the superblock holds a NaN or an infinity)
 constexpr int XCHUNK = 32;           // activation elements per digit chunk
 constexpr int NIB_LEVELS = 8;        // nibble digit levels
 constexpr int BYTE_LEVELS = 4;       // byte digit levels
 constexpr int DIG_WORDS = 32;        // digit words per chunk (either kind)
 constexpr int DIG_CHUNK_WORDS = 36;  // digit words + ChunkDesc
 constexpr int FIX_TOP = 29;          // the chunk maximum times 2^s lies in [2^FIX_TOP, 2^(FIX_TOP+1))
+constexpr int F16_SB_WORDS = 8 * DIG_CHUNK_WORDS;  // DIG_F16: a superblock's eight chunk slots
+constexpr int F16_SUM_WORD = 256;
+constexpr int F16_SCALE_WORD = 264;
 
 __host__ __device__ inline int digit_kind(int qt) { return (qt == Q4_K || qt == Q4_0) ? DIG_NIB : DIG_BYTE; }
 

@@ -953,11 +953,13 @@ __global__ __launch_bounds__(NG == 1 ? 1024 : 512) void k_gemv_mfma(GemvArgs a, 
 // ------------------------------------------------------------------ prompt prefill: up to 64 columns
 //
 // Chunked prefill ([NT] "Quick start": the -p prompt) multiplies every weight matrix by up to 64
-// prompt-token columns, so each weight is read once per 64 tokens.  The activation of one step (16
+// prompt-token columns, so each weight is read once per 64 tokens.  This form takes Q6_K (Q4_K and
+// Q5_K run on the fp16 matrix cores below).  The activation of one step (16
 // chunks: two 256-weight superblocks) for all 64 columns, 128 KB of byte digits, does not leave room
 // for the whole K range on chip, so the K loop is outermost: per step the workgroup stages that step's
 // digits of every column in LDS, and each wave multiplies its 16-row tile's weights for the step by all
-// 16 column groups -- one v_mfma_i32_16x16x32_i8 per (chunk, column group) (Q6_K: two), all sharing
+// 16 column groups -- two v_mfma_i32_16x16x32_i8 per (chunk, column group), one per 16-weight
+// sub-block, all sharing
 // the chunk's B operand, so the weights are unpacked once per 64 columns.  Lane 16 g + n accumulates
 // (row n, column 4 cg + g) of group cg in fp32.  A workgroup takes 16 tiles (256 rows) of one K split
 // and writes partial sums; k_gemm_reduce adds the splits in a fixed order and runs the epilogue.
@@ -970,7 +972,7 @@ constexpr size_t GM_LDS = (size_t)GM_SC * GM_DSTR * 8 + (size_t)GM_NG * 4 * GM_E
 
 template <int QT>
 __global__ __launch_bounds__(64 * GM_WAVES) void k_gemm_mfma(GemvArgs a) {
-  static_assert(QT == Q4_K || QT == Q5_K || QT == Q6_K, "K-quant formats with 32-weight chunks");
+  static_assert(QT == Q6_K, "Q6_K (the other K-quants take the fp16 form)");
   extern __shared__ uint4 lds[];
   uint2* ldig = (uint2*)lds;                            // [GM_SC][GM_DSTR]
   float2* ldesc = (float2*)(ldig + GM_SC * GM_DSTR);   // [64 columns][GM_ESTR]: (2^-s, 2^-s sum x_fix)
@@ -986,18 +988,16 @@ __global__ __launch_bounds__(64 * GM_WAVES) void k_gemm_mfma(GemvArgs a) {
   const bool live = r0 < rows;  // waves past the last tile stage the activation and compute nothing
   const int row = min(r0 + n, rows - 1);
   const uint32_t ro = row_off(QT, a.w, row), srow = slot_row(a.w.ilv, a.w.nch, row);
-  // per-lane bit-move amounts: Q5_K fifth bits (rotations), Q6_K high pairs (shifts)
-  const uint32_t rot_lo = (uint32_t)(28 + 2 * g) & 31u, rot_hi = (uint32_t)(29 + 2 * g) & 31u;
+  // per-lane shifts of the high-bit pairs
   const uint32_t shl_lo = (g & 1) ? 2u : 6u, shl_hi = (g & 1) ? 0u : 4u;
   float acc[GM_NG];
 #pragma unroll
   for (int cg = 0; cg < GM_NG; ++cg) acc[cg] = 0.f;
 
   // quarter qq (chunks 4 qq .. 4 qq + 3 of the step): the quant words transposed across the lane
-  // groups, the B operands and the chunks' weight scales, then for every column group the A operands
-  // from LDS, the products and the (row n, column 4 cg + g) updates.  hv: the superblock header
-  // (Q4_K / Q5_K) from the lane group that loaded it.
-  auto quarter = [&](const MfRaw<QT>& r, int qq, const uint4& hv) {
+  // groups, the B operands and the sub-blocks' weight scales, then for every column group the A
+  // operands from LDS, the products and the (row n, column 4 cg + g) updates.
+  auto quarter = [&](const MfRaw<QT>& r, int qq) {
     const uint4 qv = r.q[qq];
     uint32_t R[4] = {qv.x, qv.y, qv.z, qv.w};
     lane_swap32(R[0], R[2]);
@@ -1006,36 +1006,7 @@ __global__ __launch_bounds__(64 * GM_WAVES) void k_gemm_mfma(GemvArgs a) {
     lane_swap16(R[2], R[3]);  // R[j] = quant word g of chunk 4 qq + j
     uint64_t B0[4], B1[4];
     float w0[4], w1[4];
-    if constexpr (QT == Q4_K || QT == Q5_K) {
-      if constexpr (QT == Q5_K) {
-        const int src = n + 16 * qq;
-        const uint32_t qh[4] = {lane_fetch(src, r.qh.x), lane_fetch(src, r.qh.y), lane_fetch(src, r.qh.z),
-                                lane_fetch(src, r.qh.w)};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t l5 = __builtin_rotateright32(qh[j], rot_lo), h5 = __builtin_rotateright32(qh[j], rot_hi);
-          const uint32_t lo = (R[j] & 0x0F0F0F0Fu) | (l5 & 0x10101010u);
-          const uint32_t hi = ((R[j] >> 4) & 0x0F0F0F0Fu) | (h5 & 0x10101010u);
-          B0[j] = (uint64_t)lo | ((uint64_t)hi << 32);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {  // the stored nibbles are q XOR 8: flip back to q in 0..15
-          const uint32_t lo = (R[j] & 0x0F0F0F0Fu) ^ 0x08080808u;
-          const uint32_t hi = ((R[j] >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;
-          B0[j] = (uint64_t)lo | ((uint64_t)hi << 32);
-        }
-      }
-      const uint64_t ps = (uint64_t)hv.x | ((uint64_t)hv.y << 32);
-      const uint64_t pm = (uint64_t)hv.z | ((uint64_t)hv.w << 32);
-      const float dd = half_bits_to_float(hv.y >> 16), dm = half_bits_to_float(hv.w >> 16);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int sb = 4 * (qq & 1) + j;  // sub-block of the superblock
-        w0[j] = dd * (float)((uint32_t)(ps >> (6 * sb)) & 63u);
-        w1[j] = -(dm * (float)((uint32_t)(pm >> (6 * sb)) & 63u));
-      }
-    } else {
+    {
       const int src0 = n + 16 * ((2 * qq) & 3), src1 = n + 16 * ((2 * qq + 1) & 3);
       const uint4 qp = qq < 2 ? r.qhA : r.qhB;
 #pragma unroll
@@ -1057,52 +1028,33 @@ __global__ __launch_bounds__(64 * GM_WAVES) void k_gemm_mfma(GemvArgs a) {
         w1[j] = dq * (float)(int32_t)(int8_t)(uint8_t)((w >> 8) & 0xFFu);
       }
     }
-    // the products of column group cg + 1 are issued before group cg's are scaled, so the matrix
-    // cores work while the vector unit converts and scales (a product read right after its MFMA
-    // waits out the MFMA's latency)
-    constexpr int NP = QT == Q6_K ? 8 : 4;  // MFMAs per column group
+    // one column group's products at a time (two groups' operands overflow the 128 registers a
+    // 16-wave workgroup leaves each wave)
     auto products = [&](int cg, qwg_i32x4* P) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint2 av = ldig[(4 * qq + j) * GM_DSTR + cg * 64 + lane];
         const uint64_t A = (uint64_t)av.x | ((uint64_t)av.y << 32);
         P[j] = mfma_i8(A, B0[j]);
-        if constexpr (QT == Q6_K) P[4 + j] = mfma_i8(A, B1[j]);
+        P[4 + j] = mfma_i8(A, B1[j]);
       }
     };
-    // (Q5_K and Q6_K keep one group's products in flight only: two groups' operands overflow the 128
-    // registers a 16-wave workgroup leaves each wave)
-    constexpr bool PIPE = QT == Q4_K;
-
-    qwg_i32x4 Pc[NP], Pn[NP];
-    if (PIPE) products(0, Pc);
+    qwg_i32x4 Pc[8];
 #pragma unroll
     for (int cg = 0; cg < GM_NG; ++cg) {
-      if (PIPE) {
-        if (cg + 1 < GM_NG) products(cg + 1, Pn);
-      } else {
-        products(cg, Pc);
-      }
+      products(cg, Pc);
       __builtin_amdgcn_sched_barrier(0);  // keep the products ahead of this group's scaling
       const float4 d01 = *(const float4*)&ldesc[(4 * cg + g) * GM_ESTR + 4 * qq];
       const float4 d23 = *(const float4*)&ldesc[(4 * cg + g) * GM_ESTR + 4 * qq + 2];
       const float inv[4] = {d01.x, d01.z, d23.x, d23.z};
-      const float xs[4] = {d01.y, d01.w, d23.y, d23.w};
       float v = acc[cg];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         v = __builtin_fmaf(inv[j] * w0[j], mf_value(Pc[j]), v);
-        if constexpr (QT == Q6_K)
-          v = __builtin_fmaf(inv[j] * w1[j], mf_value(Pc[4 + j]), v);
-        else
-          v = __builtin_fmaf(w1[j], xs[j], v);
+        v = __builtin_fmaf(inv[j] * w1[j], mf_value(Pc[4 + j]), v);
       }
       acc[cg] = v;
       __builtin_amdgcn_sched_barrier(0);
-      if (PIPE) {
-#pragma unroll
-        for (int i = 0; i < NP; ++i) Pc[i] = Pn[i];
-      }
     }
   };
 
@@ -1143,20 +1095,8 @@ __global__ __launch_bounds__(64 * GM_WAVES) void k_gemm_mfma(GemvArgs a) {
     if (live) {
       const MfRaw<QT> r = cur;
       if (st + 1 < nst) cur = load(st + 1);
-      if constexpr (QT == Q4_K || QT == Q5_K) {
 #pragma unroll
-        for (int sbk = 0; sbk < 2; ++sbk) {
-          const int src = n + 16 * sbk;
-          const uint4 hv = make_uint4(lane_fetch(src, r.h.x), lane_fetch(src, r.h.y), lane_fetch(src, r.h.z),
-                                      lane_fetch(src, r.h.w));
-          quarter(r, 2 * sbk, hv);
-          quarter(r, 2 * sbk + 1, hv);
-        }
-      } else {
-        const uint4 none = make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) quarter(r, qq, none);
-      }
+      for (int qq = 0; qq < 4; ++qq) quarter(r, qq);
     }
   }
   // 3. partial sums of this split: (row r0 + n, column 4 cg + g)
@@ -1165,6 +1105,270 @@ __global__ __launch_bounds__(64 * GM_WAVES) void k_gemm_mfma(GemvArgs a) {
     for (int cg = 0; cg < GM_NG; ++cg) {
       const int col = 4 * cg + g;
       if (col < nc) a.part[((int64_t)split * nc + col) * rows + r0 + n] = acc[cg];
+    }
+  }
+}
+
+// ------------------------------------------------------------------ prompt prefill on fp16 matrix cores
+//
+// Q4_K and Q5_K prompt passes (9..64 columns) run on v_mfma_f32_16x16x32_f16 instead.  A weight of
+// these formats is dd sc q - dm m with integers sc, m < 64 and q < 32 per 32-weight chunk, so sc q
+// (< 2048) is an exact fp16 and one chunk of 16 rows is an exact B operand; the activation arrives as
+// DIG_F16 pieces (x' = hi + 2^-11 lo, one power-of-two scale 2^-sh per column and superblock).  Per
+// superblock and 16 x 16 (rows, columns) tile:
+//   P = sum over the 8 chunks of (sc q) . hi + (2^-11 sc q) . lo    16 MFMAs, fp32 accumulation
+//   M = sum over the chunks of m . 2^-6 (sum of x' over the chunk)   one MFMA (chunk sums as pieces)
+//   y += 2^-sh (dd P - 64 dm M)
+// so the vector unit finishes a product once per superblock (the i8 form merges four digit levels
+// and scales once per chunk).  The lo pieces are stored times 2^11 (and the weights that meet them
+// times 2^-11) so that neither falls into the fp16 subnormal range.  With lane l = 16 g + n:
+//   B: row n's eight weights of the chunk's quant word g (after the transpose of the i8 form);
+//   A: column 16 cg + n's pieces of the same eight elements (the DIG_F16 element order);
+//   D: (column 16 cg + 4 g + r, row n), r = 0..3.
+// A workgroup of GF_WAVES waves takes 256 rows (two 16-row tiles per wave, so every A operand read
+// from LDS meets two B operands) of one K split; the K loop is outermost as in the i8 form, each step
+// staging two superblocks of all 64 columns.
+constexpr int GF_WAVES = 8;
+constexpr int GF_BLK = 64;                              // 16-B entries of one operand block (64 lanes)
+constexpr int GF_FRAGS = 2 * 8 * 2 * 4;                 // blocks per step: [superblock][chunk][piece][group]
+constexpr size_t GF_LDS = (size_t)(GF_FRAGS + 2 * 4) * GF_BLK * 16 + 2 * 64 * 4;
+
+typedef _Float16 qwg_h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 qwg_h2 __attribute__((ext_vector_type(2)));
+typedef float qwg_f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t h2_fma(uint32_t a, uint32_t b, uint32_t c) {
+  const qwg_h2 r = __builtin_elementwise_fma(__builtin_bit_cast(qwg_h2, a), __builtin_bit_cast(qwg_h2, b),
+                                             __builtin_bit_cast(qwg_h2, c));
+  return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ qwg_f32x4 mfma_f16(const uint4& a, const uint4& b, qwg_f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(qwg_h8, a), __builtin_bit_cast(qwg_h8, b), c, 0,
+                                                0, 0);
+}
+
+// fp16 pairs (a, b) with a, b < 64 small integers t: fma(1024 + t, u, -1024 u) = t u exactly whenever
+// t u is an fp16 (the bit pattern 0x6400 | t is 1024 + t)
+constexpr uint32_t H2_ONE = 0x3C003C00u, H2_M1024 = 0xE400E400u, H2_2M11 = 0x10001000u, H2_MHALF = 0xB800B800u;
+
+// Eight weights sc q of one quant word in the DIG_F16 element order: lo holds elements 4g+0..3 in its
+// bytes (or nibbles), hi elements 16+4g+0..3; mask picks bytes (nibbles) 0 and 2 of a word.
+__device__ __forceinline__ uint4 f16_weights(uint32_t lo, uint32_t hi, uint32_t mask, uint32_t s2, uint32_t ns2) {
+  const uint32_t e = 0x64006400u;
+  uint4 r;
+  r.x = h2_fma((lo & mask) | e, s2, ns2);
+  r.y = h2_fma(((lo >> 8) & mask) | e, s2, ns2);
+  r.z = h2_fma((hi & mask) | e, s2, ns2);
+  r.w = h2_fma(((hi >> 8) & mask) | e, s2, ns2);
+  return r;
+}
+
+template <int QT>
+__global__ __launch_bounds__(64 * GF_WAVES) void k_gemm_f16(GemvArgs a) {
+  static_assert(QT == Q4_K || QT == Q5_K, "formats with integer sub-block scales and minima");
+  extern __shared__ uint4 lds[];
+  uint4* lfrag = lds;                                // [superblock][chunk][piece][group][64]
+  uint4* lmin = lds + GF_FRAGS * GF_BLK;             // [superblock][group][64]: hi sums, lo sums, zeros
+  float* lscale = (float*)(lmin + 2 * 4 * GF_BLK);   // [superblock][64 columns]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int nc = a.nc, rows = a.w.rows;
+  const int split = blockIdx.y;
+  const int kbeg = split * a.ks, klen = min(a.ks, a.k - kbeg);
+  const int nst = klen / (XCHUNK * 16);  // steps of two superblocks
+  const int cbase = kbeg / XCHUNK;
+  const int r0 = (blockIdx.x * GF_WAVES + wave) * 32;
+  const bool live = r0 < rows;
+  uint32_t ro[2], srow[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int row = min(r0 + 16 * t + n, rows - 1);
+    ro[t] = row_off(QT, a.w, row);
+    srow[t] = slot_row(a.w.ilv, a.w.nch, row);
+  }
+  const uint32_t rot_lo = (uint32_t)(28 + 2 * g) & 31u, rot_hi = (uint32_t)(29 + 2 * g) & 31u;  // Q5_K fifth bits
+  // the minimum-term B operand: lanes of group 1 meet the lo sums (stored times 2^11)
+  const uint32_t mmul = g == 1 ? H2_2M11 : H2_ONE, mneg = g == 1 ? H2_MHALF : H2_M1024;
+  qwg_f32x4 y[2][4];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg) y[t][cg] = qwg_f32x4{0.f, 0.f, 0.f, 0.f};
+  if (tid < 256) lmin[(tid >> 5) * GF_BLK + 32 + (tid & 31)] = make_uint4(0, 0, 0, 0);  // A rows of groups 2, 3
+
+  // one superblock of both tiles: r[t] the step's raw weights, hv[t] the superblock's header
+  auto superblock = [&](const MfRaw<QT>* r, int sbk, const uint4* hv) {
+    qwg_f32x4 P[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int cg = 0; cg < 4; ++cg) P[t][cg] = qwg_f32x4{0.f, 0.f, 0.f, 0.f};
+    uint64_t ps[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) ps[t] = (uint64_t)hv[t].x | ((uint64_t)hv[t].y << 32);
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2) {
+      const int qq = 2 * sbk + q2;
+      uint32_t R[2][4], qh[2][4];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const uint4 qv = r[t].q[qq];
+        R[t][0] = qv.x;
+        R[t][1] = qv.y;
+        R[t][2] = qv.z;
+        R[t][3] = qv.w;
+        lane_swap32(R[t][0], R[t][2]);
+        lane_swap32(R[t][1], R[t][3]);
+        lane_swap16(R[t][0], R[t][1]);
+        lane_swap16(R[t][2], R[t][3]);  // R[t][j] = quant word g of chunk 4 q2 + j of the superblock
+        if constexpr (QT == Q5_K) {
+          const int src = n + 16 * qq;
+          qh[t][0] = lane_fetch(src, r[t].qh.x);
+          qh[t][1] = lane_fetch(src, r[t].qh.y);
+          qh[t][2] = lane_fetch(src, r[t].qh.z);
+          qh[t][3] = lane_fetch(src, r[t].qh.w);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = 4 * q2 + j;  // chunk of the superblock
+        uint4 bh[2], bl[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const uint32_t sc = (uint32_t)(ps[t] >> (6 * c)) & 63u;
+          const uint32_t s2 = h2_fma(sc | (sc << 16) | 0x64006400u, H2_ONE, H2_M1024);  // (sc, sc)
+          const uint32_t ns2 = h2_fma(s2, H2_M1024, 0u), sl2 = h2_fma(s2, H2_2M11, 0u), nsl2 = h2_fma(s2, H2_MHALF, 0u);
+          uint32_t lo, hi, mask;
+          if constexpr (QT == Q4_K) {
+            lo = R[t][j] ^ 0x88888888u;  // the stored nibbles are q XOR 8
+            hi = lo >> 4;
+            mask = 0x000F000Fu;
+          } else {
+            const uint32_t l5 = __builtin_rotateright32(qh[t][j], rot_lo), h5 = __builtin_rotateright32(qh[t][j], rot_hi);
+            lo = (R[t][j] & 0x0F0F0F0Fu) | (l5 & 0x10101010u);
+            hi = ((R[t][j] >> 4) & 0x0F0F0F0Fu) | (h5 & 0x10101010u);
+            mask = 0x001F001Fu;
+          }
+          bh[t] = f16_weights(lo, hi, mask, s2, ns2);
+          bl[t] = f16_weights(lo, hi, mask, sl2, nsl2);
+        }
+        uint4 ah[4], al[4];
+#pragma unroll
+        for (int cg = 0; cg < 4; ++cg) {
+          ah[cg] = lfrag[(((sbk * 8 + c) * 2 + 0) * 4 + cg) * GF_BLK + lane];
+          al[cg] = lfrag[(((sbk * 8 + c) * 2 + 1) * 4 + cg) * GF_BLK + lane];
+        }
+#pragma unroll
+        for (int cg = 0; cg < 4; ++cg)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) P[t][cg] = mfma_f16(ah[cg], bh[t], P[t][cg]);
+#pragma unroll
+        for (int cg = 0; cg < 4; ++cg)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) P[t][cg] = mfma_f16(al[cg], bl[t], P[t][cg]);
+      }
+    }
+    // the minimum term (B: the 8 minima of row n, times 2^-11 for group 1) and the superblock's fold
+    uint4 mb[2];
+    float dd[2], dm64[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint64_t pm = (uint64_t)hv[t].z | ((uint64_t)hv[t].w << 32);
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t m0 = (uint32_t)(pm >> (12 * i)) & 63u, m1 = (uint32_t)(pm >> (12 * i + 6)) & 63u;
+        w[i] = h2_fma(m0 | (m1 << 16) | 0x64006400u, mmul, mneg);
+      }
+      mb[t] = make_uint4(w[0], w[1], w[2], w[3]);
+      dd[t] = half_bits_to_float(hv[t].y >> 16);
+      dm64[t] = 64.0f * half_bits_to_float(hv[t].w >> 16);
+    }
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg) {
+      const uint4 am = lmin[(sbk * 4 + cg) * GF_BLK + lane];
+      const float4 s4 = *(const float4*)&lscale[sbk * 64 + 16 * cg + 4 * g];
+      const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const qwg_f32x4 M = mfma_f16(am, mb[t], qwg_f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          y[t][cg][i] = __builtin_fmaf(sv[i], __builtin_fmaf(dd[t], P[t][cg][i], -(dm64[t] * M[i])), y[t][cg][i]);
+      }
+    }
+  };
+
+  MfRaw<QT> cur[2];
+  auto load = [&](int t, int st) { return mf_load<QT>(a.w, ro[t], srow[t], cbase + 16 * min(st, nst - 1), g); };
+  if (live && nst > 0) {
+    cur[0] = load(0, 0);
+    cur[1] = load(1, 0);
+  }
+  const int scol = (tid >> 2) & 63, sq = tid & 3;  // the staging thread's column and quant word
+  for (int st = 0; st < nst; ++st) {
+    // 1. stage the step's two superblocks of every column (columns >= nc are zeros): thread (column,
+    //    word) copies that column's entry of 16 of the 32 (superblock, chunk, piece) blocks
+    if (st > 0) __syncthreads();  // every wave is done with the previous step's operands
+    const uint4* xs = a.xd + (int64_t)(cbase + 16 * st) * XSLOTS;
+    const uint4* xc = xs + (int64_t)scol * a.xd_stride;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      uint4 v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int blk = (tid >> 8) + 2 * (8 * b + i);  // (superblock * 8 + chunk) * 2 + piece
+        v[i] = scol < nc ? xc[(blk >> 4) * (F16_SB_WORDS / 4) + (blk & 15) * 4 + sq] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int blk = (tid >> 8) + 2 * (8 * b + i);
+        lfrag[(blk * 4 + (scol >> 4)) * GF_BLK + 16 * sq + (scol & 15)] = v[i];
+      }
+    }
+    if (tid < 256) {
+      const int pc = tid & 1, col = (tid >> 1) & 63, sbk = tid >> 7;  // the chunk sums' hi / lo pieces
+      lmin[(sbk * 4 + (col >> 4)) * GF_BLK + 16 * pc + (col & 15)] =
+          col < nc ? xs[(int64_t)col * a.xd_stride + sbk * (F16_SB_WORDS / 4) + F16_SUM_WORD / 4 + pc]
+                   : make_uint4(0, 0, 0, 0);
+    } else if (tid < 384) {
+      const int col = tid & 63, sbk = (tid - 256) >> 6;
+      lscale[sbk * 64 + col] =
+          col < nc ? ((const float*)(xs + (int64_t)col * a.xd_stride + sbk * (F16_SB_WORDS / 4)))[F16_SCALE_WORD] : 0.f;
+    }
+    __syncthreads();
+    // 2. the next step's weights are requested before this step's products
+    if (live) {
+      const MfRaw<QT> r[2] = {cur[0], cur[1]};
+      if (st + 1 < nst) {
+        cur[0] = load(0, st + 1);
+        cur[1] = load(1, st + 1);
+      }
+#pragma unroll
+      for (int sbk = 0; sbk < 2; ++sbk) {
+        const int src = n + 16 * sbk;
+        uint4 hv[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          hv[t] = make_uint4(lane_fetch(src, r[t].h.x), lane_fetch(src, r[t].h.y), lane_fetch(src, r[t].h.z),
+                             lane_fetch(src, r[t].h.w));
+        superblock(r, sbk, hv);
+      }
+    }
+  }
+  // 3. partial sums of this split: (row r0 + 16 t + n, column 16 cg + 4 g + i)
+  if (live) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int row = r0 + 16 * t + n;
+#pragma unroll
+      for (int cg = 0; cg < 4; ++cg)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int col = 16 * cg + 4 * g + i;
+          if (row < rows && col < nc) a.part[((int64_t)split * nc + col) * rows + row] = y[t][cg][i];
+        }
     }
   }
 }
@@ -1197,6 +1401,57 @@ __global__ __launch_bounds__(256) void k_gemm_reduce(const float* part, int kspl
   if (row < rows) run_epilogue(EPI, e, n, row, v, vp);
 }
 
+// DIG_F16 pieces of one superblock: the 32 lanes of a half-wave hold its 8 chunks (lane m of each
+// quad takes elements 4m..4m+3 and 16+4m..16+4m+3 of its chunk in v), o is the column's base and c
+// the lane's chunk.  All 32 lanes must call it.
+__device__ inline void digitize_f16(const float* v, int m, uint32_t* o, int c, bool write) {
+  float mx = 0.f, nf = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    mx = fmaxf(mx, fabsf(v[i]));
+    nf = __builtin_fmaf(v[i], 0.0f, nf);  // NaN exactly when an element is a NaN or an infinity
+  }
+#pragma unroll
+  for (int d = 1; d < 32; d <<= 1) {
+    mx = fmaxf(mx, __shfl_xor(mx, d));
+    nf += __shfl_xor(nf, d);
+  }
+  const bool bad = __builtin_isnan(nf);
+  // x' = x 2^sh with the maximum in [2^14, 2^15); 2^-sh >= 2^-149 stays representable
+  int sh = 0;
+  if (mx > 0.f && !bad) sh = min(149, 15 - __builtin_amdgcn_frexp_expf(mx));
+  float xp[8], sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    xp[i] = bad ? 0.f : ldexpf(v[i], sh);
+    sum += xp[i];
+  }
+  sum = quad_sum(sum) * 0.015625f;  // 2^-6 x the chunk's sum of x' (below 2^14)
+  if (!write) return;
+  auto pieces = [](float a, float b, uint32_t& hi, uint32_t& lo) {  // (a, b) as hi and lo half pairs
+    const _Float16 ah = (_Float16)a, bh = (_Float16)b;
+    const _Float16 al = (_Float16)((a - (float)ah) * 2048.f), bl = (_Float16)((b - (float)bh) * 2048.f);
+    hi = (uint32_t)__builtin_bit_cast(uint16_t, ah) | ((uint32_t)__builtin_bit_cast(uint16_t, bh) << 16);
+    lo = (uint32_t)__builtin_bit_cast(uint16_t, al) | ((uint32_t)__builtin_bit_cast(uint16_t, bl) << 16);
+  };
+  uint4 h, l;
+  pieces(xp[0], xp[2], h.x, l.x);  // elements 4m, 4m+2
+  pieces(xp[1], xp[3], h.y, l.y);  // 4m+1, 4m+3
+  pieces(xp[4], xp[6], h.z, l.z);  // 16+4m, 16+4m+2
+  pieces(xp[5], xp[7], h.w, l.w);  // 16+4m+1, 16+4m+3
+  uint32_t* sb = o + (int64_t)(c >> 3) * F16_SB_WORDS;
+  const int cl = c & 7;
+  *(uint4*)(sb + ((cl * 2 + 0) * 4 + m) * 4) = h;
+  *(uint4*)(sb + ((cl * 2 + 1) * 4 + m) * 4) = l;
+  if (m == 0) {
+    const _Float16 shh = (_Float16)sum, shl = (_Float16)((sum - (float)shh) * 2048.f);
+    uint16_t* s16 = (uint16_t*)(sb + F16_SUM_WORD);
+    s16[cl] = __builtin_bit_cast(uint16_t, shh);
+    s16[8 + cl] = __builtin_bit_cast(uint16_t, shl);
+    if (cl == 0) sb[F16_SCALE_WORD] = __float_as_uint(bad ? __builtin_nanf("") : ldexpf(1.0f, -sh));
+  }
+}
+
 // Activation digits of nc columns of length k, four threads per 32-element chunk (thread m takes
 // elements 4m..4m+3 and 16+4m..16+4m+3 with two float4 loads).  With a gain vector the digits are
 // of g * x and sq receives each chunk's sum of x^2 (for the consumer's RMSNorm).
@@ -1222,7 +1477,10 @@ __global__ __launch_bounds__(256) void k_digitize(const float* x, int64_t x_stri
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] *= g[i];
   }
-  digitize_group(v, m, kind, out + (int64_t)n * out_stride + (int64_t)cc * DIG_CHUNK_WORDS, ok);
+  if (kind == DIG_F16)  // whole superblocks: k is a multiple of 256, so a half-wave's chunks are all valid or not
+    digitize_f16(v, m, out + (int64_t)n * out_stride, cc, ok);
+  else
+    digitize_group(v, m, kind, out + (int64_t)n * out_stride + (int64_t)cc * DIG_CHUNK_WORDS, ok);
   if (sq) {
     ss += __shfl_xor(ss, 1);
     ss += __shfl_xor(ss, 2);
@@ -1262,7 +1520,8 @@ constexpr int mf_waves(int ng) { return ng == 1 ? 16 : 8; }
 // then the K parts per tile S in {1, 2, 4, 8, 16} that minimise rounds x steps per wave, where a
 // round is one block per workgroup and a workgroup runs on each CU.
 int gemv_digit_kind(int qt, int64_t k, int nc) {
-  return plan_gemv(qt, 1, k, nc, EPI_STORE).mfma ? DIG_BYTE : digit_kind(qt);
+  const int mf = plan_gemv(qt, 1, k, nc, EPI_STORE).mfma;
+  return mf == 3 ? DIG_F16 : mf ? DIG_BYTE : digit_kind(qt);
 }
 
 static GemvPlan plan_mfma(int64_t rows, int64_t k, int nc) {
@@ -1317,17 +1576,19 @@ static GemvPlan plan_mfma(int64_t rows, int64_t k, int nc) {
 // formats whose 4-row two-pass kernel fits 128 registers without spilling
 static bool two_pass_ok(int qt) { return qt == Q4_0 || qt == Q4_K || qt == Q8_0; }
 
-// The prefill form (9..64 columns): 16 tiles of 16 rows per workgroup, and K splits (whole steps of 16
+// The prefill form (9..64 columns): 256 rows per workgroup (Q4_K / Q5_K: 8 waves of two 16-row tiles
+// on the fp16 matrix cores; Q6_K: 16 waves of one tile on the i8 ones), and K splits (whole steps of 16
 // chunks) until the workgroups cover about one per CU; the splits always go through k_gemm_reduce.
-static GemvPlan plan_gemm64(int64_t rows, int64_t k, int nc) {
+static GemvPlan plan_gemm64(int qt, int64_t rows, int64_t k, int nc) {
   GemvPlan p{};
-  p.mfma = 2;
+  const bool f16 = qt == Q4_K || qt == Q5_K;
+  p.mfma = f16 ? 3 : 2;
   p.ncm = 4 * GM_NG;
-  p.waves = GM_WAVES;
-  p.rows_per_wave = 16;
+  p.waves = f16 ? GF_WAVES : GM_WAVES;
+  p.rows_per_wave = f16 ? 32 : 16;
   p.depth = 1;
   p.passes = 1;
-  const int64_t nblk = (rows + 16 * GM_WAVES - 1) / (16 * GM_WAVES);
+  const int64_t nblk = (rows + 255) / 256;
   const int64_t nsteps = k / (XCHUNK * GM_SC);
   int64_t ksplit = std::max<int64_t>(1, std::min<int64_t>(nsteps, (PERSISTENT_WGS + nblk / 2) / std::max<int64_t>(1, nblk)));
   const int64_t sps = (nsteps + ksplit - 1) / ksplit;
@@ -1335,13 +1596,13 @@ static GemvPlan plan_gemm64(int64_t rows, int64_t k, int nc) {
   p.ks = (int)(sps * XCHUNK * GM_SC);
   p.ksplit = (int)ksplit;
   p.grid_x = (int)nblk;
-  p.lds = GM_LDS;
+  p.lds = f16 ? GF_LDS : GM_LDS;
   p.part_bytes = (size_t)ksplit * nc * rows * sizeof(float);
   return p;
 }
 
 GemvPlan plan_gemv(int qt, int64_t rows, int64_t k, int nc, int epi, int mfma) {
-  if (nc > MAX_COLS && (qt == Q4_K || qt == Q5_K || qt == Q6_K) && k % 512 == 0) return plan_gemm64(rows, k, nc);
+  if (nc > MAX_COLS && (qt == Q4_K || qt == Q5_K || qt == Q6_K) && k % 512 == 0) return plan_gemm64(qt, rows, k, nc);
   if ((mfma < 0 ? g_mfma : mfma) && nc >= 2 && nc <= 8 && (qt == Q4_K || qt == Q5_K || qt == Q6_K) &&
       k % 512 == 0)  // steps are two superblocks
     return plan_mfma(rows, k, nc);
@@ -1439,7 +1700,7 @@ bool gemv_can_digitize_input(const GemvPlan& p, int epi) {
 }
 
 bool gemv_can_digitize_output(const GemvPlan& p, int epi, int64_t rows) {
-  if (p.mfma == 2) return false;  // the prefill form's reduce kernel writes fp32 only
+  if (p.mfma >= 2) return false;  // the prefill forms' reduce kernel writes fp32 only
   if (epi != EPI_RESID && epi != EPI_SWIGLU) return false;
   if (rows % (epi == EPI_SWIGLU ? 2 * XCHUNK : XCHUNK) != 0) return false;
   if (p.ksplit > 1) return true;  // the reduce kernel covers 256 rows per block
@@ -1561,8 +1822,8 @@ hipError_t launch_gemv(int qt, const MatView& w, int64_t k, const void* xd, int6
                        const EpiArgs& e, float* part, hipStream_t st, const GemvPlan& p, hipEvent_t ev_start,
                        hipEvent_t ev_stop) {
   // the kernels keep per-column sums in arrays of MAX_COLS (the prefill form: 64 columns)
-  if (nc < 1 || nc > p.ncm || (p.mfma != 2 && nc > MAX_COLS)) return hipErrorInvalidValue;
-  if (e.dig_out && !gemv_can_digitize_output(p, epi, w.rows)) return hipErrorInvalidValue;
+  if (nc < 1 || nc > p.ncm || (p.mfma < 2 && nc > MAX_COLS)) return hipErrorInvalidValue;
+  if (e.dig_out && (e.dig_kind == DIG_F16 || !gemv_can_digitize_output(p, epi, w.rows))) return hipErrorInvalidValue;
   GemvArgs a;
   a.w = w;
   a.xd = (const uint4*)xd;
@@ -1581,15 +1842,21 @@ hipError_t launch_gemv(int qt, const MatView& w, int64_t k, const void* xd, int6
   // the stop event goes on the last kernel: the GEMV itself, or the split reduction after it
   const Dispatch d1{st, ev_start, p.ksplit == 1 ? ev_stop : nullptr};
   hipError_t err;
-  if (p.mfma == 2) {
+  if (p.mfma >= 2) {
     if (e.xf || !part) return hipErrorInvalidValue;
     grid.x = p.grid_x;
     const Dispatch d0{st, ev_start, nullptr};
-    switch (qt) {
-      case Q4_K: go(d0, k_gemm_mfma<Q4_K>, grid, block, p.lds, a); break;
-      case Q5_K: go(d0, k_gemm_mfma<Q5_K>, grid, block, p.lds, a); break;
-      case Q6_K: go(d0, k_gemm_mfma<Q6_K>, grid, block, p.lds, a); break;
-      default: return hipErrorInvalidValue;
+    if (p.mfma == 3) {
+      switch (qt) {
+        case Q4_K: go(d0, k_gemm_f16<Q4_K>, grid, block, p.lds, a); break;
+        case Q5_K: go(d0, k_gemm_f16<Q5_K>, grid, block, p.lds, a); break;
+        default: return hipErrorInvalidValue;
+      }
+    } else {
+      switch (qt) {
+        case Q6_K: go(d0, k_gemm_mfma<Q6_K>, grid, block, p.lds, a); break;
+        default: return hipErrorInvalidValue;
+      }
     }
     err = hipGetLastError();
     if (err != hipSuccess) return err;

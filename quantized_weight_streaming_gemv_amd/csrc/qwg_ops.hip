@@ -656,6 +656,7 @@ hipError_t launch_attn(const float* q, int64_t q_stride, const uint16_t* kc, con
                        const AttnPlan& p, hipStream_t st, uint32_t* dig_out, int64_t dig_stride, int dig_kind) {
   const int NQ = nc * (n_q / n_kv);
   if (n_q / n_kv > 64 || NQ > 4096 || p.nsplit < 1) return hipErrorInvalidValue;
+  if (dig_out && dig_kind != DIG_NIB && dig_kind != DIG_BYTE) return hipErrorInvalidValue;  // per-chunk kinds only
   AttnArgs a;
   a.q = q;
   a.q_stride = q_stride;
