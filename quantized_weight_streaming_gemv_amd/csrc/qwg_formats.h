@@ -273,8 +273,8 @@ enum DigitKind : int { DIG_NIB = 0, DIG_BYTE = 1, DIG_F16 = 2 };
 // DIG_F16 (the operands of the fp16 prompt GEMM, Q4_K / Q5_K with 9..64 columns) is not a fixed-point
 // form: per column and 256-element superblock, x' = x 2^sh with the superblock maximum in [2^14, 2^15)
 // (2^-sh kept a normal or subnormal fp32 power of two), each element as two fp16 pieces
-// hi = fp16(x') and lo = fp16((x' - hi) 2^11), and each chunk's sum of x' (times 2^-6) as the same
-// two pieces.  In the superblock's 8 x 36 words:
+// hi = fp16(x') and lo = fp16(x' - hi) (lo may be subnormal), and each chunk's sum of x' (times 2^-6)
+// as the same two pieces.  In the superblock's 8 x 36 words:
 //   words 0..255: [chunk c][piece p][group m] 4 words = eight fp16 of elements 4m, 4m+2, 4m+1, 4m+3,
 //                 16+4m, 16+4m+2, 16+4m+1, 16+4m+3 (the order in which one packed quant word's
 //                 nibbles unpack into half pairs)

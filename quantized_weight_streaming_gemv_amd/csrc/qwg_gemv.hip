@@ -1114,24 +1114,26 @@ __global__ __launch_bounds__(64 * GM_WAVES) void k_gemm_mfma(GemvArgs a) {
 // Q4_K and Q5_K prompt passes (9..64 columns) run on v_mfma_f32_16x16x32_f16 instead.  A weight of
 // these formats is dd sc q - dm m with integers sc, m < 64 and q < 32 per 32-weight chunk, so sc q
 // (< 2048) is an exact fp16 and one chunk of 16 rows is an exact B operand; the activation arrives as
-// DIG_F16 pieces (x' = hi + 2^-11 lo, one power-of-two scale 2^-sh per column and superblock).  Per
+// DIG_F16 pieces (x' = hi + lo, one power-of-two scale 2^-sh per column and superblock).  Per
 // superblock and 16 x 16 (rows, columns) tile:
-//   P = sum over the 8 chunks of (sc q) . hi + (2^-11 sc q) . lo    16 MFMAs, fp32 accumulation
-//   M = sum over the chunks of m . 2^-6 (sum of x' over the chunk)   one MFMA (chunk sums as pieces)
+//   P = sum over the 8 chunks of (sc q) . hi + (sc q) . lo         16 MFMAs, fp32 accumulation
+//   M = sum over the chunks of m . 2^-6 (sum of x' over the chunk)  one MFMA (chunk sums as pieces)
 //   y += 2^-sh (dd P - 64 dm M)
 // so the vector unit finishes a product once per superblock (the i8 form merges four digit levels
-// and scales once per chunk).  The lo pieces are stored times 2^11 (and the weights that meet them
-// times 2^-11) so that neither falls into the fp16 subnormal range.  With lane l = 16 g + n:
+// and scales once per chunk).  The matrix cores take fp16 subnormal inputs as they are (checked on
+// gfx950), so a lo piece below 2^-14 keeps its value to 2^-25.  With lane l = 16 g + n:
 //   B: row n's eight weights of the chunk's quant word g (after the transpose of the i8 form);
 //   A: column 16 cg + n's pieces of the same eight elements (the DIG_F16 element order);
 //   D: (column 16 cg + 4 g + r, row n), r = 0..3.
-// A workgroup of GF_WAVES waves takes 256 rows (two 16-row tiles per wave, so every A operand read
-// from LDS meets two B operands) of one K split; the K loop is outermost as in the i8 form, each step
-// staging two superblocks of all 64 columns.
+// A workgroup of 8 waves takes 256 rows (two 16-row tiles per wave, so every A operand read from LDS
+// meets two B operands) of one K split.  The K loop is outermost, one superblock of all 64 columns
+// per step, in two LDS buffers: while the waves multiply one superblock, the next one's operands are
+// on their way from global memory straight into the other buffer (global_load_lds_dwordx4, no
+// registers), so the staging no longer stalls every wave between steps.
 constexpr int GF_WAVES = 8;
-constexpr int GF_BLK = 64;                              // 16-B entries of one operand block (64 lanes)
-constexpr int GF_FRAGS = 2 * 8 * 2 * 4;                 // blocks per step: [superblock][chunk][piece][group]
-constexpr size_t GF_LDS = (size_t)(GF_FRAGS + 2 * 4) * GF_BLK * 16 + 2 * 64 * 4;
+constexpr int GF_BLK = 64;                                // 16-B entries of one operand block (64 lanes)
+constexpr int GF_FRAGS = 8 * 2 * 4;                       // operand blocks per superblock: [chunk][piece][group]
+constexpr int GF_BUF = (GF_FRAGS + 4) * GF_BLK + 64 / 4;  // 16-B entries per buffer (+ 4 minimum-term blocks, scales)
 
 typedef _Float16 qwg_h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 qwg_h2 __attribute__((ext_vector_type(2)));
@@ -1149,7 +1151,7 @@ __device__ __forceinline__ qwg_f32x4 mfma_f16(const uint4& a, const uint4& b, qw
 
 // fp16 pairs (a, b) with a, b < 64 small integers t: fma(1024 + t, u, -1024 u) = t u exactly whenever
 // t u is an fp16 (the bit pattern 0x6400 | t is 1024 + t)
-constexpr uint32_t H2_ONE = 0x3C003C00u, H2_M1024 = 0xE400E400u, H2_2M11 = 0x10001000u, H2_MHALF = 0xB800B800u;
+constexpr uint32_t H2_ONE = 0x3C003C00u, H2_M1024 = 0xE400E400u;
 
 // Eight weights sc q of one quant word in the DIG_F16 element order: lo holds elements 4g+0..3 in its
 // bytes (or nibbles), hi elements 16+4g+0..3; mask picks bytes (nibbles) 0 and 2 of a word.
@@ -1163,135 +1165,192 @@ __device__ __forceinline__ uint4 f16_weights(uint32_t lo, uint32_t hi, uint32_t 
   return r;
 }
 
+// One superblock of one 16-row tile as lane (n, g) loads it: chunks g and 4 + g of row n (q), the
+// row's superblock header (h), and (Q5_K) the fifth bits of chunks 4 (g & 1) .. 4 (g & 1) + 3.
+template <int QT>
+struct SbRaw {
+  uint4 q[2];
+  uint4 h;
+};
+template <>
+struct SbRaw<Q5_K> {
+  uint4 q[2];
+  uint4 h;
+  uint4 qh;
+};
+template <int QT>
+__device__ __forceinline__ SbRaw<QT> sb_load(const MatView& w, uint32_t ro, uint32_t srow, int sb, int g) {
+  SbRaw<QT> r;
+  const uint32_t s0 = srow + slot_chunk(w.ilv, 8u * (uint32_t)sb);  // the superblock's chunks are consecutive slots
+  r.q[0] = ld_stream_u4(w.q + (s0 + (uint32_t)g) * 16u);
+  r.q[1] = ld_stream_u4(w.q + (s0 + 4u + (uint32_t)g) * 16u);
+  r.h = ld<uint4>(w.a + ro + (uint32_t)sb * 16u);
+  if constexpr (QT == Q5_K) r.qh = ld<uint4>(w.b + (s0 + 4u * (uint32_t)(g & 1)) * 4u);
+  return r;
+}
+
+typedef const __attribute__((address_space(1))) void* qwg_gptr;
+typedef __attribute__((address_space(3))) void* qwg_lptr;
+
+// Requests superblock sb of every column (DIG_F16 pieces) into LDS buffer buf: wave w copies the
+// operand blocks (chunk, piece) = (w >> 2) + 2 j, j = 0..7, of column group w & 3 (lane 16 g + i: word g
+// of column 16 (w & 3) + i), waves 0..3 also their group's minimum-term block (lanes 0..15 hi sums,
+// 16..31 lo sums), wave 4 the 64 scales.  Lanes of columns >= nc load nothing: their entries keep the
+// zeros the kernel wrote at its start.
+__device__ __forceinline__ void f16_stage(uint4* buf, const GemvArgs& a, int sb, int wave, int lane) {
+  const int cg = wave & 3, gq = lane >> 4, col = 16 * cg + (lane & 15);
+  const uint4* xc = a.xd + (int64_t)col * a.xd_stride + (int64_t)sb * (F16_SB_WORDS / 4);
+  if (col < a.nc) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int cp = (wave >> 2) + 2 * j;  // chunk * 2 + piece
+      __builtin_amdgcn_global_load_lds((qwg_gptr)(xc + cp * 4 + gq), (qwg_lptr)(buf + (cp * 4 + cg) * GF_BLK), 16, 0, 0);
+    }
+  }
+  if (wave < 4 && lane < 32 && col < a.nc)
+    __builtin_amdgcn_global_load_lds((qwg_gptr)(xc + F16_SUM_WORD / 4 + gq), (qwg_lptr)(buf + (GF_FRAGS + cg) * GF_BLK),
+                                     16, 0, 0);
+  if (wave == 4 && lane < a.nc)
+    __builtin_amdgcn_global_load_lds(
+        (qwg_gptr)((const uint32_t*)(a.xd + (int64_t)lane * a.xd_stride + (int64_t)sb * (F16_SB_WORDS / 4)) +
+                   F16_SCALE_WORD),
+        (qwg_lptr)(buf + (GF_FRAGS + 4) * GF_BLK), 4, 0, 0);
+}
+
 template <int QT>
 __global__ __launch_bounds__(64 * GF_WAVES) void k_gemm_f16(GemvArgs a) {
   static_assert(QT == Q4_K || QT == Q5_K, "formats with integer sub-block scales and minima");
-  extern __shared__ uint4 lds[];
-  uint4* lfrag = lds;                                // [superblock][chunk][piece][group][64]
-  uint4* lmin = lds + GF_FRAGS * GF_BLK;             // [superblock][group][64]: hi sums, lo sums, zeros
-  float* lscale = (float*)(lmin + 2 * 4 * GF_BLK);   // [superblock][64 columns]
+  constexpr int T = 2;  // tiles per wave
+  // two buffers, each [chunk][piece][group][64] operand blocks, [group][64] minimum-term blocks and
+  // the 64 columns' scales; separate arrays, so the compiler sees that the requests into one buffer
+  // never touch the one being read
+  __shared__ uint4 buf0[GF_BUF], buf1[GF_BUF];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int nc = a.nc, rows = a.w.rows;
   const int split = blockIdx.y;
   const int kbeg = split * a.ks, klen = min(a.ks, a.k - kbeg);
-  const int nst = klen / (XCHUNK * 16);  // steps of two superblocks
-  const int cbase = kbeg / XCHUNK;
-  const int r0 = (blockIdx.x * GF_WAVES + wave) * 32;
+  const int nsb = klen / (XCHUNK * 8);  // superblocks of this split (an even number)
+  const int sb0 = kbeg / (XCHUNK * 8);
+  const int r0 = (blockIdx.x * GF_WAVES + wave) * 16 * T;
   const bool live = r0 < rows;
-  uint32_t ro[2], srow[2];
+  uint32_t ro[T], srow[T];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < T; ++t) {
     const int row = min(r0 + 16 * t + n, rows - 1);
     ro[t] = row_off(QT, a.w, row);
     srow[t] = slot_row(a.w.ilv, a.w.nch, row);
   }
   const uint32_t rot_lo = (uint32_t)(28 + 2 * g) & 31u, rot_hi = (uint32_t)(29 + 2 * g) & 31u;  // Q5_K fifth bits
-  // the minimum-term B operand: lanes of group 1 meet the lo sums (stored times 2^11)
-  const uint32_t mmul = g == 1 ? H2_2M11 : H2_ONE, mneg = g == 1 ? H2_MHALF : H2_M1024;
-  qwg_f32x4 y[2][4];
+  qwg_f32x4 y[T][4];
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < T; ++t)
 #pragma unroll
     for (int cg = 0; cg < 4; ++cg) y[t][cg] = qwg_f32x4{0.f, 0.f, 0.f, 0.f};
-  if (tid < 256) lmin[(tid >> 5) * GF_BLK + 32 + (tid & 31)] = make_uint4(0, 0, 0, 0);  // A rows of groups 2, 3
 
-  // one superblock of both tiles: r[t] the step's raw weights, hv[t] the superblock's header
-  auto superblock = [&](const MfRaw<QT>* r, int sbk, const uint4* hv) {
-    qwg_f32x4 P[2][4];
+  // the superblock in buffer b, with r[t] its raw weights.  Chunk c's A operands are read from LDS and
+  // its B operands built while chunk c - 1's products run (two sets of each, chosen at compile time).
+  auto superblock = [&](const uint4* b, const SbRaw<QT>* r) {
+    const uint4* lmin = b + GF_FRAGS * GF_BLK;
+    const float* lscale = (const float*)(b + (GF_FRAGS + 4) * GF_BLK);
+    qwg_f32x4 P[T][4];
+    uint64_t ps[T];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < T; ++t) ps[t] = (uint64_t)r[t].h.x | ((uint64_t)r[t].h.y << 32);
+    uint32_t R[2][T][4], qh[2][T][4];  // transposed quant words (and fifth bits) of quarters 0, 1
 #pragma unroll
-      for (int cg = 0; cg < 4; ++cg) P[t][cg] = qwg_f32x4{0.f, 0.f, 0.f, 0.f};
-    uint64_t ps[2];
+    for (int q2 = 0; q2 < 2; ++q2)
 #pragma unroll
-    for (int t = 0; t < 2; ++t) ps[t] = (uint64_t)hv[t].x | ((uint64_t)hv[t].y << 32);
-#pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2) {
-      const int qq = 2 * sbk + q2;
-      uint32_t R[2][4], qh[2][4];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const uint4 qv = r[t].q[qq];
-        R[t][0] = qv.x;
-        R[t][1] = qv.y;
-        R[t][2] = qv.z;
-        R[t][3] = qv.w;
-        lane_swap32(R[t][0], R[t][2]);
-        lane_swap32(R[t][1], R[t][3]);
-        lane_swap16(R[t][0], R[t][1]);
-        lane_swap16(R[t][2], R[t][3]);  // R[t][j] = quant word g of chunk 4 q2 + j of the superblock
+      for (int t = 0; t < T; ++t) {
+        const uint4 qv = r[t].q[q2];
+        R[q2][t][0] = qv.x;
+        R[q2][t][1] = qv.y;
+        R[q2][t][2] = qv.z;
+        R[q2][t][3] = qv.w;
+        lane_swap32(R[q2][t][0], R[q2][t][2]);
+        lane_swap32(R[q2][t][1], R[q2][t][3]);
+        lane_swap16(R[q2][t][0], R[q2][t][1]);
+        lane_swap16(R[q2][t][2], R[q2][t][3]);  // R[q2][t][j] = quant word g of chunk 4 q2 + j
         if constexpr (QT == Q5_K) {
-          const int src = n + 16 * qq;
-          qh[t][0] = lane_fetch(src, r[t].qh.x);
-          qh[t][1] = lane_fetch(src, r[t].qh.y);
-          qh[t][2] = lane_fetch(src, r[t].qh.z);
-          qh[t][3] = lane_fetch(src, r[t].qh.w);
+          const int src = n + 16 * q2;
+          qh[q2][t][0] = lane_fetch(src, r[t].qh.x);
+          qh[q2][t][1] = lane_fetch(src, r[t].qh.y);
+          qh[q2][t][2] = lane_fetch(src, r[t].qh.z);
+          qh[q2][t][3] = lane_fetch(src, r[t].qh.w);
         }
       }
+    uint4 ah[2][4], al[2][4], bw[2][T];
+    auto fetch_a = [&](int c, uint4* h, uint4* l) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = 4 * q2 + j;  // chunk of the superblock
-        uint4 bh[2], bl[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const uint32_t sc = (uint32_t)(ps[t] >> (6 * c)) & 63u;
-          const uint32_t s2 = h2_fma(sc | (sc << 16) | 0x64006400u, H2_ONE, H2_M1024);  // (sc, sc)
-          const uint32_t ns2 = h2_fma(s2, H2_M1024, 0u), sl2 = h2_fma(s2, H2_2M11, 0u), nsl2 = h2_fma(s2, H2_MHALF, 0u);
-          uint32_t lo, hi, mask;
-          if constexpr (QT == Q4_K) {
-            lo = R[t][j] ^ 0x88888888u;  // the stored nibbles are q XOR 8
-            hi = lo >> 4;
-            mask = 0x000F000Fu;
-          } else {
-            const uint32_t l5 = __builtin_rotateright32(qh[t][j], rot_lo), h5 = __builtin_rotateright32(qh[t][j], rot_hi);
-            lo = (R[t][j] & 0x0F0F0F0Fu) | (l5 & 0x10101010u);
-            hi = ((R[t][j] >> 4) & 0x0F0F0F0Fu) | (h5 & 0x10101010u);
-            mask = 0x001F001Fu;
-          }
-          bh[t] = f16_weights(lo, hi, mask, s2, ns2);
-          bl[t] = f16_weights(lo, hi, mask, sl2, nsl2);
-        }
-        uint4 ah[4], al[4];
-#pragma unroll
-        for (int cg = 0; cg < 4; ++cg) {
-          ah[cg] = lfrag[(((sbk * 8 + c) * 2 + 0) * 4 + cg) * GF_BLK + lane];
-          al[cg] = lfrag[(((sbk * 8 + c) * 2 + 1) * 4 + cg) * GF_BLK + lane];
-        }
-#pragma unroll
-        for (int cg = 0; cg < 4; ++cg)
-#pragma unroll
-          for (int t = 0; t < 2; ++t) P[t][cg] = mfma_f16(ah[cg], bh[t], P[t][cg]);
-#pragma unroll
-        for (int cg = 0; cg < 4; ++cg)
-#pragma unroll
-          for (int t = 0; t < 2; ++t) P[t][cg] = mfma_f16(al[cg], bl[t], P[t][cg]);
+      for (int cg = 0; cg < 4; ++cg) {
+        h[cg] = b[((c * 2 + 0) * 4 + cg) * GF_BLK + lane];
+        l[cg] = b[((c * 2 + 1) * 4 + cg) * GF_BLK + lane];
       }
+    };
+    auto build_b = [&](int c, uint4* bo) {
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const uint32_t word = R[c >> 2][t][c & 3];
+        const uint32_t sc = (uint32_t)(ps[t] >> (6 * c)) & 63u;
+        const uint32_t s2 = h2_fma(sc | (sc << 16) | 0x64006400u, H2_ONE, H2_M1024);  // (sc, sc)
+        const uint32_t ns2 = h2_fma(s2, H2_M1024, 0u);
+        uint32_t lo, hi, mask;
+        if constexpr (QT == Q4_K) {
+          lo = word ^ 0x88888888u;  // the stored nibbles are q XOR 8
+          hi = lo >> 4;
+          mask = 0x000F000Fu;
+        } else {
+          const uint32_t f = qh[c >> 2][t][c & 3];
+          const uint32_t l5 = __builtin_rotateright32(f, rot_lo), h5 = __builtin_rotateright32(f, rot_hi);
+          lo = (word & 0x0F0F0F0Fu) | (l5 & 0x10101010u);
+          hi = ((word >> 4) & 0x0F0F0F0Fu) | (h5 & 0x10101010u);
+          mask = 0x001F001Fu;
+        }
+        bo[t] = f16_weights(lo, hi, mask, s2, ns2);
+      }
+    };
+    fetch_a(0, ah[0], al[0]);
+    build_b(0, bw[0]);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int cur = c & 1, nxt = cur ^ 1;
+      if (c + 1 < 8) fetch_a(c + 1, ah[nxt], al[nxt]);
+      __builtin_amdgcn_sched_barrier(0);  // the next chunk's LDS reads go out first
+      if (c + 1 < 8) build_b(c + 1, bw[nxt]);
+      const qwg_f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cg = 0; cg < 4; ++cg)
+#pragma unroll
+        for (int t = 0; t < T; ++t) P[t][cg] = mfma_f16(ah[cur][cg], bw[cur][t], c == 0 ? z : P[t][cg]);
+#pragma unroll
+      for (int cg = 0; cg < 4; ++cg)
+#pragma unroll
+        for (int t = 0; t < T; ++t) P[t][cg] = mfma_f16(al[cur][cg], bw[cur][t], P[t][cg]);
     }
-    // the minimum term (B: the 8 minima of row n, times 2^-11 for group 1) and the superblock's fold
-    uint4 mb[2];
-    float dd[2], dm64[2];
+    // the minimum term (B: the 8 minima of row n) and the superblock's fold
+    uint4 mb[T];
+    float dd[T], dm64[T];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const uint64_t pm = (uint64_t)hv[t].z | ((uint64_t)hv[t].w << 32);
+    for (int t = 0; t < T; ++t) {
+      const uint64_t pm = (uint64_t)r[t].h.z | ((uint64_t)r[t].h.w << 32);
       uint32_t w[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t m0 = (uint32_t)(pm >> (12 * i)) & 63u, m1 = (uint32_t)(pm >> (12 * i + 6)) & 63u;
-        w[i] = h2_fma(m0 | (m1 << 16) | 0x64006400u, mmul, mneg);
+        w[i] = h2_fma(m0 | (m1 << 16) | 0x64006400u, H2_ONE, H2_M1024);
       }
       mb[t] = make_uint4(w[0], w[1], w[2], w[3]);
-      dd[t] = half_bits_to_float(hv[t].y >> 16);
-      dm64[t] = 64.0f * half_bits_to_float(hv[t].w >> 16);
+      dd[t] = half_bits_to_float(r[t].h.y >> 16);
+      dm64[t] = 64.0f * half_bits_to_float(r[t].h.w >> 16);
     }
 #pragma unroll
     for (int cg = 0; cg < 4; ++cg) {
-      const uint4 am = lmin[(sbk * 4 + cg) * GF_BLK + lane];
-      const float4 s4 = *(const float4*)&lscale[sbk * 64 + 16 * cg + 4 * g];
+      const uint4 am = lmin[cg * GF_BLK + lane];
+      const float4 s4 = *(const float4*)&lscale[16 * cg + 4 * g];
       const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < T; ++t) {
         const qwg_f32x4 M = mfma_f16(am, mb[t], qwg_f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -1300,67 +1359,45 @@ __global__ __launch_bounds__(64 * GF_WAVES) void k_gemm_f16(GemvArgs a) {
     }
   };
 
-  MfRaw<QT> cur[2];
-  auto load = [&](int t, int st) { return mf_load<QT>(a.w, ro[t], srow[t], cbase + 16 * min(st, nst - 1), g); };
-  if (live && nst > 0) {
-    cur[0] = load(0, 0);
-    cur[1] = load(1, 0);
+  // zeros in both buffers: the entries of columns >= nc and the minimum-term lanes 32..63 stay zero
+  for (int i = tid; i < GF_BUF; i += 64 * GF_WAVES) {
+    buf0[i] = make_uint4(0, 0, 0, 0);
+    buf1[i] = make_uint4(0, 0, 0, 0);
   }
-  const int scol = (tid >> 2) & 63, sq = tid & 3;  // the staging thread's column and quant word
-  for (int st = 0; st < nst; ++st) {
-    // 1. stage the step's two superblocks of every column (columns >= nc are zeros): thread (column,
-    //    word) copies that column's entry of 16 of the 32 (superblock, chunk, piece) blocks
-    if (st > 0) __syncthreads();  // every wave is done with the previous step's operands
-    const uint4* xs = a.xd + (int64_t)(cbase + 16 * st) * XSLOTS;
-    const uint4* xc = xs + (int64_t)scol * a.xd_stride;
+  __syncthreads();
+  // raw weights in two named sets (even and odd superblocks), so that a request lands where the
+  // multiply after next reads it, without copies on the loop's back-edge
+  SbRaw<QT> wa[T], wb[T];
+  auto load = [&](SbRaw<QT>* dst, int sbi) {
+    if (live && sbi < nsb) {
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      uint4 v[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int blk = (tid >> 8) + 2 * (8 * b + i);  // (superblock * 8 + chunk) * 2 + piece
-        v[i] = scol < nc ? xc[(blk >> 4) * (F16_SB_WORDS / 4) + (blk & 15) * 4 + sq] : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int blk = (tid >> 8) + 2 * (8 * b + i);
-        lfrag[(blk * 4 + (scol >> 4)) * GF_BLK + 16 * sq + (scol & 15)] = v[i];
-      }
+      for (int t = 0; t < T; ++t) dst[t] = sb_load<QT>(a.w, ro[t], srow[t], sb0 + sbi, g);
     }
-    if (tid < 256) {
-      const int pc = tid & 1, col = (tid >> 1) & 63, sbk = tid >> 7;  // the chunk sums' hi / lo pieces
-      lmin[(sbk * 4 + (col >> 4)) * GF_BLK + 16 * pc + (col & 15)] =
-          col < nc ? xs[(int64_t)col * a.xd_stride + sbk * (F16_SB_WORDS / 4) + F16_SUM_WORD / 4 + pc]
-                   : make_uint4(0, 0, 0, 0);
-    } else if (tid < 384) {
-      const int col = tid & 63, sbk = (tid - 256) >> 6;
-      lscale[sbk * 64 + col] =
-          col < nc ? ((const float*)(xs + (int64_t)col * a.xd_stride + sbk * (F16_SB_WORDS / 4)))[F16_SCALE_WORD] : 0.f;
-    }
+  };
+  // one step: request superblock sbi + 1 (operands into `nxt`, weights into wn), multiply superblock
+  // sbi from `now` with weights wc, then wait for this wave's requests and meet the other waves (after
+  // which `now` may be overwritten and `nxt` is complete)
+  auto step = [&](int sbi, const uint4* now, uint4* nxt, const SbRaw<QT>* wc, SbRaw<QT>* wn) {
+    if (sbi + 1 < nsb) f16_stage(nxt, a, sb0 + sbi + 1, wave, lane);
+    load(wn, sbi + 1);
+    if (live) superblock(now, wc);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
-    // 2. the next step's weights are requested before this step's products
-    if (live) {
-      const MfRaw<QT> r[2] = {cur[0], cur[1]};
-      if (st + 1 < nst) {
-        cur[0] = load(0, st + 1);
-        cur[1] = load(1, st + 1);
-      }
-#pragma unroll
-      for (int sbk = 0; sbk < 2; ++sbk) {
-        const int src = n + 16 * sbk;
-        uint4 hv[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-          hv[t] = make_uint4(lane_fetch(src, r[t].h.x), lane_fetch(src, r[t].h.y), lane_fetch(src, r[t].h.z),
-                             lane_fetch(src, r[t].h.w));
-        superblock(r, sbk, hv);
-      }
-    }
+  };
+  if (nsb > 0) {
+    f16_stage(buf0, a, sb0, wave, lane);
+    load(wa, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's requests are in LDS
+    __syncthreads();
   }
-  // 3. partial sums of this split: (row r0 + 16 t + n, column 16 cg + 4 g + i)
+  for (int sbi = 0; sbi < nsb; sbi += 2) {
+    step(sbi, buf0, buf1, wa, wb);
+    if (sbi + 1 < nsb) step(sbi + 1, buf1, buf0, wb, wa);
+  }
+  // partial sums of this split: (row r0 + 16 t + n, column 16 cg + 4 g + i)
   if (live) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < T; ++t) {
       const int row = r0 + 16 * t + n;
 #pragma unroll
       for (int cg = 0; cg < 4; ++cg)
@@ -1430,7 +1467,7 @@ __device__ inline void digitize_f16(const float* v, int m, uint32_t* o, int c, b
   if (!write) return;
   auto pieces = [](float a, float b, uint32_t& hi, uint32_t& lo) {  // (a, b) as hi and lo half pairs
     const _Float16 ah = (_Float16)a, bh = (_Float16)b;
-    const _Float16 al = (_Float16)((a - (float)ah) * 2048.f), bl = (_Float16)((b - (float)bh) * 2048.f);
+    const _Float16 al = (_Float16)(a - (float)ah), bl = (_Float16)(b - (float)bh);
     hi = (uint32_t)__builtin_bit_cast(uint16_t, ah) | ((uint32_t)__builtin_bit_cast(uint16_t, bh) << 16);
     lo = (uint32_t)__builtin_bit_cast(uint16_t, al) | ((uint32_t)__builtin_bit_cast(uint16_t, bl) << 16);
   };
@@ -1444,7 +1481,7 @@ __device__ inline void digitize_f16(const float* v, int m, uint32_t* o, int c, b
   *(uint4*)(sb + ((cl * 2 + 0) * 4 + m) * 4) = h;
   *(uint4*)(sb + ((cl * 2 + 1) * 4 + m) * 4) = l;
   if (m == 0) {
-    const _Float16 shh = (_Float16)sum, shl = (_Float16)((sum - (float)shh) * 2048.f);
+    const _Float16 shh = (_Float16)sum, shl = (_Float16)(sum - (float)shh);
     uint16_t* s16 = (uint16_t*)(sb + F16_SUM_WORD);
     s16[cl] = __builtin_bit_cast(uint16_t, shh);
     s16[8 + cl] = __builtin_bit_cast(uint16_t, shl);
@@ -1596,7 +1633,7 @@ static GemvPlan plan_gemm64(int qt, int64_t rows, int64_t k, int nc) {
   p.ks = (int)(sps * XCHUNK * GM_SC);
   p.ksplit = (int)ksplit;
   p.grid_x = (int)nblk;
-  p.lds = f16 ? GF_LDS : GM_LDS;
+  p.lds = f16 ? 0 : GM_LDS;  // the fp16 form's buffers are static
   p.part_bytes = (size_t)ksplit * nc * rows * sizeof(float);
   return p;
 }
