@@ -1153,15 +1153,16 @@ __device__ __forceinline__ qwg_f32x4 mfma_f16(const uint4& a, const uint4& b, qw
 // t u is an fp16 (the bit pattern 0x6400 | t is 1024 + t)
 constexpr uint32_t H2_ONE = 0x3C003C00u, H2_M1024 = 0xE400E400u;
 
-// Eight weights sc q of one quant word in the DIG_F16 element order: lo holds elements 4g+0..3 in its
-// bytes (or nibbles), hi elements 16+4g+0..3; mask picks bytes (nibbles) 0 and 2 of a word.
-__device__ __forceinline__ uint4 f16_weights(uint32_t lo, uint32_t hi, uint32_t mask, uint32_t s2, uint32_t ns2) {
-  const uint32_t e = 0x64006400u;
+// Eight weights sc q of one quant word in the DIG_F16 element order: byte j of lo holds q of element
+// 4g+j, byte j of hi that of 16+4g+j (q < 32).  One byte permute per pair puts 0x64 above bytes (0, 2)
+// or (1, 3), the bit patterns of 1024 + q.
+__device__ __forceinline__ uint4 f16_weights(uint32_t lo, uint32_t hi, uint32_t s2, uint32_t ns2) {
+  const uint32_t e = 0x64646464u;
   uint4 r;
-  r.x = h2_fma((lo & mask) | e, s2, ns2);
-  r.y = h2_fma(((lo >> 8) & mask) | e, s2, ns2);
-  r.z = h2_fma((hi & mask) | e, s2, ns2);
-  r.w = h2_fma(((hi >> 8) & mask) | e, s2, ns2);
+  r.x = h2_fma(__builtin_amdgcn_perm(e, lo, 0x04020400u), s2, ns2);
+  r.y = h2_fma(__builtin_amdgcn_perm(e, lo, 0x04030401u), s2, ns2);
+  r.z = h2_fma(__builtin_amdgcn_perm(e, hi, 0x04020400u), s2, ns2);
+  r.w = h2_fma(__builtin_amdgcn_perm(e, hi, 0x04030401u), s2, ns2);
   return r;
 }
 
@@ -1295,19 +1296,17 @@ __global__ __launch_bounds__(64 * GF_WAVES) void k_gemm_f16(GemvArgs a) {
         const uint32_t sc = (uint32_t)(ps[t] >> (6 * c)) & 63u;
         const uint32_t s2 = h2_fma(sc | (sc << 16) | 0x64006400u, H2_ONE, H2_M1024);  // (sc, sc)
         const uint32_t ns2 = h2_fma(s2, H2_M1024, 0u);
-        uint32_t lo, hi, mask;
+        uint32_t lo, hi;  // q of elements 4g+j and 16+4g+j in byte j
         if constexpr (QT == Q4_K) {
-          lo = word ^ 0x88888888u;  // the stored nibbles are q XOR 8
-          hi = lo >> 4;
-          mask = 0x000F000Fu;
+          lo = (word ^ 0x88888888u) & 0x0F0F0F0Fu;  // the stored nibbles are q XOR 8
+          hi = ((word >> 4) ^ 0x08080808u) & 0x0F0F0F0Fu;
         } else {
           const uint32_t f = qh[c >> 2][t][c & 3];
           const uint32_t l5 = __builtin_rotateright32(f, rot_lo), h5 = __builtin_rotateright32(f, rot_hi);
           lo = (word & 0x0F0F0F0Fu) | (l5 & 0x10101010u);
           hi = ((word >> 4) & 0x0F0F0F0Fu) | (h5 & 0x10101010u);
-          mask = 0x001F001Fu;
         }
-        bo[t] = f16_weights(lo, hi, mask, s2, ns2);
+        bo[t] = f16_weights(lo, hi, s2, ns2);
       }
     };
     fetch_a(0, ah[0], al[0]);
