@@ -1226,6 +1226,7 @@ __global__ __launch_bounds__(64 * GF_WAVES) void k_gemm_f16(GemvArgs a) {
   // the 64 columns' scales; separate arrays, so the compiler sees that the requests into one buffer
   // never touch the one being read
   __shared__ uint4 buf0[GF_BUF], buf1[GF_BUF];
+  __shared__ float lrs[64];  // fused SwiGLU epilogue (no K split, a.part null): each column's RMSNorm scale
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
@@ -1363,6 +1364,17 @@ __global__ __launch_bounds__(64 * GF_WAVES) void k_gemm_f16(GemvArgs a) {
     buf0[i] = make_uint4(0, 0, 0, 0);
     buf1[i] = make_uint4(0, 0, 0, 0);
   }
+  const bool fused = a.part == nullptr;
+  if (fused) {  // eight threads per column sum its chunks' squares
+    const int col = tid >> 3;
+    float sq = 0.f;
+    if (a.e.sq_in && col < nc)
+      for (int i = tid & 7; i < a.e.sq_in_n; i += 8) sq += a.e.sq_in[(int64_t)col * a.e.sq_in_stride + i];
+    sq += __shfl_xor(sq, 1);
+    sq += __shfl_xor(sq, 2);
+    sq += __shfl_xor(sq, 4);
+    if ((tid & 7) == 0) lrs[col] = a.e.sq_in ? 1.0f / sqrtf(sq / a.e.rms_k + a.e.eps) : 1.0f;
+  }
   __syncthreads();
   // raw weights in two named sets (even and odd superblocks), so that a request lands where the
   // multiply after next reads it, without copies on the loop's back-edge
@@ -1393,7 +1405,8 @@ __global__ __launch_bounds__(64 * GF_WAVES) void k_gemm_f16(GemvArgs a) {
     step(sbi, buf0, buf1, wa, wb);
     if (sbi + 1 < nsb) step(sbi + 1, buf1, buf0, wb, wa);
   }
-  // partial sums of this split: (row r0 + 16 t + n, column 16 cg + 4 g + i)
+  // (row r0 + 16 t + n, column 16 cg + 4 g + i): the SwiGLU epilogue (rows n and n ^ 1, the gate and
+  // up pair, are lanes l and l ^ 1), or this split's partial sums
   if (live) {
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -1403,7 +1416,13 @@ __global__ __launch_bounds__(64 * GF_WAVES) void k_gemm_f16(GemvArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int col = 16 * cg + 4 * g + i;
-          if (row < rows && col < nc) a.part[((int64_t)split * nc + col) * rows + row] = y[t][cg][i];
+          if (fused) {
+            const float v = y[t][cg][i] * lrs[col];
+            const float vp = __shfl_xor(v, 1);
+            if (row < rows && col < nc) run_epilogue(EPI_SWIGLU, a.e, col, row, v, vp);
+          } else if (row < rows && col < nc) {
+            a.part[((int64_t)split * nc + col) * rows + row] = y[t][cg][i];
+          }
         }
     }
   }
@@ -1879,15 +1898,20 @@ hipError_t launch_gemv(int qt, const MatView& w, int64_t k, const void* xd, int6
   const Dispatch d1{st, ev_start, p.ksplit == 1 ? ev_stop : nullptr};
   hipError_t err;
   if (p.mfma >= 2) {
-    if (e.xf || !part) return hipErrorInvalidValue;
+    // the fp16 form runs the SwiGLU epilogue itself when K is not split
+    const bool fused = p.mfma == 3 && p.ksplit == 1 && epi == EPI_SWIGLU;
+    if (e.xf || (!part && !fused)) return hipErrorInvalidValue;
     grid.x = p.grid_x;
-    const Dispatch d0{st, ev_start, nullptr};
+    const Dispatch d0{st, ev_start, fused ? ev_stop : nullptr};
     if (p.mfma == 3) {
+      GemvArgs af = a;
+      if (fused) af.part = nullptr;
       switch (qt) {
-        case Q4_K: go(d0, k_gemm_f16<Q4_K>, grid, block, p.lds, a); break;
-        case Q5_K: go(d0, k_gemm_f16<Q5_K>, grid, block, p.lds, a); break;
+        case Q4_K: go(d0, k_gemm_f16<Q4_K>, grid, block, p.lds, af); break;
+        case Q5_K: go(d0, k_gemm_f16<Q5_K>, grid, block, p.lds, af); break;
         default: return hipErrorInvalidValue;
       }
+      if (fused) return hipGetLastError();
     } else {
       switch (qt) {
         case Q6_K: go(d0, k_gemm_mfma<Q6_K>, grid, block, p.lds, a); break;
