@@ -393,13 +393,13 @@ static int gemv(qwg_model* m, int tensor_class, int qt, const MatView& w, const 
     e.eps = m->d.rms_eps;
   }
   const bool want = od.buf >= 0;
-  const bool fused = want && gemv_can_digitize_output(gp, epi, w.rows) &&
-                     gemv_digit_kind(od.qt, epi == EPI_SWIGLU ? w.rows / 2 : w.rows, nc) != DIG_F16;
+  const int okind = want ? gemv_digit_kind(od.qt, epi == EPI_SWIGLU ? w.rows / 2 : w.rows, nc) : -1;
+  const bool fused = want && gemv_can_digitize_output(gp, epi, w.rows, okind);
   if (fused) {
     e.dig_out = (uint32_t*)(m->arena + m->xd[od.buf]);
     e.dig_stride = m->xd_col / 4;
     e.dig_gain = od.gain;
-    e.dig_kind = gemv_digit_kind(od.qt, epi == EPI_SWIGLU ? w.rows / 2 : w.rows, nc);
+    e.dig_kind = okind;
     e.sq_out = od.sq ? m->f(m->sq) : nullptr;
     e.sq_out_stride = m->sq_col;
   }
@@ -483,8 +483,8 @@ static int layer_kernels(qwg_model* m, int l, const uint8_t* base, int nc, int p
   // silu(gate) * up reaches the down GEMV as digits written by the gate|up epilogue when its launch
   // geometry covers whole 32-output chunks, else the down GEMV digitizes the fp32 vector itself
   const int64_t gu_rows = P.gu.L.rows;
-  const bool act_digits =
-      gemv_can_digitize_output(plan_gemv(qt_gu, gu_rows, H, nc, EPI_SWIGLU), EPI_SWIGLU, gu_rows);
+  const bool act_digits = gemv_can_digitize_output(plan_gemv(qt_gu, gu_rows, H, nc, EPI_SWIGLU), EPI_SWIGLU, gu_rows,
+                                                   gemv_digit_kind(qt_down, gu_rows / 2, nc));
   OutDigits to_down;
   if (act_digits) {
     to_down.buf = 1;

@@ -1453,7 +1453,53 @@ __global__ __launch_bounds__(256) void k_gemm_reduce(const float* part, int kspl
     for (int s = 0; s < ksplit; ++s) v += part[((int64_t)s * nc + n) * rows + row];
   v *= rs;
   const float vp = __shfl_xor(v, 1);
-  if (row < rows) run_epilogue(EPI, e, n, row, v, vp);
+  const float o = row < rows ? run_epilogue(EPI, e, n, row, v, vp) : 0.f;
+  if constexpr (EPI == EPI_RESID) {
+    if (e.dig_out) {
+      // the block's 256 outputs are superblock blockIdx.x of column n: its DIG_F16 pieces (of gain *
+      // h) and per-chunk sums of h^2, as k_digitize writes them (the host checks rows % 256 == 0)
+      __shared__ float bmax[4], bnan[4];
+      const float x = e.dig_gain ? o * e.dig_gain[row] : o;
+      float mx = fabsf(x), nf = __builtin_fmaf(x, 0.0f, 0.f), ss = o * o;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        mx = fmaxf(mx, __shfl_xor(mx, off));
+        nf += __shfl_xor(nf, off);
+      }
+      if ((tid & 63) == 0) {
+        bmax[tid >> 6] = mx;
+        bnan[tid >> 6] = nf;
+      }
+      __syncthreads();
+      mx = fmaxf(fmaxf(bmax[0], bmax[1]), fmaxf(bmax[2], bmax[3]));
+      const bool bad = __builtin_isnan(bnan[0] + bnan[1] + bnan[2] + bnan[3]);
+      int sh = 0;
+      if (mx > 0.f && !bad) sh = min(149, 15 - __builtin_amdgcn_frexp_expf(mx));
+      const float xp = bad ? 0.f : ldexpf(x, sh);
+      float cs = xp;  // the chunk's sum of x' (and of h^2): the 32 rows of a chunk are a half-wave
+#pragma unroll
+      for (int off = 16; off > 0; off >>= 1) {
+        cs += __shfl_xor(cs, off);
+        ss += __shfl_xor(ss, off);
+      }
+      uint32_t* sb = e.dig_out + (int64_t)n * e.dig_stride + (int64_t)blockIdx.x * F16_SB_WORDS;
+      const int c = tid >> 5, p = tid & 31, m = (p & 15) >> 2, j = p & 3;
+      const int el = 4 * (p >> 4) + ((j == 1) ? 2 : (j == 2) ? 1 : j);  // the element order of the pieces
+      const _Float16 hi = (_Float16)xp, lo = (_Float16)(xp - (float)hi);
+      uint16_t* h16 = (uint16_t*)sb;
+      h16[(((c * 2 + 0) * 4 + m) * 4) * 2 + el] = __builtin_bit_cast(uint16_t, hi);
+      h16[(((c * 2 + 1) * 4 + m) * 4) * 2 + el] = __builtin_bit_cast(uint16_t, lo);
+      if (p == 0) {
+        const float s6 = cs * 0.015625f;
+        const _Float16 shh = (_Float16)s6, shl = (_Float16)(s6 - (float)shh);
+        uint16_t* s16 = (uint16_t*)(sb + F16_SUM_WORD);
+        s16[c] = __builtin_bit_cast(uint16_t, shh);
+        s16[8 + c] = __builtin_bit_cast(uint16_t, shl);
+        if (e.sq_out) e.sq_out[(int64_t)n * e.sq_out_stride + (int64_t)blockIdx.x * 8 + c] = ss;
+        if (c == 0) sb[F16_SCALE_WORD] = __float_as_uint(bad ? __builtin_nanf("") : ldexpf(1.0f, -sh));
+      }
+    }
+  }
 }
 
 // DIG_F16 pieces of one superblock: the 32 lanes of a half-wave hold its 8 chunks (lane m of each
@@ -1754,8 +1800,9 @@ bool gemv_can_digitize_input(const GemvPlan& p, int epi) {
   return (p.rows_per_wave == 4 && p.passes == 1) || (p.rows_per_wave == 2 && p.passes == 2);
 }
 
-bool gemv_can_digitize_output(const GemvPlan& p, int epi, int64_t rows) {
-  if (p.mfma >= 2) return false;  // the prefill forms' reduce kernel writes fp32 only
+bool gemv_can_digitize_output(const GemvPlan& p, int epi, int64_t rows, int kind) {
+  if (p.mfma >= 2) return epi == EPI_RESID && kind == DIG_F16 && rows % 256 == 0;
+  if (kind != DIG_NIB && kind != DIG_BYTE) return false;
   if (epi != EPI_RESID && epi != EPI_SWIGLU) return false;
   if (rows % (epi == EPI_SWIGLU ? 2 * XCHUNK : XCHUNK) != 0) return false;
   if (p.ksplit > 1) return true;  // the reduce kernel covers 256 rows per block
@@ -1878,7 +1925,7 @@ hipError_t launch_gemv(int qt, const MatView& w, int64_t k, const void* xd, int6
                        hipEvent_t ev_stop) {
   // the kernels keep per-column sums in arrays of MAX_COLS (the prefill form: 64 columns)
   if (nc < 1 || nc > p.ncm || (p.mfma < 2 && nc > MAX_COLS)) return hipErrorInvalidValue;
-  if (e.dig_out && (e.dig_kind == DIG_F16 || !gemv_can_digitize_output(p, epi, w.rows))) return hipErrorInvalidValue;
+  if (e.dig_out && !gemv_can_digitize_output(p, epi, w.rows, e.dig_kind)) return hipErrorInvalidValue;
   GemvArgs a;
   a.w = w;
   a.xd = (const uint4*)xd;

@@ -134,9 +134,11 @@ hipError_t launch_read(const void* src, int64_t bytes, uint32_t* sink, hipStream
 // a one-wave kernel that waits `ticks` of the wall clock (wall_clock64) and exits
 hipError_t launch_spin(uint64_t ticks, hipStream_t st);
 
-// Output values that the fused digitization of a GEMV covers per workgroup must be whole
-// 32-element chunks: true if every workgroup of the plan writes whole chunks of the output.
-bool gemv_can_digitize_output(const GemvPlan& p, int epi, int64_t rows);
+// True if the plan's kernels can write the output as activation digits of the given kind
+// (gemv_digit_kind of the consumer) themselves: the one- and several-column forms when every
+// workgroup writes whole 32-element chunks of a per-chunk kind; the prompt GEMMs' residual reduce
+// when the consumer takes fp16 pieces and each of its 256-row blocks is one whole superblock.
+bool gemv_can_digitize_output(const GemvPlan& p, int epi, int64_t rows, int kind);
 // true if the plan has a variant that digitizes an fp32 input itself (EpiArgs::xf)
 bool gemv_can_digitize_input(const GemvPlan& p, int epi);
 
