@@ -36,14 +36,14 @@ HBM_PEAK_GBPS = 8000.0
 # taken again.
 GEMV_TRAFFIC = {
     "workload": "llama70b-q4_k-resident",
-    "sources_sha256": "a805c914e336b6e431f0e284bf85eb41d9f51b83cd6e41f9684f7148e546cca5",
+    "sources_sha256": "181c10db3bfe53d937d203fecf8a38cefc824b12e9e354b73c3a1872c16723a6",
     "fetch_scale": 1.99975, "write_scale": 1.00000,
     "classes": {  # label -> (fetch KiB, write KiB) per launch
-        "qkv": (23920.2, 44.8),
-        "wo": (19194.1, 80.0),
-        "gate_up": (132515.8, 112.1),
-        "down": (65739.8, 80.0),
-        "head": (290335.6, 539.5),
+        "qkv": (24028.3, 44.8),
+        "wo": (19190.3, 80.0),
+        "gate_up": (132506.8, 112.1),
+        "down": (65731.6, 80.0),
+        "head": (290369.3, 539.4),
     },
 }
 GEMV_SOURCES = ("qwg_gemv.hip", "qwg_formats.h", "qwg_kernels.h")
