@@ -410,29 +410,41 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attn(AttnArgs a) {
 // Passes of 32 or more query rows per KV head (the prompt pass, [NT] "Quick start": -p; the
 // self-speculative verify pass, [NT] "Key features") on the matrix cores: one workgroup per (kv
 // head g, split s of ATT_T positions, block of cpw columns) holds up to 64 query rows (cpw = 64 / G
-// columns), 16 per wave, and computes them with v_mfma_f32_16x16x4_f32 (fp32 operands, fp32
-// accumulation; K converted exactly from fp16):
-//   1. the K tile and the V tile (its dimensions regrouped so that dimensions n, n + 16, ..., n + 112
-//      are adjacent) are staged in LDS; each lane loads 32 dimensions of its query row;
-//   2. S^T = K Q^T per 16-position tile: lane 16 kk + i takes K row i and query row i, dimensions
-//      32 kk .. 32 kk + 31 (the contraction runs over the dimensions in that order), and receives
-//      S[position 4 kk + v][row i], v = 0..3, for each of the 4 tiles;
+// columns), 16 per wave, and computes them with v_mfma_f32_16x16x32_f16 (fp32 accumulation).  K and
+// V enter as the fp16 values the cache holds; a query row is scaled by a power of two (its maximum
+// into [2^14, 2^15)) and split into fp16 pieces hi + lo (22 significant bits), and so are the softmax
+// weights (in [0, 1]), so every product keeps about fp32 precision.  With lane l = 16 kk + i:
+//   1. the K tile (row-major) and the V tile (transposed: dimension-major, the positions of each
+//      32-position block ordered 4 kk .. 4 kk + 3, 16 + 4 kk .. 16 + 4 kk + 3 per lane group kk) are
+//      staged in LDS; the lane loads dimensions 32 st + 8 kk .. 32 st + 7 + 8 kk of its query row i;
+//   2. S^T = K Q^T per 16-position tile: A = K rows (positions), B = the query pieces, contracting
+//      over 32 dimensions per MFMA, so the lane receives S[position 4 kk + v][row i], v = 0..3;
 //   3. per row: split max m, exp(s - m) and sum l (across the four lanes 16 kk + i) with causal masking;
-//   4. O = P V: the P values the lane holds are exactly the A operand of a 16x16x4 product whose
-//      4-position step is {16 pt + 4 kk + v : kk}, and the regrouped V row gives the B operand of the
-//      8 dimension tiles in one 16-byte read;
+//   4. O = P V per 32-position block: the eight weights the lane holds (positions 4 kk + v and
+//      16 + 4 kk + v of the block) are exactly its A operand, and one 16-byte read of the transposed V
+//      tile is the B operand of a 16-dimension tile;
 //   5. the unnormalised output, m and l go to the workspace for k_attn_merge, as in k_attn.
 constexpr int AM_WAVES = 4;
+constexpr int VROW = ATT_T + 8;  // halves per dimension row of the transposed V tile (16-B pad)
 typedef float qwg_f32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ qwg_f32x4 mfma_f32_4(float a, float b, qwg_f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+typedef _Float16 qwg_h8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ qwg_f32x4 mfma_h16(const uint4& a, const uint4& b, qwg_f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(qwg_h8, a), __builtin_bit_cast(qwg_h8, b), c, 0, 0,
+                                                0);
 }
-static size_t attn_mfma_lds_bytes() { return (size_t)ATT_T * KROW * 2 + (size_t)ATT_T * HEAD_DIM * 2; }
+// fp16 pieces of (a, b): hi = fp16(x) and lo = fp16(x - hi), as half pairs
+__device__ __forceinline__ void split_h2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  const _Float16 ah = (_Float16)a, bh = (_Float16)b;
+  const _Float16 al = (_Float16)(a - (float)ah), bl = (_Float16)(b - (float)bh);
+  hi = (uint32_t)__builtin_bit_cast(uint16_t, ah) | ((uint32_t)__builtin_bit_cast(uint16_t, bh) << 16);
+  lo = (uint32_t)__builtin_bit_cast(uint16_t, al) | ((uint32_t)__builtin_bit_cast(uint16_t, bl) << 16);
+}
+static size_t attn_mfma_lds_bytes() { return (size_t)ATT_T * KROW * 2 + (size_t)HEAD_DIM * VROW * 2; }
 
 __global__ __launch_bounds__(64 * AM_WAVES) void k_attn_mfma(AttnArgs a, int cpw) {
   extern __shared__ float sm[];
   uint16_t* ks = (uint16_t*)sm;      // [ATT_T][KROW]
-  uint16_t* vs = ks + ATT_T * KROW;  // [ATT_T][HEAD_DIM]: dimension 16 dt + n at n * 8 + dt
+  uint16_t* vt = ks + ATT_T * KROW;  // [HEAD_DIM][VROW]
   const int g = blockIdx.x, s = blockIdx.y, n0 = blockIdx.z * cpw;
   const int G = a.n_q / a.n_kv, NQ = a.nc * G;
   const int R = min(cpw, a.nc - n0) * G;  // rows of this workgroup: column n0 + j / G, head g*G + j % G
@@ -441,76 +453,84 @@ __global__ __launch_bounds__(64 * AM_WAVES) void k_attn_mfma(AttnArgs a, int cpw
   const int t0 = s * ATT_T;
   const int tn = min(ATT_T, a.n_pos + a.nc - 1 - t0);
 
-  // 1. tiles (every global load issued before the first LDS store) and this lane's query dimensions
+  // 1. tiles (every global load issued before the first LDS store: K rows with 16 threads per
+  //    position, V with one thread per position and 8 dimensions) and this lane's query dimensions
   constexpr int TP = ATT_T * 16 / (64 * AM_WAVES);
   uint4 kv[TP], vv[TP];
 #pragma unroll
   for (int j = 0; j < TP; ++j) {
-    const int idx = tid + 64 * AM_WAVES * j, t = idx >> 4, c = idx & 15;
-    const int64_t off = (int64_t)(t0 + min(t, tn - 1)) * a.kv_stride + (int64_t)g * HEAD_DIM + c * 8;
-    kv[j] = *(const uint4*)(a.kc + off);
-    vv[j] = *(const uint4*)(a.vc + off);
+    const int idx = tid + 64 * AM_WAVES * j;
+    const int t = idx >> 4, c = idx & 15, tv = idx & 63, cv = idx >> 6;
+    kv[j] = *(const uint4*)(a.kc + (int64_t)(t0 + min(t, tn - 1)) * a.kv_stride + (int64_t)g * HEAD_DIM + c * 8);
+    vv[j] = *(const uint4*)(a.vc + (int64_t)(t0 + min(tv, tn - 1)) * a.kv_stride + (int64_t)g * HEAD_DIM + cv * 8);
   }
   const int jr = wave * 16 + i;  // the query row of this lane
   const bool rvalid = jr < R;
   const int jq = min(jr, R - 1);
   const int ncol = n0 + jq / G;
-  float qf[32];
+  float qf[32];  // dimensions 32 st + 8 kk + e at qf[8 st + e]
   {
-    const float4* qp = (const float4*)(a.q + (int64_t)ncol * a.q_stride + (int64_t)(g * G + jq % G) * HEAD_DIM + 32 * kk);
+    const float4* qp =
+        (const float4*)(a.q + (int64_t)ncol * a.q_stride + (int64_t)(g * G + jq % G) * HEAD_DIM + 8 * kk);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float4 v = qp[u];
-      qf[4 * u] = v.x;
-      qf[4 * u + 1] = v.y;
-      qf[4 * u + 2] = v.z;
-      qf[4 * u + 3] = v.w;
-    }
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float4 v = qp[8 * st + h];
+        qf[8 * st + 4 * h] = v.x;
+        qf[8 * st + 4 * h + 1] = v.y;
+        qf[8 * st + 4 * h + 2] = v.z;
+        qf[8 * st + 4 * h + 3] = v.w;
+      }
   }
 #pragma unroll
   for (int j = 0; j < TP; ++j) {
-    const int idx = tid + 64 * AM_WAVES * j, t = idx >> 4, c = idx & 15;
+    const int idx = tid + 64 * AM_WAVES * j;
+    const int t = idx >> 4, c = idx & 15, tv = idx & 63, cv = idx >> 6;
     *(uint4*)(ks + t * KROW + c * 8) = kv[j];
+    const int slot = (tv & 32) + 8 * ((tv & 15) >> 2) + 4 * ((tv >> 4) & 1) + (tv & 3);
     const uint32_t w[4] = {vv[j].x, vv[j].y, vv[j].z, vv[j].w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e)  // dimension 8 c + e = 16 (c >> 1) + 8 (c & 1) + e
-      vs[t * HEAD_DIM + (8 * (c & 1) + e) * 8 + (c >> 1)] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+    for (int e = 0; e < 8; ++e) vt[(8 * cv + e) * VROW + slot] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+  }
+  // the query row's scale (its four lanes share the maximum) and pieces
+  float qmx = 0.f;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) qmx = fmaxf(qmx, fabsf(qf[e]));
+  qmx = fmaxf(qmx, __shfl_xor(qmx, 16));
+  qmx = fmaxf(qmx, __shfl_xor(qmx, 32));
+  int qsh = 0;
+  if (qmx > 0.f && qmx <= 3.4e38f) qsh = min(149, 15 - __builtin_amdgcn_frexp_expf(qmx));
+  uint4 qh[4], ql[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      split_h2(ldexpf(qf[8 * st + 2 * e], qsh), ldexpf(qf[8 * st + 2 * e + 1], qsh), h[e], l[e]);
+    qh[st] = make_uint4(h[0], h[1], h[2], h[3]);
+    ql[st] = make_uint4(l[0], l[1], l[2], l[3]);
   }
   __syncthreads();
   if (wave * 16 >= R) return;  // no rows (wave-uniform; no barrier follows)
 
-  // 2. scores, two 16-position tiles at a time (independent accumulation chains)
+  // 2. scores: per 16-position tile, 4 steps of 32 dimensions x two query pieces
   qwg_f32x4 sc[4];
 #pragma unroll
-  for (int ph = 0; ph < 2; ++ph) {
-    float kf[2][32];
+  for (int pt = 0; pt < 4; ++pt) {
+    qwg_f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint16_t* kr = ks + (16 * (2 * ph + h) + i) * KROW + 32 * kk;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint4 kp = *(const uint4*)(kr + 8 * q);
-        const uint32_t w[4] = {kp.x, kp.y, kp.z, kp.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kf[h][8 * q + 2 * e] = half_bits_to_float(w[e] & 0xFFFFu);
-          kf[h][8 * q + 2 * e + 1] = half_bits_to_float(w[e] >> 16);
-        }
-      }
+    for (int st = 0; st < 4; ++st) {
+      const uint4 kr = *(const uint4*)(ks + (16 * pt + i) * KROW + 32 * st + 8 * kk);
+      c = mfma_h16(kr, qh[st], c);
+      c = mfma_h16(kr, ql[st], c);
     }
-    qwg_f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0;
-#pragma unroll
-    for (int st = 0; st < 32; ++st) {
-      c0 = mfma_f32_4(kf[0][st], qf[st], c0);
-      c1 = mfma_f32_4(kf[1][st], qf[st], c1);
-    }
-    sc[2 * ph] = c0;
-    sc[2 * ph + 1] = c1;
+    sc[pt] = c;
   }
 
   // 3. split-local softmax of row i over the positions 16 pt + 4 kk + v
-  const float scale = 0.08838834764831845f;  // 1/sqrt(128)
-  const int lim = a.n_pos + ncol - t0;       // positions below lim (and tn) are visible to the row
+  const float scale = ldexpf(0.08838834764831845f, -qsh);  // 1/sqrt(128), undoing the query's scale
+  const int lim = a.n_pos + ncol - t0;                      // positions below lim (and tn) are visible to the row
   float p[4][4], m = -INFINITY;
 #pragma unroll
   for (int pt = 0; pt < 4; ++pt)
@@ -534,20 +554,25 @@ __global__ __launch_bounds__(64 * AM_WAVES) void k_attn_mfma(AttnArgs a, int cpw
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
 
-  // 4. O = P V over the 16 steps of 4 positions, 8 dimension tiles
+  // 4. O = P V: per 32-position block, the weights' two pieces against 8 dimension tiles
   qwg_f32x4 o[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int pt = 0; pt < 4; ++pt)
+  for (int b = 0; b < 2; ++b) {
+    uint32_t h[4], lo[4];
+    split_h2(p[2 * b][0], p[2 * b][1], h[0], lo[0]);
+    split_h2(p[2 * b][2], p[2 * b][3], h[1], lo[1]);
+    split_h2(p[2 * b + 1][0], p[2 * b + 1][1], h[2], lo[2]);
+    split_h2(p[2 * b + 1][2], p[2 * b + 1][3], h[3], lo[3]);
+    const uint4 ph = make_uint4(h[0], h[1], h[2], h[3]), pl = make_uint4(lo[0], lo[1], lo[2], lo[3]);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const uint4 vp = *(const uint4*)(vs + (16 * pt + 4 * kk + v) * HEAD_DIM + i * 8);
-      const uint32_t w[4] = {vp.x, vp.y, vp.z, vp.w};
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-        o[dt] = mfma_f32_4(p[pt][v], half_bits_to_float((w[dt >> 1] >> (16 * (dt & 1))) & 0xFFFFu), o[dt]);
+    for (int dt = 0; dt < 8; ++dt) {
+      const uint4 vb = *(const uint4*)(vt + (16 * dt + i) * VROW + 32 * b + 8 * kk);
+      o[dt] = mfma_h16(ph, vb, o[dt]);
+      o[dt] = mfma_h16(pl, vb, o[dt]);
     }
+  }
 
   // 5. records: lane 16 kk + i holds O[row 4 kk + v][dimension 16 dt + i]
   float* base = a.part + ((int64_t)g * a.nsplit + s) * NQ * (HEAD_DIM + 2);
