@@ -265,6 +265,7 @@ struct AttnArgs {
   int n_pos;
   int n_q, n_kv, nc;
   int nsplit;
+  int tiles;      // ATT_T-position tiles per split (the matrix-core form; k_attn takes one)
   float* part;    // [n_kv][nsplit][NQ][HEAD_DIM + 2]: split max, sum and unnormalised output
   float* out;
   int64_t out_stride;
@@ -283,8 +284,15 @@ constexpr int ATT_THREADS = 64 * ATT_WAVES;
 AttnPlan plan_attn(int n_pos, int n_q, int n_kv, int nc) {
   AttnPlan p{};
   const int nqg = nc * (n_q / n_kv);
-  p.T = ATT_T;
   const int span = n_pos + nc - 1;
+  p.T = ATT_T;
+  if (nqg >= 32) {
+    // the matrix-core form: splits of up to four tiles while the grid keeps about two workgroups
+    // per CU (fewer, longer splits leave the merge less to combine)
+    const int64_t wg1 = (int64_t)n_kv * ((span + ATT_T - 1) / ATT_T) * ((nc + std::max(1, 64 / (n_q / n_kv)) - 1) /
+                                                                     std::max(1, 64 / (n_q / n_kv)));
+    while (p.T < 4 * ATT_T && wg1 * ATT_T / (2 * p.T) >= 512) p.T *= 2;
+  }
   p.nsplit = (span + p.T - 1) / p.T;
   p.work_bytes = (size_t)n_kv * p.nsplit * nqg * (HEAD_DIM + 2) * sizeof(float);
   return p;
@@ -450,26 +458,19 @@ __global__ __launch_bounds__(64 * AM_WAVES) void k_attn_mfma(AttnArgs a, int cpw
   const int R = min(cpw, a.nc - n0) * G;  // rows of this workgroup: column n0 + j / G, head g*G + j % G
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = lane & 15, kk = lane >> 4;
-  const int t0 = s * ATT_T;
-  const int tn = min(ATT_T, a.n_pos + a.nc - 1 - t0);
-
-  // 1. tiles (every global load issued before the first LDS store: K rows with 16 threads per
-  //    position, V with one thread per position and 8 dimensions) and this lane's query dimensions
-  constexpr int TP = ATT_T * 16 / (64 * AM_WAVES);
-  uint4 kv[TP], vv[TP];
-#pragma unroll
-  for (int j = 0; j < TP; ++j) {
-    const int idx = tid + 64 * AM_WAVES * j;
-    const int t = idx >> 4, c = idx & 15, tv = idx & 63, cv = idx >> 6;
-    kv[j] = *(const uint4*)(a.kc + (int64_t)(t0 + min(t, tn - 1)) * a.kv_stride + (int64_t)g * HEAD_DIM + c * 8);
-    vv[j] = *(const uint4*)(a.vc + (int64_t)(t0 + min(tv, tn - 1)) * a.kv_stride + (int64_t)g * HEAD_DIM + cv * 8);
-  }
-  const int jr = wave * 16 + i;  // the query row of this lane
+  const int span = a.n_pos + a.nc - 1;
+  const bool rows = wave * 16 < R;  // this wave has query rows (wave-uniform)
+  const int jr = wave * 16 + i;     // the query row of this lane
   const bool rvalid = jr < R;
   const int jq = min(jr, R - 1);
   const int ncol = n0 + jq / G;
-  float qf[32];  // dimensions 32 st + 8 kk + e at qf[8 st + e]
+
+  // the query row's dimensions 32 st + 8 kk .. 32 st + 7 + 8 kk, its scale (its four lanes share the
+  // maximum) and pieces
+  uint4 qh[4], ql[4];
+  int qsh = 0;
   {
+    float qf[32];  // dimension 32 st + 8 kk + e at qf[8 st + e]
     const float4* qp =
         (const float4*)(a.q + (int64_t)ncol * a.q_stride + (int64_t)(g * G + jq % G) * HEAD_DIM + 8 * kk);
 #pragma unroll
@@ -482,97 +483,129 @@ __global__ __launch_bounds__(64 * AM_WAVES) void k_attn_mfma(AttnArgs a, int cpw
         qf[8 * st + 4 * h + 2] = v.z;
         qf[8 * st + 4 * h + 3] = v.w;
       }
-  }
+    float qmx = 0.f;
 #pragma unroll
-  for (int j = 0; j < TP; ++j) {
-    const int idx = tid + 64 * AM_WAVES * j;
-    const int t = idx >> 4, c = idx & 15, tv = idx & 63, cv = idx >> 6;
-    *(uint4*)(ks + t * KROW + c * 8) = kv[j];
-    const int slot = (tv & 32) + 8 * ((tv & 15) >> 2) + 4 * ((tv >> 4) & 1) + (tv & 3);
-    const uint32_t w[4] = {vv[j].x, vv[j].y, vv[j].z, vv[j].w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) vt[(8 * cv + e) * VROW + slot] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-  }
-  // the query row's scale (its four lanes share the maximum) and pieces
-  float qmx = 0.f;
-#pragma unroll
-  for (int e = 0; e < 32; ++e) qmx = fmaxf(qmx, fabsf(qf[e]));
-  qmx = fmaxf(qmx, __shfl_xor(qmx, 16));
-  qmx = fmaxf(qmx, __shfl_xor(qmx, 32));
-  int qsh = 0;
-  if (qmx > 0.f && qmx <= 3.4e38f) qsh = min(149, 15 - __builtin_amdgcn_frexp_expf(qmx));
-  uint4 qh[4], ql[4];
-#pragma unroll
-  for (int st = 0; st < 4; ++st) {
-    uint32_t h[4], l[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      split_h2(ldexpf(qf[8 * st + 2 * e], qsh), ldexpf(qf[8 * st + 2 * e + 1], qsh), h[e], l[e]);
-    qh[st] = make_uint4(h[0], h[1], h[2], h[3]);
-    ql[st] = make_uint4(l[0], l[1], l[2], l[3]);
-  }
-  __syncthreads();
-  if (wave * 16 >= R) return;  // no rows (wave-uniform; no barrier follows)
-
-  // 2. scores: per 16-position tile, 4 steps of 32 dimensions x two query pieces
-  qwg_f32x4 sc[4];
-#pragma unroll
-  for (int pt = 0; pt < 4; ++pt) {
-    qwg_f32x4 c = {0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < 32; ++e) qmx = fmaxf(qmx, fabsf(qf[e]));
+    qmx = fmaxf(qmx, __shfl_xor(qmx, 16));
+    qmx = fmaxf(qmx, __shfl_xor(qmx, 32));
+    if (qmx > 0.f && qmx <= 3.4e38f) qsh = min(149, 15 - __builtin_amdgcn_frexp_expf(qmx));
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      const uint4 kr = *(const uint4*)(ks + (16 * pt + i) * KROW + 32 * st + 8 * kk);
-      c = mfma_h16(kr, qh[st], c);
-      c = mfma_h16(kr, ql[st], c);
+      uint32_t h[4], l[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        split_h2(ldexpf(qf[8 * st + 2 * e], qsh), ldexpf(qf[8 * st + 2 * e + 1], qsh), h[e], l[e]);
+      qh[st] = make_uint4(h[0], h[1], h[2], h[3]);
+      ql[st] = make_uint4(l[0], l[1], l[2], l[3]);
     }
-    sc[pt] = c;
   }
-
-  // 3. split-local softmax of row i over the positions 16 pt + 4 kk + v
   const float scale = ldexpf(0.08838834764831845f, -qsh);  // 1/sqrt(128), undoing the query's scale
-  const int lim = a.n_pos + ncol - t0;                      // positions below lim (and tn) are visible to the row
-  float p[4][4], m = -INFINITY;
-#pragma unroll
-  for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int pos = 16 * pt + 4 * kk + v;
-      const bool ok = rvalid && pos < tn && pos < lim;
-      p[pt][v] = ok ? sc[pt][v] * scale : -INFINITY;
-      m = fmaxf(m, p[pt][v]);
-    }
-  m = fmaxf(m, __shfl_xor(m, 16));
-  m = fmaxf(m, __shfl_xor(m, 32));
-  float l = 0.f;
-#pragma unroll
-  for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      p[pt][v] = p[pt][v] == -INFINITY ? 0.f : __expf(p[pt][v] - m);
-      l += p[pt][v];
-    }
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
 
-  // 4. O = P V: per 32-position block, the weights' two pieces against 8 dimension tiles
+  // the split's running max and sum of row i, and the unnormalised output (rows 4 kk + v)
+  float m = -INFINITY, l = 0.f;
   qwg_f32x4 o[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = {0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < a.tiles; ++u) {
+    const int t0 = (s * a.tiles + u) * ATT_T;
+    const int tn = min(ATT_T, span - t0);
+    if (tn <= 0) break;  // past the last position (the same for every wave)
+    if (u > 0) __syncthreads();  // every wave is done with the previous tile
+
+    // 1. the tile (every global load issued before the first LDS store: K rows with 16 threads per
+    //    position, V with one thread per position and 8 dimensions)
+    constexpr int TP = ATT_T * 16 / (64 * AM_WAVES);
+    uint4 kv[TP], vv[TP];
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    uint32_t h[4], lo[4];
-    split_h2(p[2 * b][0], p[2 * b][1], h[0], lo[0]);
-    split_h2(p[2 * b][2], p[2 * b][3], h[1], lo[1]);
-    split_h2(p[2 * b + 1][0], p[2 * b + 1][1], h[2], lo[2]);
-    split_h2(p[2 * b + 1][2], p[2 * b + 1][3], h[3], lo[3]);
-    const uint4 ph = make_uint4(h[0], h[1], h[2], h[3]), pl = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    for (int j = 0; j < TP; ++j) {
+      const int idx = tid + 64 * AM_WAVES * j;
+      const int t = idx >> 4, c = idx & 15, tv = idx & 63, cv = idx >> 6;
+      kv[j] = *(const uint4*)(a.kc + (int64_t)(t0 + min(t, tn - 1)) * a.kv_stride + (int64_t)g * HEAD_DIM + c * 8);
+      vv[j] = *(const uint4*)(a.vc + (int64_t)(t0 + min(tv, tn - 1)) * a.kv_stride + (int64_t)g * HEAD_DIM + cv * 8);
+    }
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const uint4 vb = *(const uint4*)(vt + (16 * dt + i) * VROW + 32 * b + 8 * kk);
-      o[dt] = mfma_h16(ph, vb, o[dt]);
-      o[dt] = mfma_h16(pl, vb, o[dt]);
+    for (int j = 0; j < TP; ++j) {
+      const int idx = tid + 64 * AM_WAVES * j;
+      const int t = idx >> 4, c = idx & 15, tv = idx & 63, cv = idx >> 6;
+      *(uint4*)(ks + t * KROW + c * 8) = kv[j];
+      const int slot = (tv & 32) + 8 * ((tv & 15) >> 2) + 4 * ((tv >> 4) & 1) + (tv & 3);
+      const uint32_t w[4] = {vv[j].x, vv[j].y, vv[j].z, vv[j].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vt[(8 * cv + e) * VROW + slot] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+    }
+    __syncthreads();
+    if (!rows) continue;
+
+    // 2. scores: per 16-position tile, 4 steps of 32 dimensions x two query pieces
+    qwg_f32x4 sc[4];
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) {
+      qwg_f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const uint4 kr = *(const uint4*)(ks + (16 * pt + i) * KROW + 32 * st + 8 * kk);
+        c = mfma_h16(kr, qh[st], c);
+        c = mfma_h16(kr, ql[st], c);
+      }
+      sc[pt] = c;
+    }
+
+    // 3. softmax of row i over the positions 16 pt + 4 kk + v, folded into the split's running max
+    //    and sum; alpha rescales what the earlier tiles left (0 before the first visible position)
+    const int lim = a.n_pos + ncol - t0;  // positions below lim (and tn) are visible to the row
+    float p[4][4], mt = -INFINITY;
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int pos = 16 * pt + 4 * kk + v;
+        const bool ok = rvalid && pos < tn && pos < lim;
+        p[pt][v] = ok ? sc[pt][v] * scale : -INFINITY;
+        mt = fmaxf(mt, p[pt][v]);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float mn = fmaxf(m, mt);
+    const float alpha = m == -INFINITY ? 0.f : __expf(m - mn);
+    float lt = 0.f;
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        p[pt][v] = p[pt][v] == -INFINITY ? 0.f : __expf(p[pt][v] - mn);
+        lt += p[pt][v];
+      }
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    l = l * alpha + lt;
+    m = mn;
+    if (u > 0) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float av = __shfl(alpha, 4 * kk + v);  // row 4 kk + v's factor (lane 4 kk + v holds that row)
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) o[dt][v] *= av;
+      }
+    }
+
+    // 4. O += P V: per 32-position block, the weights' two pieces against 8 dimension tiles
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      uint32_t h[4], lo[4];
+      split_h2(p[2 * b][0], p[2 * b][1], h[0], lo[0]);
+      split_h2(p[2 * b][2], p[2 * b][3], h[1], lo[1]);
+      split_h2(p[2 * b + 1][0], p[2 * b + 1][1], h[2], lo[2]);
+      split_h2(p[2 * b + 1][2], p[2 * b + 1][3], h[3], lo[3]);
+      const uint4 ph = make_uint4(h[0], h[1], h[2], h[3]), pl = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const uint4 vb = *(const uint4*)(vt + (16 * dt + i) * VROW + 32 * b + 8 * kk);
+        o[dt] = mfma_h16(ph, vb, o[dt]);
+        o[dt] = mfma_h16(pl, vb, o[dt]);
+      }
     }
   }
+  if (!rows) return;
 
   // 5. records: lane 16 kk + i holds O[row 4 kk + v][dimension 16 dt + i]
   float* base = a.part + ((int64_t)g * a.nsplit + s) * NQ * (HEAD_DIM + 2);
@@ -693,6 +726,7 @@ hipError_t launch_attn(const float* q, int64_t q_stride, const uint16_t* kc, con
   a.n_kv = n_kv;
   a.nc = nc;
   a.nsplit = p.nsplit;
+  a.tiles = p.T / ATT_T;
   a.part = (float*)work;
   a.out = out;
   a.out_stride = out_stride;
