@@ -286,9 +286,10 @@ def main() -> int:
                          "gets what fits, the rest streams from pinned host memory (0: the workload's placement)")
     ap.add_argument("--file-layers", type=int, default=0,
                     help="move the first N streamed layers to files (the file-backed tier; files in $TMPDIR)")
-    ap.add_argument("--prefill", type=int, default=0,
-                    help="after the decode measurements, time a prefill of this many prompt tokens")
-    ap.add_argument("--prefill-cols", type=int, default=8, help="columns per prefill pass (the model's max_cols)")
+    ap.add_argument("--prefill", type=int, default=64,
+                    help="after the decode measurements, time a prefill of this many prompt tokens (0: none); "
+                         "reported under 'prefill', the metric stays decode tok/s")
+    ap.add_argument("--prefill-cols", type=int, default=64, help="columns per prefill pass (the model's max_cols)")
     ap.add_argument("--verify-form", choices=["mfma", "dot"], default="mfma",
                     help="2..4-column Q5_K/Q6_K GEMVs of the verify pass: matrix cores or integer dot products")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -425,10 +426,15 @@ def main() -> int:
         m.prefill(prompt)
         torch.cuda.synchronize()
         dt_p = time.perf_counter() - t0
-        prefill = {"tokens": args.prefill, "columns_per_pass": max_cols, "ms": round(dt_p * 1e3, 3),
+        # passes wider than 8 columns need the prompt GEMM: K-quant layer matrices with K % 512 == 0
+        kq = all(wl.qtype_of(t, l) in (synth.Q4_K, synth.Q5_K, synth.Q6_K)
+                 for l in range(wl.n_layers) for t in (synth.WQ, synth.WO, synth.WGATE, synth.WDOWN))
+        kq = kq and wl.hidden % 512 == 0 and wl.ffn % 512 == 0 and (wl.n_q * wl.head_dim) % 512 == 0
+        width = max_cols if kq else min(max_cols, 8)
+        prefill = {"tokens": args.prefill, "columns_per_pass": width, "ms": round(dt_p * 1e3, 3),
                    "tok_s": round(args.prefill / dt_p, 1)}
         log("prefill of %d tokens in passes of %d columns: %.2f ms, %.1f tok/s"
-            % (args.prefill, max_cols, dt_p * 1e3, args.prefill / dt_p))
+            % (args.prefill, width, dt_p * 1e3, args.prefill / dt_p))
     h2d_b, h2d_ms = m.stream_stats()
     file_b, file_ms = m.file_stats()
     step_bytes = round_bytes(wl, n_pos_mid) if spec else token_bytes(wl, n_pos_mid)
