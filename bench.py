@@ -432,7 +432,11 @@ def main() -> int:
         kq = kq and wl.hidden % 512 == 0 and wl.ffn % 512 == 0 and (wl.n_q * wl.head_dim) % 512 == 0
         width = max_cols if kq else min(max_cols, 8)
         prefill = {"tokens": args.prefill, "columns_per_pass": width, "ms": round(dt_p * 1e3, 3),
-                   "tok_s": round(args.prefill / dt_p, 1)}
+                   "tok_s": round(args.prefill / dt_p, 1),
+                   "arithmetic": ("passes of 9-64 columns: Q4_K/Q5_K GEMMs and the attention on "
+                                  "v_mfma_f32_16x16x32_f16 with exact fp16 weights (K/V) and two-piece "
+                                  "fp16 activations (queries, softmax weights), fp32 accumulation; "
+                                  "Q6_K GEMMs exact int8 products")}
         log("prefill of %d tokens in passes of %d columns: %.2f ms, %.1f tok/s"
             % (args.prefill, width, dt_p * 1e3, args.prefill / dt_p))
     h2d_b, h2d_ms = m.stream_stats()

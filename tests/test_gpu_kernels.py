@@ -272,6 +272,23 @@ def test_gemv_prefill_columns_outliers_and_nan(ops, qt):
     assert gemv_ok(y[keep], yr[keep], ar[keep]).all()
 
 
+@pytest.mark.parametrize("qt", [synth.Q4_K, synth.Q5_K], ids=["Q4_K", "Q5_K"])
+def test_prompt_gemm_bias_and_margin(ops, qt):
+    """The fp16 prompt GEMM (Q4_K / Q5_K at 64 columns) is not exact: its fp32 accumulation inside the
+    matrix cores leaves a small negative mean error.  Measured on this shape: worst row 3e-4 of the
+    bound, mean signed error -3e-10 sum|w x|.  Held well inside: 1e-2 of the bound and |mean| < 1.2e-9
+    sum|w x| (a bf16 variant with three activation pieces showed -1.4e-9 and was dropped)."""
+    rows, k, nc = 1000, 8192, 64
+    W = synth.matrix(synth.DEFAULT_DIST[qt], k, rows, tkey=synth.key(15, qt * 1000 + k))
+    x = synth.normal_f32(synth.key(15, 70 + nc), nc * k).reshape(nc, k)
+    y = ops.gemv(qt, packed_of(ops, qt, W, rows, k), rows, k, dev(x)).cpu().numpy().astype(np.float64)
+    yr, ar = oracle.gemv(qt, W, rows, k, x)
+    ratio = np.abs(y - yr) / (1e-4 * ar + 1e-6)
+    bias = float(((y - yr) / ar).mean())
+    assert ratio.max() < 1e-2, float(ratio.max())
+    assert abs(bias) < 1.2e-9, bias
+
+
 def test_gemv_q8_0_4096_full(ops):
     """The single Q8_0 GEMV workload: W 4096 x 4096, q ~ U[-127,127], d = |N|*0.02, x ~ N(0,1)."""
     qt, rows, k = synth.Q8_0, 4096, 4096
