@@ -239,7 +239,7 @@ static int plan_model(qwg_model* m) {
   }
   m->part_bytes = pb;
   m->part = take(pb > 0 ? pb : 256);
-  m->attn_bytes = plan_attn(d.max_ctx, d.n_q, d.n_kv, C).work_bytes;
+  m->attn_bytes = attn_work_bound(d.max_ctx, d.n_q, d.n_kv, C);
   m->attn = take(m->attn_bytes);
   if (m->n_streamed > 0) {
     m->slot[0] = take(m->image_max);

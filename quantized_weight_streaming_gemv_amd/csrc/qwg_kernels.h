@@ -116,6 +116,9 @@ struct AttnPlan {
   size_t work_bytes;
 };
 AttnPlan plan_attn(int n_pos, int n_q, int n_kv, int nc);
+// Workspace bytes that cover plan_attn(p, n_q, n_kv, c) for every p <= n_pos and c <= nc (the tile
+// count per split depends on the shape, so the plan's own size is not monotonic in either)
+size_t attn_work_bound(int n_pos, int n_q, int n_kv, int nc);
 // column j attends to positions [0, n_pos + j); with dig_out, the output is also written as
 // activation digits (kind dig_kind, column stride dig_stride words) for the next GEMV
 hipError_t launch_attn(const float* q, int64_t q_stride, const uint16_t* kc, const uint16_t* vc, int64_t kv_stride,

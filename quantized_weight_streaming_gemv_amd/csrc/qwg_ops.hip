@@ -298,6 +298,13 @@ AttnPlan plan_attn(int n_pos, int n_q, int n_kv, int nc) {
   return p;
 }
 
+size_t attn_work_bound(int n_pos, int n_q, int n_kv, int nc) {
+  // single-tile splits have the most records; longer splits only ever need fewer
+  const int64_t span = (int64_t)n_pos + nc - 1;
+  return (size_t)n_kv * (size_t)((span + ATT_T - 1) / ATT_T) * (size_t)nc * (size_t)(n_q / n_kv) * (HEAD_DIM + 2) *
+         sizeof(float);
+}
+
 // LDS of a k_attn workgroup for G query rows: q, scores, the K and V tiles
 static size_t attn_lds_bytes(int rows) {
   return (size_t)rows * HEAD_DIM * 4 + (size_t)rows * ATT_T * 4 + (size_t)ATT_T * KROW * 2 + (size_t)ATT_T * HEAD_DIM * 2;
