@@ -36,7 +36,7 @@ HBM_PEAK_GBPS = 8000.0
 # taken again.
 GEMV_TRAFFIC = {
     "workload": "llama70b-q4_k-resident",
-    "sources_sha256": "181c10db3bfe53d937d203fecf8a38cefc824b12e9e354b73c3a1872c16723a6",
+    "sources_sha256": "818bef10f59d8b8a53cd6a76f48f9c7a759a9a2d4a958b8fb30102584a72e111",
     "fetch_scale": 1.99975, "write_scale": 1.00000,
     "classes": {  # label -> (fetch KiB, write KiB) per launch
         "qkv": (24028.3, 44.8),
