@@ -99,10 +99,13 @@ int qwg_dequantize(int qtype, const void* d_packed, int64_t rows, int64_t k, flo
  * and Q6_K with k a multiple of 512; k <= 65536.
  * n_cols > 1 is the multi-column form used to verify self-speculative drafts ([NT] "Key features");
  * 9..64 columns run the prompt-prefill GEMM ([NT] "Quick start": -p), which reads each weight once
- * per call on the matrix cores.
+ * per call on the matrix cores.  Every form is within |y - y_exact| <= 1e-4 sum|W x| + 1e-6 per
+ * output; the products are exact integers (32-bit fixed-point activation digits) except for
+ * 9..64 columns of Q4_K / Q5_K, which multiply exact fp16 weights by two-piece fp16 activations
+ * with fp32 accumulation.
  * d_work: caller-owned device scratch of at least qwg_gemv_work_bytes(qtype, rows, k, n_cols) bytes
- * (16-byte aligned), which the call overwrites with the activation's fixed-point digits and, for
- * shapes whose activation does not fit on chip at once, the K-split partial sums.  Calls in flight
+ * (16-byte aligned), which the call overwrites with the activation's digits (or fp16 pieces) and,
+ * for shapes whose activation does not fit on chip at once, the K-split partial sums.  Calls in flight
  * at the same time (on one stream or several) need their own d_work; the library allocates nothing
  * and never synchronizes here.  d_packed and d_x 16-byte aligned.  rows == 0 leaves d_y untouched.
  * qwg_gemv_work_bytes returns 0 for shapes the call rejects. */
@@ -179,8 +182,10 @@ int qwg_rope(float* d_v, int n_heads, int head_dim, const float* d_table, int po
  * head_dim must be 128; n_cols <= 64; n_kv <= 64; n_q / n_kv <= 64; n_pos <= 262144.  With fewer than 32
  * query rows per KV head (n_cols * n_q / n_kv < 32: decode steps, short verify passes) each workgroup
  * takes one (kv head, split, column); from 32 rows (a prompt pass, a verify pass of 4+ columns at
- * n_q / n_kv = 8) the call runs on the matrix cores (fp32 products and sums), 64 / (n_q / n_kv)
- * columns (at most 64 query rows) per workgroup.
+ * n_q / n_kv = 8) the call runs on the matrix cores, 64 / (n_q / n_kv) columns (at most 64 query
+ * rows) per workgroup and up to four 64-position tiles per split: K and V as the fp16 values given,
+ * queries and softmax weights as two fp16 pieces each (22 significant bits), fp32 sums, within the
+ * error of fp32 arithmetic.
  * qwg_attn_work_bytes returns 0 for shapes outside these limits. */
 size_t qwg_attn_work_bytes(int n_pos, int n_q, int n_kv, int head_dim, int n_cols);
 int qwg_attn_decode(const float* d_q, const uint16_t* d_kc, const uint16_t* d_vc, int n_pos, int n_q, int n_kv,
