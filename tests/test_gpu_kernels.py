@@ -361,7 +361,7 @@ def test_rope_table_and_kernel(ops):
                                             (16, 2, 70, 3), (64, 8, 257, 5), (32, 2, 9000, 1), (24, 2, 300, 2),
                                             (8, 8, 130, 2), (2, 1, 262144, 2), (64, 8, 300, 13),
                                             (8, 2, 100, 64), (64, 8, 2049, 64), (64, 2, 70, 12), (64, 1, 90, 64),
-                                            (24, 2, 300, 20)])
+                                            (24, 2, 300, 20), (64, 8, 2049, 32)])
 def test_attention(ops, nq, nkv, npos, nc):
     # (32, 2, 9000): 141 splits and 16 query rows per KV head; (24, 2, 300, 2): 12 rows per head;
     # (8, 8, 130, 2): one query head per KV head (plain multi-head attention); (2, 1, 262144, 2): the
@@ -369,7 +369,9 @@ def test_attention(ops, nq, nkv, npos, nc):
     # (64, 8, 4097, 4), (64, 8, 257, 5) and the prompt-width cases) on the matrix cores: 64 / G columns
     # per workgroup (64 query rows, 16 per wave), with a last block of 5 columns in (64, 8, 300, 13),
     # one column of 64 rows per workgroup in (64, 1, 90, 64), and G = 12 in (24, 2, 300, 20): 5
-    # columns, 60 rows, the last wave's block partly empty
+    # columns, 60 rows, the last wave's block partly empty.  Wide passes fold several 64-position
+    # tiles into one split: four in (64, 8, 2049, 64) (9 splits), two in (64, 8, 2049, 32) (17
+    # splits, the last of one tile)
     import torch
     hd = 128
     ctx = npos + nc - 1
