@@ -119,9 +119,9 @@ def test_mixed_layer_types_spec_step(qwg):
 @pytest.mark.parametrize("case", [(synth.Q4_K, synth.Q4_K, 4, -1, 11), (synth.Q6_K, synth.Q5_K, 4, -1, 11),
                                   (synth.Q4_K, synth.Q4_K, 8, 2, 11), (synth.Q4_K, synth.Q4_K, 64, -1, 40),
                                   (synth.Q6_K, synth.Q5_K, 64, -1, 70), (synth.Q4_K, synth.Q4_K, 16, 2, 37),
-                                  (synth.Q8_0, synth.Q8_0, 64, -1, 19)],
+                                  (synth.Q8_0, synth.Q8_0, 64, -1, 19), (synth.Q5_K, synth.Q4_K, 64, -1, 97)],
                          ids=["q4k-4col", "q6k-q5k-4col-mfma", "q4k-8col-streamed", "q4k-64col", "q6k-q5k-64col-2pass",
-                              "q4k-16col-streamed", "q8_0-64col-falls-back-to-8"])
+                              "q4k-16col-streamed", "q8_0-64col-falls-back-to-8", "q5k-q4k-64col-then-33"])
 def test_prefill_matches_sequential_steps(qwg, case):
     """Prefill of a prompt in passes of max_cols columns (ragged last pass; 9..64-column passes on the
     prefill GEMM, Q8_0 in passes of 8) equals sequential decode steps of the oracle: next token, its
@@ -129,10 +129,11 @@ def test_prefill_matches_sequential_steps(qwg, case):
     qa, qf, cols, res, n_prompt = case
     wl = synth.tiny(qa, qf, wid=230 + cols + res)
     prompt = [(wl.first_token() + 7919 * i) % wl.vocab for i in range(n_prompt)]
-    m = qwg.make_model(wl, max_cols=cols, n_resident=res, max_ctx=wl.n_prior + 80)
+    ctx = wl.n_prior + max(80, n_prompt + 8)
+    m = qwg.make_model(wl, max_cols=cols, n_resident=res, max_ctx=ctx)
     qwg.load(m, wl)
     nxt, logits = m.prefill(prompt, want_logits=True)
-    om = oracle.OracleModel(wl, max_ctx=wl.n_prior + 80)
+    om = oracle.OracleModel(wl, max_ctx=ctx)
     for t in prompt:
         r = om.decode(t)
     assert m.n_past == om.n_past == wl.n_prior + len(prompt)
