@@ -19,6 +19,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -33,10 +34,11 @@ HBM_PEAK_GBPS = 8000.0
 # counter reads for a device copy of 256 MiB (FETCH_SIZE reads half of the copy's 256 MiB: scale
 # 1.99975; WRITE_SIZE all of it: scale 1.0).  Valid only for the kernel sources it was taken on (their
 # sha256 below): after any change to them `roofline.traffic` is reported as null until the passes are
-# taken again.
+# taken again, or until the decode kernels' device assembly is shown to be unchanged (label numbers
+# aside) and the sha is moved to the new sources.
 GEMV_TRAFFIC = {
     "workload": "llama70b-q4_k-resident",
-    "sources_sha256": "818bef10f59d8b8a53cd6a76f48f9c7a759a9a2d4a958b8fb30102584a72e111",
+    "sources_sha256": "4296ac0256acfe180d8b5ebc39f5ffc57fa9670b133ad39e9cd2927f1518ccbf",
     "fetch_scale": 1.99975, "write_scale": 1.00000,
     "classes": {  # label -> (fetch KiB, write KiB) per launch
         "qkv": (24028.3, 44.8),
@@ -290,6 +292,7 @@ def main() -> int:
                     help="after the decode measurements, time a prefill of this many prompt tokens (0: none); "
                          "reported under 'prefill', the metric stays decode tok/s")
     ap.add_argument("--prefill-cols", type=int, default=64, help="columns per prefill pass (the model's max_cols)")
+    ap.add_argument("--prefill-reps", type=int, default=5, help="timed prefill passes (the median is reported)")
     ap.add_argument("--verify-form", choices=["mfma", "dot"], default="mfma",
                     help="2..4-column Q5_K/Q6_K GEMVs of the verify pass: matrix cores or integer dot products")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -419,20 +422,28 @@ def main() -> int:
     prefill = None
     if args.prefill > 0:
         # a deterministic synthetic prompt, after everything else (it extends the context)
+        # (each pass starts at the same position: the context is cut back to it after every pass)
         prompt = [(wl.first_token() + 7919 * i) % wl.vocab for i in range(args.prefill)]
+        base = m.n_past
         m.prefill(prompt[: max_cols])  # warm-up pass
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        m.prefill(prompt)
-        torch.cuda.synchronize()
-        dt_p = time.perf_counter() - t0
+        m.truncate(base)
+        reps = []
+        for _ in range(max(1, args.prefill_reps)):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            m.prefill(prompt)
+            torch.cuda.synchronize()
+            reps.append(time.perf_counter() - t0)
+            m.truncate(base)
+        dt_p = statistics.median(reps)
         # passes wider than 8 columns need the prompt GEMM: K-quant layer matrices with K % 512 == 0
         kq = all(wl.qtype_of(t, l) in (synth.Q4_K, synth.Q5_K, synth.Q6_K)
                  for l in range(wl.n_layers) for t in (synth.WQ, synth.WO, synth.WGATE, synth.WDOWN))
         kq = kq and wl.hidden % 512 == 0 and wl.ffn % 512 == 0 and (wl.n_q * wl.head_dim) % 512 == 0
         width = max_cols if kq else min(max_cols, 8)
         prefill = {"tokens": args.prefill, "columns_per_pass": width, "ms": round(dt_p * 1e3, 3),
-                   "tok_s": round(args.prefill / dt_p, 1),
+                   "tok_s": round(args.prefill / dt_p, 1), "timing": "median of %d passes" % len(reps),
+                   "ms_each": [round(x * 1e3, 3) for x in reps], "context_before": base,
                    "arithmetic": ("passes of 9-64 columns: Q4_K/Q5_K GEMMs and the attention on "
                                   "v_mfma_f32_16x16x32_f16 with exact fp16 weights (K/V) and two-piece "
                                   "fp16 activations (queries, softmax weights), fp32 accumulation; "

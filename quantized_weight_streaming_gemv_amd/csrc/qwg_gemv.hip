@@ -1126,14 +1126,18 @@ __global__ __launch_bounds__(64 * GM_WAVES) void k_gemm_mfma(GemvArgs a) {
 //   A: column 16 cg + n's pieces of the same eight elements (the DIG_F16 element order);
 //   D: (column 16 cg + 4 g + r, row n), r = 0..3.
 // A workgroup of 8 waves takes 256 rows (two 16-row tiles per wave, so every A operand read from LDS
-// meets two B operands) of one K split.  The K loop is outermost, one superblock of all 64 columns
-// per step, in two LDS buffers: while the waves multiply one superblock, the next one's operands are
-// on their way from global memory straight into the other buffer (global_load_lds_dwordx4, no
-// registers), so the staging no longer stalls every wave between steps.
+// meets two B operands) of one K split.  The K loop is outermost, one superblock of all columns per
+// step, in two LDS buffers: while the waves multiply one superblock, the next one's operands are on
+// their way from global memory straight into the other buffer (global_load_lds_dwordx4, no
+// registers), so the staging no longer stalls every wave between steps.  The kernel is built for
+// CG = 1, 2 or 4 column groups of 16 (passes of up to 16, 32 or 64 columns), so that a narrow pass
+// multiplies no empty groups and its smaller buffers leave room for a second workgroup per CU.
 constexpr int GF_WAVES = 8;
-constexpr int GF_BLK = 64;                                // 16-B entries of one operand block (64 lanes)
-constexpr int GF_FRAGS = 8 * 2 * 4;                       // operand blocks per superblock: [chunk][piece][group]
-constexpr int GF_BUF = (GF_FRAGS + 4) * GF_BLK + 64 / 4;  // 16-B entries per buffer (+ 4 minimum-term blocks, scales)
+constexpr int GF_BLK = 64;  // 16-B entries of one operand block (64 lanes)
+// operand blocks per superblock ([chunk][piece][group]) and 16-B entries per buffer (those, a
+// minimum-term block per group and the 64 column scales)
+constexpr int gf_frags(int cg) { return 8 * 2 * cg; }
+constexpr int gf_buf(int cg) { return (gf_frags(cg) + cg) * GF_BLK + 64 / 4; }
 
 typedef _Float16 qwg_h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 qwg_h2 __attribute__((ext_vector_type(2)));
@@ -1194,38 +1198,42 @@ typedef const __attribute__((address_space(1))) void* qwg_gptr;
 typedef __attribute__((address_space(3))) void* qwg_lptr;
 
 // Requests superblock sb of every column (DIG_F16 pieces) into LDS buffer buf: wave w copies the
-// operand blocks (chunk, piece) = (w >> 2) + 2 j, j = 0..7, of column group w & 3 (lane 16 g + i: word g
-// of column 16 (w & 3) + i), waves 0..3 also their group's minimum-term block (lanes 0..15 hi sums,
-// 16..31 lo sums), wave 4 the 64 scales.  Lanes of columns >= nc load nothing: their entries keep the
-// zeros the kernel wrote at its start.
+// operand blocks (chunk, piece) = w / CG + (8 / CG) j, j = 0..2 CG - 1, of column group w % CG (lane
+// 16 g + i: word g of column 16 (w % CG) + i), waves 0..CG - 1 also their group's minimum-term block
+// (lanes 0..15 hi sums, 16..31 lo sums), wave 4 the scales.  Lanes of columns >= nc load nothing: their
+// entries keep the zeros the kernel wrote at its start.
+template <int CG>
 __device__ __forceinline__ void f16_stage(uint4* buf, const GemvArgs& a, int sb, int wave, int lane) {
-  const int cg = wave & 3, gq = lane >> 4, col = 16 * cg + (lane & 15);
+  static_assert(CG == 1 || CG == 2 || CG == 4, "a whole number of groups per wave");
+  const int cg = (int)((unsigned)wave % CG), gq = lane >> 4, col = 16 * cg + (lane & 15);
   const uint4* xc = a.xd + (int64_t)col * a.xd_stride + (int64_t)sb * (F16_SB_WORDS / 4);
   if (col < a.nc) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int cp = (wave >> 2) + 2 * j;  // chunk * 2 + piece
-      __builtin_amdgcn_global_load_lds((qwg_gptr)(xc + cp * 4 + gq), (qwg_lptr)(buf + (cp * 4 + cg) * GF_BLK), 16, 0, 0);
+    for (int j = 0; j < 2 * CG; ++j) {
+      const int cp = (int)((unsigned)wave / CG) + (8 / CG) * j;  // chunk * 2 + piece
+      __builtin_amdgcn_global_load_lds((qwg_gptr)(xc + cp * 4 + gq), (qwg_lptr)(buf + (cp * CG + cg) * GF_BLK), 16, 0,
+                                       0);
     }
   }
-  if (wave < 4 && lane < 32 && col < a.nc)
-    __builtin_amdgcn_global_load_lds((qwg_gptr)(xc + F16_SUM_WORD / 4 + gq), (qwg_lptr)(buf + (GF_FRAGS + cg) * GF_BLK),
-                                     16, 0, 0);
+  if (wave < CG && lane < 32 && col < a.nc)
+    __builtin_amdgcn_global_load_lds((qwg_gptr)(xc + F16_SUM_WORD / 4 + gq),
+                                     (qwg_lptr)(buf + (gf_frags(CG) + cg) * GF_BLK), 16, 0, 0);
   if (wave == 4 && lane < a.nc)
     __builtin_amdgcn_global_load_lds(
         (qwg_gptr)((const uint32_t*)(a.xd + (int64_t)lane * a.xd_stride + (int64_t)sb * (F16_SB_WORDS / 4)) +
                    F16_SCALE_WORD),
-        (qwg_lptr)(buf + (GF_FRAGS + 4) * GF_BLK), 4, 0, 0);
+        (qwg_lptr)(buf + (gf_frags(CG) + CG) * GF_BLK), 4, 0, 0);
 }
 
-template <int QT>
+template <int QT, int CG>
 __global__ __launch_bounds__(64 * GF_WAVES) void k_gemm_f16(GemvArgs a) {
   static_assert(QT == Q4_K || QT == Q5_K, "formats with integer sub-block scales and minima");
   constexpr int T = 2;  // tiles per wave
+  constexpr int FR = gf_frags(CG), BUF = gf_buf(CG);
   // two buffers, each [chunk][piece][group][64] operand blocks, [group][64] minimum-term blocks and
-  // the 64 columns' scales; separate arrays, so the compiler sees that the requests into one buffer
+  // the 64 column scales; separate arrays, so the compiler sees that the requests into one buffer
   // never touch the one being read
-  __shared__ uint4 buf0[GF_BUF], buf1[GF_BUF];
+  __shared__ uint4 buf0[BUF], buf1[BUF];
   __shared__ float lrs[64];  // fused SwiGLU epilogue (no K split, a.part null): each column's RMSNorm scale
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1245,18 +1253,18 @@ __global__ __launch_bounds__(64 * GF_WAVES) void k_gemm_f16(GemvArgs a) {
     srow[t] = slot_row(a.w.ilv, a.w.nch, row);
   }
   const uint32_t rot_lo = (uint32_t)(28 + 2 * g) & 31u, rot_hi = (uint32_t)(29 + 2 * g) & 31u;  // Q5_K fifth bits
-  qwg_f32x4 y[T][4];
+  qwg_f32x4 y[T][CG];
 #pragma unroll
   for (int t = 0; t < T; ++t)
 #pragma unroll
-    for (int cg = 0; cg < 4; ++cg) y[t][cg] = qwg_f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int cg = 0; cg < CG; ++cg) y[t][cg] = qwg_f32x4{0.f, 0.f, 0.f, 0.f};
 
   // the superblock in buffer b, with r[t] its raw weights.  Chunk c's A operands are read from LDS and
   // its B operands built while chunk c - 1's products run (two sets of each, chosen at compile time).
   auto superblock = [&](const uint4* b, const SbRaw<QT>* r) {
-    const uint4* lmin = b + GF_FRAGS * GF_BLK;
-    const float* lscale = (const float*)(b + (GF_FRAGS + 4) * GF_BLK);
-    qwg_f32x4 P[T][4];
+    const uint4* lmin = b + FR * GF_BLK;
+    const float* lscale = (const float*)(b + (FR + CG) * GF_BLK);
+    qwg_f32x4 P[T][CG];
     uint64_t ps[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) ps[t] = (uint64_t)r[t].h.x | ((uint64_t)r[t].h.y << 32);
@@ -1282,12 +1290,12 @@ __global__ __launch_bounds__(64 * GF_WAVES) void k_gemm_f16(GemvArgs a) {
           qh[q2][t][3] = lane_fetch(src, r[t].qh.w);
         }
       }
-    uint4 ah[2][4], al[2][4], bw[2][T];
+    uint4 ah[2][CG], al[2][CG], bw[2][T];
     auto fetch_a = [&](int c, uint4* h, uint4* l) {
 #pragma unroll
-      for (int cg = 0; cg < 4; ++cg) {
-        h[cg] = b[((c * 2 + 0) * 4 + cg) * GF_BLK + lane];
-        l[cg] = b[((c * 2 + 1) * 4 + cg) * GF_BLK + lane];
+      for (int cg = 0; cg < CG; ++cg) {
+        h[cg] = b[((c * 2 + 0) * CG + cg) * GF_BLK + lane];
+        l[cg] = b[((c * 2 + 1) * CG + cg) * GF_BLK + lane];
       }
     };
     auto build_b = [&](int c, uint4* bo) {
@@ -1320,11 +1328,11 @@ __global__ __launch_bounds__(64 * GF_WAVES) void k_gemm_f16(GemvArgs a) {
       if (c + 1 < 8) build_b(c + 1, bw[nxt]);
       const qwg_f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int cg = 0; cg < 4; ++cg)
+      for (int cg = 0; cg < CG; ++cg)
 #pragma unroll
         for (int t = 0; t < T; ++t) P[t][cg] = mfma_f16(ah[cur][cg], bw[cur][t], c == 0 ? z : P[t][cg]);
 #pragma unroll
-      for (int cg = 0; cg < 4; ++cg)
+      for (int cg = 0; cg < CG; ++cg)
 #pragma unroll
         for (int t = 0; t < T; ++t) P[t][cg] = mfma_f16(al[cur][cg], bw[cur][t], P[t][cg]);
     }
@@ -1345,7 +1353,7 @@ __global__ __launch_bounds__(64 * GF_WAVES) void k_gemm_f16(GemvArgs a) {
       dm64[t] = 64.0f * half_bits_to_float(r[t].h.w >> 16);
     }
 #pragma unroll
-    for (int cg = 0; cg < 4; ++cg) {
+    for (int cg = 0; cg < CG; ++cg) {
       const uint4 am = lmin[cg * GF_BLK + lane];
       const float4 s4 = *(const float4*)&lscale[16 * cg + 4 * g];
       const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
@@ -1360,7 +1368,7 @@ __global__ __launch_bounds__(64 * GF_WAVES) void k_gemm_f16(GemvArgs a) {
   };
 
   // zeros in both buffers: the entries of columns >= nc and the minimum-term lanes 32..63 stay zero
-  for (int i = tid; i < GF_BUF; i += 64 * GF_WAVES) {
+  for (int i = tid; i < BUF; i += 64 * GF_WAVES) {
     buf0[i] = make_uint4(0, 0, 0, 0);
     buf1[i] = make_uint4(0, 0, 0, 0);
   }
@@ -1389,14 +1397,14 @@ __global__ __launch_bounds__(64 * GF_WAVES) void k_gemm_f16(GemvArgs a) {
   // sbi from `now` with weights wc, then wait for this wave's requests and meet the other waves (after
   // which `now` may be overwritten and `nxt` is complete)
   auto step = [&](int sbi, const uint4* now, uint4* nxt, const SbRaw<QT>* wc, SbRaw<QT>* wn) {
-    if (sbi + 1 < nsb) f16_stage(nxt, a, sb0 + sbi + 1, wave, lane);
+    if (sbi + 1 < nsb) f16_stage<CG>(nxt, a, sb0 + sbi + 1, wave, lane);
     load(wn, sbi + 1);
     if (live) superblock(now, wc);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
   };
   if (nsb > 0) {
-    f16_stage(buf0, a, sb0, wave, lane);
+    f16_stage<CG>(buf0, a, sb0, wave, lane);
     load(wa, 0);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's requests are in LDS
     __syncthreads();
@@ -1412,7 +1420,7 @@ __global__ __launch_bounds__(64 * GF_WAVES) void k_gemm_f16(GemvArgs a) {
     for (int t = 0; t < T; ++t) {
       const int row = r0 + 16 * t + n;
 #pragma unroll
-      for (int cg = 0; cg < 4; ++cg)
+      for (int cg = 0; cg < CG; ++cg)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int col = 16 * cg + 4 * g + i;
@@ -1953,9 +1961,15 @@ hipError_t launch_gemv(int qt, const MatView& w, int64_t k, const void* xd, int6
     if (p.mfma == 3) {
       GemvArgs af = a;
       if (fused) af.part = nullptr;
-      switch (qt) {
-        case Q4_K: go(d0, k_gemm_f16<Q4_K>, grid, block, p.lds, af); break;
-        case Q5_K: go(d0, k_gemm_f16<Q5_K>, grid, block, p.lds, af); break;
+      // the narrowest build whose groups hold nc columns
+      const int ncg = nc <= 16 ? 1 : nc <= 32 ? 2 : nc <= 64 ? 4 : 0;
+      switch (qt * 8 + ncg) {
+        case Q4_K * 8 + 1: go(d0, k_gemm_f16<Q4_K, 1>, grid, block, p.lds, af); break;
+        case Q4_K * 8 + 2: go(d0, k_gemm_f16<Q4_K, 2>, grid, block, p.lds, af); break;
+        case Q4_K * 8 + 4: go(d0, k_gemm_f16<Q4_K, 4>, grid, block, p.lds, af); break;
+        case Q5_K * 8 + 1: go(d0, k_gemm_f16<Q5_K, 1>, grid, block, p.lds, af); break;
+        case Q5_K * 8 + 2: go(d0, k_gemm_f16<Q5_K, 2>, grid, block, p.lds, af); break;
+        case Q5_K * 8 + 4: go(d0, k_gemm_f16<Q5_K, 4>, grid, block, p.lds, af); break;
         default: return hipErrorInvalidValue;
       }
       if (fused) return hipGetLastError();

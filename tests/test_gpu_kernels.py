@@ -241,10 +241,11 @@ def test_gemv_two_streams_in_flight(ops):
 @pytest.mark.parametrize("qt", [synth.Q4_K, synth.Q5_K, synth.Q6_K], ids=["Q4_K", "Q5_K", "Q6_K"])
 @pytest.mark.parametrize("shape", [(16, 512), (300, 2048), (1000, 8192), (70, 28672), (4096 + 48 + 6, 1024)],
                          ids=["one_tile", "ragged", "k8192", "k28672_splits", "many_blocks"])
-@pytest.mark.parametrize("nc", [9, 33, 64])
+@pytest.mark.parametrize("nc", [9, 16, 17, 32, 33, 64])
 def test_gemv_prefill_columns(ops, qt, shape, nc):
-    """9..64 columns (the prompt-prefill GEMM: 64 columns per step staged in LDS, 16-row tiles, K splits
-    added by the reduction kernel): every row of every column within the row bound."""
+    """9..64 columns (the prompt-prefill GEMM: every column of a superblock staged in LDS, 16-row
+    tiles, builds for 16, 32 and 64 columns, K splits added by the reduction kernel): every row of
+    every column within the row bound."""
     rows, k = shape
     W = synth.matrix(synth.DEFAULT_DIST[qt], k, rows, tkey=synth.key(15, qt * 1000 + k))
     x = synth.normal_f32(synth.key(15, 70 + nc), nc * k).reshape(nc, k)
@@ -287,6 +288,22 @@ def test_prompt_gemm_bias_and_margin(ops, qt):
     bias = float(((y - yr) / ar).mean())
     assert ratio.max() < 1e-2, float(ratio.max())
     assert abs(bias) < 1.2e-9, bias
+
+
+@pytest.mark.parametrize("qt", [synth.Q4_K, synth.Q5_K], ids=["Q4_K", "Q5_K"])
+@pytest.mark.parametrize("shape", [(1000, 8192), (300, 28672)], ids=["k8192", "k28672_splits"])
+def test_prompt_gemm_narrow_builds_match_wide(ops, qt, shape):
+    """The fp16 prompt GEMM is built for one, two and four groups of 16 columns: a pass of 9, 16, 17,
+    32 or 33 columns gives exactly the first columns of a 64-column pass over the same inputs (each
+    column's products and their order do not depend on the other columns)."""
+    rows, k = shape
+    W = synth.matrix(synth.DEFAULT_DIST[qt], k, rows, tkey=synth.key(15, qt * 1000 + k + 1))
+    x = synth.normal_f32(synth.key(15, 170), 64 * k).reshape(64, k)
+    P = packed_of(ops, qt, W, rows, k)
+    y64 = ops.gemv(qt, P, rows, k, dev(x)).cpu().numpy()
+    for nc in (9, 16, 17, 32, 33):
+        y = ops.gemv(qt, P, rows, k, dev(np.ascontiguousarray(x[:nc]))).cpu().numpy()
+        assert np.array_equal(y, y64[:nc]), (nc, np.argwhere(y != y64[:nc])[:5])
 
 
 def test_gemv_q8_0_4096_full(ops):
