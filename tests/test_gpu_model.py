@@ -127,7 +127,17 @@ def test_prefill_matches_sequential_steps(qwg, case):
     prefill GEMM, Q8_0 in passes of 8) equals sequential decode steps of the oracle: next token, its
     logits, the KV rows, n_past."""
     qa, qf, cols, res, n_prompt = case
-    wl = synth.tiny(qa, qf, wid=230 + cols + res)
+    _prefill_vs_steps(qwg, synth.tiny(qa, qf, wid=230 + cols + res), cols, res, n_prompt)
+
+
+def test_prefill_three_query_heads_per_kv_head(qwg):
+    """12 query heads on 4 KV heads (three per KV head, an attention output of 1536 per column): a
+    40-token prompt in one 64-column pass equals sequential decode steps of the oracle."""
+    wl = synth.tiny(synth.Q4_K, wid=301, hidden=1536, n_q=12, n_kv=4)
+    _prefill_vs_steps(qwg, wl, 64, -1, 40)
+
+
+def _prefill_vs_steps(qwg, wl, cols, res, n_prompt):
     prompt = [(wl.first_token() + 7919 * i) % wl.vocab for i in range(n_prompt)]
     ctx = wl.n_prior + max(80, n_prompt + 8)
     m = qwg.make_model(wl, max_cols=cols, n_resident=res, max_ctx=ctx)
