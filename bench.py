@@ -38,7 +38,7 @@ HBM_PEAK_GBPS = 8000.0
 # aside) and the sha is moved to the new sources.
 GEMV_TRAFFIC = {
     "workload": "llama70b-q4_k-resident",
-    "sources_sha256": "4296ac0256acfe180d8b5ebc39f5ffc57fa9670b133ad39e9cd2927f1518ccbf",
+    "sources_sha256": "9194cdf48ad4306f4c39fca075009f893957c666c49a9df4a6680050005a2a8e",
     "fetch_scale": 1.99975, "write_scale": 1.00000,
     "classes": {  # label -> (fetch KiB, write KiB) per launch
         "qkv": (24028.3, 44.8),

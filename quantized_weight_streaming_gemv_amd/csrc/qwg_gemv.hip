@@ -1268,6 +1268,10 @@ __global__ __launch_bounds__(64 * GF_WAVES) void k_gemm_f16(GemvArgs a) {
     uint64_t ps[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) ps[t] = (uint64_t)r[t].h.x | ((uint64_t)r[t].h.y << 32);
+    // Q5_K fifth bits: the narrow builds fetch every chunk's from lane n + 16 q2 at once; the
+    // four-group build, short of registers (spills otherwise), fetches each chunk's when it builds
+    // the chunk's operand
+    constexpr bool late5 = CG == 4;
     uint32_t R[2][T][4], qh[2][T][4];  // transposed quant words (and fifth bits) of quarters 0, 1
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2)
@@ -1282,7 +1286,7 @@ __global__ __launch_bounds__(64 * GF_WAVES) void k_gemm_f16(GemvArgs a) {
         lane_swap32(R[q2][t][1], R[q2][t][3]);
         lane_swap16(R[q2][t][0], R[q2][t][1]);
         lane_swap16(R[q2][t][2], R[q2][t][3]);  // R[q2][t][j] = quant word g of chunk 4 q2 + j
-        if constexpr (QT == Q5_K) {
+        if constexpr (QT == Q5_K && !late5) {
           const int src = n + 16 * q2;
           qh[q2][t][0] = lane_fetch(src, r[t].qh.x);
           qh[q2][t][1] = lane_fetch(src, r[t].qh.y);
@@ -1310,7 +1314,10 @@ __global__ __launch_bounds__(64 * GF_WAVES) void k_gemm_f16(GemvArgs a) {
           lo = (word ^ 0x88888888u) & 0x0F0F0F0Fu;  // the stored nibbles are q XOR 8
           hi = ((word >> 4) ^ 0x08080808u) & 0x0F0F0F0Fu;
         } else {
-          const uint32_t f = qh[c >> 2][t][c & 3];
+          const uint4& qv = r[t].qh;
+          const uint32_t f =
+              late5 ? lane_fetch(n + 16 * (c >> 2), (c & 3) == 0 ? qv.x : (c & 3) == 1 ? qv.y : (c & 3) == 2 ? qv.z : qv.w)
+                    : qh[c >> 2][t][c & 3];
           const uint32_t l5 = __builtin_rotateright32(f, rot_lo), h5 = __builtin_rotateright32(f, rot_hi);
           lo = (word & 0x0F0F0F0Fu) | (l5 & 0x10101010u);
           hi = ((word >> 4) & 0x0F0F0F0Fu) | (h5 & 0x10101010u);
