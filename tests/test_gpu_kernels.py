@@ -336,6 +336,29 @@ def test_gemv_size_limits(ops, qt, nc):
         ops.gemv(qt, torch.zeros(1 << 20, dtype=torch.uint8, device=DEV), 1, k + 256, torch.zeros(k + 256, device=DEV))
 
 
+@pytest.mark.parametrize("qt", [synth.Q4_K, synth.Q5_K, synth.Q6_K], ids=["Q4_K", "Q5_K", "Q6_K"])
+@pytest.mark.parametrize("nc", [16, 64])
+def test_prompt_gemm_size_limits(ops, qt, nc):
+    """The prompt GEMM at K = 65536 (the largest K the library takes: 256 superblocks in K splits) on
+    one ragged 5-row tile, within the row bound, in its one-group and four-group builds (Q4_K, Q5_K)
+    and the i8 form (Q6_K); 0 rows leaves the output alone; 65 columns, one more than the widest
+    pass, is refused before anything runs."""
+    from quantized_weight_streaming_gemv_amd import QwgError
+    rows, k = 5, 65536
+    W = synth.matrix(synth.DEFAULT_DIST[qt], k, rows, tkey=synth.key(2, qt * 1000 + 5))
+    x = synth.normal_f32(synth.key(2, 90 + nc), nc * k).reshape(nc, k)
+    y = ops.gemv(qt, packed_of(ops, qt, W, rows, k), rows, k, dev(x)).cpu().numpy()
+    yr, ar = oracle.gemv(qt, W, rows, k, x)
+    assert gemv_ok(y, yr, ar).all()
+    out = torch.full((nc, 4), 7.0, dtype=torch.float32, device=DEV)
+    ops.gemv(qt, torch.zeros(1024, dtype=torch.uint8, device=DEV), 0, 512, dev(np.ascontiguousarray(x[:, :512])),
+             out=out)
+    assert (out == 7.0).all().item()
+    with pytest.raises(QwgError):
+        ops.gemv(qt, torch.zeros(4096, dtype=torch.uint8, device=DEV), 1, 512,
+                 torch.zeros((65, 512), dtype=torch.float32, device=DEV))
+
+
 def test_gemv_rejects_bad_shapes(ops):
     from quantized_weight_streaming_gemv_amd import QwgError
     W = torch.zeros(1024, dtype=torch.uint8, device=DEV)
