@@ -421,10 +421,12 @@ def main() -> int:
     m.set_timing(-1)
     prefill = None
     if args.prefill > 0:
-        # a deterministic synthetic prompt, after everything else (it extends the context)
-        # (each pass starts at the same position: the context is cut back to it after every pass)
+        # a deterministic synthetic prompt, after everything else, each pass after the workload's
+        # cached positions: the context is cut back to them before the warm-up pass and after every
+        # timed pass (the decode steps' KV rows are overwritten; nothing after this reads them)
         prompt = [(wl.first_token() + 7919 * i) % wl.vocab for i in range(args.prefill)]
-        base = m.n_past
+        base = wl.n_prior
+        m.truncate(base)
         m.prefill(prompt[: max_cols])  # warm-up pass
         m.truncate(base)
         reps = []
